@@ -1,0 +1,414 @@
+/*
+ * ct_oracle.c -- plain fp64 reference for the N-D transposed convolution
+ * (ONNX ConvTranspose).
+ *
+ * TEST INFRASTRUCTURE ONLY.  Only tests/, __graft_entry__.smoke() and bench.py's
+ * cpu_baseline leg may load this library.  It shares no code, header, table or helper
+ * with the HIP library; it has its own attribute resolver.
+ *
+ * What it computes (webgpu-kernels "ai.onnx.ConvTranspose" README):
+ *   - Description: the transpose of a convolution ("fractionally strided convolution",
+ *     "deconvolution") of X by filter W plus an optional bias B, with grouping.
+ *   - Inputs: X is (N, C, D1..Dn); W is (C, M/group, k1..kn); bias has length M.
+ *   - Attributes: auto_pad, dilations, group, kernel_shape, output_padding,
+ *     output_shape, pads (all begins, then all ends), strides.
+ *   - Outputs: Y has X's rank; spatial sizes follow from input size, kernel, strides,
+ *     dilations and padding.
+ * The ClikaRT "conv_transpose" API page states the same weight convention
+ * (input-channel first, C_out = weight[1]*groups) and that output_padding grows only
+ * the high side of each output axis.
+ *
+ * Definition used (the scatter form of the transposed convolution): every input sample
+ * X[n,c,i] is sent through every tap k of its group's filter to output position
+ *     o_a = i_a*s_a - b_a + k_a*d_a      on each spatial axis a,
+ * and added there when 0 <= o_a < O_a on all axes; out channel m = g*Mg + m' receives
+ * from input channels c of group g = c / Cg through W[c, m', k].  Y starts at bias[m]
+ * (or 0), so output positions no sample reaches hold the bias.
+ *
+ * Readings where the pages are silent (each one is listed in the design notes):
+ *   - output_padding must satisfy 0 <= op < max(stride, dilation);
+ *   - strides and dilations are >= 1; explicit pads are >= 0;
+ *   - explicit pads together with an auto_pad other than NOTSET are an error;
+ *   - SAME_UPPER / SAME_LOWER give O = L*s; the total padding
+ *     tot = s*(L-1) + op + d*(K-1) + 1 - O is split with C's truncating division,
+ *     the odd extra going to the end (UPPER) or the beginning (LOWER);
+ *   - output_shape, when given, sets O; tot is split as above (extra at the
+ *     beginning only for SAME_LOWER); explicit pads given as well must sum to tot;
+ *   - kernel_shape, when given, must equal W's spatial dims.
+ *
+ * Build: gcc -O2 -fopenmp -shared -fPIC ct_oracle.c -o libctoracle.so
+ */
+#include <stdint.h>
+#include <stdio.h>
+#include <stdlib.h>
+#include <string.h>
+
+#define OR_OK 0
+#define OR_INVALID 1
+
+#define OR_NOTSET 0
+#define OR_SAME_UPPER 1
+#define OR_SAME_LOWER 2
+#define OR_VALID 3
+
+typedef struct {
+    int nsp;
+    int64_t N, C, M, group, Cg, Mg;
+    int64_t L[3], K[3], s[3], d[3], b[3], e[3], op[3], O[3];
+} or_geom;
+
+static int or_fail(char *err, int errlen, const char *msg)
+{
+    if (err && errlen > 0) {
+        strncpy(err, msg, (size_t)errlen - 1);
+        err[errlen - 1] = 0;
+    }
+    return OR_INVALID;
+}
+
+/* Attribute defaults, validation, padding and output size (README, Attributes table). */
+static int or_resolve(int nsp, const int64_t *xs, const int64_t *ws, int auto_pad,
+                      const int64_t *strides, const int64_t *dilations, const int64_t *pads,
+                      const int64_t *output_padding, const int64_t *output_shape,
+                      const int64_t *kernel_shape, int64_t group, or_geom *g,
+                      char *err, int errlen)
+{
+    int a;
+    if (nsp < 1 || nsp > 3)
+        return or_fail(err, errlen, "spatial rank must be 1, 2 or 3");
+    if (auto_pad < OR_NOTSET || auto_pad > OR_VALID)
+        return or_fail(err, errlen, "unknown auto_pad");
+    if (group < 1)
+        return or_fail(err, errlen, "group must be >= 1");
+    for (a = 0; a < nsp + 2; a++) {
+        if (xs[a] < 0)
+            return or_fail(err, errlen, "negative input dimension");
+    }
+    if (ws[0] != xs[1])
+        return or_fail(err, errlen, "W.shape[0] must equal C");
+    if (ws[1] < 1)
+        return or_fail(err, errlen, "W.shape[1] (M/group) must be >= 1");
+    if (xs[1] % group != 0)
+        return or_fail(err, errlen, "C must be divisible by group");
+    if (pads && auto_pad != OR_NOTSET)
+        return or_fail(err, errlen, "explicit pads cannot be combined with auto_pad");
+
+    g->nsp = nsp;
+    g->N = xs[0];
+    g->C = xs[1];
+    g->group = group;
+    g->Cg = xs[1] / group;
+    g->Mg = ws[1];
+    g->M = ws[1] * group;
+
+    for (a = 0; a < nsp; a++) {
+        int64_t L = xs[2 + a], K = ws[2 + a];
+        int64_t s = strides ? strides[a] : 1;
+        int64_t d = dilations ? dilations[a] : 1;
+        int64_t op = output_padding ? output_padding[a] : 0;
+        int64_t full, O, b, e, tot;
+        if (K < 1)
+            return or_fail(err, errlen, "kernel dimensions must be >= 1");
+        if (kernel_shape && kernel_shape[a] != K)
+            return or_fail(err, errlen, "kernel_shape must match W's spatial dims");
+        if (s < 1)
+            return or_fail(err, errlen, "strides must be >= 1");
+        if (d < 1)
+            return or_fail(err, errlen, "dilations must be >= 1");
+        if (op < 0 || op >= (s > d ? s : d))
+            return or_fail(err, errlen, "output_padding must be in [0, max(stride, dilation))");
+        if (pads && (pads[a] < 0 || pads[a + nsp] < 0))
+            return or_fail(err, errlen, "explicit pads must be >= 0");
+
+        /* Size of the whole scatter footprint including output_padding. */
+        full = s * (L - 1) + op + d * (K - 1) + 1;
+        if (output_shape) {
+            O = output_shape[a];
+            if (O < 0)
+                return or_fail(err, errlen, "output_shape entries must be >= 0");
+            tot = full - O;
+            if (pads) {
+                if (pads[a] + pads[a + nsp] != tot)
+                    return or_fail(err, errlen, "pads disagree with output_shape");
+                b = pads[a];
+                e = pads[a + nsp];
+            } else if (auto_pad == OR_SAME_LOWER) {
+                e = tot / 2;
+                b = tot - e;
+            } else {
+                b = tot / 2;
+                e = tot - b;
+            }
+        } else if (auto_pad == OR_SAME_UPPER || auto_pad == OR_SAME_LOWER) {
+            O = L * s;
+            tot = full - O;
+            if (auto_pad == OR_SAME_UPPER) {
+                b = tot / 2;
+                e = tot - b;
+            } else {
+                e = tot / 2;
+                b = tot - e;
+            }
+        } else if (auto_pad == OR_VALID) {
+            b = 0;
+            e = 0;
+            O = full;
+        } else {
+            b = pads ? pads[a] : 0;
+            e = pads ? pads[a + nsp] : 0;
+            O = full - b - e;
+        }
+        if (O < 0)
+            return or_fail(err, errlen, "resolved output size is negative");
+        g->L[a] = L;
+        g->K[a] = K;
+        g->s[a] = s;
+        g->d[a] = d;
+        g->b[a] = b;
+        g->e[a] = e;
+        g->op[a] = op;
+        g->O[a] = O;
+    }
+    return OR_OK;
+}
+
+static int64_t or_prod(const int64_t *v, int n)
+{
+    int64_t p = 1;
+    int a;
+    for (a = 0; a < n; a++)
+        p *= v[a];
+    return p;
+}
+
+/* Row-major decode of a flat index into per-axis coordinates (last axis fastest). */
+static void or_decode(int64_t flat, const int64_t *dims, int n, int64_t *coord)
+{
+    int a;
+    for (a = n - 1; a >= 0; a--) {
+        coord[a] = flat % dims[a];
+        flat /= dims[a];
+    }
+}
+
+/* Resolved shape of Y = (N, M, O1..On) and the begin/end pads actually applied. */
+int oracle_output_shape(int nsp, const int64_t *x_shape, const int64_t *w_shape, int auto_pad,
+                        const int64_t *strides, const int64_t *dilations, const int64_t *pads,
+                        const int64_t *output_padding, const int64_t *output_shape,
+                        const int64_t *kernel_shape, int64_t group, int64_t *y_shape,
+                        int64_t *pads_out, char *err, int errlen)
+{
+    or_geom g;
+    int a, rc;
+    rc = or_resolve(nsp, x_shape, w_shape, auto_pad, strides, dilations, pads, output_padding,
+                    output_shape, kernel_shape, group, &g, err, errlen);
+    if (rc != OR_OK)
+        return rc;
+    y_shape[0] = g.N;
+    y_shape[1] = g.M;
+    for (a = 0; a < nsp; a++) {
+        y_shape[2 + a] = g.O[a];
+        if (pads_out) {
+            pads_out[a] = g.b[a];
+            pads_out[a + nsp] = g.e[a];
+        }
+    }
+    return OR_OK;
+}
+
+/* Useful multiply-accumulates: (input sample, tap) pairs that land inside Y, times
+ * N * Cg * M.  Counted by enumeration of every (i, k) pair on each axis. */
+int oracle_useful_macs(int nsp, const int64_t *x_shape, const int64_t *w_shape, int auto_pad,
+                       const int64_t *strides, const int64_t *dilations, const int64_t *pads,
+                       const int64_t *output_padding, const int64_t *output_shape,
+                       const int64_t *kernel_shape, int64_t group, double *macs_out,
+                       char *err, int errlen)
+{
+    or_geom g;
+    int a, rc;
+    double total;
+    rc = or_resolve(nsp, x_shape, w_shape, auto_pad, strides, dilations, pads, output_padding,
+                    output_shape, kernel_shape, group, &g, err, errlen);
+    if (rc != OR_OK)
+        return rc;
+    total = (double)g.N * (double)g.Cg * (double)g.M;
+    for (a = 0; a < nsp; a++) {
+        int64_t i, k, hits = 0;
+        for (i = 0; i < g.L[a]; i++)
+            for (k = 0; k < g.K[a]; k++) {
+                int64_t o = i * g.s[a] - g.b[a] + k * g.d[a];
+                if (o >= 0 && o < g.O[a])
+                    hits++;
+            }
+        total *= (double)hits;
+    }
+    *macs_out = total;
+    return OR_OK;
+}
+
+/* Whole output by the scatter definition.  y has N*M*prod(O) doubles (NCHW order).
+ * Threads split the (n, m) output planes, which are written by one thread each; the
+ * sum inside a plane runs c, then input index i, then tap k, all ascending, so the
+ * result does not depend on the thread count. */
+int oracle_convtranspose_f64(int nsp, const int64_t *x_shape, const double *x,
+                             const int64_t *w_shape, const double *w, const double *bias,
+                             int auto_pad, const int64_t *strides, const int64_t *dilations,
+                             const int64_t *pads, const int64_t *output_padding,
+                             const int64_t *output_shape, const int64_t *kernel_shape,
+                             int64_t group, double *y, int64_t y_len, char *err, int errlen)
+{
+    or_geom g;
+    int rc;
+    int64_t in_plane, out_plane, taps, t, plane;
+    int64_t *tap_coord;
+    rc = or_resolve(nsp, x_shape, w_shape, auto_pad, strides, dilations, pads, output_padding,
+                    output_shape, kernel_shape, group, &g, err, errlen);
+    if (rc != OR_OK)
+        return rc;
+    in_plane = or_prod(g.L, nsp);
+    out_plane = or_prod(g.O, nsp);
+    taps = or_prod(g.K, nsp);
+    if (y_len != g.N * g.M * out_plane)
+        return or_fail(err, errlen, "y buffer length does not match the resolved output");
+    if (g.N * g.M * out_plane == 0)
+        return OR_OK;
+
+    tap_coord = (int64_t *)malloc(sizeof(int64_t) * 3 * (size_t)(taps > 0 ? taps : 1));
+    if (!tap_coord)
+        return or_fail(err, errlen, "out of host memory");
+    for (t = 0; t < taps; t++)
+        or_decode(t, g.K, nsp, tap_coord + 3 * t);
+
+#pragma omp parallel for schedule(dynamic, 1)
+    for (plane = 0; plane < g.N * g.M; plane++) {
+        int64_t n = plane / g.M, m = plane % g.M;
+        int64_t grp = m / g.Mg, mm = m % g.Mg;
+        double *yp = y + plane * out_plane;
+        int64_t p, cc, ii, kk;
+        int a;
+        for (p = 0; p < out_plane; p++)
+            yp[p] = bias ? bias[m] : 0.0;
+        for (cc = 0; cc < g.Cg; cc++) {
+            int64_t c = grp * g.Cg + cc;
+            const double *xp = x + (n * g.C + c) * in_plane;
+            const double *wp = w + (c * g.Mg + mm) * taps;
+            for (ii = 0; ii < in_plane; ii++) {
+                int64_t icoord[3];
+                double xv = xp[ii];
+                or_decode(ii, g.L, nsp, icoord);
+                for (kk = 0; kk < taps; kk++) {
+                    const int64_t *kc = tap_coord + 3 * kk;
+                    int64_t flat = 0;
+                    int inside = 1;
+                    for (a = 0; a < nsp; a++) {
+                        int64_t o = icoord[a] * g.s[a] - g.b[a] + kc[a] * g.d[a];
+                        if (o < 0 || o >= g.O[a]) {
+                            inside = 0;
+                            break;
+                        }
+                        flat = flat * g.O[a] + o;
+                    }
+                    if (inside)
+                        yp[flat] += xv * wp[kk];
+                }
+            }
+        }
+    }
+    free(tap_coord);
+    return OR_OK;
+}
+
+/* Selected outputs by the same definition: for each requested output position the sum
+ * runs over exactly the (c, i, k) whose scatter target is that position, in the same
+ * order as above (c, then i, then k), so each value equals the full routine's.
+ * points holds npts rows of (n, m, o1..on). */
+int oracle_convtranspose_at(int nsp, const int64_t *x_shape, const double *x,
+                            const int64_t *w_shape, const double *w, const double *bias,
+                            int auto_pad, const int64_t *strides, const int64_t *dilations,
+                            const int64_t *pads, const int64_t *output_padding,
+                            const int64_t *output_shape, const int64_t *kernel_shape,
+                            int64_t group, const int64_t *points, int64_t npts, double *out,
+                            char *err, int errlen)
+{
+    or_geom g;
+    int rc;
+    int64_t in_plane, taps, q;
+    int bad = 0;
+    rc = or_resolve(nsp, x_shape, w_shape, auto_pad, strides, dilations, pads, output_padding,
+                    output_shape, kernel_shape, group, &g, err, errlen);
+    if (rc != OR_OK)
+        return rc;
+    in_plane = or_prod(g.L, nsp);
+    taps = or_prod(g.K, nsp);
+
+#pragma omp parallel for schedule(dynamic, 16)
+    for (q = 0; q < npts; q++) {
+        const int64_t *pt = points + q * (nsp + 2);
+        int64_t n = pt[0], m = pt[1];
+        int64_t grp, mm, cc;
+        /* per axis: the input coordinates i and taps k with i*s - b + k*d == o */
+        int64_t pi[3][64], pk[3][64], np_[3];
+        int a, ok = 1;
+        double acc;
+        if (n < 0 || n >= g.N || m < 0 || m >= g.M)
+            ok = 0;
+        for (a = 0; ok && a < nsp; a++) {
+            int64_t o = pt[2 + a], i, k;
+            if (o < 0 || o >= g.O[a]) {
+                ok = 0;
+                break;
+            }
+            np_[a] = 0;
+            for (i = 0; i < g.L[a]; i++)
+                for (k = 0; k < g.K[a]; k++)
+                    if (i * g.s[a] - g.b[a] + k * g.d[a] == o) {
+                        if (np_[a] >= 64) {
+                            ok = 0;
+                            break;
+                        }
+                        pi[a][np_[a]] = i;
+                        pk[a][np_[a]] = k;
+                        np_[a]++;
+                    }
+        }
+        if (!ok) {
+#pragma omp atomic write
+            bad = 1;
+            out[q] = 0.0;
+            continue;
+        }
+        grp = m / g.Mg;
+        mm = m % g.Mg;
+        acc = bias ? bias[m] : 0.0;
+        for (cc = 0; cc < g.Cg; cc++) {
+            int64_t c = grp * g.Cg + cc;
+            const double *xp = x + (n * g.C + c) * in_plane;
+            const double *wp = w + (c * g.Mg + mm) * taps;
+            int64_t sel[3] = {0, 0, 0};
+            int empty = 0;
+            for (a = 0; a < nsp; a++)
+                if (np_[a] == 0)
+                    empty = 1;
+            /* lexicographic walk over the per-axis pair lists = ascending i */
+            while (!empty) {
+                int64_t iflat = 0, kflat = 0;
+                for (a = 0; a < nsp; a++) {
+                    iflat = iflat * g.L[a] + pi[a][sel[a]];
+                    kflat = kflat * g.K[a] + pk[a][sel[a]];
+                }
+                acc += xp[iflat] * wp[kflat];
+                for (a = nsp - 1; a >= 0; a--) {
+                    if (++sel[a] < np_[a])
+                        break;
+                    sel[a] = 0;
+                }
+                if (a < 0)
+                    break;
+            }
+        }
+        out[q] = acc;
+    }
+    if (bad)
+        return or_fail(err, errlen, "a requested point lies outside Y (or has > 64 taps per axis)");
+    return OR_OK;
+}

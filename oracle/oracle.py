@@ -1,0 +1,172 @@
+"""Python face of the fp64 ConvTranspose oracle (``ct_oracle.c``).
+
+TEST INFRASTRUCTURE ONLY: only ``tests/``, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` may import this module.  It shares nothing with
+the HIP library and imports nothing from it.
+
+The arithmetic lives in ``ct_oracle.c`` (the scatter definition of the transposed
+convolution from the webgpu-kernels "ai.onnx.ConvTranspose" README, sections
+Description, Inputs, Attributes and Outputs).  This file only builds that library,
+widens inputs exactly to fp64 and passes pointers.  Inputs are in the logical
+(N, C, D1..Dn) layout; callers holding channels-last data permute first.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+from typing import Optional, Sequence
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "ct_oracle.c")
+_LIB = os.path.join(_HERE, "libctoracle.so")
+AUTO_PAD = {"NOTSET": 0, "SAME_UPPER": 1, "SAME_LOWER": 2, "VALID": 3}
+_lib = None
+
+
+class OracleError(ValueError):
+    """The oracle rejected the attributes or shapes."""
+
+
+def build(src: str = _SRC, out: str = _LIB) -> str:
+    """Compile the oracle with gcc (OpenMP, -O2, no fast-math)."""
+    cmd = ["gcc", "-O2", "-std=c99", "-fopenmp", "-shared", "-fPIC", src, "-o", out]
+    subprocess.run(cmd, check=True)
+    return out
+
+
+def load(path: Optional[str] = None):
+    """Load (building first if needed) the oracle shared library."""
+    global _lib
+    if path is None and _lib is not None:
+        return _lib
+    p = path or _LIB
+    if path is None and (not os.path.exists(p) or os.path.getmtime(p) < os.path.getmtime(_SRC)):
+        build()
+    lib = ctypes.CDLL(p)
+    i64p = ctypes.POINTER(ctypes.c_int64)
+    f64p = ctypes.POINTER(ctypes.c_double)
+    attrs = [ctypes.c_int, i64p, i64p, i64p, i64p, i64p, i64p, ctypes.c_int64]
+    lib.oracle_output_shape.argtypes = [ctypes.c_int, i64p, i64p] + attrs + [
+        i64p, i64p, ctypes.c_char_p, ctypes.c_int]
+    lib.oracle_useful_macs.argtypes = [ctypes.c_int, i64p, i64p] + attrs + [
+        f64p, ctypes.c_char_p, ctypes.c_int]
+    lib.oracle_convtranspose_f64.argtypes = [ctypes.c_int, i64p, f64p, i64p, f64p, f64p] + attrs + [
+        f64p, ctypes.c_int64, ctypes.c_char_p, ctypes.c_int]
+    lib.oracle_convtranspose_at.argtypes = [ctypes.c_int, i64p, f64p, i64p, f64p, f64p] + attrs + [
+        i64p, ctypes.c_int64, f64p, ctypes.c_char_p, ctypes.c_int]
+    for fn in ("oracle_output_shape", "oracle_useful_macs", "oracle_convtranspose_f64",
+               "oracle_convtranspose_at"):
+        getattr(lib, fn).restype = ctypes.c_int
+    if path is None:
+        _lib = lib
+    return lib
+
+
+def _i64(v: Optional[Sequence[int]]):
+    if v is None:
+        return None, None
+    a = np.ascontiguousarray(np.asarray(v, dtype=np.int64))
+    return a, a.ctypes.data_as(ctypes.POINTER(ctypes.c_int64))
+
+
+def _f64(a: Optional[np.ndarray]):
+    if a is None:
+        return None, None
+    a = np.ascontiguousarray(np.asarray(a).astype(np.float64))  # exact widening of f16/f32
+    return a, a.ctypes.data_as(ctypes.POINTER(ctypes.c_double))
+
+
+def _attr_args(auto_pad="NOTSET", strides=None, dilations=None, pads=None, output_padding=None,
+               output_shape=None, kernel_shape=None, group=1):
+    keep = []
+    out = [AUTO_PAD[auto_pad]]
+    for v in (strides, dilations, pads, output_padding, output_shape, kernel_shape):
+        arr, ptr = _i64(v)
+        keep.append(arr)
+        out.append(ptr)
+    out.append(int(group))
+    return out, keep
+
+
+def _check(rc: int, err) -> None:
+    if rc != 0:
+        raise OracleError(err.value.decode(errors="replace"))
+
+
+def output_shape(x_shape, w_shape, lib=None, **attrs):
+    """Resolved Y shape (N, M, O1..On) and the applied pads [b1..bn, e1..en]."""
+    lib = lib or load()
+    nsp = len(x_shape) - 2
+    if len(w_shape) != len(x_shape):
+        raise OracleError("W must have the same rank as X")
+    xs, xp = _i64(x_shape)
+    ws, wp = _i64(w_shape)
+    args, keep = _attr_args(**attrs)
+    ys = np.zeros(nsp + 2, dtype=np.int64)
+    pd = np.zeros(2 * nsp, dtype=np.int64)
+    err = ctypes.create_string_buffer(256)
+    rc = lib.oracle_output_shape(nsp, xp, wp, *args,
+                                 ys.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)),
+                                 pd.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)), err, 256)
+    _check(rc, err)
+    return tuple(int(v) for v in ys), [int(v) for v in pd]
+
+
+def useful_macs(x_shape, w_shape, lib=None, **attrs) -> int:
+    """(input sample, tap) pairs landing inside Y, times N * C/group * M."""
+    lib = lib or load()
+    nsp = len(x_shape) - 2
+    xs, xp = _i64(x_shape)
+    ws, wp = _i64(w_shape)
+    args, keep = _attr_args(**attrs)
+    out = ctypes.c_double(0)
+    err = ctypes.create_string_buffer(256)
+    rc = lib.oracle_useful_macs(nsp, xp, wp, *args, ctypes.byref(out), err, 256)
+    _check(rc, err)
+    return int(out.value)
+
+
+def convtranspose(x: np.ndarray, w: np.ndarray, bias: Optional[np.ndarray] = None, lib=None,
+                  **attrs) -> np.ndarray:
+    """Whole Y in fp64 by the scatter definition (logical NC.. layout)."""
+    lib = lib or load()
+    x64, xp = _f64(x)
+    w64, wp = _f64(w)
+    b64, bp = _f64(bias)
+    yshape, _ = output_shape(x64.shape, w64.shape, lib=lib, **attrs)
+    if b64 is not None and b64.shape != (yshape[1],):
+        raise OracleError("bias must be 1-D of length M")
+    y = np.zeros(yshape, dtype=np.float64)
+    args, keep = _attr_args(**attrs)
+    xs, xsp = _i64(x64.shape)
+    ws, wsp = _i64(w64.shape)
+    err = ctypes.create_string_buffer(256)
+    rc = lib.oracle_convtranspose_f64(x64.ndim - 2, xsp, xp, wsp, wp, bp, *args,
+                                      y.ctypes.data_as(ctypes.POINTER(ctypes.c_double)),
+                                      y.size, err, 256)
+    _check(rc, err)
+    return y
+
+
+def convtranspose_at(x: np.ndarray, w: np.ndarray, bias: Optional[np.ndarray], points: np.ndarray,
+                     lib=None, **attrs) -> np.ndarray:
+    """Y at the given output positions (rows of (n, m, o1..on)), fp64."""
+    lib = lib or load()
+    x64, xp = _f64(x)
+    w64, wp = _f64(w)
+    b64, bp = _f64(bias)
+    pts = np.ascontiguousarray(np.asarray(points, dtype=np.int64))
+    out = np.zeros(len(pts), dtype=np.float64)
+    args, keep = _attr_args(**attrs)
+    xs, xsp = _i64(x64.shape)
+    ws, wsp = _i64(w64.shape)
+    err = ctypes.create_string_buffer(256)
+    rc = lib.oracle_convtranspose_at(x64.ndim - 2, xsp, xp, wsp, wp, bp, *args,
+                                     pts.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)),
+                                     len(pts), out.ctypes.data_as(ctypes.POINTER(ctypes.c_double)),
+                                     err, 256)
+    _check(rc, err)
+    return out

@@ -1,0 +1,65 @@
+"""Planted mistakes in copies of the oracle: each one must make some pin fail.
+
+Every mutant is a textual edit of ct_oracle.c compiled into a temporary library and
+checked in a subprocess, so the oracle source itself carries no mutation hooks.  Each
+edit keeps every memory access in bounds."""
+import concurrent.futures as cf
+import os
+import subprocess
+import sys
+import tempfile
+
+import pytest
+
+from oracle import oracle as O
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+
+MUTANTS = {
+    "begin_pad_sign": ("* g.s[a] - g.b[a] + kc[a] * g.d[a];", "* g.s[a] + g.b[a] + kc[a] * g.d[a];"),
+    "end_pad_for_begin": ("* g.s[a] - g.b[a] + kc[a] * g.d[a];", "* g.s[a] - g.e[a] + kc[a] * g.d[a];"),
+    "stride_dilation_swapped": ("icoord[a] * g.s[a] - g.b[a] + kc[a] * g.d[a];",
+                                "icoord[a] * g.d[a] - g.b[a] + kc[a] * g.s[a];"),
+    "dilation_ignored": ("+ kc[a] * g.d[a];", "+ kc[a];"),
+    "weight_read_as_M_C": ("w + (c * g.Mg + mm) * taps", "w + (mm * g.C + c) * taps"),
+    "taps_reversed": ("yp[flat] += xv * wp[kk];", "yp[flat] += xv * wp[taps - 1 - kk];"),
+    "bias_dropped": ("bias ? bias[m] : 0.0", "0.0"),
+    "output_padding_dropped": ("full = s * (L - 1) + op + d * (K - 1) + 1;",
+                               "full = s * (L - 1) + d * (K - 1) + 1;"),
+    "footprint_off_by_one": ("full = s * (L - 1) + op + d * (K - 1) + 1;",
+                             "full = s * (L - 1) + op + d * (K - 1);"),
+    "same_sides_swapped": ("            if (auto_pad == OR_SAME_UPPER) {",
+                           "            if (auto_pad == OR_SAME_LOWER) {"),
+    "same_split_floor": ("            if (auto_pad == OR_SAME_UPPER) {\n                b = tot / 2;",
+                         "            if (auto_pad == OR_SAME_UPPER) {\n                b = tot >= 0 ? tot / 2 : (tot - 1) / 2;"),
+    "output_shape_extra_at_begin": ("} else if (auto_pad == OR_SAME_LOWER) {",
+                                    "} else if (auto_pad != OR_SAME_LOWER) {"),
+    "group_of_out_channel": ("int64_t grp = m / g.Mg, mm = m % g.Mg;",
+                             "int64_t grp = m % g.group, mm = m / g.group;"),
+    "group_channels_interleaved": ("int64_t c = grp * g.Cg + cc;", "int64_t c = cc * g.group + grp;"),
+    "points_pad_sign": ("if (i * g.s[a] - g.b[a] + k * g.d[a] == o) {",
+                        "if (i * g.s[a] + g.b[a] + k * g.d[a] == o) {"),
+    "useful_macs_upper_bound_inclusive": ("if (o >= 0 && o < g.O[a])\n                    hits++;",
+                                          "if (o >= 0 && o <= g.O[a])\n                    hits++;"),
+}
+
+
+def _run_mutant(name, tmp):
+    old, new = MUTANTS[name]
+    src = open(os.path.join(os.path.dirname(O.__file__), "ct_oracle.c")).read()
+    assert old in src, f"mutant {name}: pattern not found in ct_oracle.c"
+    path_c = os.path.join(tmp, f"{name}.c")
+    path_so = os.path.join(tmp, f"lib{name}.so")
+    open(path_c, "w").write(src.replace(old, new))
+    O.build(path_c, path_so)
+    r = subprocess.run([sys.executable, os.path.join(HERE, "_mutant_runner.py"), path_so],
+                       capture_output=True, text=True, timeout=300)
+    return r.returncode, r.stdout + r.stderr
+
+
+def test_every_planted_mistake_is_caught():
+    with tempfile.TemporaryDirectory() as tmp:
+        with cf.ThreadPoolExecutor(max_workers=6) as ex:
+            res = dict(zip(MUTANTS, ex.map(lambda n: _run_mutant(n, tmp), MUTANTS)))
+    missed = {n: out for n, (rc, out) in res.items() if rc != 0}
+    assert not missed, f"mutants not caught by any pin: {missed}"
