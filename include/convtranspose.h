@@ -1,0 +1,162 @@
+/*
+ * convtranspose.h -- C ABI of libconvtranspose.so, an N-D transposed convolution
+ * (ONNX ConvTranspose) for AMD Instinct MI355X (gfx950).
+ *
+ * Operation (webgpu-kernels "ai.onnx.ConvTranspose" README, sections Description,
+ * Inputs, Outputs, Attributes and Type constraints; ClikaRT "conv_transpose" API page,
+ * description):
+ *   X is (N, C, D1..Dn), W is (C, M/group, k1..kn), optional bias has length M, and
+ *   Y is (N, M, O1..On).  Every input sample X[n,c,i] is sent through every filter
+ *   tap k of its group to output position o_a = i_a*s_a - b_a + k_a*d_a on each
+ *   spatial axis a (s = stride, d = dilation, b = begin pad), and summed there when
+ *   the position lies inside Y; Y starts at bias[m].  Out channel m belongs to group
+ *   m / (M/group) and reads input channels c of that group through W[c, m % (M/group), k].
+ *   Output size per axis: O = s*(L-1) + output_padding + d*(K-1) + 1 - b - e.
+ *   Element type T is float32 or float16 for X, W, bias and Y alike; float16 inputs
+ *   are accumulated in float32 and rounded once (to nearest even) into Y.
+ *
+ * Attribute pointers: a NULL attribute pointer means "absent" and its ONNX default
+ * applies (strides 1, dilations 1, pads 0, output_padding 0; output_shape and
+ * kernel_shape not given).  Per-axis arrays have nsp entries, pads has 2*nsp
+ * (all begins, then all ends).  Readings where the pages leave a rule open:
+ *   - 0 <= output_padding < max(stride, dilation); strides, dilations >= 1; pads >= 0;
+ *   - pads together with an auto_pad other than NOTSET are rejected;
+ *   - SAME_UPPER / SAME_LOWER give O = L*stride; the total pad
+ *     tot = s*(L-1) + op + d*(K-1) + 1 - O is halved with truncation toward zero and
+ *     the odd remainder goes to the end (UPPER) or the beginning (LOWER);
+ *   - output_shape, when given, sets O and its total pad is split the same way (odd
+ *     part at the beginning only for SAME_LOWER); explicit pads given with it must
+ *     sum to that total;
+ *   - kernel_shape, when given, must equal W's spatial dims.
+ *
+ * Shapes are always passed in logical ONNX order.  Buffers are owned by the caller,
+ * must be dense in the stated layout and aligned to the element size; the library
+ * keeps no pointer after a call returns and allocates no device memory.
+ *
+ * Thread safety: every call is re-entrant; the error text is per host thread.
+ */
+#ifndef CONVTRANSPOSE_H
+#define CONVTRANSPOSE_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    CT_OK = 0,
+    CT_EINVAL = 1,        /* bad attribute, shape arithmetic, pointer or alignment      */
+    CT_ESHAPE = 2,        /* y_shape differs from the resolved output shape             */
+    CT_EUNSUPPORTED = 3,  /* dtype not served, or a forced kernel cannot serve the call */
+    CT_EDEVICE = 4        /* the HIP runtime reported an error at launch                */
+} ct_status;
+
+typedef enum { CT_FLOAT32 = 0, CT_FLOAT16 = 1 } ct_dtype;
+
+typedef enum { CT_NOTSET = 0, CT_SAME_UPPER = 1, CT_SAME_LOWER = 2, CT_VALID = 3 } ct_auto_pad;
+
+/* Kernel families (for convtranspose_nd_with_kernel and convtranspose_select_kernel). */
+typedef enum {
+    CT_KERNEL_AUTO = 0,     /* let the shape-based dispatcher choose                     */
+    CT_KERNEL_DIRECT = 1,   /* generic gather, any rank/attributes/layout/dtype          */
+    CT_KERNEL_GROUPED = 2,  /* grouped/depthwise bandwidth kernel (small C/g and M/g)    */
+    CT_KERNEL_IGEMM = 3,    /* stride-phase implicit GEMM on MFMA (float16)              */
+    CT_KERNEL_NONE = 4      /* nothing to launch: Y is empty                             */
+} ct_kernel;
+
+/*
+ * Resolve the output shape (README Attributes table and Outputs section).  Host only;
+ * touches no device.
+ *   nsp            spatial rank n, 1..3
+ *   x_shape        n+2 entries {N, C, D1..Dn}
+ *   w_shape        n+2 entries {C, M/group, k1..kn}
+ *   y_shape_out    receives n+2 entries {N, M, O1..On}
+ *   pads_out       optional (may be NULL): receives the 2n begin/end pads applied
+ *                  (these may be negative when derived from auto_pad/output_shape)
+ * Returns CT_OK, or CT_EINVAL with convtranspose_last_error() describing the problem.
+ */
+ct_status convtranspose_output_shape(int nsp, const int64_t *x_shape, const int64_t *w_shape,
+                                     ct_auto_pad auto_pad, const int64_t *strides,
+                                     const int64_t *dilations, const int64_t *pads,
+                                     const int64_t *output_padding, const int64_t *output_shape,
+                                     const int64_t *kernel_shape, int64_t group,
+                                     int64_t *y_shape_out, int64_t *pads_out);
+
+/*
+ * Number of useful multiply-accumulates of the call: the (input sample, tap) pairs
+ * whose target lies inside Y, per spatial axis, multiplied over axes and by
+ * N * (C/group) * M.  Zero-insertion holes and taps cropped by pads are not counted.
+ * Host only.  Returns CT_OK or CT_EINVAL.
+ */
+ct_status convtranspose_useful_macs(int nsp, const int64_t *x_shape, const int64_t *w_shape,
+                                    ct_auto_pad auto_pad, const int64_t *strides,
+                                    const int64_t *dilations, const int64_t *pads,
+                                    const int64_t *output_padding, const int64_t *output_shape,
+                                    const int64_t *kernel_shape, int64_t group, double *macs_out);
+
+/*
+ * The transposed convolution, enqueued on a HIP stream (README Description/Inputs/
+ * Outputs/Attributes; channels-last input and output as on the ClikaRT page).
+ *   dtype          CT_FLOAT32 or CT_FLOAT16: the element type of x, w, bias and y
+ *   nsp            spatial rank, 1..3
+ *   channels_last  0: x is stored (N, C, D1..Dn) and y (N, M, O1..On), both dense
+ *                  1: x is stored (N, D1..Dn, C) and y (N, O1..On, M), both dense
+ *                  (W keeps the ONNX layout (C, M/group, k1..kn) either way)
+ *   x, w, y        device pointers (caller-owned; y must not overlap x, w or bias)
+ *   bias           device pointer to M elements, or NULL for no bias
+ *   x_shape, w_shape, y_shape   logical shapes, n+2 entries each; y_shape must equal
+ *                  the resolved output shape, else CT_ESHAPE
+ *   auto_pad ... group          ONNX attributes as for convtranspose_output_shape
+ *   stream         hipStream_t to enqueue on (NULL: the null stream)
+ * All validation happens before anything is enqueued: on any error nothing is launched
+ * and y is untouched.  Work is asynchronous: the call returns once the kernels are
+ * enqueued.  An empty y (some dimension 0) returns CT_OK with no launch.
+ */
+ct_status convtranspose_nd(ct_dtype dtype, int nsp, int channels_last, const void *x,
+                           const int64_t *x_shape, const void *w, const int64_t *w_shape,
+                           const void *bias, void *y, const int64_t *y_shape,
+                           ct_auto_pad auto_pad, const int64_t *strides, const int64_t *dilations,
+                           const int64_t *pads, const int64_t *output_padding,
+                           const int64_t *output_shape, const int64_t *kernel_shape,
+                           int64_t group, void *stream);
+
+/*
+ * As convtranspose_nd, with the kernel family forced (CT_KERNEL_AUTO = dispatcher's
+ * choice).  Returns CT_EUNSUPPORTED, launching nothing, when the forced family cannot
+ * serve the call (e.g. CT_KERNEL_IGEMM for float32 or for shapes its tiling excludes).
+ */
+ct_status convtranspose_nd_with_kernel(ct_kernel kernel, ct_dtype dtype, int nsp, int channels_last,
+                                       const void *x, const int64_t *x_shape, const void *w,
+                                       const int64_t *w_shape, const void *bias, void *y,
+                                       const int64_t *y_shape, ct_auto_pad auto_pad,
+                                       const int64_t *strides, const int64_t *dilations,
+                                       const int64_t *pads, const int64_t *output_padding,
+                                       const int64_t *output_shape, const int64_t *kernel_shape,
+                                       int64_t group, void *stream);
+
+/*
+ * The kernel family the dispatcher picks for these arguments (pointers are inspected
+ * for alignment only, never dereferenced).  Host only.  Returns a ct_kernel value, or
+ * -1 when the arguments are invalid (see convtranspose_last_error()).
+ */
+int convtranspose_select_kernel(ct_dtype dtype, int nsp, int channels_last, const void *x,
+                                const int64_t *x_shape, const void *w, const int64_t *w_shape,
+                                const void *bias, const void *y, ct_auto_pad auto_pad,
+                                const int64_t *strides, const int64_t *dilations,
+                                const int64_t *pads, const int64_t *output_padding,
+                                const int64_t *output_shape, const int64_t *kernel_shape,
+                                int64_t group);
+
+/* Text of the last error on the calling host thread ("" after a successful call).
+ * The pointer stays valid until the next library call on that thread. */
+const char *convtranspose_last_error(void);
+
+/* Short name of a ct_kernel value ("direct", "grouped", "igemm", ...). */
+const char *convtranspose_kernel_name(int kernel);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* CONVTRANSPOSE_H */

@@ -1,0 +1,233 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 oracle.
+
+Tolerances: |y - ref| <= tol * (1 + |ref|) elementwise with tol = 1e-5 for float32 and
+2e-3 for float16 inputs (float32 accumulation).  Small-integer-valued inputs must give
+exactly the oracle's value rounded once to the element type.  Full-size benchmark
+shapes are checked on seeded sampled outputs (plus every corner); reduced shapes with
+the same attributes, ragged sizes and several tiles are checked on every output."""
+import zlib
+
+import numpy as np
+import pytest
+import torch
+
+import pins
+import workloads as W
+from oracle import oracle as O
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"f32": 1e-5, "f16": 2e-3}
+NPT = {"f32": np.float32, "f16": np.float16}
+FAMILIES = ["auto", "direct", "grouped", "igemm"]
+
+
+@pytest.fixture(scope="module")
+def T():
+    assert torch.cuda.is_available(), "GPU tests need a HIP device"
+    import transposed_convolution_amd as T
+    T.load_library()
+    return T
+
+
+def gpu_run(T, x, w, b, attrs, cl=False, kernel="auto"):
+    """Run on the GPU; returns the logical-layout result as float64, or None when the
+    forced kernel family does not serve this problem."""
+    dev = torch.device("cuda:0")
+    tx = torch.from_numpy(np.ascontiguousarray(x)).to(dev)
+    if cl:
+        tx = T.to_channels_last(tx)
+    tw = torch.from_numpy(np.ascontiguousarray(w)).to(dev)
+    tb = None if b is None else torch.from_numpy(b).to(dev)
+    try:
+        y = T.convtranspose_nd(tx, tw, tb, channels_last=cl, kernel=kernel, **attrs)
+    except T.ConvTransposeError as e:
+        if e.status == 3 and kernel not in ("auto", "direct"):
+            return None
+        raise
+    torch.cuda.synchronize()
+    return y.cpu().numpy().astype(np.float64)
+
+
+def check(got, ref, dtype, integer, what=""):
+    assert got.shape == ref.shape, (what, got.shape, ref.shape)
+    if integer:
+        want = ref.astype(NPT[dtype]).astype(np.float64)
+        bad = np.flatnonzero(got != want)
+        assert bad.size == 0, f"{what}: {bad.size} mismatches, first at {np.unravel_index(bad[0], got.shape)}: " \
+                              f"{got.flat[bad[0]]} vs {want.flat[bad[0]]}"
+    else:
+        if got.size == 0:
+            return
+        err = np.abs(got - ref) / (1.0 + np.abs(ref))
+        i = int(np.argmax(err))
+        assert err.flat[i] <= TOL[dtype], \
+            f"{what}: max rel err {err.flat[i]:.3e} at {np.unravel_index(i, got.shape)}: {got.flat[i]} vs {ref.flat[i]}"
+
+
+def _log(msg):
+    print(msg, flush=True)
+
+
+# --------------------------------------------------------------------------------------
+# benchmark configurations
+# --------------------------------------------------------------------------------------
+WHOLE = [W.C1, W.C2, W.C3]
+SAMPLED = [W.C4, W.C4_NHWC, W.C5_S1, W.C5_S1_P1, W.C5_S2]
+
+
+@pytest.mark.parametrize("integer", [False, True], ids=["float", "int"])
+@pytest.mark.parametrize("kernel", FAMILIES)
+@pytest.mark.parametrize("wl", WHOLE, ids=lambda w: w.name)
+def test_config_whole_output(T, wl, kernel, integer):
+    _log(f"[case] whole {wl.name} kernel={kernel} integer={integer}")
+    x, w, b = W.make_inputs(wl, integer=integer)
+    got = gpu_run(T, x, w, b, wl.attrs, wl.channels_last, kernel)
+    if got is None:
+        pytest.skip(f"{kernel} does not serve {wl.name}")
+    ref = O.convtranspose(x, w, b, **wl.attrs)
+    check(got, ref, wl.dtype, integer, wl.name)
+
+
+@pytest.mark.parametrize("integer", [False, True], ids=["float", "int"])
+@pytest.mark.parametrize("wl", SAMPLED, ids=lambda w: w.name)
+def test_config_sampled_outputs(T, wl, integer):
+    """Full benchmark size in the dispatcher's own launch configuration."""
+    _log(f"[case] sampled {wl.name} integer={integer}")
+    x, w, b = W.make_inputs(wl, integer=integer)
+    got = gpu_run(T, x, w, b, wl.attrs, wl.channels_last, "auto")
+    pts = W.make_points(got.shape, 3000, seed=wl.seed + 7)
+    ref = O.convtranspose_at(x, w, b, pts, **wl.attrs)
+    check(got[tuple(pts.T)], ref, wl.dtype, integer, wl.name)
+    assert np.all(np.isfinite(got))
+
+
+def reduced(wl, x_shape, w_shape, **kw):
+    return wl.with_(name=wl.name + "_reduced", x_shape=x_shape, w_shape=w_shape, **kw)
+
+
+REDUCED = [
+    reduced(W.C3, (3, 40, 29, 37), (40, 1, 4, 4), attrs=dict(W.C3.attrs, group=40)),
+    reduced(W.C3, (2, 24, 13, 70), (24, 2, 4, 4), attrs=dict(W.C3.attrs, group=12)),
+    reduced(W.C4, (2, 64, 20, 36), (64, 48, 4, 4)),
+    reduced(W.C4, (3, 40, 11, 70), (40, 72, 4, 4)),
+    reduced(W.C4_NHWC, (2, 64, 20, 36), (64, 48, 4, 4)),
+    reduced(W.C4_NHWC, (1, 136, 9, 17), (136, 24, 4, 4)),
+    reduced(W.C5_S1, (1, 32, 5, 9, 11), (32, 24, 3, 3, 3)),
+    reduced(W.C5_S1_P1, (2, 48, 4, 7, 10), (48, 40, 3, 3, 3)),
+    reduced(W.C5_S2, (1, 32, 5, 9, 11), (32, 24, 3, 3, 3)),
+    reduced(W.C5_S2.with_(channels_last=True), (2, 40, 3, 6, 9), (40, 16, 3, 3, 3)),
+    reduced(W.C2, (3, 24, 77), (24, 40, 5)),
+]
+
+
+@pytest.mark.parametrize("integer", [False, True], ids=["float", "int"])
+@pytest.mark.parametrize("kernel", FAMILIES)
+@pytest.mark.parametrize("wl", REDUCED, ids=lambda w: f"{w.name}_{w.x_shape}_{'cl' if w.channels_last else 'nc'}")
+def test_reduced_whole_output(T, wl, kernel, integer):
+    _log(f"[case] reduced {wl.name} {wl.x_shape} kernel={kernel} integer={integer}")
+    x, w, b = W.make_inputs(wl, integer=integer)
+    got = gpu_run(T, x, w, b, wl.attrs, wl.channels_last, kernel)
+    if got is None:
+        pytest.skip(f"{kernel} does not serve this shape")
+    ref = O.convtranspose(x, w, b, **wl.attrs)
+    check(got, ref, wl.dtype, integer, f"{wl.name}{wl.x_shape}")
+
+
+# --------------------------------------------------------------------------------------
+# random small problems and edge cases
+# --------------------------------------------------------------------------------------
+@pytest.mark.parametrize("cl", [False, True], ids=["nc", "cl"])
+@pytest.mark.parametrize("dtype", ["f32", "f16"])
+@pytest.mark.parametrize("kernel", FAMILIES)
+def test_random_small_problems(T, kernel, dtype, cl):
+    rng = np.random.default_rng(1000 + FAMILIES.index(kernel) * 10 + (dtype == "f16") * 2 + cl)
+    ran = 0
+    for t in range(50):
+        x, w, b, attrs = pins.random_case(rng, auto=(t % 4 == 3), max_L=9)
+        x, w = x.astype(NPT[dtype]), w.astype(NPT[dtype])
+        b = None if b is None else b.astype(NPT[dtype])
+        _log(f"[case] random #{t} {kernel} {dtype} cl={cl} x{x.shape} w{w.shape} {attrs}")
+        got = gpu_run(T, x, w, b, attrs, cl, kernel)
+        if got is None:
+            continue
+        ran += 1
+        check(got, O.convtranspose(x, w, b, **attrs), dtype, False, f"random #{t} {attrs}")
+    if kernel in ("auto", "direct"):
+        assert ran == 50
+
+
+EDGE = [
+    # (name, x_shape, w_shape, attrs, bias)
+    ("empty_batch", (0, 8, 5, 5), (8, 4, 3, 3), dict(strides=[2, 2]), True),
+    ("zero_output_width", (1, 4, 5, 1), (4, 4, 3, 2), dict(pads=[0, 0, 1, 1]), True),
+    ("no_input_channels", (2, 0, 4, 4), (0, 3, 3, 3), dict(strides=[2, 2]), True),
+    ("empty_spatial_input", (1, 3, 0, 4), (3, 2, 4, 3), dict(strides=[2, 1]), True),
+    ("kernel_smaller_than_stride", (1, 8, 5, 6), (8, 8, 2, 1), dict(strides=[3, 2]), True),
+    ("large_pads_crop", (1, 8, 9, 9), (8, 8, 5, 5), dict(strides=[2, 2], pads=[4, 3, 2, 5]), True),
+    ("same_upper_negative", (1, 4, 6, 5), (4, 4, 1, 1), dict(strides=[2, 3], auto_pad="SAME_UPPER"), True),
+    ("same_lower_odd", (1, 16, 7, 7), (16, 8, 3, 3), dict(strides=[2, 2], auto_pad="SAME_LOWER"), True),
+    ("output_shape", (1, 16, 7, 7), (16, 8, 4, 4), dict(strides=[2, 2], output_shape=[15, 13]), True),
+    ("pointwise", (2, 64, 6, 7), (64, 32, 1, 1), {}, True),
+    ("pointwise_s2", (2, 64, 6, 7), (64, 32, 1, 1), dict(strides=[2, 2]), False),
+    ("dilated", (1, 32, 8, 8), (32, 16, 3, 3), dict(dilations=[2, 3], strides=[2, 1], output_padding=[1, 2]), True),
+    ("depthwise_3d", (1, 8, 4, 5, 6), (8, 1, 3, 3, 3), dict(strides=[2, 2, 2], group=8), True),
+    ("grouped_mixed", (2, 12, 6, 6), (12, 5, 3, 3), dict(strides=[2, 2], group=3, pads=[1, 0, 0, 1]), True),
+    ("long_1d", (1, 16, 3000), (16, 8, 7), dict(strides=[4], pads=[3, 3], output_padding=[3]), True),
+    ("stride_larger_than_kernel_3d", (1, 16, 3, 4, 5), (16, 16, 2, 2, 2), dict(strides=[3, 3, 3]), True),
+]
+
+
+@pytest.mark.parametrize("cl", [False, True], ids=["nc", "cl"])
+@pytest.mark.parametrize("dtype", ["f32", "f16"])
+@pytest.mark.parametrize("kernel", FAMILIES)
+@pytest.mark.parametrize("case", EDGE, ids=lambda c: c[0])
+def test_edge_cases(T, case, kernel, dtype, cl):
+    name, xs, ws, attrs, has_b = case
+    _log(f"[case] edge {name} {kernel} {dtype} cl={cl}")
+    rng = np.random.default_rng(zlib.crc32(name.encode()))
+    x = rng.integers(-2, 3, size=xs).astype(NPT[dtype])
+    w = rng.integers(-2, 3, size=ws).astype(NPT[dtype])
+    m = ws[1] * attrs.get("group", 1)
+    b = rng.integers(-4, 5, size=m).astype(NPT[dtype]) if has_b else None
+    got = gpu_run(T, x, w, b, attrs, cl, kernel)
+    if got is None:
+        pytest.skip(f"{kernel} does not serve {name}")
+    check(got, O.convtranspose(x, w, b, **attrs), dtype, True, name)
+
+
+def test_repeat_runs_bitwise_identical(T):
+    wl = REDUCED[2]
+    x, w, b = W.make_inputs(wl)
+    a = gpu_run(T, x, w, b, wl.attrs)
+    c = gpu_run(T, x, w, b, wl.attrs)
+    assert np.array_equal(a, c)
+
+
+def test_nondefault_stream_and_out_buffer(T):
+    wl = REDUCED[2]
+    x, w, b = W.make_inputs(wl)
+    dev = torch.device("cuda:0")
+    tx, tw, tb = (torch.from_numpy(v).to(dev) for v in (x, w, b))
+    yshape = T.convtranspose_output_shape(x.shape, w.shape, **wl.attrs)[0]
+    out = torch.full(yshape, 7.0, dtype=tx.dtype, device=dev)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        y = T.convtranspose_nd(tx, tw, tb, out=out, **wl.attrs)
+    s.synchronize()
+    assert y.data_ptr() == out.data_ptr()
+    check(out.cpu().numpy().astype(np.float64), O.convtranspose(x, w, b, **wl.attrs), "f16", False)
+
+
+def test_errors_leave_output_untouched(T):
+    dev = torch.device("cuda:0")
+    x = torch.ones((1, 4, 5, 5), dtype=torch.float16, device=dev)
+    w = torch.ones((4, 3, 3, 3), dtype=torch.float16, device=dev)
+    out = torch.full((1, 3, 7, 7), 3.0, dtype=torch.float16, device=dev)
+    with pytest.raises(T.ConvTransposeError):
+        T.convtranspose_nd(x, w, None, out=out, strides=[2, 2])   # shape mismatch
+    with pytest.raises(T.ConvTransposeError):
+        T.convtranspose_nd(x, w, None, out=out, output_padding=[1, 1])
+    torch.cuda.synchronize()
+    assert bool((out == 3.0).all())

@@ -1,0 +1,160 @@
+"""Host-side checks of libconvtranspose.so that need no GPU: exported symbols, the
+attribute resolver and useful-MAC count against the oracle's independent ones, and
+argument validation (every case here fails validation or has an empty output, so no
+kernel is ever launched)."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import pins
+import workloads as W
+from oracle import oracle as O
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def T():
+    import transposed_convolution_amd as T
+    if not os.path.exists(T.library_path()):
+        from transposed_convolution_amd import build
+        build.build()
+    T.load_library()
+    return T
+
+
+def _declared_functions():
+    names = []
+    for fn in os.listdir(os.path.join(ROOT, "include")):
+        if fn.endswith(".h"):
+            src = open(os.path.join(ROOT, "include", fn)).read()
+            src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+            names += re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(\w+)\s*\(", src, flags=re.M)
+    return sorted(set(names))
+
+
+def test_library_exports_every_declared_symbol(T):
+    names = _declared_functions()
+    assert "convtranspose_nd" in names and len(names) >= 6
+    lib = ctypes.CDLL(T.library_path())
+    missing = [n for n in names if not hasattr(lib, n)]
+    assert not missing, missing
+
+
+def _random_attrs(rng, nsp):
+    at = {}
+    if rng.random() < 0.8:
+        at["strides"] = [int(v) for v in rng.integers(1, 4, size=nsp)]
+    if rng.random() < 0.6:
+        at["dilations"] = [int(v) for v in rng.integers(1, 4, size=nsp)]
+    s = at.get("strides", [1] * nsp)
+    d = at.get("dilations", [1] * nsp)
+    if rng.random() < 0.5:
+        at["output_padding"] = [int(rng.integers(0, max(a, b) + (1 if rng.random() < 0.1 else 0)))
+                                for a, b in zip(s, d)]
+    mode = rng.choice(["NOTSET", "NOTSET", "SAME_UPPER", "SAME_LOWER", "VALID"])
+    at["auto_pad"] = str(mode)
+    if mode == "NOTSET" or rng.random() < 0.05:
+        if rng.random() < 0.8:
+            at["pads"] = [int(v) for v in rng.integers(-1 if rng.random() < 0.05 else 0, 4, size=2 * nsp)]
+    if rng.random() < 0.15:
+        at["output_shape"] = [int(v) for v in rng.integers(0, 12, size=nsp)]
+    if rng.random() < 0.1:
+        at["kernel_shape"] = [int(v) for v in rng.integers(1, 4, size=nsp)]
+    at["group"] = int(rng.choice([1, 1, 2, 3, 0]) if rng.random() < 0.95 else -1)
+    return at
+
+
+def test_resolver_matches_oracle(T):
+    rng = np.random.default_rng(101)
+    agree_ok = agree_err = 0
+    for _ in range(3000):
+        nsp = int(rng.integers(1, 4))
+        C = int(rng.integers(0, 7))
+        xs = (int(rng.integers(0, 3)), C) + tuple(int(v) for v in rng.integers(0, 7, size=nsp))
+        ws = (C if rng.random() < 0.97 else C + 1, int(rng.integers(1, 4))) + tuple(
+            int(v) for v in rng.integers(1, 5, size=nsp))
+        at = _random_attrs(rng, nsp)
+        try:
+            want = O.output_shape(xs, ws, **at)
+        except O.OracleError:
+            want = None
+        try:
+            got = T.convtranspose_output_shape(xs, ws, **at)
+        except T.ConvTransposeError as e:
+            assert e.status == 1
+            got = None
+        if want is None:
+            assert got is None, (xs, ws, at, got)
+            agree_err += 1
+        else:
+            assert got is not None, (xs, ws, at, T.convtranspose_last_error())
+            assert tuple(got[0]) == tuple(want[0]) and list(got[1]) == list(want[1]), (xs, ws, at)
+            assert T.convtranspose_useful_macs(xs, ws, **at) == O.useful_macs(xs, ws, **at)
+            agree_ok += 1
+    assert agree_ok > 800 and agree_err > 300
+
+
+def test_config_shapes_and_macs(T):
+    for wl in W.CONFIGS.values():
+        assert T.convtranspose_output_shape(wl.x_shape, wl.w_shape, **wl.attrs)[0] == \
+            O.output_shape(wl.x_shape, wl.w_shape, **wl.attrs)[0]
+        assert T.convtranspose_useful_macs(wl.x_shape, wl.w_shape, **wl.attrs) == \
+            O.useful_macs(wl.x_shape, wl.w_shape, **wl.attrs)
+
+
+def _raw_call(T, kernel=0, dtype=1, nsp=2, cl=0, x=256, xs=(1, 4, 5, 5), w=512, ws=(4, 3, 3, 3),
+              bias=None, y=1024, ys=None, attrs=None):
+    lib = T.load_library()
+    attrs = attrs or {}
+    if ys is None:
+        ys = T.convtranspose_output_shape(xs, ws, **attrs)[0]
+    at = T._attr_args(nsp, **attrs)
+    vp = lambda v: None if v is None else ctypes.c_void_p(v)  # noqa: E731
+    return lib.convtranspose_nd_with_kernel(kernel, dtype, nsp, cl, vp(x), T._i64(xs), vp(w), T._i64(ws),
+                                            vp(bias), vp(y), T._i64(ys), *at, None)
+
+
+def test_validation_errors_launch_nothing(T):
+    assert _raw_call(T, ys=(1, 3, 7, 8)) == 2                       # y_shape mismatch
+    assert _raw_call(T, dtype=7) == 3                                # dtype not served
+    assert _raw_call(T, x=257) == 1                                  # misaligned fp16 pointer
+    assert _raw_call(T, x=None) == 1                                 # NULL x with data
+    assert _raw_call(T, y=None) == 1                                 # NULL y
+    assert _raw_call(T, cl=2) == 1
+    assert _raw_call(T, kernel=9) == 1
+    assert _raw_call(T, nsp=2, attrs=dict(strides=[0, 1]), ys=(1, 3, 7, 7)) == 1
+    assert "stride" in T.convtranspose_last_error()
+    assert _raw_call(T, kernel=3, dtype=0) == 3                      # MFMA path is fp16 only
+    # empty outputs: OK with nothing launched (no device is touched)
+    assert _raw_call(T, xs=(0, 4, 5, 5), x=None, y=None) == 0
+    assert T.convtranspose_last_error() == ""
+
+
+def test_dispatcher_choices(T):
+    lib = T.load_library()
+
+    def pick(wl, dtype=1, cl=0):
+        at = T._attr_args(wl.nsp, **wl.attrs)
+        k = lib.convtranspose_select_kernel(dtype, wl.nsp, cl, ctypes.c_void_p(256), T._i64(wl.x_shape),
+                                            ctypes.c_void_p(256), T._i64(wl.w_shape),
+                                            ctypes.c_void_p(256) if wl.has_bias else None,
+                                            ctypes.c_void_p(256), *at)
+        return T.convtranspose_kernel_name(k)
+
+    assert pick(W.C1, dtype=0) == "direct"
+    assert pick(W.C2, dtype=0) == "direct"
+    assert pick(W.C3) in ("grouped", "direct")
+    assert pick(W.C4) in ("igemm", "direct")
+    assert pick(W.C4, cl=1) in ("igemm", "direct")
+
+
+def test_random_cases_resolve_identically(T):
+    rng = np.random.default_rng(5)
+    for t in range(300):
+        x, w, b, attrs = pins.random_case(rng, auto=(t % 3 == 0))
+        assert T.convtranspose_output_shape(x.shape, w.shape, **attrs) == \
+            tuple(tuple(v) for v in O.output_shape(x.shape, w.shape, **attrs))

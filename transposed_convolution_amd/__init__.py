@@ -1,0 +1,263 @@
+"""MI355X-native N-D transposed convolution (ONNX ConvTranspose).
+
+This package is a thin Python binding over ``libconvtranspose.so``, whose C ABI is
+declared in ``include/convtranspose.h``.  The binding only marshals arguments: it
+resolves the output shape through the library, allocates Y with torch (torch supplies
+device memory and the stream) and passes raw pointers.  Every step of the operator
+runs in the library's HIP kernels; there is no CPU or PyTorch fallback, and a missing
+library raises.
+
+Operator: webgpu-kernels "ai.onnx.ConvTranspose" README (Description, Inputs,
+Outputs, Attributes, Type constraints); channels-last input/output as on the ClikaRT
+"conv_transpose" API page.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Sequence, Tuple
+
+import torch  # first: the library then binds to the HIP runtime torch has loaded
+
+__all__ = [
+    "ConvTransposeError", "convtranspose_nd", "convtranspose_output_shape",
+    "convtranspose_useful_macs", "convtranspose_select_kernel", "convtranspose_last_error",
+    "convtranspose_kernel_name", "library_path", "load_library", "channels_last_empty",
+    "to_channels_last", "KERNELS",
+]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "libconvtranspose.so")
+AUTO_PAD = {"NOTSET": 0, "SAME_UPPER": 1, "SAME_LOWER": 2, "VALID": 3}
+KERNELS = {"auto": 0, "direct": 1, "grouped": 2, "igemm": 3, "none": 4}
+_DTYPES = {torch.float32: 0, torch.float16: 1}
+_STATUS = {0: "CT_OK", 1: "CT_EINVAL", 2: "CT_ESHAPE", 3: "CT_EUNSUPPORTED", 4: "CT_EDEVICE"}
+_lib = None
+
+
+class ConvTransposeError(RuntimeError):
+    """A library call returned a non-OK status."""
+
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{_STATUS.get(status, status)}: {message}")
+        self.status = status
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def load_library():
+    """Load libconvtranspose.so (built in-tree by ``__graft_entry__.build()``)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        raise RuntimeError(f"{_LIB_PATH} is not built; run __graft_entry__.build() first")
+    lib = ctypes.CDLL(_LIB_PATH)
+    i64p = ctypes.POINTER(ctypes.c_int64)
+    vp = ctypes.c_void_p
+    attrs = [ctypes.c_int, i64p, i64p, i64p, i64p, i64p, i64p, ctypes.c_int64]
+    lib.convtranspose_output_shape.argtypes = [ctypes.c_int, i64p, i64p] + attrs + [i64p, i64p]
+    lib.convtranspose_useful_macs.argtypes = [ctypes.c_int, i64p, i64p] + attrs + [
+        ctypes.POINTER(ctypes.c_double)]
+    call = [ctypes.c_int, ctypes.c_int, ctypes.c_int, vp, i64p, vp, i64p, vp, vp, i64p] + attrs + [vp]
+    lib.convtranspose_nd.argtypes = call
+    lib.convtranspose_nd_with_kernel.argtypes = [ctypes.c_int] + call
+    lib.convtranspose_select_kernel.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, vp, i64p,
+                                                vp, i64p, vp, vp] + attrs
+    for fn in ("convtranspose_output_shape", "convtranspose_useful_macs", "convtranspose_nd",
+               "convtranspose_nd_with_kernel", "convtranspose_select_kernel"):
+        getattr(lib, fn).restype = ctypes.c_int
+    lib.convtranspose_last_error.restype = ctypes.c_char_p
+    lib.convtranspose_last_error.argtypes = []
+    lib.convtranspose_kernel_name.restype = ctypes.c_char_p
+    lib.convtranspose_kernel_name.argtypes = [ctypes.c_int]
+    _lib = lib
+    return lib
+
+
+def convtranspose_last_error() -> str:
+    return load_library().convtranspose_last_error().decode(errors="replace")
+
+
+def convtranspose_kernel_name(kernel: int) -> str:
+    return load_library().convtranspose_kernel_name(int(kernel)).decode()
+
+
+def _i64(v: Optional[Sequence[int]]):
+    if v is None:
+        return None
+    v = [int(t) for t in v]
+    return (ctypes.c_int64 * max(1, len(v)))(*v)
+
+
+def _attr_args(nsp, auto_pad="NOTSET", strides=None, dilations=None, pads=None, output_padding=None,
+               output_shape=None, kernel_shape=None, group=1):
+    lens = dict(strides=nsp, dilations=nsp, pads=2 * nsp, output_padding=nsp, output_shape=nsp,
+                kernel_shape=nsp)
+    vals = dict(strides=strides, dilations=dilations, pads=pads, output_padding=output_padding,
+                output_shape=output_shape, kernel_shape=kernel_shape)
+    for k, v in vals.items():
+        if v is not None and len(v) != lens[k]:
+            raise ConvTransposeError(1, f"{k} must have {lens[k]} entries")
+    if auto_pad not in AUTO_PAD:
+        raise ConvTransposeError(1, f"unknown auto_pad {auto_pad!r}")
+    return [AUTO_PAD[auto_pad]] + [_i64(vals[k]) for k in
+                                   ("strides", "dilations", "pads", "output_padding", "output_shape",
+                                    "kernel_shape")] + [int(group)]
+
+
+def _raise(st: int):
+    raise ConvTransposeError(st, convtranspose_last_error())
+
+
+def convtranspose_output_shape(x_shape, w_shape, **attrs) -> Tuple[Tuple[int, ...], Tuple[int, ...]]:
+    """Resolved Y shape (N, M, O1..On) and applied pads (begins, then ends)."""
+    lib = load_library()
+    nsp = len(x_shape) - 2
+    if len(w_shape) != len(x_shape):
+        raise ConvTransposeError(1, "W must have the same rank as X")
+    ys = (ctypes.c_int64 * (nsp + 2))()
+    pd = (ctypes.c_int64 * max(1, 2 * nsp))()
+    st = lib.convtranspose_output_shape(nsp, _i64(x_shape), _i64(w_shape), *_attr_args(nsp, **attrs),
+                                        ys, pd)
+    if st:
+        _raise(st)
+    return tuple(ys), tuple(pd[: 2 * nsp])
+
+
+def convtranspose_useful_macs(x_shape, w_shape, **attrs) -> int:
+    """Useful MACs: in-range (input sample, tap) pairs times N * C/group * M."""
+    lib = load_library()
+    nsp = len(x_shape) - 2
+    out = ctypes.c_double(0.0)
+    st = lib.convtranspose_useful_macs(nsp, _i64(x_shape), _i64(w_shape), *_attr_args(nsp, **attrs),
+                                       ctypes.byref(out))
+    if st:
+        _raise(st)
+    return int(out.value)
+
+
+def _expected_cl_strides(shape):
+    """Strides of a dense channels-last tensor with logical shape (N, C, D1..Dn)."""
+    N, C, sp = shape[0], shape[1], list(shape[2:])
+    st = [0] * len(shape)
+    st[1] = 1
+    acc = C
+    for a in range(len(sp) - 1, -1, -1):
+        st[2 + a] = acc
+        acc *= sp[a]
+    st[0] = acc
+    return st
+
+
+def _dense(t: torch.Tensor, channels_last: bool) -> bool:
+    if not channels_last:
+        return t.is_contiguous()
+    want = _expected_cl_strides(t.shape)
+    return all(sz <= 1 or s == w for sz, s, w in zip(t.shape, t.stride(), want))
+
+
+def channels_last_empty(shape, dtype, device) -> torch.Tensor:
+    """Uninitialised tensor of logical shape (N, C, D..) stored (N, D.., C)."""
+    nsp = len(shape) - 2
+    phys = torch.empty((shape[0],) + tuple(shape[2:]) + (shape[1],), dtype=dtype, device=device)
+    return phys.permute(0, nsp + 1, *range(1, nsp + 1))
+
+
+def to_channels_last(t: torch.Tensor) -> torch.Tensor:
+    """Dense channels-last copy of a logical (N, C, D..) tensor."""
+    nsp = t.dim() - 2
+    return t.permute(0, *range(2, nsp + 2), 1).contiguous().permute(0, nsp + 1, *range(1, nsp + 1))
+
+
+def _check_tensor(name, t, device, dtype):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ConvTransposeError(1, f"{name} must be on a HIP device (got {t.device})")
+    if t.device != device:
+        raise ConvTransposeError(1, f"{name} is on {t.device}, x is on {device}")
+    if t.dtype != dtype:
+        raise ConvTransposeError(3, f"{name} has dtype {t.dtype}, x has {dtype}")
+
+
+def _call_args(x, w, bias, y, attrs):
+    nsp = x.dim() - 2
+    ptr = lambda t: ctypes.c_void_p(t.data_ptr()) if t is not None else None  # noqa: E731
+    return nsp, ptr(x), _i64(x.shape), ptr(w), _i64(w.shape), ptr(bias), ptr(y), _attr_args(nsp, **attrs)
+
+
+def convtranspose_select_kernel(x, w, bias=None, *, channels_last=False, **attrs) -> str:
+    """Name of the kernel family the dispatcher would run for these tensors."""
+    lib = load_library()
+    if x.dtype not in _DTYPES:
+        raise ConvTransposeError(3, f"dtype {x.dtype} is not served")
+    nsp, xp, xs, wp, ws, bp, _, at = _call_args(x, w, bias, None, attrs)
+    yshape, _ = convtranspose_output_shape(tuple(x.shape), tuple(w.shape), **attrs)
+    # alignment of y is that of a fresh torch allocation (256 B)
+    k = lib.convtranspose_select_kernel(_DTYPES[x.dtype], nsp, int(channels_last), xp, xs, wp, ws, bp,
+                                        ctypes.c_void_p(256), *at)
+    if k < 0:
+        raise ConvTransposeError(1, convtranspose_last_error())
+    return convtranspose_kernel_name(k)
+
+
+def convtranspose_nd(x: torch.Tensor, w: torch.Tensor, bias: Optional[torch.Tensor] = None, *,
+                     auto_pad: str = "NOTSET", strides=None, dilations=None, pads=None,
+                     output_padding=None, output_shape=None, kernel_shape=None, group: int = 1,
+                     channels_last: bool = False, out: Optional[torch.Tensor] = None,
+                     kernel: str = "auto", stream: Optional[torch.cuda.Stream] = None) -> torch.Tensor:
+    """Y = ConvTranspose(X, W, bias) on the GPU, enqueued on ``stream`` (default: torch's
+    current stream of x's device).
+
+    x: logical (N, C, D1..Dn) float32/float16 on a HIP device; dense NC.. storage, or
+    dense N..C storage when ``channels_last`` (see ``to_channels_last``).
+    w: (C, M/group, k1..kn) dense.  bias: (M,) or None.  Y is allocated (or ``out`` is
+    used) with the same layout convention as x.  ``kernel`` forces a kernel family.
+    """
+    lib = load_library()
+    if x.dtype not in _DTYPES:
+        raise ConvTransposeError(3, f"dtype {x.dtype} is not served (float32, float16)")
+    if x.dim() < 3 or x.dim() > 5:
+        raise ConvTransposeError(1, "x must have rank 3, 4 or 5")
+    dev = x.device
+    _check_tensor("x", x, dev, x.dtype)
+    _check_tensor("w", w, dev, x.dtype)
+    if w.dim() != x.dim():
+        raise ConvTransposeError(1, "W must have the same rank as X")
+    if bias is not None:
+        _check_tensor("bias", bias, dev, x.dtype)
+        if bias.dim() != 1 or not bias.is_contiguous():
+            raise ConvTransposeError(1, "bias must be a dense 1-D tensor")
+        if bias.shape[0] != w.shape[1] * int(group):
+            raise ConvTransposeError(1, "bias length must equal M = W.shape[1] * group")
+    if not _dense(x, channels_last):
+        raise ConvTransposeError(1, "x is not dense in the requested layout")
+    if not w.is_contiguous():
+        raise ConvTransposeError(1, "w must be contiguous")
+    attrs = dict(auto_pad=auto_pad, strides=strides, dilations=dilations, pads=pads,
+                 output_padding=output_padding, output_shape=output_shape,
+                 kernel_shape=kernel_shape, group=group)
+    yshape, _ = convtranspose_output_shape(tuple(x.shape), tuple(w.shape), **attrs)
+    if out is None:
+        out = (channels_last_empty(yshape, x.dtype, dev) if channels_last
+               else torch.empty(yshape, dtype=x.dtype, device=dev))
+    else:
+        _check_tensor("out", out, dev, x.dtype)
+        if tuple(out.shape) != tuple(yshape):
+            raise ConvTransposeError(2, f"out has shape {tuple(out.shape)}, expected {yshape}")
+        if not _dense(out, channels_last):
+            raise ConvTransposeError(1, "out is not dense in the requested layout")
+    if kernel not in KERNELS:
+        raise ConvTransposeError(1, f"unknown kernel {kernel!r}")
+    nsp, xp, xs, wp, ws, bp, yp, at = _call_args(x, w, bias, out, attrs)
+    with torch.cuda.device(dev):
+        s = stream if stream is not None else torch.cuda.current_stream(dev)
+        st = lib.convtranspose_nd_with_kernel(KERNELS[kernel], _DTYPES[x.dtype], nsp, int(channels_last),
+                                              xp, xs, wp, ws, bp, yp, _i64(yshape), *at,
+                                              ctypes.c_void_p(s.cuda_stream))
+    if st:
+        _raise(st)
+    return out

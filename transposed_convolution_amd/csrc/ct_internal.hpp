@@ -1,0 +1,73 @@
+// ct_internal.hpp -- host-side geometry, stride-phase plan and kernel launch
+// declarations shared by the library's translation units (not part of the C ABI).
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+#include <string>
+
+#include "convtranspose.h"
+
+namespace ct {
+
+// Every problem is carried as 3 spatial axes: a rank-n problem puts its axes last and
+// fills the leading ones with a unit axis (L = K = s = d = O = 1, no pads), which adds
+// exactly one tap and one output position and changes nothing else.
+constexpr int kAxes = 3;
+
+// Resolved problem geometry (ONNX attribute table applied; README "Attributes").
+struct Geom {
+    int nsp = 0;                                  // rank as given (1..3)
+    int64_t N = 0, C = 0, M = 0, G = 1, Cg = 0, Mg = 0;
+    int64_t L[kAxes], K[kAxes], s[kAxes], d[kAxes], b[kAxes], e[kAxes], op[kAxes], O[kAxes];
+
+    int64_t in_pixels() const { return L[0] * L[1] * L[2]; }
+    int64_t out_pixels() const { return O[0] * O[1] * O[2]; }
+    int64_t taps() const { return K[0] * K[1] * K[2]; }
+    int64_t x_elems() const { return N * C * in_pixels(); }
+    int64_t w_elems() const { return C * Mg * taps(); }
+    int64_t y_elems() const { return N * M * out_pixels(); }
+};
+
+struct Attrs {
+    ct_auto_pad auto_pad = CT_NOTSET;
+    const int64_t *strides = nullptr, *dilations = nullptr, *pads = nullptr;
+    const int64_t *output_padding = nullptr, *output_shape = nullptr, *kernel_shape = nullptr;
+    int64_t group = 1;
+};
+
+// Defaults, validation, derived pads and output sizes.  Returns CT_OK or CT_EINVAL
+// (message in *err).
+ct_status resolve(int nsp, const int64_t *x_shape, const int64_t *w_shape, const Attrs &at,
+                  Geom *g, std::string *err);
+
+// Useful MACs: per axis the (i, k) pairs landing in [0, O), counted in closed form.
+double useful_macs(const Geom &g);
+
+// --- stride-phase (sub-pixel) decomposition of one axis --------------------------
+// Output positions o with o % s == r form phase r: o = r + s*j, j in [0, J).  Such an
+// output receives tap k exactly when (r + b - k*d) is a multiple of s, from input
+// i = j + beta_k with beta_k = (r + b - k*d) / s.  Taps are listed by ascending k.
+constexpr int kMaxPhaseTaps = 16;
+struct AxisPhase {
+    int r = 0;          // first output of the phase
+    int J = 0;          // outputs in the phase
+    int ntaps = 0;      // taps reaching the phase (0: only bias lands here)
+    int k[kMaxPhaseTaps];
+    int beta[kMaxPhaseTaps];
+};
+// Fills phase r of axis a; returns false when the phase has more than kMaxPhaseTaps taps.
+bool axis_phase(const Geom &g, int a, int r, AxisPhase *ph);
+
+// Launchers (one per kernel family); each returns CT_OK or CT_EDEVICE (message in err).
+ct_status launch_direct(const Geom &g, ct_dtype dt, bool cl, const void *x, const void *w,
+                        const void *bias, void *y, hipStream_t st, std::string *err);
+bool grouped_supports(const Geom &g, ct_dtype dt, bool cl);
+ct_status launch_grouped(const Geom &g, ct_dtype dt, bool cl, const void *x, const void *w,
+                         const void *bias, void *y, hipStream_t st, std::string *err);
+bool igemm_supports(const Geom &g, ct_dtype dt, bool cl, std::string *why);
+ct_status launch_igemm(const Geom &g, ct_dtype dt, bool cl, const void *x, const void *w,
+                       const void *bias, void *y, hipStream_t st, std::string *err);
+
+}  // namespace ct
