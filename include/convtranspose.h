@@ -31,13 +31,16 @@
  *
  * Shapes are always passed in logical ONNX order.  Buffers are owned by the caller,
  * must be dense in the stated layout and aligned to the element size; the library
- * keeps no pointer after a call returns and allocates no device memory.
+ * keeps no pointer after a call returns.  The implicit-GEMM path re-lays W out into
+ * scratch memory: a caller workspace (convtranspose_nd_with_kernel), or else
+ * stream-ordered scratch taken and released on the call's stream.
  *
  * Thread safety: every call is re-entrant; the error text is per host thread.
  */
 #ifndef CONVTRANSPOSE_H
 #define CONVTRANSPOSE_H
 
+#include <stddef.h>
 #include <stdint.h>
 
 #ifdef __cplusplus
@@ -111,7 +114,9 @@ ct_status convtranspose_useful_macs(int nsp, const int64_t *x_shape, const int64
  *   stream         hipStream_t to enqueue on (NULL: the null stream)
  * All validation happens before anything is enqueued: on any error nothing is launched
  * and y is untouched.  Work is asynchronous: the call returns once the kernels are
- * enqueued.  An empty y (some dimension 0) returns CT_OK with no launch.
+ * enqueued.  An empty y (some dimension 0) returns CT_OK with no launch.  When the
+ * dispatcher picks the implicit-GEMM path, scratch for the re-laid-out weights is taken
+ * with hipMallocAsync and released with hipFreeAsync on `stream`.
  */
 ct_status convtranspose_nd(ct_dtype dtype, int nsp, int channels_last, const void *x,
                            const int64_t *x_shape, const void *w, const int64_t *w_shape,
@@ -122,9 +127,16 @@ ct_status convtranspose_nd(ct_dtype dtype, int nsp, int channels_last, const voi
                            int64_t group, void *stream);
 
 /*
- * As convtranspose_nd, with the kernel family forced (CT_KERNEL_AUTO = dispatcher's
- * choice).  Returns CT_EUNSUPPORTED, launching nothing, when the forced family cannot
- * serve the call (e.g. CT_KERNEL_IGEMM for float32 or for shapes its tiling excludes).
+ * As convtranspose_nd, with the kernel family forced and an optional caller workspace.
+ *   kernel          CT_KERNEL_AUTO (the dispatcher's choice) or a family to force;
+ *                   CT_EUNSUPPORTED (nothing launched) when that family cannot serve
+ *                   the call (e.g. CT_KERNEL_IGEMM for float32).
+ *   workspace       device scratch of workspace_bytes bytes, 16-byte aligned, used for
+ *                   the implicit-GEMM path's re-laid-out weights; it must not be in use
+ *                   by other work until this call's kernels have finished on `stream`.
+ *                   NULL: the library takes stream-ordered scratch itself
+ *                   (hipMallocAsync / hipFreeAsync on `stream`), as convtranspose_nd does.
+ *                   Too small a workspace is CT_EINVAL.
  */
 ct_status convtranspose_nd_with_kernel(ct_kernel kernel, ct_dtype dtype, int nsp, int channels_last,
                                        const void *x, const int64_t *x_shape, const void *w,
@@ -133,7 +145,21 @@ ct_status convtranspose_nd_with_kernel(ct_kernel kernel, ct_dtype dtype, int nsp
                                        const int64_t *strides, const int64_t *dilations,
                                        const int64_t *pads, const int64_t *output_padding,
                                        const int64_t *output_shape, const int64_t *kernel_shape,
-                                       int64_t group, void *stream);
+                                       int64_t group, void *workspace, size_t workspace_bytes,
+                                       void *stream);
+
+/*
+ * Workspace bytes convtranspose_nd_with_kernel needs for these arguments and kernel
+ * choice (0 when the chosen family needs none).  x is inspected for alignment only and
+ * may be NULL (then assumed 256-byte aligned).  Host only.  Returns CT_OK or the status
+ * the call itself would return for invalid arguments.
+ */
+ct_status convtranspose_workspace_size(ct_kernel kernel, ct_dtype dtype, int nsp, int channels_last,
+                                       const void *x, const int64_t *x_shape, const int64_t *w_shape,
+                                       ct_auto_pad auto_pad, const int64_t *strides,
+                                       const int64_t *dilations, const int64_t *pads,
+                                       const int64_t *output_padding, const int64_t *output_shape,
+                                       const int64_t *kernel_shape, int64_t group, size_t *bytes_out);
 
 /*
  * The kernel family the dispatcher picks for these arguments (pointers are inspected

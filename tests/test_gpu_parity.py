@@ -157,6 +157,45 @@ def test_random_small_problems(T, kernel, dtype, cl):
         assert ran == 50
 
 
+@pytest.mark.parametrize("cl", [False, True], ids=["nc", "cl"])
+def test_random_igemm_shaped_problems(T, cl):
+    """Shapes the implicit-GEMM path accepts (channels per group a multiple of 8; innermost
+    input size a multiple of 8 for NC.. layout), random strides/dilations/pads/groups,
+    ragged channel and pixel tails; forced igemm and the dispatcher's choice."""
+    rng = np.random.default_rng(77 + cl)
+    ran = 0
+    for t in range(40):
+        nsp = int(rng.integers(1, 4))
+        G = int(rng.choice([1, 1, 1, 2]))
+        Cg = int(rng.choice([8, 16, 24, 40, 64]))
+        Mg = int(rng.integers(1, 80))
+        L = [int(rng.integers(1, 7)) for _ in range(nsp - 1)] + [8 * int(rng.integers(1, 5))]
+        K = [int(rng.integers(1, 5)) for _ in range(nsp)]
+        s = [int(rng.integers(1, 4)) for _ in range(nsp)]
+        d = [int(rng.integers(1, 3)) for _ in range(nsp)]
+        op = [int(rng.integers(0, max(a, b))) for a, b in zip(s, d)]
+        attrs = dict(strides=s, dilations=d, output_padding=op, group=G,
+                     pads=[int(rng.integers(0, 3)) for _ in range(2 * nsp)])
+        try:
+            O.output_shape((2, G * Cg, *L), (G * Cg, Mg, *K), **attrs)
+        except O.OracleError:
+            continue
+        integer = bool(t % 2)
+        gen = (lambda sz: rng.integers(-2, 3, size=sz)) if integer else (lambda sz: rng.normal(size=sz))
+        x = gen((2, G * Cg, *L)).astype(np.float16)
+        w = (gen((G * Cg, Mg, *K)) * (1 if integer else 0.2)).astype(np.float16)
+        b = gen(G * Mg).astype(np.float16)
+        _log(f"[case] igemm-random #{t} cl={cl} x{x.shape} w{w.shape} {attrs}")
+        ref = O.convtranspose(x, w, b, **attrs)
+        for kernel in ("igemm", "auto"):
+            got = gpu_run(T, x, w, b, attrs, cl, kernel)
+            if got is None:
+                continue
+            ran += kernel == "igemm"
+            check(got, ref, "f16", integer, f"igemm-random #{t} {kernel} {attrs}")
+    assert ran >= 25
+
+
 EDGE = [
     # (name, x_shape, w_shape, attrs, bias)
     ("empty_batch", (0, 8, 5, 5), (8, 4, 3, 3), dict(strides=[2, 2]), True),

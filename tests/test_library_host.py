@@ -115,7 +115,7 @@ def _raw_call(T, kernel=0, dtype=1, nsp=2, cl=0, x=256, xs=(1, 4, 5, 5), w=512, 
     at = T._attr_args(nsp, **attrs)
     vp = lambda v: None if v is None else ctypes.c_void_p(v)  # noqa: E731
     return lib.convtranspose_nd_with_kernel(kernel, dtype, nsp, cl, vp(x), T._i64(xs), vp(w), T._i64(ws),
-                                            vp(bias), vp(y), T._i64(ys), *at, None)
+                                            vp(bias), vp(y), T._i64(ys), *at, None, 0, None)
 
 
 def test_validation_errors_launch_nothing(T):

@@ -61,13 +61,16 @@ def load_library():
     lib.convtranspose_output_shape.argtypes = [ctypes.c_int, i64p, i64p] + attrs + [i64p, i64p]
     lib.convtranspose_useful_macs.argtypes = [ctypes.c_int, i64p, i64p] + attrs + [
         ctypes.POINTER(ctypes.c_double)]
-    call = [ctypes.c_int, ctypes.c_int, ctypes.c_int, vp, i64p, vp, i64p, vp, vp, i64p] + attrs + [vp]
-    lib.convtranspose_nd.argtypes = call
-    lib.convtranspose_nd_with_kernel.argtypes = [ctypes.c_int] + call
+    call = [ctypes.c_int, ctypes.c_int, ctypes.c_int, vp, i64p, vp, i64p, vp, vp, i64p] + attrs
+    lib.convtranspose_nd.argtypes = call + [vp]
+    lib.convtranspose_nd_with_kernel.argtypes = [ctypes.c_int] + call + [vp, ctypes.c_size_t, vp]
+    lib.convtranspose_workspace_size.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, vp,
+                                                 i64p, i64p] + attrs + [ctypes.POINTER(ctypes.c_size_t)]
     lib.convtranspose_select_kernel.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, vp, i64p,
                                                 vp, i64p, vp, vp] + attrs
     for fn in ("convtranspose_output_shape", "convtranspose_useful_macs", "convtranspose_nd",
-               "convtranspose_nd_with_kernel", "convtranspose_select_kernel"):
+               "convtranspose_nd_with_kernel", "convtranspose_select_kernel",
+               "convtranspose_workspace_size"):
         getattr(lib, fn).restype = ctypes.c_int
     lib.convtranspose_last_error.restype = ctypes.c_char_p
     lib.convtranspose_last_error.argtypes = []
@@ -153,6 +156,8 @@ def _expected_cl_strides(shape):
 
 
 def _dense(t: torch.Tensor, channels_last: bool) -> bool:
+    if t.numel() == 0:
+        return True  # nothing is read or written
     if not channels_last:
         return t.is_contiguous()
     want = _expected_cl_strides(t.shape)
@@ -253,11 +258,22 @@ def convtranspose_nd(x: torch.Tensor, w: torch.Tensor, bias: Optional[torch.Tens
     if kernel not in KERNELS:
         raise ConvTransposeError(1, f"unknown kernel {kernel!r}")
     nsp, xp, xs, wp, ws, bp, yp, at = _call_args(x, w, bias, out, attrs)
+    nbytes = ctypes.c_size_t(0)
+    st = lib.convtranspose_workspace_size(KERNELS[kernel], _DTYPES[x.dtype], nsp, int(channels_last), xp, xs,
+                                          ws, *at, ctypes.byref(nbytes))
+    if st:
+        _raise(st)
     with torch.cuda.device(dev):
         s = stream if stream is not None else torch.cuda.current_stream(dev)
+        # scratch from torch's caching allocator; stream order keeps it valid for the call
+        scratch = None
+        if nbytes.value:
+            with torch.cuda.stream(s):
+                scratch = torch.empty(nbytes.value, dtype=torch.uint8, device=dev)
         st = lib.convtranspose_nd_with_kernel(KERNELS[kernel], _DTYPES[x.dtype], nsp, int(channels_last),
                                               xp, xs, wp, ws, bp, yp, _i64(yshape), *at,
-                                              ctypes.c_void_p(s.cuda_stream))
+                                              ctypes.c_void_p(scratch.data_ptr()) if scratch is not None
+                                              else None, nbytes.value, ctypes.c_void_p(s.cuda_stream))
     if st:
         _raise(st)
     return out

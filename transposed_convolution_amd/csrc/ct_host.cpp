@@ -224,7 +224,9 @@ ct_status prepare(ct_kernel want, ct_dtype dt, int nsp, int cl, const void *x,
     std::string why;
     switch (want) {
         case CT_KERNEL_AUTO:
-            if (ct::igemm_supports(*g, dt, cl, &why))
+            // MFMA tiles are 32 wide in output channels and 32 deep in input channels:
+            // below 16 of either most of each tile would be padding.
+            if (g->Cg >= 16 && g->Mg >= 16 && ct::igemm_supports(*g, dt, cl, x, &why))
                 *chosen = CT_KERNEL_IGEMM;
             else if (ct::grouped_supports(*g, dt, cl))
                 *chosen = CT_KERNEL_GROUPED;
@@ -240,7 +242,7 @@ ct_status prepare(ct_kernel want, ct_dtype dt, int nsp, int cl, const void *x,
             *chosen = CT_KERNEL_GROUPED;
             return CT_OK;
         case CT_KERNEL_IGEMM:
-            if (!ct::igemm_supports(*g, dt, cl, &why))
+            if (!ct::igemm_supports(*g, dt, cl, x, &why))
                 return fail(CT_EUNSUPPORTED, "the implicit-GEMM kernel cannot serve this call: " + why);
             *chosen = CT_KERNEL_IGEMM;
             return CT_OK;
@@ -318,6 +320,28 @@ int convtranspose_select_kernel(ct_dtype dtype, int nsp, int channels_last, cons
     return int(k);
 }
 
+ct_status convtranspose_workspace_size(ct_kernel kernel, ct_dtype dtype, int nsp, int channels_last,
+                                       const void *x, const int64_t *x_shape, const int64_t *w_shape,
+                                       ct_auto_pad auto_pad, const int64_t *strides,
+                                       const int64_t *dilations, const int64_t *pads,
+                                       const int64_t *output_padding, const int64_t *output_shape,
+                                       const int64_t *kernel_shape, int64_t group, size_t *bytes_out)
+{
+    t_error.clear();
+    if (!bytes_out) return fail(CT_EINVAL, "bytes_out is NULL");
+    ct::Geom g;
+    ct_kernel k = CT_KERNEL_AUTO;
+    const ct::Attrs at = make_attrs(auto_pad, strides, dilations, pads, output_padding,
+                                    output_shape, kernel_shape, group);
+    // w, bias and y are not inspected for the choice beyond alignment: pass aligned stand-ins
+    const void *aligned_stub = reinterpret_cast<const void *>(uintptr_t(256));
+    ct_status st = prepare(kernel, dtype, nsp, channels_last, x ? x : aligned_stub, x_shape,
+                           aligned_stub, w_shape, nullptr, aligned_stub, nullptr, at, &g, &k);
+    if (st != CT_OK) return st;
+    *bytes_out = (k == CT_KERNEL_IGEMM) ? ct::igemm_workspace_bytes(g) : 0;
+    return CT_OK;
+}
+
 ct_status convtranspose_nd_with_kernel(ct_kernel kernel, ct_dtype dtype, int nsp, int channels_last,
                                        const void *x, const int64_t *x_shape, const void *w,
                                        const int64_t *w_shape, const void *bias, void *y,
@@ -325,10 +349,12 @@ ct_status convtranspose_nd_with_kernel(ct_kernel kernel, ct_dtype dtype, int nsp
                                        const int64_t *strides, const int64_t *dilations,
                                        const int64_t *pads, const int64_t *output_padding,
                                        const int64_t *output_shape, const int64_t *kernel_shape,
-                                       int64_t group, void *stream)
+                                       int64_t group, void *workspace, size_t workspace_bytes,
+                                       void *stream)
 {
     t_error.clear();
     if (!y_shape) return fail(CT_EINVAL, "y_shape is NULL");
+    if (workspace && !aligned(workspace, 16)) return fail(CT_EINVAL, "workspace must be 16-byte aligned");
     ct::Geom g;
     ct_kernel k = CT_KERNEL_AUTO;
     const ct::Attrs at = make_attrs(auto_pad, strides, dilations, pads, output_padding,
@@ -341,7 +367,9 @@ ct_status convtranspose_nd_with_kernel(ct_kernel kernel, ct_dtype dtype, int nsp
     std::string err;
     const bool cl = channels_last != 0;
     switch (k) {
-        case CT_KERNEL_IGEMM: st = ct::launch_igemm(g, dtype, cl, x, w, bias, y, hs, &err); break;
+        case CT_KERNEL_IGEMM:
+            st = ct::launch_igemm(g, dtype, cl, x, w, bias, y, workspace, workspace_bytes, hs, &err);
+            break;
         case CT_KERNEL_GROUPED: st = ct::launch_grouped(g, dtype, cl, x, w, bias, y, hs, &err); break;
         default: st = ct::launch_direct(g, dtype, cl, x, w, bias, y, hs, &err); break;
     }
@@ -360,7 +388,7 @@ ct_status convtranspose_nd(ct_dtype dtype, int nsp, int channels_last, const voi
     return convtranspose_nd_with_kernel(CT_KERNEL_AUTO, dtype, nsp, channels_last, x, x_shape, w,
                                         w_shape, bias, y, y_shape, auto_pad, strides, dilations,
                                         pads, output_padding, output_shape, kernel_shape, group,
-                                        stream);
+                                        nullptr, 0, stream);
 }
 
 const char *convtranspose_last_error(void) { return t_error.c_str(); }

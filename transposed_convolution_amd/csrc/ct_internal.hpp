@@ -66,8 +66,12 @@ ct_status launch_direct(const Geom &g, ct_dtype dt, bool cl, const void *x, cons
 bool grouped_supports(const Geom &g, ct_dtype dt, bool cl);
 ct_status launch_grouped(const Geom &g, ct_dtype dt, bool cl, const void *x, const void *w,
                          const void *bias, void *y, hipStream_t st, std::string *err);
-bool igemm_supports(const Geom &g, ct_dtype dt, bool cl, std::string *why);
+bool igemm_supports(const Geom &g, ct_dtype dt, bool cl, const void *x, std::string *why);
+size_t igemm_workspace_bytes(const Geom &g);
+// workspace: caller scratch of ws_bytes (>= igemm_workspace_bytes), or NULL to take
+// stream-ordered scratch with hipMallocAsync / hipFreeAsync on st.
 ct_status launch_igemm(const Geom &g, ct_dtype dt, bool cl, const void *x, const void *w,
-                       const void *bias, void *y, hipStream_t st, std::string *err);
+                       const void *bias, void *y, void *workspace, size_t ws_bytes, hipStream_t st,
+                       std::string *err);
 
 }  // namespace ct
