@@ -1,0 +1,262 @@
+#!/usr/bin/env python3
+"""ConvTranspose throughput on one MI355X.
+
+Metric: TFLOP/s counted as 2 x useful MACs (the (input sample, tap) pairs whose target
+lies inside Y, times N x C/group x M) per second of wall time for whole calls with the
+inputs already resident in device memory, plus the roofline fraction of the call's
+dominant kernel and the fp64 oracle timed on the host cores as a reference point.
+
+Default workload: the dense fp16 decoder upsampling ConvTranspose
+X[8,512,64,64], W[512,256,4,4], bias[256], stride 2, pads 1 -> Y[8,256,128,128] (NCHW),
+float32 accumulation.  Other workloads (--workload) print the same JSON line.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload c4]
+
+One timed step is one convtranspose_nd call (shape resolution, weight re-layout,
+the MFMA / bandwidth / direct kernel), enqueued through a prepared plan.  The K steps
+are bracketed by torch.cuda.synchronize(); the dominant kernel's device time comes from
+HIP events the library records around that kernel on the call's stream.
+
+--pmc-summary DIR turns two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) of this
+script with --calibrate-copy into profiles/<workload>_<kernel>_traffic.json.
+"""
+from __future__ import annotations
+
+import argparse
+import csv
+import glob
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "ConvTranspose TFLOP/s (2*useful MACs) and % of MFMA/HBM roofline on 1 MI355X"
+PEAK_TFLOPS = {"f16": 2500.0, "f32": 157.3}   # dense MFMA peaks of MI355X
+PEAK_HBM_GBS = 8000.0
+KERNEL_SOURCES = {"igemm": "ct_igemm.hip", "grouped": "ct_grouped.hip", "direct": "ct_direct.hip"}
+COPY_BYTES = 256 << 20  # calibration copy: 256 MiB read + 256 MiB written
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def workloads():
+    import workloads as W
+    return {"c1": W.C1, "c2": W.C2, "c3": W.C3, "c4": W.C4, "c4_nhwc": W.C4_NHWC,
+            "c5_s1": W.C5_S1, "c5_s1_p1": W.C5_S1_P1, "c5_s2": W.C5_S2}
+
+
+def source_digest(kernel: str) -> str:
+    path = os.path.join(ROOT, "transposed_convolution_amd", "csrc", KERNEL_SOURCES.get(kernel, ""))
+    if not os.path.isfile(path):
+        return ""
+    return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
+
+
+def traffic_file(wl_key: str, kernel: str) -> str:
+    return os.path.join(ROOT, "profiles", f"{wl_key}_{kernel}_traffic.json")
+
+
+def algorithmic_bytes(wl, y_shape) -> int:
+    esz = 2 if wl.dtype == "f16" else 4
+    n = math.prod(wl.x_shape) + math.prod(wl.w_shape) + math.prod(y_shape)
+    if wl.has_bias:
+        n += y_shape[1]
+    return n * esz
+
+
+def cpu_baseline(wl, x, w, b, images: int):
+    """The fp64 oracle on the first `images` images of the workload (all channels)."""
+    from oracle import oracle as O
+    xs = x[:images]
+    macs = O.useful_macs(xs.shape, w.shape, **wl.attrs)
+    t0 = time.perf_counter()
+    O.convtranspose(xs, w, b, **wl.attrs)
+    dt = time.perf_counter() - t0
+    return {"value": 2.0 * macs / dt / 1e12, "unit": "TFLOP/s", "cores": O.threads(), "kind": "oracle",
+            "sample": f"first {images} of {wl.x_shape[0]} images, every channel and output "
+                      f"({macs / 1e9:.2f} GMAC, {dt:.1f} s)"}
+
+
+def summarize_pmc(args):
+    """Per-launch FETCH_SIZE / WRITE_SIZE of the dominant kernel, scaled by the same
+    counters' reading for a plain device copy of known size."""
+    def rows(pattern):
+        out = []
+        for f in glob.glob(os.path.join(args.pmc_summary, "**", pattern), recursive=True):
+            with open(f) as fh:
+                out += list(csv.DictReader(fh))
+        return out
+
+    res = {}
+    for counter in ("FETCH_SIZE", "WRITE_SIZE"):
+        vals, copy = [], []
+        for r in rows("*counter_collection.csv"):
+            if r.get("Counter_Name") != counter:
+                continue
+            name = r.get("Kernel_Name", "")
+            v = float(r["Counter_Value"])
+            if args.kernel_match in name:
+                vals.append(v)
+            elif "copy" in name.lower() or "elementwise" in name.lower():
+                copy.append(v)
+        if not vals or not copy:
+            raise SystemExit(f"no {counter} rows for the kernel or the calibration copy in {args.pmc_summary}")
+        # counters are KiB per dispatch; the copy moves COPY_BYTES each way
+        scale = COPY_BYTES / (max(copy) * 1024.0)
+        res[counter] = {"kib_per_launch": sum(vals) / len(vals), "copy_kib": max(copy),
+                        "bytes_per_launch": sum(vals) / len(vals) * 1024.0 * scale, "scale": scale}
+    out = {"workload": args.workload, "kernel": args.kernel, "source_sha": source_digest(args.kernel),
+           "fetch": res["FETCH_SIZE"], "write": res["WRITE_SIZE"],
+           "bytes_per_launch": res["FETCH_SIZE"]["bytes_per_launch"] + res["WRITE_SIZE"]["bytes_per_launch"]}
+    path = traffic_file(args.workload, args.kernel)
+    with open(path, "w") as fh:
+        json.dump(out, fh, indent=1)
+    print(json.dumps(out))
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="c4", choices=sorted(workloads()))
+    ap.add_argument("--rotate", type=int, default=0,
+                    help="independent (X, Y) buffer sets cycled per step (0: 1 for MFMA-bound, 4 otherwise)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-images", type=int, default=0, help="images in the oracle sample (0: all)")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="also run one plain device copy of 256 MiB (counter calibration)")
+    ap.add_argument("--pmc-summary", default="", help="rocprofv3 output dir to summarise (no GPU use)")
+    ap.add_argument("--kernel", default="igemm", help="with --pmc-summary: kernel family")
+    ap.add_argument("--kernel-match", default="igemm_kernel", help="with --pmc-summary: kernel name part")
+    args = ap.parse_args()
+
+    if args.pmc_summary:
+        return summarize_pmc(args)
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: this ConvTranspose build has no multi-GPU path; "
+              "run it with --gpus 1", flush=True)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import transposed_convolution_amd as T
+    import workloads as W
+
+    wl = workloads()[args.workload]
+    dev = torch.device("cuda:0")
+    x, w, b = W.make_inputs(wl)
+    yshape, _ = T.convtranspose_output_shape(wl.x_shape, wl.w_shape, **wl.attrs)
+    macs = T.convtranspose_useful_macs(wl.x_shape, wl.w_shape, **wl.attrs)
+    flops = 2.0 * macs
+
+    def to_dev(a):
+        t = torch.from_numpy(a).to(dev)
+        return T.to_channels_last(t) if wl.channels_last else t
+
+    tx = to_dev(x)
+    tw = torch.from_numpy(w).to(dev)
+    tb = None if b is None else torch.from_numpy(b).to(dev)
+    kernel = T.convtranspose_select_kernel(tx, tw, tb, channels_last=wl.channels_last, **wl.attrs)
+    bound = "mfma" if kernel == "igemm" else "hbm"
+    rotate = args.rotate or (1 if bound == "mfma" else 4)
+    plans = []
+    for r in range(rotate):
+        xr = tx if r == 0 else tx.clone()
+        plans.append(T.ConvTransposePlan(xr, tw, tb, channels_last=wl.channels_last, **wl.attrs))
+    log(f"workload {wl.name}: x{wl.x_shape} w{wl.w_shape} -> y{yshape}, kernel {kernel}, "
+        f"{macs / 1e9:.2f} GMAC, {rotate} buffer set(s)")
+
+    # correctness gate on the first buffer set: sampled outputs against the oracle
+    from oracle import oracle as O
+    y = plans[0]()
+    torch.cuda.synchronize()
+    pts = W.make_points(yshape, 2000, seed=wl.seed + 11)
+    ref = O.convtranspose_at(x, w, b, pts, **wl.attrs)
+    got = y.double().cpu().numpy()[tuple(pts.T)]
+    tol = 2e-3 if wl.dtype == "f16" else 1e-5
+    err = float(np.max(np.abs(got - ref) / (1.0 + np.abs(ref))))
+    if not err <= tol:
+        raise SystemExit(f"bench output disagrees with the oracle: max rel err {err:.3e} > {tol}")
+    log(f"parity vs oracle on {len(pts)} sampled outputs: max rel err {err:.2e}")
+
+    if args.calibrate_copy:
+        src = torch.empty(COPY_BYTES, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+
+    for i in range(args.warmup):
+        plans[i % rotate]()
+    torch.cuda.synchronize()
+
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    for a, c in evs:  # create the HIP events outside the timed region
+        a.record()
+        c.record()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        T.convtranspose_profile_events(*evs[i])
+        plans[i % rotate]()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    T.convtranspose_profile_events(None, None)
+    kms = np.array([a.elapsed_time(c) for a, c in evs])  # milliseconds
+    k_avg = float(kms.mean())
+
+    ms_per_step = wall * 1e3 / args.steps
+    value = flops * args.steps / wall / 1e12
+    alg_bytes = algorithmic_bytes(wl, yshape)
+    if bound == "mfma":
+        achieved = flops / (k_avg * 1e-3) / 1e12
+        peak, unit = PEAK_TFLOPS[wl.dtype], "TFLOP/s"
+    else:
+        achieved = alg_bytes / (k_avg * 1e-3) / 1e9
+        peak, unit = PEAK_HBM_GBS, "GB/s"
+    traffic = None
+    tf = traffic_file(args.workload, kernel)
+    if os.path.isfile(tf):
+        rec = json.load(open(tf))
+        if rec.get("source_sha") == source_digest(kernel):
+            traffic = rec["bytes_per_launch"]
+    log(f"{args.steps} steps: {ms_per_step * 1e3:.1f} us/step wall, {kernel} kernel {k_avg * 1e3:.1f} us avg "
+        f"(min {kms.min() * 1e3:.1f}), {achieved:.1f} {unit} = {achieved / peak * 100:.1f}% of {peak} {unit}")
+
+    base = None
+    if not args.no_cpu_baseline:
+        images = args.cpu_images or wl.x_shape[0]
+        log(f"timing the fp64 oracle on {images} image(s) ...")
+        base = cpu_baseline(wl, x, w, b, images)
+        log(f"oracle: {base['value'] * 1e3:.3f} GFLOP/s on {base['cores']} threads")
+
+    out = {
+        "metric": METRIC, "value": round(value, 3), "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": wl.dtype,
+        "data": "synthetic",
+        "config": {"workload": f"{wl.name}: X{list(wl.x_shape)} W{list(wl.w_shape)} "
+                               f"{'bias ' if wl.has_bias else ''}{wl.attrs} -> Y{list(yshape)} "
+                               f"{'channels-last' if wl.channels_last else 'NCHW'}",
+                   "kernel": kernel, "useful_macs": macs, "accumulate": "f32", "buffer_sets": rotate,
+                   "parity_max_rel_err": err},
+        "roofline": {"bound": bound, "achieved": round(achieved, 2), "peak": peak, "unit": unit,
+                     "frac": round(achieved / peak, 4), "traffic": traffic,
+                     "kernel_us": round(k_avg * 1e3, 2), "algorithmic_bytes": alg_bytes},
+        "cpu_baseline": base,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -174,6 +174,16 @@ int convtranspose_select_kernel(ct_dtype dtype, int nsp, int channels_last, cons
                                 const int64_t *output_shape, const int64_t *kernel_shape,
                                 int64_t group);
 
+/*
+ * Measurement hook: on the calling host thread, every later call records `before`
+ * (a hipEvent_t) on its stream just before launching its dominant kernel (the MFMA
+ * kernel, not the weight re-layout; the bandwidth kernel; the direct kernel) and `after`
+ * just after it, so hipEventElapsedTime gives that kernel's device time.  Both NULL
+ * turns it off.  The events stay owned by the caller.  Returns CT_OK, or CT_EINVAL if
+ * only one of the two is NULL.
+ */
+ct_status convtranspose_profile_events(void *before, void *after);
+
 /* Text of the last error on the calling host thread ("" after a successful call).
  * The pointer stays valid until the next library call on that thread. */
 const char *convtranspose_last_error(void);

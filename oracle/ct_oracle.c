@@ -38,6 +38,7 @@
  *
  * Build: gcc -O2 -fopenmp -shared -fPIC ct_oracle.c -o libctoracle.so
  */
+#include <omp.h>
 #include <stdint.h>
 #include <stdio.h>
 #include <stdlib.h>
@@ -189,6 +190,12 @@ static void or_decode(int64_t flat, const int64_t *dims, int n, int64_t *coord)
         coord[a] = flat % dims[a];
         flat /= dims[a];
     }
+}
+
+/* Threads the parallel loops below use (for reporting a timing's core count). */
+int oracle_threads(void)
+{
+    return omp_get_max_threads();
 }
 
 /* Resolved shape of Y = (N, M, O1..On) and the begin/end pads actually applied. */

@@ -58,11 +58,17 @@ def load(path: Optional[str] = None):
     lib.oracle_convtranspose_at.argtypes = [ctypes.c_int, i64p, f64p, i64p, f64p, f64p] + attrs + [
         i64p, ctypes.c_int64, f64p, ctypes.c_char_p, ctypes.c_int]
     for fn in ("oracle_output_shape", "oracle_useful_macs", "oracle_convtranspose_f64",
-               "oracle_convtranspose_at"):
+               "oracle_convtranspose_at", "oracle_threads"):
         getattr(lib, fn).restype = ctypes.c_int
+    lib.oracle_threads.argtypes = []
     if path is None:
         _lib = lib
     return lib
+
+
+def threads(lib=None) -> int:
+    """OpenMP threads the oracle's loops run on."""
+    return int((lib or load()).oracle_threads())
 
 
 def _i64(v: Optional[Sequence[int]]):

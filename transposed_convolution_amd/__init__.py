@@ -20,7 +20,7 @@ from typing import Optional, Sequence, Tuple
 import torch  # first: the library then binds to the HIP runtime torch has loaded
 
 __all__ = [
-    "ConvTransposeError", "convtranspose_nd", "convtranspose_output_shape",
+    "ConvTransposeError", "ConvTransposePlan", "convtranspose_nd", "convtranspose_profile_events", "convtranspose_output_shape",
     "convtranspose_useful_macs", "convtranspose_select_kernel", "convtranspose_last_error",
     "convtranspose_kernel_name", "library_path", "load_library", "channels_last_empty",
     "to_channels_last", "KERNELS",
@@ -76,6 +76,8 @@ def load_library():
     lib.convtranspose_last_error.argtypes = []
     lib.convtranspose_kernel_name.restype = ctypes.c_char_p
     lib.convtranspose_kernel_name.argtypes = [ctypes.c_int]
+    lib.convtranspose_profile_events.argtypes = [vp, vp]
+    lib.convtranspose_profile_events.restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -209,6 +211,84 @@ def convtranspose_select_kernel(x, w, bias=None, *, channels_last=False, **attrs
     return convtranspose_kernel_name(k)
 
 
+class ConvTransposePlan:
+    """One ConvTranspose with its arguments resolved and marshalled once.
+
+    Construction validates the tensors, resolves Y's shape, allocates Y (unless ``out``
+    is given) and the implicit-GEMM scratch, and builds the C argument list; each call
+    then enqueues the operation on ``stream`` (default: torch's current stream of x's
+    device at construction) with a single C call.  Repeated calls reuse Y and the
+    scratch, so they must be ordered on one stream.
+    """
+
+    def __init__(self, x: torch.Tensor, w: torch.Tensor, bias: Optional[torch.Tensor] = None, *,
+                 auto_pad: str = "NOTSET", strides=None, dilations=None, pads=None,
+                 output_padding=None, output_shape=None, kernel_shape=None, group: int = 1,
+                 channels_last: bool = False, out: Optional[torch.Tensor] = None,
+                 kernel: str = "auto", stream: Optional[torch.cuda.Stream] = None):
+        lib = load_library()
+        if x.dtype not in _DTYPES:
+            raise ConvTransposeError(3, f"dtype {x.dtype} is not served (float32, float16)")
+        if x.dim() < 3 or x.dim() > 5:
+            raise ConvTransposeError(1, "x must have rank 3, 4 or 5")
+        dev = x.device
+        _check_tensor("x", x, dev, x.dtype)
+        _check_tensor("w", w, dev, x.dtype)
+        if w.dim() != x.dim():
+            raise ConvTransposeError(1, "W must have the same rank as X")
+        if bias is not None:
+            _check_tensor("bias", bias, dev, x.dtype)
+            if bias.dim() != 1 or not bias.is_contiguous():
+                raise ConvTransposeError(1, "bias must be a dense 1-D tensor")
+            if bias.shape[0] != w.shape[1] * int(group):
+                raise ConvTransposeError(1, "bias length must equal M = W.shape[1] * group")
+        if not _dense(x, channels_last):
+            raise ConvTransposeError(1, "x is not dense in the requested layout")
+        if not w.is_contiguous():
+            raise ConvTransposeError(1, "w must be contiguous")
+        if kernel not in KERNELS:
+            raise ConvTransposeError(1, f"unknown kernel {kernel!r}")
+        attrs = dict(auto_pad=auto_pad, strides=strides, dilations=dilations, pads=pads,
+                     output_padding=output_padding, output_shape=output_shape,
+                     kernel_shape=kernel_shape, group=group)
+        yshape, _ = convtranspose_output_shape(tuple(x.shape), tuple(w.shape), **attrs)
+        if out is None:
+            out = (channels_last_empty(yshape, x.dtype, dev) if channels_last
+                   else torch.empty(yshape, dtype=x.dtype, device=dev))
+        else:
+            _check_tensor("out", out, dev, x.dtype)
+            if tuple(out.shape) != tuple(yshape):
+                raise ConvTransposeError(2, f"out has shape {tuple(out.shape)}, expected {yshape}")
+            if not _dense(out, channels_last):
+                raise ConvTransposeError(1, "out is not dense in the requested layout")
+        nsp, xp, xs, wp, ws, bp, yp, at = _call_args(x, w, bias, out, attrs)
+        nbytes = ctypes.c_size_t(0)
+        st = lib.convtranspose_workspace_size(KERNELS[kernel], _DTYPES[x.dtype], nsp, int(channels_last), xp,
+                                              xs, ws, *at, ctypes.byref(nbytes))
+        if st:
+            _raise(st)
+        self.stream = stream if stream is not None else torch.cuda.current_stream(dev)
+        self.scratch = None
+        if nbytes.value:
+            with torch.cuda.stream(self.stream):
+                self.scratch = torch.empty(nbytes.value, dtype=torch.uint8, device=dev)
+        self.out = out
+        self.device = dev
+        self._keep = (x, w, bias)  # the pointers below stay valid while the plan lives
+        self._fn = lib.convtranspose_nd_with_kernel
+        self._args = (KERNELS[kernel], _DTYPES[x.dtype], nsp, int(channels_last), xp, xs, wp, ws, bp, yp,
+                      _i64(yshape), *at,
+                      ctypes.c_void_p(self.scratch.data_ptr()) if self.scratch is not None else None,
+                      nbytes.value, ctypes.c_void_p(self.stream.cuda_stream))
+
+    def __call__(self) -> torch.Tensor:
+        with torch.cuda.device(self.device):
+            st = self._fn(*self._args)
+        if st:
+            _raise(st)
+        return self.out
+
+
 def convtranspose_nd(x: torch.Tensor, w: torch.Tensor, bias: Optional[torch.Tensor] = None, *,
                      auto_pad: str = "NOTSET", strides=None, dilations=None, pads=None,
                      output_padding=None, output_shape=None, kernel_shape=None, group: int = 1,
@@ -222,58 +302,24 @@ def convtranspose_nd(x: torch.Tensor, w: torch.Tensor, bias: Optional[torch.Tens
     w: (C, M/group, k1..kn) dense.  bias: (M,) or None.  Y is allocated (or ``out`` is
     used) with the same layout convention as x.  ``kernel`` forces a kernel family.
     """
+    return ConvTransposePlan(x, w, bias, auto_pad=auto_pad, strides=strides, dilations=dilations,
+                             pads=pads, output_padding=output_padding, output_shape=output_shape,
+                             kernel_shape=kernel_shape, group=group, channels_last=channels_last,
+                             out=out, kernel=kernel, stream=stream)()
+
+
+def convtranspose_profile_events(before: Optional[torch.cuda.Event], after: Optional[torch.cuda.Event]):
+    """Have later calls on this thread record ``before``/``after`` around their dominant
+    kernel (timing events created with ``enable_timing=True``); None, None turns it off."""
     lib = load_library()
-    if x.dtype not in _DTYPES:
-        raise ConvTransposeError(3, f"dtype {x.dtype} is not served (float32, float16)")
-    if x.dim() < 3 or x.dim() > 5:
-        raise ConvTransposeError(1, "x must have rank 3, 4 or 5")
-    dev = x.device
-    _check_tensor("x", x, dev, x.dtype)
-    _check_tensor("w", w, dev, x.dtype)
-    if w.dim() != x.dim():
-        raise ConvTransposeError(1, "W must have the same rank as X")
-    if bias is not None:
-        _check_tensor("bias", bias, dev, x.dtype)
-        if bias.dim() != 1 or not bias.is_contiguous():
-            raise ConvTransposeError(1, "bias must be a dense 1-D tensor")
-        if bias.shape[0] != w.shape[1] * int(group):
-            raise ConvTransposeError(1, "bias length must equal M = W.shape[1] * group")
-    if not _dense(x, channels_last):
-        raise ConvTransposeError(1, "x is not dense in the requested layout")
-    if not w.is_contiguous():
-        raise ConvTransposeError(1, "w must be contiguous")
-    attrs = dict(auto_pad=auto_pad, strides=strides, dilations=dilations, pads=pads,
-                 output_padding=output_padding, output_shape=output_shape,
-                 kernel_shape=kernel_shape, group=group)
-    yshape, _ = convtranspose_output_shape(tuple(x.shape), tuple(w.shape), **attrs)
-    if out is None:
-        out = (channels_last_empty(yshape, x.dtype, dev) if channels_last
-               else torch.empty(yshape, dtype=x.dtype, device=dev))
-    else:
-        _check_tensor("out", out, dev, x.dtype)
-        if tuple(out.shape) != tuple(yshape):
-            raise ConvTransposeError(2, f"out has shape {tuple(out.shape)}, expected {yshape}")
-        if not _dense(out, channels_last):
-            raise ConvTransposeError(1, "out is not dense in the requested layout")
-    if kernel not in KERNELS:
-        raise ConvTransposeError(1, f"unknown kernel {kernel!r}")
-    nsp, xp, xs, wp, ws, bp, yp, at = _call_args(x, w, bias, out, attrs)
-    nbytes = ctypes.c_size_t(0)
-    st = lib.convtranspose_workspace_size(KERNELS[kernel], _DTYPES[x.dtype], nsp, int(channels_last), xp, xs,
-                                          ws, *at, ctypes.byref(nbytes))
+    handles = []
+    for ev in (before, after):
+        if ev is None:
+            handles.append(None)
+            continue
+        if not ev.cuda_event:
+            ev.record()  # torch creates the HIP event on first record
+        handles.append(ctypes.c_void_p(ev.cuda_event))
+    st = lib.convtranspose_profile_events(*handles)
     if st:
         _raise(st)
-    with torch.cuda.device(dev):
-        s = stream if stream is not None else torch.cuda.current_stream(dev)
-        # scratch from torch's caching allocator; stream order keeps it valid for the call
-        scratch = None
-        if nbytes.value:
-            with torch.cuda.stream(s):
-                scratch = torch.empty(nbytes.value, dtype=torch.uint8, device=dev)
-        st = lib.convtranspose_nd_with_kernel(KERNELS[kernel], _DTYPES[x.dtype], nsp, int(channels_last),
-                                              xp, xs, wp, ws, bp, yp, _i64(yshape), *at,
-                                              ctypes.c_void_p(scratch.data_ptr()) if scratch is not None
-                                              else None, nbytes.value, ctypes.c_void_p(s.cuda_stream))
-    if st:
-        _raise(st)
-    return out

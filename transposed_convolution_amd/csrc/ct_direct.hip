@@ -118,12 +118,14 @@ ct_status launch_t(const Geom &g, bool cl, const void *x, const void *w, const v
     const T *wt = static_cast<const T *>(w);
     const T *bt = static_cast<const T *>(bias);
     T *yt = static_cast<T *>(y);
+    mark_before(st);
     if (cl)
         hipLaunchKernelGGL((direct_kernel<T, true>), dim3(unsigned(blocks)), dim3(block), 0, st, xt, wt,
                            bt, yt, p);
     else
         hipLaunchKernelGGL((direct_kernel<T, false>), dim3(unsigned(blocks)), dim3(block), 0, st, xt,
                            wt, bt, yt, p);
+    mark_after(st);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) {
         *err = std::string("direct kernel launch failed: ") + hipGetErrorString(e);

@@ -159,6 +159,12 @@ bool axis_phase(const Geom &g, int a, int r, AxisPhase *ph)
     return true;
 }
 
+ProfileEvents &profile_events()
+{
+    thread_local ProfileEvents ev;
+    return ev;
+}
+
 }  // namespace ct
 
 // ------------------------------------------------------------------------------------
@@ -389,6 +395,15 @@ ct_status convtranspose_nd(ct_dtype dtype, int nsp, int channels_last, const voi
                                         w_shape, bias, y, y_shape, auto_pad, strides, dilations,
                                         pads, output_padding, output_shape, kernel_shape, group,
                                         nullptr, 0, stream);
+}
+
+ct_status convtranspose_profile_events(void *before, void *after)
+{
+    t_error.clear();
+    if ((before == nullptr) != (after == nullptr)) return fail(CT_EINVAL, "give both events or neither");
+    ct::profile_events().before = static_cast<hipEvent_t>(before);
+    ct::profile_events().after = static_cast<hipEvent_t>(after);
+    return CT_OK;
 }
 
 const char *convtranspose_last_error(void) { return t_error.c_str(); }

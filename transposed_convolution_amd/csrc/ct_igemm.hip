@@ -622,6 +622,7 @@ ct_status launch_igemm(const Geom &g, ct_dtype, bool cl, const void *x, const vo
     const _Float16 *bt = static_cast<const _Float16 *>(bias);
     _Float16 *yt = static_cast<_Float16 *>(y);
     const Config c = pl.cfg;
+    mark_before(st);
     if (c.waves_m == 2) {
         if (cl) launch_cfg<true, 2, 4, 4, 1, 8>(pl.a, xt, wpk, bt, yt, st);
         else launch_cfg<false, 2, 4, 4, 1, 8>(pl.a, xt, wpk, bt, yt, st);
@@ -629,6 +630,7 @@ ct_status launch_igemm(const Geom &g, ct_dtype, bool cl, const void *x, const vo
         if (cl) launch_cfg<true, 1, 2, 4, 2, 12>(pl.a, xt, wpk, bt, yt, st);
         else launch_cfg<false, 1, 2, 4, 2, 12>(pl.a, xt, wpk, bt, yt, st);
     }
+    mark_after(st);
     hipError_t e = hipGetLastError();
     if (owned) {
         const hipError_t f = hipFreeAsync(wsp, st);

@@ -60,6 +60,21 @@ struct AxisPhase {
 // Fills phase r of axis a; returns false when the phase has more than kMaxPhaseTaps taps.
 bool axis_phase(const Geom &g, int a, int r, AxisPhase *ph);
 
+// Events the caller asked to have recorded around the dominant kernel of each call on
+// this host thread (both null: none).
+struct ProfileEvents {
+    hipEvent_t before = nullptr, after = nullptr;
+};
+ProfileEvents &profile_events();
+inline void mark_before(hipStream_t st)
+{
+    if (profile_events().before) (void)hipEventRecord(profile_events().before, st);
+}
+inline void mark_after(hipStream_t st)
+{
+    if (profile_events().after) (void)hipEventRecord(profile_events().after, st);
+}
+
 // Launchers (one per kernel family); each returns CT_OK or CT_EDEVICE (message in err).
 ct_status launch_direct(const Geom &g, ct_dtype dt, bool cl, const void *x, const void *w,
                         const void *bias, void *y, hipStream_t st, std::string *err);
