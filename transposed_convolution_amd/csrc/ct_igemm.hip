@@ -47,7 +47,6 @@ constexpr int kMaxRes = 8;               // largest stride handled per axis
 constexpr int kMaxTap = 8;               // largest tap count per residue and axis
 constexpr int kMaxPh = 64;               // largest number of phases
 constexpr int kHaloBytes = 56 * 1024;    // one halo buffer
-constexpr int kThreads = 256;
 
 struct IgArgs {
     int N, C, M, Cg, Mg, Cgp, Mgp, T, G;
@@ -56,9 +55,13 @@ struct IgArgs {
     int nphase, interleave, nblocks;
     int ph_start[kMaxPh + 1];
     unsigned char ph_r[kMaxPh][3];
+    // Taps of residue r on axis a form an arithmetic progression:
+    //   k = tk0[a][r] + u * kstep[a],  beta = tb0[a][r] - u * bstep[a],  u in [0, ntap[a][r])
+    // with kstep = s / gcd(s, d) and bstep = d / gcd(s, d).
     signed char ntap[3][kMaxRes];
-    short tk[3][kMaxRes][kMaxTap];
-    short tb[3][kMaxRes][kMaxTap];
+    short tk0[3][kMaxRes];
+    short tb0[3][kMaxRes];
+    short kstep[3], bstep[3];
 };
 
 __device__ __forceinline__ int floor_div8(int v) { return v >= 0 ? v / 8 : -((-v + 7) / 8); }
@@ -78,22 +81,28 @@ struct Tile {
     bool seg;            // tile lies inside one row
 };
 
-// NCH_ITEMS: NCHW halo items (8 channels x 8 columns) per thread; NHWC_VECS: NHWC halo
-// 16-byte vectors per thread.  Together with the tile they bound the halo a block stages.
-template <bool CL, int WAVES_M, int WM, int WN, int NCH_ITEMS, int NHWC_VECS>
-__global__ __launch_bounds__(kThreads, 1) void igemm_kernel(const _Float16 *__restrict__ x,
+// WAVES wave64s per block, WAVES_M of them along output channels; each wave owns
+// WM x WN MFMA tiles of 32 x 32.  NCH_ITEMS: NCHW halo items (8 channels x 8 columns)
+// per thread; NHWC_VECS: NHWC halo 16-byte vectors per thread.  Together with the tile
+// they bound the halo a block stages.
+template <bool CL, int WAVES, int WAVES_M, int WM, int WN, int NCH_ITEMS, int NHWC_VECS>
+__global__ __launch_bounds__(WAVES * 64, 1) void igemm_kernel(const _Float16 *__restrict__ x,
                                                             const _Float16 *__restrict__ wp,
                                                             const _Float16 *__restrict__ bias,
                                                             _Float16 *__restrict__ y, IgArgs p)
 {
-    constexpr int WAVES_N = 4 / WAVES_M;
+    constexpr int kThreads = WAVES * 64;
+    constexpr int WAVES_N = WAVES / WAVES_M;
     constexpr int BM = WAVES_M * WM * 32;
     constexpr int BN = WAVES_N * WN * 32;
-    constexpr int WVEC = BM * 4 / kThreads;  // weight-tile 16-byte vectors per thread
-    static_assert(BM * 4 % kThreads == 0, "weight tile must split evenly");
+    // weight-tile 16-byte vectors per thread (threads past the tile load a valid
+    // address and store into the sink)
+    constexpr int WVEC = (BM * 4 + kThreads - 1) / kThreads;
 
     __shared__ __attribute__((aligned(16))) unsigned char lds_w[2][BM * kRow];
     __shared__ __attribute__((aligned(16))) unsigned char lds_h[2][kHaloBytes];
+    // per-lane sink for halo stores that have no destination (keeps the stores branch-free)
+    __shared__ __attribute__((aligned(16))) unsigned char lds_sink[64 * 16];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -113,6 +122,9 @@ __global__ __launch_bounds__(kThreads, 1) void igemm_kernel(const _Float16 *__re
         local = v - p.ph_start[ph];
     }
     const int r0 = p.ph_r[ph][0], r1 = p.ph_r[ph][1], r2 = p.ph_r[ph][2];
+    const int k00 = p.tk0[0][r0], k01 = p.tk0[1][r1], k02 = p.tk0[2][r2];
+    const int ks0 = p.kstep[0], ks1 = p.kstep[1], ks2 = p.kstep[2];
+    const int b00 = p.tb0[0][r0], bs0 = p.bstep[0], bs1 = p.bstep[1], bs2 = p.bstep[2];
     const int J0 = (p.O[0] - r0 + p.s[0] - 1) / p.s[0];
     const int J1 = (p.O[1] - r1 + p.s[1] - 1) / p.s[1];
     const int J2 = (p.O[2] - r2 + p.s[2] - 1) / p.s[2];
@@ -132,8 +144,8 @@ __global__ __launch_bounds__(kThreads, 1) void igemm_kernel(const _Float16 *__re
     const int g = rest % p.G;
     const int mt = rest / p.G;
 
-    const int b1min = nt1 ? p.tb[1][r1][nt1 - 1] : 0, b1max = nt1 ? p.tb[1][r1][0] : 0;
-    const int b2min = nt2 ? p.tb[2][r2][nt2 - 1] : 0, b2max = nt2 ? p.tb[2][r2][0] : 0;
+    const int b1max = p.tb0[1][r1], b1min = nt1 ? b1max - (nt1 - 1) * bs1 : b1max;
+    const int b2max = p.tb0[2][r2], b2min = nt2 ? b2max - (nt2 - 1) * bs2 : b2max;
     if (tl.seg) {
         tl.row_lo = pt / tpr;
         tl.col_lo = (pt % tpr) * BN;
@@ -157,7 +169,7 @@ __global__ __launch_bounds__(kThreads, 1) void igemm_kernel(const _Float16 *__re
     {
         int f = nt0, e = 0;
         for (int t = 0; t < nt0; ++t) {
-            const int i0 = j0 + p.tb[0][r0][t];
+            const int i0 = j0 + b00 - t * bs0;
             if (i0 >= 0 && i0 < p.L[0]) {
                 if (f == nt0) f = t;
                 e = t + 1;
@@ -209,13 +221,13 @@ __global__ __launch_bounds__(kThreads, 1) void igemm_kernel(const _Float16 *__re
     };
     const size_t wrow0 = size_t(g) * p.T;
     auto load_w = [&](const StepIdx &q, u32x4 *reg) {
-        const int tflat = (p.tk[0][r0][q.t0] * p.K[1] + p.tk[1][r1][q.t1]) * p.K[2] + p.tk[2][r2][q.t2];
+        const int tflat = ((k00 + q.t0 * ks0) * p.K[1] + (k01 + q.t1 * ks1)) * p.K[2] + (k02 + q.t2 * ks2);
         const size_t row0 = (wrow0 + tflat) * p.Mgp + size_t(mt) * BM;
         const u32x4 *src = reinterpret_cast<const u32x4 *>(wp + row0 * p.Cgp + size_t(q.chunk) * kCC);
         const int stride_vec = p.Cgp / 8;  // 16-byte vectors per Wp row
 #pragma unroll
         for (int k = 0; k < WVEC; ++k) {
-            const int u = tid + k * kThreads;
+            const int u = min(tid + k * kThreads, BM * 4 - 1);
             reg[k] = src[(u >> 2) * stride_vec + (u & 3)];
         }
     };
@@ -223,40 +235,42 @@ __global__ __launch_bounds__(kThreads, 1) void igemm_kernel(const _Float16 *__re
 #pragma unroll
         for (int k = 0; k < WVEC; ++k) {
             const int u = tid + k * kThreads;
-            *reinterpret_cast<u32x4 *>(&lds_w[buf][(u >> 2) * kRow + (u & 3) * 16]) = reg[k];
+            unsigned char *dst = u < BM * 4 ? &lds_w[buf][(u >> 2) * kRow + (u & 3) * 16] : lds_sink + lane * 16;
+            *reinterpret_cast<u32x4 *>(dst) = reg[k];
         }
     };
 
-    // Halo of group gi: channel chunk and axis-0 tap.
+    // Halo of one (channel chunk, axis-0 tap) group.  It is fetched during the first
+    // step of the previous group and stored into the other halo buffer (free for that
+    // whole group) at the end of that step.  Loads read a clamped, always valid address
+    // and a bit mask records which hold real input; zeros are substituted when storing,
+    // and every store has a destination (a per-lane sink for items past the halo), so
+    // no loaded value is merged or consumed before the MFMAs of the step are issued.
     constexpr int HREG = CL ? NHWC_VECS : NCH_ITEMS * 8;
-    static_assert(HREG > 0, "halo registers");
-    auto load_halo = [&](int chunk, int t0, u32x4 *reg) {
-        const int i0 = j0 + p.tb[0][r0][t0];
+    static_assert(HREG > 0 && HREG <= 32, "halo registers");
+    const int va = floor_div8(i2o);
+    const int nvc = floor_div8(i2o + tl.HC + 7) - va;
+    const int halo_items = CL ? tl.HR * tl.HC * 4 : tl.HR * 4 * nvc;
+    auto load_halo = [&](int chunk, int t0, u32x4 *reg) -> unsigned {
+        const int i0 = j0 + b00 - t0 * bs0;
         const int cbase = chunk * kCC;  // channel offset inside the group
+        unsigned valid = 0;
         if (CL) {
-            const int total = tl.HR * tl.HC * 4;
+            const _Float16 *xb = x + (size_t(n) * L0 + i0) * L1 * L2 * p.C + size_t(g) * p.Cg + cbase;
 #pragma unroll
             for (int k = 0; k < NHWC_VECS; ++k) {
                 const int u = tid + k * kThreads;
-                u32x4 val = {0u, 0u, 0u, 0u};
-                if (u < total) {
-                    const int pix = u >> 2, ch = u & 3;
-                    const int hr = pix / tl.HC, hc = pix - hr * tl.HC;
-                    const int i1 = i1o + hr, i2 = i2o + hc;
-                    const int c = cbase + ch * 8;
-                    if (i1 >= 0 && i1 < L1 && i2 >= 0 && i2 < L2 && c < p.Cg) {
-                        const size_t off = (((size_t(n) * L0 + i0) * L1 + i1) * L2 + i2) * p.C +
-                                           size_t(g) * p.Cg + c;
-                        val = *reinterpret_cast<const u32x4 *>(x + off);
-                    }
-                }
-                reg[k] = val;
+                const int pix = u >> 2, ch = u & 3;
+                const int hr = pix / tl.HC, hc = pix - hr * tl.HC;
+                const int i1 = i1o + hr, i2 = i2o + hc;
+                const bool ok = u < halo_items && i1 >= 0 && i1 < L1 && i2 >= 0 && i2 < L2 && cbase + ch * 8 < p.Cg;
+                const size_t off = ok ? (size_t(i1) * L2 + i2) * p.C + ch * 8 : 0;
+                reg[k] = *reinterpret_cast<const u32x4 *>((ok ? xb : x) + off);
+                valid |= unsigned(ok) << k;
             }
         } else {
             // items: (halo row, channel octet, aligned 8-column vector)
-            const int va = floor_div8(i2o);
-            const int nvc = floor_div8(i2o + tl.HC + 7) - va;
-            const int total = tl.HR * 4 * nvc;
+            const _Float16 *xb = x + (size_t(n) * p.C + size_t(g) * p.Cg + cbase) * plane_in + size_t(i0) * L1 * L2;
 #pragma unroll
             for (int it = 0; it < NCH_ITEMS; ++it) {
                 const int u = tid + it * kThreads;
@@ -265,38 +279,32 @@ __global__ __launch_bounds__(kThreads, 1) void igemm_kernel(const _Float16 *__re
                 const int oct = rem2 / nvc, vc = rem2 - oct * nvc;
                 const int i1 = i1o + hr;
                 const int i2 = (va + vc) * 8;
-                const int c = cbase + oct * 8;
-                const bool ok = u < total && i1 >= 0 && i1 < L1 && i2 >= 0 && i2 < L2 && c < p.Cg;
-                const size_t base =
-                    ok ? ((size_t(n) * p.C + size_t(g) * p.Cg + c) * plane_in +
-                          (size_t(i0) * L1 + i1) * L2 + i2)
-                       : 0;
+                const bool ok = u < halo_items && i1 >= 0 && i1 < L1 && i2 >= 0 && i2 < L2 && cbase + oct * 8 < p.Cg;
+                const _Float16 *src = ok ? xb + size_t(oct * 8) * plane_in + size_t(i1) * L2 + i2 : x;
+                const size_t step = ok ? plane_in : 0;
 #pragma unroll
-                for (int k = 0; k < 8; ++k) {
-                    u32x4 val = {0u, 0u, 0u, 0u};
-                    if (ok) val = *reinterpret_cast<const u32x4 *>(x + base + size_t(k) * plane_in);
-                    reg[it * 8 + k] = val;
-                }
+                for (int k = 0; k < 8; ++k) reg[it * 8 + k] = *reinterpret_cast<const u32x4 *>(src + k * step);
+                valid |= unsigned(ok) << it;
             }
         }
+        return valid;
     };
-    auto store_halo = [&](int buf, const u32x4 *reg) {
+    auto store_halo = [&](int buf, const u32x4 *reg, unsigned valid) {
+        const u32x4 zero = {0u, 0u, 0u, 0u};
+        unsigned char *const sink = lds_sink + lane * 16;
         if (CL) {
-            const int total = tl.HR * tl.HC * 4;
 #pragma unroll
             for (int k = 0; k < NHWC_VECS; ++k) {
                 const int u = tid + k * kThreads;
-                if (u < total)
-                    *reinterpret_cast<u32x4 *>(&lds_h[buf][(u >> 2) * kRow + (u & 3) * 16]) = reg[k];
+                unsigned char *dst = u < halo_items ? &lds_h[buf][(u >> 2) * kRow + (u & 3) * 16] : sink;
+                *reinterpret_cast<u32x4 *>(dst) = ((valid >> k) & 1u) ? reg[k] : zero;
             }
         } else {
-            const int va = floor_div8(i2o);
-            const int nvc = floor_div8(i2o + tl.HC + 7) - va;
-            const int total = tl.HR * 4 * nvc;
 #pragma unroll
             for (int it = 0; it < NCH_ITEMS; ++it) {
                 const int u = tid + it * kThreads;
-                if (u >= total) continue;
+                const bool ok = (valid >> it) & 1u;
+                const bool here = u < halo_items;
                 const int hr = u / (4 * nvc);
                 const int rem2 = u - hr * 4 * nvc;
                 const int oct = rem2 / nvc, vc = rem2 - oct * nvc;
@@ -305,14 +313,16 @@ __global__ __launch_bounds__(kThreads, 1) void igemm_kernel(const _Float16 *__re
 #pragma unroll
                 for (int pp = 0; pp < 8; ++pp) {
                     const int hc = (va + vc) * 8 + pp - i2o;
-                    if (hc < 0 || hc >= tl.HC) continue;
                     u32x4 o;
 #pragma unroll
                     for (int jj = 0; jj < 4; ++jj) {
                         const unsigned lo = in[2 * jj][pp >> 1], hi = in[2 * jj + 1][pp >> 1];
                         o[jj] = (pp & 1) ? ((lo >> 16) | (hi & 0xffff0000u)) : ((lo & 0xffffu) | (hi << 16));
                     }
-                    *reinterpret_cast<u32x4 *>(&lds_h[buf][(hr * tl.HC + hc) * kRow + oct * 16]) = o;
+                    unsigned char *dst = (here && hc >= 0 && hc < tl.HC)
+                                             ? &lds_h[buf][(hr * tl.HC + hc) * kRow + oct * 16]
+                                             : sink;
+                    *reinterpret_cast<u32x4 *>(dst) = ok ? o : zero;
                 }
             }
         }
@@ -323,30 +333,34 @@ __global__ __launch_bounds__(kThreads, 1) void igemm_kernel(const _Float16 *__re
         u32x4 wreg[WVEC];
         u32x4 hreg[HREG];
         StepIdx cur = {0, t0_first, 0, 0};
-        load_halo(0, t0_first, hreg);
+        {
+            const unsigned v0 = load_halo(0, t0_first, hreg);
+            store_halo(0, hreg, v0);
+        }
         load_w(cur, wreg);
-        store_halo(0, hreg);
         store_w(0, wreg);
         __syncthreads();
         StepIdx nxt = cur;
         advance(nxt);
         int hbuf = 0;
         for (int s = 0; s < nsteps; ++s) {
-            const bool first_in_group = cur.t1 == 0 && cur.t2 == 0;
-            // the halo of the next (chunk, t0) group is fetched during the first step of this one
-            StepIdx ng = cur;
-            bool prefetch_halo = false;
-            if (first_in_group) {
+            // the halo of the next group is fetched during the first step of this one
+            bool fetch = false;
+            unsigned hvalid = 0;
+            if (cur.t1 == 0 && cur.t2 == 0) {
+                StepIdx ng = cur;
                 ng.t1 = nt1 - 1;
                 ng.t2 = nt2 - 1;
                 advance(ng);
-                prefetch_halo = ng.chunk < p.nchunk;
-                if (prefetch_halo) load_halo(ng.chunk, ng.t0, hreg);
+                fetch = ng.chunk < p.nchunk;
+                if (fetch) hvalid = load_halo(ng.chunk, ng.t0, hreg);
             }
-            const bool more = s + 1 < nsteps;
-            if (more) load_w(nxt, wreg);
+            load_w(s + 1 < nsteps ? nxt : cur, wreg);  // the last step reloads a valid tile
+            // issue the prefetch loads here, ahead of the MFMAs (no later sinking)
+            asm volatile("" ::: "memory");
 
-            const int toff = ((p.tb[1][r1][cur.t1] - b1min) * tl.HC + (p.tb[2][r2][cur.t2] - b2min)) * kRow;
+            // tap shift inside the halo: (beta - beta_min) rows and columns
+            const int toff = ((nt1 - 1 - cur.t1) * bs1 * tl.HC + (nt2 - 1 - cur.t2) * bs2) * kRow;
             const unsigned char *hb = lds_h[hbuf] + toff;
             const unsigned char *wb = lds_w[s & 1] + (wm * WM * 32 + (lane & 31)) * kRow + (lane >> 5) * 16;
 #pragma unroll
@@ -365,8 +379,8 @@ __global__ __launch_bounds__(kThreads, 1) void igemm_kernel(const _Float16 *__re
                         acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[i], b[j], acc[i][j], 0, 0, 0);
             }
 
-            if (prefetch_halo) store_halo(hbuf ^ 1, hreg);
-            if (more) store_w((s + 1) & 1, wreg);
+            if (fetch) store_halo(hbuf ^ 1, hreg, hvalid);
+            store_w((s + 1) & 1, wreg);
             __syncthreads();
             cur = nxt;
             advance(nxt);
@@ -438,15 +452,18 @@ __global__ __launch_bounds__(256) void pack_w_kernel(const _Float16 *__restrict_
 
 // ---------------- host-side planning ----------------
 struct Config {
-    int waves_m, wm, wn, nch_items, nhwc_vecs;
+    int waves, waves_m, wm, wn, nch_items, nhwc_vecs;
+    int threads() const { return waves * 64; }
     int bm() const { return waves_m * wm * 32; }
-    int bn() const { return (4 / waves_m) * wn * 32; }
+    int bn() const { return (waves / waves_m) * wn * 32; }
 };
 
+// Both configurations run 8 waves (two per SIMD) so that one wave's loads and index
+// arithmetic overlap the other's MFMAs.
 Config pick_config(const Geom &g)
 {
-    if (g.Mg > 64) return Config{2, 4, 4, 1, 8};  // 256 x 256 block, 128 x 128 per wave
-    return Config{1, 2, 4, 2, 12};                // 64 x 512 block, 64 x 128 per wave
+    if (g.Mg > 64) return Config{8, 2, 4, 2, 1, 6};  // 256 x 256 block, 128 x 64 per wave
+    return Config{8, 1, 2, 2, 1, 6};                 // 64 x 512 block, 64 x 64 per wave
 }
 
 struct Plan {
@@ -471,14 +488,20 @@ bool make_plan(const Geom &g, Plan *pl, std::string *why)
         a.O[t] = int(g.O[t]);
         a.s[t] = int(g.s[t]);
         a.K[t] = int(g.K[t]);
+        const int64_t gsd = std::__gcd(g.s[t], g.d[t]);
+        a.kstep[t] = short(g.s[t] / gsd);
+        a.bstep[t] = short(g.d[t] / gsd);
+        if (g.K[t] > 32767 || g.d[t] / gsd > 32767) return no("kernel or dilation too large");
         for (int r = 0; r < g.s[t]; ++r) {
             AxisPhase ph;
             if (!axis_phase(g, t, r, &ph) || ph.ntaps > kMaxTap) return no("more than 8 taps per phase");
             a.ntap[t][r] = (signed char)ph.ntaps;
-            for (int k = 0; k < ph.ntaps; ++k) {
-                a.tk[t][r][k] = short(ph.k[k]);
-                a.tb[t][r][k] = short(ph.beta[k]);
-            }
+            a.tk0[t][r] = short(ph.ntaps ? ph.k[0] : 0);
+            a.tb0[t][r] = short(ph.ntaps ? ph.beta[0] : 0);
+            for (int k = 0; k < ph.ntaps; ++k)  // the progression the kernel walks
+                if (ph.k[k] != ph.k[0] + k * a.kstep[t] || ph.beta[k] != ph.beta[0] - k * a.bstep[t])
+                    return no("internal: taps are not an arithmetic progression");
+            if (ph.ntaps && (ph.beta[0] > 32767 || ph.beta[0] < -32767)) return no("pads too large");
         }
     }
     a.N = int(g.N);
@@ -520,14 +543,14 @@ bool make_plan(const Geom &g, Plan *pl, std::string *why)
                 pi.blocks = int(blocks);
                 // halo capacity check (largest tile of this phase)
                 const int n1 = a.ntap[1][r1], n2 = a.ntap[2][r2];
-                const int e1 = n1 ? a.tb[1][r1][0] - a.tb[1][r1][n1 - 1] : 0;
-                const int e2 = n2 ? a.tb[2][r2][0] - a.tb[2][r2][n2 - 1] : 0;
+                const int e1 = n1 ? (n1 - 1) * a.bstep[1] : 0;
+                const int e2 = n2 ? (n2 - 1) * a.bstep[2] : 0;
                 const int HR = seg ? 1 + e1 : std::min<int>(J1, (BN + J2 - 1) / J2 + 1) + e1;
                 const int HC = seg ? BN + e2 : J2 + e2;
                 if ((long long)HR * HC * kRow > kHaloBytes) return no("input halo exceeds LDS");
-                if ((long long)HR * HC * 4 > (long long)cfg.nhwc_vecs * kThreads) return no("halo too large");
+                if ((long long)HR * HC * 4 > (long long)cfg.nhwc_vecs * cfg.threads()) return no("halo too large");
                 const int nvc = (HC + 7) / 8 + 1;
-                if ((long long)HR * 4 * nvc > (long long)cfg.nch_items * kThreads) return no("halo too large");
+                if ((long long)HR * 4 * nvc > (long long)cfg.nch_items * cfg.threads()) return no("halo too large");
             }
     std::stable_sort(list, list + nph, [](const PhaseInfo &x, const PhaseInfo &y) { return x.taps > y.taps; });
     a.nphase = nph;
@@ -550,12 +573,12 @@ bool make_plan(const Geom &g, Plan *pl, std::string *why)
     return true;
 }
 
-template <bool CL, int WAVES_M, int WM, int WN, int NCH_ITEMS, int NHWC_VECS>
+template <bool CL, int WAVES, int WAVES_M, int WM, int WN, int NCH_ITEMS, int NHWC_VECS>
 void launch_cfg(const IgArgs &a, const _Float16 *x, const _Float16 *wp, const _Float16 *b, _Float16 *y,
                 hipStream_t st)
 {
-    hipLaunchKernelGGL((igemm_kernel<CL, WAVES_M, WM, WN, NCH_ITEMS, NHWC_VECS>), dim3(unsigned(a.nblocks)),
-                       dim3(kThreads), 0, st, x, wp, b, y, a);
+    hipLaunchKernelGGL((igemm_kernel<CL, WAVES, WAVES_M, WM, WN, NCH_ITEMS, NHWC_VECS>),
+                       dim3(unsigned(a.nblocks)), dim3(WAVES * 64), 0, st, x, wp, b, y, a);
 }
 
 }  // namespace
@@ -624,11 +647,11 @@ ct_status launch_igemm(const Geom &g, ct_dtype, bool cl, const void *x, const vo
     const Config c = pl.cfg;
     mark_before(st);
     if (c.waves_m == 2) {
-        if (cl) launch_cfg<true, 2, 4, 4, 1, 8>(pl.a, xt, wpk, bt, yt, st);
-        else launch_cfg<false, 2, 4, 4, 1, 8>(pl.a, xt, wpk, bt, yt, st);
+        if (cl) launch_cfg<true, 8, 2, 4, 2, 1, 6>(pl.a, xt, wpk, bt, yt, st);
+        else launch_cfg<false, 8, 2, 4, 2, 1, 6>(pl.a, xt, wpk, bt, yt, st);
     } else {
-        if (cl) launch_cfg<true, 1, 2, 4, 2, 12>(pl.a, xt, wpk, bt, yt, st);
-        else launch_cfg<false, 1, 2, 4, 2, 12>(pl.a, xt, wpk, bt, yt, st);
+        if (cl) launch_cfg<true, 8, 1, 2, 2, 1, 6>(pl.a, xt, wpk, bt, yt, st);
+        else launch_cfg<false, 8, 1, 2, 2, 1, 6>(pl.a, xt, wpk, bt, yt, st);
     }
     mark_after(st);
     hipError_t e = hipGetLastError();
