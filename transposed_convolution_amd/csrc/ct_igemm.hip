@@ -41,12 +41,12 @@ typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kCC = 32;                  // input channels per depth chunk
-constexpr int kRow = 80;                 // LDS bytes per staged row (32 halves + pad)
 constexpr int kMaxRes = 8;               // largest stride handled per axis
 constexpr int kMaxTap = 8;               // largest tap count per residue and axis
 constexpr int kMaxPh = 64;               // largest number of phases
-constexpr int kHaloBytes = 56 * 1024;    // one halo buffer
+constexpr int kThreads = 256;            // 4 wave64s, one per SIMD
+constexpr int kLdsBytes = 160 * 1024 - 2048;
+constexpr int kSinkBytes = 64 * 16;
 
 struct IgArgs {
     int N, C, M, Cg, Mg, Cgp, Mgp, T, G;
@@ -81,28 +81,41 @@ struct Tile {
     bool seg;            // tile lies inside one row
 };
 
-// WAVES wave64s per block, WAVES_M of them along output channels; each wave owns
-// WM x WN MFMA tiles of 32 x 32.  NCH_ITEMS: NCHW halo items (8 channels x 8 columns)
-// per thread; NHWC_VECS: NHWC halo 16-byte vectors per thread.  Together with the tile
-// they bound the halo a block stages.
-template <bool CL, int WAVES, int WAVES_M, int WM, int WN, int NCH_ITEMS, int NHWC_VECS>
-__global__ __launch_bounds__(WAVES * 64, 1) void igemm_kernel(const _Float16 *__restrict__ x,
-                                                            const _Float16 *__restrict__ wp,
+// One block = 4 wave64s; WAVES_M of them split the BM output channels, the others the
+// BN phase pixels; each wave owns WM x WN MFMA tiles of 32 x 32.  CC input channels form
+// one step (CC/16 MFMA k-steps of 16).  NCH_ITEMS: NCHW halo items (8 channels x 8
+// columns) per thread; NHWC_VECS: NHWC halo 16-byte vectors per thread.
+template <bool CL, int WAVES_M, int WM, int WN, int CC, int NCH_ITEMS, int NHWC_VECS>
+struct IgCfg {
+    static constexpr int WAVES_N = 4 / WAVES_M;
+    static constexpr int BM = WAVES_M * WM * 32;
+    static constexpr int BN = WAVES_N * WN * 32;
+    static constexpr int ROW = CC * 2 + 16;   // LDS bytes per staged row (data + 16 pad)
+    static constexpr int CHUNKS = CC / 8;     // 16-byte chunks per row
+    static constexpr int KSUB = CC / 16;      // MFMA k-steps per step
+    static constexpr int WVEC = BM * CHUNKS / kThreads;
+    static constexpr int HALO_BYTES = kLdsBytes - 2 * BM * ROW - kSinkBytes;
+    static_assert(BM * CHUNKS % kThreads == 0, "weight tile must split evenly");
+    static_assert(HALO_BYTES > 0, "LDS budget");
+};
+
+template <bool CL, int WAVES_M, int WM, int WN, int CC, int NCH_ITEMS, int NHWC_VECS>
+__global__ __launch_bounds__(kThreads, 1) void igemm_kernel(const _Float16 *x, const _Float16 *__restrict__ wp,
                                                             const _Float16 *__restrict__ bias,
                                                             _Float16 *__restrict__ y, IgArgs p)
 {
-    constexpr int kThreads = WAVES * 64;
-    constexpr int WAVES_N = WAVES / WAVES_M;
-    constexpr int BM = WAVES_M * WM * 32;
-    constexpr int BN = WAVES_N * WN * 32;
-    // weight-tile 16-byte vectors per thread (threads past the tile load a valid
-    // address and store into the sink)
-    constexpr int WVEC = (BM * 4 + kThreads - 1) / kThreads;
+    using Cfg = IgCfg<CL, WAVES_M, WM, WN, CC, NCH_ITEMS, NHWC_VECS>;
+    constexpr int WAVES_N = Cfg::WAVES_N, BM = Cfg::BM, BN = Cfg::BN, ROW = Cfg::ROW;
+    constexpr int CHUNKS = Cfg::CHUNKS, KSUB = Cfg::KSUB, WVEC = Cfg::WVEC;
+    (void)WAVES_N;
 
-    __shared__ __attribute__((aligned(16))) unsigned char lds_w[2][BM * kRow];
-    __shared__ __attribute__((aligned(16))) unsigned char lds_h[2][kHaloBytes];
-    // per-lane sink for halo stores that have no destination (keeps the stores branch-free)
-    __shared__ __attribute__((aligned(16))) unsigned char lds_sink[64 * 16];
+    // One LDS array: two weight-tile buffers, the halo buffer, and a per-lane sink for
+    // halo stores that have no destination (keeps those stores branch-free).  After the
+    // main loop the whole array holds the output tile.
+    __shared__ __attribute__((aligned(16))) unsigned char lds[kLdsBytes];
+    auto lds_w = [&](int buf) -> unsigned char * { return lds + buf * (BM * ROW); };
+    unsigned char *const lds_h = lds + 2 * BM * ROW;
+    unsigned char *const lds_sink = lds_h + Cfg::HALO_BYTES;
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -188,7 +201,7 @@ __global__ __launch_bounds__(WAVES * 64, 1) void igemm_kernel(const _Float16 *__
         if (q >= tl.q1) q = tl.q1 - 1;
         const int row = tl.seg ? tl.row_lo : q / J2;
         const int col = q - row * J2;
-        hoff[j] = ((row - tl.row_lo) * tl.HC + (col - tl.col_lo)) * kRow + (lane >> 5) * 16;
+        hoff[j] = ((row - tl.row_lo) * tl.HC + (col - tl.col_lo)) * ROW + (lane >> 5) * 16;
     }
 
     f32x16 acc[WM][WN];
@@ -199,11 +212,10 @@ __global__ __launch_bounds__(WAVES * 64, 1) void igemm_kernel(const _Float16 *__
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
-    // ---------------- loaders ----------------
     const int L0 = p.L[0], L1 = p.L[1], L2 = p.L[2];
     const size_t plane_in = size_t(L0) * L1 * L2;
 
-    // Step order: chunk, then axis-0 tap, then axis-1 tap, then axis-2 tap.
+    // ---------------- step order: chunk, axis-0 tap, axis-1 tap, axis-2 tap ----------------
     struct StepIdx {
         int chunk, t0, t1, t2;
     };
@@ -219,48 +231,49 @@ __global__ __launch_bounds__(WAVES * 64, 1) void igemm_kernel(const _Float16 *__
             }
         }
     };
+
+    // ---------------- weight tile: BM rows x CC channels of Wp ----------------
     const size_t wrow0 = size_t(g) * p.T;
     auto load_w = [&](const StepIdx &q, u32x4 *reg) {
         const int tflat = ((k00 + q.t0 * ks0) * p.K[1] + (k01 + q.t1 * ks1)) * p.K[2] + (k02 + q.t2 * ks2);
         const size_t row0 = (wrow0 + tflat) * p.Mgp + size_t(mt) * BM;
-        const u32x4 *src = reinterpret_cast<const u32x4 *>(wp + row0 * p.Cgp + size_t(q.chunk) * kCC);
+        const u32x4 *src = reinterpret_cast<const u32x4 *>(wp + row0 * p.Cgp + size_t(q.chunk) * CC);
         const int stride_vec = p.Cgp / 8;  // 16-byte vectors per Wp row
 #pragma unroll
         for (int k = 0; k < WVEC; ++k) {
-            const int u = min(tid + k * kThreads, BM * 4 - 1);
-            reg[k] = src[(u >> 2) * stride_vec + (u & 3)];
+            const int u = tid + k * kThreads;
+            reg[k] = src[(u / CHUNKS) * stride_vec + (u % CHUNKS)];
         }
     };
     auto store_w = [&](int buf, const u32x4 *reg) {
 #pragma unroll
         for (int k = 0; k < WVEC; ++k) {
             const int u = tid + k * kThreads;
-            unsigned char *dst = u < BM * 4 ? &lds_w[buf][(u >> 2) * kRow + (u & 3) * 16] : lds_sink + lane * 16;
-            *reinterpret_cast<u32x4 *>(dst) = reg[k];
+            *reinterpret_cast<u32x4 *>(&lds_w(buf)[(u / CHUNKS) * ROW + (u % CHUNKS) * 16]) = reg[k];
         }
     };
 
-    // Halo of one (channel chunk, axis-0 tap) group.  It is fetched during the first
-    // step of the previous group and stored into the other halo buffer (free for that
-    // whole group) at the end of that step.  Loads read a clamped, always valid address
-    // and a bit mask records which hold real input; zeros are substituted when storing,
-    // and every store has a destination (a per-lane sink for items past the halo), so
-    // no loaded value is merged or consumed before the MFMAs of the step are issued.
+    // ---------------- input halo of one (channel chunk, axis-0 tap) group ----------------
+    // Fetched into registers during the first step of the previous group and written to
+    // the (single) halo buffer between two barriers at the group boundary.  Loads read
+    // a clamped, always valid address; a bit mask records which hold real input and
+    // zeros are substituted when storing; every store has a destination (a per-lane sink
+    // for items past the halo).
     constexpr int HREG = CL ? NHWC_VECS : NCH_ITEMS * 8;
     static_assert(HREG > 0 && HREG <= 32, "halo registers");
     const int va = floor_div8(i2o);
     const int nvc = floor_div8(i2o + tl.HC + 7) - va;
-    const int halo_items = CL ? tl.HR * tl.HC * 4 : tl.HR * 4 * nvc;
+    const int halo_items = CL ? tl.HR * tl.HC * CHUNKS : tl.HR * nvc * CHUNKS;
     auto load_halo = [&](int chunk, int t0, u32x4 *reg) -> unsigned {
         const int i0 = j0 + b00 - t0 * bs0;
-        const int cbase = chunk * kCC;  // channel offset inside the group
+        const int cbase = chunk * CC;  // channel offset inside the group
         unsigned valid = 0;
         if (CL) {
             const _Float16 *xb = x + (size_t(n) * L0 + i0) * L1 * L2 * p.C + size_t(g) * p.Cg + cbase;
 #pragma unroll
             for (int k = 0; k < NHWC_VECS; ++k) {
                 const int u = tid + k * kThreads;
-                const int pix = u >> 2, ch = u & 3;
+                const int pix = u / CHUNKS, ch = u % CHUNKS;
                 const int hr = pix / tl.HC, hc = pix - hr * tl.HC;
                 const int i1 = i1o + hr, i2 = i2o + hc;
                 const bool ok = u < halo_items && i1 >= 0 && i1 < L1 && i2 >= 0 && i2 < L2 && cbase + ch * 8 < p.Cg;
@@ -269,14 +282,15 @@ __global__ __launch_bounds__(WAVES * 64, 1) void igemm_kernel(const _Float16 *__
                 valid |= unsigned(ok) << k;
             }
         } else {
-            // items: (halo row, channel octet, aligned 8-column vector)
+            // items (halo row, aligned 8-column vector, channel octet), octet fastest:
+            // a wave reads 8 channel planes x 128 contiguous bytes per load
             const _Float16 *xb = x + (size_t(n) * p.C + size_t(g) * p.Cg + cbase) * plane_in + size_t(i0) * L1 * L2;
 #pragma unroll
             for (int it = 0; it < NCH_ITEMS; ++it) {
                 const int u = tid + it * kThreads;
-                const int hr = u / (4 * nvc);
-                const int rem2 = u - hr * 4 * nvc;
-                const int oct = rem2 / nvc, vc = rem2 - oct * nvc;
+                const int oct = u % CHUNKS;
+                const int rv = u / CHUNKS;
+                const int hr = rv / nvc, vc = rv - hr * nvc;
                 const int i1 = i1o + hr;
                 const int i2 = (va + vc) * 8;
                 const bool ok = u < halo_items && i1 >= 0 && i1 < L1 && i2 >= 0 && i2 < L2 && cbase + oct * 8 < p.Cg;
@@ -289,14 +303,14 @@ __global__ __launch_bounds__(WAVES * 64, 1) void igemm_kernel(const _Float16 *__
         }
         return valid;
     };
-    auto store_halo = [&](int buf, const u32x4 *reg, unsigned valid) {
+    auto store_halo = [&](const u32x4 *reg, unsigned valid) {
         const u32x4 zero = {0u, 0u, 0u, 0u};
         unsigned char *const sink = lds_sink + lane * 16;
         if (CL) {
 #pragma unroll
             for (int k = 0; k < NHWC_VECS; ++k) {
                 const int u = tid + k * kThreads;
-                unsigned char *dst = u < halo_items ? &lds_h[buf][(u >> 2) * kRow + (u & 3) * 16] : sink;
+                unsigned char *dst = u < halo_items ? &lds_h[(u / CHUNKS) * ROW + (u % CHUNKS) * 16] : sink;
                 *reinterpret_cast<u32x4 *>(dst) = ((valid >> k) & 1u) ? reg[k] : zero;
             }
         } else {
@@ -305,9 +319,9 @@ __global__ __launch_bounds__(WAVES * 64, 1) void igemm_kernel(const _Float16 *__
                 const int u = tid + it * kThreads;
                 const bool ok = (valid >> it) & 1u;
                 const bool here = u < halo_items;
-                const int hr = u / (4 * nvc);
-                const int rem2 = u - hr * 4 * nvc;
-                const int oct = rem2 / nvc, vc = rem2 - oct * nvc;
+                const int oct = u % CHUNKS;
+                const int rv = u / CHUNKS;
+                const int hr = rv / nvc, vc = rv - hr * nvc;
                 const u32x4 *in = reg + it * 8;
                 // transpose 8 channels x 8 columns -> 8 columns x 8 channels
 #pragma unroll
@@ -319,9 +333,8 @@ __global__ __launch_bounds__(WAVES * 64, 1) void igemm_kernel(const _Float16 *__
                         const unsigned lo = in[2 * jj][pp >> 1], hi = in[2 * jj + 1][pp >> 1];
                         o[jj] = (pp & 1) ? ((lo >> 16) | (hi & 0xffff0000u)) : ((lo & 0xffffu) | (hi << 16));
                     }
-                    unsigned char *dst = (here && hc >= 0 && hc < tl.HC)
-                                             ? &lds_h[buf][(hr * tl.HC + hc) * kRow + oct * 16]
-                                             : sink;
+                    unsigned char *dst =
+                        (here && hc >= 0 && hc < tl.HC) ? &lds_h[(hr * tl.HC + hc) * ROW + oct * 16] : sink;
                     *reinterpret_cast<u32x4 *>(dst) = ok ? o : zero;
                 }
             }
@@ -335,82 +348,155 @@ __global__ __launch_bounds__(WAVES * 64, 1) void igemm_kernel(const _Float16 *__
         StepIdx cur = {0, t0_first, 0, 0};
         {
             const unsigned v0 = load_halo(0, t0_first, hreg);
-            store_halo(0, hreg, v0);
+            store_halo(hreg, v0);
         }
         load_w(cur, wreg);
         store_w(0, wreg);
         __syncthreads();
         StepIdx nxt = cur;
         advance(nxt);
-        int hbuf = 0;
+        unsigned hvalid = 0;
         for (int s = 0; s < nsteps; ++s) {
-            // the halo of the next group is fetched during the first step of this one
-            bool fetch = false;
-            unsigned hvalid = 0;
-            if (cur.t1 == 0 && cur.t2 == 0) {
+            const bool group_first = cur.t1 == 0 && cur.t2 == 0;
+            const bool group_last = cur.t1 == nt1 - 1 && cur.t2 == nt2 - 1;
+            if (group_first) {  // the halo of the next group, if any, comes in meanwhile
                 StepIdx ng = cur;
                 ng.t1 = nt1 - 1;
                 ng.t2 = nt2 - 1;
                 advance(ng);
-                fetch = ng.chunk < p.nchunk;
-                if (fetch) hvalid = load_halo(ng.chunk, ng.t0, hreg);
+                if (ng.chunk < p.nchunk) hvalid = load_halo(ng.chunk, ng.t0, hreg);
             }
             load_w(s + 1 < nsteps ? nxt : cur, wreg);  // the last step reloads a valid tile
             // issue the prefetch loads here, ahead of the MFMAs (no later sinking)
             asm volatile("" ::: "memory");
 
             // tap shift inside the halo: (beta - beta_min) rows and columns
-            const int toff = ((nt1 - 1 - cur.t1) * bs1 * tl.HC + (nt2 - 1 - cur.t2) * bs2) * kRow;
-            const unsigned char *hb = lds_h[hbuf] + toff;
-            const unsigned char *wb = lds_w[s & 1] + (wm * WM * 32 + (lane & 31)) * kRow + (lane >> 5) * 16;
+            const int toff = ((nt1 - 1 - cur.t1) * bs1 * tl.HC + (nt2 - 1 - cur.t2) * bs2) * ROW;
+            const unsigned char *hb = lds_h + toff;
+            const unsigned char *wb = lds_w(s & 1) + (wm * WM * 32 + (lane & 31)) * ROW + (lane >> 5) * 16;
+            f16x8 a[2][WM], b[2][WN];
 #pragma unroll
-            for (int h = 0; h < 2; ++h) {
-                f16x8 a[WM], b[WN];
+            for (int i = 0; i < WM; ++i) a[0][i] = *reinterpret_cast<const f16x8 *>(wb + i * 32 * ROW);
 #pragma unroll
-                for (int i = 0; i < WM; ++i)
-                    a[i] = *reinterpret_cast<const f16x8 *>(wb + i * 32 * kRow + h * 32);
+            for (int j = 0; j < WN; ++j) b[0][j] = *reinterpret_cast<const f16x8 *>(hb + hoff[j]);
 #pragma unroll
-                for (int j = 0; j < WN; ++j)
-                    b[j] = *reinterpret_cast<const f16x8 *>(hb + hoff[j] + h * 32);
+            for (int h = 0; h < KSUB; ++h) {
+                const int cb = h & 1, nb = cb ^ 1;
+                if (h + 1 < KSUB) {  // fragments of the next k-step, read under this one's MFMAs
+#pragma unroll
+                    for (int i = 0; i < WM; ++i)
+                        a[nb][i] = *reinterpret_cast<const f16x8 *>(wb + i * 32 * ROW + (h + 1) * 32);
+#pragma unroll
+                    for (int j = 0; j < WN; ++j)
+                        b[nb][j] = *reinterpret_cast<const f16x8 *>(hb + hoff[j] + (h + 1) * 32);
+                }
+                // fence: the reads above are issued before these MFMAs, which keep source
+                // order (each accumulator is touched once per k-step)
+                __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
                 for (int i = 0; i < WM; ++i)
 #pragma unroll
                     for (int j = 0; j < WN; ++j)
-                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[i], b[j], acc[i][j], 0, 0, 0);
+                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[cb][i], b[cb][j], acc[i][j], 0, 0, 0);
+                __builtin_amdgcn_sched_barrier(0);
             }
 
-            if (fetch) store_halo(hbuf ^ 1, hreg, hvalid);
             store_w((s + 1) & 1, wreg);
             __syncthreads();
+            if (group_last && s + 1 < nsteps) {  // refresh the halo between two barriers
+                store_halo(hreg, hvalid);
+                __syncthreads();
+            }
             cur = nxt;
             advance(nxt);
-            if (cur.t1 == 0 && cur.t2 == 0) hbuf ^= 1;
         }
     }
 
     // ---------------- epilogue: bias, round once, store ----------------
+    // The block's BM x BN output tile goes through LDS (free once the main loop is done):
+    // bias is staged once, each wave writes its accumulators as float16, and the tile
+    // is then stored with 16-byte vectors along the contiguous output direction.
+    // tile layout (pitch padded by 8 elements against bank conflicts):
+    //   CL -> [pixel][m] (m contiguous);  NC -> [m][pixel] (pixel contiguous)
+    constexpr int TP = (CL ? BM : BN) + 8;
+    static_assert((CL ? BN : BM) * TP * 2 + BM * 4 <= kLdsBytes, "output tile must fit in LDS");
+    __syncthreads();  // every wave is done reading the operand buffers
+    float *const sbias = reinterpret_cast<float *>(lds + (CL ? BN : BM) * TP * 2);
+    _Float16 *const stile = reinterpret_cast<_Float16 *>(lds);
+    for (int mm = tid; mm < BM; mm += kThreads) {
+        const int mloc = mt * BM + mm;
+        sbias[mm] = (bias && mloc < p.Mg) ? float(bias[g * p.Mg + mloc]) : 0.0f;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < WM; ++i)
+#pragma unroll
+        for (int j = 0; j < WN; ++j) {
+            const int pl = (wn * WN + j) * 32 + (lane & 31);
+#pragma unroll
+            for (int rg = 0; rg < 4; ++rg) {
+                const int ml = wm * WM * 32 + i * 32 + rg * 8 + (lane >> 5) * 4;  // 4 consecutive channels
+                _Float16 v[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) v[e] = _Float16(acc[i][j][rg * 4 + e] + sbias[ml + e]);
+                if (CL) {
+                    typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+                    const unsigned w0 = unsigned(__builtin_bit_cast(unsigned short, v[0])) |
+                                        (unsigned(__builtin_bit_cast(unsigned short, v[1])) << 16);
+                    const unsigned w1 = unsigned(__builtin_bit_cast(unsigned short, v[2])) |
+                                        (unsigned(__builtin_bit_cast(unsigned short, v[3])) << 16);
+                    *reinterpret_cast<u32x2 *>(&stile[pl * TP + ml]) = u32x2{w0, w1};
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) stile[(ml + e) * TP + pl] = v[e];
+                }
+            }
+        }
+    __syncthreads();
+
     const int O1 = p.O[1], O2 = p.O[2];
     const size_t opix = size_t(p.O[0]) * O1 * O2;
     const int o0 = r0 + p.s[0] * j0;
-#pragma unroll
-    for (int j = 0; j < WN; ++j) {
-        const int q = tl.q0 + (wn * WN + j) * 32 + (lane & 31);
-        if (q >= tl.q1) continue;
+    const int npix = tl.q1 - tl.q0;
+    const int mvalid = min(BM, p.Mg - mt * BM);
+    auto pixel_offset = [&](int pl) -> size_t {  // output pixel index of tile pixel pl
+        const int q = tl.q0 + pl;
         const int row = tl.seg ? tl.row_lo : q / J2;
         const int col = q - row * J2;
-        const int o1 = r1 + p.s[1] * row, o2 = r2 + p.s[2] * col;
-        const size_t pix = (size_t(o0) * O1 + o1) * O2 + o2;
-#pragma unroll
-        for (int i = 0; i < WM; ++i) {
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int mloc = mt * BM + wm * WM * 32 + i * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
-                if (mloc >= p.Mg) continue;
-                const int m = g * p.Mg + mloc;
-                float val = acc[i][j][r];
-                if (bias) val += float(bias[m]);
-                const size_t off = CL ? ((size_t(n) * opix + pix) * p.M + m) : ((size_t(n) * p.M + m) * opix + pix);
-                y[off] = _Float16(val);
+        return (size_t(o0) * O1 + (r1 + p.s[1] * row)) * O2 + (r2 + p.s[2] * col);
+    };
+    if (CL) {
+        // rows of BM channels per pixel: 16-byte vectors when the run is aligned
+        const bool vec = (p.M % 8 == 0) && ((g * p.Mg + mt * BM) % 8 == 0) && (mvalid % 8 == 0) &&
+                         (reinterpret_cast<uintptr_t>(y) % 16 == 0);
+        if (vec) {
+            const int per = mvalid / 8;
+            for (int u = tid; u < npix * per; u += kThreads) {
+                const int pl = u / per, c8 = u - pl * per;
+                const size_t off = (size_t(n) * opix + pixel_offset(pl)) * p.M + g * p.Mg + mt * BM + c8 * 8;
+                *reinterpret_cast<u32x4 *>(y + off) = *reinterpret_cast<const u32x4 *>(&stile[pl * TP + c8 * 8]);
+            }
+        } else {
+            for (int u = tid; u < npix * mvalid; u += kThreads) {
+                const int pl = u / mvalid, ml = u - pl * mvalid;
+                y[(size_t(n) * opix + pixel_offset(pl)) * p.M + g * p.Mg + mt * BM + ml] = stile[pl * TP + ml];
+            }
+        }
+    } else {
+        // runs of pixels per channel: contiguous in Y only along a row with unit stride
+        const bool vec = p.s[2] == 1 && !tl.seg && (J2 % 8 == 0) && (tl.q0 % 8 == 0) && (O2 % 8 == 0) && r2 == 0 &&
+                         (npix % 8 == 0) && (reinterpret_cast<uintptr_t>(y) % 16 == 0);
+        if (vec) {
+            const int per = npix / 8;
+            for (int u = tid; u < mvalid * per; u += kThreads) {
+                const int ml = u / per, p8 = u - ml * per;
+                const size_t off = (size_t(n) * p.M + g * p.Mg + mt * BM + ml) * opix + pixel_offset(p8 * 8);
+                *reinterpret_cast<u32x4 *>(y + off) = *reinterpret_cast<const u32x4 *>(&stile[ml * TP + p8 * 8]);
+            }
+        } else {
+            for (int u = tid; u < mvalid * npix; u += kThreads) {
+                const int ml = u / npix, pl = u - ml * npix;
+                y[(size_t(n) * p.M + g * p.Mg + mt * BM + ml) * opix + pixel_offset(pl)] = stile[ml * TP + pl];
             }
         }
     }
@@ -452,19 +538,19 @@ __global__ __launch_bounds__(256) void pack_w_kernel(const _Float16 *__restrict_
 
 // ---------------- host-side planning ----------------
 struct Config {
-    int waves, waves_m, wm, wn, nch_items, nhwc_vecs;
-    int threads() const { return waves * 64; }
+    int waves_m, wm, wn, cc, nch_items, nhwc_vecs;
     int bm() const { return waves_m * wm * 32; }
-    int bn() const { return (waves / waves_m) * wn * 32; }
+    int bn() const { return (4 / waves_m) * wn * 32; }
+    int row() const { return cc * 2 + 16; }
+    int chunks() const { return cc / 8; }
+    int halo_bytes() const { return kLdsBytes - 2 * bm() * row() - kSinkBytes; }
 };
 
-// Both configurations run 8 waves (two per SIMD) so that one wave's loads and index
-// arithmetic overlap the other's MFMAs.
-Config pick_config(const Geom &g)
-{
-    if (g.Mg > 64) return Config{8, 2, 4, 2, 1, 6};  // 256 x 256 block, 128 x 64 per wave
-    return Config{8, 1, 2, 2, 1, 6};                 // 64 x 512 block, 64 x 64 per wave
-}
+// The two compiled configurations (their template arguments must match launch_igemm).
+constexpr Config kWide{2, 4, 4, 64, 2, 14};    // 256 x 256 block, 128 x 128 per wave, 64 ch/step
+constexpr Config kNarrow{1, 2, 4, 32, 2, 12};  // 64 x 512 block, 64 x 128 per wave, 32 ch/step
+
+Config pick_config(const Geom &g) { return g.Mg > 64 ? kWide : kNarrow; }
 
 struct Plan {
     Config cfg;
@@ -511,8 +597,8 @@ bool make_plan(const Geom &g, Plan *pl, std::string *why)
     a.Cg = int(g.Cg);
     a.Mg = int(g.Mg);
     a.T = int(g.taps());
-    a.nchunk = int((g.Cg + kCC - 1) / kCC);
-    a.Cgp = a.nchunk * kCC;
+    a.nchunk = int((g.Cg + cfg.cc - 1) / cfg.cc);
+    a.Cgp = a.nchunk * cfg.cc;
     a.mtiles = int((g.Mg + BM - 1) / BM);
     a.Mgp = a.mtiles * BM;
 
@@ -547,10 +633,12 @@ bool make_plan(const Geom &g, Plan *pl, std::string *why)
                 const int e2 = n2 ? (n2 - 1) * a.bstep[2] : 0;
                 const int HR = seg ? 1 + e1 : std::min<int>(J1, (BN + J2 - 1) / J2 + 1) + e1;
                 const int HC = seg ? BN + e2 : J2 + e2;
-                if ((long long)HR * HC * kRow > kHaloBytes) return no("input halo exceeds LDS");
-                if ((long long)HR * HC * 4 > (long long)cfg.nhwc_vecs * cfg.threads()) return no("halo too large");
+                if ((long long)HR * HC * cfg.row() > cfg.halo_bytes()) return no("input halo exceeds LDS");
+                if ((long long)HR * HC * cfg.chunks() > (long long)cfg.nhwc_vecs * kThreads)
+                    return no("halo too large");
                 const int nvc = (HC + 7) / 8 + 1;
-                if ((long long)HR * 4 * nvc > (long long)cfg.nch_items * cfg.threads()) return no("halo too large");
+                if ((long long)HR * nvc * cfg.chunks() > (long long)cfg.nch_items * kThreads)
+                    return no("halo too large");
             }
     std::stable_sort(list, list + nph, [](const PhaseInfo &x, const PhaseInfo &y) { return x.taps > y.taps; });
     a.nphase = nph;
@@ -573,12 +661,12 @@ bool make_plan(const Geom &g, Plan *pl, std::string *why)
     return true;
 }
 
-template <bool CL, int WAVES, int WAVES_M, int WM, int WN, int NCH_ITEMS, int NHWC_VECS>
+template <bool CL, int WAVES_M, int WM, int WN, int CC, int NCH_ITEMS, int NHWC_VECS>
 void launch_cfg(const IgArgs &a, const _Float16 *x, const _Float16 *wp, const _Float16 *b, _Float16 *y,
                 hipStream_t st)
 {
-    hipLaunchKernelGGL((igemm_kernel<CL, WAVES, WAVES_M, WM, WN, NCH_ITEMS, NHWC_VECS>),
-                       dim3(unsigned(a.nblocks)), dim3(WAVES * 64), 0, st, x, wp, b, y, a);
+    hipLaunchKernelGGL((igemm_kernel<CL, WAVES_M, WM, WN, CC, NCH_ITEMS, NHWC_VECS>), dim3(unsigned(a.nblocks)),
+                       dim3(kThreads), 0, st, x, wp, b, y, a);
 }
 
 }  // namespace
@@ -646,12 +734,12 @@ ct_status launch_igemm(const Geom &g, ct_dtype, bool cl, const void *x, const vo
     _Float16 *yt = static_cast<_Float16 *>(y);
     const Config c = pl.cfg;
     mark_before(st);
-    if (c.waves_m == 2) {
-        if (cl) launch_cfg<true, 8, 2, 4, 2, 1, 6>(pl.a, xt, wpk, bt, yt, st);
-        else launch_cfg<false, 8, 2, 4, 2, 1, 6>(pl.a, xt, wpk, bt, yt, st);
+    if (c.waves_m == kWide.waves_m) {
+        if (cl) launch_cfg<true, 2, 4, 4, 64, 2, 14>(pl.a, xt, wpk, bt, yt, st);
+        else launch_cfg<false, 2, 4, 4, 64, 2, 14>(pl.a, xt, wpk, bt, yt, st);
     } else {
-        if (cl) launch_cfg<true, 8, 1, 2, 2, 1, 6>(pl.a, xt, wpk, bt, yt, st);
-        else launch_cfg<false, 8, 1, 2, 2, 1, 6>(pl.a, xt, wpk, bt, yt, st);
+        if (cl) launch_cfg<true, 1, 2, 4, 32, 2, 12>(pl.a, xt, wpk, bt, yt, st);
+        else launch_cfg<false, 1, 2, 4, 32, 2, 12>(pl.a, xt, wpk, bt, yt, st);
     }
     mark_after(st);
     hipError_t e = hipGetLastError();
