@@ -235,6 +235,46 @@ def test_edge_cases(T, case, kernel, dtype, cl):
     check(got, O.convtranspose(x, w, b, **attrs), dtype, True, name)
 
 
+DEPTHWISE = [
+    # (x_shape, kernel size, attrs): one channel in and out per group, equal strides
+    ((2, 5, 13, 21), 4, dict(strides=[2, 2], pads=[1, 1, 1, 1])),
+    ((1, 3, 9, 300), 4, dict(strides=[2, 2])),
+    ((2, 4, 10, 17), 3, dict(strides=[2, 2], pads=[1, 1, 1, 1], output_padding=[1, 1])),
+    ((1, 6, 31, 9), 3, dict(pads=[1, 1, 1, 1])),
+    ((1, 2, 12, 40), 3, dict(dilations=[2, 2], pads=[2, 2, 2, 2])),
+    ((1, 2, 7, 11), 5, {}),
+    ((1, 2, 150, 1500), 4, dict(strides=[2, 2], pads=[1, 1, 1, 1])),
+    ((1, 3, 8, 12), 4, dict(strides=[2, 2], pads=[0, 1, 2, 1])),
+    ((2, 2, 6, 1), 4, dict(strides=[2, 2], pads=[1, 1, 1, 1])),
+    ((1, 4, 9, 14), 4, dict(strides=[2, 2], auto_pad="SAME_UPPER")),
+    ((3, 7, 5, 6), 3, dict(strides=[2, 2], pads=[2, 0, 0, 2], output_padding=[1, 0])),
+]
+
+
+@pytest.mark.parametrize("integer", [False, True], ids=["float", "int"])
+@pytest.mark.parametrize("case", DEPTHWISE, ids=lambda c: f"{c[0]}_k{c[1]}_{sorted(c[2].items())}")
+def test_depthwise_shapes(T, case, integer):
+    """Depthwise problems (group == C, one output channel per group) in float16: the
+    banded per-phase effective-kernel path where the window shape is one it serves, the
+    generic grouped kernel elsewhere; ragged rows and columns, several bands per plane."""
+    xs, k, attrs = case
+    C = xs[1]
+    attrs = dict(attrs, group=C)
+    _log(f"[case] depthwise x{xs} k{k} {attrs} integer={integer}")
+    rng = np.random.default_rng(zlib.crc32(repr(case).encode()) + integer)
+    gen = (lambda sz: rng.integers(-2, 3, size=sz)) if integer else (lambda sz: rng.normal(size=sz))
+    x = gen(xs).astype(np.float16)
+    w = (gen((C, 1, k, k)) * (1 if integer else 0.3)).astype(np.float16)
+    b = gen(C).astype(np.float16)
+    ref = O.convtranspose(x, w, b, **attrs)
+    ref_nb = O.convtranspose(x, w, None, **attrs)
+    for kernel in ("grouped", "auto"):
+        got = gpu_run(T, x, w, b, attrs, False, kernel)
+        check(got, ref, "f16", integer, f"depthwise {kernel} x{xs} {attrs}")
+    got = gpu_run(T, x, w, None, attrs, False, "grouped")
+    check(got, ref_nb, "f16", integer, f"depthwise no-bias x{xs} {attrs}")
+
+
 def test_repeat_runs_bitwise_identical(T):
     wl = REDUCED[2]
     x, w, b = W.make_inputs(wl)
