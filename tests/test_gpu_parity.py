@@ -248,6 +248,13 @@ DEPTHWISE = [
     ((2, 2, 6, 1), 4, dict(strides=[2, 2], pads=[1, 1, 1, 1])),
     ((1, 4, 9, 14), 4, dict(strides=[2, 2], auto_pad="SAME_UPPER")),
     ((3, 7, 5, 6), 3, dict(strides=[2, 2], pads=[2, 0, 0, 2], output_padding=[1, 0])),
+    ((2, 3, 9, 16), 8, dict(strides=[4, 4], pads=[2, 2, 2, 2])),
+    ((1, 4, 10, 24), 2, dict(strides=[2, 2])),
+    ((1, 3, 11, 16), 6, dict(strides=[2, 2], pads=[2, 2, 2, 2])),
+    ((1, 3, 7, 16), 3, dict(strides=[2, 2], dilations=[2, 2], pads=[1, 1, 1, 1], output_padding=[1, 1])),
+    ((2, 2, 12, 13), 5, dict(pads=[2, 2, 2, 2])),
+    ((1, 2, 5, 24), 4, dict(strides=[4, 4], pads=[0, 1, 3, 0])),
+    ((1, 3, 20, 24), 4, dict(strides=[2, 2], pads=[3, 0, 0, 3], output_padding=[1, 1])),
 ]
 
 

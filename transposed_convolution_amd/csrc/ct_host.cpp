@@ -234,7 +234,7 @@ ct_status prepare(ct_kernel want, ct_dtype dt, int nsp, int cl, const void *x,
             // below 16 of either most of each tile would be padding.
             if (g->Cg >= 16 && g->Mg >= 16 && ct::igemm_supports(*g, dt, cl, x, &why))
                 *chosen = CT_KERNEL_IGEMM;
-            else if (ct::grouped_supports(*g, dt, cl))
+            else if (ct::grouped_supports(*g, dt, cl, x))
                 *chosen = CT_KERNEL_GROUPED;
             else
                 *chosen = CT_KERNEL_DIRECT;
@@ -243,7 +243,7 @@ ct_status prepare(ct_kernel want, ct_dtype dt, int nsp, int cl, const void *x,
             *chosen = CT_KERNEL_DIRECT;
             return CT_OK;
         case CT_KERNEL_GROUPED:
-            if (!ct::grouped_supports(*g, dt, cl))
+            if (!ct::grouped_supports(*g, dt, cl, x))
                 return fail(CT_EUNSUPPORTED, "the grouped kernel cannot serve this call");
             *chosen = CT_KERNEL_GROUPED;
             return CT_OK;

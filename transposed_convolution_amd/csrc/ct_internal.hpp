@@ -78,7 +78,12 @@ inline void mark_after(hipStream_t st)
 // Launchers (one per kernel family); each returns CT_OK or CT_EDEVICE (message in err).
 ct_status launch_direct(const Geom &g, ct_dtype dt, bool cl, const void *x, const void *w,
                         const void *bias, void *y, hipStream_t st, std::string *err);
-bool grouped_supports(const Geom &g, ct_dtype dt, bool cl);
+bool grouped_supports(const Geom &g, ct_dtype dt, bool cl, const void *x);
+// Depthwise specialisation inside the grouped family (one channel in and out per group,
+// float16, channels-first, equal strides 1, 2 or 4, tap runs of step 1).
+bool depthwise_supports(const Geom &g, ct_dtype dt, bool cl, const void *x);
+ct_status launch_depthwise(const Geom &g, ct_dtype dt, bool cl, const void *x, const void *w,
+                           const void *bias, void *y, hipStream_t st, std::string *err);
 ct_status launch_grouped(const Geom &g, ct_dtype dt, bool cl, const void *x, const void *w,
                          const void *bias, void *y, hipStream_t st, std::string *err);
 bool igemm_supports(const Geom &g, ct_dtype dt, bool cl, const void *x, std::string *why);
