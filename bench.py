@@ -38,7 +38,8 @@ sys.path.insert(0, ROOT)
 METRIC = "ConvTranspose TFLOP/s (2*useful MACs) and % of MFMA/HBM roofline on 1 MI355X"
 PEAK_TFLOPS = {"f16": 2500.0, "f32": 157.3}   # dense MFMA peaks of MI355X
 PEAK_HBM_GBS = 8000.0
-KERNEL_SOURCES = {"igemm": "ct_igemm.hip", "grouped": "ct_grouped.hip", "direct": "ct_direct.hip"}
+KERNEL_SOURCES = {"igemm": ["ct_igemm.hip"], "grouped": ["ct_grouped.hip", "ct_depthwise.hip"],
+                  "direct": ["ct_direct.hip"]}
 COPY_BYTES = 256 << 20  # calibration copy: 256 MiB read + 256 MiB written
 
 
@@ -53,10 +54,13 @@ def workloads():
 
 
 def source_digest(kernel: str) -> str:
-    path = os.path.join(ROOT, "transposed_convolution_amd", "csrc", KERNEL_SOURCES.get(kernel, ""))
-    if not os.path.isfile(path):
-        return ""
-    return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES.get(kernel, []):
+        path = os.path.join(ROOT, "transposed_convolution_amd", "csrc", name)
+        if not os.path.isfile(path):
+            return ""
+        h.update(open(path, "rb").read())
+    return h.hexdigest()[:16]
 
 
 def traffic_file(wl_key: str, kernel: str) -> str:
@@ -104,11 +108,12 @@ def summarize_pmc(args):
             v = float(r["Counter_Value"])
             if args.kernel_match in name:
                 vals.append(v)
-            elif "copy" in name.lower() or "elementwise" in name.lower():
+            elif "copybuffer" in name.lower():  # the runtime's device-to-device copy
                 copy.append(v)
         if not vals or not copy:
             raise SystemExit(f"no {counter} rows for the kernel or the calibration copy in {args.pmc_summary}")
-        # counters are KiB per dispatch; the copy moves COPY_BYTES each way
+        # counters are KiB per dispatch; the largest runtime copy is the calibration
+        # copy, which moves COPY_BYTES each way
         scale = COPY_BYTES / (max(copy) * 1024.0)
         res[counter] = {"kib_per_launch": sum(vals) / len(vals), "copy_kib": max(copy),
                         "bytes_per_launch": sum(vals) / len(vals) * 1024.0 * scale, "scale": scale}
