@@ -359,6 +359,9 @@ __global__ __launch_bounds__(kThreads, 1) void igemm_kernel(const _Float16 *x, c
         for (int s = 0; s < nsteps; ++s) {
             const bool group_first = cur.t1 == 0 && cur.t2 == 0;
             const bool group_last = cur.t1 == nt1 - 1 && cur.t2 == nt2 - 1;
+            // The next step's weight tile is loaded first: loads complete in issue order,
+            // so waiting for it at the end of this step does not wait for the halo loads.
+            load_w(s + 1 < nsteps ? nxt : cur, wreg);  // the last step reloads a valid tile
             if (group_first) {  // the halo of the next group, if any, comes in meanwhile
                 StepIdx ng = cur;
                 ng.t1 = nt1 - 1;
@@ -366,7 +369,6 @@ __global__ __launch_bounds__(kThreads, 1) void igemm_kernel(const _Float16 *x, c
                 advance(ng);
                 if (ng.chunk < p.nchunk) hvalid = load_halo(ng.chunk, ng.t0, hreg);
             }
-            load_w(s + 1 < nsteps ? nxt : cur, wreg);  // the last step reloads a valid tile
             // issue the prefetch loads here, ahead of the MFMAs (no later sinking)
             asm volatile("" ::: "memory");
 
@@ -494,9 +496,27 @@ __global__ __launch_bounds__(kThreads, 1) void igemm_kernel(const _Float16 *x, c
                 *reinterpret_cast<u32x4 *>(y + off) = *reinterpret_cast<const u32x4 *>(&stile[ml * TP + p8 * 8]);
             }
         } else {
-            for (int u = tid; u < mvalid * npix; u += kThreads) {
-                const int ml = u / npix, pl = u - ml * npix;
-                y[(size_t(n) * p.M + g * p.Mg + mt * BM + ml) * opix + pixel_offset(pl)] = stile[ml * TP + pl];
+            // Phase-strided rows: runs of 8 tile pixels of one channel.  When a run lies
+            // in one output row its 8 outputs sit s2 elements apart: one LDS vector read,
+            // one address, 8 stores.  Runs that cross a row or the tile end go element by
+            // element.
+            const int nruns = (npix + 7) / 8;
+            const int s2 = p.s[2];
+            for (int u = tid; u < mvalid * nruns; u += kThreads) {
+                const int ml = u / nruns, pl0 = (u - ml * nruns) * 8;
+                _Float16 *const yc = y + (size_t(n) * p.M + g * p.Mg + mt * BM + ml) * opix;
+                const int q = tl.q0 + pl0;
+                const int row = tl.seg ? tl.row_lo : q / J2;
+                const int col = q - row * J2;
+                if (pl0 + 8 <= npix && col + 8 <= J2) {
+                    const u32x4 v8 = *reinterpret_cast<const u32x4 *>(&stile[ml * TP + pl0]);
+                    _Float16 *const dst = yc + pixel_offset(pl0);
+#pragma unroll
+                    for (int e = 0; e < 8; ++e)
+                        dst[e * s2] = __builtin_bit_cast(_Float16, (unsigned short)(v8[e >> 1] >> (16 * (e & 1))));
+                } else {
+                    for (int pl = pl0; pl < min(pl0 + 8, npix); ++pl) yc[pixel_offset(pl)] = stile[ml * TP + pl];
+                }
             }
         }
     }
