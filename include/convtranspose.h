@@ -31,8 +31,8 @@
  *
  * Shapes are always passed in logical ONNX order.  Buffers are owned by the caller,
  * must be dense in the stated layout and aligned to the element size; the library
- * keeps no pointer after a call returns.  The implicit-GEMM path re-lays W out into
- * scratch memory: a caller workspace (convtranspose_nd_with_kernel), or else
+ * keeps no pointer after a call returns.  The float16 implicit-GEMM path re-lays W out
+ * into scratch memory: a caller workspace (convtranspose_nd_with_kernel), or else
  * stream-ordered scratch taken and released on the call's stream.
  *
  * Thread safety: every call is re-entrant; the error text is per host thread.
@@ -64,7 +64,7 @@ typedef enum {
     CT_KERNEL_AUTO = 0,     /* let the shape-based dispatcher choose                     */
     CT_KERNEL_DIRECT = 1,   /* generic gather, any rank/attributes/layout/dtype          */
     CT_KERNEL_GROUPED = 2,  /* grouped/depthwise bandwidth kernel (small C/g and M/g)    */
-    CT_KERNEL_IGEMM = 3,    /* stride-phase implicit GEMM on MFMA (float16)              */
+    CT_KERNEL_IGEMM = 3,    /* stride-phase implicit GEMM on MFMA (float16 and float32)  */
     CT_KERNEL_NONE = 4      /* nothing to launch: Y is empty                             */
 } ct_kernel;
 
@@ -115,8 +115,8 @@ ct_status convtranspose_useful_macs(int nsp, const int64_t *x_shape, const int64
  * All validation happens before anything is enqueued: on any error nothing is launched
  * and y is untouched.  Work is asynchronous: the call returns once the kernels are
  * enqueued.  An empty y (some dimension 0) returns CT_OK with no launch.  When the
- * dispatcher picks the implicit-GEMM path, scratch for the re-laid-out weights is taken
- * with hipMallocAsync and released with hipFreeAsync on `stream`.
+ * dispatcher picks the float16 implicit-GEMM path, scratch for the re-laid-out weights
+ * is taken with hipMallocAsync and released with hipFreeAsync on `stream`.
  */
 ct_status convtranspose_nd(ct_dtype dtype, int nsp, int channels_last, const void *x,
                            const int64_t *x_shape, const void *w, const int64_t *w_shape,
@@ -130,9 +130,10 @@ ct_status convtranspose_nd(ct_dtype dtype, int nsp, int channels_last, const voi
  * As convtranspose_nd, with the kernel family forced and an optional caller workspace.
  *   kernel          CT_KERNEL_AUTO (the dispatcher's choice) or a family to force;
  *                   CT_EUNSUPPORTED (nothing launched) when that family cannot serve
- *                   the call (e.g. CT_KERNEL_IGEMM for float32).
+ *                   the call (e.g. CT_KERNEL_GROUPED for a call with group 1).
  *   workspace       device scratch of workspace_bytes bytes, 16-byte aligned, used for
- *                   the implicit-GEMM path's re-laid-out weights; it must not be in use
+ *                   the float16 implicit-GEMM path's re-laid-out weights (the float32
+ *                   path needs none); it must not be in use
  *                   by other work until this call's kernels have finished on `stream`.
  *                   NULL: the library takes stream-ordered scratch itself
  *                   (hipMallocAsync / hipFreeAsync on `stream`), as convtranspose_nd does.

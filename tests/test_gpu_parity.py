@@ -196,6 +196,45 @@ def test_random_igemm_shaped_problems(T, cl):
     assert ran >= 25
 
 
+@pytest.mark.parametrize("cl", [False, True], ids=["nc", "cl"])
+def test_random_float32_mfma_problems(T, cl):
+    """float32 implicit GEMM on MFMA: random rank, strides, dilations, pads, groups and
+    ragged channel counts, several 64 x 64 tiles and 16-deep depth steps; forced and via
+    the dispatcher.  Tolerance 1e-5 (1+|ref|); integer-valued inputs bit-exact."""
+    rng = np.random.default_rng(303 + cl)
+    ran = 0
+    for t in range(30):
+        nsp = int(rng.integers(1, 4))
+        G = int(rng.choice([1, 1, 2, 3]))
+        Cg = int(rng.integers(1, 70))
+        Mg = int(rng.integers(1, 90))
+        L = [int(rng.integers(1, 9)) for _ in range(nsp - 1)] + [int(rng.integers(1, 40))]
+        K = [int(rng.integers(1, 4)) for _ in range(nsp)]
+        s = [int(rng.integers(1, 4)) for _ in range(nsp)]
+        d = [int(rng.integers(1, 3)) for _ in range(nsp)]
+        attrs = dict(strides=s, dilations=d, group=G,
+                     output_padding=[int(rng.integers(0, max(a, b))) for a, b in zip(s, d)],
+                     pads=[int(rng.integers(0, 3)) for _ in range(2 * nsp)])
+        xs, ws = (2, G * Cg, *L), (G * Cg, Mg, *K)
+        try:
+            O.output_shape(xs, ws, **attrs)
+        except O.OracleError:
+            continue
+        integer = bool(t % 2)
+        gen = (lambda sz: rng.integers(-2, 3, size=sz)) if integer else (lambda sz: rng.normal(size=sz))
+        x = gen(xs).astype(np.float32)
+        w = (gen(ws) * (1 if integer else 0.2)).astype(np.float32)
+        b = gen(G * Mg).astype(np.float32)
+        _log(f"[case] f32-mfma-random #{t} cl={cl} x{x.shape} w{w.shape} {attrs}")
+        ref = O.convtranspose(x, w, b, **attrs)
+        for kernel in ("igemm", "auto"):
+            got = gpu_run(T, x, w, b, attrs, cl, kernel)
+            assert got is not None, f"float32 MFMA path refused #{t}"
+            ran += kernel == "igemm"
+            check(got, ref, "f32", integer, f"f32-mfma-random #{t} {kernel} {attrs}")
+    assert ran >= 20
+
+
 EDGE = [
     # (name, x_shape, w_shape, attrs, bias)
     ("empty_batch", (0, 8, 5, 5), (8, 4, 3, 3), dict(strides=[2, 2]), True),

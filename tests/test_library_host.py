@@ -128,7 +128,8 @@ def test_validation_errors_launch_nothing(T):
     assert _raw_call(T, kernel=9) == 1
     assert _raw_call(T, nsp=2, attrs=dict(strides=[0, 1]), ys=(1, 3, 7, 7)) == 1
     assert "stride" in T.convtranspose_last_error()
-    assert _raw_call(T, kernel=3, dtype=0) == 3                      # MFMA path is fp16 only
+    assert _raw_call(T, kernel=2) == 3                               # group 1: not a grouped problem
+    assert _raw_call(T, kernel=3, dtype=0, attrs=dict(strides=[17, 1])) == 3  # stride beyond the MFMA plan
     # empty outputs: OK with nothing launched (no device is touched)
     assert _raw_call(T, xs=(0, 4, 5, 5), x=None, y=None) == 0
     assert T.convtranspose_last_error() == ""
@@ -146,7 +147,7 @@ def test_dispatcher_choices(T):
         return T.convtranspose_kernel_name(k)
 
     assert pick(W.C1, dtype=0) == "direct"
-    assert pick(W.C2, dtype=0) == "direct"
+    assert pick(W.C2, dtype=0) == "igemm"     # float32 implicit GEMM on MFMA
     assert pick(W.C3) in ("grouped", "direct")
     assert pick(W.C4) in ("igemm", "direct")
     assert pick(W.C4, cl=1) in ("igemm", "direct")

@@ -344,7 +344,7 @@ ct_status convtranspose_workspace_size(ct_kernel kernel, ct_dtype dtype, int nsp
     ct_status st = prepare(kernel, dtype, nsp, channels_last, x ? x : aligned_stub, x_shape,
                            aligned_stub, w_shape, nullptr, aligned_stub, nullptr, at, &g, &k);
     if (st != CT_OK) return st;
-    *bytes_out = (k == CT_KERNEL_IGEMM) ? ct::igemm_workspace_bytes(g) : 0;
+    *bytes_out = (k == CT_KERNEL_IGEMM) ? ct::igemm_workspace_bytes(g, dtype) : 0;
     return CT_OK;
 }
 

@@ -693,8 +693,9 @@ void launch_cfg(const IgArgs &a, const _Float16 *x, const _Float16 *wp, const _F
 
 bool igemm_supports(const Geom &g, ct_dtype dt, bool cl, const void *x, std::string *why)
 {
+    if (dt == CT_FLOAT32) return igemm32_supports(g, cl, why);
     if (dt != CT_FLOAT16) {
-        *why = "float16 only";
+        *why = "float16 and float32 only";
         return false;
     }
     if (g.Cg < 8 || g.Cg % 8 != 0) {
@@ -713,16 +714,18 @@ bool igemm_supports(const Geom &g, ct_dtype dt, bool cl, const void *x, std::str
     return make_plan(g, &pl, why);
 }
 
-size_t igemm_workspace_bytes(const Geom &g)
+size_t igemm_workspace_bytes(const Geom &g, ct_dtype dt)
 {
+    if (dt != CT_FLOAT16) return 0;  // the float32 kernel reads W in place
     Plan pl;
     std::string why;
     return make_plan(g, &pl, &why) ? pl.ws_bytes : 0;
 }
 
-ct_status launch_igemm(const Geom &g, ct_dtype, bool cl, const void *x, const void *w, const void *bias,
+ct_status launch_igemm(const Geom &g, ct_dtype dt, bool cl, const void *x, const void *w, const void *bias,
                        void *y, void *workspace, size_t ws_bytes, hipStream_t st, std::string *err)
 {
+    if (dt == CT_FLOAT32) return launch_igemm32(g, cl, x, w, bias, y, st, err);
     Plan pl;
     if (!make_plan(g, &pl, err)) return CT_EUNSUPPORTED;
     bool owned = false;

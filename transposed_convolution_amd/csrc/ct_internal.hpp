@@ -87,7 +87,11 @@ ct_status launch_depthwise(const Geom &g, ct_dtype dt, bool cl, const void *x, c
 ct_status launch_grouped(const Geom &g, ct_dtype dt, bool cl, const void *x, const void *w,
                          const void *bias, void *y, hipStream_t st, std::string *err);
 bool igemm_supports(const Geom &g, ct_dtype dt, bool cl, const void *x, std::string *why);
-size_t igemm_workspace_bytes(const Geom &g);
+size_t igemm_workspace_bytes(const Geom &g, ct_dtype dt);
+// float32 implicit GEMM on MFMA (the CT_KERNEL_IGEMM family for float32 inputs)
+bool igemm32_supports(const Geom &g, bool cl, std::string *why);
+ct_status launch_igemm32(const Geom &g, bool cl, const void *x, const void *w, const void *bias, void *y,
+                         hipStream_t st, std::string *err);
 // workspace: caller scratch of ws_bytes (>= igemm_workspace_bytes), or NULL to take
 // stream-ordered scratch with hipMallocAsync / hipFreeAsync on st.
 ct_status launch_igemm(const Geom &g, ct_dtype dt, bool cl, const void *x, const void *w,
