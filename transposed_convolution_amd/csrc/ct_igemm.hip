@@ -30,6 +30,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <type_traits>
 #include <cstring>
 
 #include "ct_internal.hpp"
@@ -264,14 +265,17 @@ __global__ __launch_bounds__(kThreads, 1) void igemm_kernel(const _Float16 *x, c
     const int va = floor_div8(i2o);
     const int nvc = floor_div8(i2o + tl.HC + 7) - va;
     const int halo_items = CL ? tl.HR * tl.HC * CHUNKS : tl.HR * nvc * CHUNKS;
-    auto load_halo = [&](int chunk, int t0, u32x4 *reg) -> unsigned {
+    // load_halo_part<KB, KE>: loads KB..KE-1 of the HREG halo loads (all of them for
+    // <0, HREG>) and returns their validity bits (NHWC: bit per load; NC..: bit per item).
+    auto load_halo_part = [&](auto kb, auto ke, int chunk, int t0, u32x4 *reg) -> unsigned {
+        constexpr int KB = decltype(kb)::value, KE = decltype(ke)::value;
         const int i0 = j0 + b00 - t0 * bs0;
         const int cbase = chunk * CC;  // channel offset inside the group
         unsigned valid = 0;
         if (CL) {
             const _Float16 *xb = x + (size_t(n) * L0 + i0) * L1 * L2 * p.C + size_t(g) * p.Cg + cbase;
 #pragma unroll
-            for (int k = 0; k < NHWC_VECS; ++k) {
+            for (int k = KB; k < KE; ++k) {
                 const int u = tid + k * kThreads;
                 const int pix = u / CHUNKS, ch = u % CHUNKS;
                 const int hr = pix / tl.HC, hc = pix - hr * tl.HC;
@@ -283,10 +287,11 @@ __global__ __launch_bounds__(kThreads, 1) void igemm_kernel(const _Float16 *x, c
             }
         } else {
             // items (halo row, aligned 8-column vector, channel octet), octet fastest:
-            // a wave reads 8 channel planes x 128 contiguous bytes per load
+            // a wave reads 8 channel planes x 128 contiguous bytes per load; load index
+            // = item * 8 + channel of the octet
             const _Float16 *xb = x + (size_t(n) * p.C + size_t(g) * p.Cg + cbase) * plane_in + size_t(i0) * L1 * L2;
 #pragma unroll
-            for (int it = 0; it < NCH_ITEMS; ++it) {
+            for (int it = KB / 8; it < (KE + 7) / 8; ++it) {
                 const int u = tid + it * kThreads;
                 const int oct = u % CHUNKS;
                 const int rv = u / CHUNKS;
@@ -297,11 +302,16 @@ __global__ __launch_bounds__(kThreads, 1) void igemm_kernel(const _Float16 *x, c
                 const _Float16 *src = ok ? xb + size_t(oct * 8) * plane_in + size_t(i1) * L2 + i2 : x;
                 const size_t step = ok ? plane_in : 0;
 #pragma unroll
-                for (int k = 0; k < 8; ++k) reg[it * 8 + k] = *reinterpret_cast<const u32x4 *>(src + k * step);
+                for (int k = 0; k < 8; ++k)
+                    if (it * 8 + k >= KB && it * 8 + k < KE)
+                        reg[it * 8 + k] = *reinterpret_cast<const u32x4 *>(src + k * step);
                 valid |= unsigned(ok) << it;
             }
         }
         return valid;
+    };
+    auto load_halo = [&](int chunk, int t0, u32x4 *reg) -> unsigned {
+        return load_halo_part(std::integral_constant<int, 0>{}, std::integral_constant<int, HREG>{}, chunk, t0, reg);
     };
     auto store_halo = [&](const u32x4 *reg, unsigned valid) {
         const u32x4 zero = {0u, 0u, 0u, 0u};
@@ -353,29 +363,12 @@ __global__ __launch_bounds__(kThreads, 1) void igemm_kernel(const _Float16 *x, c
         load_w(cur, wreg);
         store_w(0, wreg);
         __syncthreads();
-        StepIdx nxt = cur;
-        advance(nxt);
-        unsigned hvalid = 0;
-        for (int s = 0; s < nsteps; ++s) {
-            const bool group_first = cur.t1 == 0 && cur.t2 == 0;
-            const bool group_last = cur.t1 == nt1 - 1 && cur.t2 == nt2 - 1;
-            // The next step's weight tile is loaded first: loads complete in issue order,
-            // so waiting for it at the end of this step does not wait for the halo loads.
-            load_w(s + 1 < nsteps ? nxt : cur, wreg);  // the last step reloads a valid tile
-            if (group_first) {  // the halo of the next group, if any, comes in meanwhile
-                StepIdx ng = cur;
-                ng.t1 = nt1 - 1;
-                ng.t2 = nt2 - 1;
-                advance(ng);
-                if (ng.chunk < p.nchunk) hvalid = load_halo(ng.chunk, ng.t0, hreg);
-            }
-            // issue the prefetch loads here, ahead of the MFMAs (no later sinking)
-            asm volatile("" ::: "memory");
-
+        // MFMAs of one step: weight tile from buffer buf, the halo window of the step's taps
+        auto mma_step = [&](const StepIdx &cur, int buf) {
             // tap shift inside the halo: (beta - beta_min) rows and columns
             const int toff = ((nt1 - 1 - cur.t1) * bs1 * tl.HC + (nt2 - 1 - cur.t2) * bs2) * ROW;
             const unsigned char *hb = lds_h + toff;
-            const unsigned char *wb = lds_w(s & 1) + (wm * WM * 32 + (lane & 31)) * ROW + (lane >> 5) * 16;
+            const unsigned char *wb = lds_w(buf) + (wm * WM * 32 + (lane & 31)) * ROW + (lane >> 5) * 16;
             f16x8 a[2][WM], b[2][WN];
 #pragma unroll
             for (int i = 0; i < WM; ++i) a[0][i] = *reinterpret_cast<const f16x8 *>(wb + i * 32 * ROW);
@@ -402,15 +395,81 @@ __global__ __launch_bounds__(kThreads, 1) void igemm_kernel(const _Float16 *x, c
                         acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[cb][i], b[cb][j], acc[i][j], 0, 0, 0);
                 __builtin_amdgcn_sched_barrier(0);
             }
+        };
 
-            store_w((s + 1) & 1, wreg);
-            __syncthreads();
-            if (group_last && s + 1 < nsteps) {  // refresh the halo between two barriers
-                store_halo(hreg, hvalid);
-                __syncthreads();
+        if (!CL && nt1 * nt2 == 4) {
+            // Four taps per (chunk, axis-0 tap) group: one group per iteration, unrolled.
+            // Each step loads the next step's weight tile and then a fixed quarter of the
+            // next group's halo, all unconditionally, so every wait for a weight tile
+            // leaves the halo quarter issued after it in flight.  (Channels-first only:
+            // the channels-last kernel runs out of registers with this loop.)
+            const int ngroups = nsteps / 4;
+            StepIdx grp = cur;
+            for (int gi = 0; gi < ngroups; ++gi) {
+                StepIdx ng = grp;
+                ng.t1 = nt1 - 1;
+                ng.t2 = nt2 - 1;
+                advance(ng);
+                const bool has_ng = gi + 1 < ngroups;
+                const int hch = has_ng ? ng.chunk : grp.chunk, ht0 = has_ng ? ng.t0 : grp.t0;  // last: a harmless reload
+                unsigned hv = 0;
+                auto g4_step = [&](auto U) {
+                    constexpr int u = decltype(U)::value;
+                    constexpr int PB = HREG * u / 4, PE = HREG * (u + 1) / 4;
+                    const int s = gi * 4 + u;
+                    StepIdx c = grp;
+                    c.t1 = u / nt2;
+                    c.t2 = u - c.t1 * nt2;
+                    StepIdx nx = c;
+                    advance(nx);
+                    load_w(s + 1 < nsteps ? nx : c, wreg);  // the last step reloads a valid tile
+                    hv |= load_halo_part(std::integral_constant<int, PB>{}, std::integral_constant<int, PE>{}, hch,
+                                         ht0, hreg);
+                    asm volatile("" ::: "memory");  // the loads go out ahead of the MFMAs
+                    mma_step(c, s & 1);
+                    store_w((s + 1) & 1, wreg);
+                    __syncthreads();
+                };
+                g4_step(std::integral_constant<int, 0>{});
+                g4_step(std::integral_constant<int, 1>{});
+                g4_step(std::integral_constant<int, 2>{});
+                g4_step(std::integral_constant<int, 3>{});
+                if (has_ng) {  // the next group's halo, between two barriers
+                    store_halo(hreg, hv);
+                    __syncthreads();
+                }
+                grp = ng;
             }
-            cur = nxt;
+        } else {
+            StepIdx nxt = cur;
             advance(nxt);
+            unsigned hvalid = 0;
+            for (int s = 0; s < nsteps; ++s) {
+                const bool group_first = cur.t1 == 0 && cur.t2 == 0;
+                const bool group_last = cur.t1 == nt1 - 1 && cur.t2 == nt2 - 1;
+                // The next step's weight tile is loaded first: loads complete in issue
+                // order, so waiting for it at the end of this step does not wait for the
+                // halo loads.
+                load_w(s + 1 < nsteps ? nxt : cur, wreg);  // the last step reloads a valid tile
+                if (group_first) {  // the halo of the next group, if any, comes in meanwhile
+                    StepIdx ng = cur;
+                    ng.t1 = nt1 - 1;
+                    ng.t2 = nt2 - 1;
+                    advance(ng);
+                    if (ng.chunk < p.nchunk) hvalid = load_halo(ng.chunk, ng.t0, hreg);
+                }
+                // issue the prefetch loads here, ahead of the MFMAs (no later sinking)
+                asm volatile("" ::: "memory");
+                mma_step(cur, s & 1);
+                store_w((s + 1) & 1, wreg);
+                __syncthreads();
+                if (group_last && s + 1 < nsteps) {  // refresh the halo between two barriers
+                    store_halo(hreg, hvalid);
+                    __syncthreads();
+                }
+                cur = nxt;
+                advance(nxt);
+            }
         }
     }
 
