@@ -11,20 +11,24 @@
 // which is a GEMM with rows = output channels, columns = the phase's output pixels and
 // depth = input channels x taps.  No zero-inserted input is ever formed.
 //
-// Kernel structure (one workgroup = 4 wave64s, one phase, BM output channels x BN phase
-// pixels of one (n, j0) plane):
+// Kernel structure (one workgroup = 4 wave64s, one phase, a BM (output channels) x BN
+// (phase pixels of one (n, j0) plane) tile; 256 x 256 with 64 channels per depth step
+// when M/group > 64, else 64 x 512 with 32 channels per step):
 //   * W is first re-laid out by pack_w_kernel into Wp[g][tap][m][c] (c contiguous,
-//     zero padded to whole 32-channel chunks and whole channel tiles), so every weight
-//     tile is a run of 16-byte loads.
-//   * For each 32-channel chunk and each valid tap along axis 0, the input "halo" that
-//     the tile's taps along axes 1 and 2 touch is staged once in LDS as
-//     [row][col][32 channels]; every (t1, t2) tap then reads a shifted window of it.
-//   * The MFMA v_mfma_f32_32x32x16_f16 runs with the weight tile as A (32 channels of
-//     m) and the shifted halo window as B (32 pixels); float32 accumulators.
-//   * Weight tiles and halos are double-buffered in LDS and prefetched into registers
-//     one step ahead.  LDS rows are 80 bytes (64 data + 16 pad): 16-byte reads of 8 or
-//     16 consecutive rows then fall in distinct bank groups.
-//   * Epilogue: + bias, one round-to-nearest-even conversion, store.
+//     zero padded to whole depth steps and whole channel tiles), so every weight tile is
+//     a run of 16-byte loads.
+//   * For each channel chunk and each valid tap along axis 0, the input "halo" that the
+//     tile's taps along axes 1 and 2 touch is staged once in LDS as [row][col][channels];
+//     every (t1, t2) tap then reads a shifted window of it.
+//   * The MFMA v_mfma_f32_32x32x16_f16 runs with the weight tile as A (32 channels of m)
+//     and the shifted halo window as B (32 pixels); float32 accumulators.
+//   * Weight tiles are double-buffered in LDS and prefetched into registers one step
+//     ahead, ahead of any halo loads (loads complete in issue order); the next group's
+//     halo is prefetched into registers during the current group (with four taps per
+//     group, a quarter per step, so every load count is static).  LDS rows carry 16
+//     bytes of padding so 16-byte reads of consecutive rows fall in distinct banks.
+//   * Epilogue: the output tile is staged through LDS, bias added, one
+//     round-to-nearest-even conversion, 16-byte stores along the contiguous direction.
 //   * Blocks are re-ordered so that the blocks an XCD receives (hardware round-robin)
 //     are consecutive in work order: all phases of one pixel tile share that XCD's L2.
 #include <hip/hip_runtime.h>
