@@ -321,6 +321,44 @@ def test_depthwise_shapes(T, case, integer):
     check(got, ref_nb, "f16", integer, f"depthwise no-bias x{xs} {attrs}")
 
 
+PAIRS = [
+    # (x_shape, w_shape, attrs): M/group > 64 and stride 2 on the innermost axis, the
+    # channels-first shapes whose two column phases one block computes together when the
+    # output width is even and both phases have the same tap count
+    ((2, 64, 9, 16), (64, 96, 4, 4), dict(strides=[2, 2], pads=[1, 1, 1, 1])),
+    ((1, 16, 264), (16, 72, 4), dict(strides=[2], pads=[1, 1])),  # tiles inside one row, ragged
+    ((2, 16, 3, 24), (16, 72, 2, 4), dict(strides=[1, 2], pads=[0, 1, 0, 1])),
+    ((2, 24, 6, 24), (24, 130, 3, 6), dict(strides=[2, 2], pads=[1, 2, 0, 2])),  # 3 taps a phase, 2 channel tiles
+    ((1, 40, 40), (40, 100, 4), dict(strides=[2], pads=[1, 1])),
+    ((1, 16, 3, 5, 16), (16, 72, 3, 3, 4), dict(strides=[1, 2, 2], pads=[1] * 6)),
+    ((1, 8, 7, 8), (8, 65, 2, 2), dict(strides=[2, 2], output_padding=[1, 0])),  # one tap a phase
+    ((2, 16, 5, 24), (16, 96, 4, 4), dict(strides=[2, 2], pads=[1] * 4, dilations=[1, 3])),  # width 54
+    ((1, 16, 6, 40), (16, 80, 3, 5), dict(strides=[2, 2], pads=[1, 2, 1, 2], output_padding=[1, 1])),  # 3 + 2 taps
+    ((1, 16, 4, 16), (16, 200, 4, 4), dict(strides=[2, 2], pads=[1] * 4, output_padding=[0, 1])),  # odd width
+    ((2, 32, 4, 32), (32, 96, 4, 4), dict(strides=[2, 2], pads=[1] * 4, group=2)),
+]
+
+
+@pytest.mark.parametrize("integer", [False, True], ids=["float", "int"])
+@pytest.mark.parametrize("case", PAIRS, ids=lambda c: f"{c[0]}_{c[1]}")
+def test_column_phase_pairs(T, case, integer):
+    """Dense float16 problems around the column-phase pairing of the MFMA kernel: paired
+    shapes (vector and element stores, tiles inside one row, several channel tiles) and
+    neighbours that stay unpaired (odd width, unequal tap counts)."""
+    xs, ws, attrs = case
+    _log(f"[case] pair x{xs} w{ws} {attrs} integer={integer}")
+    rng = np.random.default_rng(zlib.crc32(repr(case).encode()) + integer)
+    gen = (lambda sz: rng.integers(-2, 3, size=sz)) if integer else (lambda sz: rng.normal(size=sz))
+    x = gen(xs).astype(np.float16)
+    w = (gen(ws) * (1 if integer else 0.1)).astype(np.float16)
+    b = gen(ws[1] * attrs.get("group", 1)).astype(np.float16)
+    ref = O.convtranspose(x, w, b, **attrs)
+    for kernel in ("igemm", "auto"):
+        got = gpu_run(T, x, w, b, attrs, False, kernel)
+        assert got is not None, "the implicit-GEMM kernel serves these shapes"
+        check(got, ref, "f16", integer, f"pair {kernel} x{xs} w{ws} {attrs}")
+
+
 def test_repeat_runs_bitwise_identical(T):
     wl = REDUCED[2]
     x, w, b = W.make_inputs(wl)

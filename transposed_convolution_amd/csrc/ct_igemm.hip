@@ -51,6 +51,8 @@ constexpr int kMaxTap = 8;               // largest tap count per residue and ax
 constexpr int kMaxPh = 64;               // largest number of phases
 constexpr int kThreads = 256;            // 4 wave64s, one per SIMD
 constexpr int kLdsBytes = 160 * 1024 - 2048;
+// LDS bytes one block may use when OCC blocks share a compute unit (160 KB of LDS per CU)
+constexpr int lds_budget(int occ) { return occ == 1 ? kLdsBytes : 160 * 1024 / occ - 1024; }
 constexpr int kSinkBytes = 64 * 16;
 
 struct IgArgs {
@@ -89,8 +91,13 @@ struct Tile {
 // One block = 4 wave64s; WAVES_M of them split the BM output channels, the others the
 // BN phase pixels; each wave owns WM x WN MFMA tiles of 32 x 32.  CC input channels form
 // one step (CC/16 MFMA k-steps of 16).  NCH_ITEMS: NCHW halo items (8 channels x 8
-// columns) per thread; NHWC_VECS: NHWC halo 16-byte vectors per thread.
-template <bool CL, int WAVES_M, int WM, int WN, int CC, int NCH_ITEMS, int NHWC_VECS>
+// columns) per thread; NHWC_VECS: NHWC halo 16-byte vectors per thread; OCC: blocks per
+// compute unit the register and LDS budgets are sized for.
+// PAIR (channels-first, stride 2 on the innermost axis, two wave rows): the two wave rows
+// compute the two column phases r2 = 0, 1 of the same BM/2 output channels instead of two
+// channel halves of one phase, so the block owns whole output rows and stores them with
+// 16-byte vectors.
+template <bool CL, int WAVES_M, int WM, int WN, int CC, int NCH_ITEMS, int NHWC_VECS, int OCC>
 struct IgCfg {
     static constexpr int WAVES_N = 4 / WAVES_M;
     static constexpr int BM = WAVES_M * WM * 32;
@@ -99,25 +106,28 @@ struct IgCfg {
     static constexpr int CHUNKS = CC / 8;     // 16-byte chunks per row
     static constexpr int KSUB = CC / 16;      // MFMA k-steps per step
     static constexpr int WVEC = BM * CHUNKS / kThreads;
-    static constexpr int HALO_BYTES = kLdsBytes - 2 * BM * ROW - kSinkBytes;
+    static constexpr int LDS = lds_budget(OCC);
+    static constexpr int HALO_BYTES = LDS - 2 * BM * ROW - kSinkBytes;
     static_assert(BM * CHUNKS % kThreads == 0, "weight tile must split evenly");
     static_assert(HALO_BYTES > 0, "LDS budget");
 };
 
-template <bool CL, int WAVES_M, int WM, int WN, int CC, int NCH_ITEMS, int NHWC_VECS>
-__global__ __launch_bounds__(kThreads, 1) void igemm_kernel(const _Float16 *x, const _Float16 *__restrict__ wp,
+template <bool CL, int WAVES_M, int WM, int WN, int CC, int NCH_ITEMS, int NHWC_VECS, int OCC, bool PAIR>
+__global__ __launch_bounds__(kThreads, OCC) void igemm_kernel(const _Float16 *x, const _Float16 *__restrict__ wp,
                                                             const _Float16 *__restrict__ bias,
                                                             _Float16 *__restrict__ y, IgArgs p)
 {
-    using Cfg = IgCfg<CL, WAVES_M, WM, WN, CC, NCH_ITEMS, NHWC_VECS>;
+    using Cfg = IgCfg<CL, WAVES_M, WM, WN, CC, NCH_ITEMS, NHWC_VECS, OCC>;
     constexpr int WAVES_N = Cfg::WAVES_N, BM = Cfg::BM, BN = Cfg::BN, ROW = Cfg::ROW;
     constexpr int CHUNKS = Cfg::CHUNKS, KSUB = Cfg::KSUB, WVEC = Cfg::WVEC;
     (void)WAVES_N;
+    static_assert(!PAIR || (!CL && WAVES_M == 2), "column-phase pairs: channels-first, two wave rows");
+    constexpr int BMM = PAIR ? BM / 2 : BM;  // output channels per block
 
     // One LDS array: two weight-tile buffers, the halo buffer, and a per-lane sink for
     // halo stores that have no destination (keeps those stores branch-free).  After the
     // main loop the whole array holds the output tile.
-    __shared__ __attribute__((aligned(16))) unsigned char lds[kLdsBytes];
+    __shared__ __attribute__((aligned(16))) unsigned char lds[Cfg::LDS];
     auto lds_w = [&](int buf) -> unsigned char * { return lds + buf * (BM * ROW); };
     unsigned char *const lds_h = lds + 2 * BM * ROW;
     unsigned char *const lds_sink = lds_h + Cfg::HALO_BYTES;
@@ -139,7 +149,7 @@ __global__ __launch_bounds__(kThreads, 1) void igemm_kernel(const _Float16 *x, c
         while (v >= p.ph_start[ph + 1]) ++ph;
         local = v - p.ph_start[ph];
     }
-    const int r0 = p.ph_r[ph][0], r1 = p.ph_r[ph][1], r2 = p.ph_r[ph][2];
+    const int r0 = p.ph_r[ph][0], r1 = p.ph_r[ph][1], r2 = p.ph_r[ph][2];  // PAIR: r2 = 0
     const int k00 = p.tk0[0][r0], k01 = p.tk0[1][r1], k02 = p.tk0[2][r2];
     const int ks0 = p.kstep[0], ks1 = p.kstep[1], ks2 = p.kstep[2];
     const int b00 = p.tb0[0][r0], bs0 = p.bstep[0], bs1 = p.bstep[1], bs2 = p.bstep[2];
@@ -163,7 +173,13 @@ __global__ __launch_bounds__(kThreads, 1) void igemm_kernel(const _Float16 *x, c
     const int mt = rest / p.G;
 
     const int b1max = p.tb0[1][r1], b1min = nt1 ? b1max - (nt1 - 1) * bs1 : b1max;
-    const int b2max = p.tb0[2][r2], b2min = nt2 ? b2max - (nt2 - 1) * bs2 : b2max;
+    int b2max = p.tb0[2][r2], b2min = nt2 ? b2max - (nt2 - 1) * bs2 : b2max;
+    if (PAIR) {  // the halo spans the taps of both column phases (same tap count)
+        b2max = max(b2max, int(p.tb0[2][1]));
+        b2min = min(b2min, p.tb0[2][1] - (nt2 - 1) * bs2);
+    }
+    // PAIR: column shift of this wave's phase inside the halo
+    const int cshift = PAIR ? p.tb0[2][wm] - (nt2 - 1) * bs2 - b2min : 0;
     if (tl.seg) {
         tl.row_lo = pt / tpr;
         tl.col_lo = (pt % tpr) * BN;
@@ -239,15 +255,32 @@ __global__ __launch_bounds__(kThreads, 1) void igemm_kernel(const _Float16 *x, c
 
     // ---------------- weight tile: BM rows x CC channels of Wp ----------------
     const size_t wrow0 = size_t(g) * p.T;
+    // PAIR: rows [0, BMM) hold column phase 0's tap, rows [BMM, BM) phase 1's tap; the
+    // loads k < WVEC/2 of every thread cover exactly the first half.
+    static_assert(!PAIR || (WVEC % 2 == 0 && (WVEC / 2) * kThreads == BMM * CHUNKS), "phase halves");
     auto load_w = [&](const StepIdx &q, u32x4 *reg) {
-        const int tflat = ((k00 + q.t0 * ks0) * p.K[1] + (k01 + q.t1 * ks1)) * p.K[2] + (k02 + q.t2 * ks2);
-        const size_t row0 = (wrow0 + tflat) * p.Mgp + size_t(mt) * BM;
-        const u32x4 *src = reinterpret_cast<const u32x4 *>(wp + row0 * p.Cgp + size_t(q.chunk) * CC);
         const int stride_vec = p.Cgp / 8;  // 16-byte vectors per Wp row
+        if constexpr (!PAIR) {
+            const int tflat = ((k00 + q.t0 * ks0) * p.K[1] + (k01 + q.t1 * ks1)) * p.K[2] + (k02 + q.t2 * ks2);
+            const size_t row0 = (wrow0 + tflat) * p.Mgp + size_t(mt) * BM;
+            const u32x4 *src = reinterpret_cast<const u32x4 *>(wp + row0 * p.Cgp + size_t(q.chunk) * CC);
 #pragma unroll
-        for (int k = 0; k < WVEC; ++k) {
-            const int u = tid + k * kThreads;
-            reg[k] = src[(u / CHUNKS) * stride_vec + (u % CHUNKS)];
+            for (int k = 0; k < WVEC; ++k) {
+                const int u = tid + k * kThreads;
+                reg[k] = src[(u / CHUNKS) * stride_vec + (u % CHUNKS)];
+            }
+        } else {
+            const int tb = ((k00 + q.t0 * ks0) * p.K[1] + (k01 + q.t1 * ks1)) * p.K[2] + q.t2 * ks2;
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {  // column phase h: WVEC / 2 loads
+                const size_t row0 = (wrow0 + tb + p.tk0[2][h]) * p.Mgp + size_t(mt) * BMM;
+                const u32x4 *src = reinterpret_cast<const u32x4 *>(wp + row0 * p.Cgp + size_t(q.chunk) * CC);
+#pragma unroll
+                for (int k = 0; k < WVEC / 2; ++k) {
+                    const int u = tid + k * kThreads;
+                    reg[h * (WVEC / 2) + k] = src[(u / CHUNKS) * stride_vec + (u % CHUNKS)];
+                }
+            }
         }
     };
     auto store_w = [&](int buf, const u32x4 *reg) {
@@ -370,7 +403,7 @@ __global__ __launch_bounds__(kThreads, 1) void igemm_kernel(const _Float16 *x, c
         // MFMAs of one step: weight tile from buffer buf, the halo window of the step's taps
         auto mma_step = [&](const StepIdx &cur, int buf) {
             // tap shift inside the halo: (beta - beta_min) rows and columns
-            const int toff = ((nt1 - 1 - cur.t1) * bs1 * tl.HC + (nt2 - 1 - cur.t2) * bs2) * ROW;
+            const int toff = ((nt1 - 1 - cur.t1) * bs1 * tl.HC + (nt2 - 1 - cur.t2) * bs2 + cshift) * ROW;
             const unsigned char *hb = lds_h + toff;
             const unsigned char *wb = lds_w(buf) + (wm * WM * 32 + (lane & 31)) * ROW + (lane >> 5) * 16;
             f16x8 a[2][WM], b[2][WN];
@@ -483,13 +516,14 @@ __global__ __launch_bounds__(kThreads, 1) void igemm_kernel(const _Float16 *x, c
     // is then stored with 16-byte vectors along the contiguous output direction.
     // tile layout (pitch padded by 8 elements against bank conflicts):
     //   CL -> [pixel][m] (m contiguous);  NC -> [m][pixel] (pixel contiguous)
-    constexpr int TP = (CL ? BM : BN) + 8;
-    static_assert((CL ? BN : BM) * TP * 2 + BM * 4 <= kLdsBytes, "output tile must fit in LDS");
+    // PAIR -> [m][pixel, phase] (the block's output rows, contiguous)
+    constexpr int TP = (CL ? BM : (PAIR ? 2 * BN : BN)) + 8;
+    static_assert((CL ? BN : BMM) * TP * 2 + BMM * 4 <= Cfg::LDS, "output tile must fit in LDS");
     __syncthreads();  // every wave is done reading the operand buffers
-    float *const sbias = reinterpret_cast<float *>(lds + (CL ? BN : BM) * TP * 2);
+    float *const sbias = reinterpret_cast<float *>(lds + (CL ? BN : BMM) * TP * 2);
     _Float16 *const stile = reinterpret_cast<_Float16 *>(lds);
-    for (int mm = tid; mm < BM; mm += kThreads) {
-        const int mloc = mt * BM + mm;
+    for (int mm = tid; mm < BMM; mm += kThreads) {
+        const int mloc = mt * BMM + mm;
         sbias[mm] = (bias && mloc < p.Mg) ? float(bias[g * p.Mg + mloc]) : 0.0f;
     }
     __syncthreads();
@@ -500,7 +534,7 @@ __global__ __launch_bounds__(kThreads, 1) void igemm_kernel(const _Float16 *x, c
             const int pl = (wn * WN + j) * 32 + (lane & 31);
 #pragma unroll
             for (int rg = 0; rg < 4; ++rg) {
-                const int ml = wm * WM * 32 + i * 32 + rg * 8 + (lane >> 5) * 4;  // 4 consecutive channels
+                const int ml = (PAIR ? 0 : wm * WM * 32) + i * 32 + rg * 8 + (lane >> 5) * 4;  // 4 consecutive channels
                 _Float16 v[4];
 #pragma unroll
                 for (int e = 0; e < 4; ++e) v[e] = _Float16(acc[i][j][rg * 4 + e] + sbias[ml + e]);
@@ -511,6 +545,9 @@ __global__ __launch_bounds__(kThreads, 1) void igemm_kernel(const _Float16 *x, c
                     const unsigned w1 = unsigned(__builtin_bit_cast(unsigned short, v[2])) |
                                         (unsigned(__builtin_bit_cast(unsigned short, v[3])) << 16);
                     *reinterpret_cast<u32x2 *>(&stile[pl * TP + ml]) = u32x2{w0, w1};
+                } else if (PAIR) {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) stile[(ml + e) * TP + 2 * pl + wm] = v[e];
                 } else {
 #pragma unroll
                     for (int e = 0; e < 4; ++e) stile[(ml + e) * TP + pl] = v[e];
@@ -523,14 +560,33 @@ __global__ __launch_bounds__(kThreads, 1) void igemm_kernel(const _Float16 *x, c
     const size_t opix = size_t(p.O[0]) * O1 * O2;
     const int o0 = r0 + p.s[0] * j0;
     const int npix = tl.q1 - tl.q0;
-    const int mvalid = min(BM, p.Mg - mt * BM);
+    const int mvalid = min(BMM, p.Mg - mt * BMM);
     auto pixel_offset = [&](int pl) -> size_t {  // output pixel index of tile pixel pl
         const int q = tl.q0 + pl;
         const int row = tl.seg ? tl.row_lo : q / J2;
         const int col = q - row * J2;
         return (size_t(o0) * O1 + (r1 + p.s[1] * row)) * O2 + (r2 + p.s[2] * col);
     };
-    if (CL) {
+    if (PAIR) {
+        // both column phases of each tile pixel: 2 * npix consecutive outputs per tile row
+        // segment; 16-byte vectors when rows are whole vectors (then no vector crosses a row)
+        const bool vec = (O2 % 8 == 0) && (tl.q0 % 4 == 0) && (npix % 4 == 0) &&
+                         (reinterpret_cast<uintptr_t>(y) % 16 == 0);
+        if (vec) {
+            const int per = npix / 4;
+            for (int u = tid; u < mvalid * per; u += kThreads) {
+                const int ml = u / per, v4 = u - ml * per;
+                const size_t off = (size_t(n) * p.M + g * p.Mg + mt * BMM + ml) * opix + pixel_offset(v4 * 4);
+                *reinterpret_cast<u32x4 *>(y + off) = *reinterpret_cast<const u32x4 *>(&stile[ml * TP + v4 * 8]);
+            }
+        } else {
+            for (int u = tid; u < mvalid * 2 * npix; u += kThreads) {
+                const int ml = u / (2 * npix), e2 = u - ml * (2 * npix);
+                y[(size_t(n) * p.M + g * p.Mg + mt * BMM + ml) * opix + pixel_offset(e2 >> 1) + (e2 & 1)] =
+                    stile[ml * TP + e2];
+            }
+        }
+    } else if (CL) {
         // rows of BM channels per pixel: 16-byte vectors when the run is aligned
         const bool vec = (p.M % 8 == 0) && ((g * p.Mg + mt * BM) % 8 == 0) && (mvalid % 8 == 0) &&
                          (reinterpret_cast<uintptr_t>(y) % 16 == 0);
@@ -621,34 +677,35 @@ __global__ __launch_bounds__(256) void pack_w_kernel(const _Float16 *__restrict_
 
 // ---------------- host-side planning ----------------
 struct Config {
-    int waves_m, wm, wn, cc, nch_items, nhwc_vecs;
+    int waves_m, wm, wn, cc, nch_items, nhwc_vecs, occ;
     int bm() const { return waves_m * wm * 32; }
     int bn() const { return (4 / waves_m) * wn * 32; }
     int row() const { return cc * 2 + 16; }
     int chunks() const { return cc / 8; }
-    int halo_bytes() const { return kLdsBytes - 2 * bm() * row() - kSinkBytes; }
+    int halo_bytes() const { return lds_budget(occ) - 2 * bm() * row() - kSinkBytes; }
 };
 
 // The two compiled configurations (their template arguments must match launch_igemm).
-constexpr Config kWide{2, 4, 4, 64, 2, 14};    // 256 x 256 block, 128 x 128 per wave, 64 ch/step
-constexpr Config kNarrow{1, 2, 4, 32, 2, 12};  // 64 x 512 block, 64 x 128 per wave, 32 ch/step
+constexpr Config kWide{2, 4, 4, 64, 2, 14, 1};    // 256 x 256 block, 128 x 128 per wave, 64 ch/step
+constexpr Config kNarrow{1, 2, 4, 32, 2, 12, 1};  // 64 x 512 block, 64 x 128 per wave, 32 ch/step
 
 Config pick_config(const Geom &g) { return g.Mg > 64 ? kWide : kNarrow; }
 
 struct Plan {
     Config cfg;
+    bool pair;  // column-phase pairs (see IgCfg)
     IgArgs a;
     size_t ws_bytes;
 };
 
-bool make_plan(const Geom &g, Plan *pl, std::string *why)
+bool make_plan(const Geom &g, bool cl, Plan *pl, std::string *why)
 {
     auto no = [&](const char *m) {
         *why = m;
         return false;
     };
     const Config cfg = pick_config(g);
-    const int BM = cfg.bm(), BN = cfg.bn();
+    const int BN = cfg.bn();
     std::memset(&pl->a, 0, sizeof(pl->a));
     IgArgs &a = pl->a;
     for (int t = 0; t < kAxes; ++t) {
@@ -682,8 +739,12 @@ bool make_plan(const Geom &g, Plan *pl, std::string *why)
     a.T = int(g.taps());
     a.nchunk = int((g.Cg + cfg.cc - 1) / cfg.cc);
     a.Cgp = a.nchunk * cfg.cc;
-    a.mtiles = int((g.Mg + BM - 1) / BM);
-    a.Mgp = a.mtiles * BM;
+    // Column-phase pairs: channels-first output, stride 2 on the innermost axis, an even
+    // output width (both phases then have the same pixel grid) and equal tap counts.
+    const bool pair = !cl && cfg.waves_m == 2 && g.s[2] == 2 && g.O[2] % 2 == 0 && a.ntap[2][0] == a.ntap[2][1];
+    const int BMM = pair ? cfg.bm() / 2 : cfg.bm();
+    a.mtiles = int((g.Mg + BMM - 1) / BMM);
+    a.Mgp = a.mtiles * BMM;
 
     // phases with outputs, heaviest (most taps) first
     struct PhaseInfo {
@@ -693,7 +754,7 @@ bool make_plan(const Geom &g, Plan *pl, std::string *why)
     int nph = 0;
     for (int r0 = 0; r0 < g.s[0]; ++r0)
         for (int r1 = 0; r1 < g.s[1]; ++r1)
-            for (int r2 = 0; r2 < g.s[2]; ++r2) {
+            for (int r2 = 0; r2 < (pair ? 1 : g.s[2]); ++r2) {  // a pair is listed as r2 = 0
                 if (r0 >= g.O[0] || r1 >= g.O[1] || r2 >= g.O[2]) continue;
                 if (nph == kMaxPh) return no("more than 64 phases");
                 PhaseInfo &pi = list[nph++];
@@ -713,15 +774,17 @@ bool make_plan(const Geom &g, Plan *pl, std::string *why)
                 // halo capacity check (largest tile of this phase)
                 const int n1 = a.ntap[1][r1], n2 = a.ntap[2][r2];
                 const int e1 = n1 ? (n1 - 1) * a.bstep[1] : 0;
-                const int e2 = n2 ? (n2 - 1) * a.bstep[2] : 0;
+                int e2 = n2 ? (n2 - 1) * a.bstep[2] : 0;
+                if (pair && n2)  // union of both phases' columns
+                    e2 = std::max<int>(a.tb0[2][0], a.tb0[2][1]) - std::min<int>(a.tb0[2][0], a.tb0[2][1]) + e2;
                 const int HR = seg ? 1 + e1 : std::min<int>(J1, (BN + J2 - 1) / J2 + 1) + e1;
                 const int HC = seg ? BN + e2 : J2 + e2;
                 if ((long long)HR * HC * cfg.row() > cfg.halo_bytes()) return no("input halo exceeds LDS");
-                if ((long long)HR * HC * cfg.chunks() > (long long)cfg.nhwc_vecs * kThreads)
-                    return no("halo too large");
+                if (cl && (long long)HR * HC * cfg.chunks() > (long long)cfg.nhwc_vecs * kThreads)
+                    return no("input halo exceeds the loads of one block");
                 const int nvc = (HC + 7) / 8 + 1;
-                if ((long long)HR * nvc * cfg.chunks() > (long long)cfg.nch_items * kThreads)
-                    return no("halo too large");
+                if (!cl && (long long)HR * nvc * cfg.chunks() > (long long)cfg.nch_items * kThreads)
+                    return no("input halo exceeds the loads of one block");
             }
     std::stable_sort(list, list + nph, [](const PhaseInfo &x, const PhaseInfo &y) { return x.taps > y.taps; });
     a.nphase = nph;
@@ -740,15 +803,16 @@ bool make_plan(const Geom &g, Plan *pl, std::string *why)
     a.nblocks = int(total);
     a.interleave = uniform ? 1 : 0;
     pl->cfg = cfg;
+    pl->pair = pair;
     pl->ws_bytes = size_t(a.G) * a.T * a.Mgp * a.Cgp * sizeof(_Float16);
     return true;
 }
 
-template <bool CL, int WAVES_M, int WM, int WN, int CC, int NCH_ITEMS, int NHWC_VECS>
+template <bool CL, int WAVES_M, int WM, int WN, int CC, int NCH_ITEMS, int NHWC_VECS, int OCC, bool PAIR = false>
 void launch_cfg(const IgArgs &a, const _Float16 *x, const _Float16 *wp, const _Float16 *b, _Float16 *y,
                 hipStream_t st)
 {
-    hipLaunchKernelGGL((igemm_kernel<CL, WAVES_M, WM, WN, CC, NCH_ITEMS, NHWC_VECS>), dim3(unsigned(a.nblocks)),
+    hipLaunchKernelGGL((igemm_kernel<CL, WAVES_M, WM, WN, CC, NCH_ITEMS, NHWC_VECS, OCC, PAIR>), dim3(unsigned(a.nblocks)),
                        dim3(kThreads), 0, st, x, wp, b, y, a);
 }
 
@@ -774,7 +838,7 @@ bool igemm_supports(const Geom &g, ct_dtype dt, bool cl, const void *x, std::str
         return false;
     }
     Plan pl;
-    return make_plan(g, &pl, why);
+    return make_plan(g, cl, &pl, why);
 }
 
 size_t igemm_workspace_bytes(const Geom &g, ct_dtype dt)
@@ -782,7 +846,11 @@ size_t igemm_workspace_bytes(const Geom &g, ct_dtype dt)
     if (dt != CT_FLOAT16) return 0;  // the float32 kernel reads W in place
     Plan pl;
     std::string why;
-    return make_plan(g, &pl, &why) ? pl.ws_bytes : 0;
+    // the larger of the two layouts' packed weights (column-phase pairs pad M less)
+    size_t bytes = 0;
+    for (const bool cl : {false, true})
+        if (make_plan(g, cl, &pl, &why)) bytes = std::max(bytes, pl.ws_bytes);
+    return bytes;
 }
 
 ct_status launch_igemm(const Geom &g, ct_dtype dt, bool cl, const void *x, const void *w, const void *bias,
@@ -790,7 +858,7 @@ ct_status launch_igemm(const Geom &g, ct_dtype dt, bool cl, const void *x, const
 {
     if (dt == CT_FLOAT32) return launch_igemm32(g, cl, x, w, bias, y, st, err);
     Plan pl;
-    if (!make_plan(g, &pl, err)) return CT_EUNSUPPORTED;
+    if (!make_plan(g, cl, &pl, err)) return CT_EUNSUPPORTED;
     bool owned = false;
     void *wsp = workspace;
     if (!wsp) {
@@ -821,11 +889,12 @@ ct_status launch_igemm(const Geom &g, ct_dtype dt, bool cl, const void *x, const
     const Config c = pl.cfg;
     mark_before(st);
     if (c.waves_m == kWide.waves_m) {
-        if (cl) launch_cfg<true, 2, 4, 4, 64, 2, 14>(pl.a, xt, wpk, bt, yt, st);
-        else launch_cfg<false, 2, 4, 4, 64, 2, 14>(pl.a, xt, wpk, bt, yt, st);
+        if (cl) launch_cfg<true, 2, 4, 4, 64, 2, 14, 1>(pl.a, xt, wpk, bt, yt, st);
+        else if (pl.pair) launch_cfg<false, 2, 4, 4, 64, 2, 14, 1, true>(pl.a, xt, wpk, bt, yt, st);
+        else launch_cfg<false, 2, 4, 4, 64, 2, 14, 1>(pl.a, xt, wpk, bt, yt, st);
     } else {
-        if (cl) launch_cfg<true, 1, 2, 4, 32, 2, 12>(pl.a, xt, wpk, bt, yt, st);
-        else launch_cfg<false, 1, 2, 4, 32, 2, 12>(pl.a, xt, wpk, bt, yt, st);
+        if (cl) launch_cfg<true, 1, 2, 4, 32, 2, 12, 1>(pl.a, xt, wpk, bt, yt, st);
+        else launch_cfg<false, 1, 2, 4, 32, 2, 12, 1>(pl.a, xt, wpk, bt, yt, st);
     }
     mark_after(st);
     hipError_t e = hipGetLastError();
