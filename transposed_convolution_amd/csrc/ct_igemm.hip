@@ -54,6 +54,7 @@ constexpr int kLdsBytes = 160 * 1024 - 2048;
 // LDS bytes one block may use when OCC blocks share a compute unit (160 KB of LDS per CU)
 constexpr int lds_budget(int occ) { return occ == 1 ? kLdsBytes : 160 * 1024 / occ - 1024; }
 constexpr int kSinkBytes = 64 * 16;
+constexpr int kBiasBytes = 256 * 4;      // the block's bias as float32 (at most 256 channels)
 
 struct IgArgs {
     int N, C, M, Cg, Mg, Cgp, Mgp, T, G;
@@ -107,7 +108,7 @@ struct IgCfg {
     static constexpr int KSUB = CC / 16;      // MFMA k-steps per step
     static constexpr int WVEC = BM * CHUNKS / kThreads;
     static constexpr int LDS = lds_budget(OCC);
-    static constexpr int HALO_BYTES = LDS - 2 * BM * ROW - kSinkBytes;
+    static constexpr int HALO_BYTES = LDS - 2 * BM * ROW - kSinkBytes - kBiasBytes;
     static_assert(BM * CHUNKS % kThreads == 0, "weight tile must split evenly");
     static_assert(HALO_BYTES > 0, "LDS budget");
 };
@@ -131,6 +132,8 @@ __global__ __launch_bounds__(kThreads, OCC) void igemm_kernel(const _Float16 *x,
     auto lds_w = [&](int buf) -> unsigned char * { return lds + buf * (BM * ROW); };
     unsigned char *const lds_h = lds + 2 * BM * ROW;
     unsigned char *const lds_sink = lds_h + Cfg::HALO_BYTES;
+    float *const sbias = reinterpret_cast<float *>(lds_sink + kSinkBytes);  // kept to the end
+    static_assert(BM <= 256, "bias region");
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -388,6 +391,13 @@ __global__ __launch_bounds__(kThreads, OCC) void igemm_kernel(const _Float16 *x,
         }
     };
 
+    // The bias of the block's channels, staged once (read in the epilogue; the first
+    // barrier below, or the epilogue's own, makes it visible).
+    for (int mm = tid; mm < BMM; mm += kThreads) {
+        const int m = mt * BMM + mm;
+        sbias[mm] = (bias && m < p.Mg) ? float(bias[g * p.Mg + m]) : 0.0f;
+    }
+
     // ---------------- main loop ----------------
     if (nsteps > 0) {
         u32x4 wreg[WVEC];
@@ -511,51 +521,16 @@ __global__ __launch_bounds__(kThreads, OCC) void igemm_kernel(const _Float16 *x,
     }
 
     // ---------------- epilogue: bias, round once, store ----------------
-    // The block's BM x BN output tile goes through LDS (free once the main loop is done):
-    // bias is staged once, each wave writes its accumulators as float16, and the tile
-    // is then stored with 16-byte vectors along the contiguous output direction.
-    // tile layout (pitch padded by 8 elements against bank conflicts):
-    //   CL -> [pixel][m] (m contiguous);  NC -> [m][pixel] (pixel contiguous)
-    // PAIR -> [m][pixel, phase] (the block's output rows, contiguous)
-    constexpr int TP = (CL ? BM : (PAIR ? 2 * BN : BN)) + 8;
-    static_assert((CL ? BN : BMM) * TP * 2 + BMM * 4 <= Cfg::LDS, "output tile must fit in LDS");
-    __syncthreads();  // every wave is done reading the operand buffers
-    float *const sbias = reinterpret_cast<float *>(lds + (CL ? BN : BMM) * TP * 2);
-    _Float16 *const stile = reinterpret_cast<_Float16 *>(lds);
-    for (int mm = tid; mm < BMM; mm += kThreads) {
-        const int mloc = mt * BMM + mm;
-        sbias[mm] = (bias && mloc < p.Mg) ? float(bias[g * p.Mg + mloc]) : 0.0f;
-    }
-    __syncthreads();
+    // Accumulator element r of tile (i, j) belongs to channel i*32 + (r/4)*8 + (lane/32)*4
+    // + r%4 of the wave's rows; the bias is added in float32 before the one rounding.
+    typedef float f32x4 __attribute__((ext_vector_type(4)));
+    if (nsteps == 0) __syncthreads();  // no main-loop barrier made the staged bias visible
+    const int mwave = PAIR ? 0 : wm * WM * 32;  // first channel of the wave inside the tile
+    auto bias_of = [&](int i, int rg, float *bv) {
+        const f32x4 b4 = *reinterpret_cast<const f32x4 *>(&sbias[mwave + i * 32 + rg * 8 + (lane >> 5) * 4]);
 #pragma unroll
-    for (int i = 0; i < WM; ++i)
-#pragma unroll
-        for (int j = 0; j < WN; ++j) {
-            const int pl = (wn * WN + j) * 32 + (lane & 31);
-#pragma unroll
-            for (int rg = 0; rg < 4; ++rg) {
-                const int ml = (PAIR ? 0 : wm * WM * 32) + i * 32 + rg * 8 + (lane >> 5) * 4;  // 4 consecutive channels
-                _Float16 v[4];
-#pragma unroll
-                for (int e = 0; e < 4; ++e) v[e] = _Float16(acc[i][j][rg * 4 + e] + sbias[ml + e]);
-                if (CL) {
-                    typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
-                    const unsigned w0 = unsigned(__builtin_bit_cast(unsigned short, v[0])) |
-                                        (unsigned(__builtin_bit_cast(unsigned short, v[1])) << 16);
-                    const unsigned w1 = unsigned(__builtin_bit_cast(unsigned short, v[2])) |
-                                        (unsigned(__builtin_bit_cast(unsigned short, v[3])) << 16);
-                    *reinterpret_cast<u32x2 *>(&stile[pl * TP + ml]) = u32x2{w0, w1};
-                } else if (PAIR) {
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) stile[(ml + e) * TP + 2 * pl + wm] = v[e];
-                } else {
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) stile[(ml + e) * TP + pl] = v[e];
-                }
-            }
-        }
-    __syncthreads();
-
+        for (int e = 0; e < 4; ++e) bv[e] = b4[e];
+    };
     const int O1 = p.O[1], O2 = p.O[2];
     const size_t opix = size_t(p.O[0]) * O1 * O2;
     const int o0 = r0 + p.s[0] * j0;
@@ -567,6 +542,72 @@ __global__ __launch_bounds__(kThreads, OCC) void igemm_kernel(const _Float16 *x,
         const int col = q - row * J2;
         return (size_t(o0) * O1 + (r1 + p.s[1] * row)) * O2 + (r2 + p.s[2] * col);
     };
+    if constexpr (CL) {
+        // Channels-last: straight from the accumulators.  A lane holds 4 consecutive
+        // channels of one pixel per (tile, row group); lanes l and l + 32 hold adjacent
+        // quadruples, so each store instruction writes 16 contiguous bytes per pixel.
+        typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+        const bool vec = (p.M % 4 == 0) && ((g * p.Mg + mt * BM) % 4 == 0) && (reinterpret_cast<uintptr_t>(y) % 8 == 0);
+        const int mrow = wm * WM * 32;  // first channel of the wave inside the tile
+        _Float16 *yp[WN];
+#pragma unroll
+        for (int j = 0; j < WN; ++j) {
+            const int pl = min((wn * WN + j) * 32 + (lane & 31), npix - 1);
+            yp[j] = y + (size_t(n) * opix + pixel_offset(pl)) * p.M + g * p.Mg + mt * BM;
+        }
+#pragma unroll
+        for (int i = 0; i < WM; ++i)
+#pragma unroll
+            for (int rg = 0; rg < 4; ++rg) {
+                const int ml = mrow + i * 32 + rg * 8 + (lane >> 5) * 4;
+                float bv[4];
+                bias_of(i, rg, bv);
+#pragma unroll
+                for (int j = 0; j < WN; ++j) {
+                    if ((wn * WN + j) * 32 + (lane & 31) >= npix) continue;
+                    _Float16 v[4];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) v[e] = _Float16(acc[i][j][rg * 4 + e] + bv[e]);
+                    if (vec && ml + 4 <= mvalid) {
+                        const unsigned w0 = unsigned(__builtin_bit_cast(unsigned short, v[0])) |
+                                            (unsigned(__builtin_bit_cast(unsigned short, v[1])) << 16);
+                        const unsigned w1 = unsigned(__builtin_bit_cast(unsigned short, v[2])) |
+                                            (unsigned(__builtin_bit_cast(unsigned short, v[3])) << 16);
+                        *reinterpret_cast<u32x2 *>(yp[j] + ml) = u32x2{w0, w1};
+                    } else {
+#pragma unroll
+                        for (int e = 0; e < 4; ++e)
+                            if (ml + e < mvalid) yp[j][ml + e] = v[e];
+                    }
+                }
+            }
+        return;
+    }
+    // Channels-first: the block's output tile goes through LDS (free once the main loop is
+    // done) and is stored with 16-byte vectors along the contiguous pixel direction.
+    // tile layout (pitch padded by 8 elements against bank conflicts):
+    //   NC -> [m][pixel];  PAIR -> [m][pixel, phase] (the block's output rows, contiguous)
+    constexpr int TP = (PAIR ? 2 * BN : BN) + 8;
+    static_assert(BMM * TP * 2 <= Cfg::LDS - kBiasBytes, "output tile must fit in LDS below the bias");
+    __syncthreads();  // every wave is done reading the operand buffers
+    _Float16 *const stile = reinterpret_cast<_Float16 *>(lds);
+#pragma unroll
+    for (int i = 0; i < WM; ++i)
+#pragma unroll
+        for (int rg = 0; rg < 4; ++rg) {
+            const int ml = (PAIR ? 0 : wm * WM * 32) + i * 32 + rg * 8 + (lane >> 5) * 4;  // 4 consecutive channels
+            float bv[4];
+            bias_of(i, rg, bv);
+#pragma unroll
+            for (int j = 0; j < WN; ++j) {
+                const int pl = (wn * WN + j) * 32 + (lane & 31);
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    stile[(ml + e) * TP + (PAIR ? 2 * pl + wm : pl)] = _Float16(acc[i][j][rg * 4 + e] + bv[e]);
+            }
+        }
+    __syncthreads();
+
     if (PAIR) {
         // both column phases of each tile pixel: 2 * npix consecutive outputs per tile row
         // segment; 16-byte vectors when rows are whole vectors (then no vector crosses a row)
@@ -584,23 +625,6 @@ __global__ __launch_bounds__(kThreads, OCC) void igemm_kernel(const _Float16 *x,
                 const int ml = u / (2 * npix), e2 = u - ml * (2 * npix);
                 y[(size_t(n) * p.M + g * p.Mg + mt * BMM + ml) * opix + pixel_offset(e2 >> 1) + (e2 & 1)] =
                     stile[ml * TP + e2];
-            }
-        }
-    } else if (CL) {
-        // rows of BM channels per pixel: 16-byte vectors when the run is aligned
-        const bool vec = (p.M % 8 == 0) && ((g * p.Mg + mt * BM) % 8 == 0) && (mvalid % 8 == 0) &&
-                         (reinterpret_cast<uintptr_t>(y) % 16 == 0);
-        if (vec) {
-            const int per = mvalid / 8;
-            for (int u = tid; u < npix * per; u += kThreads) {
-                const int pl = u / per, c8 = u - pl * per;
-                const size_t off = (size_t(n) * opix + pixel_offset(pl)) * p.M + g * p.Mg + mt * BM + c8 * 8;
-                *reinterpret_cast<u32x4 *>(y + off) = *reinterpret_cast<const u32x4 *>(&stile[pl * TP + c8 * 8]);
-            }
-        } else {
-            for (int u = tid; u < npix * mvalid; u += kThreads) {
-                const int pl = u / mvalid, ml = u - pl * mvalid;
-                y[(size_t(n) * opix + pixel_offset(pl)) * p.M + g * p.Mg + mt * BM + ml] = stile[pl * TP + ml];
             }
         }
     } else {
@@ -682,7 +706,7 @@ struct Config {
     int bn() const { return (4 / waves_m) * wn * 32; }
     int row() const { return cc * 2 + 16; }
     int chunks() const { return cc / 8; }
-    int halo_bytes() const { return lds_budget(occ) - 2 * bm() * row() - kSinkBytes; }
+    int halo_bytes() const { return lds_budget(occ) - 2 * bm() * row() - kSinkBytes - kBiasBytes; }
 };
 
 // The two compiled configurations (their template arguments must match launch_igemm).
