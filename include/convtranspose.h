@@ -69,6 +69,23 @@ typedef enum {
 } ct_kernel;
 
 /*
+ * Activation applied to every output element after the bias, in the accumulation
+ * precision (float32), before the one rounding into T (ClikaRT "conv_transpose" API page:
+ * its `activation` argument, default Identity; the pages do not list the other values,
+ * so these are the elementwise functions with a plain closed form):
+ *   CT_ACT_IDENTITY    v
+ *   CT_ACT_RELU        v > 0 ? v : 0
+ *   CT_ACT_LEAKY_RELU  v >= 0 ? v : p0 * v          (p0 = slope, finite)
+ *   CT_ACT_CLIP        v < p0 ? p0 : (v > p1 ? p1 : v)   (p0 <= p1, both finite)
+ */
+typedef enum {
+    CT_ACT_IDENTITY = 0,
+    CT_ACT_RELU = 1,
+    CT_ACT_LEAKY_RELU = 2,
+    CT_ACT_CLIP = 3
+} ct_activation;
+
+/*
  * Resolve the output shape (README Attributes table and Outputs section).  Host only;
  * touches no device.
  *   nsp            spatial rank n, 1..3
@@ -148,6 +165,25 @@ ct_status convtranspose_nd_with_kernel(ct_kernel kernel, ct_dtype dtype, int nsp
                                        const int64_t *output_shape, const int64_t *kernel_shape,
                                        int64_t group, void *workspace, size_t workspace_bytes,
                                        void *stream);
+
+/*
+ * As convtranspose_nd_with_kernel, with an activation fused into the output stage of
+ * whichever kernel runs (see ct_activation): y = act(ConvTranspose(x, w, bias)), the
+ * activation evaluated in float32 on the accumulated value plus bias, then one rounding
+ * into T.  act_p0 / act_p1 are the activation's parameters (ignored where it has none).
+ * An unknown activation, a non-finite parameter or p0 > p1 for CT_ACT_CLIP is
+ * CT_EINVAL (nothing launched).  With CT_ACT_IDENTITY this is exactly
+ * convtranspose_nd_with_kernel.
+ */
+ct_status convtranspose_nd_fused(ct_kernel kernel, ct_dtype dtype, int nsp, int channels_last,
+                                 const void *x, const int64_t *x_shape, const void *w,
+                                 const int64_t *w_shape, const void *bias, void *y,
+                                 const int64_t *y_shape, ct_auto_pad auto_pad,
+                                 const int64_t *strides, const int64_t *dilations,
+                                 const int64_t *pads, const int64_t *output_padding,
+                                 const int64_t *output_shape, const int64_t *kernel_shape,
+                                 int64_t group, ct_activation activation, float act_p0, float act_p1,
+                                 void *workspace, size_t workspace_bytes, void *stream);
 
 /*
  * Workspace bytes convtranspose_nd_with_kernel needs for these arguments and kernel

@@ -176,3 +176,29 @@ def convtranspose_at(x: np.ndarray, w: np.ndarray, bias: Optional[np.ndarray], p
                                      err, 256)
     _check(rc, err)
     return out
+
+
+ACTIVATIONS = ("identity", "relu", "leaky_relu", "clip")
+
+
+def activation(y: np.ndarray, kind: str = "identity", params: Sequence[float] = ()) -> np.ndarray:
+    """The output activation applied elementwise, in fp64, to Y (bias included).
+
+    ClikaRT "conv_transpose" API page: the call takes an ``activation`` argument whose
+    default is Identity; the page does not list the other members, so each one here is
+    the elementwise function of its usual definition:
+      relu        v if v > 0, else 0
+      leaky_relu  v if v >= 0, else slope * v            (params = (slope,))
+      clip        lower if v < lower, upper if v > upper, else v   (params = (lower, upper))
+    """
+    y = np.asarray(y, dtype=np.float64)
+    p = [float(v) for v in params]
+    if kind == "identity" and not p:
+        return y.copy()
+    if kind == "relu" and not p:
+        return np.where(y > 0.0, y, 0.0)
+    if kind == "leaky_relu" and len(p) == 1 and np.isfinite(p[0]):
+        return np.where(y >= 0.0, y, p[0] * y)
+    if kind == "clip" and len(p) == 2 and np.all(np.isfinite(p)) and p[0] <= p[1]:
+        return np.where(y < p[0], p[0], np.where(y > p[1], p[1], y))
+    raise OracleError(f"activation {kind!r} with parameters {params!r} is not defined")

@@ -475,7 +475,36 @@ def pin_rejects_invalid(lib):
         raise AssertionError(f"accepted mismatched shapes {xs2} {ws2}")
 
 
-ALL_PINS = [pin_golden, pin_benchmark_shapes, pin_torch_library, pin_brute_force_gather,
+def pin_activation_closed_forms(lib, seed=22):
+    """The output activations against closed forms built from |v| (not from the
+    comparisons the oracle uses): relu(v) = (v + |v|) / 2, leaky(v) = relu(v) - a relu(-v),
+    clip(v) = lo + relu(v - lo) - relu(v - hi); identity leaves Y alone; undefined
+    parameter sets are refused."""
+    rng = np.random.default_rng(seed)
+    v = np.concatenate([rng.normal(size=500) * 3, [0.0, -0.0, 1.5, -1.5, 2.0, -2.0]])
+    relu = lambda t: (t + np.abs(t)) / 2
+    assert np.array_equal(O.activation(v, "identity"), v)
+    assert np.allclose(O.activation(v, "relu"), relu(v), rtol=0, atol=1e-15)
+    for a in (0.0, 0.01, 0.25, 1.0, -0.5, 3.0):
+        assert np.allclose(O.activation(v, "leaky_relu", (a,)), relu(v) - a * relu(-v), rtol=0, atol=1e-14)
+    for lo, hi in ((-1.0, 1.0), (0.0, 6.0), (-2.0, -2.0), (-0.5, 4.0)):
+        assert np.allclose(O.activation(v, "clip", (lo, hi)), lo + relu(v - lo) - relu(v - hi), rtol=0, atol=1e-14)
+    # applied to a transposed convolution: elementwise on the whole output
+    x = rng.normal(size=(2, 3, 5))
+    w = rng.normal(size=(3, 2, 3))
+    b = rng.normal(size=2)
+    y = O.convtranspose(x, w, b, lib=lib, strides=[2], pads=[1, 0])
+    assert np.allclose(O.activation(y, "relu"), relu(y), rtol=0, atol=1e-14)
+    for kind, params in (("relu", (1.0,)), ("leaky_relu", ()), ("leaky_relu", (np.inf,)),
+                         ("clip", (1.0, 0.0)), ("clip", (0.0,)), ("gelu", ())):
+        try:
+            O.activation(y, kind, params)
+        except O.OracleError:
+            continue
+        raise AssertionError(f"activation {kind} {params} accepted")
+
+
+ALL_PINS = [pin_activation_closed_forms, pin_golden, pin_benchmark_shapes, pin_torch_library, pin_brute_force_gather,
             pin_zero_insertion, pin_numpy_convolve, pin_adjoint, pin_stride1_forward,
             pin_pointwise_matmul, pin_group_split, pin_linearity_translation, pin_useful_macs,
             pin_points_match_whole, pin_rejects_invalid]

@@ -359,6 +359,57 @@ def test_column_phase_pairs(T, case, integer):
         check(got, ref, "f16", integer, f"pair {kernel} x{xs} w{ws} {attrs}")
 
 
+ACT_CASES = [
+    # (name, x_shape, w_shape, attrs, dtype, channels_last, forced kernel)
+    ("igemm16_pair", (2, 64, 9, 16), (64, 96, 4, 4), dict(strides=[2, 2], pads=[1] * 4), "f16", False, "igemm"),
+    ("igemm16_nc", (2, 32, 6, 16), (32, 80, 3, 3), dict(strides=[2, 2], pads=[1] * 4), "f16", False, "igemm"),
+    ("igemm16_cl", (2, 64, 9, 13), (64, 80, 4, 4), dict(strides=[2, 2], pads=[1] * 4), "f16", True, "igemm"),
+    ("igemm16_narrow", (1, 32, 4, 5, 8), (32, 24, 3, 3, 3), dict(strides=[2, 2, 2], pads=[1] * 6,
+                                                                  output_padding=[1] * 3), "f16", False, "igemm"),
+    ("igemm32", (3, 24, 77), (24, 40, 5), dict(strides=[3], dilations=[2], pads=[2, 2], output_padding=[1]),
+     "f32", False, "igemm"),
+    ("igemm32_cl", (2, 16, 6, 7), (16, 24, 3, 3), dict(strides=[2, 2], pads=[1] * 4), "f32", True, "igemm"),
+    ("depthwise", (2, 16, 9, 16), (16, 1, 4, 4), dict(strides=[2, 2], pads=[1] * 4, group=16), "f16", False,
+     "grouped"),
+    ("grouped", (2, 24, 13, 70), (24, 2, 4, 4), dict(strides=[2, 2], pads=[1] * 4, group=12), "f16", False,
+     "grouped"),
+    ("direct16", (1, 6, 5, 7), (6, 5, 3, 2), dict(strides=[2, 3], pads=[1, 0, 0, 1]), "f16", True, "direct"),
+    ("direct32", (2, 4, 9), (4, 3, 4), dict(strides=[2], dilations=[2], pads=[1, 2]), "f32", False, "direct"),
+]
+ACTS = [("relu", ()), ("leaky_relu", (0.25,)), ("clip", (-2.0, 3.0))]
+
+
+@pytest.mark.parametrize("integer", [False, True], ids=["float", "int"])
+@pytest.mark.parametrize("case", ACT_CASES, ids=lambda c: c[0])
+def test_fused_activation(T, case, integer):
+    """The output activation fused into every kernel family's output stage (float32,
+    after the bias, before the one rounding) against the oracle's activation of its
+    fp64 result; integer-valued inputs bit-exact."""
+    name, xs, ws, attrs, dtype, cl, kernel = case
+    rng = np.random.default_rng(zlib.crc32(name.encode()) + integer)
+    gen = (lambda sz: rng.integers(-2, 3, size=sz)) if integer else (lambda sz: rng.normal(size=sz))
+    x = gen(xs).astype(NPT[dtype])
+    w = (gen(ws) * (1 if integer else 0.3)).astype(NPT[dtype])
+    b = gen(ws[1] * attrs.get("group", 1)).astype(NPT[dtype])
+    ref = O.convtranspose(x, w, b, **attrs)
+    dev = torch.device("cuda:0")
+    tx = torch.from_numpy(x).to(dev)
+    if cl:
+        tx = T.to_channels_last(tx)
+    tw, tb = torch.from_numpy(w).to(dev), torch.from_numpy(b).to(dev)
+    for act, params in ACTS:
+        _log(f"[case] activation {name} {act} integer={integer}")
+        y = T.convtranspose_nd(tx, tw, tb, channels_last=cl, kernel=kernel, activation=act, act_params=params,
+                               **attrs)
+        torch.cuda.synchronize()
+        got = y.cpu().numpy().astype(np.float64)
+        check(got, O.activation(ref, act, params), dtype, integer, f"{name} {act}")
+    # the default stays the plain operation
+    y = T.convtranspose_nd(tx, tw, tb, channels_last=cl, kernel=kernel, **attrs)
+    torch.cuda.synchronize()
+    check(y.cpu().numpy().astype(np.float64), ref, dtype, integer, f"{name} identity")
+
+
 def test_repeat_runs_bitwise_identical(T):
     wl = REDUCED[2]
     x, w, b = W.make_inputs(wl)

@@ -135,6 +135,32 @@ def test_validation_errors_launch_nothing(T):
     assert T.convtranspose_last_error() == ""
 
 
+def _fused_call(T, act, p0=0.0, p1=0.0, **kw):
+    """convtranspose_nd_fused with the arguments of _raw_call and an activation."""
+    lib = T.load_library()
+    xs, ws = (1, 4, 5, 5), (4, 3, 3, 3)
+    ys = kw.get("ys") or T.convtranspose_output_shape(xs, ws)[0]
+    at = T._attr_args(2)
+    vp = ctypes.c_void_p
+    return lib.convtranspose_nd_fused(0, 1, 2, 0, vp(256), T._i64(xs), vp(512), T._i64(ws), None, vp(1024),
+                                      T._i64(ys), *at, act, p0, p1, None, 0, None)
+
+
+def test_activation_arguments_validated_before_launch(T):
+    inf, nan = float("inf"), float("nan")
+    assert _fused_call(T, 9) == 1 and "activation" in T.convtranspose_last_error()
+    assert _fused_call(T, -1) == 1
+    assert _fused_call(T, 2, inf) == 1 and "slope" in T.convtranspose_last_error()   # leaky ReLU slope
+    assert _fused_call(T, 2, nan) == 1
+    assert _fused_call(T, 3, 1.0, 0.0) == 1 and "clip" in T.convtranspose_last_error()  # lower > upper
+    assert _fused_call(T, 3, nan, 1.0) == 1
+    assert _fused_call(T, 3, 0.0, inf) == 1
+    # a valid activation still meets the ordinary validation (y_shape mismatch, nothing launched)
+    assert _fused_call(T, 1, ys=(1, 3, 7, 8)) == 2
+    assert _fused_call(T, 3, -1.0, 1.0, ys=(1, 3, 7, 8)) == 2
+    assert set(T.ACTIVATIONS) == set(O.ACTIVATIONS)
+
+
 def test_dispatcher_choices(T):
     lib = T.load_library()
 

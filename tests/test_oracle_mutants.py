@@ -9,6 +9,7 @@ import subprocess
 import sys
 import tempfile
 
+import numpy as np
 import pytest
 
 from oracle import oracle as O
@@ -63,3 +64,26 @@ def test_every_planted_mistake_is_caught():
             res = dict(zip(MUTANTS, ex.map(lambda n: _run_mutant(n, tmp), MUTANTS)))
     missed = {n: out for n, (rc, out) in res.items() if rc != 0}
     assert not missed, f"mutants not caught by any pin: {missed}"
+
+
+ACT_MUTANTS = {
+    # plausible slips in the activation, each planted into a wrapper of the oracle's own
+    "relu_keeps_negatives": lambda f: lambda y, k="identity", p=(): (
+        np.abs(np.asarray(y, dtype=np.float64)) if k == "relu" else f(y, k, p)),
+    "leaky_slope_on_positive_side": lambda f: lambda y, k="identity", p=(): (
+        np.where(np.asarray(y) >= 0, p[0] * np.asarray(y), np.asarray(y)) if k == "leaky_relu" else f(y, k, p)),
+    "clip_bounds_swapped": lambda f: lambda y, k="identity", p=(): (
+        np.minimum(np.maximum(np.asarray(y, dtype=np.float64), p[1]), p[0]) if k == "clip" and len(p) == 2 and p[0] <= p[1]
+        else f(y, k, p)),
+    "clip_upper_only": lambda f: lambda y, k="identity", p=(): (
+        np.minimum(np.asarray(y, dtype=np.float64), p[1]) if k == "clip" and len(p) == 2 and p[0] <= p[1]
+        else f(y, k, p)),
+}
+
+
+@pytest.mark.parametrize("name", sorted(ACT_MUTANTS))
+def test_activation_mistakes_are_caught(name, monkeypatch):
+    import pins
+    monkeypatch.setattr(O, "activation", ACT_MUTANTS[name](O.activation))
+    with pytest.raises(AssertionError):
+        pins.pin_activation_closed_forms(O.load())

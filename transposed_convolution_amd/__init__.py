@@ -23,13 +23,16 @@ __all__ = [
     "ConvTransposeError", "ConvTransposePlan", "convtranspose_nd", "convtranspose_profile_events", "convtranspose_output_shape",
     "convtranspose_useful_macs", "convtranspose_select_kernel", "convtranspose_last_error",
     "convtranspose_kernel_name", "library_path", "load_library", "channels_last_empty",
-    "to_channels_last", "KERNELS",
+    "to_channels_last", "KERNELS", "ACTIVATIONS",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libconvtranspose.so")
 AUTO_PAD = {"NOTSET": 0, "SAME_UPPER": 1, "SAME_LOWER": 2, "VALID": 3}
 KERNELS = {"auto": 0, "direct": 1, "grouped": 2, "igemm": 3, "none": 4}
+# output activation fused into the kernels' output stage (ct_activation), with the number
+# of parameters each takes: leaky_relu (slope,), clip (lower, upper)
+ACTIVATIONS = {"identity": (0, 0), "relu": (1, 0), "leaky_relu": (2, 1), "clip": (3, 2)}
 _DTYPES = {torch.float32: 0, torch.float16: 1}
 _STATUS = {0: "CT_OK", 1: "CT_EINVAL", 2: "CT_ESHAPE", 3: "CT_EUNSUPPORTED", 4: "CT_EDEVICE"}
 _lib = None
@@ -64,12 +67,14 @@ def load_library():
     call = [ctypes.c_int, ctypes.c_int, ctypes.c_int, vp, i64p, vp, i64p, vp, vp, i64p] + attrs
     lib.convtranspose_nd.argtypes = call + [vp]
     lib.convtranspose_nd_with_kernel.argtypes = [ctypes.c_int] + call + [vp, ctypes.c_size_t, vp]
+    lib.convtranspose_nd_fused.argtypes = [ctypes.c_int] + call + [ctypes.c_int, ctypes.c_float, ctypes.c_float,
+                                                                   vp, ctypes.c_size_t, vp]
     lib.convtranspose_workspace_size.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, vp,
                                                  i64p, i64p] + attrs + [ctypes.POINTER(ctypes.c_size_t)]
     lib.convtranspose_select_kernel.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, vp, i64p,
                                                 vp, i64p, vp, vp] + attrs
     for fn in ("convtranspose_output_shape", "convtranspose_useful_macs", "convtranspose_nd",
-               "convtranspose_nd_with_kernel", "convtranspose_select_kernel",
+               "convtranspose_nd_with_kernel", "convtranspose_nd_fused", "convtranspose_select_kernel",
                "convtranspose_workspace_size"):
         getattr(lib, fn).restype = ctypes.c_int
     lib.convtranspose_last_error.restype = ctypes.c_char_p
@@ -225,8 +230,15 @@ class ConvTransposePlan:
                  auto_pad: str = "NOTSET", strides=None, dilations=None, pads=None,
                  output_padding=None, output_shape=None, kernel_shape=None, group: int = 1,
                  channels_last: bool = False, out: Optional[torch.Tensor] = None,
-                 kernel: str = "auto", stream: Optional[torch.cuda.Stream] = None):
+                 kernel: str = "auto", stream: Optional[torch.cuda.Stream] = None,
+                 activation: str = "identity", act_params: Sequence[float] = ()):
         lib = load_library()
+        if activation not in ACTIVATIONS:
+            raise ConvTransposeError(1, f"unknown activation {activation!r}")
+        act_kind, act_n = ACTIVATIONS[activation]
+        if len(act_params) != act_n:
+            raise ConvTransposeError(1, f"{activation} takes {act_n} parameter(s)")
+        act_p = [float(v) for v in act_params] + [0.0] * (2 - act_n)
         if x.dtype not in _DTYPES:
             raise ConvTransposeError(3, f"dtype {x.dtype} is not served (float32, float16)")
         if x.dim() < 3 or x.dim() > 5:
@@ -275,9 +287,9 @@ class ConvTransposePlan:
         self.out = out
         self.device = dev
         self._keep = (x, w, bias)  # the pointers below stay valid while the plan lives
-        self._fn = lib.convtranspose_nd_with_kernel
+        self._fn = lib.convtranspose_nd_fused
         self._args = (KERNELS[kernel], _DTYPES[x.dtype], nsp, int(channels_last), xp, xs, wp, ws, bp, yp,
-                      _i64(yshape), *at,
+                      _i64(yshape), *at, act_kind, act_p[0], act_p[1],
                       ctypes.c_void_p(self.scratch.data_ptr()) if self.scratch is not None else None,
                       nbytes.value, ctypes.c_void_p(self.stream.cuda_stream))
 
@@ -293,7 +305,8 @@ def convtranspose_nd(x: torch.Tensor, w: torch.Tensor, bias: Optional[torch.Tens
                      auto_pad: str = "NOTSET", strides=None, dilations=None, pads=None,
                      output_padding=None, output_shape=None, kernel_shape=None, group: int = 1,
                      channels_last: bool = False, out: Optional[torch.Tensor] = None,
-                     kernel: str = "auto", stream: Optional[torch.cuda.Stream] = None) -> torch.Tensor:
+                     kernel: str = "auto", stream: Optional[torch.cuda.Stream] = None,
+                     activation: str = "identity", act_params: Sequence[float] = ()) -> torch.Tensor:
     """Y = ConvTranspose(X, W, bias) on the GPU, enqueued on ``stream`` (default: torch's
     current stream of x's device).
 
@@ -301,11 +314,15 @@ def convtranspose_nd(x: torch.Tensor, w: torch.Tensor, bias: Optional[torch.Tens
     dense N..C storage when ``channels_last`` (see ``to_channels_last``).
     w: (C, M/group, k1..kn) dense.  bias: (M,) or None.  Y is allocated (or ``out`` is
     used) with the same layout convention as x.  ``kernel`` forces a kernel family.
+    ``activation`` ("identity", "relu", "leaky_relu" with ``act_params=(slope,)``, "clip"
+    with ``act_params=(lower, upper)``) is applied to every output in float32, after the
+    bias and before the one rounding, inside the kernel that computes it.
     """
     return ConvTransposePlan(x, w, bias, auto_pad=auto_pad, strides=strides, dilations=dilations,
                              pads=pads, output_padding=output_padding, output_shape=output_shape,
                              kernel_shape=kernel_shape, group=group, channels_last=channels_last,
-                             out=out, kernel=kernel, stream=stream)()
+                             out=out, kernel=kernel, stream=stream, activation=activation,
+                             act_params=act_params)()
 
 
 def convtranspose_profile_events(before: Optional[torch.cuda.Event], after: Optional[torch.cuda.Event]):

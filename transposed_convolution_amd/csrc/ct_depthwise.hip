@@ -44,6 +44,7 @@ struct DwArgs {
     int span1;     // staged rows beyond the band's input rows: hi1 - lo1 + 1
     int stage_elems;    // halves per stage buffer (multiple of 8)
     int a0_1[kDwMaxS];  // per row residue: its window's row offset from lo1
+    Act act;            // output activation
 };
 
 template <int S, int T1, int T2, int OFF2, int NQ>
@@ -221,6 +222,10 @@ __global__ __launch_bounds__(kDwThreads) void depthwise_kernel(const _Float16 *_
                         }
                         out[je * S + rwp] = acc;
                     }
+                }
+                if (!p.act.identity()) {
+#pragma unroll
+                    for (int e = 0; e < OC; ++e) out[e] = p.act(out[e]);
                 }
                 if (oh < cur.oh1) {
                     _Float16 *yr = yplane + size_t(oh) * p.O2 + seg * OC;
@@ -424,13 +429,14 @@ bool depthwise_supports(const Geom &g, ct_dtype dt, bool cl, const void *x)
 }
 
 ct_status launch_depthwise(const Geom &g, ct_dtype dt, bool cl, const void *x, const void *w, const void *bias,
-                           void *y, hipStream_t st, std::string *err)
+                           void *y, const Act &act, hipStream_t st, std::string *err)
 {
     DwPlan pl;
     if (!make_dwplan(g, dt, cl, x, &pl)) {
         *err = "depthwise kernel cannot serve this call";
         return CT_EUNSUPPORTED;
     }
+    pl.a.act = act;
     mark_before(st);
     if (pl.S == 1 && pl.T1 == 3) launch_o<1, 3, 3, 0>(pl, x, w, bias, y, st);
     else if (pl.S == 1) launch_o<1, 5, 5, 0>(pl, x, w, bias, y, st);

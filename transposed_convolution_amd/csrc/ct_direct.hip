@@ -21,6 +21,7 @@ struct DirectArgs {
     int64_t total;  // elements of Y
     int N, C, M, Cg, Mg, has_bias;
     int L[kAxes], K[kAxes], s[kAxes], d[kAxes], b[kAxes], O[kAxes];
+    Act act;  // output activation
 };
 
 template <typename T, bool CL>
@@ -87,15 +88,16 @@ __global__ __launch_bounds__(256) void direct_kernel(const T *__restrict__ x, co
             }
         }
         if (p.has_bias) acc += float(bias[m]);
-        y[idx] = T(acc);
+        y[idx] = T(p.act(acc));
     }
 }
 
 template <typename T>
 ct_status launch_t(const Geom &g, bool cl, const void *x, const void *w, const void *bias, void *y,
-                   hipStream_t st, std::string *err)
+                   const Act &act, hipStream_t st, std::string *err)
 {
     DirectArgs p;
+    p.act = act;
     p.total = g.y_elems();
     p.N = int(g.N);
     p.C = int(g.C);
@@ -137,10 +139,10 @@ ct_status launch_t(const Geom &g, bool cl, const void *x, const void *w, const v
 }  // namespace
 
 ct_status launch_direct(const Geom &g, ct_dtype dt, bool cl, const void *x, const void *w,
-                        const void *bias, void *y, hipStream_t st, std::string *err)
+                        const void *bias, void *y, const Act &act, hipStream_t st, std::string *err)
 {
-    if (dt == CT_FLOAT16) return launch_t<_Float16>(g, cl, x, w, bias, y, st, err);
-    return launch_t<float>(g, cl, x, w, bias, y, st, err);
+    if (dt == CT_FLOAT16) return launch_t<_Float16>(g, cl, x, w, bias, y, act, st, err);
+    return launch_t<float>(g, cl, x, w, bias, y, act, st, err);
 }
 
 }  // namespace ct

@@ -43,6 +43,7 @@ struct GArgs {
     short k0_1[kGMaxRes], be_1[kGMaxRes], nt_1[kGMaxRes];
     short k0_2[kGMaxRes], be_2[kGMaxRes], nt_2[kGMaxRes];
     short ks1, ks2, bs1, bs2;
+    Act act;  // output activation
 };
 
 __device__ __forceinline__ int fdiv(int a, int q) { return a >= 0 ? a / q : -((-a + q - 1) / q); }
@@ -130,6 +131,10 @@ __global__ __launch_bounds__(kGThreads) void grouped_kernel(const T *__restrict_
                     }
                 }
             }
+        }
+        if (!p.act.identity()) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) acc[e] = p.act(acc[e]);
         }
         T *yr = y + ((size_t(n) * p.M + size_t(g) * p.Mg + mm) * p.O1 + oh) * p.O2 + ow0;
         const bool full = ow0 + 8 <= p.O2;
@@ -242,15 +247,16 @@ bool grouped_supports(const Geom &g, ct_dtype dt, bool cl, const void *x)
 }
 
 ct_status launch_grouped(const Geom &g, ct_dtype dt, bool cl, const void *x, const void *w, const void *bias,
-                         void *y, hipStream_t st, std::string *err)
+                         void *y, const Act &act, hipStream_t st, std::string *err)
 {
     if (!grouped_supports(g, dt, cl, x)) {
         *err = "grouped kernel cannot serve this call";
         return CT_EUNSUPPORTED;
     }
-    if (depthwise_supports(g, dt, cl, x)) return launch_depthwise(g, dt, cl, x, w, bias, y, st, err);
+    if (depthwise_supports(g, dt, cl, x)) return launch_depthwise(g, dt, cl, x, w, bias, y, act, st, err);
     GPlan pl;
     if (!make_gplan(g, dt == CT_FLOAT16 ? 2 : 4, &pl, err)) return CT_EUNSUPPORTED;
+    pl.a.act = act;
     mark_before(st);
     if (dt == CT_FLOAT16)
         hipLaunchKernelGGL(grouped_kernel<_Float16>, dim3(unsigned(pl.blocks)), dim3(kGThreads), 0, st,

@@ -9,6 +9,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cstring>
+#include <cmath>
 #include <string>
 
 #include "ct_internal.hpp"
@@ -348,17 +349,33 @@ ct_status convtranspose_workspace_size(ct_kernel kernel, ct_dtype dtype, int nsp
     return CT_OK;
 }
 
-ct_status convtranspose_nd_with_kernel(ct_kernel kernel, ct_dtype dtype, int nsp, int channels_last,
-                                       const void *x, const int64_t *x_shape, const void *w,
-                                       const int64_t *w_shape, const void *bias, void *y,
-                                       const int64_t *y_shape, ct_auto_pad auto_pad,
-                                       const int64_t *strides, const int64_t *dilations,
-                                       const int64_t *pads, const int64_t *output_padding,
-                                       const int64_t *output_shape, const int64_t *kernel_shape,
-                                       int64_t group, void *workspace, size_t workspace_bytes,
-                                       void *stream)
+ct_status convtranspose_nd_fused(ct_kernel kernel, ct_dtype dtype, int nsp, int channels_last,
+                                 const void *x, const int64_t *x_shape, const void *w,
+                                 const int64_t *w_shape, const void *bias, void *y,
+                                 const int64_t *y_shape, ct_auto_pad auto_pad,
+                                 const int64_t *strides, const int64_t *dilations,
+                                 const int64_t *pads, const int64_t *output_padding,
+                                 const int64_t *output_shape, const int64_t *kernel_shape,
+                                 int64_t group, ct_activation activation, float act_p0, float act_p1,
+                                 void *workspace, size_t workspace_bytes, void *stream)
 {
     t_error.clear();
+    ct::Act act;
+    act.kind = int(activation);
+    act.p0 = act_p0;
+    act.p1 = act_p1;
+    switch (activation) {
+        case CT_ACT_IDENTITY:
+        case CT_ACT_RELU: break;
+        case CT_ACT_LEAKY_RELU:
+            if (!std::isfinite(act_p0)) return fail(CT_EINVAL, "leaky ReLU slope must be finite");
+            break;
+        case CT_ACT_CLIP:
+            if (!std::isfinite(act_p0) || !std::isfinite(act_p1) || !(act_p0 <= act_p1))
+                return fail(CT_EINVAL, "clip bounds must be finite with lower <= upper");
+            break;
+        default: return fail(CT_EINVAL, "unknown activation");
+    }
     if (!y_shape) return fail(CT_EINVAL, "y_shape is NULL");
     if (workspace && !aligned(workspace, 16)) return fail(CT_EINVAL, "workspace must be 16-byte aligned");
     ct::Geom g;
@@ -374,13 +391,29 @@ ct_status convtranspose_nd_with_kernel(ct_kernel kernel, ct_dtype dtype, int nsp
     const bool cl = channels_last != 0;
     switch (k) {
         case CT_KERNEL_IGEMM:
-            st = ct::launch_igemm(g, dtype, cl, x, w, bias, y, workspace, workspace_bytes, hs, &err);
+            st = ct::launch_igemm(g, dtype, cl, x, w, bias, y, act, workspace, workspace_bytes, hs, &err);
             break;
-        case CT_KERNEL_GROUPED: st = ct::launch_grouped(g, dtype, cl, x, w, bias, y, hs, &err); break;
-        default: st = ct::launch_direct(g, dtype, cl, x, w, bias, y, hs, &err); break;
+        case CT_KERNEL_GROUPED: st = ct::launch_grouped(g, dtype, cl, x, w, bias, y, act, hs, &err); break;
+        default: st = ct::launch_direct(g, dtype, cl, x, w, bias, y, act, hs, &err); break;
     }
     if (st != CT_OK) return fail(st, err);
     return CT_OK;
+}
+
+ct_status convtranspose_nd_with_kernel(ct_kernel kernel, ct_dtype dtype, int nsp, int channels_last,
+                                       const void *x, const int64_t *x_shape, const void *w,
+                                       const int64_t *w_shape, const void *bias, void *y,
+                                       const int64_t *y_shape, ct_auto_pad auto_pad,
+                                       const int64_t *strides, const int64_t *dilations,
+                                       const int64_t *pads, const int64_t *output_padding,
+                                       const int64_t *output_shape, const int64_t *kernel_shape,
+                                       int64_t group, void *workspace, size_t workspace_bytes,
+                                       void *stream)
+{
+    return convtranspose_nd_fused(kernel, dtype, nsp, channels_last, x, x_shape, w, w_shape, bias, y,
+                                  y_shape, auto_pad, strides, dilations, pads, output_padding,
+                                  output_shape, kernel_shape, group, CT_ACT_IDENTITY, 0.0f, 0.0f,
+                                  workspace, workspace_bytes, stream);
 }
 
 ct_status convtranspose_nd(ct_dtype dtype, int nsp, int channels_last, const void *x,

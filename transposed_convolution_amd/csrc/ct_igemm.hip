@@ -70,6 +70,7 @@ struct IgArgs {
     short tk0[3][kMaxRes];
     short tb0[3][kMaxRes];
     short kstep[3], bstep[3];
+    Act act;  // output activation
 };
 
 __device__ __forceinline__ int floor_div8(int v) { return v >= 0 ? v / 8 : -((-v + 7) / 8); }
@@ -567,7 +568,7 @@ __global__ __launch_bounds__(kThreads, OCC) void igemm_kernel(const _Float16 *x,
                     if ((wn * WN + j) * 32 + (lane & 31) >= npix) continue;
                     _Float16 v[4];
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) v[e] = _Float16(acc[i][j][rg * 4 + e] + bv[e]);
+                    for (int e = 0; e < 4; ++e) v[e] = _Float16(p.act(acc[i][j][rg * 4 + e] + bv[e]));
                     if (vec && ml + 4 <= mvalid) {
                         const unsigned w0 = unsigned(__builtin_bit_cast(unsigned short, v[0])) |
                                             (unsigned(__builtin_bit_cast(unsigned short, v[1])) << 16);
@@ -603,7 +604,7 @@ __global__ __launch_bounds__(kThreads, OCC) void igemm_kernel(const _Float16 *x,
                 const int pl = (wn * WN + j) * 32 + (lane & 31);
 #pragma unroll
                 for (int e = 0; e < 4; ++e)
-                    stile[(ml + e) * TP + (PAIR ? 2 * pl + wm : pl)] = _Float16(acc[i][j][rg * 4 + e] + bv[e]);
+                    stile[(ml + e) * TP + (PAIR ? 2 * pl + wm : pl)] = _Float16(p.act(acc[i][j][rg * 4 + e] + bv[e]));
             }
         }
     __syncthreads();
@@ -878,11 +879,12 @@ size_t igemm_workspace_bytes(const Geom &g, ct_dtype dt)
 }
 
 ct_status launch_igemm(const Geom &g, ct_dtype dt, bool cl, const void *x, const void *w, const void *bias,
-                       void *y, void *workspace, size_t ws_bytes, hipStream_t st, std::string *err)
+                       void *y, const Act &act, void *workspace, size_t ws_bytes, hipStream_t st, std::string *err)
 {
-    if (dt == CT_FLOAT32) return launch_igemm32(g, cl, x, w, bias, y, st, err);
+    if (dt == CT_FLOAT32) return launch_igemm32(g, cl, x, w, bias, y, act, st, err);
     Plan pl;
     if (!make_plan(g, cl, &pl, err)) return CT_EUNSUPPORTED;
+    pl.a.act = act;
     bool owned = false;
     void *wsp = workspace;
     if (!wsp) {

@@ -40,6 +40,7 @@ struct I32Args {
     signed char ntap[3][kMaxRes32];
     short tk0[3][kMaxRes32], tb0[3][kMaxRes32];
     short kstep[3], bstep[3];
+    Act act;  // output activation
 };
 
 __global__ __launch_bounds__(kThreads32) void igemm32_kernel(const float *__restrict__ x, const float *__restrict__ w,
@@ -167,7 +168,7 @@ __global__ __launch_bounds__(kThreads32) void igemm32_kernel(const float *__rest
         const int ml = mt * kBM + wm * 32 + (e >> 2) * 8 + (lane >> 5) * 4 + (e & 3);
         if (ml >= p.Mg) continue;
         const int m = g * p.Mg + ml;
-        const float val = acc[e] + (bias ? bias[m] : 0.0f);
+        const float val = p.act(acc[e] + (bias ? bias[m] : 0.0f));
         if (p.cl) y[(size_t(n) * opix + pix) * p.M + m] = val;
         else y[(size_t(n) * p.M + m) * opix + pix] = val;
     }
@@ -260,11 +261,12 @@ bool igemm32_supports(const Geom &g, bool cl, std::string *why)
 }
 
 ct_status launch_igemm32(const Geom &g, bool cl, const void *x, const void *w, const void *bias, void *y,
-                         hipStream_t st, std::string *err)
+                         const Act &act, hipStream_t st, std::string *err)
 {
     I32Args a;
     int blocks = 0;
     if (!make_plan32(g, cl, &a, &blocks, err)) return CT_EUNSUPPORTED;
+    a.act = act;
     mark_before(st);
     if (blocks > 0)
         hipLaunchKernelGGL(igemm32_kernel, dim3(unsigned(blocks)), dim3(kThreads32), 0, st,

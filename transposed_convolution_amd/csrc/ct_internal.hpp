@@ -75,27 +75,44 @@ inline void mark_after(hipStream_t st)
     if (profile_events().after) (void)hipEventRecord(profile_events().after, st);
 }
 
+// Activation of the output stage (see ct_activation in convtranspose.h), evaluated in
+// float32 on the accumulated value plus bias, before the one rounding.
+struct Act {
+    int kind = CT_ACT_IDENTITY;
+    float p0 = 0.0f, p1 = 0.0f;
+    __host__ __device__ bool identity() const { return kind == CT_ACT_IDENTITY; }
+    __host__ __device__ float operator()(float v) const
+    {
+        switch (kind) {
+        case CT_ACT_RELU: return v > 0.0f ? v : 0.0f;
+        case CT_ACT_LEAKY_RELU: return v >= 0.0f ? v : p0 * v;
+        case CT_ACT_CLIP: return v < p0 ? p0 : (v > p1 ? p1 : v);
+        default: return v;
+        }
+    }
+};
+
 // Launchers (one per kernel family); each returns CT_OK or CT_EDEVICE (message in err).
 ct_status launch_direct(const Geom &g, ct_dtype dt, bool cl, const void *x, const void *w,
-                        const void *bias, void *y, hipStream_t st, std::string *err);
+                        const void *bias, void *y, const Act &act, hipStream_t st, std::string *err);
 bool grouped_supports(const Geom &g, ct_dtype dt, bool cl, const void *x);
 // Depthwise specialisation inside the grouped family (one channel in and out per group,
 // float16, channels-first, equal strides 1, 2 or 4, tap runs of step 1).
 bool depthwise_supports(const Geom &g, ct_dtype dt, bool cl, const void *x);
 ct_status launch_depthwise(const Geom &g, ct_dtype dt, bool cl, const void *x, const void *w,
-                           const void *bias, void *y, hipStream_t st, std::string *err);
+                           const void *bias, void *y, const Act &act, hipStream_t st, std::string *err);
 ct_status launch_grouped(const Geom &g, ct_dtype dt, bool cl, const void *x, const void *w,
-                         const void *bias, void *y, hipStream_t st, std::string *err);
+                         const void *bias, void *y, const Act &act, hipStream_t st, std::string *err);
 bool igemm_supports(const Geom &g, ct_dtype dt, bool cl, const void *x, std::string *why);
 size_t igemm_workspace_bytes(const Geom &g, ct_dtype dt);
 // float32 implicit GEMM on MFMA (the CT_KERNEL_IGEMM family for float32 inputs)
 bool igemm32_supports(const Geom &g, bool cl, std::string *why);
 ct_status launch_igemm32(const Geom &g, bool cl, const void *x, const void *w, const void *bias, void *y,
-                         hipStream_t st, std::string *err);
+                         const Act &act, hipStream_t st, std::string *err);
 // workspace: caller scratch of ws_bytes (>= igemm_workspace_bytes), or NULL to take
 // stream-ordered scratch with hipMallocAsync / hipFreeAsync on st.
 ct_status launch_igemm(const Geom &g, ct_dtype dt, bool cl, const void *x, const void *w,
-                       const void *bias, void *y, void *workspace, size_t ws_bytes, hipStream_t st,
-                       std::string *err);
+                       const void *bias, void *y, const Act &act, void *workspace, size_t ws_bytes,
+                       hipStream_t st, std::string *err);
 
 }  // namespace ct
