@@ -51,7 +51,8 @@ def log(*a):
 def workloads():
     import workloads as W
     return {"c1": W.C1, "c2": W.C2, "c3": W.C3, "c4": W.C4, "c4_nhwc": W.C4_NHWC,
-            "c5_s1": W.C5_S1, "c5_s1_p1": W.C5_S1_P1, "c5_s2": W.C5_S2}
+            "c5_s1": W.C5_S1, "c5_s1_p1": W.C5_S1_P1, "c5_s2": W.C5_S2,
+            "f2_k2s2": W.F2_K2S2, "f2_1x1": W.F2_1X1}
 
 
 def source_digest(kernel: str) -> str:

@@ -521,149 +521,154 @@ __global__ __launch_bounds__(kThreads, OCC) void igemm_kernel(const _Float16 *x,
         }
     }
 
-    // ---------------- epilogue: bias, round once, store ----------------
-    // Accumulator element r of tile (i, j) belongs to channel i*32 + (r/4)*8 + (lane/32)*4
-    // + r%4 of the wave's rows; the bias is added in float32 before the one rounding.
-    typedef float f32x4 __attribute__((ext_vector_type(4)));
-    if (nsteps == 0) __syncthreads();  // no main-loop barrier made the staged bias visible
-    const int mwave = PAIR ? 0 : wm * WM * 32;  // first channel of the wave inside the tile
-    auto bias_of = [&](int i, int rg, float *bv) {
-        const f32x4 b4 = *reinterpret_cast<const f32x4 *>(&sbias[mwave + i * 32 + rg * 8 + (lane >> 5) * 4]);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) bv[e] = b4[e];
-    };
-    const int O1 = p.O[1], O2 = p.O[2];
-    const size_t opix = size_t(p.O[0]) * O1 * O2;
-    const int o0 = r0 + p.s[0] * j0;
-    const int npix = tl.q1 - tl.q0;
-    const int mvalid = min(BMM, p.Mg - mt * BMM);
-    auto pixel_offset = [&](int pl) -> size_t {  // output pixel index of tile pixel pl
-        const int q = tl.q0 + pl;
-        const int row = tl.seg ? tl.row_lo : q / J2;
-        const int col = q - row * J2;
-        return (size_t(o0) * O1 + (r1 + p.s[1] * row)) * O2 + (r2 + p.s[2] * col);
-    };
-    if constexpr (CL) {
-        // Channels-last: straight from the accumulators.  A lane holds 4 consecutive
-        // channels of one pixel per (tile, row group); lanes l and l + 32 hold adjacent
-        // quadruples, so each store instruction writes 16 contiguous bytes per pixel.
-        typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
-        const bool vec = (p.M % 4 == 0) && ((g * p.Mg + mt * BM) % 4 == 0) && (reinterpret_cast<uintptr_t>(y) % 8 == 0);
-        const int mrow = wm * WM * 32;  // first channel of the wave inside the tile
-        _Float16 *yp[WN];
-#pragma unroll
-        for (int j = 0; j < WN; ++j) {
-            const int pl = min((wn * WN + j) * 32 + (lane & 31), npix - 1);
-            yp[j] = y + (size_t(n) * opix + pixel_offset(pl)) * p.M + g * p.Mg + mt * BM;
+    // The output stage, instantiated once per activation kind (one uniform switch picks
+    // the instance), so no value pays for a dispatch.
+    auto output_stage = [&](auto fin) {
+        // ---------------- epilogue: bias, round once, store ----------------
+        // Accumulator element r of tile (i, j) belongs to channel i*32 + (r/4)*8 + (lane/32)*4
+        // + r%4 of the wave's rows; the bias is added in float32 before the one rounding.
+        typedef float f32x4 __attribute__((ext_vector_type(4)));
+        if (nsteps == 0) __syncthreads();  // no main-loop barrier made the staged bias visible
+        const int mwave = PAIR ? 0 : wm * WM * 32;  // first channel of the wave inside the tile
+        auto bias_of = [&](int i, int rg, float *bv) {
+            const f32x4 b4 = *reinterpret_cast<const f32x4 *>(&sbias[mwave + i * 32 + rg * 8 + (lane >> 5) * 4]);
+    #pragma unroll
+            for (int e = 0; e < 4; ++e) bv[e] = b4[e];
+        };
+        const int O1 = p.O[1], O2 = p.O[2];
+        const size_t opix = size_t(p.O[0]) * O1 * O2;
+        const int o0 = r0 + p.s[0] * j0;
+        const int npix = tl.q1 - tl.q0;
+        const int mvalid = min(BMM, p.Mg - mt * BMM);
+        auto pixel_offset = [&](int pl) -> size_t {  // output pixel index of tile pixel pl
+            const int q = tl.q0 + pl;
+            const int row = tl.seg ? tl.row_lo : q / J2;
+            const int col = q - row * J2;
+            return (size_t(o0) * O1 + (r1 + p.s[1] * row)) * O2 + (r2 + p.s[2] * col);
+        };
+        if constexpr (CL) {
+            // Channels-last: straight from the accumulators.  A lane holds 4 consecutive
+            // channels of one pixel per (tile, row group); lanes l and l + 32 hold adjacent
+            // quadruples, so each store instruction writes 16 contiguous bytes per pixel.
+            typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+            const bool vec = (p.M % 4 == 0) && ((g * p.Mg + mt * BM) % 4 == 0) && (reinterpret_cast<uintptr_t>(y) % 8 == 0);
+            const int mrow = wm * WM * 32;  // first channel of the wave inside the tile
+            _Float16 *yp[WN];
+    #pragma unroll
+            for (int j = 0; j < WN; ++j) {
+                const int pl = min((wn * WN + j) * 32 + (lane & 31), npix - 1);
+                yp[j] = y + (size_t(n) * opix + pixel_offset(pl)) * p.M + g * p.Mg + mt * BM;
+            }
+    #pragma unroll
+            for (int i = 0; i < WM; ++i)
+    #pragma unroll
+                for (int rg = 0; rg < 4; ++rg) {
+                    const int ml = mrow + i * 32 + rg * 8 + (lane >> 5) * 4;
+                    float bv[4];
+                    bias_of(i, rg, bv);
+    #pragma unroll
+                    for (int j = 0; j < WN; ++j) {
+                        if ((wn * WN + j) * 32 + (lane & 31) >= npix) continue;
+                        _Float16 v[4];
+    #pragma unroll
+                        for (int e = 0; e < 4; ++e) v[e] = _Float16(fin(acc[i][j][rg * 4 + e] + bv[e]));
+                        if (vec && ml + 4 <= mvalid) {
+                            const unsigned w0 = unsigned(__builtin_bit_cast(unsigned short, v[0])) |
+                                                (unsigned(__builtin_bit_cast(unsigned short, v[1])) << 16);
+                            const unsigned w1 = unsigned(__builtin_bit_cast(unsigned short, v[2])) |
+                                                (unsigned(__builtin_bit_cast(unsigned short, v[3])) << 16);
+                            *reinterpret_cast<u32x2 *>(yp[j] + ml) = u32x2{w0, w1};
+                        } else {
+    #pragma unroll
+                            for (int e = 0; e < 4; ++e)
+                                if (ml + e < mvalid) yp[j][ml + e] = v[e];
+                        }
+                    }
+                }
+            return;
         }
-#pragma unroll
+        // Channels-first: the block's output tile goes through LDS (free once the main loop is
+        // done) and is stored with 16-byte vectors along the contiguous pixel direction.
+        // tile layout (pitch padded by 8 elements against bank conflicts):
+        //   NC -> [m][pixel];  PAIR -> [m][pixel, phase] (the block's output rows, contiguous)
+        constexpr int TP = (PAIR ? 2 * BN : BN) + 8;
+        static_assert(BMM * TP * 2 <= Cfg::LDS - kBiasBytes, "output tile must fit in LDS below the bias");
+        __syncthreads();  // every wave is done reading the operand buffers
+        _Float16 *const stile = reinterpret_cast<_Float16 *>(lds);
+    #pragma unroll
         for (int i = 0; i < WM; ++i)
-#pragma unroll
+    #pragma unroll
             for (int rg = 0; rg < 4; ++rg) {
-                const int ml = mrow + i * 32 + rg * 8 + (lane >> 5) * 4;
+                const int ml = (PAIR ? 0 : wm * WM * 32) + i * 32 + rg * 8 + (lane >> 5) * 4;  // 4 consecutive channels
                 float bv[4];
                 bias_of(i, rg, bv);
-#pragma unroll
+    #pragma unroll
                 for (int j = 0; j < WN; ++j) {
-                    if ((wn * WN + j) * 32 + (lane & 31) >= npix) continue;
-                    _Float16 v[4];
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) v[e] = _Float16(p.act(acc[i][j][rg * 4 + e] + bv[e]));
-                    if (vec && ml + 4 <= mvalid) {
-                        const unsigned w0 = unsigned(__builtin_bit_cast(unsigned short, v[0])) |
-                                            (unsigned(__builtin_bit_cast(unsigned short, v[1])) << 16);
-                        const unsigned w1 = unsigned(__builtin_bit_cast(unsigned short, v[2])) |
-                                            (unsigned(__builtin_bit_cast(unsigned short, v[3])) << 16);
-                        *reinterpret_cast<u32x2 *>(yp[j] + ml) = u32x2{w0, w1};
+                    const int pl = (wn * WN + j) * 32 + (lane & 31);
+    #pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        stile[(ml + e) * TP + (PAIR ? 2 * pl + wm : pl)] = _Float16(fin(acc[i][j][rg * 4 + e] + bv[e]));
+                }
+            }
+        __syncthreads();
+
+        if (PAIR) {
+            // both column phases of each tile pixel: 2 * npix consecutive outputs per tile row
+            // segment; 16-byte vectors when rows are whole vectors (then no vector crosses a row)
+            const bool vec = (O2 % 8 == 0) && (tl.q0 % 4 == 0) && (npix % 4 == 0) &&
+                             (reinterpret_cast<uintptr_t>(y) % 16 == 0);
+            if (vec) {
+                const int per = npix / 4;
+                for (int u = tid; u < mvalid * per; u += kThreads) {
+                    const int ml = u / per, v4 = u - ml * per;
+                    const size_t off = (size_t(n) * p.M + g * p.Mg + mt * BMM + ml) * opix + pixel_offset(v4 * 4);
+                    *reinterpret_cast<u32x4 *>(y + off) = *reinterpret_cast<const u32x4 *>(&stile[ml * TP + v4 * 8]);
+                }
+            } else {
+                for (int u = tid; u < mvalid * 2 * npix; u += kThreads) {
+                    const int ml = u / (2 * npix), e2 = u - ml * (2 * npix);
+                    y[(size_t(n) * p.M + g * p.Mg + mt * BMM + ml) * opix + pixel_offset(e2 >> 1) + (e2 & 1)] =
+                        stile[ml * TP + e2];
+                }
+            }
+        } else {
+            // runs of pixels per channel: contiguous in Y only along a row with unit stride
+            const bool vec = p.s[2] == 1 && !tl.seg && (J2 % 8 == 0) && (tl.q0 % 8 == 0) && (O2 % 8 == 0) && r2 == 0 &&
+                             (npix % 8 == 0) && (reinterpret_cast<uintptr_t>(y) % 16 == 0);
+            if (vec) {
+                const int per = npix / 8;
+                for (int u = tid; u < mvalid * per; u += kThreads) {
+                    const int ml = u / per, p8 = u - ml * per;
+                    const size_t off = (size_t(n) * p.M + g * p.Mg + mt * BM + ml) * opix + pixel_offset(p8 * 8);
+                    *reinterpret_cast<u32x4 *>(y + off) = *reinterpret_cast<const u32x4 *>(&stile[ml * TP + p8 * 8]);
+                }
+            } else {
+                // Phase-strided rows: runs of 8 tile pixels of one channel.  When a run lies
+                // in one output row its 8 outputs sit s2 elements apart: one LDS vector read,
+                // one address, 8 stores.  Runs that cross a row or the tile end go element by
+                // element.
+                const int nruns = (npix + 7) / 8;
+                const int s2 = p.s[2];
+                for (int u = tid; u < mvalid * nruns; u += kThreads) {
+                    const int ml = u / nruns, pl0 = (u - ml * nruns) * 8;
+                    _Float16 *const yc = y + (size_t(n) * p.M + g * p.Mg + mt * BM + ml) * opix;
+                    const int q = tl.q0 + pl0;
+                    const int row = tl.seg ? tl.row_lo : q / J2;
+                    const int col = q - row * J2;
+                    if (pl0 + 8 <= npix && col + 8 <= J2) {
+                        const u32x4 v8 = *reinterpret_cast<const u32x4 *>(&stile[ml * TP + pl0]);
+                        _Float16 *const dst = yc + pixel_offset(pl0);
+    #pragma unroll
+                        for (int e = 0; e < 8; ++e)
+                            dst[e * s2] = __builtin_bit_cast(_Float16, (unsigned short)(v8[e >> 1] >> (16 * (e & 1))));
                     } else {
-#pragma unroll
-                        for (int e = 0; e < 4; ++e)
-                            if (ml + e < mvalid) yp[j][ml + e] = v[e];
+                        for (int pl = pl0; pl < min(pl0 + 8, npix); ++pl) yc[pixel_offset(pl)] = stile[ml * TP + pl];
                     }
                 }
             }
-        return;
-    }
-    // Channels-first: the block's output tile goes through LDS (free once the main loop is
-    // done) and is stored with 16-byte vectors along the contiguous pixel direction.
-    // tile layout (pitch padded by 8 elements against bank conflicts):
-    //   NC -> [m][pixel];  PAIR -> [m][pixel, phase] (the block's output rows, contiguous)
-    constexpr int TP = (PAIR ? 2 * BN : BN) + 8;
-    static_assert(BMM * TP * 2 <= Cfg::LDS - kBiasBytes, "output tile must fit in LDS below the bias");
-    __syncthreads();  // every wave is done reading the operand buffers
-    _Float16 *const stile = reinterpret_cast<_Float16 *>(lds);
-#pragma unroll
-    for (int i = 0; i < WM; ++i)
-#pragma unroll
-        for (int rg = 0; rg < 4; ++rg) {
-            const int ml = (PAIR ? 0 : wm * WM * 32) + i * 32 + rg * 8 + (lane >> 5) * 4;  // 4 consecutive channels
-            float bv[4];
-            bias_of(i, rg, bv);
-#pragma unroll
-            for (int j = 0; j < WN; ++j) {
-                const int pl = (wn * WN + j) * 32 + (lane & 31);
-#pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    stile[(ml + e) * TP + (PAIR ? 2 * pl + wm : pl)] = _Float16(p.act(acc[i][j][rg * 4 + e] + bv[e]));
-            }
         }
-    __syncthreads();
-
-    if (PAIR) {
-        // both column phases of each tile pixel: 2 * npix consecutive outputs per tile row
-        // segment; 16-byte vectors when rows are whole vectors (then no vector crosses a row)
-        const bool vec = (O2 % 8 == 0) && (tl.q0 % 4 == 0) && (npix % 4 == 0) &&
-                         (reinterpret_cast<uintptr_t>(y) % 16 == 0);
-        if (vec) {
-            const int per = npix / 4;
-            for (int u = tid; u < mvalid * per; u += kThreads) {
-                const int ml = u / per, v4 = u - ml * per;
-                const size_t off = (size_t(n) * p.M + g * p.Mg + mt * BMM + ml) * opix + pixel_offset(v4 * 4);
-                *reinterpret_cast<u32x4 *>(y + off) = *reinterpret_cast<const u32x4 *>(&stile[ml * TP + v4 * 8]);
-            }
-        } else {
-            for (int u = tid; u < mvalid * 2 * npix; u += kThreads) {
-                const int ml = u / (2 * npix), e2 = u - ml * (2 * npix);
-                y[(size_t(n) * p.M + g * p.Mg + mt * BMM + ml) * opix + pixel_offset(e2 >> 1) + (e2 & 1)] =
-                    stile[ml * TP + e2];
-            }
-        }
-    } else {
-        // runs of pixels per channel: contiguous in Y only along a row with unit stride
-        const bool vec = p.s[2] == 1 && !tl.seg && (J2 % 8 == 0) && (tl.q0 % 8 == 0) && (O2 % 8 == 0) && r2 == 0 &&
-                         (npix % 8 == 0) && (reinterpret_cast<uintptr_t>(y) % 16 == 0);
-        if (vec) {
-            const int per = npix / 8;
-            for (int u = tid; u < mvalid * per; u += kThreads) {
-                const int ml = u / per, p8 = u - ml * per;
-                const size_t off = (size_t(n) * p.M + g * p.Mg + mt * BM + ml) * opix + pixel_offset(p8 * 8);
-                *reinterpret_cast<u32x4 *>(y + off) = *reinterpret_cast<const u32x4 *>(&stile[ml * TP + p8 * 8]);
-            }
-        } else {
-            // Phase-strided rows: runs of 8 tile pixels of one channel.  When a run lies
-            // in one output row its 8 outputs sit s2 elements apart: one LDS vector read,
-            // one address, 8 stores.  Runs that cross a row or the tile end go element by
-            // element.
-            const int nruns = (npix + 7) / 8;
-            const int s2 = p.s[2];
-            for (int u = tid; u < mvalid * nruns; u += kThreads) {
-                const int ml = u / nruns, pl0 = (u - ml * nruns) * 8;
-                _Float16 *const yc = y + (size_t(n) * p.M + g * p.Mg + mt * BM + ml) * opix;
-                const int q = tl.q0 + pl0;
-                const int row = tl.seg ? tl.row_lo : q / J2;
-                const int col = q - row * J2;
-                if (pl0 + 8 <= npix && col + 8 <= J2) {
-                    const u32x4 v8 = *reinterpret_cast<const u32x4 *>(&stile[ml * TP + pl0]);
-                    _Float16 *const dst = yc + pixel_offset(pl0);
-#pragma unroll
-                    for (int e = 0; e < 8; ++e)
-                        dst[e * s2] = __builtin_bit_cast(_Float16, (unsigned short)(v8[e >> 1] >> (16 * (e & 1))));
-                } else {
-                    for (int pl = pl0; pl < min(pl0 + 8, npix); ++pl) yc[pixel_offset(pl)] = stile[ml * TP + pl];
-                }
-            }
-        }
-    }
+    };
+    with_activation(p.act, output_stage);
 }
 
 // Wp[g][t][m][c] = W[g*Cg + c][m][t], zero outside c < Cg, m < Mg.  One thread writes

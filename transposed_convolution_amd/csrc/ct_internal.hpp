@@ -81,16 +81,38 @@ struct Act {
     int kind = CT_ACT_IDENTITY;
     float p0 = 0.0f, p1 = 0.0f;
     __host__ __device__ bool identity() const { return kind == CT_ACT_IDENTITY; }
+    // Every candidate is formed and one selected: with a block-uniform kind this is a few
+    // selects per element and no branches (a switch here became per-element branches).
+    // Hot output loops test identity() once and skip the call.
     __host__ __device__ float operator()(float v) const
     {
-        switch (kind) {
-        case CT_ACT_RELU: return v > 0.0f ? v : 0.0f;
-        case CT_ACT_LEAKY_RELU: return v >= 0.0f ? v : p0 * v;
-        case CT_ACT_CLIP: return v < p0 ? p0 : (v > p1 ? p1 : v);
-        default: return v;
-        }
+        const float relu = v > 0.0f ? v : 0.0f;
+        const float leaky = v >= 0.0f ? v : p0 * v;
+        const float clip = v < p0 ? p0 : (v > p1 ? p1 : v);
+        return kind == CT_ACT_RELU ? relu : kind == CT_ACT_LEAKY_RELU ? leaky : kind == CT_ACT_CLIP ? clip : v;
     }
 };
+
+// Calls f(fn) with fn the activation as a branch-free float -> float function, one
+// instance per kind: output loops written inside f then carry no per-element dispatch.
+template <typename F>
+__device__ __forceinline__ void with_activation(const Act &a, F &&f)
+{
+    switch (a.kind) {
+    case CT_ACT_RELU: f([](float v) { return v > 0.0f ? v : 0.0f; }); break;
+    case CT_ACT_LEAKY_RELU: {
+        const float slope = a.p0;
+        f([slope](float v) { return v >= 0.0f ? v : slope * v; });
+        break;
+    }
+    case CT_ACT_CLIP: {
+        const float lo = a.p0, hi = a.p1;
+        f([lo, hi](float v) { return v < lo ? lo : (v > hi ? hi : v); });
+        break;
+    }
+    default: f([](float v) { return v; }); break;
+    }
+}
 
 // Launchers (one per kernel family); each returns CT_OK or CT_EDEVICE (message in err).
 ct_status launch_direct(const Geom &g, ct_dtype dt, bool cl, const void *x, const void *w,

@@ -128,3 +128,12 @@ C5_S2 = C5_S1.with_(
     attrs=dict(strides=[2, 2, 2], pads=[1] * 6, output_padding=[1, 1, 1], group=1), note="")
 
 CONFIGS = {w.name: w for w in (C1, C2, C3, C4, C4_NHWC, C5_S1, C5_S1_P1, C5_S2)}
+
+# Extra shapes (not benchmark configurations): the decoder tensors of C4 with kernels no
+# longer than the stride, where every output receives at most one tap per axis.
+F2_K2S2 = C4.with_(name="f2_2d_f16_k2_s2", w_shape=(512, 256, 2, 2),
+                   attrs=dict(strides=[2, 2], pads=[0, 0, 0, 0], group=1),
+                   w_dist=("N", 0.0, 1.0 / math.sqrt(512 * 4)), seed=6)
+F2_1X1 = C4.with_(name="f2_2d_f16_1x1", w_shape=(512, 256, 1, 1), attrs=dict(strides=[1, 1], group=1),
+                  w_dist=("N", 0.0, 1.0 / math.sqrt(512)), seed=7)
+EXTRAS = {w.name: w for w in (F2_K2S2, F2_1X1)}
