@@ -411,8 +411,15 @@ __global__ __launch_bounds__(kThreads, OCC) void igemm_kernel(const _Float16 *x,
         load_w(cur, wreg);
         store_w(0, wreg);
         __syncthreads();
-        // MFMAs of one step: weight tile from buffer buf, the halo window of the step's taps
-        auto mma_step = [&](const StepIdx &cur, int buf) {
+        // MFMAs of one step: weight tile from buffer buf, the halo window of the step's taps.
+        // pre_w() issues the next weight tile's global loads, pre_h() a part of the next
+        // halo, post() the weight tile's LDS writes; they are spread between the MFMAs of
+        // the first, the second and the last k-step (one load per MFMA, one LDS write per
+        // two MFMAs) rather than issued in bursts, so no wave waits at issue for the memory
+        // pipes the four waves share.  The weight loads stay ahead of the halo loads (the
+        // k-step boundary is a scheduling fence): loads complete in issue order, and the
+        // LDS writes must not wait for the halo.
+        auto mma_step = [&](const StepIdx &cur, int buf, auto pre_w, auto pre_h, auto post) {
             // tap shift inside the halo: (beta - beta_min) rows and columns
             const int toff = ((nt1 - 1 - cur.t1) * bs1 * tl.HC + (nt2 - 1 - cur.t2) * bs2 + cshift) * ROW;
             const unsigned char *hb = lds_h + toff;
@@ -433,9 +440,29 @@ __global__ __launch_bounds__(kThreads, OCC) void igemm_kernel(const _Float16 *x,
                     for (int j = 0; j < WN; ++j)
                         b[nb][j] = *reinterpret_cast<const f16x8 *>(hb + hoff[j] + (h + 1) * 32);
                 }
-                // fence: the reads above are issued before these MFMAs, which keep source
-                // order (each accumulator is touched once per k-step)
-                __builtin_amdgcn_sched_barrier(0);
+                if (h == 0 || (h == 1 && h < KSUB - 1)) {
+                    if (h == 0) pre_w();
+                    else pre_h();
+                    // fragment reads first, then alternate one global load and one MFMA
+                    __builtin_amdgcn_sched_group_barrier(0x100, 2 * (WM + WN), 0);
+#pragma unroll
+                    for (int k = 0; k < WM * WN; ++k) {
+                        __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+                        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                    }
+                } else if (h == KSUB - 1) {
+                    if (KSUB == 2) pre_h();
+                    post();
+#pragma unroll
+                    for (int k = 0; k < WM * WN / 2; ++k) {
+                        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+                        __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);
+                    }
+                } else {
+                    // fence: the reads above are issued before these MFMAs
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+                // the MFMAs keep source order (each accumulator is touched once per k-step)
 #pragma unroll
                 for (int i = 0; i < WM; ++i)
 #pragma unroll
@@ -470,12 +497,14 @@ __global__ __launch_bounds__(kThreads, OCC) void igemm_kernel(const _Float16 *x,
                     c.t2 = u - c.t1 * nt2;
                     StepIdx nx = c;
                     advance(nx);
-                    load_w(s + 1 < nsteps ? nx : c, wreg);  // the last step reloads a valid tile
-                    hv |= load_halo_part(std::integral_constant<int, PB>{}, std::integral_constant<int, PE>{}, hch,
-                                         ht0, hreg);
-                    asm volatile("" ::: "memory");  // the loads go out ahead of the MFMAs
-                    mma_step(c, s & 1);
-                    store_w((s + 1) & 1, wreg);
+                    const StepIdx wnext = s + 1 < nsteps ? nx : c;  // the last step reloads a valid tile
+                    mma_step(
+                        c, s & 1, [&] { load_w(wnext, wreg); },
+                        [&] {
+                            hv |= load_halo_part(std::integral_constant<int, PB>{}, std::integral_constant<int, PE>{},
+                                                 hch, ht0, hreg);
+                        },
+                        [&] { store_w((s + 1) & 1, wreg); });
                     __syncthreads();
                 };
                 g4_step(std::integral_constant<int, 0>{});
@@ -508,8 +537,7 @@ __global__ __launch_bounds__(kThreads, OCC) void igemm_kernel(const _Float16 *x,
                 }
                 // issue the prefetch loads here, ahead of the MFMAs (no later sinking)
                 asm volatile("" ::: "memory");
-                mma_step(cur, s & 1);
-                store_w((s + 1) & 1, wreg);
+                mma_step(cur, s & 1, [] {}, [] {}, [&] { store_w((s + 1) & 1, wreg); });
                 __syncthreads();
                 if (group_last && s + 1 < nsteps) {  // refresh the halo between two barriers
                     store_halo(hreg, hvalid);
