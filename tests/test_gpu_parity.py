@@ -359,6 +359,37 @@ def test_column_phase_pairs(T, case, integer):
         check(got, ref, "f16", integer, f"pair {kernel} x{xs} w{ws} {attrs}")
 
 
+SINGLE_TAP = [
+    # (x_shape, w_shape, attrs): M/group > 64 and at most one tap per axis in every phase
+    # (kernels no longer than the stride, 1x1): the implicit-GEMM kernel's instance that
+    # double-buffers each step's input tile
+    ((2, 64, 9, 16), (64, 96, 1, 1), dict(strides=[1, 1])),
+    ((2, 64, 9, 16), (64, 80, 1, 1), dict(strides=[1, 1])),
+    ((2, 32, 7, 16), (32, 72, 2, 2), dict(strides=[2, 2])),
+    ((1, 40, 6, 24), (40, 130, 3, 3), dict(strides=[3, 3], pads=[0, 1, 0, 1])),
+    ((1, 16, 3, 5, 8), (16, 72, 2, 2, 2), dict(strides=[2, 2, 2])),
+    ((2, 24, 5, 16), (24, 100, 2, 1), dict(strides=[2, 1], output_padding=[1, 0])),
+]
+
+
+@pytest.mark.parametrize("integer", [False, True], ids=["float", "int"])
+@pytest.mark.parametrize("cl", [False, True], ids=["nc", "cl"])
+@pytest.mark.parametrize("case", SINGLE_TAP, ids=lambda c: f"{c[0]}_{c[1]}")
+def test_single_tap_groups(T, case, cl, integer):
+    xs, ws, attrs = case
+    _log(f"[case] single-tap x{xs} w{ws} {attrs} cl={cl} integer={integer}")
+    rng = np.random.default_rng(zlib.crc32(repr(case).encode()) + 2 * cl + integer)
+    gen = (lambda sz: rng.integers(-2, 3, size=sz)) if integer else (lambda sz: rng.normal(size=sz))
+    x = gen(xs).astype(np.float16)
+    w = (gen(ws) * (1 if integer else 0.1)).astype(np.float16)
+    b = gen(ws[1]).astype(np.float16)
+    ref = O.convtranspose(x, w, b, **attrs)
+    for kernel in ("igemm", "auto"):
+        got = gpu_run(T, x, w, b, attrs, cl, kernel)
+        assert got is not None, "the implicit-GEMM kernel serves these shapes"
+        check(got, ref, "f16", integer, f"single-tap {kernel} x{xs} w{ws} {attrs} cl={cl}")
+
+
 ACT_CASES = [
     # (name, x_shape, w_shape, attrs, dtype, channels_last, forced kernel)
     ("igemm16_pair", (2, 64, 9, 16), (64, 96, 4, 4), dict(strides=[2, 2], pads=[1] * 4), "f16", False, "igemm"),
