@@ -419,3 +419,166 @@ int oracle_convtranspose_at(int nsp, const int64_t *x_shape, const double *x,
         return or_fail(err, errlen, "a requested point lies outside Y (or has > 64 taps per axis)");
     return OR_OK;
 }
+
+/* ------------------------------------------------------------------------------------
+ * Forward convolution (ONNX Conv), the adjoint of the transposed convolution with the
+ * same W.  Attributes follow the webgpu-kernels "ai.onnx.QLinearConv" README (its
+ * Attributes table is that of a convolution): auto_pad NOTSET / SAME_UPPER /
+ * SAME_LOWER / VALID with SAME giving O = ceil(L / s), pads in ONNX order, strides,
+ * dilations, group, kernel_shape; W is (M, C/group, k1..kn) (its Inputs table).
+ *
+ * Definition: Y[n, m, o] = bias[m] + sum over c of m's group and taps k of
+ *     X[n, c, o*s - b + k*d] * W[m, c', k],   X = 0 outside [0, L) on each axis.
+ * Readings (the pages print no output-size formula): the outputs are the window
+ * positions that fit inside the padded input, O = floor((L + b + e - d(K-1) - 1)/s) + 1
+ * (0 when no window fits); SAME's total pad is max(0, (O-1)s + d(K-1) + 1 - L), the
+ * odd extra at the end (UPPER) or the beginning (LOWER); pads together with an
+ * auto_pad other than NOTSET, negative pads and non-positive strides or dilations are
+ * errors.
+ * ---------------------------------------------------------------------------------- */
+typedef struct {
+    int nsp;
+    int64_t N, C, M, group, Cg, Mg;
+    int64_t L[3], K[3], s[3], d[3], b[3], e[3], O[3];
+} or_cgeom;
+
+static int or_conv_resolve(int nsp, const int64_t *xs, const int64_t *ws, int auto_pad,
+                           const int64_t *strides, const int64_t *dilations, const int64_t *pads,
+                           const int64_t *kernel_shape, int64_t group, or_cgeom *g, char *err,
+                           int errlen)
+{
+    int a;
+    if (nsp < 1 || nsp > 3)
+        return or_fail(err, errlen, "spatial rank must be 1, 2 or 3");
+    if (auto_pad < OR_NOTSET || auto_pad > OR_VALID)
+        return or_fail(err, errlen, "unknown auto_pad");
+    if (pads && auto_pad != OR_NOTSET)
+        return or_fail(err, errlen, "pads cannot be combined with an automatic padding mode");
+    if (group < 1)
+        return or_fail(err, errlen, "group must be >= 1");
+    memset(g, 0, sizeof(*g));
+    g->nsp = nsp;
+    g->N = xs[0];
+    g->C = xs[1];
+    g->M = ws[0];
+    g->group = group;
+    if (g->N < 0 || g->C < 0 || g->M < 0 || ws[1] < 0)
+        return or_fail(err, errlen, "negative dimension");
+    if (g->C % group != 0 || g->M % group != 0)
+        return or_fail(err, errlen, "C and M must be multiples of group");
+    g->Cg = g->C / group;
+    g->Mg = g->M / group;
+    if (ws[1] != g->Cg)
+        return or_fail(err, errlen, "W.shape[1] must equal C / group");
+    for (a = 0; a < nsp; a++) {
+        int64_t L = xs[2 + a], K = ws[2 + a], s = strides ? strides[a] : 1, d = dilations ? dilations[a] : 1;
+        int64_t b = 0, e = 0, num;
+        if (L < 0 || K < 1)
+            return or_fail(err, errlen, "bad spatial size or kernel size");
+        if (kernel_shape && kernel_shape[a] != K)
+            return or_fail(err, errlen, "kernel_shape does not match W");
+        if (s < 1 || d < 1)
+            return or_fail(err, errlen, "strides and dilations must be >= 1");
+        if (auto_pad == OR_NOTSET && pads) {
+            b = pads[a];
+            e = pads[nsp + a];
+            if (b < 0 || e < 0)
+                return or_fail(err, errlen, "pads must be >= 0");
+        } else if (auto_pad == OR_SAME_UPPER || auto_pad == OR_SAME_LOWER) {
+            int64_t O = (L + s - 1) / s, tot = (O - 1) * s + d * (K - 1) + 1 - L;
+            if (tot < 0)
+                tot = 0;
+            if (auto_pad == OR_SAME_UPPER) {
+                b = tot / 2;
+                e = tot - b;
+            } else {
+                e = tot / 2;
+                b = tot - e;
+            }
+        }
+        num = L + b + e - d * (K - 1) - 1;
+        g->L[a] = L;
+        g->K[a] = K;
+        g->s[a] = s;
+        g->d[a] = d;
+        g->b[a] = b;
+        g->e[a] = e;
+        g->O[a] = num >= 0 ? num / s + 1 : 0;
+    }
+    return OR_OK;
+}
+
+int oracle_conv_output_shape(int nsp, const int64_t *x_shape, const int64_t *w_shape, int auto_pad,
+                             const int64_t *strides, const int64_t *dilations, const int64_t *pads,
+                             const int64_t *kernel_shape, int64_t group, int64_t *y_shape,
+                             int64_t *pads_out, char *err, int errlen)
+{
+    or_cgeom g;
+    int a, rc = or_conv_resolve(nsp, x_shape, w_shape, auto_pad, strides, dilations, pads, kernel_shape,
+                                group, &g, err, errlen);
+    if (rc != OR_OK)
+        return rc;
+    y_shape[0] = g.N;
+    y_shape[1] = g.M;
+    for (a = 0; a < nsp; a++) {
+        y_shape[2 + a] = g.O[a];
+        if (pads_out) {
+            pads_out[a] = g.b[a];
+            pads_out[nsp + a] = g.e[a];
+        }
+    }
+    return OR_OK;
+}
+
+/* Whole output by the gather definition (NCHW order); threads split the (n, m) planes,
+ * and each output sums its group's channels c, then taps k, ascending. */
+int oracle_conv_f64(int nsp, const int64_t *x_shape, const double *x, const int64_t *w_shape,
+                    const double *w, const double *bias, int auto_pad, const int64_t *strides,
+                    const int64_t *dilations, const int64_t *pads, const int64_t *kernel_shape,
+                    int64_t group, double *y, int64_t y_len, char *err, int errlen)
+{
+    or_cgeom g;
+    int64_t in_plane, out_plane, taps, plane;
+    int rc = or_conv_resolve(nsp, x_shape, w_shape, auto_pad, strides, dilations, pads, kernel_shape,
+                             group, &g, err, errlen);
+    if (rc != OR_OK)
+        return rc;
+    in_plane = or_prod(g.L, nsp);
+    out_plane = or_prod(g.O, nsp);
+    taps = or_prod(g.K, nsp);
+    if (y_len != g.N * g.M * out_plane)
+        return or_fail(err, errlen, "y buffer length does not match the resolved output");
+#pragma omp parallel for schedule(dynamic, 1)
+    for (plane = 0; plane < g.N * g.M; plane++) {
+        int64_t n = plane / g.M, m = plane % g.M, grp = m / g.Mg;
+        double *yp = y + plane * out_plane;
+        int64_t p, cc, kk;
+        int a;
+        for (p = 0; p < out_plane; p++) {
+            int64_t ocoord[3];
+            double acc = bias ? bias[m] : 0.0;
+            or_decode(p, g.O, nsp, ocoord);
+            for (cc = 0; cc < g.Cg; cc++) {
+                const double *xp = x + (n * g.C + grp * g.Cg + cc) * in_plane;
+                const double *wp = w + (m * g.Cg + cc) * taps;
+                for (kk = 0; kk < taps; kk++) {
+                    int64_t kc[3], flat = 0;
+                    int inside = 1;
+                    or_decode(kk, g.K, nsp, kc);
+                    for (a = 0; a < nsp; a++) {
+                        int64_t i = ocoord[a] * g.s[a] - g.b[a] + kc[a] * g.d[a];
+                        if (i < 0 || i >= g.L[a]) {
+                            inside = 0;
+                            break;
+                        }
+                        flat = flat * g.L[a] + i;
+                    }
+                    if (inside)
+                        acc += xp[flat] * wp[kk];
+                }
+            }
+            yp[p] = acc;
+        }
+    }
+    return OR_OK;
+}

@@ -57,8 +57,13 @@ def load(path: Optional[str] = None):
         f64p, ctypes.c_int64, ctypes.c_char_p, ctypes.c_int]
     lib.oracle_convtranspose_at.argtypes = [ctypes.c_int, i64p, f64p, i64p, f64p, f64p] + attrs + [
         i64p, ctypes.c_int64, f64p, ctypes.c_char_p, ctypes.c_int]
+    cattrs = [ctypes.c_int, i64p, i64p, i64p, i64p, ctypes.c_int64]  # forward convolution
+    lib.oracle_conv_output_shape.argtypes = [ctypes.c_int, i64p, i64p] + cattrs + [
+        i64p, i64p, ctypes.c_char_p, ctypes.c_int]
+    lib.oracle_conv_f64.argtypes = [ctypes.c_int, i64p, f64p, i64p, f64p, f64p] + cattrs + [
+        f64p, ctypes.c_int64, ctypes.c_char_p, ctypes.c_int]
     for fn in ("oracle_output_shape", "oracle_useful_macs", "oracle_convtranspose_f64",
-               "oracle_convtranspose_at", "oracle_threads"):
+               "oracle_convtranspose_at", "oracle_threads", "oracle_conv_output_shape", "oracle_conv_f64"):
         getattr(lib, fn).restype = ctypes.c_int
     lib.oracle_threads.argtypes = []
     if path is None:
@@ -202,3 +207,57 @@ def activation(y: np.ndarray, kind: str = "identity", params: Sequence[float] = 
     if kind == "clip" and len(p) == 2 and np.all(np.isfinite(p)) and p[0] <= p[1]:
         return np.where(y < p[0], p[0], np.where(y > p[1], p[1], y))
     raise OracleError(f"activation {kind!r} with parameters {params!r} is not defined")
+
+
+# ------------------------------------------------------------------------------------
+# Forward convolution (ONNX Conv with the same W layout (M, C/group, k..)): the adjoint
+# of the transposed convolution.  Arithmetic in ct_oracle.c (oracle_conv_f64).
+# ------------------------------------------------------------------------------------
+def _conv_attr_args(auto_pad="NOTSET", strides=None, dilations=None, pads=None, kernel_shape=None, group=1):
+    keep = []
+    out = [AUTO_PAD[auto_pad]]
+    for v in (strides, dilations, pads, kernel_shape):
+        arr, ptr = _i64(v)
+        keep.append(arr)
+        out.append(ptr)
+    out.append(int(group))
+    return out, keep
+
+
+def conv_output_shape(x_shape, w_shape, lib=None, **attrs):
+    """Resolved forward-convolution output shape (N, M, O1..On) and the applied pads."""
+    lib = lib or load()
+    nsp = len(x_shape) - 2
+    if len(w_shape) != len(x_shape):
+        raise OracleError("W must have the same rank as X")
+    xs, xp = _i64(x_shape)
+    ws, wp = _i64(w_shape)
+    args, keep = _conv_attr_args(**attrs)
+    ys = np.zeros(nsp + 2, dtype=np.int64)
+    pd = np.zeros(2 * nsp, dtype=np.int64)
+    err = ctypes.create_string_buffer(256)
+    rc = lib.oracle_conv_output_shape(nsp, xp, wp, *args,
+                                      ys.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)),
+                                      pd.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)), err, 256)
+    _check(rc, err)
+    return tuple(int(v) for v in ys), [int(v) for v in pd]
+
+
+def conv(x: np.ndarray, w: np.ndarray, bias: Optional[np.ndarray] = None, lib=None, **attrs) -> np.ndarray:
+    """Whole forward-convolution output in fp64 by the gather definition (NC.. layout)."""
+    lib = lib or load()
+    x64, xp = _f64(x)
+    w64, wp = _f64(w)
+    b64, bp = _f64(bias)
+    yshape, _ = conv_output_shape(x64.shape, w64.shape, lib=lib, **attrs)
+    if b64 is not None and b64.shape != (yshape[1],):
+        raise OracleError("bias must be 1-D of length M")
+    y = np.zeros(yshape, dtype=np.float64)
+    args, keep = _conv_attr_args(**attrs)
+    xs, xsp = _i64(x64.shape)
+    ws, wsp = _i64(w64.shape)
+    err = ctypes.create_string_buffer(256)
+    rc = lib.oracle_conv_f64(x64.ndim - 2, xsp, xp, wsp, wp, bp, *args,
+                             y.ctypes.data_as(ctypes.POINTER(ctypes.c_double)), y.size, err, 256)
+    _check(rc, err)
+    return y

@@ -504,7 +504,147 @@ def pin_activation_closed_forms(lib, seed=22):
         raise AssertionError(f"activation {kind} {params} accepted")
 
 
+# ------------------------------------------------------------------------------------
+# Forward convolution (ONNX Conv, the adjoint of the transposed convolution)
+# ------------------------------------------------------------------------------------
+def random_conv_case(rng: np.random.Generator, nsp=None, auto=False, max_L=7):
+    """A random small forward-convolution problem (W is (M, C/group, k..))."""
+    while True:
+        n = int(nsp or rng.integers(1, 4))
+        group = int(rng.choice([1, 1, 2, 3]))
+        Cg, Mg = int(rng.integers(1, 4)), int(rng.integers(1, 4))
+        N = int(rng.integers(1, 3))
+        Ls = [int(rng.integers(1, max_L + 1)) for _ in range(n)]
+        Ks = [int(rng.integers(1, 4)) for _ in range(n)]
+        s = [int(rng.integers(1, 4)) for _ in range(n)]
+        d = [int(rng.integers(1, 3)) for _ in range(n)]
+        attrs = dict(strides=s, dilations=d, group=group)
+        if auto:
+            attrs["auto_pad"] = str(rng.choice(["SAME_UPPER", "SAME_LOWER", "VALID"]))
+        else:
+            attrs["pads"] = [int(rng.integers(0, 3)) for _ in range(2 * n)]
+        x = rng.normal(size=(N, Cg * group, *Ls))
+        w = rng.normal(size=(Mg * group, Cg, *Ks))
+        b = rng.normal(size=(Mg * group,)) if rng.random() < 0.7 else None
+        try:
+            ys, _ = O.conv_output_shape(x.shape, w.shape, **attrs)
+        except O.OracleError:
+            continue
+        if min(ys) == 0:
+            continue
+        return x, w, b, attrs
+
+
+def pin_conv_torch_library(lib, count=120, seed=31):
+    """The forward convolution against PyTorch's CPU convolution in float64 on the input
+    zero-padded by the applied pads (PyTorch takes symmetric padding only)."""
+    rng = np.random.default_rng(seed)
+    for t in range(count):
+        x, w, b, attrs = random_conv_case(rng, auto=(t % 4 == 3))
+        nsp = x.ndim - 2
+        ys, pads = O.conv_output_shape(x.shape, w.shape, lib=lib, **attrs)
+        fpad = []
+        for a in reversed(range(nsp)):  # F.pad takes the last axis first
+            fpad += [pads[a], pads[nsp + a]]
+        for a in range(nsp):  # a padded axis shorter than the dilated kernel has no output
+            if x.shape[2 + a] + pads[a] + pads[nsp + a] < attrs["dilations"][a] * (w.shape[2 + a] - 1) + 1:
+                raise AssertionError(f"outputs {ys} where no window fits the padded input: {attrs}")
+        xt = F.pad(torch.from_numpy(x), fpad)
+        ref = _CV[nsp](xt, torch.from_numpy(w), None if b is None else torch.from_numpy(b),
+                       stride=tuple(attrs["strides"]), dilation=tuple(attrs["dilations"]),
+                       groups=attrs["group"]).numpy()
+        got = O.conv(x, w, b, lib=lib, **attrs)
+        assert got.shape == ref.shape == tuple(ys), (got.shape, ref.shape, attrs)
+        assert np.allclose(got, ref, rtol=1e-12, atol=1e-12), attrs
+    # SAME_UPPER at stride 1 is PyTorch's padding="same" (extra pad at the end)
+    for t in range(30):
+        x, w, b, attrs = random_conv_case(rng)
+        attrs = dict(strides=[1] * (x.ndim - 2), dilations=attrs["dilations"], group=attrs["group"],
+                     auto_pad="SAME_UPPER")
+        got = O.conv(x, w, b, lib=lib, **attrs)
+        ref = _CV[x.ndim - 2](torch.from_numpy(x), torch.from_numpy(w), None if b is None else torch.from_numpy(b),
+                              dilation=tuple(attrs["dilations"]), groups=attrs["group"], padding="same").numpy()
+        assert got.shape == ref.shape and np.allclose(got, ref, rtol=1e-12, atol=1e-12), attrs
+    # SAME keeps ceil(L / s) outputs (QLinearConv Attributes, auto_pad)
+    for t in range(60):
+        x, w, b, attrs = random_conv_case(rng)
+        for mode in ("SAME_UPPER", "SAME_LOWER"):
+            a2 = dict(strides=attrs["strides"], dilations=attrs["dilations"], group=attrs["group"], auto_pad=mode)
+            ys, _ = O.conv_output_shape(x.shape, w.shape, lib=lib, **a2)
+            assert list(ys[2:]) == [-(-L // s) for L, s in zip(x.shape[2:], attrs["strides"])]
+
+
+def pin_conv_brute_force(lib, count=40, seed=32):
+    """Tiny problems by a different loop nest: every input sample is sent to the outputs
+    o with o*s - b + k*d equal to its index (a scatter, where the oracle gathers)."""
+    rng = np.random.default_rng(seed)
+    for _ in range(count):
+        x, w, b, attrs = random_conv_case(rng, max_L=5)
+        nsp = x.ndim - 2
+        ys, pads = O.conv_output_shape(x.shape, w.shape, lib=lib, **attrs)
+        s, d, G = attrs["strides"], attrs["dilations"], attrs["group"]
+        Mg, Cg = w.shape[0] // G, w.shape[1]
+        y = np.zeros(ys)
+        if b is not None:
+            y += b.reshape((1, -1) + (1,) * nsp)
+        for idx in np.ndindex(*x.shape):
+            n, c, i = idx[0], idx[1], idx[2:]
+            g = c // Cg
+            for k in np.ndindex(*w.shape[2:]):
+                o = []
+                for a in range(nsp):
+                    q = i[a] + pads[a] - k[a] * d[a]
+                    if q < 0 or q % s[a] or q // s[a] >= ys[2 + a]:
+                        break
+                    o.append(q // s[a])
+                else:
+                    for mm in range(Mg):
+                        m = g * Mg + mm
+                        y[(n, m) + tuple(o)] += x[idx] * w[(m, c - g * Cg) + k]
+        assert np.allclose(O.conv(x, w, b, lib=lib, **attrs), y, rtol=1e-12, atol=1e-12), attrs
+
+
+def pin_conv_adjoint(lib, count=80, seed=33):
+    """<ConvT_W(x), a> == <x, Conv_W(a)>: the forward convolution with the same W,
+    strides, dilations and begin pads, and end pads e - output_padding, is the adjoint
+    of the (separately pinned) transposed convolution."""
+    rng = np.random.default_rng(seed)
+    done = 0
+    while done < count:
+        x, w, _, attrs = random_case(rng)
+        nsp = x.ndim - 2
+        _, pads = O.output_shape(x.shape, w.shape, lib=lib, **attrs)
+        op = attrs["output_padding"]
+        ends = [pads[nsp + a] - op[a] for a in range(nsp)]
+        if min(ends) < 0 or min(pads[:nsp]) < 0:
+            continue
+        y = O.convtranspose(x, w, None, lib=lib, **attrs)
+        a = rng.normal(size=y.shape)
+        cattrs = dict(strides=attrs["strides"], dilations=attrs["dilations"], group=attrs["group"],
+                      pads=list(pads[:nsp]) + ends)
+        back = O.conv(a, w, None, lib=lib, **cattrs)
+        assert back.shape == x.shape, (back.shape, x.shape, attrs)
+        lhs, rhs = float(np.sum(a * y)), float(np.sum(x * back))
+        assert abs(lhs - rhs) <= 1e-10 * (1.0 + abs(lhs)), (lhs, rhs, attrs)
+        done += 1
+
+
+def pin_conv_rejects_invalid(lib):
+    x, w = np.zeros((1, 4, 6, 6)), np.zeros((6, 2, 3, 3))
+    bad = [dict(group=3), dict(group=2, strides=[0, 1]), dict(group=2, dilations=[1, 0]),
+           dict(group=2, pads=[1, 1, -1, 0]), dict(group=2, pads=[1, 1, 1, 1], auto_pad="VALID"),
+           dict(group=2, kernel_shape=[3, 2])]
+    for attrs in bad:
+        try:
+            O.conv(x, w, None, lib=lib, **attrs)
+        except O.OracleError:
+            continue
+        raise AssertionError(f"accepted {attrs}")
+    O.conv(x, w, None, lib=lib, group=2)  # the valid base case
+
+
 ALL_PINS = [pin_activation_closed_forms, pin_golden, pin_benchmark_shapes, pin_torch_library, pin_brute_force_gather,
             pin_zero_insertion, pin_numpy_convolve, pin_adjoint, pin_stride1_forward,
             pin_pointwise_matmul, pin_group_split, pin_linearity_translation, pin_useful_macs,
-            pin_points_match_whole, pin_rejects_invalid]
+            pin_points_match_whole, pin_rejects_invalid, pin_conv_torch_library, pin_conv_brute_force,
+            pin_conv_adjoint, pin_conv_rejects_invalid]

@@ -42,6 +42,17 @@ MUTANTS = {
                         "if (i * g.s[a] + g.b[a] + k * g.d[a] == o) {"),
     "useful_macs_upper_bound_inclusive": ("if (o >= 0 && o < g.O[a])\n                    hits++;",
                                           "if (o >= 0 && o <= g.O[a])\n                    hits++;"),
+    # forward convolution
+    "conv_pad_sign": ("int64_t i = ocoord[a] * g.s[a] - g.b[a] + kc[a] * g.d[a];",
+                      "int64_t i = ocoord[a] * g.s[a] + g.b[a] + kc[a] * g.d[a];"),
+    "conv_dilation_ignored": ("int64_t i = ocoord[a] * g.s[a] - g.b[a] + kc[a] * g.d[a];",
+                              "int64_t i = ocoord[a] * g.s[a] - g.b[a] + kc[a];"),
+    "conv_group_channels": ("x + (n * g.C + grp * g.Cg + cc) * in_plane", "x + (n * g.C + cc) * in_plane"),
+    "conv_output_size_rounded_up": ("g->O[a] = num >= 0 ? num / s + 1 : 0;",
+                                    "g->O[a] = num >= 0 ? (num + s - 1) / s + 1 : 0;"),
+    "conv_same_total_off_by_one": ("tot = (O - 1) * s + d * (K - 1) + 1 - L;", "tot = (O - 1) * s + d * (K - 1) - L;"),
+    "conv_weight_read_transposed": ("const double *wp = w + (m * g.Cg + cc) * taps;",
+                                    "const double *wp = w + (cc * g.M + m) * taps;"),
 }
 
 
