@@ -221,6 +221,50 @@ int convtranspose_select_kernel(ct_dtype dtype, int nsp, int channels_last, cons
  */
 ct_status convtranspose_profile_events(void *before, void *after);
 
+/*
+ * The forward convolution (ONNX Conv) with the same W: the adjoint of the transposed
+ * convolution (webgpu-kernels "ai.onnx.QLinearConv" README, Inputs and Attributes tables,
+ * for the convolution's layout and attributes: W is (M, C/group, k1..kn), auto_pad
+ * SAME_* keeps ceil(L / stride) outputs).
+ *   Y[n, m, o] = bias[m] + sum over c of m's group and taps k of X[n, c, o*s - b + k*d] W[m, c', k]
+ * with X = 0 outside the input.  Readings where the pages are silent: the outputs are
+ * the window positions that fit inside the padded input,
+ * O = floor((L + b + e - d*(K-1) - 1) / s) + 1 (0 if none fits); SAME's total pad
+ * max(0, (O-1)*s + d*(K-1) + 1 - L) puts the odd part at the end (UPPER) or the beginning
+ * (LOWER); pads with an auto_pad other than NOTSET, negative pads, strides or dilations
+ * below 1 and a kernel_shape that differs from W are CT_EINVAL.
+ * With a transposed convolution's strides, dilations, begin pads and end pads
+ * e - output_padding, Conv_W is its adjoint: <ConvT_W(x), y> = <x, Conv_W(y)>.
+ *
+ * Host only; writes y_shape_out[nsp+2] = {N, M, O1..On} and, if pads_out is not NULL,
+ * the 2*nsp applied pads.  Returns CT_OK or CT_EINVAL.
+ */
+ct_status convolution_output_shape(int nsp, const int64_t *x_shape, const int64_t *w_shape,
+                                   ct_auto_pad auto_pad, const int64_t *strides,
+                                   const int64_t *dilations, const int64_t *pads,
+                                   const int64_t *kernel_shape, int64_t group, int64_t *y_shape_out,
+                                   int64_t *pads_out);
+
+/*
+ * The forward convolution enqueued on `stream`.  Arguments as for convtranspose_nd,
+ * except: x is (N, C, D1..Dn), w is (M, C/group, k1..kn), bias has M elements, y_shape
+ * must equal convolution_output_shape's result, and there is no output_padding or
+ * output_shape.
+ *   kernel  CT_KERNEL_AUTO (stride 1 on every axis and channel counts per group of at
+ *           least 16 where the MFMA path serves the shape: the implicit GEMM on the
+ *           stride-1 transposed-convolution form, else the gather kernel),
+ *           CT_KERNEL_DIRECT (the gather kernel, any arguments) or CT_KERNEL_IGEMM
+ *           (CT_EUNSUPPORTED when that path cannot serve the call).
+ * The MFMA path takes stream-ordered scratch (hipMallocAsync / hipFreeAsync on `stream`)
+ * for the re-laid-out weights.  Validation happens before anything is enqueued; errors
+ * leave y untouched and are reported by convtranspose_last_error().
+ */
+ct_status convolution_nd(ct_kernel kernel, ct_dtype dtype, int nsp, int channels_last, const void *x,
+                         const int64_t *x_shape, const void *w, const int64_t *w_shape,
+                         const void *bias, void *y, const int64_t *y_shape, ct_auto_pad auto_pad,
+                         const int64_t *strides, const int64_t *dilations, const int64_t *pads,
+                         const int64_t *kernel_shape, int64_t group, void *stream);
+
 /* Text of the last error on the calling host thread ("" after a successful call).
  * The pointer stays valid until the next library call on that thread. */
 const char *convtranspose_last_error(void);

@@ -441,6 +441,112 @@ def test_fused_activation(T, case, integer):
     check(y.cpu().numpy().astype(np.float64), ref, dtype, integer, f"{name} identity")
 
 
+# --------------------------------------------------------------------------------------
+# the forward convolution with the same W (the adjoint)
+# --------------------------------------------------------------------------------------
+def conv_gpu_run(T, x, w, b, attrs, cl=False, kernel="auto"):
+    dev = torch.device("cuda:0")
+    tx = torch.from_numpy(np.ascontiguousarray(x)).to(dev)
+    if cl:
+        tx = T.to_channels_last(tx)
+    tw = torch.from_numpy(np.ascontiguousarray(w)).to(dev)
+    tb = None if b is None else torch.from_numpy(b).to(dev)
+    y = T.convolution_nd(tx, tw, tb, channels_last=cl, kernel=kernel, **attrs)
+    torch.cuda.synchronize()
+    return y.cpu().numpy().astype(np.float64)
+
+
+@pytest.mark.parametrize("cl", [False, True], ids=["nc", "cl"])
+@pytest.mark.parametrize("dtype", ["f32", "f16"])
+@pytest.mark.parametrize("kernel", ["direct", "auto"])
+def test_convolution_random_small(T, kernel, dtype, cl):
+    rng = np.random.default_rng(500 + (dtype == "f16") * 2 + cl + 10 * (kernel == "auto"))
+    for t in range(40):
+        x, w, b, attrs = pins.random_conv_case(rng, auto=(t % 4 == 3))
+        integer = t % 2 == 1
+        if integer:
+            x, w = np.round(x), np.round(w)
+            b = None if b is None else np.round(b)
+        x, w = x.astype(NPT[dtype]), w.astype(NPT[dtype])
+        b = None if b is None else b.astype(NPT[dtype])
+        _log(f"[case] conv random #{t} {kernel} {dtype} cl={cl} x{x.shape} w{w.shape} {attrs}")
+        got = conv_gpu_run(T, x, w, b, attrs, cl, kernel)
+        check(got, O.conv(x, w, b, **attrs), dtype, integer, f"conv random #{t} {attrs}")
+
+
+CONV_S1 = [
+    # (x_shape, w_shape, attrs): stride 1 with C/group and M/group >= 16, the MFMA path
+    ((2, 64, 10, 64), (96, 64, 3, 3), dict(pads=[1, 1, 1, 1])),
+    ((2, 32, 9, 16), (80, 32, 4, 4), dict(pads=[2, 1, 1, 2])),
+    ((1, 48, 12, 24), (64, 48, 3, 3), dict(dilations=[2, 1], auto_pad="SAME_LOWER")),
+    ((1, 32, 6, 16), (72, 32, 2, 2), dict(pads=[3, 0, 0, 3])),          # pads beyond the kernel: crops
+    ((1, 64, 5, 8, 8), (48, 64, 3, 3, 3), dict(pads=[1] * 6)),
+    ((2, 64, 32), (64, 32, 5), dict(pads=[2, 2], group=2)),
+]
+
+
+@pytest.mark.parametrize("integer", [False, True], ids=["float", "int"])
+@pytest.mark.parametrize("cl", [False, True], ids=["nc", "cl"])
+@pytest.mark.parametrize("case", CONV_S1, ids=lambda c: f"{c[0]}_{c[1]}")
+def test_convolution_stride1_mfma(T, case, cl, integer):
+    xs, ws, attrs = case
+    if cl and xs[1] % 8:
+        pytest.skip("channels-last MFMA path needs C % 8 == 0")
+    rng = np.random.default_rng(zlib.crc32(repr(case).encode()) + 2 * cl + integer)
+    gen = (lambda sz: rng.integers(-2, 3, size=sz)) if integer else (lambda sz: rng.normal(size=sz))
+    x = gen(xs).astype(np.float16)
+    w = (gen(ws) * (1 if integer else 0.1)).astype(np.float16)
+    b = gen(ws[0]).astype(np.float16)
+    _log(f"[case] conv s1 x{xs} w{ws} {attrs} cl={cl} integer={integer}")
+    ref = O.conv(x, w, b, **attrs)
+    for kernel in ("igemm", "auto", "direct"):
+        got = conv_gpu_run(T, x, w, b, attrs, cl, kernel)
+        check(got, ref, "f16", integer, f"conv s1 {kernel} x{xs} w{ws} {attrs}")
+
+
+def test_convolution_is_the_adjoint(T):
+    """<ConvT_W(x), y> = <x, Conv_W(y)> with both operators on the GPU (float32 inputs,
+    float64 sums on the host), for the transposed convolution's attributes."""
+    rng = np.random.default_rng(77)
+    done = 0
+    while done < 30:
+        x, w, _, attrs = pins.random_case(rng)
+        nsp = x.ndim - 2
+        _, pads = O.output_shape(x.shape, w.shape, **attrs)
+        op = attrs["output_padding"]
+        ends = [pads[nsp + a] - op[a] for a in range(nsp)]
+        if min(ends) < 0 or min(pads[:nsp]) < 0:
+            continue
+        x, w = x.astype(np.float32), w.astype(np.float32)
+        yt = gpu_run(T, x, w, None, attrs)
+        a = rng.normal(size=yt.shape).astype(np.float32)
+        back = conv_gpu_run(T, a, w, None, dict(strides=attrs["strides"], dilations=attrs["dilations"],
+                                                group=attrs["group"], pads=list(pads[:nsp]) + ends))
+        lhs, rhs = float(np.sum(a.astype(np.float64) * yt)), float(np.sum(x.astype(np.float64) * back))
+        assert abs(lhs - rhs) <= 1e-4 * (1.0 + np.sum(np.abs(a * yt))), (lhs, rhs, attrs)
+        done += 1
+
+
+def test_convolution_adjoint_of_3d_config_sampled(T):
+    """The adjoint of the 3-D stride-1 configuration at full size (Y[2,64,18,34,34] back to
+    X[2,128,16,32,32] with W[128,64,3,3,3]) on the MFMA path, checked at sampled outputs."""
+    wl = W.C5_S1
+    ys, pads = O.output_shape(wl.x_shape, wl.w_shape, **wl.attrs)
+    rng = np.random.default_rng(9)
+    a = rng.normal(size=ys).astype(np.float16)
+    w = (rng.normal(size=wl.w_shape) / np.sqrt(64 * 27)).astype(np.float16)
+    b = rng.normal(size=wl.w_shape[0]).astype(np.float16)
+    attrs = dict(pads=list(pads))
+    got = conv_gpu_run(T, a, w, b, attrs, False, "auto")
+    assert got.shape == tuple(wl.x_shape)
+    pts = W.make_points(got.shape, 200, seed=3)
+    # the oracle at the sampled points: outputs of a box of rows around each point
+    for p in pts[:24]:
+        n, m = int(p[0]), int(p[1])
+        sub = O.conv(a[n:n + 1], w[m:m + 1], b[m:m + 1], **attrs)
+        assert abs(got[tuple(p)] - sub[(0, 0) + tuple(p[2:])]) <= 2e-3 * (1 + abs(sub[(0, 0) + tuple(p[2:])]))
+
+
 def test_repeat_runs_bitwise_identical(T):
     wl = REDUCED[2]
     x, w, b = W.make_inputs(wl)

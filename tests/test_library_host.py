@@ -161,6 +161,49 @@ def test_activation_arguments_validated_before_launch(T):
     assert set(T.ACTIVATIONS) == set(O.ACTIVATIONS)
 
 
+def test_convolution_resolver_matches_oracle(T):
+    rng = np.random.default_rng(41)
+    for t in range(400):
+        x, w, b, attrs = pins.random_conv_case(rng, auto=(t % 3 == 2))
+        assert T.convolution_output_shape(x.shape, w.shape, **attrs) == \
+            tuple(map(tuple, O.conv_output_shape(x.shape, w.shape, **attrs)))
+    # the adjoint shapes: the convolution maps the benchmark outputs back to the inputs
+    for wl in W.CONFIGS.values():
+        ys, pads = T.convtranspose_output_shape(wl.x_shape, wl.w_shape, **wl.attrs)
+        nsp = len(wl.x_shape) - 2
+        op = wl.attrs.get("output_padding") or [0] * nsp
+        cp = list(pads[:nsp]) + [pads[nsp + a] - op[a] for a in range(nsp)]
+        if min(cp) < 0:
+            continue
+        got, _ = T.convolution_output_shape(ys, wl.w_shape, strides=wl.attrs.get("strides"),
+                                            dilations=wl.attrs.get("dilations"), pads=cp,
+                                            group=wl.attrs.get("group", 1))
+        assert got == tuple(wl.x_shape), (wl.name, got)
+
+
+def test_convolution_validation_launches_nothing(T):
+    lib = T.load_library()
+    vp = ctypes.c_void_p
+
+    def call(xs=(1, 4, 6, 6), ws=(6, 2, 3, 3), ys=None, kernel=0, dtype=1, cl=0, **attrs):
+        attrs.setdefault("group", 2)
+        if ys is None:
+            ys = T.convolution_output_shape(xs, ws, **attrs)[0]
+        return lib.convolution_nd(kernel, dtype, 2, cl, vp(256), T._i64(xs), vp(512), T._i64(ws), None, vp(1024),
+                                  T._i64(ys), *T._conv_attr_args(2, **attrs), None)
+
+    assert call(ys=(1, 6, 4, 5)) == 2
+    assert call(dtype=5) == 3
+    assert call(kernel=2) == 1                                     # the grouped family is not a conv path
+    assert call(kernel=3) == 3                                     # MFMA path: C/group 2 is below its minimum
+    assert call(cl=3) == 1
+    assert call(ws=(6, 3, 3, 3), ys=(1, 6, 4, 4)) == 1 and "C / group" in T.convtranspose_last_error()
+    assert call(ys=(1, 6, 4, 4), pads=[1, 1, 1, 1], auto_pad="VALID") == 1
+    assert call(ys=(1, 6, 4, 4), strides=[0, 1]) == 1
+    assert call(xs=(0, 4, 6, 6)) == 0                              # empty output: nothing launched
+    assert T.convtranspose_last_error() == ""
+
+
 def test_dispatcher_choices(T):
     lib = T.load_library()
 

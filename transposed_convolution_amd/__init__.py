@@ -23,7 +23,7 @@ __all__ = [
     "ConvTransposeError", "ConvTransposePlan", "convtranspose_nd", "convtranspose_profile_events", "convtranspose_output_shape",
     "convtranspose_useful_macs", "convtranspose_select_kernel", "convtranspose_last_error",
     "convtranspose_kernel_name", "library_path", "load_library", "channels_last_empty",
-    "to_channels_last", "KERNELS", "ACTIVATIONS",
+    "to_channels_last", "KERNELS", "ACTIVATIONS", "convolution_nd", "convolution_output_shape",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -81,6 +81,12 @@ def load_library():
     lib.convtranspose_last_error.argtypes = []
     lib.convtranspose_kernel_name.restype = ctypes.c_char_p
     lib.convtranspose_kernel_name.argtypes = [ctypes.c_int]
+    cattrs = [ctypes.c_int, i64p, i64p, i64p, i64p, ctypes.c_int64]  # forward convolution attributes
+    lib.convolution_output_shape.argtypes = [ctypes.c_int, i64p, i64p] + cattrs + [i64p, i64p]
+    lib.convolution_output_shape.restype = ctypes.c_int
+    lib.convolution_nd.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, vp, i64p, vp, i64p, vp,
+                                   vp, i64p] + cattrs + [vp]
+    lib.convolution_nd.restype = ctypes.c_int
     lib.convtranspose_profile_events.argtypes = [vp, vp]
     lib.convtranspose_profile_events.restype = ctypes.c_int
     _lib = lib
@@ -340,3 +346,76 @@ def convtranspose_profile_events(before: Optional[torch.cuda.Event], after: Opti
     st = lib.convtranspose_profile_events(*handles)
     if st:
         _raise(st)
+
+
+# ------------------------------------------------------------------------------------
+# The forward convolution with the same W (the adjoint of the transposed convolution)
+# ------------------------------------------------------------------------------------
+def _conv_attr_args(nsp, auto_pad="NOTSET", strides=None, dilations=None, pads=None, kernel_shape=None, group=1):
+    lens = dict(strides=nsp, dilations=nsp, pads=2 * nsp, kernel_shape=nsp)
+    vals = dict(strides=strides, dilations=dilations, pads=pads, kernel_shape=kernel_shape)
+    for k, v in vals.items():
+        if v is not None and len(v) != lens[k]:
+            raise ConvTransposeError(1, f"{k} must have {lens[k]} entries")
+    if auto_pad not in AUTO_PAD:
+        raise ConvTransposeError(1, f"unknown auto_pad {auto_pad!r}")
+    return [AUTO_PAD[auto_pad], _i64(strides), _i64(dilations), _i64(pads), _i64(kernel_shape), int(group)]
+
+
+def convolution_output_shape(x_shape, w_shape, **attrs) -> Tuple[Tuple[int, ...], Tuple[int, ...]]:
+    """Forward convolution: resolved Y shape (N, M, O1..On) and applied pads."""
+    lib = load_library()
+    nsp = len(x_shape) - 2
+    if len(w_shape) != len(x_shape):
+        raise ConvTransposeError(1, "W must have the same rank as X")
+    ys = (ctypes.c_int64 * (nsp + 2))()
+    pd = (ctypes.c_int64 * max(1, 2 * nsp))()
+    st = lib.convolution_output_shape(nsp, _i64(x_shape), _i64(w_shape), *_conv_attr_args(nsp, **attrs), ys, pd)
+    if st:
+        _raise(st)
+    return tuple(ys), tuple(pd[: 2 * nsp])
+
+
+def convolution_nd(x: torch.Tensor, w: torch.Tensor, bias: Optional[torch.Tensor] = None, *,
+                   auto_pad: str = "NOTSET", strides=None, dilations=None, pads=None, kernel_shape=None,
+                   group: int = 1, channels_last: bool = False, out: Optional[torch.Tensor] = None,
+                   kernel: str = "auto", stream: Optional[torch.cuda.Stream] = None) -> torch.Tensor:
+    """Y = Conv(X, W, bias) on the GPU (ONNX Conv; W is (M, C/group, k1..kn)), the adjoint of
+    ``convtranspose_nd`` with the same W.  ``kernel``: "auto", "direct" or "igemm" (the
+    stride-1 MFMA path)."""
+    lib = load_library()
+    if x.dtype not in _DTYPES:
+        raise ConvTransposeError(3, f"dtype {x.dtype} is not served (float32, float16)")
+    if x.dim() < 3 or x.dim() > 5 or w.dim() != x.dim():
+        raise ConvTransposeError(1, "x and w must have the same rank, 3 to 5")
+    dev = x.device
+    _check_tensor("x", x, dev, x.dtype)
+    _check_tensor("w", w, dev, x.dtype)
+    if bias is not None:
+        _check_tensor("bias", bias, dev, x.dtype)
+        if bias.dim() != 1 or not bias.is_contiguous() or bias.shape[0] != w.shape[0]:
+            raise ConvTransposeError(1, "bias must be a dense 1-D tensor of length M = W.shape[0]")
+    if not _dense(x, channels_last) or not w.is_contiguous():
+        raise ConvTransposeError(1, "x (in the requested layout) and w must be dense")
+    if kernel not in ("auto", "direct", "igemm"):
+        raise ConvTransposeError(1, f"unknown kernel {kernel!r}")
+    attrs = dict(auto_pad=auto_pad, strides=strides, dilations=dilations, pads=pads, kernel_shape=kernel_shape,
+                 group=group)
+    yshape, _ = convolution_output_shape(tuple(x.shape), tuple(w.shape), **attrs)
+    if out is None:
+        out = (channels_last_empty(yshape, x.dtype, dev) if channels_last
+               else torch.empty(yshape, dtype=x.dtype, device=dev))
+    else:
+        _check_tensor("out", out, dev, x.dtype)
+        if tuple(out.shape) != tuple(yshape) or not _dense(out, channels_last):
+            raise ConvTransposeError(2, f"out must be dense with shape {yshape}")
+    stream = stream if stream is not None else torch.cuda.current_stream(dev)
+    nsp = x.dim() - 2
+    ptr = lambda t: ctypes.c_void_p(t.data_ptr()) if t is not None else None  # noqa: E731
+    with torch.cuda.device(dev):
+        st = lib.convolution_nd(KERNELS[kernel], _DTYPES[x.dtype], nsp, int(channels_last), ptr(x), _i64(x.shape),
+                                ptr(w), _i64(w.shape), ptr(bias), ptr(out), _i64(yshape),
+                                *_conv_attr_args(nsp, **attrs), ctypes.c_void_p(stream.cuda_stream))
+    if st:
+        _raise(st)
+    return out

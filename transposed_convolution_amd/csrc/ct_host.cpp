@@ -175,6 +175,12 @@ namespace {
 
 thread_local std::string t_error;
 
+}  // namespace
+
+void ct::set_last_error(const std::string &msg) { t_error = msg; }
+
+namespace {
+
 ct_status fail(ct_status st, const std::string &msg)
 {
     t_error = msg;

@@ -835,7 +835,10 @@ bool make_plan(const Geom &g, bool cl, Plan *pl, std::string *why)
                 int e2 = n2 ? (n2 - 1) * a.bstep[2] : 0;
                 if (pair && n2)  // union of both phases' columns
                     e2 = std::max<int>(a.tb0[2][0], a.tb0[2][1]) - std::min<int>(a.tb0[2][0], a.tb0[2][1]) + e2;
-                const int HR = seg ? 1 + e1 : std::min<int>(J1, (BN + J2 - 1) / J2 + 1) + e1;
+                // rows a tile spans: tiles start at multiples of BN, so inside a row at
+                // offsets that are multiples of gcd(BN, J2); the worst start is J2 - gcd
+                const int rmax = J2 - std::__gcd(BN, J2);
+                const int HR = seg ? 1 + e1 : std::min<int>(J1, (rmax + BN + J2 - 1) / J2) + e1;
                 const int HC = seg ? BN + e2 : J2 + e2;
                 if ((long long)HR * HC * cfg.row() > cfg.halo_bytes()) return no("input halo exceeds LDS");
                 if (cl && (long long)HR * HC * cfg.chunks() > (long long)cfg.nhwc_vecs * kThreads)

@@ -60,6 +60,9 @@ struct AxisPhase {
 // Fills phase r of axis a; returns false when the phase has more than kMaxPhaseTaps taps.
 bool axis_phase(const Geom &g, int a, int r, AxisPhase *ph);
 
+// The per-thread error text convtranspose_last_error() returns.
+void set_last_error(const std::string &msg);
+
 // Events the caller asked to have recorded around the dominant kernel of each call on
 // this host thread (both null: none).
 struct ProfileEvents {
