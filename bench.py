@@ -52,7 +52,9 @@ def workloads():
     import workloads as W
     return {"c1": W.C1, "c2": W.C2, "c3": W.C3, "c4": W.C4, "c4_nhwc": W.C4_NHWC,
             "c5_s1": W.C5_S1, "c5_s1_p1": W.C5_S1_P1, "c5_s2": W.C5_S2,
-            "f2_k2s2": W.F2_K2S2, "f2_1x1": W.F2_1X1}
+            "f2_k2s2": W.F2_K2S2, "f2_1x1": W.F2_1X1,
+            # the forward convolution with the same W (the adjoint) of a configuration
+            "adj_c5_s1": W.C5_S1, "adj_c4": W.C4}
 
 
 def source_digest(kernel: str) -> str:
@@ -166,6 +168,79 @@ def summarize_pmc(args):
     print(json.dumps(out))
 
 
+def bench_adjoint(args):
+    """The forward convolution with a configuration's W, strides, dilations, begin pads and
+    end pads e - output_padding: it maps a Y-shaped tensor back to X's shape (the adjoint).
+    Useful MACs are the configuration's (the same (input, tap) pairs)."""
+    import numpy as np
+    import torch
+
+    import transposed_convolution_amd as T
+    import workloads as W
+    from oracle import oracle as O
+
+    base = workloads()[args.workload]
+    if int(base.attrs.get("group", 1)) != 1:
+        raise SystemExit("the adjoint bench samples one output channel at a time: group 1 only")
+    dev = torch.device("cuda:0")
+    _, w, _ = W.make_inputs(base)
+    ys, pads = T.convtranspose_output_shape(base.x_shape, base.w_shape, **base.attrs)
+    nsp = len(base.x_shape) - 2
+    op = base.attrs.get("output_padding") or [0] * nsp
+    attrs = dict(strides=base.attrs.get("strides"), dilations=base.attrs.get("dilations"),
+                 group=base.attrs.get("group", 1),
+                 pads=list(pads[:nsp]) + [pads[nsp + a] - op[a] for a in range(nsp)])
+    rng = np.random.default_rng(base.seed + 200)
+    a = rng.normal(size=ys).astype(np.float16)
+    b = rng.normal(size=base.w_shape[0]).astype(np.float16)
+    ta, tw, tb = (torch.from_numpy(v).to(dev) for v in (a, w, b))
+    macs = T.convtranspose_useful_macs(base.x_shape, base.w_shape, **base.attrs)
+    flops = 2.0 * macs
+    out = T.convolution_nd(ta, tw, tb, **attrs)
+    torch.cuda.synchronize()
+    assert tuple(out.shape) == tuple(base.x_shape)
+    lib = T.load_library()
+    # kernel the dispatcher ran: the MFMA path needs stride 1 (see convolution_nd)
+    kernel = "igemm" if all(s == 1 for s in (attrs["strides"] or [1] * nsp)) else "direct"
+    got = out.double().cpu().numpy()
+    pts = W.make_points(got.shape, 16, seed=base.seed + 12)
+    err = 0.0
+    for p in pts:
+        n, m = int(p[0]), int(p[1])
+        ref = O.conv(a[n:n + 1], w[m:m + 1], b[m:m + 1], **attrs)[(0, 0) + tuple(p[2:])]
+        err = max(err, abs(got[tuple(p)] - ref) / (1 + abs(ref)))
+    if not err <= 2e-3:
+        raise SystemExit(f"adjoint output disagrees with the oracle: max rel err {err:.3e}")
+    log(f"adjoint of {base.name}: y{ys} -> x{base.x_shape}, {attrs}, {macs / 1e9:.2f} GMAC, parity {err:.2e}")
+    for _ in range(args.warmup):
+        T.convolution_nd(ta, tw, tb, out=out, **attrs)
+    torch.cuda.synchronize()
+    evs = KernelEvents(args.steps)
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        evs.arm(lib, i)
+        T.convolution_nd(ta, tw, tb, out=out, **attrs)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    lib.convtranspose_profile_events(None, None)
+    k_avg = float(np.mean(evs.milliseconds()))
+    peak = PEAK_TFLOPS["f16"] if kernel == "igemm" else 157.3  # gather kernel: float32 vector ALU
+    achieved = flops / (k_avg * 1e-3) / 1e12
+    log(f"{args.steps} steps: {wall * 1e6 / args.steps:.1f} us/step wall, {kernel} kernel {k_avg * 1e3:.1f} us avg, "
+        f"{achieved:.1f} TFLOP/s = {achieved / peak * 100:.1f}% of {peak}")
+    print(json.dumps({
+        "metric": METRIC, "value": round(flops * args.steps / wall / 1e12, 3), "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(wall * 1e3 / args.steps, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f16", "data": "synthetic",
+        "config": {"workload": f"adjoint (forward convolution) of {base.name}: X{list(ys)} W{list(base.w_shape)} "
+                               f"{attrs} -> Y{list(base.x_shape)}", "kernel": kernel, "useful_macs": macs,
+                   "parity_max_rel_err": err},
+        "roofline": {"bound": "mfma" if kernel == "igemm" else "alu", "achieved": round(achieved, 2), "peak": peak,
+                     "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": None,
+                     "kernel_us": round(k_avg * 1e3, 2)},
+        "cpu_baseline": None}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -197,6 +272,8 @@ def main():
     import transposed_convolution_amd as T
     import workloads as W
 
+    if args.workload.startswith("adj_"):
+        return bench_adjoint(args)
     wl = workloads()[args.workload]
     dev = torch.device("cuda:0")
     x, w, b = W.make_inputs(wl)
