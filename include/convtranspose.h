@@ -265,6 +265,24 @@ ct_status convolution_nd(ct_kernel kernel, ct_dtype dtype, int nsp, int channels
                          const int64_t *strides, const int64_t *dilations, const int64_t *pads,
                          const int64_t *kernel_shape, int64_t group, void *stream);
 
+/*
+ * Tile configuration of the float16 implicit-GEMM (MFMA) kernel, a control for tests and
+ * tuning (the pages leave the kernel's blocking to the implementation).  tile = -1
+ * restores the automatic choice, the default: the largest tile that pads the output
+ * channels little and still gives every compute unit a block.  tile = 0..4 forces one
+ * block shape (output channels x output pixels): 0 = 256 x 256, 1 = 128 x 256,
+ * 2 = 64 x 512, 3 = 64 x 256, 4 = 64 x 128 (the last two run two blocks per compute unit).
+ * A forced tile that cannot serve a call (its input halo does not fit) makes an
+ * implicit-GEMM call fail with CT_EUNSUPPORTED and CT_KERNEL_AUTO choose another kernel
+ * family.  The setting is process-wide and is read when a call is made; changing it
+ * while another host thread makes calls gives that thread either setting.
+ * Returns CT_OK, or CT_EINVAL for a tile outside -1..4.
+ */
+ct_status convtranspose_set_igemm_tile(int tile);
+
+/* The current setting of convtranspose_set_igemm_tile (-1: automatic). */
+int convtranspose_igemm_tile(void);
+
 /* Text of the last error on the calling host thread ("" after a successful call).
  * The pointer stays valid until the next library call on that thread. */
 const char *convtranspose_last_error(void);

@@ -5,6 +5,7 @@ Tolerances: |y - ref| <= tol * (1 + |ref|) elementwise with tol = 1e-5 for float
 exactly the oracle's value rounded once to the element type.  Full-size benchmark
 shapes are checked on seeded sampled outputs (plus every corner); reduced shapes with
 the same attributes, ragged sizes and several tiles are checked on every output."""
+import contextlib
 import zlib
 
 import numpy as np
@@ -67,6 +68,16 @@ def check(got, ref, dtype, integer, what=""):
 
 def _log(msg):
     print(msg, flush=True)
+
+
+@contextlib.contextmanager
+def forced_tile(T, tile):
+    """Run the float16 MFMA kernel with one block shape (None: the automatic choice)."""
+    T.set_igemm_tile(tile)
+    try:
+        yield
+    finally:
+        T.set_igemm_tile(None)
 
 
 # --------------------------------------------------------------------------------------
@@ -159,9 +170,10 @@ def test_random_small_problems(T, kernel, dtype, cl):
 
 @pytest.mark.parametrize("cl", [False, True], ids=["nc", "cl"])
 def test_random_igemm_shaped_problems(T, cl):
-    """Shapes the implicit-GEMM path accepts (channels per group a multiple of 8; innermost
-    input size a multiple of 8 for NC.. layout), random strides/dilations/pads/groups,
-    ragged channel and pixel tails; forced igemm and the dispatcher's choice."""
+    """Shapes the implicit-GEMM path accepts (channels per group a multiple of 8; an even
+    innermost input size for NC.. layout, a multiple of 8 or not), random
+    strides/dilations/pads/groups, ragged channel and pixel tails; forced igemm with the
+    automatic block shape and with one forced shape per case, and the dispatcher's choice."""
     rng = np.random.default_rng(77 + cl)
     ran = 0
     for t in range(40):
@@ -169,7 +181,7 @@ def test_random_igemm_shaped_problems(T, cl):
         G = int(rng.choice([1, 1, 1, 2]))
         Cg = int(rng.choice([8, 16, 24, 40, 64]))
         Mg = int(rng.integers(1, 80))
-        L = [int(rng.integers(1, 7)) for _ in range(nsp - 1)] + [8 * int(rng.integers(1, 5))]
+        L = [int(rng.integers(1, 7)) for _ in range(nsp - 1)] + [int(rng.choice([8, 16, 24, 32, 6, 10, 18, 34]))]
         K = [int(rng.integers(1, 5)) for _ in range(nsp)]
         s = [int(rng.integers(1, 4)) for _ in range(nsp)]
         d = [int(rng.integers(1, 3)) for _ in range(nsp)]
@@ -185,14 +197,16 @@ def test_random_igemm_shaped_problems(T, cl):
         x = gen((2, G * Cg, *L)).astype(np.float16)
         w = (gen((G * Cg, Mg, *K)) * (1 if integer else 0.2)).astype(np.float16)
         b = gen(G * Mg).astype(np.float16)
-        _log(f"[case] igemm-random #{t} cl={cl} x{x.shape} w{w.shape} {attrs}")
+        tile = T.IGEMM_TILES[t % len(T.IGEMM_TILES)]
+        _log(f"[case] igemm-random #{t} cl={cl} x{x.shape} w{w.shape} {attrs} (and tile {tile})")
         ref = O.convtranspose(x, w, b, **attrs)
-        for kernel in ("igemm", "auto"):
-            got = gpu_run(T, x, w, b, attrs, cl, kernel)
+        for kernel, forced in (("igemm", None), ("auto", None), ("igemm", tile)):
+            with forced_tile(T, forced):
+                got = gpu_run(T, x, w, b, attrs, cl, kernel)
             if got is None:
                 continue
-            ran += kernel == "igemm"
-            check(got, ref, "f16", integer, f"igemm-random #{t} {kernel} {attrs}")
+            ran += kernel == "igemm" and forced is None
+            check(got, ref, "f16", integer, f"igemm-random #{t} {kernel} tile {forced} {attrs}")
     assert ran >= 25
 
 
@@ -353,10 +367,50 @@ def test_column_phase_pairs(T, case, integer):
     w = (gen(ws) * (1 if integer else 0.1)).astype(np.float16)
     b = gen(ws[1] * attrs.get("group", 1)).astype(np.float16)
     ref = O.convtranspose(x, w, b, **attrs)
-    for kernel in ("igemm", "auto"):
-        got = gpu_run(T, x, w, b, attrs, False, kernel)
+    # the two block shapes with two wave rows pair column phases; the automatic choice
+    # takes a smaller tile for problems this small
+    for kernel, tile in (("igemm", "256x256"), ("igemm", "128x256"), ("igemm", None), ("auto", None)):
+        with forced_tile(T, tile):
+            got = gpu_run(T, x, w, b, attrs, False, kernel)
         assert got is not None, "the implicit-GEMM kernel serves these shapes"
-        check(got, ref, "f16", integer, f"pair {kernel} x{xs} w{ws} {attrs}")
+        check(got, ref, "f16", integer, f"pair {kernel} tile {tile} x{xs} w{ws} {attrs}")
+
+
+TILE_CASES = [
+    # (x_shape, w_shape, attrs): several pixel tiles with ragged ends for every block shape,
+    # several channel tiles, 1-D / 2-D / 3-D, strides 1-3
+    ((2, 64, 20, 36), (64, 48, 4, 4), dict(strides=[2, 2], pads=[1, 1, 1, 1])),
+    ((3, 40, 11, 24), (40, 72, 4, 4), dict(strides=[2, 2], pads=[1, 1, 1, 1])),
+    ((2, 72, 13, 40), (72, 300, 3, 3), dict(strides=[1, 1], pads=[1, 1, 1, 1])),
+    ((1, 32, 5, 9, 16), (32, 24, 3, 3, 3), dict(strides=[1, 1, 1])),
+    ((1, 32, 5, 7, 16), (32, 40, 3, 3, 3), dict(strides=[2, 2, 2], pads=[1] * 6, output_padding=[1] * 3)),
+    ((2, 48, 600), (48, 130, 5), dict(strides=[3], pads=[2, 1], dilations=[2])),
+    ((2, 32, 6, 16), (32, 64, 1, 1), dict(strides=[1, 1])),
+    ((1, 16, 4, 5, 18), (16, 40, 3, 3, 3), dict(strides=[1, 1, 1], pads=[2] * 6)),  # rows of 18: 4-byte loads
+    ((2, 24, 7, 34), (24, 96, 4, 4), dict(strides=[2, 2], pads=[1] * 4)),             # rows of 34, unpaired
+]
+
+
+@pytest.mark.parametrize("integer", [False, True], ids=["float", "int"])
+@pytest.mark.parametrize("cl", [False, True], ids=["nc", "cl"])
+@pytest.mark.parametrize("tile", ["256x256", "128x256", "64x512", "64x256", "64x128"])
+def test_forced_tiles(T, tile, cl, integer):
+    """Every block shape of the float16 MFMA kernel on whole outputs."""
+    ran = 0
+    for xs, ws, attrs in TILE_CASES:
+        _log(f"[case] tile {tile} cl={cl} x{xs} w{ws} {attrs} integer={integer}")
+        rng = np.random.default_rng(zlib.crc32(repr((xs, ws, attrs)).encode()) + integer)
+        gen = (lambda sz: rng.integers(-2, 3, size=sz)) if integer else (lambda sz: rng.normal(size=sz))
+        x = gen(xs).astype(np.float16)
+        w = (gen(ws) * (1 if integer else 0.1)).astype(np.float16)
+        b = gen(ws[1] * attrs.get("group", 1)).astype(np.float16)
+        with forced_tile(T, tile):
+            got = gpu_run(T, x, w, b, attrs, cl, "igemm")
+        if got is None:
+            continue
+        ran += 1
+        check(got, O.convtranspose(x, w, b, **attrs), "f16", integer, f"tile {tile} x{xs} w{ws} {attrs}")
+    assert ran >= len(TILE_CASES) - 2, f"tile {tile} served only {ran} of {len(TILE_CASES)} shapes"
 
 
 SINGLE_TAP = [

@@ -222,6 +222,50 @@ def test_dispatcher_choices(T):
     assert pick(W.C4, cl=1) in ("igemm", "direct")
 
 
+def test_igemm_tile_control(T):
+    """The block-shape override of the float16 MFMA kernel: validated, read back, and
+    honoured by the dispatcher (host-side planning only; nothing is launched)."""
+    lib = T.load_library()
+
+    def pick(wl, cl=0):
+        at = T._attr_args(wl.nsp, **wl.attrs)
+        k = lib.convtranspose_select_kernel(1, wl.nsp, cl, ctypes.c_void_p(256), T._i64(wl.x_shape),
+                                            ctypes.c_void_p(256), T._i64(wl.w_shape), ctypes.c_void_p(256),
+                                            ctypes.c_void_p(256), *at)
+        return T.convtranspose_kernel_name(k)
+
+    assert lib.convtranspose_igemm_tile() == -1
+    for bad in (-2, len(T.IGEMM_TILES)):
+        assert lib.convtranspose_set_igemm_tile(bad) == 1 and "tile" in T.convtranspose_last_error()
+        assert lib.convtranspose_igemm_tile() == -1
+    try:
+        for t, name in enumerate(T.IGEMM_TILES):
+            T.set_igemm_tile(name)
+            assert lib.convtranspose_igemm_tile() == t and T.igemm_tile() == name
+        # C5 stride 1 (J = 34 x 34 output planes): the 256 x 256 tile's input halo does not
+        # fit one block's loads, the automatic choice and the 64 x 128 tile serve it
+        T.set_igemm_tile("256x256")
+        assert pick(W.C5_S1) != "igemm"
+        T.set_igemm_tile("64x128")
+        assert pick(W.C5_S1) == "igemm"
+    finally:
+        T.set_igemm_tile(None)
+    assert pick(W.C5_S1) == "igemm" and T.igemm_tile() is None
+
+
+def test_igemm_channels_first_row_widths(T):
+    """Channels-first input rows of any even width go to the MFMA kernel (16-byte loads
+    when the width is a multiple of 8, 4-byte loads otherwise); odd widths do not."""
+    lib = T.load_library()
+    for width, ok in ((32, True), (34, True), (18, True), (6, True), (33, False), (7, False)):
+        wl = W.C5_S1.with_(x_shape=(2, 64, 18, 34, width), w_shape=(64, 128, 3, 3, 3))
+        at = T._attr_args(wl.nsp, **wl.attrs)
+        k = lib.convtranspose_select_kernel(1, wl.nsp, 0, ctypes.c_void_p(256), T._i64(wl.x_shape),
+                                            ctypes.c_void_p(256), T._i64(wl.w_shape), ctypes.c_void_p(256),
+                                            ctypes.c_void_p(256), *at)
+        assert (T.convtranspose_kernel_name(k) == "igemm") == ok, (width, T.convtranspose_kernel_name(k))
+
+
 def test_random_cases_resolve_identically(T):
     rng = np.random.default_rng(5)
     for t in range(300):

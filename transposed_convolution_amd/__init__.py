@@ -24,6 +24,7 @@ __all__ = [
     "convtranspose_useful_macs", "convtranspose_select_kernel", "convtranspose_last_error",
     "convtranspose_kernel_name", "library_path", "load_library", "channels_last_empty",
     "to_channels_last", "KERNELS", "ACTIVATIONS", "convolution_nd", "convolution_output_shape",
+    "IGEMM_TILES", "set_igemm_tile", "igemm_tile",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -89,6 +90,10 @@ def load_library():
     lib.convolution_nd.restype = ctypes.c_int
     lib.convtranspose_profile_events.argtypes = [vp, vp]
     lib.convtranspose_profile_events.restype = ctypes.c_int
+    lib.convtranspose_set_igemm_tile.argtypes = [ctypes.c_int]
+    lib.convtranspose_set_igemm_tile.restype = ctypes.c_int
+    lib.convtranspose_igemm_tile.argtypes = []
+    lib.convtranspose_igemm_tile.restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -329,6 +334,24 @@ def convtranspose_nd(x: torch.Tensor, w: torch.Tensor, bias: Optional[torch.Tens
                              kernel_shape=kernel_shape, group=group, channels_last=channels_last,
                              out=out, kernel=kernel, stream=stream, activation=activation,
                              act_params=act_params)()
+
+
+IGEMM_TILES = ("256x256", "128x256", "64x512", "64x256", "64x128")
+
+
+def set_igemm_tile(tile: Optional[str]) -> None:
+    """Force one block shape of the float16 MFMA kernel (a name from IGEMM_TILES, output
+    channels x output pixels), or None for the automatic choice.  Process-wide."""
+    lib = load_library()
+    st = lib.convtranspose_set_igemm_tile(-1 if tile is None else IGEMM_TILES.index(tile))
+    if st:
+        _raise(st)
+
+
+def igemm_tile() -> Optional[str]:
+    """The forced block shape of the float16 MFMA kernel, or None (automatic)."""
+    t = load_library().convtranspose_igemm_tile()
+    return None if t < 0 else IGEMM_TILES[t]
 
 
 def convtranspose_profile_events(before: Optional[torch.cuda.Event], after: Optional[torch.cuda.Event]):

@@ -445,6 +445,17 @@ ct_status convtranspose_profile_events(void *before, void *after)
     return CT_OK;
 }
 
+ct_status convtranspose_set_igemm_tile(int tile)
+{
+    t_error.clear();
+    if (tile < -1 || tile >= ct::igemm_tile_count())
+        return fail(CT_EINVAL, "tile must be -1 (automatic) or 0.." + std::to_string(ct::igemm_tile_count() - 1));
+    ct::igemm_force_tile(tile);
+    return CT_OK;
+}
+
+int convtranspose_igemm_tile(void) { return ct::igemm_forced_tile(); }
+
 const char *convtranspose_last_error(void) { return t_error.c_str(); }
 
 const char *convtranspose_kernel_name(int kernel)

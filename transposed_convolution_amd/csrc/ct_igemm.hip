@@ -34,6 +34,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <atomic>
 #include <type_traits>
 #include <cstring>
 
@@ -99,6 +100,9 @@ struct Tile {
 // compute the two column phases r2 = 0, 1 of the same BM/2 output channels instead of two
 // channel halves of one phase, so the block owns whole output rows and stores them with
 // 16-byte vectors.
+// ROWS8 (channels-first): input rows are whole 16-byte vectors (innermost size a multiple
+// of 8), so a halo vector is one 16-byte load; otherwise (an even innermost size) it is
+// four 4-byte loads and the columns past the row end are zeroed when the halo is stored.
 template <bool CL, int WAVES_M, int WM, int WN, int CC, int NCH_ITEMS, int NHWC_VECS, int OCC>
 struct IgCfg {
     static constexpr int WAVES_N = 4 / WAVES_M;
@@ -114,7 +118,7 @@ struct IgCfg {
     static_assert(HALO_BYTES > 0, "LDS budget");
 };
 
-template <bool CL, int WAVES_M, int WM, int WN, int CC, int NCH_ITEMS, int NHWC_VECS, int OCC, bool PAIR>
+template <bool CL, int WAVES_M, int WM, int WN, int CC, int NCH_ITEMS, int NHWC_VECS, int OCC, bool PAIR, bool ROWS8>
 __global__ __launch_bounds__(kThreads, OCC) void igemm_kernel(const _Float16 *x, const _Float16 *__restrict__ wp,
                                                             const _Float16 *__restrict__ bias,
                                                             _Float16 *__restrict__ y, IgArgs p)
@@ -124,6 +128,7 @@ __global__ __launch_bounds__(kThreads, OCC) void igemm_kernel(const _Float16 *x,
     constexpr int CHUNKS = Cfg::CHUNKS, KSUB = Cfg::KSUB, WVEC = Cfg::WVEC;
     (void)WAVES_N;
     static_assert(!PAIR || (!CL && WAVES_M == 2), "column-phase pairs: channels-first, two wave rows");
+    static_assert(ROWS8 || (!CL && !PAIR), "narrow-row loads: channels-first, unpaired");
     constexpr int BMM = PAIR ? BM / 2 : BM;  // output channels per block
 
     // One LDS array: two weight-tile buffers, the halo buffer, and a per-lane sink for
@@ -342,10 +347,25 @@ __global__ __launch_bounds__(kThreads, OCC) void igemm_kernel(const _Float16 *x,
                 const bool ok = u < halo_items && i1 >= 0 && i1 < L1 && i2 >= 0 && i2 < L2 && cbase + oct * 8 < p.Cg;
                 const _Float16 *src = ok ? xb + size_t(oct * 8) * plane_in + size_t(i1) * L2 + i2 : x;
                 const size_t step = ok ? plane_in : 0;
+                if constexpr (ROWS8) {
 #pragma unroll
-                for (int k = 0; k < 8; ++k)
-                    if (it * 8 + k >= KB && it * 8 + k < KE)
-                        reg[it * 8 + k] = *reinterpret_cast<const u32x4 *>(src + k * step);
+                    for (int k = 0; k < 8; ++k)
+                        if (it * 8 + k >= KB && it * 8 + k < KE)
+                            reg[it * 8 + k] = *reinterpret_cast<const u32x4 *>(src + k * step);
+                } else {
+                    // a column pair at or past the row end reads a valid address instead
+                    // (store_halo replaces its values by zeros)
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        const bool in = ok && i2 + 2 * q < L2;
+                        const _Float16 *sq = in ? src + 2 * q : x;
+                        const size_t sstep = in ? step : 0;
+#pragma unroll
+                        for (int k = 0; k < 8; ++k)
+                            if (it * 8 + k >= KB && it * 8 + k < KE)
+                                reg[it * 8 + k][q] = *reinterpret_cast<const unsigned *>(sq + k * sstep);
+                    }
+                }
                 valid |= unsigned(ok) << it;
             }
         }
@@ -386,7 +406,8 @@ __global__ __launch_bounds__(kThreads, OCC) void igemm_kernel(const _Float16 *x,
                     }
                     unsigned char *dst =
                         (here && hc >= 0 && hc < tl.HC) ? &lds_h[(hr * tl.HC + hc) * ROW + oct * 16] : sink;
-                    *reinterpret_cast<u32x4 *>(dst) = ok ? o : zero;
+                    const bool inside = ROWS8 || (va + vc) * 8 + pp < L2;  // past the row end: zero
+                    *reinterpret_cast<u32x4 *>(dst) = (ok && inside) ? o : zero;
                 }
             }
         }
@@ -671,27 +692,15 @@ __global__ __launch_bounds__(kThreads, OCC) void igemm_kernel(const _Float16 *x,
                     *reinterpret_cast<u32x4 *>(y + off) = *reinterpret_cast<const u32x4 *>(&stile[ml * TP + p8 * 8]);
                 }
             } else {
-                // Phase-strided rows: runs of 8 tile pixels of one channel.  When a run lies
-                // in one output row its 8 outputs sit s2 elements apart: one LDS vector read,
-                // one address, 8 stores.  Runs that cross a row or the tile end go element by
-                // element.
-                const int nruns = (npix + 7) / 8;
-                const int s2 = p.s[2];
-                for (int u = tid; u < mvalid * nruns; u += kThreads) {
-                    const int ml = u / nruns, pl0 = (u - ml * nruns) * 8;
-                    _Float16 *const yc = y + (size_t(n) * p.M + g * p.Mg + mt * BM + ml) * opix;
-                    const int q = tl.q0 + pl0;
-                    const int row = tl.seg ? tl.row_lo : q / J2;
-                    const int col = q - row * J2;
-                    if (pl0 + 8 <= npix && col + 8 <= J2) {
-                        const u32x4 v8 = *reinterpret_cast<const u32x4 *>(&stile[ml * TP + pl0]);
-                        _Float16 *const dst = yc + pixel_offset(pl0);
-    #pragma unroll
-                        for (int e = 0; e < 8; ++e)
-                            dst[e * s2] = __builtin_bit_cast(_Float16, (unsigned short)(v8[e >> 1] >> (16 * (e & 1))));
-                    } else {
-                        for (int pl = pl0; pl < min(pl0 + 8, npix); ++pl) yc[pixel_offset(pl)] = stile[ml * TP + pl];
-                    }
+                // Phase-strided or ragged rows: a wave stores 64 consecutive tile pixels of
+                // one channel (lane = pixel), so each store instruction touches the few
+                // output lines those pixels span; the pixel offsets are computed once per
+                // 64-pixel block and reused for every channel.
+                for (int pb = 0; pb < npix; pb += 64) {
+                    const int pl = pb + lane;
+                    if (pl >= npix) continue;
+                    _Float16 *const yq = y + (size_t(n) * p.M + g * p.Mg + mt * BM) * opix + pixel_offset(pl);
+                    for (int ml = wave; ml < mvalid; ml += 4) yq[size_t(ml) * opix] = stile[ml * TP + pl];
                 }
             }
         }
@@ -741,13 +750,25 @@ struct Config {
     int row() const { return cc * 2 + 16; }
     int chunks() const { return cc / 8; }
     int halo_bytes() const { return lds_budget(occ) - 2 * bm() * row() - kSinkBytes - kBiasBytes; }
+    bool operator==(const Config &o) const
+    {
+        return waves_m == o.waves_m && wm == o.wm && wn == o.wn && cc == o.cc && nch_items == o.nch_items &&
+               nhwc_vecs == o.nhwc_vecs && occ == o.occ;
+    }
 };
 
 // The two compiled configurations (their template arguments must match launch_igemm).
 constexpr Config kWide{2, 4, 4, 64, 2, 14, 1};    // 256 x 256 block, 128 x 128 per wave, 64 ch/step
 constexpr Config kNarrow{1, 2, 4, 32, 2, 12, 1};  // 64 x 512 block, 64 x 128 per wave, 32 ch/step
+constexpr Config kHalf{2, 2, 4, 64, 2, 14, 1};    // 128 x 256 block, 64 x 128 per wave, 64 ch/step
+constexpr Config kMid{1, 2, 2, 32, 2, 12, 2};     // 64 x 256 block, 64 x 64 per wave, 32 ch/step, two blocks per CU
+constexpr Config kSmall{1, 2, 1, 64, 2, 8, 2};    // 64 x 128 block, 64 x 32 per wave, two blocks per CU
 
-Config pick_config(const Geom &g) { return g.Mg > 64 ? kWide : kNarrow; }
+// Candidates from the largest tile to the smallest.  Larger tiles re-read less and keep
+// the MFMA pipes busier, but a launch with fewer blocks than the chip has block slots
+// leaves compute units idle for its whole duration, which costs more (measured on the
+// C4/C5 shapes and on C4 with one image).
+constexpr Config kConfigs[] = {kWide, kHalf, kNarrow, kMid, kSmall};
 
 struct Plan {
     Config cfg;
@@ -756,13 +777,12 @@ struct Plan {
     size_t ws_bytes;
 };
 
-bool make_plan(const Geom &g, bool cl, Plan *pl, std::string *why)
+bool make_plan_cfg(const Geom &g, bool cl, const Config &cfg, Plan *pl, std::string *why)
 {
     auto no = [&](const char *m) {
         *why = m;
         return false;
     };
-    const Config cfg = pick_config(g);
     const int BN = cfg.bn();
     std::memset(&pl->a, 0, sizeof(pl->a));
     IgArgs &a = pl->a;
@@ -798,8 +818,10 @@ bool make_plan(const Geom &g, bool cl, Plan *pl, std::string *why)
     a.nchunk = int((g.Cg + cfg.cc - 1) / cfg.cc);
     a.Cgp = a.nchunk * cfg.cc;
     // Column-phase pairs: channels-first output, stride 2 on the innermost axis, an even
-    // output width (both phases then have the same pixel grid) and equal tap counts.
-    const bool pair = !cl && cfg.waves_m == 2 && g.s[2] == 2 && g.O[2] % 2 == 0 && a.ntap[2][0] == a.ntap[2][1];
+    // output width (both phases then have the same pixel grid), equal tap counts and input
+    // rows of whole 16-byte vectors.
+    const bool pair = !cl && cfg.waves_m == 2 && g.s[2] == 2 && g.O[2] % 2 == 0 && a.ntap[2][0] == a.ntap[2][1] &&
+                      g.L[2] % 8 == 0;
     const int BMM = pair ? cfg.bm() / 2 : cfg.bm();
     a.mtiles = int((g.Mg + BMM - 1) / BMM);
     a.Mgp = a.mtiles * BMM;
@@ -869,12 +891,73 @@ bool make_plan(const Geom &g, bool cl, Plan *pl, std::string *why)
     return true;
 }
 
-template <bool CL, int WAVES_M, int WM, int WN, int CC, int NCH_ITEMS, int NHWC_VECS, int OCC, bool PAIR = false>
+// The largest tile that pads the output channels little (Mgp / Mg within 15 % of the
+// least padding any servable tile has) and still gives every block slot of the chip (256
+// compute units x blocks per unit) a block; if none does, the least-padded tile with the
+// most blocks.
+constexpr int kNumConfigs = int(sizeof(kConfigs) / sizeof(kConfigs[0]));
+std::atomic<int> g_forced_tile{-1};  // index into kConfigs, or -1: automatic
+
+bool make_plan(const Geom &g, bool cl, Plan *pl, std::string *why)
+{
+    const int forced = g_forced_tile.load(std::memory_order_relaxed);
+    if (forced >= 0) return make_plan_cfg(g, cl, kConfigs[forced], pl, why);
+    constexpr int kCUs = 256;
+    constexpr int kN = kNumConfigs;
+    Plan cand[kN];
+    bool ok[kN];
+    double waste[kN], best_waste = 1e30;
+    for (int i = 0; i < kN; ++i) {
+        std::string w;
+        ok[i] = make_plan_cfg(g, cl, kConfigs[i], &cand[i], &w);
+        if (!ok[i]) {
+            if (i == 0 || why->empty()) *why = w;
+            continue;
+        }
+        waste[i] = double(cand[i].a.Mgp) / double(g.Mg);
+        best_waste = std::min(best_waste, waste[i]);
+    }
+    int pick = -1;
+    for (int i = 0; i < kN; ++i) {
+        if (!ok[i] || waste[i] > 1.15 * best_waste) continue;
+        if (cand[i].a.nblocks >= kCUs * kConfigs[i].occ) {
+            pick = i;
+            break;
+        }
+        if (pick < 0 || cand[i].a.nblocks > cand[pick].a.nblocks) pick = i;
+    }
+    if (pick < 0) return false;
+    *pl = cand[pick];
+    return true;
+}
+
+template <bool CL, int WAVES_M, int WM, int WN, int CC, int NCH_ITEMS, int NHWC_VECS, int OCC, bool PAIR = false,
+          bool ROWS8 = true>
 void launch_cfg(const IgArgs &a, const _Float16 *x, const _Float16 *wp, const _Float16 *b, _Float16 *y,
                 hipStream_t st)
 {
-    hipLaunchKernelGGL((igemm_kernel<CL, WAVES_M, WM, WN, CC, NCH_ITEMS, NHWC_VECS, OCC, PAIR>), dim3(unsigned(a.nblocks)),
+    hipLaunchKernelGGL((igemm_kernel<CL, WAVES_M, WM, WN, CC, NCH_ITEMS, NHWC_VECS, OCC, PAIR, ROWS8>), dim3(unsigned(a.nblocks)),
                        dim3(kThreads), 0, st, x, wp, b, y, a);
+}
+
+// Launches the instance of one configuration for the plan's layout (and column-phase
+// pairing, which exists for the two-wave-row configurations only).
+template <int WAVES_M, int WM, int WN, int CC, int NCH_ITEMS, int NHWC_VECS, int OCC>
+bool launch_config(const Config &c, const Plan &pl, bool cl, const _Float16 *x, const _Float16 *wp,
+                   const _Float16 *b, _Float16 *y, hipStream_t st)
+{
+    if (!(c == Config{WAVES_M, WM, WN, CC, NCH_ITEMS, NHWC_VECS, OCC})) return false;
+    if (cl)
+        launch_cfg<true, WAVES_M, WM, WN, CC, NCH_ITEMS, NHWC_VECS, OCC>(pl.a, x, wp, b, y, st);
+    else if (pl.a.L[2] % 8 != 0)
+        launch_cfg<false, WAVES_M, WM, WN, CC, NCH_ITEMS, NHWC_VECS, OCC, false, false>(pl.a, x, wp, b, y, st);
+    else if (!pl.pair)
+        launch_cfg<false, WAVES_M, WM, WN, CC, NCH_ITEMS, NHWC_VECS, OCC>(pl.a, x, wp, b, y, st);
+    else if constexpr (WAVES_M == 2)
+        launch_cfg<false, WAVES_M, WM, WN, CC, NCH_ITEMS, NHWC_VECS, OCC, true>(pl.a, x, wp, b, y, st);
+    else
+        return false;
+    return true;
 }
 
 }  // namespace
@@ -890,8 +973,8 @@ bool igemm_supports(const Geom &g, ct_dtype dt, bool cl, const void *x, std::str
         *why = "C/group must be a multiple of 8";
         return false;
     }
-    if (cl ? (g.C % 8 != 0) : (g.L[2] % 8 != 0)) {
-        *why = cl ? "C must be a multiple of 8" : "innermost input size must be a multiple of 8";
+    if (cl ? (g.C % 8 != 0) : (g.L[2] % 2 != 0)) {
+        *why = cl ? "C must be a multiple of 8" : "innermost input size must be even";
         return false;
     }
     if (reinterpret_cast<uintptr_t>(x) % 16 != 0) {
@@ -907,12 +990,20 @@ size_t igemm_workspace_bytes(const Geom &g, ct_dtype dt)
     if (dt != CT_FLOAT16) return 0;  // the float32 kernel reads W in place
     Plan pl;
     std::string why;
-    // the larger of the two layouts' packed weights (column-phase pairs pad M less)
+    // the largest packed weights of any tile and layout (tiles pad M differently), so a
+    // workspace stays large enough whichever tile a later call uses
     size_t bytes = 0;
-    for (const bool cl : {false, true})
-        if (make_plan(g, cl, &pl, &why)) bytes = std::max(bytes, pl.ws_bytes);
+    for (const Config &c : kConfigs)
+        for (const bool cl : {false, true})
+            if (make_plan_cfg(g, cl, c, &pl, &why)) bytes = std::max(bytes, pl.ws_bytes);
     return bytes;
 }
+
+int igemm_tile_count() { return kNumConfigs; }
+
+void igemm_force_tile(int tile) { g_forced_tile.store(tile, std::memory_order_relaxed); }
+
+int igemm_forced_tile() { return g_forced_tile.load(std::memory_order_relaxed); }
 
 ct_status launch_igemm(const Geom &g, ct_dtype dt, bool cl, const void *x, const void *w, const void *bias,
                        void *y, const Act &act, void *workspace, size_t ws_bytes, hipStream_t st, std::string *err)
@@ -950,16 +1041,14 @@ ct_status launch_igemm(const Geom &g, ct_dtype dt, bool cl, const void *x, const
     _Float16 *yt = static_cast<_Float16 *>(y);
     const Config c = pl.cfg;
     mark_before(st);
-    if (c.waves_m == kWide.waves_m) {
-        if (cl) launch_cfg<true, 2, 4, 4, 64, 2, 14, 1>(pl.a, xt, wpk, bt, yt, st);
-        else if (pl.pair) launch_cfg<false, 2, 4, 4, 64, 2, 14, 1, true>(pl.a, xt, wpk, bt, yt, st);
-        else launch_cfg<false, 2, 4, 4, 64, 2, 14, 1>(pl.a, xt, wpk, bt, yt, st);
-    } else {
-        if (cl) launch_cfg<true, 1, 2, 4, 32, 2, 12, 1>(pl.a, xt, wpk, bt, yt, st);
-        else launch_cfg<false, 1, 2, 4, 32, 2, 12, 1>(pl.a, xt, wpk, bt, yt, st);
-    }
+    // (the template arguments repeat the Config constants above)
+    const bool launched = launch_config<2, 4, 4, 64, 2, 14, 1>(c, pl, cl, xt, wpk, bt, yt, st) ||
+                          launch_config<1, 2, 4, 32, 2, 12, 1>(c, pl, cl, xt, wpk, bt, yt, st) ||
+                          launch_config<2, 2, 4, 64, 2, 14, 1>(c, pl, cl, xt, wpk, bt, yt, st) ||
+                          launch_config<1, 2, 2, 32, 2, 12, 2>(c, pl, cl, xt, wpk, bt, yt, st) ||
+                          launch_config<1, 2, 1, 64, 2, 8, 2>(c, pl, cl, xt, wpk, bt, yt, st);
     mark_after(st);
-    hipError_t e = hipGetLastError();
+    hipError_t e = launched ? hipGetLastError() : hipErrorInvalidConfiguration;
     if (owned) {
         const hipError_t f = hipFreeAsync(wsp, st);
         if (e == hipSuccess) e = f;

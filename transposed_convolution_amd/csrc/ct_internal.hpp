@@ -130,6 +130,11 @@ ct_status launch_grouped(const Geom &g, ct_dtype dt, bool cl, const void *x, con
                          const void *bias, void *y, const Act &act, hipStream_t st, std::string *err);
 bool igemm_supports(const Geom &g, ct_dtype dt, bool cl, const void *x, std::string *why);
 size_t igemm_workspace_bytes(const Geom &g, ct_dtype dt);
+// Tile configurations of the float16 implicit-GEMM kernel: how many there are, and a
+// process-wide override (-1: automatic choice).
+int igemm_tile_count();
+void igemm_force_tile(int tile);
+int igemm_forced_tile();
 // float32 implicit GEMM on MFMA (the CT_KERNEL_IGEMM family for float32 inputs)
 bool igemm32_supports(const Geom &g, bool cl, std::string *why);
 ct_status launch_igemm32(const Geom &g, bool cl, const void *x, const void *w, const void *bias, void *y,
