@@ -38,6 +38,7 @@
  *
  * Build: gcc -O2 -fopenmp -shared -fPIC ct_oracle.c -o libctoracle.so
  */
+#include <math.h>
 #include <omp.h>
 #include <stdint.h>
 #include <stdio.h>
@@ -580,5 +581,141 @@ int oracle_conv_f64(int nsp, const int64_t *x_shape, const double *x, const int6
             yp[p] = acc;
         }
     }
+    return OR_OK;
+}
+
+/* ------------------------------------------------------------------------------------
+ * Quantized transposed convolution with the QLinear scale / zero-point scheme of the
+ * webgpu-kernels "ai.onnx.QLinearConv" README (Description and Inputs table): x and y
+ * are quantized per tensor (scale, zero point), w per tensor or per output channel
+ * (w_scale and w_zero_point of length 1 or M), and the optional int32 bias carries scale
+ * x_scale * w_scale and zero point 0.  The pages describe the scheme for the forward
+ * convolution; here it is carried over to the transposed convolution unchanged.
+ *
+ * Definition used: the integer sum of the scatter form (the same (c, i, k) pairs as
+ * oracle_convtranspose_f64) over zero-point-shifted operands,
+ *     acc[n, m, o] = B[m] + sum (x[n, c, i] - x_zp) * (w[c, m', k] - w_zp[m]),
+ * computed exactly (int64), then
+ *     y = saturate(round_half_even(float(acc32) * mult[m]) + y_zp),
+ *     mult[m] = float(float(x_scale * w_scale[m]) / y_scale),
+ * where acc32 is acc reduced modulo 2^32 to int32 (the accumulator type of the bias)
+ * and every floating-point step is one IEEE float32 operation.  Readings where the
+ * pages are silent: the float32 order of the requantization above, round half to even,
+ * saturation to [y_lo, y_hi] (0..255 for uint8, -128..127 for int8).
+ *
+ * x and w arrive widened to int32 (their uint8 / int8 values), NCHW order.  acc_out
+ * (nullable) receives the exact sums; y_out the quantized outputs (as int32 values).
+ * ---------------------------------------------------------------------------------- */
+static float or_requant_mult(float x_scale, float w_scale, float y_scale)
+{
+    volatile float xw = x_scale * w_scale; /* one float32 product, rounded */
+    volatile float mult = xw / y_scale;    /* one float32 quotient, rounded */
+    return mult;
+}
+
+static int32_t or_requantize(int64_t acc, float mult, int32_t y_zp, int32_t y_lo, int32_t y_hi)
+{
+    int32_t acc32 = (int32_t)(uint32_t)(uint64_t)acc; /* modulo 2^32 */
+    volatile float v = (float)acc32 * mult;
+    float r = rintf(v); /* default rounding mode: to nearest, ties to even */
+    double q = (double)r + (double)y_zp;
+    if (q < (double)y_lo)
+        return y_lo;
+    if (q > (double)y_hi)
+        return y_hi;
+    return (int32_t)q;
+}
+
+int oracle_qconvtranspose(int nsp, const int64_t *x_shape, const int32_t *x, int32_t x_zp, float x_scale,
+                          const int64_t *w_shape, const int32_t *w, const int32_t *w_zp, const float *w_scale,
+                          int64_t wq_len, const int32_t *bias, float y_scale, int32_t y_zp, int32_t y_lo,
+                          int32_t y_hi, int auto_pad, const int64_t *strides, const int64_t *dilations,
+                          const int64_t *pads, const int64_t *output_padding, const int64_t *output_shape,
+                          const int64_t *kernel_shape, int64_t group, int64_t *acc_out, int32_t *y_out,
+                          int64_t y_len, char *err, int errlen)
+{
+    or_geom g;
+    int rc;
+    int64_t in_plane, out_plane, taps, t, plane;
+    int64_t *tap_coord;
+    rc = or_resolve(nsp, x_shape, w_shape, auto_pad, strides, dilations, pads, output_padding,
+                    output_shape, kernel_shape, group, &g, err, errlen);
+    if (rc != OR_OK)
+        return rc;
+    if (wq_len != 1 && wq_len != g.M)
+        return or_fail(err, errlen, "w_scale / w_zero_point must have length 1 or M");
+    if (y_lo > y_hi)
+        return or_fail(err, errlen, "empty output range");
+    in_plane = or_prod(g.L, nsp);
+    out_plane = or_prod(g.O, nsp);
+    taps = or_prod(g.K, nsp);
+    if (y_len != g.N * g.M * out_plane)
+        return or_fail(err, errlen, "y buffer length does not match the resolved output");
+    if (g.N * g.M * out_plane == 0)
+        return OR_OK;
+
+    tap_coord = (int64_t *)malloc(sizeof(int64_t) * 3 * (size_t)(taps > 0 ? taps : 1));
+    if (!tap_coord)
+        return or_fail(err, errlen, "out of host memory");
+    for (t = 0; t < taps; t++)
+        or_decode(t, g.K, nsp, tap_coord + 3 * t);
+
+#pragma omp parallel for schedule(dynamic, 1)
+    for (plane = 0; plane < g.N * g.M; plane++) {
+        int64_t n = plane / g.M, m = plane % g.M;
+        int64_t grp = m / g.Mg, mm = m % g.Mg;
+        int64_t q = wq_len == 1 ? 0 : m;
+        int64_t *acc = (int64_t *)malloc(sizeof(int64_t) * (size_t)out_plane);
+        float mult = or_requant_mult(x_scale, w_scale[q], y_scale);
+        int64_t p, cc, ii, kk;
+        int a;
+        if (!acc)
+            continue; /* reported below: y keeps the caller's contents */
+        for (p = 0; p < out_plane; p++)
+            acc[p] = bias ? bias[m] : 0;
+        for (cc = 0; cc < g.Cg; cc++) {
+            int64_t c = grp * g.Cg + cc;
+            const int32_t *xp = x + (n * g.C + c) * in_plane;
+            const int32_t *wp = w + (c * g.Mg + mm) * taps;
+            for (ii = 0; ii < in_plane; ii++) {
+                int64_t icoord[3];
+                int64_t xv = (int64_t)xp[ii] - x_zp;
+                or_decode(ii, g.L, nsp, icoord);
+                for (kk = 0; kk < taps; kk++) {
+                    const int64_t *kc = tap_coord + 3 * kk;
+                    int64_t flat = 0;
+                    int inside = 1;
+                    for (a = 0; a < nsp; a++) {
+                        int64_t o = icoord[a] * g.s[a] - g.b[a] + kc[a] * g.d[a];
+                        if (o < 0 || o >= g.O[a]) {
+                            inside = 0;
+                            break;
+                        }
+                        flat = flat * g.O[a] + o;
+                    }
+                    if (inside)
+                        acc[flat] += xv * ((int64_t)wp[kk] - w_zp[q]);
+                }
+            }
+        }
+        for (p = 0; p < out_plane; p++) {
+            if (acc_out)
+                acc_out[plane * out_plane + p] = acc[p];
+            y_out[plane * out_plane + p] = or_requantize(acc[p], mult, y_zp, y_lo, y_hi);
+        }
+        free(acc);
+    }
+    free(tap_coord);
+    return OR_OK;
+}
+
+/* The requantization step alone on given accumulators (acc of length n, channel index
+ * ch[i] into mult inputs), for pinning it against values fixed by its definition. */
+int oracle_requantize(const int64_t *acc, int64_t n, float x_scale, const float *w_scale, const int64_t *ch,
+                      float y_scale, int32_t y_zp, int32_t y_lo, int32_t y_hi, int32_t *y_out)
+{
+    int64_t i;
+    for (i = 0; i < n; i++)
+        y_out[i] = or_requantize(acc[i], or_requant_mult(x_scale, w_scale[ch[i]], y_scale), y_zp, y_lo, y_hi);
     return OR_OK;
 }

@@ -32,7 +32,7 @@ class OracleError(ValueError):
 
 def build(src: str = _SRC, out: str = _LIB) -> str:
     """Compile the oracle with gcc (OpenMP, -O2, no fast-math)."""
-    cmd = ["gcc", "-O2", "-std=c99", "-fopenmp", "-shared", "-fPIC", src, "-o", out]
+    cmd = ["gcc", "-O2", "-std=c99", "-fopenmp", "-shared", "-fPIC", src, "-o", out, "-lm"]
     subprocess.run(cmd, check=True)
     return out
 
@@ -62,8 +62,16 @@ def load(path: Optional[str] = None):
         i64p, i64p, ctypes.c_char_p, ctypes.c_int]
     lib.oracle_conv_f64.argtypes = [ctypes.c_int, i64p, f64p, i64p, f64p, f64p] + cattrs + [
         f64p, ctypes.c_int64, ctypes.c_char_p, ctypes.c_int]
+    i32p = ctypes.POINTER(ctypes.c_int32)
+    f32p = ctypes.POINTER(ctypes.c_float)
+    c_i32, c_f32 = ctypes.c_int32, ctypes.c_float
+    lib.oracle_qconvtranspose.argtypes = [ctypes.c_int, i64p, i32p, c_i32, c_f32, i64p, i32p, i32p, f32p,
+                                          ctypes.c_int64, i32p, c_f32, c_i32, c_i32, c_i32] + attrs + [
+        i64p, i32p, ctypes.c_int64, ctypes.c_char_p, ctypes.c_int]
+    lib.oracle_requantize.argtypes = [i64p, ctypes.c_int64, c_f32, f32p, i64p, c_f32, c_i32, c_i32, c_i32, i32p]
     for fn in ("oracle_output_shape", "oracle_useful_macs", "oracle_convtranspose_f64",
-               "oracle_convtranspose_at", "oracle_threads", "oracle_conv_output_shape", "oracle_conv_f64"):
+               "oracle_convtranspose_at", "oracle_threads", "oracle_conv_output_shape", "oracle_conv_f64",
+               "oracle_qconvtranspose", "oracle_requantize"):
         getattr(lib, fn).restype = ctypes.c_int
     lib.oracle_threads.argtypes = []
     if path is None:
@@ -261,3 +269,67 @@ def conv(x: np.ndarray, w: np.ndarray, bias: Optional[np.ndarray] = None, lib=No
                              y.ctypes.data_as(ctypes.POINTER(ctypes.c_double)), y.size, err, 256)
     _check(rc, err)
     return y
+
+
+# --------------------------------------------------------------------------------------
+# quantized transposed convolution (QLinear scale / zero-point scheme)
+# --------------------------------------------------------------------------------------
+QRANGE = {"uint8": (0, 255), "int8": (-128, 127)}
+
+
+def _i32(a):
+    a = np.ascontiguousarray(np.asarray(a).astype(np.int32))
+    return a, a.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
+
+
+def _f32(a):
+    a = np.ascontiguousarray(np.asarray(a, dtype=np.float32).reshape(-1))
+    return a, a.ctypes.data_as(ctypes.POINTER(ctypes.c_float))
+
+
+def qconvtranspose(x: np.ndarray, w: np.ndarray, x_scale: float, x_zero_point: int, w_scale, w_zero_point,
+                   y_scale: float, y_zero_point: int, y_type: str = "uint8", bias: Optional[np.ndarray] = None,
+                   return_acc: bool = False, lib=None, **attrs):
+    """Quantized transposed convolution (NC.. layout): the exact integer scatter sum of
+    zero-point-shifted operands plus the int32 bias, requantized in float32 to y_type.
+    w_scale / w_zero_point: one value or one per output channel M.  Returns y (int32
+    array of y_type values), and the exact accumulators too with ``return_acc``."""
+    lib = lib or load()
+    x32, xp = _i32(x)
+    w32, wp = _i32(w)
+    ws32, wsp = _f32(w_scale)
+    wz32, wzp = _i32(np.asarray(w_zero_point).reshape(-1))
+    if ws32.size != wz32.size:
+        raise OracleError("w_scale and w_zero_point must have the same length")
+    b32, bp = _i32(bias) if bias is not None else (None, None)
+    yshape, _ = output_shape(x32.shape, w32.shape, lib=lib, **attrs)
+    if b32 is not None and b32.shape != (yshape[1],):
+        raise OracleError("bias must be 1-D of length M")
+    lo, hi = QRANGE[y_type]
+    y = np.zeros(yshape, dtype=np.int32)
+    acc = np.zeros(yshape, dtype=np.int64) if return_acc else None
+    args, keep = _attr_args(**attrs)
+    xs, xsp = _i64(x32.shape)
+    wsh, wshp = _i64(w32.shape)
+    err = ctypes.create_string_buffer(256)
+    rc = lib.oracle_qconvtranspose(x32.ndim - 2, xsp, xp, int(x_zero_point), float(x_scale), wshp, wp, wzp, wsp,
+                                   ws32.size, bp, float(y_scale), int(y_zero_point), lo, hi, *args,
+                                   acc.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)) if acc is not None else None,
+                                   y.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), y.size, err, 256)
+    _check(rc, err)
+    return (y, acc) if return_acc else y
+
+
+def requantize(acc, x_scale: float, w_scale, channel, y_scale: float, y_zero_point: int, y_type: str = "uint8",
+               lib=None) -> np.ndarray:
+    """The requantization step alone: acc (int64 values) of output channels ``channel``."""
+    lib = lib or load()
+    a = np.ascontiguousarray(np.asarray(acc, dtype=np.int64).reshape(-1))
+    ch = np.ascontiguousarray(np.broadcast_to(np.asarray(channel, dtype=np.int64), a.shape))
+    ws32, wsp = _f32(w_scale)
+    lo, hi = QRANGE[y_type]
+    y = np.zeros(a.shape, dtype=np.int32)
+    lib.oracle_requantize(a.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)), a.size, float(x_scale), wsp,
+                          ch.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)), float(y_scale), int(y_zero_point),
+                          lo, hi, y.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)))
+    return y.reshape(np.shape(acc))

@@ -11,7 +11,11 @@ import pins  # noqa: E402
 from oracle import oracle as O  # noqa: E402
 
 lib = O.load(sys.argv[1])
-order = sorted(pins.ALL_PINS, key=lambda p: p is pins.pin_brute_force_gather)
+# the pins of the mutated routine's family first (only the time to the first failure changes)
+family = {"q": "pin_q", "conv": "pin_conv"}.get((sys.argv[2] if len(sys.argv) > 2 else "").split("_")[0], "")
+order = sorted(pins.ALL_PINS, key=lambda p: (not (family and p.__name__.startswith(family)) and
+                                             not (family == "pin_q" and p.__name__ == "pin_requantize_definition"),
+                                             p is pins.pin_brute_force_gather))
 for pin in order:
     try:
         pin(lib)

@@ -643,8 +643,133 @@ def pin_conv_rejects_invalid(lib):
     O.conv(x, w, None, lib=lib, group=2)  # the valid base case
 
 
+# ----------------------------------------------------------------------------------
+# quantized transposed convolution (QLinear scheme of the "ai.onnx.QLinearConv" README)
+# ----------------------------------------------------------------------------------
+QT = {"uint8": (0, 255), "int8": (-128, 127)}
+
+
+def random_qcase(rng: np.random.Generator, auto=False, margin=0):
+    """A random small quantized problem: uint8 / int8 operands and output, per-tensor or
+    per-output-channel weight parameters, optional int32 bias.  ``margin`` keeps values
+    that far inside their type's range."""
+    x, w, _, attrs = random_case(rng, auto=auto)
+    tx, tw, ty = (str(rng.choice(["uint8", "int8"])) for _ in range(3))
+    M = w.shape[1] * attrs.get("group", 1)
+    nq = M if rng.random() < 0.5 else 1
+    draw = lambda t, size=None: rng.integers(QT[t][0] + margin, QT[t][1] - margin + 1, size=size)  # noqa: E731
+    q = dict(x=draw(tx, x.shape), w=draw(tw, w.shape), x_scale=np.float32(rng.uniform(0.005, 0.05)),
+             x_zero_point=int(draw(tx)), w_scale=rng.uniform(0.002, 0.05, size=nq).astype(np.float32),
+             w_zero_point=draw(tw, nq), y_scale=np.float32(rng.uniform(0.02, 1.0)), y_zero_point=int(draw(ty)),
+             y_type=ty, bias=rng.integers(-20000, 20001, size=M) if rng.random() < 0.7 else None)
+    return q, attrs, (tx, tw)
+
+
+def _shifted_operands(q):
+    """x - x_zp and w[c, m', k] - w_zp[group(c) * Mg + m'] as float64 (exact integers)."""
+    x, w = q["x"], q["w"]
+    C, Mg = w.shape[:2]
+    M = q["bias"].shape[0] if q["bias"] is not None else None
+    wz = np.asarray(q["w_zero_point"]).reshape(-1)
+    G = 1 if wz.size == 1 else wz.size // Mg
+    if wz.size == 1:
+        wzc = np.full((C, Mg), wz[0])
+    else:
+        Cg = C // G
+        m_of = (np.arange(C) // Cg)[:, None] * Mg + np.arange(Mg)[None, :]
+        wzc = wz[m_of]
+    del M
+    return (x - q["x_zero_point"]).astype(np.float64), (w - wzc.reshape((C, Mg) + (1,) * (w.ndim - 2))).astype(np.float64)
+
+
+def pin_qconv_accumulator(lib, count=120, seed=41):
+    """The exact integer sums against PyTorch's float64 conv_transpose of the
+    zero-point-shifted operands plus the bias (exact: every value is a small integer)."""
+    rng = np.random.default_rng(seed)
+    for t in range(count):
+        q, attrs, _ = random_qcase(rng, auto=(t % 4 == 3))
+        _, acc = O.qconvtranspose(**q, return_acc=True, lib=lib, **attrs)
+        xs, ws = _shifted_operands(q)
+        ref = torch_reference(xs, ws, None if q["bias"] is None else q["bias"].astype(np.float64), attrs, lib)
+        assert np.array_equal(ref, np.round(ref))
+        assert np.array_equal(acc, ref.astype(np.int64)), f"case {t}: accumulators differ {attrs}"
+
+
+def pin_qconv_dequantized(lib, count=120, seed=42):
+    """Quantized outputs against the real-valued result: PyTorch's float64
+    conv_transpose of the dequantized operands ((q - zero point) * scale) plus the
+    dequantized bias, divided by y_scale, rounded half to even, shifted by y_zp and
+    saturated.  The float32 requantization may differ from this float64 value only by
+    one step, and only next to a rounding tie."""
+    rng = np.random.default_rng(seed)
+    for t in range(count):
+        q, attrs, _ = random_qcase(rng, auto=(t % 4 == 3))
+        y = O.qconvtranspose(**q, lib=lib, **attrs)
+        xs, ws = _shifted_operands(q)
+        M = y.shape[1]
+        wsc = np.broadcast_to(np.asarray(q["w_scale"], dtype=np.float64).reshape(-1), (M,))
+        Mg, C = q["w"].shape[1], q["w"].shape[0]
+        G = attrs.get("group", 1)
+        wsc_c = wsc[((np.arange(C) // (C // G))[:, None] * Mg + np.arange(Mg)[None, :])]
+        xr = xs * float(q["x_scale"])
+        wr = ws * wsc_c.reshape((C, Mg) + (1,) * (ws.ndim - 2))
+        br = None if q["bias"] is None else q["bias"] * float(q["x_scale"]) * wsc
+        real = torch_reference(xr, wr, br, attrs, lib) / float(q["y_scale"])
+        lo, hi = QT[q["y_type"]]
+        want = np.clip(np.rint(real) + q["y_zero_point"], lo, hi)
+        diff = np.abs(y - want)
+        frac = np.abs(real - np.floor(real) - 0.5)
+        near_tie = frac < 1e-4 * np.maximum(1.0, np.abs(real))
+        assert np.all(diff <= 1) and np.all(near_tie[diff == 1]), \
+            f"case {t}: {int((diff > 0).sum())} outputs differ from the dequantized result"
+
+
+def pin_requantize_definition(lib):
+    """Values fixed by the definition of the requantization step: round half to even,
+    the zero point added after rounding, saturation to the output type, and the int32
+    accumulator taken modulo 2^32."""
+    acc = np.arange(-5, 6)
+    # multiplier 1 * 0.5 / 1 = 0.5 exactly: -2.5 .. 2.5 in steps of 0.5
+    want = np.array([-2, -2, -2, -1, 0, 0, 0, 1, 2, 2, 2])
+    assert np.array_equal(O.requantize(acc, 1.0, [0.5], 0, 1.0, 0, "int8", lib=lib), want)
+    assert np.array_equal(O.requantize(acc, 1.0, [0.5], 0, 1.0, 10, "uint8", lib=lib), want + 10)
+    # multiplier 0.5 * 0.5 / 1 = 0.25: 0.5 -> 0, 1.5 -> 2, 2.5 -> 2, -1.5 -> -2
+    assert np.array_equal(O.requantize([2, 6, 10, -6], 0.5, [0.5], 0, 1.0, 0, "int8", lib=lib), [0, 2, 2, -2])
+    # per-channel multipliers: channel 1 has w_scale 2 (multiplier 2)
+    assert np.array_equal(O.requantize([3, 3], 1.0, [0.5, 2.0], [0, 1], 1.0, 0, "int8", lib=lib), [2, 6])
+    # saturation after the zero point
+    assert np.array_equal(O.requantize([1000, -1000, 490, 500], 1.0, [0.5], 0, 1.0, 10, "uint8", lib=lib),
+                          [255, 0, 255, 255])
+    assert np.array_equal(O.requantize([1000, -1000, 234, 236], 1.0, [0.5], 0, 1.0, 10, "int8", lib=lib),
+                          [127, -128, 127, 127])
+    assert np.array_equal(O.requantize([-276, -278], 1.0, [0.5], 0, 1.0, 10, "int8", lib=lib), [-128, -128])
+    assert np.array_equal(O.requantize([-274], 1.0, [0.5], 0, 1.0, 10, "int8", lib=lib), [-127])
+    # int32 accumulator: 2^32 + 3 wraps to 3, 2^31 wraps to -2^31
+    assert np.array_equal(O.requantize([2 ** 32 + 3], 1.0, [1.0], 0, 1.0, 0, "int8", lib=lib), [3])
+    assert np.array_equal(O.requantize([2 ** 31], 1.0, [1.0], 0, 1.0, 0, "int8", lib=lib), [-128])
+
+
+def pin_qconv_zero_point_shifts(lib, count=40, seed=43):
+    """Moving x (or w) and its zero point by the same amount leaves every output
+    unchanged; per-channel parameters that are all equal act like per-tensor ones."""
+    rng = np.random.default_rng(seed)
+    for t in range(count):
+        q, attrs, (tx, tw) = random_qcase(rng, margin=8)
+        y = O.qconvtranspose(**q, lib=lib, **attrs)
+        dx, dw = int(rng.integers(-8, 9)), int(rng.integers(-8, 9))
+        q2 = dict(q, x=q["x"] + dx, x_zero_point=q["x_zero_point"] + dx, w=q["w"] + dw,
+                  w_zero_point=np.asarray(q["w_zero_point"]) + dw)
+        assert np.array_equal(O.qconvtranspose(**q2, lib=lib, **attrs), y), f"case {t}: zero-point shift"
+        M = y.shape[1]
+        q3 = dict(q, w_scale=np.full(M, q["w_scale"][0], np.float32),
+                  w_zero_point=np.full(M, np.asarray(q["w_zero_point"]).reshape(-1)[0]))
+        q4 = dict(q, w_scale=q["w_scale"][:1], w_zero_point=np.asarray(q["w_zero_point"]).reshape(-1)[:1])
+        assert np.array_equal(O.qconvtranspose(**q3, lib=lib, **attrs), O.qconvtranspose(**q4, lib=lib, **attrs))
+
+
 ALL_PINS = [pin_activation_closed_forms, pin_golden, pin_benchmark_shapes, pin_torch_library, pin_brute_force_gather,
             pin_zero_insertion, pin_numpy_convolve, pin_adjoint, pin_stride1_forward,
             pin_pointwise_matmul, pin_group_split, pin_linearity_translation, pin_useful_macs,
             pin_points_match_whole, pin_rejects_invalid, pin_conv_torch_library, pin_conv_brute_force,
-            pin_conv_adjoint, pin_conv_rejects_invalid]
+            pin_conv_adjoint, pin_conv_rejects_invalid, pin_qconv_accumulator, pin_qconv_dequantized,
+            pin_requantize_definition, pin_qconv_zero_point_shifts]

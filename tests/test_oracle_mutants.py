@@ -53,6 +53,21 @@ MUTANTS = {
     "conv_same_total_off_by_one": ("tot = (O - 1) * s + d * (K - 1) + 1 - L;", "tot = (O - 1) * s + d * (K - 1) - L;"),
     "conv_weight_read_transposed": ("const double *wp = w + (m * g.Cg + cc) * taps;",
                                     "const double *wp = w + (cc * g.M + m) * taps;"),
+    # quantized transposed convolution
+    "q_x_zero_point_dropped": ("int64_t xv = (int64_t)xp[ii] - x_zp;", "int64_t xv = (int64_t)xp[ii];"),
+    "q_w_zero_point_per_tensor": ("acc[flat] += xv * ((int64_t)wp[kk] - w_zp[q]);",
+                                  "acc[flat] += xv * ((int64_t)wp[kk] - w_zp[0]);"),
+    "q_w_scale_per_tensor": ("float mult = or_requant_mult(x_scale, w_scale[q], y_scale);",
+                             "float mult = or_requant_mult(x_scale, w_scale[0], y_scale);"),
+    "q_bias_dropped": ("acc[p] = bias ? bias[m] : 0;", "acc[p] = 0;"),
+    "q_round_half_away": ("float r = rintf(v);", "float r = roundf(v);"),
+    "q_round_truncate": ("float r = rintf(v);", "float r = truncf(v);"),
+    "q_no_upper_saturation": ("    if (q > (double)y_hi)\n        return y_hi;\n", ""),
+    "q_y_zero_point_dropped": ("double q = (double)r + (double)y_zp;", "double q = (double)r;"),
+    "q_y_zero_point_before_rounding": ("volatile float v = (float)acc32 * mult;",
+                                       "volatile float v = (float)acc32 * mult + (float)y_zp;"),
+    "q_multiplier_inverted": ("volatile float mult = xw / y_scale;", "volatile float mult = xw * y_scale;"),
+    "q_accumulator_not_wrapped": ("volatile float v = (float)acc32 * mult;", "volatile float v = (float)acc * mult;"),
 }
 
 
@@ -64,7 +79,7 @@ def _run_mutant(name, tmp):
     path_so = os.path.join(tmp, f"lib{name}.so")
     open(path_c, "w").write(src.replace(old, new))
     O.build(path_c, path_so)
-    r = subprocess.run([sys.executable, os.path.join(HERE, "_mutant_runner.py"), path_so],
+    r = subprocess.run([sys.executable, os.path.join(HERE, "_mutant_runner.py"), path_so, name],
                        capture_output=True, text=True, timeout=300)
     return r.returncode, r.stdout + r.stderr
 
