@@ -54,7 +54,9 @@ def workloads():
             "c5_s1": W.C5_S1, "c5_s1_p1": W.C5_S1_P1, "c5_s2": W.C5_S2,
             "f2_k2s2": W.F2_K2S2, "f2_1x1": W.F2_1X1,
             # the forward convolution with the same W (the adjoint) of a configuration
-            "adj_c5_s1": W.C5_S1, "adj_c4": W.C4}
+            "adj_c5_s1": W.C5_S1, "adj_c4": W.C4,
+            # the quantized (QLinear scheme) decoder shapes
+            "f4_int8": W.F4_C4}
 
 
 def source_digest(kernel: str) -> str:
@@ -241,6 +243,74 @@ def bench_adjoint(args):
         "cpu_baseline": None}), flush=True)
 
 
+def bench_quant(args):
+    """The quantized transposed convolution (QLinear scheme) on the C4 decoder shapes:
+    uint8 x, int8 per-channel w, uint8 y, int32 bias.  Checked code for code against the
+    oracle on whole planes of the first image and channels before timing."""
+    import numpy as np
+    import torch
+
+    import transposed_convolution_amd as T
+    from oracle import oracle as O
+
+    qw = workloads()[args.workload]
+    q = __import__("workloads").make_qinputs(qw)
+    dev = torch.device("cuda:0")
+    tq = {"uint8": torch.uint8, "int8": torch.int8}
+    tx = torch.from_numpy(q["x"]).to(dev)
+    tw = torch.from_numpy(q["w"]).to(dev)
+    ws = torch.from_numpy(q["w_scale"]).to(dev)
+    wz = torch.from_numpy(q["w_zero_point"]).to(dev)
+    tb = torch.from_numpy(q["bias"]).to(dev)
+    call = dict(x=tx, x_scale=float(q["x_scale"]), x_zero_point=int(q["x_zero_point"]), w=tw, w_scale=ws,
+                w_zero_point=wz, y_scale=float(q["y_scale"]), y_zero_point=int(q["y_zero_point"]),
+                y_dtype=tq[qw.y_type], bias=tb, **qw.attrs)
+    y = T.qlinear_convtranspose_nd(**call)
+    torch.cuda.synchronize()
+    got = y[:1, :8].cpu().numpy().astype(np.int64)
+    sub = dict(q, x=q["x"][:1], w=q["w"][:, :8], w_scale=q["w_scale"][:8], w_zero_point=q["w_zero_point"][:8],
+               bias=q["bias"][:8])
+    ref = O.qconvtranspose(**sub, **qw.attrs)
+    if not np.array_equal(got, ref):
+        raise SystemExit(f"quantized output disagrees with the oracle in {int((got != ref).sum())} codes")
+    macs = T.convtranspose_useful_macs(qw.x_shape, qw.w_shape, **qw.attrs)
+    # the oracle timed on the whole first image (every channel)
+    sub = dict(q, x=q["x"][:1])
+    sub_macs = T.convtranspose_useful_macs((1,) + qw.x_shape[1:], qw.w_shape, **qw.attrs)
+    t0 = time.perf_counter()
+    O.qconvtranspose(**sub, **qw.attrs)
+    cpu_dt = time.perf_counter() - t0
+    lib = T.load_library()
+    for _ in range(args.warmup):
+        T.qlinear_convtranspose_nd(**call, out=y)
+    torch.cuda.synchronize()
+    evs = KernelEvents(args.steps)
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        evs.arm(lib, i)
+        T.qlinear_convtranspose_nd(**call, out=y)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    lib.convtranspose_profile_events(None, None)
+    k_avg = float(np.mean(evs.milliseconds()))
+    ops = 2.0 * macs
+    achieved = ops / (k_avg * 1e-3) / 1e12
+    peak = 157.3  # vector ALU: 256 CUs x 64 lanes x 2 ops (multiply-add) x 2.4 GHz x 2 (dual issue)
+    log(f"{args.workload}: {macs / 1e9:.2f} GMAC, {args.steps} steps: {wall * 1e6 / args.steps:.1f} us/step wall, "
+        f"direct kernel {k_avg * 1e3:.1f} us avg, {achieved:.2f} TOP/s = {achieved / peak * 100:.1f}% of {peak}")
+    print(json.dumps({
+        "metric": METRIC, "value": round(ops * args.steps / wall / 1e12, 3), "unit": "TOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(wall * 1e3 / args.steps, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "u8/i8 -> i32", "data": "synthetic",
+        "config": {"workload": f"{qw.name}: X{list(qw.x_shape)} {qw.x_type} W{list(qw.w_shape)} {qw.w_type} "
+                               f"per-channel -> Y {qw.y_type}, {qw.attrs}", "kernel": "direct", "useful_macs": macs},
+        "roofline": {"bound": "alu", "achieved": round(achieved, 3), "peak": peak, "unit": "TOP/s",
+                     "frac": round(achieved / peak, 5), "traffic": None, "kernel_us": round(k_avg * 1e3, 2)},
+        "cpu_baseline": {"value": round(2.0 * sub_macs / cpu_dt / 1e12, 6), "unit": "TOP/s", "cores": O.threads(),
+                         "kind": "oracle", "sample": f"image 0 of {qw.x_shape[0]}, every channel ({sub_macs / 1e9:.2f} GMAC, "
+                                                     f"{cpu_dt:.1f} s)"}}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -274,6 +344,8 @@ def main():
 
     if args.workload.startswith("adj_"):
         return bench_adjoint(args)
+    if args.workload == "f4_int8":
+        return bench_quant(args)
     wl = workloads()[args.workload]
     dev = torch.device("cuda:0")
     x, w, b = W.make_inputs(wl)

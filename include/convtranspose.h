@@ -55,7 +55,9 @@ typedef enum {
     CT_EDEVICE = 4        /* the HIP runtime reported an error at launch                */
 } ct_status;
 
-typedef enum { CT_FLOAT32 = 0, CT_FLOAT16 = 1 } ct_dtype;
+/* element types: the float types serve the float entry points, the 8-bit integer types
+ * the quantized one (qlinear_convtranspose_nd) */
+typedef enum { CT_FLOAT32 = 0, CT_FLOAT16 = 1, CT_INT8 = 2, CT_UINT8 = 3 } ct_dtype;
 
 typedef enum { CT_NOTSET = 0, CT_SAME_UPPER = 1, CT_SAME_LOWER = 2, CT_VALID = 3 } ct_auto_pad;
 
@@ -264,6 +266,49 @@ ct_status convolution_nd(ct_kernel kernel, ct_dtype dtype, int nsp, int channels
                          const void *bias, void *y, const int64_t *y_shape, ct_auto_pad auto_pad,
                          const int64_t *strides, const int64_t *dilations, const int64_t *pads,
                          const int64_t *kernel_shape, int64_t group, void *stream);
+
+/*
+ * Quantized transposed convolution with the QLinear scheme of the webgpu-kernels
+ * "ai.onnx.QLinearConv" README (Description and Inputs table), which the pages give for the
+ * forward convolution and which is applied here to the transposed one:
+ *   acc[n, m, o] = bias[m] + sum over the scatter pairs (c, i, k) that reach o (the same
+ *                  pairs as convtranspose_nd) of (x[n, c, i] - x_zero_point) *
+ *                  (w[c, m', k] - w_zero_point[m]),        summed in int32 modulo 2^32
+ *   y[n, m, o]   = saturate(round_half_even(float(acc) * mult[m]) + y_zero_point)
+ *   mult[m]      = float(float(x_scale * w_scale[m]) / y_scale)
+ * Readings where the pages are silent: the float32 order of the requantization above
+ * (each step one IEEE float32 operation), rounding half to even, saturation to the range
+ * of y's type, and the int32 accumulator wrapping modulo 2^32.
+ *
+ *   kernel          CT_KERNEL_AUTO or CT_KERNEL_DIRECT (the gather kernel serves every
+ *                   call); any other family fails with CT_EUNSUPPORTED
+ *   x, x_type       device tensor of CT_UINT8 or CT_INT8, logical shape x_shape =
+ *                   {N, C, D1..Dn}, layout as in convtranspose_nd (channels_last)
+ *   x_scale, x_zero_point   per-tensor parameters of x (host values); x_scale must be
+ *                   positive and finite, x_zero_point inside x_type's range
+ *   w, w_type       device tensor {C, M/group, k1..kn} of CT_UINT8 or CT_INT8
+ *   w_scale         device float32 array of wq_len values (positive and finite; not
+ *                   checked: they stay on the device)
+ *   w_zero_point    device array of wq_len values of w_type
+ *   wq_len          1 (per tensor) or M (per output channel)
+ *   bias            device int32 array of length M (scale x_scale * w_scale[m], zero
+ *                   point 0), or NULL
+ *   y, y_type       device tensor of CT_UINT8 or CT_INT8 with y_shape = the resolved
+ *                   {N, M, O1..On}, in x's layout
+ *   y_scale, y_zero_point   per-tensor parameters of y (host values), y_scale positive
+ *                   and finite, y_zero_point inside y_type's range
+ *   attributes and stream   as convtranspose_nd
+ * Validation happens before anything is enqueued; errors leave y untouched.  The caller
+ * owns every buffer; nothing is allocated.
+ */
+ct_status qlinear_convtranspose_nd(ct_kernel kernel, int nsp, int channels_last, const void *x, ct_dtype x_type,
+                                   const int64_t *x_shape, float x_scale, int32_t x_zero_point, const void *w,
+                                   ct_dtype w_type, const int64_t *w_shape, const float *w_scale,
+                                   const void *w_zero_point, int64_t wq_len, const int32_t *bias, void *y,
+                                   ct_dtype y_type, const int64_t *y_shape, float y_scale, int32_t y_zero_point,
+                                   ct_auto_pad auto_pad, const int64_t *strides, const int64_t *dilations,
+                                   const int64_t *pads, const int64_t *output_padding, const int64_t *output_shape,
+                                   const int64_t *kernel_shape, int64_t group, void *stream);
 
 /*
  * Tile configuration of the float16 implicit-GEMM (MFMA) kernel, a control for tests and

@@ -636,3 +636,101 @@ def test_errors_leave_output_untouched(T):
         T.convtranspose_nd(x, w, None, out=out, output_padding=[1, 1])
     torch.cuda.synchronize()
     assert bool((out == 3.0).all())
+
+
+# --------------------------------------------------------------------------------------
+# quantized transposed convolution (QLinear scheme): bit-exact against the oracle
+# --------------------------------------------------------------------------------------
+_TQ = {"uint8": torch.uint8, "int8": torch.int8}
+
+
+def qgpu_run(T, q, attrs, cl=False):
+    """The quantized op on the GPU for oracle-style arguments (numpy, NC.. layout);
+    returns int64 codes in the logical layout."""
+    dev = torch.device("cuda:0")
+    tx = torch.from_numpy(np.ascontiguousarray(q["x"]).astype(np.dtype(str(q["x"].dtype)))).to(dev)
+    if cl:
+        tx = T.to_channels_last(tx)
+    tw = torch.from_numpy(np.ascontiguousarray(q["w"])).to(dev)
+    ws = torch.from_numpy(np.asarray(q["w_scale"], dtype=np.float32).reshape(-1)).to(dev)
+    wz = torch.from_numpy(np.asarray(q["w_zero_point"]).reshape(-1).astype(q["w"].dtype)).to(dev)
+    tb = None if q["bias"] is None else torch.from_numpy(np.asarray(q["bias"], dtype=np.int32)).to(dev)
+    y = T.qlinear_convtranspose_nd(tx, float(q["x_scale"]), int(q["x_zero_point"]), tw, ws, wz, float(q["y_scale"]),
+                                   int(q["y_zero_point"]), _TQ[q["y_type"]], tb, channels_last=cl, **attrs)
+    torch.cuda.synchronize()
+    return y.cpu().numpy().astype(np.int64)
+
+
+def _as_types(q, tx, tw):
+    npt = {"uint8": np.uint8, "int8": np.int8}
+    return dict(q, x=q["x"].astype(npt[tx]), w=q["w"].astype(npt[tw]),
+                w_zero_point=np.asarray(q["w_zero_point"]).astype(npt[tw]))
+
+
+@pytest.mark.parametrize("cl", [False, True], ids=["nc", "cl"])
+def test_qlinear_random_small(T, cl):
+    """Random 1-D/2-D/3-D problems over every uint8/int8 combination of x, w and y,
+    per-tensor and per-channel weight parameters, with and without bias: every output
+    code equal to the oracle's."""
+    rng = np.random.default_rng(500 + cl)
+    for t in range(60):
+        q, attrs, (tx, tw) = pins.random_qcase(rng, auto=(t % 4 == 3))
+        q = _as_types(q, tx, tw)
+        _log(f"[case] qlinear #{t} cl={cl} x{q['x'].shape}:{tx} w{q['w'].shape}:{tw} y:{q['y_type']} {attrs}")
+        got = qgpu_run(T, q, attrs, cl)
+        ref = O.qconvtranspose(**q, **attrs)
+        bad = np.flatnonzero(got != ref)
+        assert bad.size == 0, f"qlinear #{t}: {bad.size} codes differ, first {got.flat[bad[0]]} vs {ref.flat[bad[0]]}"
+
+
+QREDUCED = [
+    W.F4_C4.with_(x_shape=(2, 64, 9, 11), w_shape=(64, 40, 4, 4)),
+    W.F4_C4.with_(x_shape=(1, 24, 7, 5), w_shape=(24, 16, 3, 3), x_type="int8", x_zero_point=-3, w_type="uint8",
+                  y_type="int8", y_zero_point=5, per_channel=False,
+                  attrs=dict(strides=[2, 3], pads=[1, 0, 2, 1], output_padding=[1, 2], dilations=[2, 1])),
+    W.F4_C4.with_(x_shape=(2, 16, 3, 4, 5), w_shape=(16, 8, 3, 3, 3), bias_max=0,
+                  attrs=dict(strides=[2, 2, 2], pads=[1] * 6, output_padding=[1] * 3)),
+    W.F4_C4.with_(x_shape=(2, 32, 6, 6), w_shape=(32, 4, 2, 2), attrs=dict(strides=[2, 2], group=4)),
+]
+
+
+@pytest.mark.parametrize("cl", [False, True], ids=["nc", "cl"])
+@pytest.mark.parametrize("qw", QREDUCED, ids=lambda w: f"{w.x_shape}_{w.x_type}_{w.w_type}_{w.y_type}")
+def test_qlinear_reduced_whole_output(T, qw, cl):
+    q = W.make_qinputs(qw)
+    _log(f"[case] qlinear reduced {qw.x_shape} {qw.attrs} cl={cl}")
+    got = qgpu_run(T, q, qw.attrs, cl)
+    assert np.array_equal(got, O.qconvtranspose(**q, **qw.attrs))
+
+
+def test_qlinear_full_size_sampled(T):
+    """The quantized C4-shaped workload at full size: whole output planes of the first
+    and last image and of the first and last 8 output channels against the oracle run on
+    those images and channels only."""
+    qw = W.F4_C4
+    q = W.make_qinputs(qw)
+    _log(f"[case] qlinear full size {qw.x_shape}")
+    got = qgpu_run(T, q, qw.attrs)
+    M = got.shape[1]
+    for n in (0, qw.x_shape[0] - 1):
+        for m0 in (0, M - 8):
+            sub = dict(q, x=q["x"][n:n + 1], w=q["w"][:, m0:m0 + 8], w_scale=q["w_scale"][m0:m0 + 8],
+                       w_zero_point=q["w_zero_point"][m0:m0 + 8], bias=q["bias"][m0:m0 + 8])
+            ref = O.qconvtranspose(**sub, **qw.attrs)
+            assert np.array_equal(got[n:n + 1, m0:m0 + 8], ref), f"image {n}, channels {m0}..{m0 + 7}"
+    lo, hi = W.QRANGE[qw.y_type]
+    assert 0.0 < np.mean((got == lo) | (got == hi)) < 0.05   # the recipe's spread: few saturated codes
+
+
+def test_qlinear_empty_and_tapless(T):
+    """An empty batch launches nothing; outputs no tap reaches (kernel shorter than the
+    stride) hold the requantized bias."""
+    q = W.make_qinputs(W.F4_C4.with_(x_shape=(0, 8, 4, 4), w_shape=(8, 8, 1, 1), attrs=dict(strides=[3, 3])))
+    assert qgpu_run(T, q, dict(strides=[3, 3])).shape == (0, 8, 10, 10)
+    qw = W.F4_C4.with_(x_shape=(1, 8, 4, 4), w_shape=(8, 8, 1, 1), attrs=dict(strides=[3, 3]))
+    q = W.make_qinputs(qw)
+    got = qgpu_run(T, q, qw.attrs)
+    ref = O.qconvtranspose(**q, **qw.attrs)
+    assert np.array_equal(got, ref)
+    assert np.array_equal(got[0, :, 1, 1], O.requantize(q["bias"], q["x_scale"], q["w_scale"], np.arange(8),
+                                                         q["y_scale"], q["y_zero_point"], q["y_type"]))

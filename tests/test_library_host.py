@@ -266,6 +266,30 @@ def test_igemm_channels_first_row_widths(T):
         assert (T.convtranspose_kernel_name(k) == "igemm") == ok, (width, T.convtranspose_kernel_name(k))
 
 
+def test_qlinear_validation_launches_nothing(T):
+    """Argument checks of the quantized entry point, all before any launch (the fake
+    device pointers are never dereferenced), and an empty output that launches nothing."""
+    lib = T.load_library()
+    P = ctypes.c_void_p(256)
+    U8, I8 = 3, 2
+
+    def call(xt=U8, wt=I8, yt=U8, xs=(1, 4, 3, 3), ws=(4, 2, 3, 3), ys=(1, 2, 7, 7), x_scale=0.1, x_zp=128,
+             y_scale=0.2, y_zp=0, wq=1, kernel=0, strides=(2, 2)):
+        at = T._attr_args(2, strides=list(strides))
+        return lib.qlinear_convtranspose_nd(kernel, 2, 0, P, xt, T._i64(xs), x_scale, x_zp, P, wt, T._i64(ws), P, P,
+                                            wq, None, P, yt, T._i64(ys), y_scale, y_zp, *at, None)
+
+    assert call(xt=1) == 3 and "CT_UINT8 or CT_INT8" in T.convtranspose_last_error()
+    assert call(yt=0) == 3
+    assert call(kernel=3) == 3                                     # no MFMA path for the quantized op
+    assert call(x_scale=0.0) == 1 and call(x_scale=float("inf")) == 1 and call(y_scale=-1.0) == 1
+    assert call(x_zp=256) == 1 and call(xt=I8, x_zp=128) == 1 and call(yt=I8, y_zp=-129) == 1
+    assert call(wq=3) == 1 and "length 1 or M" in T.convtranspose_last_error()
+    assert call(ys=(1, 2, 6, 7)) == 2                              # y_shape differs from the resolved shape
+    assert call(xs=(0, 4, 3, 3), ys=(0, 2, 7, 7)) == 0             # empty output: nothing launched
+    assert T.convtranspose_last_error() == ""
+
+
 def test_random_cases_resolve_identically(T):
     rng = np.random.default_rng(5)
     for t in range(300):

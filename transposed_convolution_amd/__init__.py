@@ -24,7 +24,7 @@ __all__ = [
     "convtranspose_useful_macs", "convtranspose_select_kernel", "convtranspose_last_error",
     "convtranspose_kernel_name", "library_path", "load_library", "channels_last_empty",
     "to_channels_last", "KERNELS", "ACTIVATIONS", "convolution_nd", "convolution_output_shape",
-    "IGEMM_TILES", "set_igemm_tile", "igemm_tile",
+    "IGEMM_TILES", "set_igemm_tile", "igemm_tile", "qlinear_convtranspose_nd",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -90,6 +90,11 @@ def load_library():
     lib.convolution_nd.restype = ctypes.c_int
     lib.convtranspose_profile_events.argtypes = [vp, vp]
     lib.convtranspose_profile_events.restype = ctypes.c_int
+    c_i32, c_f32 = ctypes.c_int32, ctypes.c_float
+    lib.qlinear_convtranspose_nd.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, vp, ctypes.c_int, i64p, c_f32,
+                                             c_i32, vp, ctypes.c_int, i64p, vp, vp, ctypes.c_int64, vp, vp,
+                                             ctypes.c_int, i64p, c_f32, c_i32] + attrs + [vp]
+    lib.qlinear_convtranspose_nd.restype = ctypes.c_int
     lib.convtranspose_set_igemm_tile.argtypes = [ctypes.c_int]
     lib.convtranspose_set_igemm_tile.restype = ctypes.c_int
     lib.convtranspose_igemm_tile.argtypes = []
@@ -439,6 +444,70 @@ def convolution_nd(x: torch.Tensor, w: torch.Tensor, bias: Optional[torch.Tensor
         st = lib.convolution_nd(KERNELS[kernel], _DTYPES[x.dtype], nsp, int(channels_last), ptr(x), _i64(x.shape),
                                 ptr(w), _i64(w.shape), ptr(bias), ptr(out), _i64(yshape),
                                 *_conv_attr_args(nsp, **attrs), ctypes.c_void_p(stream.cuda_stream))
+    if st:
+        _raise(st)
+    return out
+
+
+_QTYPES = {torch.int8: 2, torch.uint8: 3}
+
+
+def qlinear_convtranspose_nd(x: torch.Tensor, x_scale: float, x_zero_point: int, w: torch.Tensor,
+                             w_scale: torch.Tensor, w_zero_point: torch.Tensor, y_scale: float, y_zero_point: int,
+                             y_dtype: torch.dtype = torch.uint8, bias: Optional[torch.Tensor] = None, *,
+                             auto_pad: str = "NOTSET", strides=None, dilations=None, pads=None, output_padding=None,
+                             output_shape=None, kernel_shape=None, group: int = 1, channels_last: bool = False,
+                             out: Optional[torch.Tensor] = None, kernel: str = "auto",
+                             stream: Optional[torch.cuda.Stream] = None) -> torch.Tensor:
+    """Quantized ConvTranspose (QLinear scheme) on the GPU: uint8/int8 x, w and y; x and y
+    quantized per tensor (host scalars), w per tensor or per output channel (w_scale
+    float32 and w_zero_point of w's dtype, 1 or M values, on x's device); bias int32."""
+    lib = load_library()
+    for name, t in (("x", x), ("w", w), ("w_zero_point", w_zero_point)):
+        if t.dtype not in _QTYPES:
+            raise ConvTransposeError(3, f"{name} must be uint8 or int8 (got {t.dtype})")
+    if y_dtype not in _QTYPES:
+        raise ConvTransposeError(3, f"y_dtype must be uint8 or int8 (got {y_dtype})")
+    if w_zero_point.dtype != w.dtype:
+        raise ConvTransposeError(3, "w_zero_point must have w's dtype")
+    if x.dim() < 3 or x.dim() > 5 or w.dim() != x.dim():
+        raise ConvTransposeError(1, "x and w must have the same rank, 3 to 5")
+    dev = x.device
+    _check_tensor("x", x, dev, x.dtype)
+    _check_tensor("w", w, dev, w.dtype)
+    _check_tensor("w_scale", w_scale, dev, torch.float32)
+    _check_tensor("w_zero_point", w_zero_point, dev, w.dtype)
+    if w_scale.dim() != 1 or w_zero_point.dim() != 1 or w_scale.numel() != w_zero_point.numel() \
+            or not w_scale.is_contiguous() or not w_zero_point.is_contiguous():
+        raise ConvTransposeError(1, "w_scale and w_zero_point must be dense 1-D tensors of the same length")
+    if bias is not None:
+        _check_tensor("bias", bias, dev, torch.int32)
+        if bias.dim() != 1 or not bias.is_contiguous():
+            raise ConvTransposeError(1, "bias must be a dense 1-D int32 tensor")
+    if not _dense(x, channels_last) or not w.is_contiguous():
+        raise ConvTransposeError(1, "x (in the requested layout) and w must be dense")
+    if kernel not in KERNELS:
+        raise ConvTransposeError(1, f"unknown kernel {kernel!r}")
+    attrs = dict(auto_pad=auto_pad, strides=strides, dilations=dilations, pads=pads, output_padding=output_padding,
+                 output_shape=output_shape, kernel_shape=kernel_shape, group=group)
+    yshape, _ = convtranspose_output_shape(tuple(x.shape), tuple(w.shape), **attrs)
+    if out is None:
+        out = (channels_last_empty(yshape, y_dtype, dev) if channels_last
+               else torch.empty(yshape, dtype=y_dtype, device=dev))
+    else:
+        _check_tensor("out", out, dev, y_dtype)
+        if tuple(out.shape) != tuple(yshape) or not _dense(out, channels_last):
+            raise ConvTransposeError(2, f"out must be dense with shape {yshape}")
+    stream = stream if stream is not None else torch.cuda.current_stream(dev)
+    nsp = x.dim() - 2
+    ptr = lambda t: ctypes.c_void_p(t.data_ptr()) if t is not None else None  # noqa: E731
+    with torch.cuda.device(dev):
+        st = lib.qlinear_convtranspose_nd(KERNELS[kernel], nsp, int(channels_last), ptr(x), _QTYPES[x.dtype],
+                                          _i64(x.shape), float(x_scale), int(x_zero_point), ptr(w),
+                                          _QTYPES[w.dtype], _i64(w.shape), ptr(w_scale), ptr(w_zero_point),
+                                          w_scale.numel(), ptr(bias), ptr(out), _QTYPES[y_dtype], _i64(yshape),
+                                          float(y_scale), int(y_zero_point), *_attr_args(nsp, **attrs),
+                                          ctypes.c_void_p(stream.cuda_stream))
     if st:
         _raise(st)
     return out

@@ -137,3 +137,70 @@ F2_K2S2 = C4.with_(name="f2_2d_f16_k2_s2", w_shape=(512, 256, 2, 2),
 F2_1X1 = C4.with_(name="f2_2d_f16_1x1", w_shape=(512, 256, 1, 1), attrs=dict(strides=[1, 1], group=1),
                   w_dist=("N", 0.0, 1.0 / math.sqrt(512)), seed=7)
 EXTRAS = {w.name: w for w in (F2_K2S2, F2_1X1)}
+
+
+# --------------------------------------------------------------------------------------
+# quantized problems (QLinear scale / zero-point scheme)
+# --------------------------------------------------------------------------------------
+QRANGE = {"uint8": (0, 255), "int8": (-128, 127)}
+
+
+@dataclasses.dataclass(frozen=True)
+class QWorkload:
+    """A quantized ConvTranspose: shapes, attributes, element types and the recipe of the
+    quantization parameters.  x and w are drawn uniformly over their types' whole range;
+    the weight zero point is 0 for int8 weights and 128 for uint8 ones (symmetric
+    weights), one per output channel when ``per_channel``; w_scale is U(0.8, 1.2) times
+    ``w_scale`` per channel; bias is uniform in [-bias_max, bias_max]."""
+
+    name: str
+    x_shape: Tuple[int, ...]
+    w_shape: Tuple[int, ...]
+    attrs: dict
+    x_type: str
+    w_type: str
+    y_type: str
+    x_scale: float
+    x_zero_point: int
+    w_scale: float
+    y_scale: float
+    y_zero_point: int
+    per_channel: bool
+    bias_max: int
+    seed: int
+    channels_last: bool = False
+
+    @property
+    def nsp(self) -> int:
+        return len(self.x_shape) - 2
+
+    def with_(self, **kw) -> "QWorkload":
+        return dataclasses.replace(self, **kw)
+
+
+def make_qinputs(qw: QWorkload) -> dict:
+    """Keyword arguments of a quantized call (numpy arrays; NC.. layout), drawn from
+    ``default_rng(seed)`` in the order x, w, w_scale, bias."""
+    rng = np.random.default_rng(qw.seed)
+    npt = {"uint8": np.uint8, "int8": np.int8}
+    lo, hi = QRANGE[qw.x_type]
+    x = rng.integers(lo, hi + 1, size=qw.x_shape).astype(npt[qw.x_type])
+    lo, hi = QRANGE[qw.w_type]
+    w = rng.integers(lo, hi + 1, size=qw.w_shape).astype(npt[qw.w_type])
+    M = qw.w_shape[1] * int(qw.attrs.get("group", 1))
+    nq = M if qw.per_channel else 1
+    w_scale = (qw.w_scale * rng.uniform(0.8, 1.2, size=nq)).astype(np.float32)
+    w_zp = np.full(nq, 0 if qw.w_type == "int8" else 128).astype(npt[qw.w_type])
+    bias = rng.integers(-qw.bias_max, qw.bias_max + 1, size=M).astype(np.int32) if qw.bias_max > 0 else None
+    return dict(x=x, w=w, x_scale=np.float32(qw.x_scale), x_zero_point=qw.x_zero_point, w_scale=w_scale,
+                w_zero_point=w_zp, y_scale=np.float32(qw.y_scale), y_zero_point=qw.y_zero_point, y_type=qw.y_type,
+                bias=bias)
+
+
+# The C4 decoder shapes quantized: uint8 activations (zero point 128), int8 weights with
+# per-channel scales, uint8 output; the scales put the output's spread at about 50 codes.
+F4_C4 = QWorkload("f4_2d_int8_decoder_s2", (8, 512, 64, 64), (512, 256, 4, 4),
+                  dict(strides=[2, 2], pads=[1, 1, 1, 1], group=1), "uint8", "int8", "uint8",
+                  x_scale=0.02, x_zero_point=128, w_scale=0.001, y_scale=0.1, y_zero_point=128,
+                  per_channel=True, bias_max=50000, seed=8)
+QCONFIGS = {F4_C4.name: F4_C4}
