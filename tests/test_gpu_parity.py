@@ -644,9 +644,10 @@ def test_errors_leave_output_untouched(T):
 _TQ = {"uint8": torch.uint8, "int8": torch.int8}
 
 
-def qgpu_run(T, q, attrs, cl=False):
+def qgpu_run(T, q, attrs, cl=False, kernel="auto"):
     """The quantized op on the GPU for oracle-style arguments (numpy, NC.. layout);
-    returns int64 codes in the logical layout."""
+    returns int64 codes in the logical layout, or None when a forced kernel family does
+    not serve the call."""
     dev = torch.device("cuda:0")
     tx = torch.from_numpy(np.ascontiguousarray(q["x"]).astype(np.dtype(str(q["x"].dtype)))).to(dev)
     if cl:
@@ -655,8 +656,14 @@ def qgpu_run(T, q, attrs, cl=False):
     ws = torch.from_numpy(np.asarray(q["w_scale"], dtype=np.float32).reshape(-1)).to(dev)
     wz = torch.from_numpy(np.asarray(q["w_zero_point"]).reshape(-1).astype(q["w"].dtype)).to(dev)
     tb = None if q["bias"] is None else torch.from_numpy(np.asarray(q["bias"], dtype=np.int32)).to(dev)
-    y = T.qlinear_convtranspose_nd(tx, float(q["x_scale"]), int(q["x_zero_point"]), tw, ws, wz, float(q["y_scale"]),
-                                   int(q["y_zero_point"]), _TQ[q["y_type"]], tb, channels_last=cl, **attrs)
+    try:
+        y = T.qlinear_convtranspose_nd(tx, float(q["x_scale"]), int(q["x_zero_point"]), tw, ws, wz,
+                                       float(q["y_scale"]), int(q["y_zero_point"]), _TQ[q["y_type"]], tb,
+                                       channels_last=cl, kernel=kernel, **attrs)
+    except T.ConvTransposeError as e:
+        if e.status == 3 and kernel not in ("auto", "direct"):
+            return None
+        raise
     torch.cuda.synchronize()
     return y.cpu().numpy().astype(np.int64)
 
@@ -709,8 +716,8 @@ def test_qlinear_full_size_sampled(T):
     those images and channels only."""
     qw = W.F4_C4
     q = W.make_qinputs(qw)
-    _log(f"[case] qlinear full size {qw.x_shape}")
-    got = qgpu_run(T, q, qw.attrs)
+    _log(f"[case] qlinear full size {qw.x_shape} channels_last={qw.channels_last}")
+    got = qgpu_run(T, q, qw.attrs, qw.channels_last)
     M = got.shape[1]
     for n in (0, qw.x_shape[0] - 1):
         for m0 in (0, M - 8):
@@ -734,3 +741,54 @@ def test_qlinear_empty_and_tapless(T):
     assert np.array_equal(got, ref)
     assert np.array_equal(got[0, :, 1, 1], O.requantize(q["bias"], q["x_scale"], q["w_scale"], np.arange(8),
                                                          q["y_scale"], q["y_zero_point"], q["y_type"]))
+
+
+Q8_CASES = [
+    # (x_shape, w_shape, attrs): C/group a multiple of 16 (the int8 MFMA kernel's
+    # channels-last 16-byte vectors); ragged output channels and pixel tiles, a second
+    # partial channel step (C/group = 160), groups, 1-D / 2-D / 3-D
+    ((2, 64, 9, 12), (64, 40, 4, 4), dict(strides=[2, 2], pads=[1, 1, 1, 1])),
+    ((1, 32, 5, 9, 11), (32, 24, 3, 3, 3), dict(strides=[1, 1, 1])),
+    ((1, 48, 6, 7), (48, 72, 3, 3), dict(strides=[2, 2], pads=[1, 1, 1, 1], output_padding=[1, 1])),
+    ((2, 32, 50), (32, 20, 5), dict(strides=[3], dilations=[2], pads=[2, 1])),
+    ((2, 64, 6, 6), (64, 8, 2, 2), dict(strides=[2, 2], group=2)),
+    ((1, 160, 5, 6), (160, 24, 4, 4), dict(strides=[2, 2], pads=[1, 1, 1, 1])),
+    ((1, 256, 8, 8), (256, 64, 4, 4), dict(strides=[2, 2], pads=[1, 1, 1, 1])),
+]
+
+
+@pytest.mark.parametrize("tile", [None, "256x256", "128x256", "64x128"])
+def test_qlinear_int8_mfma(T, tile):
+    """The int8 MFMA implicit GEMM (channels-last) on whole outputs, every uint8/int8
+    combination: symmetric weights (no input-sum correction) and arbitrary zero points
+    (per-channel weight zero points exercise the per-pixel input sums)."""
+    rng = np.random.default_rng(900 + (0 if tile is None else T.IGEMM_TILES.index(tile) + 1))
+    ran = 0
+    for ci, (xs, ws, attrs) in enumerate(Q8_CASES):
+        for general in (False, True):
+            tx, tw, ty = (str(rng.choice(["uint8", "int8"])) for _ in range(3))
+            M = ws[1] * attrs.get("group", 1)
+            nq = M if (general or ci % 2) else 1
+            lo, hi = pins.QT[tx]
+            x = rng.integers(lo, hi + 1, size=xs)
+            x_zp = int(rng.integers(lo, hi + 1))
+            lo, hi = pins.QT[tw]
+            w = rng.integers(lo, hi + 1, size=ws)
+            w_zp = rng.integers(lo, hi + 1, size=nq) if general else np.full(nq, 0 if tw == "int8" else 128)
+            depth = xs[1] // attrs.get("group", 1) * 4
+            q = _as_types(dict(x=x, w=w, x_scale=np.float32(0.02), x_zero_point=x_zp,
+                               w_scale=rng.uniform(0.5, 1.5, size=nq).astype(np.float32) * np.float32(0.01),
+                               w_zero_point=w_zp, y_scale=np.float32(0.0004 * np.sqrt(depth) * 74 * 74 / 50),
+                               y_zero_point=int(rng.integers(*pins.QT[ty])), y_type=ty,
+                               bias=rng.integers(-50000, 50001, size=M) if ci % 3 else None), tx, tw)
+            _log(f"[case] int8 mfma tile {tile} #{ci} general={general} x{xs}:{tx} w{ws}:{tw} y:{ty} {attrs}")
+            with forced_tile(T, tile):
+                got = qgpu_run(T, q, attrs, cl=True, kernel="igemm")
+            if got is None:
+                continue
+            ran += 1
+            ref = O.qconvtranspose(**q, **attrs)
+            bad = np.flatnonzero(got != ref)
+            assert bad.size == 0, f"int8 mfma #{ci}: {bad.size} of {got.size} codes differ, first at " \
+                                  f"{np.unravel_index(bad[0], got.shape)}: {got.flat[bad[0]]} vs {ref.flat[bad[0]]}"
+    assert ran >= len(Q8_CASES), f"the int8 kernel served only {ran} cases"

@@ -45,6 +45,8 @@ namespace {
 
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef int i32x16 __attribute__((ext_vector_type(16)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kMaxRes = 8;               // largest stride handled per axis
@@ -56,6 +58,10 @@ constexpr int kLdsBytes = 160 * 1024 - 2048;
 constexpr int lds_budget(int occ) { return occ == 1 ? kLdsBytes : 160 * 1024 / occ - 1024; }
 constexpr int kSinkBytes = 64 * 16;
 constexpr int kBiasBytes = 256 * 4;      // the block's bias as float32 (at most 256 channels)
+// quantized instances: per channel of the block the int32 compensation, the float32
+// requantization multiplier and the shifted weight zero point
+constexpr int kQTailBytes = 3 * 256 * 4;
+constexpr int tail_bytes(bool q8) { return q8 ? kQTailBytes : kBiasBytes; }
 
 struct IgArgs {
     int N, C, M, Cg, Mg, Cgp, Mgp, T, G;
@@ -72,6 +78,18 @@ struct IgArgs {
     short tb0[3][kMaxRes];
     short kstep[3], bstep[3];
     Act act;  // output activation
+    // quantized instances only (QLinear scheme; see the kernel's Q8 comments)
+    struct Quant {
+        const float *w_scale;   // 1 or M values
+        const void *w_zp;       // 1 or M values of w's type
+        const int *bias;        // M values or null
+        const int *wsum;        // [G][T][Mgp]: sum over c of the shifted weights
+        const int *xsum;        // [N][G][L0][L1][L2]: sum over the group's channels of the shifted input
+        float x_scale, y_scale;
+        int x_zp, y_zp, y_lo, y_hi;  // x_zp in the signed (shifted) domain
+        unsigned xflip;              // 0x80808080 for uint8 x (to the signed domain), else 0
+        int w_u8, w_per_channel, y_u8;
+    } q;
 };
 
 __device__ __forceinline__ int floor_div8(int v) { return v >= 0 ? v / 8 : -((-v + 7) / 8); }
@@ -103,7 +121,7 @@ struct Tile {
 // ROWS8 (channels-first): input rows are whole 16-byte vectors (innermost size a multiple
 // of 8), so a halo vector is one 16-byte load; otherwise (an even innermost size) it is
 // four 4-byte loads and the columns past the row end are zeroed when the halo is stored.
-template <bool CL, int WAVES_M, int WM, int WN, int CC, int NCH_ITEMS, int NHWC_VECS, int OCC>
+template <bool CL, int WAVES_M, int WM, int WN, int CC, int NCH_ITEMS, int NHWC_VECS, int OCC, bool Q8 = false>
 struct IgCfg {
     static constexpr int WAVES_N = 4 / WAVES_M;
     static constexpr int BM = WAVES_M * WM * 32;
@@ -113,17 +131,34 @@ struct IgCfg {
     static constexpr int KSUB = CC / 16;      // MFMA k-steps per step
     static constexpr int WVEC = BM * CHUNKS / kThreads;
     static constexpr int LDS = lds_budget(OCC);
-    static constexpr int HALO_BYTES = LDS - 2 * BM * ROW - kSinkBytes - kBiasBytes;
+    static constexpr int HALO_BYTES = LDS - 2 * BM * ROW - kSinkBytes - tail_bytes(Q8);
     static_assert(BM * CHUNKS % kThreads == 0, "weight tile must split evenly");
     static_assert(HALO_BYTES > 0, "LDS budget");
 };
 
-template <bool CL, int WAVES_M, int WM, int WN, int CC, int NCH_ITEMS, int NHWC_VECS, int OCC, bool PAIR, bool ROWS8>
+// Q8 (channels-last): the quantized operation on the int8 MFMA v_mfma_i32_32x32x32_i8.
+// Operands are taken to the signed domain (uint8 values XOR 0x80, i.e. minus 128, and
+// the zero points with them); input positions outside the input hold the input zero
+// point instead of 0, so every iterated tap contributes (x - x_zp) * (w - w_zp) and
+//   sum (x - x_zp)(w - w_zp) = sum x w - w_zp * Sx - x_zp * Sw + x_zp * w_zp * Cg * T
+// with Sx the sum of the iterated inputs (from the channel sums xsum, per pixel; only
+// when some w_zp is non-zero), Sw the sum of the iterated weights (from wsum, per
+// channel) and T the iterated tap count.  A step is CC * 2 int8 channels (the same
+// 16-byte chunks and LDS rows as the float16 instances).
+template <bool CL, int WAVES_M, int WM, int WN, int CC, int NCH_ITEMS, int NHWC_VECS, int OCC, bool PAIR, bool ROWS8,
+          bool Q8 = false>
 __global__ __launch_bounds__(kThreads, OCC) void igemm_kernel(const _Float16 *x, const _Float16 *__restrict__ wp,
                                                             const _Float16 *__restrict__ bias,
                                                             _Float16 *__restrict__ y, IgArgs p)
 {
-    using Cfg = IgCfg<CL, WAVES_M, WM, WN, CC, NCH_ITEMS, NHWC_VECS, OCC>;
+    using Cfg = IgCfg<CL, WAVES_M, WM, WN, CC, NCH_ITEMS, NHWC_VECS, OCC, Q8>;
+    static_assert(!Q8 || (CL && !PAIR && ROWS8), "quantized instances: channels-last");
+    using XE = std::conditional_t<Q8, signed char, _Float16>;  // element of x and of the packed weights
+    using AccV = std::conditional_t<Q8, i32x16, f32x16>;
+    constexpr int CCH = Q8 ? 2 * CC : CC;   // channels per step
+    constexpr int CH16 = Q8 ? 16 : 8;       // channels per 16-byte chunk
+    const XE *const xe = reinterpret_cast<const XE *>(x);
+    const XE *const we = reinterpret_cast<const XE *>(wp);
     constexpr int WAVES_N = Cfg::WAVES_N, BM = Cfg::BM, BN = Cfg::BN, ROW = Cfg::ROW;
     constexpr int CHUNKS = Cfg::CHUNKS, KSUB = Cfg::KSUB, WVEC = Cfg::WVEC;
     (void)WAVES_N;
@@ -139,6 +174,9 @@ __global__ __launch_bounds__(kThreads, OCC) void igemm_kernel(const _Float16 *x,
     unsigned char *const lds_h = lds + 2 * BM * ROW;
     unsigned char *const lds_sink = lds_h + Cfg::HALO_BYTES;
     float *const sbias = reinterpret_cast<float *>(lds_sink + kSinkBytes);  // kept to the end
+    int *const sq_comp = reinterpret_cast<int *>(lds_sink + kSinkBytes);      // Q8: the same region
+    float *const sq_mult = reinterpret_cast<float *>(sq_comp + 256);
+    int *const sq_wz = sq_comp + 512;
     static_assert(BM <= 256, "bias region");
 
     const int tid = threadIdx.x;
@@ -234,13 +272,13 @@ __global__ __launch_bounds__(kThreads, OCC) void igemm_kernel(const _Float16 *x,
         hoff[j] = ((row - tl.row_lo) * tl.HC + (col - tl.col_lo)) * ROW + (lane >> 5) * 16;
     }
 
-    f32x16 acc[WM][WN];
+    AccV acc[WM][WN];
 #pragma unroll
     for (int i = 0; i < WM; ++i)
 #pragma unroll
         for (int j = 0; j < WN; ++j)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0;
 
     const int L0 = p.L[0], L1 = p.L[1], L2 = p.L[2];
     const size_t plane_in = size_t(L0) * L1 * L2;
@@ -268,11 +306,11 @@ __global__ __launch_bounds__(kThreads, OCC) void igemm_kernel(const _Float16 *x,
     // loads k < WVEC/2 of every thread cover exactly the first half.
     static_assert(!PAIR || (WVEC % 2 == 0 && (WVEC / 2) * kThreads == BMM * CHUNKS), "phase halves");
     auto load_w = [&](const StepIdx &q, u32x4 *reg) {
-        const int stride_vec = p.Cgp / 8;  // 16-byte vectors per Wp row
+        const int stride_vec = p.Cgp / CH16;  // 16-byte vectors per Wp row
         if constexpr (!PAIR) {
             const int tflat = ((k00 + q.t0 * ks0) * p.K[1] + (k01 + q.t1 * ks1)) * p.K[2] + (k02 + q.t2 * ks2);
             const size_t row0 = (wrow0 + tflat) * p.Mgp + size_t(mt) * BM;
-            const u32x4 *src = reinterpret_cast<const u32x4 *>(wp + row0 * p.Cgp + size_t(q.chunk) * CC);
+            const u32x4 *src = reinterpret_cast<const u32x4 *>(we + row0 * p.Cgp + size_t(q.chunk) * CCH);
 #pragma unroll
             for (int k = 0; k < WVEC; ++k) {
                 const int u = tid + k * kThreads;
@@ -283,7 +321,7 @@ __global__ __launch_bounds__(kThreads, OCC) void igemm_kernel(const _Float16 *x,
 #pragma unroll
             for (int h = 0; h < 2; ++h) {  // column phase h: WVEC / 2 loads
                 const size_t row0 = (wrow0 + tb + p.tk0[2][h]) * p.Mgp + size_t(mt) * BMM;
-                const u32x4 *src = reinterpret_cast<const u32x4 *>(wp + row0 * p.Cgp + size_t(q.chunk) * CC);
+                const u32x4 *src = reinterpret_cast<const u32x4 *>(we + row0 * p.Cgp + size_t(q.chunk) * CCH);
 #pragma unroll
                 for (int k = 0; k < WVEC / 2; ++k) {
                     const int u = tid + k * kThreads;
@@ -316,26 +354,28 @@ __global__ __launch_bounds__(kThreads, OCC) void igemm_kernel(const _Float16 *x,
     auto load_halo_part = [&](auto kb, auto ke, int chunk, int t0, u32x4 *reg) -> unsigned {
         constexpr int KB = decltype(kb)::value, KE = decltype(ke)::value;
         const int i0 = j0 + b00 - t0 * bs0;
-        const int cbase = chunk * CC;  // channel offset inside the group
+        const int cbase = chunk * CCH;  // channel offset inside the group
         unsigned valid = 0;
         if (CL) {
-            const _Float16 *xb = x + (size_t(n) * L0 + i0) * L1 * L2 * p.C + size_t(g) * p.Cg + cbase;
+            const XE *xb = xe + (size_t(n) * L0 + i0) * L1 * L2 * p.C + size_t(g) * p.Cg + cbase;
 #pragma unroll
             for (int k = KB; k < KE; ++k) {
                 const int u = tid + k * kThreads;
                 const int pix = u / CHUNKS, ch = u % CHUNKS;
                 const int hr = pix / tl.HC, hc = pix - hr * tl.HC;
                 const int i1 = i1o + hr, i2 = i2o + hc;
-                const bool ok = u < halo_items && i1 >= 0 && i1 < L1 && i2 >= 0 && i2 < L2 && cbase + ch * 8 < p.Cg;
-                const size_t off = ok ? (size_t(i1) * L2 + i2) * p.C + ch * 8 : 0;
-                reg[k] = *reinterpret_cast<const u32x4 *>((ok ? xb : x) + off);
-                valid |= unsigned(ok) << k;
+                const bool inside = u < halo_items && i1 >= 0 && i1 < L1 && i2 >= 0 && i2 < L2;
+                const bool ok = inside && cbase + ch * CH16 < p.Cg;
+                const size_t off = ok ? (size_t(i1) * L2 + i2) * p.C + ch * CH16 : 0;
+                reg[k] = *reinterpret_cast<const u32x4 *>((ok ? xb : xe) + off);
+                // Q8: the bit records the position only (channel padding is zeroed on store)
+                valid |= unsigned(Q8 ? inside : ok) << k;
             }
         } else {
             // items (halo row, aligned 8-column vector, channel octet), octet fastest:
             // a wave reads 8 channel planes x 128 contiguous bytes per load; load index
             // = item * 8 + channel of the octet
-            const _Float16 *xb = x + (size_t(n) * p.C + size_t(g) * p.Cg + cbase) * plane_in + size_t(i0) * L1 * L2;
+            const XE *xb = xe + (size_t(n) * p.C + size_t(g) * p.Cg + cbase) * plane_in + size_t(i0) * L1 * L2;
 #pragma unroll
             for (int it = KB / 8; it < (KE + 7) / 8; ++it) {
                 const int u = tid + it * kThreads;
@@ -345,7 +385,7 @@ __global__ __launch_bounds__(kThreads, OCC) void igemm_kernel(const _Float16 *x,
                 const int i1 = i1o + hr;
                 const int i2 = (va + vc) * 8;
                 const bool ok = u < halo_items && i1 >= 0 && i1 < L1 && i2 >= 0 && i2 < L2 && cbase + oct * 8 < p.Cg;
-                const _Float16 *src = ok ? xb + size_t(oct * 8) * plane_in + size_t(i1) * L2 + i2 : x;
+                const XE *src = ok ? xb + size_t(oct * 8) * plane_in + size_t(i1) * L2 + i2 : xe;
                 const size_t step = ok ? plane_in : 0;
                 if constexpr (ROWS8) {
 #pragma unroll
@@ -358,7 +398,7 @@ __global__ __launch_bounds__(kThreads, OCC) void igemm_kernel(const _Float16 *x,
 #pragma unroll
                     for (int q = 0; q < 4; ++q) {
                         const bool in = ok && i2 + 2 * q < L2;
-                        const _Float16 *sq = in ? src + 2 * q : x;
+                        const XE *sq = in ? src + 2 * q : xe;
                         const size_t sstep = in ? step : 0;
 #pragma unroll
                         for (int k = 0; k < 8; ++k)
@@ -374,7 +414,7 @@ __global__ __launch_bounds__(kThreads, OCC) void igemm_kernel(const _Float16 *x,
     auto load_halo = [&](int chunk, int t0, u32x4 *reg) -> unsigned {
         return load_halo_part(std::integral_constant<int, 0>{}, std::integral_constant<int, HREG>{}, chunk, t0, reg);
     };
-    auto store_halo = [&](const u32x4 *reg, unsigned valid) {
+    auto store_halo = [&](const u32x4 *reg, unsigned valid, int chunk) {
         const u32x4 zero = {0u, 0u, 0u, 0u};
         unsigned char *const sink = lds_sink + lane * 16;
         if (CL) {
@@ -382,7 +422,19 @@ __global__ __launch_bounds__(kThreads, OCC) void igemm_kernel(const _Float16 *x,
             for (int k = 0; k < NHWC_VECS; ++k) {
                 const int u = tid + k * kThreads;
                 unsigned char *dst = u < halo_items ? &lds_h[(u / CHUNKS) * ROW + (u % CHUNKS) * 16] : sink;
-                *reinterpret_cast<u32x4 *>(dst) = ((valid >> k) & 1u) ? reg[k] : zero;
+                if constexpr (Q8) {
+                    // channels past C/group hold 0, positions outside the input the input
+                    // zero point, the others the input in the signed domain
+                    const unsigned fb = unsigned(p.q.x_zp) & 0xffu;
+                    const unsigned f4 = fb | (fb << 8) | (fb << 16) | (fb << 24);
+                    const u32x4 fill = {f4, f4, f4, f4};
+                    const u32x4 flip = {p.q.xflip, p.q.xflip, p.q.xflip, p.q.xflip};
+                    const bool chok = (u % CHUNKS) * CH16 < p.Cg - chunk * CCH;
+                    *reinterpret_cast<u32x4 *>(dst) = !chok ? zero : (((valid >> k) & 1u) ? (reg[k] ^ flip) : fill);
+                } else {
+                    (void)chunk;
+                    *reinterpret_cast<u32x4 *>(dst) = ((valid >> k) & 1u) ? reg[k] : zero;
+                }
             }
         } else {
 #pragma unroll
@@ -414,10 +466,47 @@ __global__ __launch_bounds__(kThreads, OCC) void igemm_kernel(const _Float16 *x,
     };
 
     // The bias of the block's channels, staged once (read in the epilogue; the first
-    // barrier below, or the epilogue's own, makes it visible).
-    for (int mm = tid; mm < BMM; mm += kThreads) {
-        const int m = mt * BMM + mm;
-        sbias[mm] = (bias && m < p.Mg) ? float(bias[g * p.Mg + m]) : 0.0f;
+    // barrier below, or the epilogue's own, makes it visible).  Q8: per channel the
+    // compensation bias - x_zp * Sw + x_zp * w_zp * Cg * T (int32, modulo 2^32), the
+    // requantization multiplier and the shifted weight zero point; need_sx: some channel
+    // of the block has a non-zero weight zero point.
+    int need_sx = 0;
+    if constexpr (Q8) {
+        const unsigned taps_it = unsigned((t0_end - t0_first) * nt1 * nt2);
+        int nz = 0;
+        for (int mm = tid; mm < BM; mm += kThreads) {
+            const int m = mt * BM + mm;
+            int comp = 0, wz = 0;
+            float mult = 0.0f;
+            if (m < p.Mg) {
+                const int mg = g * p.Mg + m;
+                const int qi = p.q.w_per_channel ? mg : 0;
+                wz = p.q.w_u8 ? int(static_cast<const unsigned char *>(p.q.w_zp)[qi]) - 128
+                              : int(static_cast<const signed char *>(p.q.w_zp)[qi]);
+                unsigned sw = 0;
+                for (int t0 = t0_first; t0 < t0_end; ++t0)
+                    for (int t1 = 0; t1 < nt1; ++t1)
+                        for (int t2 = 0; t2 < nt2; ++t2) {
+                            const int tflat = ((k00 + t0 * ks0) * p.K[1] + (k01 + t1 * ks1)) * p.K[2] + (k02 + t2 * ks2);
+                            sw += unsigned(p.q.wsum[(size_t(g) * p.T + tflat) * p.Mgp + m]);
+                        }
+                unsigned c = p.q.bias ? unsigned(p.q.bias[mg]) : 0u;
+                c -= unsigned(p.q.x_zp) * sw;
+                c += unsigned(p.q.x_zp) * unsigned(wz) * unsigned(p.Cg) * taps_it;
+                comp = __builtin_bit_cast(int, c);
+                mult = requant_mult(p.q.x_scale, p.q.w_scale[qi], p.q.y_scale);
+            }
+            sq_comp[mm] = comp;
+            sq_mult[mm] = mult;
+            sq_wz[mm] = wz;
+            nz |= wz != 0;
+        }
+        need_sx = __syncthreads_or(nz);
+    } else {
+        for (int mm = tid; mm < BMM; mm += kThreads) {
+            const int m = mt * BMM + mm;
+            sbias[mm] = (bias && m < p.Mg) ? float(bias[g * p.Mg + m]) : 0.0f;
+        }
     }
 
     // ---------------- main loop ----------------
@@ -427,7 +516,7 @@ __global__ __launch_bounds__(kThreads, OCC) void igemm_kernel(const _Float16 *x,
         StepIdx cur = {0, t0_first, 0, 0};
         {
             const unsigned v0 = load_halo(0, t0_first, hreg);
-            store_halo(hreg, v0);
+            store_halo(hreg, v0, 0);
         }
         load_w(cur, wreg);
         store_w(0, wreg);
@@ -488,7 +577,12 @@ __global__ __launch_bounds__(kThreads, OCC) void igemm_kernel(const _Float16 *x,
                 for (int i = 0; i < WM; ++i)
 #pragma unroll
                     for (int j = 0; j < WN; ++j)
-                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[cb][i], b[cb][j], acc[i][j], 0, 0, 0);
+                        if constexpr (Q8)
+                            acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(__builtin_bit_cast(i32x4, a[cb][i]),
+                                                                             __builtin_bit_cast(i32x4, b[cb][j]),
+                                                                             acc[i][j], 0, 0, 0);
+                        else
+                            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[cb][i], b[cb][j], acc[i][j], 0, 0, 0);
                 __builtin_amdgcn_sched_barrier(0);
             }
         };
@@ -533,7 +627,7 @@ __global__ __launch_bounds__(kThreads, OCC) void igemm_kernel(const _Float16 *x,
                 g4_step(std::integral_constant<int, 2>{});
                 g4_step(std::integral_constant<int, 3>{});
                 if (has_ng) {  // the next group's halo, between two barriers
-                    store_halo(hreg, hv);
+                    store_halo(hreg, hv, hch);
                     __syncthreads();
                 }
                 grp = ng;
@@ -542,6 +636,7 @@ __global__ __launch_bounds__(kThreads, OCC) void igemm_kernel(const _Float16 *x,
             StepIdx nxt = cur;
             advance(nxt);
             unsigned hvalid = 0;
+            int hchunk = 0;  // channel chunk of the halo held in registers
             for (int s = 0; s < nsteps; ++s) {
                 const bool group_first = cur.t1 == 0 && cur.t2 == 0;
                 const bool group_last = cur.t1 == nt1 - 1 && cur.t2 == nt2 - 1;
@@ -554,14 +649,17 @@ __global__ __launch_bounds__(kThreads, OCC) void igemm_kernel(const _Float16 *x,
                     ng.t1 = nt1 - 1;
                     ng.t2 = nt2 - 1;
                     advance(ng);
-                    if (ng.chunk < p.nchunk) hvalid = load_halo(ng.chunk, ng.t0, hreg);
+                    if (ng.chunk < p.nchunk) {
+                        hvalid = load_halo(ng.chunk, ng.t0, hreg);
+                        hchunk = ng.chunk;
+                    }
                 }
                 // issue the prefetch loads here, ahead of the MFMAs (no later sinking)
                 asm volatile("" ::: "memory");
                 mma_step(cur, s & 1, [] {}, [] {}, [&] { store_w((s + 1) & 1, wreg); });
                 __syncthreads();
                 if (group_last && s + 1 < nsteps) {  // refresh the halo between two barriers
-                    store_halo(hreg, hvalid);
+                    store_halo(hreg, hvalid, hchunk);
                     __syncthreads();
                 }
                 cur = nxt;
@@ -705,7 +803,77 @@ __global__ __launch_bounds__(kThreads, OCC) void igemm_kernel(const _Float16 *x,
             }
         }
     };
-    with_activation(p.act, output_stage);
+    if constexpr (Q8) {
+        // ---------------- quantized epilogue: compensation, requantization, store ----------------
+        // (the staged per-channel values were made visible by the staging's own barrier)
+        const int O1 = p.O[1], O2 = p.O[2];
+        const size_t opix = size_t(p.O[0]) * O1 * O2;
+        const int o0 = r0 + p.s[0] * j0;
+        const int npix = tl.q1 - tl.q0;
+        const int mvalid = min(BM, p.Mg - mt * BM);
+        const int mrow = wm * WM * 32;
+        unsigned char *const yb = reinterpret_cast<unsigned char *>(y);
+        const bool vec = (p.M % 4 == 0) && ((g * p.Mg + mt * BM) % 4 == 0) && (reinterpret_cast<uintptr_t>(y) % 4 == 0);
+        unsigned char *yp[WN];
+        unsigned sx[WN];  // sum of the iterated shifted inputs of the lane's pixels
+#pragma unroll
+        for (int j = 0; j < WN; ++j) {
+            const int pl = min((wn * WN + j) * 32 + (lane & 31), npix - 1);
+            const int q = tl.q0 + pl;
+            const int row = tl.seg ? tl.row_lo : q / J2;
+            const int col = q - row * J2;
+            yp[j] = yb + ((size_t(n) * opix + (size_t(o0) * O1 + (r1 + p.s[1] * row)) * O2 + (r2 + p.s[2] * col)) * p.M +
+                          g * p.Mg + mt * BM);
+            unsigned acc_s = 0;
+            if (need_sx) {
+                for (int t0 = t0_first; t0 < t0_end; ++t0) {
+                    const int i0 = j0 + b00 - t0 * bs0;
+                    for (int t1 = 0; t1 < nt1; ++t1) {
+                        const int i1 = row + p.tb0[1][r1] - t1 * bs1;
+                        for (int t2 = 0; t2 < nt2; ++t2) {
+                            const int i2 = col + p.tb0[2][r2] - t2 * bs2;
+                            const bool inside = i1 >= 0 && i1 < L1 && i2 >= 0 && i2 < L2;
+                            acc_s += inside ? unsigned(p.q.xsum[(((size_t(n) * p.G + g) * L0 + i0) * L1 + i1) * L2 + i2])
+                                            : unsigned(p.Cg) * unsigned(p.q.x_zp);
+                        }
+                    }
+                }
+            }
+            sx[j] = acc_s;
+        }
+#pragma unroll
+        for (int i = 0; i < WM; ++i)
+#pragma unroll
+            for (int rg = 0; rg < 4; ++rg) {
+                const int ml = mrow + i * 32 + rg * 8 + (lane >> 5) * 4;  // 4 consecutive channels
+                const i32x4 cp = *reinterpret_cast<const i32x4 *>(&sq_comp[ml]);
+                const i32x4 wz = *reinterpret_cast<const i32x4 *>(&sq_wz[ml]);
+                float mult[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) mult[e] = sq_mult[ml + e];
+#pragma unroll
+                for (int j = 0; j < WN; ++j) {
+                    if ((wn * WN + j) * 32 + (lane & 31) >= npix) continue;
+                    unsigned packed = 0;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const unsigned a = unsigned(acc[i][j][rg * 4 + e]) + unsigned(cp[e]) - unsigned(wz[e]) * sx[j];
+                        const int code = requantize(a, mult[e], p.q.y_zp, p.q.y_lo, p.q.y_hi);
+                        packed |= (unsigned(code) & 0xffu) << (8 * e);
+                    }
+                    if (vec && ml + 4 <= mvalid) {
+                        *reinterpret_cast<unsigned *>(yp[j] + ml) = packed;
+                    } else {
+#pragma unroll
+                        for (int e = 0; e < 4; ++e)
+                            if (ml + e < mvalid) yp[j][ml + e] = (unsigned char)(packed >> (8 * e));
+                    }
+                }
+            }
+    } else {
+        (void)need_sx;
+        with_activation(p.act, output_stage);
+    }
 }
 
 // Wp[g][t][m][c] = W[g*Cg + c][m][t], zero outside c < Cg, m < Mg.  One thread writes
@@ -742,6 +910,72 @@ __global__ __launch_bounds__(256) void pack_w_kernel(const _Float16 *__restrict_
     *reinterpret_cast<u32x4 *>(dst) = o;
 }
 
+// Quantized weights: Wp[g][t][m][c] = w[g*Cg + c][m][t] in the signed domain (uint8
+// values XOR 0x80), zero outside c < Cg, m < Mg; one thread writes 16 consecutive c.
+struct PackQArgs {
+    int G, Cg, Mg, Cgp, Mgp, T, w_u8;
+    long long total;  // G * (Cgp/16) * Mgp * T
+};
+
+__global__ __launch_bounds__(256) void pack_wq_kernel(const unsigned char *__restrict__ w, signed char *__restrict__ wp,
+                                                      PackQArgs a)
+{
+    const long long u = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+    if (u >= a.total) return;
+    const int t = int(u % a.T);
+    long long rest = u / a.T;
+    const int m = int(rest % a.Mgp);
+    rest /= a.Mgp;
+    const int cv = int(rest % (a.Cgp / 16));
+    const int g = int(rest / (a.Cgp / 16));
+    const unsigned flip = a.w_u8 ? 0x80u : 0u;
+    u32x4 o = {0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+        const int c = cv * 16 + k;
+        const unsigned e = (c < a.Cg && m < a.Mg) ? (unsigned(w[((size_t(g) * a.Cg + c) * a.Mg + m) * a.T + t]) ^ flip) : 0u;
+        o[k >> 2] |= e << (8 * (k & 3));
+    }
+    *reinterpret_cast<u32x4 *>(wp + ((size_t(g) * a.T + t) * a.Mgp + m) * a.Cgp + cv * 16) = o;
+}
+
+// wsum[g][t][m] = sum over c of Wp[g][t][m][c] (signed bytes).
+__global__ __launch_bounds__(256) void wsum_kernel(const signed char *__restrict__ wp, int *__restrict__ wsum,
+                                                   long long rows, int Cgp)
+{
+    const long long r = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+    if (r >= rows) return;
+    const u32x4 *src = reinterpret_cast<const u32x4 *>(wp + size_t(r) * Cgp);
+    int sum = 0;
+    for (int v = 0; v < Cgp / 16; ++v) {
+        const u32x4 q = src[v];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) sum = __builtin_amdgcn_sdot4(int(q[k]), 0x01010101, sum, false);
+    }
+    wsum[r] = sum;
+}
+
+// xsum[n][g][pixel] = sum over the group's channels of x in the signed domain
+// (channels-last x: the channels of a pixel are contiguous).
+__global__ __launch_bounds__(256) void xsum_kernel(const unsigned char *__restrict__ x, int *__restrict__ xsum,
+                                                   long long total, int G, int Cg, long long pixels, unsigned flip)
+{
+    const long long u = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+    if (u >= total) return;  // u = (n * G + g) * pixels + pixel
+    const long long pix = u % pixels;
+    const long long ng = u / pixels;
+    const int g = int(ng % G);
+    const long long n = ng / G;
+    const u32x4 *src = reinterpret_cast<const u32x4 *>(x + (size_t(n) * pixels + pix) * size_t(G) * Cg + size_t(g) * Cg);
+    int sum = 0;
+    for (int v = 0; v < Cg / 16; ++v) {
+        const u32x4 q = src[v];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) sum = __builtin_amdgcn_sdot4(int(q[k] ^ flip), 0x01010101, sum, false);
+    }
+    xsum[u] = sum;
+}
+
 // ---------------- host-side planning ----------------
 struct Config {
     int waves_m, wm, wn, cc, nch_items, nhwc_vecs, occ;
@@ -749,7 +983,7 @@ struct Config {
     int bn() const { return (4 / waves_m) * wn * 32; }
     int row() const { return cc * 2 + 16; }
     int chunks() const { return cc / 8; }
-    int halo_bytes() const { return lds_budget(occ) - 2 * bm() * row() - kSinkBytes - kBiasBytes; }
+    int halo_bytes(bool q8 = false) const { return lds_budget(occ) - 2 * bm() * row() - kSinkBytes - tail_bytes(q8); }
     bool operator==(const Config &o) const
     {
         return waves_m == o.waves_m && wm == o.wm && wn == o.wn && cc == o.cc && nch_items == o.nch_items &&
@@ -777,7 +1011,8 @@ struct Plan {
     size_t ws_bytes;
 };
 
-bool make_plan_cfg(const Geom &g, bool cl, const Config &cfg, Plan *pl, std::string *why)
+// q8: the quantized instances (int8 elements, CC * 2 channels per step).
+bool make_plan_cfg(const Geom &g, bool cl, const Config &cfg, Plan *pl, std::string *why, bool q8 = false)
 {
     auto no = [&](const char *m) {
         *why = m;
@@ -815,13 +1050,14 @@ bool make_plan_cfg(const Geom &g, bool cl, const Config &cfg, Plan *pl, std::str
     a.Cg = int(g.Cg);
     a.Mg = int(g.Mg);
     a.T = int(g.taps());
-    a.nchunk = int((g.Cg + cfg.cc - 1) / cfg.cc);
-    a.Cgp = a.nchunk * cfg.cc;
+    const int cch = q8 ? 2 * cfg.cc : cfg.cc;  // channels per step
+    a.nchunk = int((g.Cg + cch - 1) / cch);
+    a.Cgp = a.nchunk * cch;
     // Column-phase pairs: channels-first output, stride 2 on the innermost axis, an even
     // output width (both phases then have the same pixel grid), equal tap counts and input
     // rows of whole 16-byte vectors.
-    const bool pair = !cl && cfg.waves_m == 2 && g.s[2] == 2 && g.O[2] % 2 == 0 && a.ntap[2][0] == a.ntap[2][1] &&
-                      g.L[2] % 8 == 0;
+    const bool pair = !q8 && !cl && cfg.waves_m == 2 && g.s[2] == 2 && g.O[2] % 2 == 0 &&
+                      a.ntap[2][0] == a.ntap[2][1] && g.L[2] % 8 == 0;
     const int BMM = pair ? cfg.bm() / 2 : cfg.bm();
     a.mtiles = int((g.Mg + BMM - 1) / BMM);
     a.Mgp = a.mtiles * BMM;
@@ -862,7 +1098,7 @@ bool make_plan_cfg(const Geom &g, bool cl, const Config &cfg, Plan *pl, std::str
                 const int rmax = J2 - std::__gcd(BN, J2);
                 const int HR = seg ? 1 + e1 : std::min<int>(J1, (rmax + BN + J2 - 1) / J2) + e1;
                 const int HC = seg ? BN + e2 : J2 + e2;
-                if ((long long)HR * HC * cfg.row() > cfg.halo_bytes()) return no("input halo exceeds LDS");
+                if ((long long)HR * HC * cfg.row() > cfg.halo_bytes(q8)) return no("input halo exceeds LDS");
                 if (cl && (long long)HR * HC * cfg.chunks() > (long long)cfg.nhwc_vecs * kThreads)
                     return no("input halo exceeds the loads of one block");
                 const int nvc = (HC + 7) / 8 + 1;
@@ -887,7 +1123,7 @@ bool make_plan_cfg(const Geom &g, bool cl, const Config &cfg, Plan *pl, std::str
     a.interleave = uniform ? 1 : 0;
     pl->cfg = cfg;
     pl->pair = pair;
-    pl->ws_bytes = size_t(a.G) * a.T * a.Mgp * a.Cgp * sizeof(_Float16);
+    pl->ws_bytes = size_t(a.G) * a.T * a.Mgp * a.Cgp * (q8 ? 1 : sizeof(_Float16));
     return true;
 }
 
@@ -898,10 +1134,19 @@ bool make_plan_cfg(const Geom &g, bool cl, const Config &cfg, Plan *pl, std::str
 constexpr int kNumConfigs = int(sizeof(kConfigs) / sizeof(kConfigs[0]));
 std::atomic<int> g_forced_tile{-1};  // index into kConfigs, or -1: automatic
 
-bool make_plan(const Geom &g, bool cl, Plan *pl, std::string *why)
+// tiles with quantized (int8) instances
+bool has_q8(const Config &c) { return c == kWide || c == kHalf || c == kSmall; }
+
+bool make_plan(const Geom &g, bool cl, Plan *pl, std::string *why, bool q8 = false)
 {
     const int forced = g_forced_tile.load(std::memory_order_relaxed);
-    if (forced >= 0) return make_plan_cfg(g, cl, kConfigs[forced], pl, why);
+    if (forced >= 0) {
+        if (q8 && !has_q8(kConfigs[forced])) {
+            *why = "the forced tile has no int8 instance";
+            return false;
+        }
+        return make_plan_cfg(g, cl, kConfigs[forced], pl, why, q8);
+    }
     constexpr int kCUs = 256;
     constexpr int kN = kNumConfigs;
     Plan cand[kN];
@@ -909,7 +1154,8 @@ bool make_plan(const Geom &g, bool cl, Plan *pl, std::string *why)
     double waste[kN], best_waste = 1e30;
     for (int i = 0; i < kN; ++i) {
         std::string w;
-        ok[i] = make_plan_cfg(g, cl, kConfigs[i], &cand[i], &w);
+        ok[i] = (!q8 || has_q8(kConfigs[i])) && make_plan_cfg(g, cl, kConfigs[i], &cand[i], &w, q8);
+        if (q8 && !has_q8(kConfigs[i])) w = "no int8 instance";
         if (!ok[i]) {
             if (i == 0 || why->empty()) *why = w;
             continue;
@@ -932,11 +1178,11 @@ bool make_plan(const Geom &g, bool cl, Plan *pl, std::string *why)
 }
 
 template <bool CL, int WAVES_M, int WM, int WN, int CC, int NCH_ITEMS, int NHWC_VECS, int OCC, bool PAIR = false,
-          bool ROWS8 = true>
+          bool ROWS8 = true, bool Q8 = false>
 void launch_cfg(const IgArgs &a, const _Float16 *x, const _Float16 *wp, const _Float16 *b, _Float16 *y,
                 hipStream_t st)
 {
-    hipLaunchKernelGGL((igemm_kernel<CL, WAVES_M, WM, WN, CC, NCH_ITEMS, NHWC_VECS, OCC, PAIR, ROWS8>), dim3(unsigned(a.nblocks)),
+    hipLaunchKernelGGL((igemm_kernel<CL, WAVES_M, WM, WN, CC, NCH_ITEMS, NHWC_VECS, OCC, PAIR, ROWS8, Q8>), dim3(unsigned(a.nblocks)),
                        dim3(kThreads), 0, st, x, wp, b, y, a);
 }
 
@@ -957,6 +1203,17 @@ bool launch_config(const Config &c, const Plan &pl, bool cl, const _Float16 *x, 
         launch_cfg<false, WAVES_M, WM, WN, CC, NCH_ITEMS, NHWC_VECS, OCC, true>(pl.a, x, wp, b, y, st);
     else
         return false;
+    return true;
+}
+
+// The int8 (quantized, channels-last) instance of one configuration.
+template <int WAVES_M, int WM, int WN, int CC, int NCH_ITEMS, int NHWC_VECS, int OCC>
+bool launch_config_q8(const Config &c, const Plan &pl, const void *x, const void *wp, void *y, hipStream_t st)
+{
+    if (!(c == Config{WAVES_M, WM, WN, CC, NCH_ITEMS, NHWC_VECS, OCC})) return false;
+    launch_cfg<true, WAVES_M, WM, WN, CC, NCH_ITEMS, NHWC_VECS, OCC, false, true, true>(
+        pl.a, static_cast<const _Float16 *>(x), static_cast<const _Float16 *>(wp), nullptr, static_cast<_Float16 *>(y),
+        st);
     return true;
 }
 
@@ -1055,6 +1312,122 @@ ct_status launch_igemm(const Geom &g, ct_dtype dt, bool cl, const void *x, const
     }
     if (e != hipSuccess) {
         *err = std::string("implicit-GEMM launch failed: ") + hipGetErrorString(e);
+        return CT_EDEVICE;
+    }
+    return CT_OK;
+}
+
+}  // namespace ct
+
+namespace ct {
+
+// Largest depth (C/group x taps of one phase) whose int8 products cannot overflow the
+// MFMA's int32 accumulator: depth * 128 * 128 < 2^31.
+constexpr int64_t kMaxQ8Depth = (int64_t(1) << 31) / (128 * 128) - 1;
+
+bool qigemm_supports(const Geom &g, bool cl, const void *x, std::string *why)
+{
+    if (!cl) {
+        *why = "the int8 implicit GEMM serves channels-last tensors";
+        return false;
+    }
+    if (g.Cg % 16 != 0 || g.C % 16 != 0) {
+        *why = "C/group must be a multiple of 16";
+        return false;
+    }
+    if (reinterpret_cast<uintptr_t>(x) % 16 != 0) {
+        *why = "x must be 16-byte aligned";
+        return false;
+    }
+    int64_t taps = 1;
+    for (int a = 0; a < kAxes; ++a) {
+        int64_t most = 0;
+        for (int r = 0; r < g.s[a]; ++r) {
+            AxisPhase ph;
+            if (!axis_phase(g, a, r, &ph)) {
+                *why = "more than 16 taps per phase";
+                return false;
+            }
+            most = std::max<int64_t>(most, ph.ntaps);
+        }
+        taps *= most;
+    }
+    if (g.Cg * taps > kMaxQ8Depth) {
+        *why = "depth too large for exact int32 accumulation";
+        return false;
+    }
+    Plan pl;
+    return make_plan(g, true, &pl, why, true);
+}
+
+ct_status launch_qigemm(const Geom &g, bool cl, const void *x, const void *w, void *y, const QuantCall &qc,
+                        hipStream_t st, std::string *err)
+{
+    Plan pl;
+    if (!cl || !make_plan(g, true, &pl, err, true)) return CT_EUNSUPPORTED;
+    IgArgs &a = pl.a;
+    // workspace: packed weights, their channel sums, the input's channel sums
+    const size_t wp_bytes = (pl.ws_bytes + 255) / 256 * 256;
+    const size_t wsum_elems = size_t(a.G) * a.T * a.Mgp;
+    const size_t wsum_bytes = (wsum_elems * 4 + 255) / 256 * 256;
+    const long long pixels = (long long)g.in_pixels();
+    const long long xsum_elems = (long long)g.N * g.G * pixels;
+    const size_t total = wp_bytes + wsum_bytes + size_t(std::max<long long>(xsum_elems, 1)) * 4;
+    void *ws = nullptr;
+    hipError_t e = hipMallocAsync(&ws, total, st);
+    if (e != hipSuccess) {
+        *err = std::string("workspace allocation failed: ") + hipGetErrorString(e);
+        return CT_EDEVICE;
+    }
+    signed char *wpk = static_cast<signed char *>(ws);
+    int *wsum = reinterpret_cast<int *>(static_cast<char *>(ws) + wp_bytes);
+    int *xsum = reinterpret_cast<int *>(static_cast<char *>(ws) + wp_bytes + wsum_bytes);
+
+    PackQArgs pa;
+    pa.G = a.G;
+    pa.Cg = a.Cg;
+    pa.Mg = a.Mg;
+    pa.Cgp = a.Cgp;
+    pa.Mgp = a.Mgp;
+    pa.T = a.T;
+    pa.w_u8 = qc.w_type == CT_UINT8;
+    pa.total = (long long)pa.G * (pa.Cgp / 16) * pa.Mgp * pa.T;
+    hipLaunchKernelGGL(pack_wq_kernel, dim3(unsigned((pa.total + 255) / 256)), dim3(256), 0, st,
+                       static_cast<const unsigned char *>(w), wpk, pa);
+    hipLaunchKernelGGL(wsum_kernel, dim3(unsigned((wsum_elems + 255) / 256)), dim3(256), 0, st, wpk, wsum,
+                       (long long)wsum_elems, a.Cgp);
+    const unsigned xflip = qc.x_type == CT_UINT8 ? 0x80808080u : 0u;
+    if (xsum_elems > 0)
+        hipLaunchKernelGGL(xsum_kernel, dim3(unsigned((xsum_elems + 255) / 256)), dim3(256), 0, st,
+                           static_cast<const unsigned char *>(x), xsum, xsum_elems, a.G, a.Cg, pixels, xflip);
+
+    a.q.w_scale = qc.w_scale;
+    a.q.w_zp = qc.w_zp;
+    a.q.bias = qc.bias;
+    a.q.wsum = wsum;
+    a.q.xsum = xsum;
+    a.q.x_scale = qc.x_scale;
+    a.q.y_scale = qc.y_scale;
+    a.q.x_zp = qc.x_type == CT_UINT8 ? qc.x_zp - 128 : qc.x_zp;
+    a.q.y_zp = qc.y_zp;
+    a.q.y_lo = qc.y_type == CT_INT8 ? -128 : 0;
+    a.q.y_hi = qc.y_type == CT_INT8 ? 127 : 255;
+    a.q.xflip = xflip;
+    a.q.w_u8 = qc.w_type == CT_UINT8;
+    a.q.w_per_channel = qc.wq_len == g.M && g.M != 1;
+    a.q.y_u8 = qc.y_type == CT_UINT8;
+    const Config c = pl.cfg;
+    mark_before(st);
+    // (the template arguments repeat the Config constants above)
+    const bool launched = launch_config_q8<2, 4, 4, 64, 2, 14, 1>(c, pl, x, wpk, y, st) ||
+                          launch_config_q8<2, 2, 4, 64, 2, 14, 1>(c, pl, x, wpk, y, st) ||
+                          launch_config_q8<1, 2, 1, 64, 2, 8, 2>(c, pl, x, wpk, y, st);
+    mark_after(st);
+    e = launched ? hipGetLastError() : hipErrorInvalidConfiguration;
+    const hipError_t f = hipFreeAsync(ws, st);
+    if (e == hipSuccess) e = f;
+    if (e != hipSuccess) {
+        *err = std::string("int8 implicit-GEMM launch failed: ") + hipGetErrorString(e);
         return CT_EDEVICE;
     }
     return CT_OK;

@@ -117,6 +117,43 @@ __device__ __forceinline__ void with_activation(const Act &a, F &&f)
     }
 }
 
+// Requantization of the quantized operation (QLinear scheme): the multiplier
+// float(float(x_scale * w_scale) / y_scale) and saturate(round_half_even(float(acc) *
+// mult) + y_zp), each step one IEEE float32 operation (no contraction; '/' is the
+// correctly rounded divide).  acc is the int32 accumulator as its 32-bit pattern.
+__device__ __forceinline__ float requant_mult(float x_scale, float w_scale, float y_scale)
+{
+#pragma clang fp contract(off)
+    const float xw = x_scale * w_scale;
+    return xw / y_scale;
+}
+
+__device__ __forceinline__ int requantize(unsigned acc, float mult, int y_zp, int y_lo, int y_hi)
+{
+#pragma clang fp contract(off)
+    const float v = float(__builtin_bit_cast(int, acc)) * mult;
+    const float r = rintf(v);  // to nearest, ties to even
+    // saturate before converting (r may be far outside the int range)
+    const float lo = float(y_lo - y_zp), hi = float(y_hi - y_zp);
+    const float c = r < lo ? lo : (r > hi ? hi : r);
+    return int(c) + y_zp;
+}
+
+// The quantized operation's parameters (see qlinear_convtranspose_nd).
+struct QuantCall {
+    ct_dtype x_type, w_type, y_type;
+    float x_scale, y_scale;
+    int x_zp, y_zp;
+    const float *w_scale;
+    const void *w_zp;
+    int64_t wq_len;
+    const int *bias;
+};
+// The quantized operation on the int8 MFMA implicit GEMM (channels-last only).
+bool qigemm_supports(const Geom &g, bool cl, const void *x, std::string *why);
+ct_status launch_qigemm(const Geom &g, bool cl, const void *x, const void *w, void *y, const QuantCall &qc,
+                        hipStream_t st, std::string *err);
+
 // Launchers (one per kernel family); each returns CT_OK or CT_EDEVICE (message in err).
 ct_status launch_direct(const Geom &g, ct_dtype dt, bool cl, const void *x, const void *w,
                         const void *bias, void *y, const Act &act, hipStream_t st, std::string *err);

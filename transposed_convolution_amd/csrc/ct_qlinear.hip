@@ -29,25 +29,6 @@ struct QDirectArgs {
     float x_scale, y_scale;
 };
 
-// float(float(x_scale * w_scale) / y_scale) with no contraction of the two steps.
-__device__ __forceinline__ float requant_mult(float x_scale, float w_scale, float y_scale)
-{
-#pragma clang fp contract(off)
-    const float xw = x_scale * w_scale;
-    return xw / y_scale;
-}
-
-__device__ __forceinline__ int requantize(unsigned acc, float mult, int y_zp, int y_lo, int y_hi)
-{
-#pragma clang fp contract(off)
-    const float v = float(__builtin_bit_cast(int, acc)) * mult;
-    const float r = rintf(v);  // to nearest, ties to even
-    // saturate before converting (r may be far outside int range)
-    const float lo = float(y_lo - y_zp), hi = float(y_hi - y_zp);
-    const float c = r < lo ? lo : (r > hi ? hi : r);
-    return int(c) + y_zp;
-}
-
 // One thread per output element (the gather form of the scatter rule, as in the float
 // gather kernel); integer products of zero-point-shifted operands summed in uint32
 // (two's complement wrap-around, i.e. modulo 2^32).
@@ -181,8 +162,8 @@ ct_status qlinear_convtranspose_nd(ct_kernel kernel, int nsp, int channels_last,
     set_last_error(std::string());
     if (!is_q8(x_type) || !is_q8(w_type) || !is_q8(y_type))
         return q_fail(CT_EUNSUPPORTED, "x, w and y types must be CT_UINT8 or CT_INT8");
-    if (kernel != CT_KERNEL_AUTO && kernel != CT_KERNEL_DIRECT)
-        return q_fail(CT_EUNSUPPORTED, "the quantized operation runs on the gather kernel (CT_KERNEL_AUTO or DIRECT)");
+    if (kernel != CT_KERNEL_AUTO && kernel != CT_KERNEL_DIRECT && kernel != CT_KERNEL_IGEMM)
+        return q_fail(CT_EUNSUPPORTED, "the quantized operation runs on the gather or the int8 implicit-GEMM kernel");
     if (channels_last != 0 && channels_last != 1) return q_fail(CT_EINVAL, "channels_last must be 0 or 1");
     if (!std::isfinite(x_scale) || !(x_scale > 0.0f) || !std::isfinite(y_scale) || !(y_scale > 0.0f))
         return q_fail(CT_EINVAL, "x_scale and y_scale must be positive and finite");
@@ -217,6 +198,30 @@ ct_status qlinear_convtranspose_nd(ct_kernel kernel, int nsp, int channels_last,
     if (g.x_elems() > 0 && !x) return q_fail(CT_EINVAL, "x is NULL");
     if (g.w_elems() > 0 && !w) return q_fail(CT_EINVAL, "w is NULL");
 
+    const hipStream_t hs = static_cast<hipStream_t>(stream);
+    const bool cl = channels_last != 0;
+    std::string why;
+    const bool mfma = kernel != CT_KERNEL_DIRECT && g.x_elems() > 0 && qigemm_supports(g, cl, x, &why);
+    if (kernel == CT_KERNEL_IGEMM && !mfma)
+        return q_fail(CT_EUNSUPPORTED, "the int8 implicit-GEMM kernel cannot serve this call: " + why);
+    if (mfma) {
+        QuantCall qc;
+        qc.x_type = x_type;
+        qc.w_type = w_type;
+        qc.y_type = y_type;
+        qc.x_scale = x_scale;
+        qc.y_scale = y_scale;
+        qc.x_zp = x_zero_point;
+        qc.y_zp = y_zero_point;
+        qc.w_scale = w_scale;
+        qc.w_zp = w_zero_point;
+        qc.wq_len = wq_len;
+        qc.bias = reinterpret_cast<const int *>(bias);
+        st = launch_qigemm(g, cl, x, w, y, qc, hs, &err);
+        if (st != CT_OK) return q_fail(st, err);
+        return CT_OK;
+    }
+
     QDirectArgs p;
     p.total = g.y_elems();
     p.N = int(g.N);
@@ -242,8 +247,6 @@ ct_status qlinear_convtranspose_nd(ct_kernel kernel, int nsp, int channels_last,
     p.y_scale = y_scale;
     int64_t blocks = (p.total + 255) / 256;
     if (blocks > (1 << 20)) blocks = 1 << 20;  // grid-stride loop covers the rest
-    const hipStream_t hs = static_cast<hipStream_t>(stream);
-    const bool cl = channels_last != 0;
     const int *bt = reinterpret_cast<const int *>(bias);
     mark_before(hs);
     if (x_type == CT_INT8)

@@ -198,9 +198,10 @@ def make_qinputs(qw: QWorkload) -> dict:
 
 
 # The C4 decoder shapes quantized: uint8 activations (zero point 128), int8 weights with
-# per-channel scales, uint8 output; the scales put the output's spread at about 50 codes.
-F4_C4 = QWorkload("f4_2d_int8_decoder_s2", (8, 512, 64, 64), (512, 256, 4, 4),
+# per-channel scales, uint8 output, channels-last; the scales put the output's spread at
+# about 50 codes.
+F4_C4 = QWorkload("f4_2d_int8_decoder_s2_nhwc", (8, 512, 64, 64), (512, 256, 4, 4),
                   dict(strides=[2, 2], pads=[1, 1, 1, 1], group=1), "uint8", "int8", "uint8",
                   x_scale=0.02, x_zero_point=128, w_scale=0.001, y_scale=0.1, y_zero_point=128,
-                  per_channel=True, bias_max=50000, seed=8)
+                  per_channel=True, bias_max=50000, seed=8, channels_last=True)
 QCONFIGS = {F4_C4.name: F4_C4}
