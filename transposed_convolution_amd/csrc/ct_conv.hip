@@ -267,7 +267,9 @@ ct_status launch_stride1(const CGeom &c, ct_dtype dt, bool cl, const void *x, co
                          void *y, hipStream_t st, std::string *err)
 {
     const Geom g = stride1_as_transposed(c);
-    const size_t esz = dt == CT_FLOAT32 ? 4 : 2;
+    if (dt == CT_FLOAT16)  // the weight re-layout reads the convolution's W directly
+        return launch_igemm(g, dt, cl, x, w, bias, y, Act{}, nullptr, 0, st, err, true);
+    const size_t esz = 4;
     const int64_t wn = c.M * c.Cg * c.taps();
     const size_t ws = igemm_workspace_bytes(g, dt);
     const size_t wbytes = (size_t(wn) * esz + 255) / 256 * 256;
@@ -278,14 +280,8 @@ ct_status launch_stride1(const CGeom &c, ct_dtype dt, bool cl, const void *x, co
         return CT_EDEVICE;
     }
     const unsigned blocks = unsigned((wn + 255) / 256);
-    if (dt == CT_FLOAT16)
-        hipLaunchKernelGGL(conv_w_to_transposed<_Float16>, dim3(blocks), dim3(256), 0, st,
-                           static_cast<const _Float16 *>(w), static_cast<_Float16 *>(buf), wn, int(c.Cg),
-                           int(c.Mg), int(c.K[0]), int(c.K[1]), int(c.K[2]));
-    else
-        hipLaunchKernelGGL(conv_w_to_transposed<float>, dim3(blocks), dim3(256), 0, st, static_cast<const float *>(w),
-                           static_cast<float *>(buf), wn, int(c.Cg), int(c.Mg), int(c.K[0]), int(c.K[1]),
-                           int(c.K[2]));
+    hipLaunchKernelGGL(conv_w_to_transposed<float>, dim3(blocks), dim3(256), 0, st, static_cast<const float *>(w),
+                       static_cast<float *>(buf), wn, int(c.Cg), int(c.Mg), int(c.K[0]), int(c.K[1]), int(c.K[2]));
     ct_status s = launch_igemm(g, dt, cl, x, buf, bias, y, Act{}, ws ? static_cast<char *>(buf) + wbytes : nullptr,
                                ws, st, err);
     e = hipFreeAsync(buf, st);

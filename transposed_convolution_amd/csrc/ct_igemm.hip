@@ -878,9 +878,11 @@ __global__ __launch_bounds__(kThreads, OCC) void igemm_kernel(const _Float16 *x,
 
 // Wp[g][t][m][c] = W[g*Cg + c][m][t], zero outside c < Cg, m < Mg.  One thread writes
 // 8 consecutive c (16 bytes); consecutive threads take consecutive taps so that the
-// 8 strided reads of W are coalesced across the wave.
+// 8 strided reads of W are coalesced across the wave.  conv: W is a forward
+// convolution's weight (M, C/group, k) whose stride-1 adjoint this call computes, read
+// with its taps reversed: Wp[g][t][m][c] = Wconv[g*Mg + m][c][T-1-t].
 struct PackArgs {
-    int G, Cg, Mg, Cgp, Mgp, T;
+    int G, Cg, Mg, Cgp, Mgp, T, conv;
     long long total;  // G * (Cgp/8) * Mgp * T
 };
 
@@ -899,8 +901,9 @@ __global__ __launch_bounds__(256) void pack_w_kernel(const _Float16 *__restrict_
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
         const int c = cv * 8 + k;
-        const _Float16 e =
-            (c < a.Cg && m < a.Mg) ? w[((size_t(g) * a.Cg + c) * a.Mg + m) * a.T + t] : _Float16(0.0f);
+        const size_t src = a.conv ? ((size_t(g) * a.Mg + m) * a.Cg + c) * a.T + (a.T - 1 - t)
+                                  : ((size_t(g) * a.Cg + c) * a.Mg + m) * a.T + t;
+        const _Float16 e = (c < a.Cg && m < a.Mg) ? w[src] : _Float16(0.0f);
         v[k] = __builtin_bit_cast(unsigned short, e);
     }
     _Float16 *dst = wp + ((size_t(g) * a.T + t) * a.Mgp + m) * a.Cgp + cv * 8;
@@ -939,27 +942,37 @@ __global__ __launch_bounds__(256) void pack_wq_kernel(const unsigned char *__res
     *reinterpret_cast<u32x4 *>(wp + ((size_t(g) * a.T + t) * a.Mgp + m) * a.Cgp + cv * 16) = o;
 }
 
-// wsum[g][t][m] = sum over c of Wp[g][t][m][c] (signed bytes).
+// wsum[g][t][m] = sum over c of Wp[g][t][m][c] (signed bytes); one wave per row.
 __global__ __launch_bounds__(256) void wsum_kernel(const signed char *__restrict__ wp, int *__restrict__ wsum,
                                                    long long rows, int Cgp)
 {
-    const long long r = (long long)blockIdx.x * blockDim.x + threadIdx.x;
-    if (r >= rows) return;
+    const long long r = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+    if (r >= rows) return;  // the whole wave
     const u32x4 *src = reinterpret_cast<const u32x4 *>(wp + size_t(r) * Cgp);
     int sum = 0;
-    for (int v = 0; v < Cgp / 16; ++v) {
+    for (int v = lane; v < Cgp / 16; v += 64) {
         const u32x4 q = src[v];
 #pragma unroll
         for (int k = 0; k < 4; ++k) sum = __builtin_amdgcn_sdot4(int(q[k]), 0x01010101, sum, false);
     }
-    wsum[r] = sum;
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) sum += __shfl_xor(sum, off);
+    if (lane == 0) wsum[r] = sum;
 }
 
 // xsum[n][g][pixel] = sum over the group's channels of x in the signed domain
-// (channels-last x: the channels of a pixel are contiguous).
+// (channels-last x: the channels of a pixel are contiguous).  Only the per-pixel
+// correction of non-zero weight zero points reads it: when every weight zero point is 0
+// in the signed domain, every block returns at once.
 __global__ __launch_bounds__(256) void xsum_kernel(const unsigned char *__restrict__ x, int *__restrict__ xsum,
-                                                   long long total, int G, int Cg, long long pixels, unsigned flip)
+                                                   long long total, int G, int Cg, long long pixels, unsigned flip,
+                                                   const unsigned char *__restrict__ w_zp, int wq_len, int w_u8)
 {
+    int nz = 0;
+    for (int i = threadIdx.x; i < wq_len; i += blockDim.x)
+        nz |= (w_u8 ? int(w_zp[i]) - 128 : int((signed char)w_zp[i])) != 0;
+    if (!__syncthreads_or(nz)) return;
     const long long u = (long long)blockIdx.x * blockDim.x + threadIdx.x;
     if (u >= total) return;  // u = (n * G + g) * pixels + pixel
     const long long pix = u % pixels;
@@ -1263,7 +1276,8 @@ void igemm_force_tile(int tile) { g_forced_tile.store(tile, std::memory_order_re
 int igemm_forced_tile() { return g_forced_tile.load(std::memory_order_relaxed); }
 
 ct_status launch_igemm(const Geom &g, ct_dtype dt, bool cl, const void *x, const void *w, const void *bias,
-                       void *y, const Act &act, void *workspace, size_t ws_bytes, hipStream_t st, std::string *err)
+                       void *y, const Act &act, void *workspace, size_t ws_bytes, hipStream_t st, std::string *err,
+                       bool w_conv)
 {
     if (dt == CT_FLOAT32) return launch_igemm32(g, cl, x, w, bias, y, act, st, err);
     Plan pl;
@@ -1289,6 +1303,7 @@ ct_status launch_igemm(const Geom &g, ct_dtype dt, bool cl, const void *x, const
     pa.Cgp = pl.a.Cgp;
     pa.Mgp = pl.a.Mgp;
     pa.T = pl.a.T;
+    pa.conv = w_conv ? 1 : 0;
     pa.total = (long long)pa.G * (pa.Cgp / 8) * pa.Mgp * pa.T;
     const _Float16 *wt = static_cast<const _Float16 *>(w);
     _Float16 *wpk = static_cast<_Float16 *>(wsp);
@@ -1394,12 +1409,13 @@ ct_status launch_qigemm(const Geom &g, bool cl, const void *x, const void *w, vo
     pa.total = (long long)pa.G * (pa.Cgp / 16) * pa.Mgp * pa.T;
     hipLaunchKernelGGL(pack_wq_kernel, dim3(unsigned((pa.total + 255) / 256)), dim3(256), 0, st,
                        static_cast<const unsigned char *>(w), wpk, pa);
-    hipLaunchKernelGGL(wsum_kernel, dim3(unsigned((wsum_elems + 255) / 256)), dim3(256), 0, st, wpk, wsum,
+    hipLaunchKernelGGL(wsum_kernel, dim3(unsigned((wsum_elems + 3) / 4)), dim3(256), 0, st, wpk, wsum,
                        (long long)wsum_elems, a.Cgp);
     const unsigned xflip = qc.x_type == CT_UINT8 ? 0x80808080u : 0u;
     if (xsum_elems > 0)
         hipLaunchKernelGGL(xsum_kernel, dim3(unsigned((xsum_elems + 255) / 256)), dim3(256), 0, st,
-                           static_cast<const unsigned char *>(x), xsum, xsum_elems, a.G, a.Cg, pixels, xflip);
+                           static_cast<const unsigned char *>(x), xsum, xsum_elems, a.G, a.Cg, pixels, xflip,
+                           static_cast<const unsigned char *>(qc.w_zp), int(qc.wq_len), qc.w_type == CT_UINT8 ? 1 : 0);
 
     a.q.w_scale = qc.w_scale;
     a.q.w_zp = qc.w_zp;

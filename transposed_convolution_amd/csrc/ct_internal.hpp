@@ -177,9 +177,11 @@ bool igemm32_supports(const Geom &g, bool cl, std::string *why);
 ct_status launch_igemm32(const Geom &g, bool cl, const void *x, const void *w, const void *bias, void *y,
                          const Act &act, hipStream_t st, std::string *err);
 // workspace: caller scratch of ws_bytes (>= igemm_workspace_bytes), or NULL to take
-// stream-ordered scratch with hipMallocAsync / hipFreeAsync on st.
+// stream-ordered scratch with hipMallocAsync / hipFreeAsync on st.  w_conv (float16
+// only): w is a forward convolution's weight (M, C/group, k) and g the stride-1
+// transposed convolution that equals that convolution; it is read with reversed taps.
 ct_status launch_igemm(const Geom &g, ct_dtype dt, bool cl, const void *x, const void *w,
                        const void *bias, void *y, const Act &act, void *workspace, size_t ws_bytes,
-                       hipStream_t st, std::string *err);
+                       hipStream_t st, std::string *err, bool w_conv = false);
 
 }  // namespace ct
