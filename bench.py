@@ -56,7 +56,7 @@ def workloads():
             # the forward convolution with the same W (the adjoint) of a configuration
             "adj_c5_s1": W.C5_S1, "adj_c4": W.C4,
             # the quantized (QLinear scheme) decoder shapes
-            "f4_int8": W.F4_C4}
+            "f4_int8": W.F4_C4, "f4_int8_nchw": W.F4_C4.with_(name="f4_2d_int8_decoder_s2", channels_last=False)}
 
 
 def source_digest(kernel: str) -> str:
@@ -260,7 +260,7 @@ def bench_quant(args):
     tx = torch.from_numpy(q["x"]).to(dev)
     if qw.channels_last:
         tx = T.to_channels_last(tx)
-    kernel = "igemm" if qw.channels_last else "direct"  # forced: a call the kernel cannot serve fails
+    kernel = "igemm"  # forced: a call the kernel cannot serve fails
     tw = torch.from_numpy(q["w"]).to(dev)
     ws = torch.from_numpy(q["w_scale"]).to(dev)
     wz = torch.from_numpy(q["w_zero_point"]).to(dev)
@@ -278,11 +278,16 @@ def bench_quant(args):
         raise SystemExit(f"quantized output disagrees with the oracle in {int((got != ref).sum())} codes")
     macs = T.convtranspose_useful_macs(qw.x_shape, qw.w_shape, **qw.attrs)
     # the oracle timed on the whole first image (every channel)
-    sub = dict(q, x=q["x"][:1])
-    sub_macs = T.convtranspose_useful_macs((1,) + qw.x_shape[1:], qw.w_shape, **qw.attrs)
-    t0 = time.perf_counter()
-    O.qconvtranspose(**sub, **qw.attrs)
-    cpu_dt = time.perf_counter() - t0
+    cpu = None
+    if not args.no_cpu_baseline:
+        sub = dict(q, x=q["x"][:1])
+        sub_macs = T.convtranspose_useful_macs((1,) + qw.x_shape[1:], qw.w_shape, **qw.attrs)
+        t0 = time.perf_counter()
+        O.qconvtranspose(**sub, **qw.attrs)
+        cpu_dt = time.perf_counter() - t0
+        cpu = {"value": round(2.0 * sub_macs / cpu_dt / 1e12, 6), "unit": "TOP/s", "cores": O.threads(),
+               "kind": "oracle", "sample": f"image 0 of {qw.x_shape[0]}, every channel ({sub_macs / 1e9:.2f} GMAC, "
+                                           f"{cpu_dt:.1f} s)"}
     lib = T.load_library()
     for _ in range(args.warmup):
         T.qlinear_convtranspose_nd(**call, out=y)
@@ -312,9 +317,7 @@ def bench_quant(args):
         "roofline": {"bound": "mfma" if kernel == "igemm" else "alu", "achieved": round(achieved, 3), "peak": peak,
                      "unit": "TOP/s",
                      "frac": round(achieved / peak, 5), "traffic": None, "kernel_us": round(k_avg * 1e3, 2)},
-        "cpu_baseline": {"value": round(2.0 * sub_macs / cpu_dt / 1e12, 6), "unit": "TOP/s", "cores": O.threads(),
-                         "kind": "oracle", "sample": f"image 0 of {qw.x_shape[0]}, every channel ({sub_macs / 1e9:.2f} GMAC, "
-                                                     f"{cpu_dt:.1f} s)"}}), flush=True)
+        "cpu_baseline": cpu}), flush=True)
 
 
 def main():
@@ -350,7 +353,7 @@ def main():
 
     if args.workload.startswith("adj_"):
         return bench_adjoint(args)
-    if args.workload == "f4_int8":
+    if args.workload.startswith("f4_int8"):
         return bench_quant(args)
     wl = workloads()[args.workload]
     dev = torch.device("cuda:0")

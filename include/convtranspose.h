@@ -280,8 +280,11 @@ ct_status convolution_nd(ct_kernel kernel, ct_dtype dtype, int nsp, int channels
  * (each step one IEEE float32 operation), rounding half to even, saturation to the range
  * of y's type, and the int32 accumulator wrapping modulo 2^32.
  *
- *   kernel          CT_KERNEL_AUTO or CT_KERNEL_DIRECT (the gather kernel serves every
- *                   call); any other family fails with CT_EUNSUPPORTED
+ *   kernel          CT_KERNEL_AUTO (the int8 MFMA implicit GEMM when it serves the call:
+ *                   C/group a multiple of 16 and C/group x taps of a phase below 2^17;
+ *                   otherwise the gather kernel), CT_KERNEL_DIRECT (the gather kernel,
+ *                   every call) or CT_KERNEL_IGEMM (CT_EUNSUPPORTED when it cannot serve);
+ *                   other families fail with CT_EUNSUPPORTED
  *   x, x_type       device tensor of CT_UINT8 or CT_INT8, logical shape x_shape =
  *                   {N, C, D1..Dn}, layout as in convtranspose_nd (channels_last)
  *   x_scale, x_zero_point   per-tensor parameters of x (host values); x_scale must be
@@ -299,7 +302,9 @@ ct_status convolution_nd(ct_kernel kernel, ct_dtype dtype, int nsp, int channels
  *                   and finite, y_zero_point inside y_type's range
  *   attributes and stream   as convtranspose_nd
  * Validation happens before anything is enqueued; errors leave y untouched.  The caller
- * owns every buffer; nothing is allocated.
+ * owns every buffer; the MFMA path takes stream-ordered scratch (hipMallocAsync /
+ * hipFreeAsync on stream) for the packed weights, their channel sums, the input's channel
+ * sums and, for channels-first tensors, channels-last copies of x and y.
  */
 ct_status qlinear_convtranspose_nd(ct_kernel kernel, int nsp, int channels_last, const void *x, ct_dtype x_type,
                                    const int64_t *x_shape, float x_scale, int32_t x_zero_point, const void *w,

@@ -757,12 +757,14 @@ Q8_CASES = [
 ]
 
 
+@pytest.mark.parametrize("cl", [True, False], ids=["cl", "nc"])
 @pytest.mark.parametrize("tile", [None, "256x256", "128x256", "64x128"])
-def test_qlinear_int8_mfma(T, tile):
-    """The int8 MFMA implicit GEMM (channels-last) on whole outputs, every uint8/int8
-    combination: symmetric weights (no input-sum correction) and arbitrary zero points
-    (per-channel weight zero points exercise the per-pixel input sums)."""
-    rng = np.random.default_rng(900 + (0 if tile is None else T.IGEMM_TILES.index(tile) + 1))
+def test_qlinear_int8_mfma(T, tile, cl):
+    """The int8 MFMA implicit GEMM on whole outputs, every uint8/int8 combination:
+    symmetric weights (no input-sum correction) and arbitrary zero points (per-channel
+    weight zero points exercise the per-pixel input sums); channels-first tensors go
+    through the layout transposes."""
+    rng = np.random.default_rng(900 + (0 if tile is None else T.IGEMM_TILES.index(tile) + 1) + 10 * (not cl))
     ran = 0
     for ci, (xs, ws, attrs) in enumerate(Q8_CASES):
         for general in (False, True):
@@ -781,9 +783,9 @@ def test_qlinear_int8_mfma(T, tile):
                                w_zero_point=w_zp, y_scale=np.float32(0.0004 * np.sqrt(depth) * 74 * 74 / 50),
                                y_zero_point=int(rng.integers(*pins.QT[ty])), y_type=ty,
                                bias=rng.integers(-50000, 50001, size=M) if ci % 3 else None), tx, tw)
-            _log(f"[case] int8 mfma tile {tile} #{ci} general={general} x{xs}:{tx} w{ws}:{tw} y:{ty} {attrs}")
+            _log(f"[case] int8 mfma tile {tile} cl={cl} #{ci} general={general} x{xs}:{tx} w{ws}:{tw} y:{ty} {attrs}")
             with forced_tile(T, tile):
-                got = qgpu_run(T, q, attrs, cl=True, kernel="igemm")
+                got = qgpu_run(T, q, attrs, cl=cl, kernel="igemm")
             if got is None:
                 continue
             ran += 1

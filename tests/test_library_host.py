@@ -281,7 +281,7 @@ def test_qlinear_validation_launches_nothing(T):
 
     assert call(xt=1) == 3 and "CT_UINT8 or CT_INT8" in T.convtranspose_last_error()
     assert call(yt=0) == 3
-    assert call(kernel=3) == 3                                     # no MFMA path for the quantized op
+    assert call(kernel=3) == 3                                     # C = 4: the int8 MFMA kernel needs 16
     assert call(x_scale=0.0) == 1 and call(x_scale=float("inf")) == 1 and call(y_scale=-1.0) == 1
     assert call(x_zp=256) == 1 and call(xt=I8, x_zp=128) == 1 and call(yt=I8, y_zp=-129) == 1
     assert call(wq=3) == 1 and "length 1 or M" in T.convtranspose_last_error()

@@ -1340,17 +1340,51 @@ namespace ct {
 // MFMA's int32 accumulator: depth * 128 * 128 < 2^31.
 constexpr int64_t kMaxQ8Depth = (int64_t(1) << 31) / (128 * 128) - 1;
 
+// Byte transpose of a batch of [rows][cols] matrices into [cols][rows] (channels-first
+// <-> channels-last for 8-bit tensors), through a 64 x 64 LDS tile per block.
+__global__ __launch_bounds__(256) void transpose8_kernel(const unsigned char *__restrict__ src,
+                                                         unsigned char *__restrict__ dst, long long rows,
+                                                         long long cols)
+{
+    __shared__ unsigned char tile[64][65];
+    const long long r0 = (long long)blockIdx.y * 64, c0 = (long long)blockIdx.x * 64;
+    const size_t base = size_t(blockIdx.z) * size_t(rows) * size_t(cols);
+    const int t = threadIdx.x;
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {  // 64 rows x 64 columns, consecutive threads on consecutive columns
+        const int e = t + k * 256, rr = e / 64, cc = e % 64;
+        if (r0 + rr < rows && c0 + cc < cols) tile[rr][cc] = src[base + size_t(r0 + rr) * cols + c0 + cc];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+        const int e = t + k * 256, cc = e / 64, rr = e % 64;
+        if (r0 + rr < rows && c0 + cc < cols) dst[base + size_t(c0 + cc) * rows + r0 + rr] = tile[rr][cc];
+    }
+}
+
+void transpose8(const void *src, void *dst, long long batch, long long rows, long long cols, hipStream_t st)
+{
+    if (batch * rows * cols == 0) return;
+    const dim3 grid(unsigned((cols + 63) / 64), unsigned((rows + 63) / 64), unsigned(batch));
+    hipLaunchKernelGGL(transpose8_kernel, grid, dim3(256), 0, st, static_cast<const unsigned char *>(src),
+                       static_cast<unsigned char *>(dst), rows, cols);
+}
+
+// Channels-first calls run the channels-last kernel between two transposes (x in, y out)
+// through scratch.
 bool qigemm_supports(const Geom &g, bool cl, const void *x, std::string *why)
 {
-    if (!cl) {
-        *why = "the int8 implicit GEMM serves channels-last tensors";
+    // the transposes' grids: (pixels or M) / 64 x (C or output pixels) / 64 x N
+    if (!cl && ((g.C + 63) / 64 > 65535 || (g.out_pixels() + 63) / 64 > 65535 || g.N > 65535)) {
+        *why = "too large for the layout transposes";
         return false;
     }
     if (g.Cg % 16 != 0 || g.C % 16 != 0) {
         *why = "C/group must be a multiple of 16";
         return false;
     }
-    if (reinterpret_cast<uintptr_t>(x) % 16 != 0) {
+    if (cl && reinterpret_cast<uintptr_t>(x) % 16 != 0) {
         *why = "x must be 16-byte aligned";
         return false;
     }
@@ -1375,19 +1409,24 @@ bool qigemm_supports(const Geom &g, bool cl, const void *x, std::string *why)
     return make_plan(g, true, &pl, why, true);
 }
 
+
 ct_status launch_qigemm(const Geom &g, bool cl, const void *x, const void *w, void *y, const QuantCall &qc,
                         hipStream_t st, std::string *err)
 {
     Plan pl;
-    if (!cl || !make_plan(g, true, &pl, err, true)) return CT_EUNSUPPORTED;
+    if (!make_plan(g, true, &pl, err, true)) return CT_EUNSUPPORTED;
     IgArgs &a = pl.a;
-    // workspace: packed weights, their channel sums, the input's channel sums
+    // workspace: packed weights, their channel sums, the input's channel sums; for
+    // channels-first calls also x and y in channels-last order
     const size_t wp_bytes = (pl.ws_bytes + 255) / 256 * 256;
     const size_t wsum_elems = size_t(a.G) * a.T * a.Mgp;
     const size_t wsum_bytes = (wsum_elems * 4 + 255) / 256 * 256;
     const long long pixels = (long long)g.in_pixels();
     const long long xsum_elems = (long long)g.N * g.G * pixels;
-    const size_t total = wp_bytes + wsum_bytes + size_t(std::max<long long>(xsum_elems, 1)) * 4;
+    const size_t xsum_bytes = (size_t(std::max<long long>(xsum_elems, 1)) * 4 + 255) / 256 * 256;
+    const size_t xt_bytes = cl ? 0 : (size_t(g.x_elems()) + 255) / 256 * 256;
+    const size_t yt_bytes = cl ? 0 : (size_t(g.y_elems()) + 255) / 256 * 256;
+    const size_t total = wp_bytes + wsum_bytes + xsum_bytes + xt_bytes + yt_bytes;
     void *ws = nullptr;
     hipError_t e = hipMallocAsync(&ws, total, st);
     if (e != hipSuccess) {
@@ -1397,6 +1436,13 @@ ct_status launch_qigemm(const Geom &g, bool cl, const void *x, const void *w, vo
     signed char *wpk = static_cast<signed char *>(ws);
     int *wsum = reinterpret_cast<int *>(static_cast<char *>(ws) + wp_bytes);
     int *xsum = reinterpret_cast<int *>(static_cast<char *>(ws) + wp_bytes + wsum_bytes);
+    void *const y_final = y;
+    if (!cl) {  // x (N, C, pixels) -> (N, pixels, C); the kernel writes y as (N, pixels, M)
+        char *xt = static_cast<char *>(ws) + wp_bytes + wsum_bytes + xsum_bytes;
+        transpose8(x, xt, g.N, g.C, pixels, st);
+        x = xt;
+        y = xt + xt_bytes;
+    }
 
     PackQArgs pa;
     pa.G = a.G;
@@ -1439,6 +1485,7 @@ ct_status launch_qigemm(const Geom &g, bool cl, const void *x, const void *w, vo
                           launch_config_q8<2, 2, 4, 64, 2, 14, 1>(c, pl, x, wpk, y, st) ||
                           launch_config_q8<1, 2, 1, 64, 2, 8, 2>(c, pl, x, wpk, y, st);
     mark_after(st);
+    if (!cl) transpose8(y, y_final, g.N, g.out_pixels(), g.M, st);
     e = launched ? hipGetLastError() : hipErrorInvalidConfiguration;
     const hipError_t f = hipFreeAsync(ws, st);
     if (e == hipSuccess) e = f;
