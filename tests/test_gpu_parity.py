@@ -558,6 +558,57 @@ def test_convolution_stride1_mfma(T, case, cl, integer):
         check(got, ref, "f16", integer, f"conv s1 {kernel} x{xs} w{ws} {attrs}")
 
 
+CONV_STRIDED = [
+    # (x_shape, w_shape, attrs): strided, dilation 1, on the MFMA path through the input
+    # phases taken as channels (C/group x stride product >= 16, M/group >= 16); kernels
+    # shorter, equal to and longer than the stride, odd phase-copy widths, SAME, groups
+    ((2, 16, 16, 30), (48, 16, 4, 4), dict(strides=[2, 2], pads=[1, 1, 1, 1])),      # the C4 adjoint's form
+    ((1, 8, 13, 20), (32, 8, 3, 3), dict(strides=[2, 2], pads=[1, 0, 1, 2])),
+    ((1, 16, 9, 24), (40, 16, 5, 3), dict(strides=[3, 2], auto_pad="SAME_UPPER")),
+    ((2, 32, 40), (24, 32, 2), dict(strides=[2])),                                    # K = s: one tap per phase
+    ((1, 8, 6, 10, 12), (32, 8, 3, 3, 3), dict(strides=[2, 2, 2], pads=[1] * 6)),
+    ((2, 32, 12, 12), (32, 16, 4, 4), dict(strides=[2, 2], pads=[1] * 4, group=2)),
+]
+
+
+@pytest.mark.parametrize("integer", [False, True], ids=["float", "int"])
+@pytest.mark.parametrize("cl", [False, True], ids=["nc", "cl"])
+@pytest.mark.parametrize("case", CONV_STRIDED, ids=lambda c: f"{c[0]}_{c[1]}")
+def test_convolution_strided_mfma(T, case, cl, integer):
+    xs, ws, attrs = case
+    if cl and xs[1] % 8:
+        pytest.skip("channels-last MFMA path needs C % 8 == 0")
+    rng = np.random.default_rng(zlib.crc32(repr(case).encode()) + 2 * cl + integer + 7)
+    gen = (lambda sz: rng.integers(-2, 3, size=sz)) if integer else (lambda sz: rng.normal(size=sz))
+    x = gen(xs).astype(np.float16)
+    w = (gen(ws) * (1 if integer else 0.1)).astype(np.float16)
+    b = gen(ws[0]).astype(np.float16)
+    _log(f"[case] conv strided x{xs} w{ws} {attrs} cl={cl} integer={integer}")
+    ref = O.conv(x, w, b, **attrs)
+    for kernel in ("igemm", "auto"):
+        got = conv_gpu_run(T, x, w, b, attrs, cl, kernel)
+        check(got, ref, "f16", integer, f"conv strided {kernel} x{xs} w{ws} {attrs}")
+
+
+def test_convolution_adjoint_of_c4_sampled(T):
+    """The adjoint of the C4 configuration at full size (stride 2, pads 1, MFMA path
+    through the input phases): whole output planes of several (image, channel) pairs
+    against the oracle run on that image and channel."""
+    wl = W.C4
+    _, w, _ = W.make_inputs(wl)
+    ys, pads = O.output_shape(wl.x_shape, wl.w_shape, **wl.attrs)
+    rng = np.random.default_rng(404)
+    a = rng.normal(size=ys).astype(np.float16)
+    b = rng.normal(size=wl.w_shape[0]).astype(np.float16)
+    attrs = dict(strides=[2, 2], pads=list(pads))
+    _log(f"[case] conv adjoint of C4: x{ys} w{wl.w_shape} {attrs}")
+    got = conv_gpu_run(T, a, w, b, attrs, False, "igemm")
+    assert got.shape == tuple(wl.x_shape)
+    for n, m in ((0, 0), (7, 511), (3, 200), (5, 17)):
+        ref = O.conv(a[n:n + 1], w[m:m + 1], b[m:m + 1], **attrs)
+        check(got[n:n + 1, m:m + 1], ref, "f16", False, f"C4 adjoint plane ({n}, {m})")
+
+
 def test_convolution_is_the_adjoint(T):
     """<ConvT_W(x), y> = <x, Conv_W(y)> with both operators on the GPU (float32 inputs,
     float64 sums on the host), for the transposed convolution's attributes."""

@@ -12,10 +12,15 @@
 // (LOWER).  With the transposed convolution's strides, dilations and begin pads and end
 // pads e - output_padding this is its adjoint: <ConvT_W(x), y> = <x, Conv_W(y)>.
 //
-// Two paths:
+// Paths:
 //   * stride 1 on every axis: the same correlation is a stride-1 transposed convolution
 //     with W re-laid out as (C, M/group, k) and its taps reversed, begin pads
 //     d(K-1) - b and end pads d(K-1) - e, so it runs on the MFMA implicit GEMM;
+//   * stride s > 1 with dilation 1: split every tap k = s*k' + rho; input phase rho of
+//     the zero-padded input, xs_rho[j] = X[s*j + rho - b], is read at j = o + k', so
+//       Y[o] = sum over rho, k' of xs_rho[o + k'] W[s*k' + rho]
+//     is a stride-1 correlation over s^n times the channels with ceil(K/s) taps (the
+//     input phases become channels, "space to depth"); it runs on the path above;
 //   * otherwise (and wherever the MFMA kernel does not serve the shape): a gather
 //     kernel, one thread per output element, float32 accumulation.
 #include <hip/hip_runtime.h>
@@ -274,7 +279,7 @@ ct_status launch_stride1(const CGeom &c, ct_dtype dt, bool cl, const void *x, co
     const size_t ws = igemm_workspace_bytes(g, dt);
     const size_t wbytes = (size_t(wn) * esz + 255) / 256 * 256;
     void *buf = nullptr;
-    hipError_t e = hipMallocAsync(&buf, wbytes + ws, st);
+    hipError_t e = scratch_malloc(&buf, wbytes + ws, st);
     if (e != hipSuccess) {
         *err = std::string("scratch allocation failed: ") + hipGetErrorString(e);
         return CT_EDEVICE;
@@ -284,6 +289,168 @@ ct_status launch_stride1(const CGeom &c, ct_dtype dt, bool cl, const void *x, co
                        static_cast<float *>(buf), wn, int(c.Cg), int(c.Mg), int(c.K[0]), int(c.K[1]), int(c.K[2]));
     ct_status s = launch_igemm(g, dt, cl, x, buf, bias, y, Act{}, ws ? static_cast<char *>(buf) + wbytes : nullptr,
                                ws, st, err);
+    e = hipFreeAsync(buf, st);
+    if (s == CT_OK && e != hipSuccess) {
+        *err = std::string("scratch release failed: ") + hipGetErrorString(e);
+        s = CT_EDEVICE;
+    }
+    return s;
+}
+
+// The stride-1 problem a strided, dilation-1 convolution becomes when its input phases
+// are taken as channels: C' = C * P (P = product of the strides), K' = ceil(K / s),
+// L' = O + K' - 1, no pads.  even_rows: the innermost L' is rounded up to an even size
+// (the channels-first MFMA loads take whole 4-byte column pairs) and the extra column
+// cropped by an end pad of -1.
+CGeom s2d_geom(const CGeom &c, bool even_rows)
+{
+    CGeom q = c;
+    int64_t P = 1;
+    for (int a = 0; a < kAxes; ++a) P *= c.s[a];
+    q.C = c.C * P;
+    q.Cg = c.Cg * P;
+    for (int a = 0; a < kAxes; ++a) {
+        q.K[a] = (c.K[a] + c.s[a] - 1) / c.s[a];
+        q.L[a] = c.O[a] + q.K[a] - 1;
+        q.s[a] = 1;
+        q.d[a] = 1;
+        q.b[a] = q.e[a] = 0;
+    }
+    if (even_rows && q.L[kAxes - 1] % 2 != 0) {
+        q.L[kAxes - 1] += 1;
+        q.e[kAxes - 1] = -1;
+    }
+    return q;
+}
+
+struct S2dArgs {
+    int64_t total;  // elements of xs
+    int C, P;
+    int L[kAxes], s[kAxes], b[kAxes], J[kAxes];
+};
+
+// xs[n][c * P + rho][j] = X[n][c][s * j + rho - b] (0 outside X); rho is the flattened
+// per-axis phase (rho0 * s1 + rho1) * s2 + rho2.  Channels-last tensors keep their
+// layout: xs[n][j][c * P + rho].  One thread makes 8 consecutive elements of xs (along
+// the innermost axis, or along the channels for channels-last); 32-bit indices (the
+// plan keeps xs below 2^31 elements).
+template <typename T, bool CL>
+__global__ __launch_bounds__(256) void s2d_kernel(const T *__restrict__ x, T *__restrict__ xs, S2dArgs p)
+{
+    const int Cp = p.C * p.P;
+    const int inner = CL ? Cp : p.J[2];  // the run a thread's 8 elements lie in
+    const int g8 = (inner + 7) / 8;
+    const int rows = int(p.total / inner);
+    const int u = int(blockIdx.x) * int(blockDim.x) + int(threadIdx.x);
+    if (u >= rows * g8) return;
+    int row = u / g8;
+    const int e0 = (u - row * g8) * 8;
+    const int in_pix = p.L[0] * p.L[1] * p.L[2];
+    int n, cp = 0, j0, j1, j2 = 0;
+    if (CL) {  // row = ((n * J0 + j0) * J1 + j1) * J2 + j2
+        j2 = row % p.J[2];
+        row /= p.J[2];
+        j1 = row % p.J[1];
+        row /= p.J[1];
+        j0 = row % p.J[0];
+        n = row / p.J[0];
+    } else {   // row = ((n * Cp + cp) * J0 + j0) * J1 + j1
+        j1 = row % p.J[1];
+        row /= p.J[1];
+        j0 = row % p.J[0];
+        row /= p.J[0];
+        cp = row % Cp;
+        n = row / Cp;
+    }
+    T *const dst = xs + size_t(u / g8) * inner;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        const int k = e0 + e;  // j2 (channels-first) or cp (channels-last)
+        if (k >= inner) break;
+        const int cpe = CL ? k : cp, j2e = CL ? j2 : k;
+        const int c = cpe / p.P, rho = cpe - c * p.P;
+        const int r2 = rho % p.s[2], r1 = (rho / p.s[2]) % p.s[1], r0 = rho / (p.s[2] * p.s[1]);
+        const int i0 = p.s[0] * j0 + r0 - p.b[0], i1 = p.s[1] * j1 + r1 - p.b[1], i2 = p.s[2] * j2e + r2 - p.b[2];
+        T v = T(0);
+        if (i0 >= 0 && i0 < p.L[0] && i1 >= 0 && i1 < p.L[1] && i2 >= 0 && i2 < p.L[2]) {
+            const int ipix = (i0 * p.L[1] + i1) * p.L[2] + i2;
+            v = CL ? x[(size_t(n) * in_pix + ipix) * p.C + c] : x[(size_t(n) * p.C + c) * in_pix + ipix];
+        }
+        dst[k] = v;
+    }
+}
+
+// W'[m][cc * P + rho][k'] = W[m][cc][s * k' + rho] (0 where s * k' + rho >= K).
+template <typename T>
+__global__ __launch_bounds__(256) void s2d_w_kernel(const T *__restrict__ w, T *__restrict__ wq, int64_t total,
+                                                    int Cg, int P, S2dArgs p, int K0, int K1, int K2, int Q0, int Q1,
+                                                    int Q2)
+{
+    const int64_t u = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
+    if (u >= total) return;
+    const int qt = Q0 * Q1 * Q2;
+    const int kq = int(u % qt);
+    int64_t r = u / qt;
+    const int cp = int(r % (int64_t(Cg) * P));
+    const int64_t m = r / (int64_t(Cg) * P);
+    const int cc = cp / P, rho = cp - cc * P;
+    const int r2 = rho % p.s[2], r1 = (rho / p.s[2]) % p.s[1], r0 = rho / (p.s[2] * p.s[1]);
+    const int q2 = kq % Q2, q1 = (kq / Q2) % Q1, q0 = kq / (Q1 * Q2);
+    const int k0 = p.s[0] * q0 + r0, k1 = p.s[1] * q1 + r1, k2 = p.s[2] * q2 + r2;
+    wq[u] = (k0 < K0 && k1 < K1 && k2 < K2) ? w[((m * Cg + cc) * K0 + k0) * K1 * K2 + int64_t(k1) * K2 + k2] : T(0);
+}
+
+ct_status launch_s2d(const CGeom &c, ct_dtype dt, bool cl, const void *x, const void *w, const void *bias, void *y,
+                     hipStream_t st, std::string *err)
+{
+    const CGeom q = s2d_geom(c, !cl);
+    const size_t esz = dt == CT_FLOAT32 ? 4 : 2;
+    S2dArgs p;
+    p.C = int(c.C);
+    p.P = int(q.C / c.C);
+    for (int a = 0; a < kAxes; ++a) {
+        p.L[a] = int(c.L[a]);
+        p.s[a] = int(c.s[a]);
+        p.b[a] = int(c.b[a]);
+        p.J[a] = int(q.L[a]);
+    }
+    p.total = q.N * q.C * q.in_pixels();
+    const int64_t wn = q.M * q.Cg * q.taps();
+    const size_t xs_bytes = (size_t(p.total) * esz + 255) / 256 * 256;
+    const size_t wq_bytes = (size_t(wn) * esz + 255) / 256 * 256;
+    void *buf = nullptr;
+    hipError_t e = scratch_malloc(&buf, xs_bytes + wq_bytes, st);
+    if (e != hipSuccess) {
+        *err = std::string("scratch allocation failed: ") + hipGetErrorString(e);
+        return CT_EDEVICE;
+    }
+    void *xs = buf;
+    void *wq = static_cast<char *>(buf) + xs_bytes;
+    const int64_t inner = cl ? q.C : q.L[kAxes - 1];
+    const int64_t threads = inner > 0 ? p.total / inner * ((inner + 7) / 8) : 0;
+    const unsigned bx = unsigned((threads + 255) / 256), bw = unsigned((wn + 255) / 256);
+    const int K0 = int(c.K[0]), K1 = int(c.K[1]), K2 = int(c.K[2]);
+    const int Q0 = int(q.K[0]), Q1 = int(q.K[1]), Q2 = int(q.K[2]);
+    if (dt == CT_FLOAT16) {
+        using T = _Float16;
+        if (p.total > 0) {
+            if (cl) hipLaunchKernelGGL((s2d_kernel<T, true>), dim3(bx), dim3(256), 0, st, static_cast<const T *>(x), static_cast<T *>(xs), p);
+            else hipLaunchKernelGGL((s2d_kernel<T, false>), dim3(bx), dim3(256), 0, st, static_cast<const T *>(x), static_cast<T *>(xs), p);
+        }
+        if (wn > 0)
+            hipLaunchKernelGGL(s2d_w_kernel<T>, dim3(bw), dim3(256), 0, st, static_cast<const T *>(w), static_cast<T *>(wq),
+                               wn, int(c.Cg), p.P, p, K0, K1, K2, Q0, Q1, Q2);
+    } else {
+        using T = float;
+        if (p.total > 0) {
+            if (cl) hipLaunchKernelGGL((s2d_kernel<T, true>), dim3(bx), dim3(256), 0, st, static_cast<const T *>(x), static_cast<T *>(xs), p);
+            else hipLaunchKernelGGL((s2d_kernel<T, false>), dim3(bx), dim3(256), 0, st, static_cast<const T *>(x), static_cast<T *>(xs), p);
+        }
+        if (wn > 0)
+            hipLaunchKernelGGL(s2d_w_kernel<T>, dim3(bw), dim3(256), 0, st, static_cast<const T *>(w), static_cast<T *>(wq),
+                               wn, int(c.Cg), p.P, p, K0, K1, K2, Q0, Q1, Q2);
+    }
+    ct_status s = launch_stride1(q, dt, cl, xs, wq, bias, y, st, err);
     e = hipFreeAsync(buf, st);
     if (s == CT_OK && e != hipSuccess) {
         *err = std::string("scratch release failed: ") + hipGetErrorString(e);
@@ -313,12 +480,30 @@ Attrs conv_attrs(ct_auto_pad auto_pad, const int64_t *strides, const int64_t *di
     return at;
 }
 
-// Which path convolution_nd takes (CT_KERNEL_IGEMM: the stride-1 MFMA path).
-ct_kernel conv_choose(const CGeom &c, ct_dtype dt, bool cl, const void *x, ct_kernel want, std::string *why)
+// Which path convolution_nd takes (CT_KERNEL_IGEMM: the MFMA path, stride 1 directly or
+// a strided convolution through its input phases, *s2d).
+ct_kernel conv_choose(const CGeom &c, ct_dtype dt, bool cl, const void *x, ct_kernel want, std::string *why,
+                      bool *s2d)
 {
-    bool s1 = true;
-    for (int a = 0; a < kAxes; ++a) s1 = s1 && c.s[a] == 1;
-    const bool fast = s1 && c.Cg >= 16 && c.Mg >= 16 && igemm_supports(stride1_as_transposed(c), dt, cl, x, why);
+    bool s1 = true, d1 = true;
+    for (int a = 0; a < kAxes; ++a) {
+        s1 = s1 && c.s[a] == 1;
+        d1 = d1 && c.d[a] == 1;
+    }
+    bool fast = false;
+    *s2d = false;
+    if (s1) {
+        fast = c.Cg >= 16 && c.Mg >= 16 && igemm_supports(stride1_as_transposed(c), dt, cl, x, why);
+    } else if (d1 && c.out_pixels() > 0) {
+        const CGeom q = s2d_geom(c, !cl);
+        // the phase copy is 256-byte aligned scratch, so x's own alignment does not matter
+        fast = q.N * q.C * q.in_pixels() < (int64_t(1) << 31) && c.N * c.C * c.in_pixels() < (int64_t(1) << 31) &&
+               q.Cg >= 16 && c.Mg >= 16 &&
+               igemm_supports(stride1_as_transposed(q), dt, cl, reinterpret_cast<const void *>(256), why);
+        *s2d = fast;
+    } else {
+        *why = "strided convolutions with dilation > 1 run on the gather kernel";
+    }
     if (want == CT_KERNEL_DIRECT) return CT_KERNEL_DIRECT;
     if (want == CT_KERNEL_IGEMM) return fast ? CT_KERNEL_IGEMM : CT_KERNEL_NONE;
     return fast ? CT_KERNEL_IGEMM : CT_KERNEL_DIRECT;
@@ -385,12 +570,15 @@ ct_status convolution_nd(ct_kernel kernel, ct_dtype dtype, int nsp, int channels
     if (g.M * g.Cg * g.taps() > 0 && !w) return ct::conv_fail(CT_EINVAL, "w is NULL");
     const bool cl = channels_last != 0;
     std::string why;
-    const ct_kernel k = ct::conv_choose(g, dtype, cl, x, kernel, &why);
+    bool s2d = false;
+    const ct_kernel k = ct::conv_choose(g, dtype, cl, x, kernel, &why, &s2d);
     if (k == CT_KERNEL_NONE)
-        return ct::conv_fail(CT_EUNSUPPORTED, "the implicit-GEMM path serves stride-1 convolutions only" +
+        return ct::conv_fail(CT_EUNSUPPORTED, "the implicit-GEMM path cannot serve this convolution" +
                                                   (why.empty() ? std::string() : ": " + why));
     const hipStream_t hs = static_cast<hipStream_t>(stream);
-    if (k == CT_KERNEL_IGEMM)
+    if (k == CT_KERNEL_IGEMM && s2d)
+        st = ct::launch_s2d(g, dtype, cl, x, w, bias, y, hs, &err);
+    else if (k == CT_KERNEL_IGEMM)
         st = ct::launch_stride1(g, dtype, cl, x, w, bias, y, hs, &err);
     else if (dtype == CT_FLOAT16)
         st = ct::launch_direct_t<_Float16>(g, cl, x, w, bias, y, hs, &err);

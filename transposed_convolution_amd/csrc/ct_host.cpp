@@ -9,6 +9,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cstring>
+#include <atomic>
 #include <cmath>
 #include <string>
 
@@ -158,6 +159,22 @@ bool axis_phase(const Geom &g, int a, int r, AxisPhase *ph)
         ++ph->ntaps;
     }
     return true;
+}
+
+hipError_t scratch_malloc(void **p, size_t bytes, hipStream_t st)
+{
+    static std::atomic<bool> pool_set[64];
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev >= 0 && dev < 64 && !pool_set[dev].exchange(true)) {
+        hipMemPool_t pool;
+        if (hipDeviceGetDefaultMemPool(&pool, dev) == hipSuccess) {
+            uint64_t keep = UINT64_MAX;
+            (void)hipMemPoolSetAttribute(pool, hipMemPoolAttrReleaseThreshold, &keep);
+        }
+    }
+    return hipMallocAsync(p, bytes, st);
 }
 
 ProfileEvents &profile_events()

@@ -1286,7 +1286,7 @@ ct_status launch_igemm(const Geom &g, ct_dtype dt, bool cl, const void *x, const
     bool owned = false;
     void *wsp = workspace;
     if (!wsp) {
-        hipError_t e = hipMallocAsync(&wsp, pl.ws_bytes, st);
+        hipError_t e = scratch_malloc(&wsp, pl.ws_bytes, st);
         if (e != hipSuccess) {
             *err = std::string("workspace allocation failed: ") + hipGetErrorString(e);
             return CT_EDEVICE;
@@ -1428,7 +1428,7 @@ ct_status launch_qigemm(const Geom &g, bool cl, const void *x, const void *w, vo
     const size_t yt_bytes = cl ? 0 : (size_t(g.y_elems()) + 255) / 256 * 256;
     const size_t total = wp_bytes + wsum_bytes + xsum_bytes + xt_bytes + yt_bytes;
     void *ws = nullptr;
-    hipError_t e = hipMallocAsync(&ws, total, st);
+    hipError_t e = scratch_malloc(&ws, total, st);
     if (e != hipSuccess) {
         *err = std::string("workspace allocation failed: ") + hipGetErrorString(e);
         return CT_EDEVICE;

@@ -60,6 +60,11 @@ struct AxisPhase {
 // Fills phase r of axis a; returns false when the phase has more than kMaxPhaseTaps taps.
 bool axis_phase(const Geom &g, int a, int r, AxisPhase *ph);
 
+// Stream-ordered scratch (hipMallocAsync on st).  The first call on a device raises the
+// release threshold of the device's default memory pool, so freed scratch stays in the
+// pool for the next call instead of being unmapped and mapped again.
+hipError_t scratch_malloc(void **p, size_t bytes, hipStream_t st);
+
 // The per-thread error text convtranspose_last_error() returns.
 void set_last_error(const std::string &msg);
 
