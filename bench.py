@@ -215,14 +215,15 @@ def bench_adjoint(args):
     if not err <= 2e-3:
         raise SystemExit(f"adjoint output disagrees with the oracle: max rel err {err:.3e}")
     log(f"adjoint of {base.name}: y{ys} -> x{base.x_shape}, {attrs}, {macs / 1e9:.2f} GMAC, parity {err:.2e}")
+    call = T.PreparedCall(T.convolution_nd, ta, tw, tb, out=out, kernel="igemm", **attrs)
     for _ in range(args.warmup):
-        T.convolution_nd(ta, tw, tb, out=out, kernel="igemm", **attrs)
+        call()
     torch.cuda.synchronize()
     evs = KernelEvents(args.steps)
     t0 = time.perf_counter()
     for i in range(args.steps):
         evs.arm(lib, i)
-        T.convolution_nd(ta, tw, tb, out=out, kernel="igemm", **attrs)
+        call()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     lib.convtranspose_profile_events(None, None)
@@ -290,14 +291,15 @@ def bench_quant(args):
                "kind": "oracle", "sample": f"image 0 of {qw.x_shape[0]}, every channel ({sub_macs / 1e9:.2f} GMAC, "
                                            f"{cpu_dt:.1f} s)"}
     lib = T.load_library()
+    prepared = T.PreparedCall(T.qlinear_convtranspose_nd, **call, out=y)
     for _ in range(args.warmup):
-        T.qlinear_convtranspose_nd(**call, out=y)
+        prepared()
     torch.cuda.synchronize()
     evs = KernelEvents(args.steps)
     t0 = time.perf_counter()
     for i in range(args.steps):
         evs.arm(lib, i)
-        T.qlinear_convtranspose_nd(**call, out=y)
+        prepared()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     lib.convtranspose_profile_events(None, None)

@@ -845,3 +845,29 @@ def test_qlinear_int8_mfma(T, tile, cl):
             assert bad.size == 0, f"int8 mfma #{ci}: {bad.size} of {got.size} codes differ, first at " \
                                   f"{np.unravel_index(bad[0], got.shape)}: {got.flat[bad[0]]} vs {ref.flat[bad[0]]}"
     assert ran >= len(Q8_CASES), f"the int8 kernel served only {ran} cases"
+
+
+def test_prepared_calls_repeat_the_direct_call(T):
+    """PreparedCall (arguments marshalled once) gives, call after call, exactly what the
+    direct call gives, for the forward convolution and the quantized operation."""
+    dev = torch.device("cuda:0")
+    rng = np.random.default_rng(31)
+    a = torch.from_numpy(rng.normal(size=(2, 16, 10, 16)).astype(np.float16)).to(dev)
+    w = torch.from_numpy((rng.normal(size=(48, 16, 4, 4)) * 0.1).astype(np.float16)).to(dev)
+    b = torch.from_numpy(rng.normal(size=48).astype(np.float16)).to(dev)
+    attrs = dict(strides=[2, 2], pads=[1, 1, 1, 1])
+    want = T.convolution_nd(a, w, b, **attrs).clone()
+    call = T.PreparedCall(T.convolution_nd, a, w, b, **attrs)
+    for _ in range(3):
+        assert torch.equal(call(), want)
+    qw = W.F4_C4.with_(x_shape=(1, 32, 6, 8), w_shape=(32, 24, 4, 4))
+    q = W.make_qinputs(qw)
+    args = dict(x=torch.from_numpy(q["x"]).to(dev), x_scale=float(q["x_scale"]), x_zero_point=int(q["x_zero_point"]),
+                w=torch.from_numpy(q["w"]).to(dev), w_scale=torch.from_numpy(q["w_scale"]).to(dev),
+                w_zero_point=torch.from_numpy(q["w_zero_point"]).to(dev), y_scale=float(q["y_scale"]),
+                y_zero_point=int(q["y_zero_point"]), y_dtype=torch.uint8, bias=torch.from_numpy(q["bias"]).to(dev))
+    want = T.qlinear_convtranspose_nd(**args, **qw.attrs).clone()
+    call = T.PreparedCall(T.qlinear_convtranspose_nd, **args, **qw.attrs)
+    for _ in range(3):
+        assert torch.equal(call(), want)
+    torch.cuda.synchronize()

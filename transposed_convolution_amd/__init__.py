@@ -24,7 +24,7 @@ __all__ = [
     "convtranspose_useful_macs", "convtranspose_select_kernel", "convtranspose_last_error",
     "convtranspose_kernel_name", "library_path", "load_library", "channels_last_empty",
     "to_channels_last", "KERNELS", "ACTIVATIONS", "convolution_nd", "convolution_output_shape",
-    "IGEMM_TILES", "set_igemm_tile", "igemm_tile", "qlinear_convtranspose_nd",
+    "IGEMM_TILES", "set_igemm_tile", "igemm_tile", "qlinear_convtranspose_nd", "PreparedCall",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -407,10 +407,11 @@ def convolution_output_shape(x_shape, w_shape, **attrs) -> Tuple[Tuple[int, ...]
 def convolution_nd(x: torch.Tensor, w: torch.Tensor, bias: Optional[torch.Tensor] = None, *,
                    auto_pad: str = "NOTSET", strides=None, dilations=None, pads=None, kernel_shape=None,
                    group: int = 1, channels_last: bool = False, out: Optional[torch.Tensor] = None,
-                   kernel: str = "auto", stream: Optional[torch.cuda.Stream] = None) -> torch.Tensor:
+                   kernel: str = "auto", stream: Optional[torch.cuda.Stream] = None,
+                   _prepare_only: bool = False) -> torch.Tensor:
     """Y = Conv(X, W, bias) on the GPU (ONNX Conv; W is (M, C/group, k1..kn)), the adjoint of
     ``convtranspose_nd`` with the same W.  ``kernel``: "auto", "direct" or "igemm" (the
-    stride-1 MFMA path)."""
+    MFMA path: stride 1, or strided with dilation 1 through the input phases)."""
     lib = load_library()
     if x.dtype not in _DTYPES:
         raise ConvTransposeError(3, f"dtype {x.dtype} is not served (float32, float16)")
@@ -440,10 +441,12 @@ def convolution_nd(x: torch.Tensor, w: torch.Tensor, bias: Optional[torch.Tensor
     stream = stream if stream is not None else torch.cuda.current_stream(dev)
     nsp = x.dim() - 2
     ptr = lambda t: ctypes.c_void_p(t.data_ptr()) if t is not None else None  # noqa: E731
+    args = (KERNELS[kernel], _DTYPES[x.dtype], nsp, int(channels_last), ptr(x), _i64(x.shape), ptr(w), _i64(w.shape),
+            ptr(bias), ptr(out), _i64(yshape), *_conv_attr_args(nsp, **attrs), ctypes.c_void_p(stream.cuda_stream))
+    if _prepare_only:
+        return lib.convolution_nd, args, out
     with torch.cuda.device(dev):
-        st = lib.convolution_nd(KERNELS[kernel], _DTYPES[x.dtype], nsp, int(channels_last), ptr(x), _i64(x.shape),
-                                ptr(w), _i64(w.shape), ptr(bias), ptr(out), _i64(yshape),
-                                *_conv_attr_args(nsp, **attrs), ctypes.c_void_p(stream.cuda_stream))
+        st = lib.convolution_nd(*args)
     if st:
         _raise(st)
     return out
@@ -458,7 +461,7 @@ def qlinear_convtranspose_nd(x: torch.Tensor, x_scale: float, x_zero_point: int,
                              auto_pad: str = "NOTSET", strides=None, dilations=None, pads=None, output_padding=None,
                              output_shape=None, kernel_shape=None, group: int = 1, channels_last: bool = False,
                              out: Optional[torch.Tensor] = None, kernel: str = "auto",
-                             stream: Optional[torch.cuda.Stream] = None) -> torch.Tensor:
+                             stream: Optional[torch.cuda.Stream] = None, _prepare_only: bool = False) -> torch.Tensor:
     """Quantized ConvTranspose (QLinear scheme) on the GPU: uint8/int8 x, w and y; x and y
     quantized per tensor (host scalars), w per tensor or per output channel (w_scale
     float32 and w_zero_point of w's dtype, 1 or M values, on x's device); bias int32."""
@@ -501,13 +504,36 @@ def qlinear_convtranspose_nd(x: torch.Tensor, x_scale: float, x_zero_point: int,
     stream = stream if stream is not None else torch.cuda.current_stream(dev)
     nsp = x.dim() - 2
     ptr = lambda t: ctypes.c_void_p(t.data_ptr()) if t is not None else None  # noqa: E731
+    args = (KERNELS[kernel], nsp, int(channels_last), ptr(x), _QTYPES[x.dtype], _i64(x.shape), float(x_scale),
+            int(x_zero_point), ptr(w), _QTYPES[w.dtype], _i64(w.shape), ptr(w_scale), ptr(w_zero_point),
+            w_scale.numel(), ptr(bias), ptr(out), _QTYPES[y_dtype], _i64(yshape), float(y_scale), int(y_zero_point),
+            *_attr_args(nsp, **attrs), ctypes.c_void_p(stream.cuda_stream))
+    if _prepare_only:
+        return lib.qlinear_convtranspose_nd, args, out
     with torch.cuda.device(dev):
-        st = lib.qlinear_convtranspose_nd(KERNELS[kernel], nsp, int(channels_last), ptr(x), _QTYPES[x.dtype],
-                                          _i64(x.shape), float(x_scale), int(x_zero_point), ptr(w),
-                                          _QTYPES[w.dtype], _i64(w.shape), ptr(w_scale), ptr(w_zero_point),
-                                          w_scale.numel(), ptr(bias), ptr(out), _QTYPES[y_dtype], _i64(yshape),
-                                          float(y_scale), int(y_zero_point), *_attr_args(nsp, **attrs),
-                                          ctypes.c_void_p(stream.cuda_stream))
+        st = lib.qlinear_convtranspose_nd(*args)
     if st:
         _raise(st)
     return out
+
+
+class PreparedCall:
+    """One call of ``convolution_nd`` or ``qlinear_convtranspose_nd`` with its arguments
+    validated and marshalled once: ``PreparedCall(convolution_nd, x, w, ...)`` takes the
+    function's own arguments; each call then enqueues the operation with a single C
+    call, writing the same output tensor (``.out``).  Repeated calls must be ordered on
+    one stream; the tensors must outlive the object."""
+
+    def __init__(self, fn, *args, **kwargs):
+        if fn not in (convolution_nd, qlinear_convtranspose_nd):
+            raise TypeError("PreparedCall serves convolution_nd and qlinear_convtranspose_nd")
+        self._fn, self._args, self.out = fn(*args, _prepare_only=True, **kwargs)
+        self._keep = (args, kwargs)  # the pointers stay valid while the object lives
+        self.device = self.out.device
+
+    def __call__(self) -> torch.Tensor:
+        with torch.cuda.device(self.device):
+            st = self._fn(*self._args)
+        if st:
+            _raise(st)
+        return self.out
