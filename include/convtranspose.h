@@ -33,7 +33,10 @@
  * must be dense in the stated layout and aligned to the element size; the library
  * keeps no pointer after a call returns.  The float16 implicit-GEMM path re-lays W out
  * into scratch memory: a caller workspace (convtranspose_nd_with_kernel), or else
- * stream-ordered scratch taken and released on the call's stream.
+ * stream-ordered scratch taken and released on the call's stream.  Such scratch comes
+ * from the device's default memory pool, whose release threshold the first such call
+ * on a device raises (freed scratch stays in the pool for later calls; this applies to
+ * every user of that pool in the process).
  *
  * Thread safety: every call is re-entrant; the error text is per host thread.
  */
@@ -252,13 +255,17 @@ ct_status convolution_output_shape(int nsp, const int64_t *x_shape, const int64_
  * except: x is (N, C, D1..Dn), w is (M, C/group, k1..kn), bias has M elements, y_shape
  * must equal convolution_output_shape's result, and there is no output_padding or
  * output_shape.
- *   kernel  CT_KERNEL_AUTO (stride 1 on every axis and channel counts per group of at
- *           least 16 where the MFMA path serves the shape: the implicit GEMM on the
- *           stride-1 transposed-convolution form, else the gather kernel),
- *           CT_KERNEL_DIRECT (the gather kernel, any arguments) or CT_KERNEL_IGEMM
- *           (CT_EUNSUPPORTED when that path cannot serve the call).
+ *   kernel  CT_KERNEL_AUTO (the MFMA path where it serves the shape, else the gather
+ *           kernel), CT_KERNEL_DIRECT (the gather kernel, any arguments) or
+ *           CT_KERNEL_IGEMM (CT_EUNSUPPORTED when the MFMA path cannot serve the call).
+ *           The MFMA path takes stride-1 convolutions with C/group and M/group of at
+ *           least 16 as the stride-1 transposed convolution (the same correlation with
+ *           reversed taps), and strided convolutions with dilation 1 after taking the
+ *           input phases as channels: tap k = s*k' + rho reads phase rho of the padded
+ *           input, xs_rho[j] = X[s*j + rho - b], at j = o + k', a stride-1 correlation
+ *           over C * prod(s) channels with ceil(K / s) taps.
  * The MFMA path takes stream-ordered scratch (hipMallocAsync / hipFreeAsync on `stream`)
- * for the re-laid-out weights.  Validation happens before anything is enqueued; errors
+ * for the re-laid-out weights and, for strided calls, the input's phase copy.  Validation happens before anything is enqueued; errors
  * leave y untouched and are reported by convtranspose_last_error().
  */
 ct_status convolution_nd(ct_kernel kernel, ct_dtype dtype, int nsp, int channels_last, const void *x,

@@ -88,7 +88,7 @@ struct IgArgs {
         float x_scale, y_scale;
         int x_zp, y_zp, y_lo, y_hi;  // x_zp in the signed (shifted) domain
         unsigned xflip;              // 0x80808080 for uint8 x (to the signed domain), else 0
-        int w_u8, w_per_channel, y_u8;
+        int w_u8, w_per_channel;
     } q;
 };
 
@@ -1477,7 +1477,6 @@ ct_status launch_qigemm(const Geom &g, bool cl, const void *x, const void *w, vo
     a.q.xflip = xflip;
     a.q.w_u8 = qc.w_type == CT_UINT8;
     a.q.w_per_channel = qc.wq_len == g.M && g.M != 1;
-    a.q.y_u8 = qc.y_type == CT_UINT8;
     const Config c = pl.cfg;
     mark_before(st);
     // (the template arguments repeat the Config constants above)
