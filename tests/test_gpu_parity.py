@@ -571,23 +571,24 @@ CONV_STRIDED = [
 ]
 
 
+@pytest.mark.parametrize("dtype", ["f16", "f32"])
 @pytest.mark.parametrize("integer", [False, True], ids=["float", "int"])
 @pytest.mark.parametrize("cl", [False, True], ids=["nc", "cl"])
 @pytest.mark.parametrize("case", CONV_STRIDED, ids=lambda c: f"{c[0]}_{c[1]}")
-def test_convolution_strided_mfma(T, case, cl, integer):
+def test_convolution_strided_mfma(T, case, cl, integer, dtype):
     xs, ws, attrs = case
     if cl and xs[1] % 8:
         pytest.skip("channels-last MFMA path needs C % 8 == 0")
     rng = np.random.default_rng(zlib.crc32(repr(case).encode()) + 2 * cl + integer + 7)
     gen = (lambda sz: rng.integers(-2, 3, size=sz)) if integer else (lambda sz: rng.normal(size=sz))
-    x = gen(xs).astype(np.float16)
-    w = (gen(ws) * (1 if integer else 0.1)).astype(np.float16)
-    b = gen(ws[0]).astype(np.float16)
-    _log(f"[case] conv strided x{xs} w{ws} {attrs} cl={cl} integer={integer}")
+    x = gen(xs).astype(NPT[dtype])
+    w = (gen(ws) * (1 if integer else 0.1)).astype(NPT[dtype])
+    b = gen(ws[0]).astype(NPT[dtype])
+    _log(f"[case] conv strided x{xs} w{ws} {attrs} cl={cl} integer={integer} {dtype}")
     ref = O.conv(x, w, b, **attrs)
     for kernel in ("igemm", "auto"):
         got = conv_gpu_run(T, x, w, b, attrs, cl, kernel)
-        check(got, ref, "f16", integer, f"conv strided {kernel} x{xs} w{ws} {attrs}")
+        check(got, ref, dtype, integer, f"conv strided {kernel} x{xs} w{ws} {attrs}")
 
 
 def test_convolution_adjoint_of_c4_sampled(T):
@@ -805,6 +806,7 @@ Q8_CASES = [
     ((2, 64, 6, 6), (64, 8, 2, 2), dict(strides=[2, 2], group=2)),
     ((1, 160, 5, 6), (160, 24, 4, 4), dict(strides=[2, 2], pads=[1, 1, 1, 1])),
     ((1, 256, 8, 8), (256, 64, 4, 4), dict(strides=[2, 2], pads=[1, 1, 1, 1])),
+    ((1, 16, 5, 6), (16, 32, 1, 2), dict(strides=[3, 2], output_padding=[2, 1])),   # phases no tap reaches
 ]
 
 
