@@ -186,7 +186,10 @@ __global__ __launch_bounds__(kThreads, OCC) void igemm_kernel(const _Float16 *x,
     const int wn = wave / WAVES_M;
 
     // ---------------- which phase / tile this block computes ----------------
-    const int v = xcd_remap(blockIdx.x, p.nblocks);
+    // Equal phases: each XCD takes a contiguous range of work (the phases of a pixel tile
+    // share its L2).  Unequal phases: launch order, heaviest phase first, so the blocks
+    // of every weight class spread over all XCDs and the light ones fill in last.
+    const int v = p.interleave ? xcd_remap(blockIdx.x, p.nblocks) : int(blockIdx.x);
     int ph, local;
     if (p.interleave) {
         ph = v % p.nphase;
@@ -1128,7 +1131,7 @@ bool make_plan_cfg(const Geom &g, bool cl, const Config &cfg, Plan *pl, std::str
         a.ph_r[i][1] = (unsigned char)list[i].r[1];
         a.ph_r[i][2] = (unsigned char)list[i].r[2];
         total += list[i].blocks;
-        uniform = uniform && list[i].blocks == list[0].blocks;
+        uniform = uniform && list[i].blocks == list[0].blocks && list[i].taps == list[0].taps;
     }
     a.ph_start[nph] = int(total);
     if (total > INT32_MAX) return no("too many blocks");
