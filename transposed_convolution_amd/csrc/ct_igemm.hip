@@ -1345,6 +1345,9 @@ constexpr int64_t kMaxQ8Depth = (int64_t(1) << 31) / (128 * 128) - 1;
 
 // Byte transpose of a batch of [rows][cols] matrices into [cols][rows] (channels-first
 // <-> channels-last for 8-bit tensors), through a 64 x 64 LDS tile per block.
+// VEC: rows and columns are multiples of 16 (and the buffers 16-byte aligned), so each
+// thread moves one 16-byte vector in and one out; otherwise bytes, bounds-checked.
+template <bool VEC>
 __global__ __launch_bounds__(256) void transpose8_kernel(const unsigned char *__restrict__ src,
                                                          unsigned char *__restrict__ dst, long long rows,
                                                          long long cols)
@@ -1353,16 +1356,33 @@ __global__ __launch_bounds__(256) void transpose8_kernel(const unsigned char *__
     const long long r0 = (long long)blockIdx.y * 64, c0 = (long long)blockIdx.x * 64;
     const size_t base = size_t(blockIdx.z) * size_t(rows) * size_t(cols);
     const int t = threadIdx.x;
+    if constexpr (VEC) {
+        const int rr = t / 4, cq = (t % 4) * 16;  // row of the tile, first of 16 columns
+        if (r0 + rr < rows && c0 + cq < cols) {
+            const u32x4 v = *reinterpret_cast<const u32x4 *>(src + base + size_t(r0 + rr) * cols + c0 + cq);
 #pragma unroll
-    for (int k = 0; k < 16; ++k) {  // 64 rows x 64 columns, consecutive threads on consecutive columns
-        const int e = t + k * 256, rr = e / 64, cc = e % 64;
-        if (r0 + rr < rows && c0 + cc < cols) tile[rr][cc] = src[base + size_t(r0 + rr) * cols + c0 + cc];
-    }
-    __syncthreads();
+            for (int e = 0; e < 16; ++e) tile[rr][cq + e] = (unsigned char)(v[e >> 2] >> (8 * (e & 3)));
+        }
+        __syncthreads();
+        const int cc = t / 4, rq = (t % 4) * 16;  // output row (= input column), first of 16 bytes
+        if (c0 + cc < cols && r0 + rq < rows) {
+            u32x4 o = {0u, 0u, 0u, 0u};
 #pragma unroll
-    for (int k = 0; k < 16; ++k) {
-        const int e = t + k * 256, cc = e / 64, rr = e % 64;
-        if (r0 + rr < rows && c0 + cc < cols) dst[base + size_t(c0 + cc) * rows + r0 + rr] = tile[rr][cc];
+            for (int e = 0; e < 16; ++e) o[e >> 2] |= unsigned(tile[rq + e][cc]) << (8 * (e & 3));
+            *reinterpret_cast<u32x4 *>(dst + base + size_t(c0 + cc) * rows + r0 + rq) = o;
+        }
+    } else {
+#pragma unroll
+        for (int k = 0; k < 16; ++k) {  // 64 rows x 64 columns, consecutive threads on consecutive columns
+            const int e = t + k * 256, rr = e / 64, cc = e % 64;
+            if (r0 + rr < rows && c0 + cc < cols) tile[rr][cc] = src[base + size_t(r0 + rr) * cols + c0 + cc];
+        }
+        __syncthreads();
+#pragma unroll
+        for (int k = 0; k < 16; ++k) {
+            const int e = t + k * 256, cc = e / 64, rr = e % 64;
+            if (r0 + rr < rows && c0 + cc < cols) dst[base + size_t(c0 + cc) * rows + r0 + rr] = tile[rr][cc];
+        }
     }
 }
 
@@ -1370,8 +1390,14 @@ void transpose8(const void *src, void *dst, long long batch, long long rows, lon
 {
     if (batch * rows * cols == 0) return;
     const dim3 grid(unsigned((cols + 63) / 64), unsigned((rows + 63) / 64), unsigned(batch));
-    hipLaunchKernelGGL(transpose8_kernel, grid, dim3(256), 0, st, static_cast<const unsigned char *>(src),
-                       static_cast<unsigned char *>(dst), rows, cols);
+    const bool vec = rows % 16 == 0 && cols % 16 == 0 && reinterpret_cast<uintptr_t>(src) % 16 == 0 &&
+                     reinterpret_cast<uintptr_t>(dst) % 16 == 0;
+    if (vec)
+        hipLaunchKernelGGL(transpose8_kernel<true>, grid, dim3(256), 0, st, static_cast<const unsigned char *>(src),
+                           static_cast<unsigned char *>(dst), rows, cols);
+    else
+        hipLaunchKernelGGL(transpose8_kernel<false>, grid, dim3(256), 0, st, static_cast<const unsigned char *>(src),
+                           static_cast<unsigned char *>(dst), rows, cols);
 }
 
 // Channels-first calls run the channels-last kernel between two transposes (x in, y out)
