@@ -739,10 +739,21 @@ __global__ __launch_bounds__(kThreads, OCC) void igemm_kernel(const _Float16 *x,
         }
         // Channels-first: the block's output tile goes through LDS (free once the main loop is
         // done) and is stored with 16-byte vectors along the contiguous pixel direction.
-        // tile layout (pitch padded by 8 elements against bank conflicts):
-        //   NC -> [m][pixel];  PAIR -> [m][pixel, phase] (the block's output rows, contiguous)
-        constexpr int TP = (PAIR ? 2 * BN : BN) + 8;
-        static_assert(BMM * TP * 2 <= Cfg::LDS - kBiasBytes, "output tile must fit in LDS below the bias");
+        // Two wave rows (PACKED): tile layout [pixel][m] (PAIR: [column phase][pixel][m]),
+        // channels innermost with a pitch of BMM + 4 elements: a lane's 4 consecutive
+        // channels of one pixel are one 8-byte write, and a pitch of an odd number of 8-byte
+        // words spreads the writes of 32 consecutive pixels over all banks; the store loop
+        // regroups 8 pixels (PAIR: 4 pixels x 2 phases) of each channel into one 16-byte
+        // vector.  One wave row (64-channel tiles, where the epilogue weighs less): layout
+        // [m][pixel] with a pitch of BN + 8 elements, written per element.
+        typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+        typedef float f32x2 __attribute__((ext_vector_type(2)));
+        typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+        constexpr bool PACKED = WAVES_M == 2;
+        constexpr int CP = BMM + 4, TP = BN + 8;
+        static_assert(CP % 8 == 4, "pitch: an odd number of 8-byte words");
+        static_assert((PACKED ? (PAIR ? 2 : 1) * BN * CP : BMM * TP) * 2 <= Cfg::LDS - kBiasBytes,
+                      "output tile must fit in LDS below the bias");
         __syncthreads();  // every wave is done reading the operand buffers
         _Float16 *const stile = reinterpret_cast<_Float16 *>(lds);
     #pragma unroll
@@ -755,12 +766,27 @@ __global__ __launch_bounds__(kThreads, OCC) void igemm_kernel(const _Float16 *x,
     #pragma unroll
                 for (int j = 0; j < WN; ++j) {
                     const int pl = (wn * WN + j) * 32 + (lane & 31);
+                    if constexpr (PACKED) {
+                        float v[4];
     #pragma unroll
-                    for (int e = 0; e < 4; ++e)
-                        stile[(ml + e) * TP + (PAIR ? 2 * pl + wm : pl)] = _Float16(fin(acc[i][j][rg * 4 + e] + bv[e]));
+                        for (int e = 0; e < 4; ++e) v[e] = fin(acc[i][j][rg * 4 + e] + bv[e]);
+                        // one rounding to nearest even per value (packed conversion)
+                        const f16x2 lo = __builtin_convertvector(f32x2{v[0], v[1]}, f16x2);
+                        const f16x2 hi = __builtin_convertvector(f32x2{v[2], v[3]}, f16x2);
+                        *reinterpret_cast<u32x2 *>(&stile[((PAIR ? wm * BN : 0) + pl) * CP + ml]) =
+                            u32x2{__builtin_bit_cast(unsigned, lo), __builtin_bit_cast(unsigned, hi)};
+                    } else {
+    #pragma unroll
+                        for (int e = 0; e < 4; ++e)
+                            stile[(ml + e) * TP + pl] = _Float16(fin(acc[i][j][rg * 4 + e] + bv[e]));
+                    }
                 }
             }
         __syncthreads();
+        // 16-bit element (c & 1) of word w, for channel c of a staged quadruple
+        auto lo_hi = [](unsigned a, unsigned b, int c) {  // a -> low half, b -> high half
+            return (c & 1) ? ((a >> 16) | (b & 0xffff0000u)) : ((a & 0xffffu) | (b << 16));
+        };
 
         if (PAIR) {
             // both column phases of each tile pixel: 2 * npix consecutive outputs per tile row
@@ -768,29 +794,73 @@ __global__ __launch_bounds__(kThreads, OCC) void igemm_kernel(const _Float16 *x,
             const bool vec = (O2 % 8 == 0) && (tl.q0 % 4 == 0) && (npix % 4 == 0) &&
                              (reinterpret_cast<uintptr_t>(y) % 16 == 0);
             if (vec) {
-                const int per = npix / 4;
-                for (int u = tid; u < mvalid * per; u += kThreads) {
-                    const int ml = u / per, v4 = u - ml * per;
-                    const size_t off = (size_t(n) * p.M + g * p.Mg + mt * BMM + ml) * opix + pixel_offset(v4 * 4);
-                    *reinterpret_cast<u32x4 *>(y + off) = *reinterpret_cast<const u32x4 *>(&stile[ml * TP + v4 * 8]);
+                // A lane takes 4 channels x 4 pixels x 2 phases (four 16-byte stores); a wave
+                // covers 8 channel quads x 8 pixel quads, so per channel 8 lanes write 128
+                // contiguous bytes.
+                const int mq = (mvalid + 3) / 4, pq = npix / 4;
+                const int nbp = (pq + 7) / 8, nblk = ((mq + 7) / 8) * nbp;
+                for (int blk = wave; blk < nblk; blk += kThreads / 64) {
+                    const int m4 = (blk / nbp) * 8 + (lane >> 3);
+                    const int v4 = (blk % nbp) * 8 + (lane & 7);
+                    if (m4 >= mq || v4 >= pq) continue;
+                    u32x2 d0[4], d1[4];  // phase 0 / phase 1: the 4 channels of pixel 4 * v4 + k
+    #pragma unroll
+                    for (int k = 0; k < 4; ++k) {
+                        d0[k] = *reinterpret_cast<const u32x2 *>(&stile[(4 * v4 + k) * CP + 4 * m4]);
+                        d1[k] = *reinterpret_cast<const u32x2 *>(&stile[(BN + 4 * v4 + k) * CP + 4 * m4]);
+                    }
+                    _Float16 *const yq = y + (size_t(n) * p.M + g * p.Mg + mt * BMM + 4 * m4) * opix + pixel_offset(4 * v4);
+    #pragma unroll
+                    for (int c = 0; c < 4; ++c) {
+                        if (4 * m4 + c >= mvalid) break;
+                        u32x4 o;
+    #pragma unroll
+                        for (int k = 0; k < 4; ++k)
+                            o[k] = lo_hi(c < 2 ? d0[k].x : d0[k].y, c < 2 ? d1[k].x : d1[k].y, c);
+                        *reinterpret_cast<u32x4 *>(yq + size_t(c) * opix) = o;
+                    }
                 }
             } else {
                 for (int u = tid; u < mvalid * 2 * npix; u += kThreads) {
                     const int ml = u / (2 * npix), e2 = u - ml * (2 * npix);
                     y[(size_t(n) * p.M + g * p.Mg + mt * BMM + ml) * opix + pixel_offset(e2 >> 1) + (e2 & 1)] =
-                        stile[ml * TP + e2];
+                        stile[((e2 & 1) * BN + (e2 >> 1)) * CP + ml];
                 }
             }
         } else {
             // runs of pixels per channel: contiguous in Y only along a row with unit stride
             const bool vec = p.s[2] == 1 && !tl.seg && (J2 % 8 == 0) && (tl.q0 % 8 == 0) && (O2 % 8 == 0) && r2 == 0 &&
                              (npix % 8 == 0) && (reinterpret_cast<uintptr_t>(y) % 16 == 0);
-            if (vec) {
+            if (vec && !PACKED) {
                 const int per = npix / 8;
                 for (int u = tid; u < mvalid * per; u += kThreads) {
                     const int ml = u / per, p8 = u - ml * per;
                     const size_t off = (size_t(n) * p.M + g * p.Mg + mt * BM + ml) * opix + pixel_offset(p8 * 8);
                     *reinterpret_cast<u32x4 *>(y + off) = *reinterpret_cast<const u32x4 *>(&stile[ml * TP + p8 * 8]);
+                }
+            } else if (vec) {
+                // A lane takes 4 channels x 8 pixels (four 16-byte stores); a wave covers 8
+                // channel quads x 8 pixel octets, so per channel 8 lanes write 128 contiguous
+                // bytes.
+                const int mq = (mvalid + 3) / 4, po = npix / 8;
+                const int nbp = (po + 7) / 8, nblk = ((mq + 7) / 8) * nbp;
+                for (int blk = wave; blk < nblk; blk += kThreads / 64) {
+                    const int m4 = (blk / nbp) * 8 + (lane >> 3);
+                    const int p8 = (blk % nbp) * 8 + (lane & 7);
+                    if (m4 >= mq || p8 >= po) continue;
+                    u32x2 d[8];  // the 4 channels of pixel 8 * p8 + k
+    #pragma unroll
+                    for (int k = 0; k < 8; ++k) d[k] = *reinterpret_cast<const u32x2 *>(&stile[(8 * p8 + k) * CP + 4 * m4]);
+                    _Float16 *const yq = y + (size_t(n) * p.M + g * p.Mg + mt * BM + 4 * m4) * opix + pixel_offset(8 * p8);
+    #pragma unroll
+                    for (int c = 0; c < 4; ++c) {
+                        if (4 * m4 + c >= mvalid) break;
+                        u32x4 o;
+    #pragma unroll
+                        for (int k = 0; k < 4; ++k)
+                            o[k] = lo_hi(c < 2 ? d[2 * k].x : d[2 * k].y, c < 2 ? d[2 * k + 1].x : d[2 * k + 1].y, c);
+                        *reinterpret_cast<u32x4 *>(yq + size_t(c) * opix) = o;
+                    }
                 }
             } else {
                 // Phase-strided or ragged rows: a wave stores 64 consecutive tile pixels of
@@ -801,7 +871,8 @@ __global__ __launch_bounds__(kThreads, OCC) void igemm_kernel(const _Float16 *x,
                     const int pl = pb + lane;
                     if (pl >= npix) continue;
                     _Float16 *const yq = y + (size_t(n) * p.M + g * p.Mg + mt * BM) * opix + pixel_offset(pl);
-                    for (int ml = wave; ml < mvalid; ml += 4) yq[size_t(ml) * opix] = stile[ml * TP + pl];
+                    for (int ml = wave; ml < mvalid; ml += 4)
+                        yq[size_t(ml) * opix] = stile[PACKED ? pl * CP + ml : ml * TP + pl];
                 }
             }
         }
