@@ -181,7 +181,7 @@ __global__ __launch_bounds__(kThreads, OCC) void igemm_kernel(const _Float16 *x,
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = tid >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: a scalar
     const int wm = wave % WAVES_M;
     const int wn = wave / WAVES_M;
 
@@ -674,6 +674,10 @@ __global__ __launch_bounds__(kThreads, OCC) void igemm_kernel(const _Float16 *x,
     // The output stage, instantiated once per activation kind (one uniform switch picks
     // the instance), so no value pays for a dispatch.
     auto output_stage = [&](auto fin) {
+        // lane and thread index recomputed here (two instructions) instead of being kept
+        // live across the main loop, where the register allocator spills them to memory
+        const int lane = int(__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u)));
+        const int tid = wave * 64 + lane;
         // ---------------- epilogue: bias, round once, store ----------------
         // Accumulator element r of tile (i, j) belongs to channel i*32 + (r/4)*8 + (lane/32)*4
         // + r%4 of the wave's rows; the bias is added in float32 before the one rounding.
