@@ -700,8 +700,8 @@ __global__ __launch_bounds__(kThreads, OCC) void igemm_kernel(const _Float16 *x,
             const int col = q - row * J2;
             return (size_t(o0) * O1 + (r1 + p.s[1] * row)) * O2 + (r2 + p.s[2] * col);
         };
-        if constexpr (CL) {
-            // Channels-last: straight from the accumulators.  A lane holds 4 consecutive
+        if constexpr (CL && WAVES_M != 2) {
+            // Channels-last, one wave row: straight from the accumulators.  A lane holds 4 consecutive
             // channels of one pixel per (tile, row group); lanes l and l + 32 hold adjacent
             // quadruples, so each store instruction writes 16 contiguous bytes per pixel.
             typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
@@ -741,8 +741,10 @@ __global__ __launch_bounds__(kThreads, OCC) void igemm_kernel(const _Float16 *x,
                 }
             return;
         }
-        // Channels-first: the block's output tile goes through LDS (free once the main loop is
-        // done) and is stored with 16-byte vectors along the contiguous pixel direction.
+        // Channels-first, and channels-last with two wave rows: the block's output tile goes
+        // through LDS (free once the main loop is done) and is stored with 16-byte vectors
+        // along the contiguous direction (pixels; channels for channels-last, where a wave
+        // then writes whole 128-byte lines instead of 8 bytes per lane and pixel).
         // Two wave rows (PACKED): tile layout [pixel][m] (PAIR: [column phase][pixel][m]),
         // channels innermost with a pitch of BMM + 4 elements: a lane's 4 consecutive
         // channels of one pixel are one 8-byte write, and a pitch of an odd number of 8-byte
@@ -787,6 +789,28 @@ __global__ __launch_bounds__(kThreads, OCC) void igemm_kernel(const _Float16 *x,
                 }
             }
         __syncthreads();
+        if constexpr (CL) {
+            // 8 channels of one pixel per lane and store; a pixel's channels of the tile are
+            // contiguous in Y
+            const bool vec = (p.M % 8 == 0) && ((g * p.Mg + mt * BM) % 8 == 0) && (mvalid % 8 == 0) &&
+                             (reinterpret_cast<uintptr_t>(y) % 16 == 0);
+            _Float16 *const yt = y + size_t(n) * opix * p.M + g * p.Mg + mt * BM;
+            if (vec) {
+                const int nc8 = mvalid / 8;
+                for (int u = tid; u < npix * nc8; u += kThreads) {
+                    const int pl = u / nc8, c8 = u - pl * nc8;
+                    const u32x2 lo = *reinterpret_cast<const u32x2 *>(&stile[pl * CP + c8 * 8]);
+                    const u32x2 hi = *reinterpret_cast<const u32x2 *>(&stile[pl * CP + c8 * 8 + 4]);
+                    *reinterpret_cast<u32x4 *>(yt + pixel_offset(pl) * p.M + c8 * 8) = u32x4{lo.x, lo.y, hi.x, hi.y};
+                }
+            } else {
+                for (int u = tid; u < npix * mvalid; u += kThreads) {
+                    const int pl = u / mvalid, ml = u - pl * mvalid;
+                    yt[pixel_offset(pl) * p.M + ml] = stile[pl * CP + ml];
+                }
+            }
+            return;
+        }
         // 16-bit element (c & 1) of word w, for channel c of a staged quadruple
         auto lo_hi = [](unsigned a, unsigned b, int c) {  // a -> low half, b -> high half
             return (c & 1) ? ((a >> 16) | (b & 0xffff0000u)) : ((a & 0xffffu) | (b << 16));
