@@ -184,10 +184,10 @@ __global__ __launch_bounds__(kDwThreads) void depthwise_kernel(const _Float16 *_
                     wt[rh][rwp][a] = (T2 & 1) ? float(e[T2 - 1]) : 0.0f;
                 }
 
-        // ---- load the next unit ahead (clamped: the last unit reloads itself) ----
+        // ---- load the next unit ahead, if there is one ----
         const int tn = t + int(gridDim.x);
         const Unit nxt = unit_of(min(tn, p.units - 1));
-        issue(nxt);
+        if (tn < p.units) issue(nxt);
 
         // ---- compute and store the current unit ----
         const int jrows = cur.j1hi - cur.j1lo + 1;
