@@ -334,6 +334,30 @@ struct S2dArgs {
 // layout: xs[n][j][c * P + rho].  One thread makes 8 consecutive elements of xs (along
 // the innermost axis, or along the channels for channels-last); 32-bit indices (the
 // plan keeps xs below 2^31 elements).
+// Eight consecutive values as 16-byte stores (dst 16-byte aligned), built from the values
+// themselves: a reinterpreted local array would be placed in scratch memory.
+template <typename T>
+__device__ __forceinline__ void store8(T *dst, const T (&v)[8])
+{
+    typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+    if constexpr (sizeof(T) == 2) {
+        u32x4 o;
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+            o[k] = unsigned(__builtin_bit_cast(unsigned short, v[2 * k])) |
+                   (unsigned(__builtin_bit_cast(unsigned short, v[2 * k + 1])) << 16);
+        *reinterpret_cast<u32x4 *>(dst) = o;
+    } else {
+        static_assert(sizeof(T) == 4, "16- or 32-bit values");
+        const u32x4 o0 = {__builtin_bit_cast(unsigned, v[0]), __builtin_bit_cast(unsigned, v[1]),
+                          __builtin_bit_cast(unsigned, v[2]), __builtin_bit_cast(unsigned, v[3])};
+        const u32x4 o1 = {__builtin_bit_cast(unsigned, v[4]), __builtin_bit_cast(unsigned, v[5]),
+                          __builtin_bit_cast(unsigned, v[6]), __builtin_bit_cast(unsigned, v[7])};
+        reinterpret_cast<u32x4 *>(dst)[0] = o0;
+        reinterpret_cast<u32x4 *>(dst)[1] = o1;
+    }
+}
+
 template <typename T, bool CL>
 __global__ __launch_bounds__(256) void s2d_kernel(const T *__restrict__ x, T *__restrict__ xs, S2dArgs p)
 {
@@ -363,20 +387,31 @@ __global__ __launch_bounds__(256) void s2d_kernel(const T *__restrict__ x, T *__
         n = row / Cp;
     }
     T *const dst = xs + size_t(u / g8) * inner;
+    // every load is issued unconditionally from a valid address and masked afterwards, so
+    // the eight loads are in flight together (loads under bounds branches were waited for
+    // one at a time)
+    T vals[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-        const int k = e0 + e;  // j2 (channels-first) or cp (channels-last)
-        if (k >= inner) break;
+        const int k = min(e0 + e, inner - 1);  // j2 (channels-first) or cp (channels-last)
         const int cpe = CL ? k : cp, j2e = CL ? j2 : k;
         const int c = cpe / p.P, rho = cpe - c * p.P;
         const int r2 = rho % p.s[2], r1 = (rho / p.s[2]) % p.s[1], r0 = rho / (p.s[2] * p.s[1]);
         const int i0 = p.s[0] * j0 + r0 - p.b[0], i1 = p.s[1] * j1 + r1 - p.b[1], i2 = p.s[2] * j2e + r2 - p.b[2];
-        T v = T(0);
-        if (i0 >= 0 && i0 < p.L[0] && i1 >= 0 && i1 < p.L[1] && i2 >= 0 && i2 < p.L[2]) {
-            const int ipix = (i0 * p.L[1] + i1) * p.L[2] + i2;
-            v = CL ? x[(size_t(n) * in_pix + ipix) * p.C + c] : x[(size_t(n) * p.C + c) * in_pix + ipix];
-        }
-        dst[k] = v;
+        const bool ok = e0 + e < inner && i0 >= 0 && i0 < p.L[0] && i1 >= 0 && i1 < p.L[1] && i2 >= 0 && i2 < p.L[2];
+        const int ipix = (i0 * p.L[1] + i1) * p.L[2] + i2;
+        const size_t off = !ok ? 0 : CL ? (size_t(n) * in_pix + ipix) * p.C + c : (size_t(n) * p.C + c) * in_pix + ipix;
+        const T v = x[off];
+        vals[e] = ok ? v : T(0);
+    }
+    if (inner % 8 == 0) {
+        // whole runs of 8 (the scratch copy is 256-byte aligned): one 16-byte store per
+        // 16 bytes instead of one store per element
+        store8(dst + e0, vals);
+    } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+            if (e0 + e < inner) dst[e0 + e] = vals[e];
     }
 }
 
@@ -386,18 +421,42 @@ __global__ __launch_bounds__(256) void s2d_w_kernel(const T *__restrict__ w, T *
                                                     int Cg, int P, S2dArgs p, int K0, int K1, int K2, int Q0, int Q1,
                                                     int Q2)
 {
-    const int64_t u = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
-    if (u >= total) return;
-    const int qt = Q0 * Q1 * Q2;
-    const int kq = int(u % qt);
-    int64_t r = u / qt;
-    const int cp = int(r % (int64_t(Cg) * P));
-    const int64_t m = r / (int64_t(Cg) * P);
-    const int cc = cp / P, rho = cp - cc * P;
-    const int r2 = rho % p.s[2], r1 = (rho / p.s[2]) % p.s[1], r0 = rho / (p.s[2] * p.s[1]);
-    const int q2 = kq % Q2, q1 = (kq / Q2) % Q1, q0 = kq / (Q1 * Q2);
-    const int k0 = p.s[0] * q0 + r0, k1 = p.s[1] * q1 + r1, k2 = p.s[2] * q2 + r2;
-    wq[u] = (k0 < K0 && k1 < K1 && k2 < K2) ? w[((m * Cg + cc) * K0 + k0) * K1 * K2 + int64_t(k1) * K2 + k2] : T(0);
+    // 8 consecutive outputs per thread (one 16-byte store per 16 bytes): the index is split
+    // once and then advanced with carries, not divided per element
+    const int64_t u0 = (int64_t(blockIdx.x) * blockDim.x + threadIdx.x) * 8;
+    if (u0 >= total) return;
+    const int qt = Q0 * Q1 * Q2, cgp = Cg * P;
+    int kq = int(u0 % qt);
+    const int64_t r = u0 / qt;
+    int cp = int(r % cgp);
+    int64_t m = r / cgp;
+    T vals[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        {  // unconditional load from a valid address, masked afterwards (see s2d_kernel)
+            const int cc = cp / P, rho = cp - cc * P;
+            const int r2 = rho % p.s[2], r1 = (rho / p.s[2]) % p.s[1], r0 = rho / (p.s[2] * p.s[1]);
+            const int q2 = kq % Q2, q1 = (kq / Q2) % Q1, q0 = kq / (Q1 * Q2);
+            const int k0 = p.s[0] * q0 + r0, k1 = p.s[1] * q1 + r1, k2 = p.s[2] * q2 + r2;
+            const bool ok = u0 + e < total && k0 < K0 && k1 < K1 && k2 < K2;
+            const T v = w[ok ? ((m * Cg + cc) * K0 + k0) * K1 * K2 + int64_t(k1) * K2 + k2 : 0];
+            vals[e] = ok ? v : T(0);
+        }
+        if (++kq == qt) {
+            kq = 0;
+            if (++cp == cgp) {
+                cp = 0;
+                ++m;
+            }
+        }
+    }
+    if (total % 8 == 0) {  // whole runs of 8 (the scratch copy is 256-byte aligned)
+        store8(wq + u0, vals);
+    } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+            if (u0 + e < total) wq[u0 + e] = vals[e];
+    }
 }
 
 ct_status launch_s2d(const CGeom &c, ct_dtype dt, bool cl, const void *x, const void *w, const void *bias, void *y,
@@ -428,7 +487,7 @@ ct_status launch_s2d(const CGeom &c, ct_dtype dt, bool cl, const void *x, const 
     void *wq = static_cast<char *>(buf) + xs_bytes;
     const int64_t inner = cl ? q.C : q.L[kAxes - 1];
     const int64_t threads = inner > 0 ? p.total / inner * ((inner + 7) / 8) : 0;
-    const unsigned bx = unsigned((threads + 255) / 256), bw = unsigned((wn + 255) / 256);
+    const unsigned bx = unsigned((threads + 255) / 256), bw = unsigned((wn + 8 * 256 - 1) / (8 * 256));
     const int K0 = int(c.K[0]), K1 = int(c.K[1]), K2 = int(c.K[2]);
     const int Q0 = int(q.K[0]), Q1 = int(q.K[1]), Q2 = int(q.K[2]);
     if (dt == CT_FLOAT16) {
