@@ -993,20 +993,34 @@ __global__ __launch_bounds__(256) void pack_w_kernel(const _Float16 *__restrict_
 {
     const long long u = (long long)blockIdx.x * blockDim.x + threadIdx.x;
     if (u >= a.total) return;
-    const int t = int(u % a.T);
-    long long rest = u / a.T;
-    const int m = int(rest % a.Mgp);
-    rest /= a.Mgp;
-    const int cv = int(rest % (a.Cgp / 8));
-    const int g = int(rest / (a.Cgp / 8));
+    int t, m, cv, g;
+    if (a.total <= 0x7fffffffLL) {  // 32-bit index arithmetic (64-bit division is a long sequence)
+        unsigned rest = unsigned(u);
+        t = int(rest % unsigned(a.T));
+        rest /= unsigned(a.T);
+        m = int(rest % unsigned(a.Mgp));
+        rest /= unsigned(a.Mgp);
+        cv = int(rest % unsigned(a.Cgp / 8));
+        g = int(rest / unsigned(a.Cgp / 8));
+    } else {
+        t = int(u % a.T);
+        long long rest = u / a.T;
+        m = int(rest % a.Mgp);
+        rest /= a.Mgp;
+        cv = int(rest % (a.Cgp / 8));
+        g = int(rest / (a.Cgp / 8));
+    }
     unsigned short v[8];
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
         const int c = cv * 8 + k;
         const size_t src = a.conv ? ((size_t(g) * a.Mg + m) * a.Cg + c) * a.T + (a.T - 1 - t)
                                   : ((size_t(g) * a.Cg + c) * a.Mg + m) * a.T + t;
-        const _Float16 e = (c < a.Cg && m < a.Mg) ? w[src] : _Float16(0.0f);
-        v[k] = __builtin_bit_cast(unsigned short, e);
+        // unconditional load from a valid address, masked afterwards: loads under a
+        // branch are waited for one at a time
+        const bool ok = c < a.Cg && m < a.Mg;
+        const _Float16 e = w[ok ? src : 0];
+        v[k] = ok ? __builtin_bit_cast(unsigned short, e) : (unsigned short)0;
     }
     _Float16 *dst = wp + ((size_t(g) * a.T + t) * a.Mgp + m) * a.Cgp + cv * 8;
     u32x4 o;
@@ -1027,19 +1041,31 @@ __global__ __launch_bounds__(256) void pack_wq_kernel(const unsigned char *__res
 {
     const long long u = (long long)blockIdx.x * blockDim.x + threadIdx.x;
     if (u >= a.total) return;
-    const int t = int(u % a.T);
-    long long rest = u / a.T;
-    const int m = int(rest % a.Mgp);
-    rest /= a.Mgp;
-    const int cv = int(rest % (a.Cgp / 16));
-    const int g = int(rest / (a.Cgp / 16));
+    int t, m, cv, g;
+    if (a.total <= 0x7fffffffLL) {  // 32-bit index arithmetic (64-bit division is a long sequence)
+        unsigned rest = unsigned(u);
+        t = int(rest % unsigned(a.T));
+        rest /= unsigned(a.T);
+        m = int(rest % unsigned(a.Mgp));
+        rest /= unsigned(a.Mgp);
+        cv = int(rest % unsigned(a.Cgp / 16));
+        g = int(rest / unsigned(a.Cgp / 16));
+    } else {
+        t = int(u % a.T);
+        long long rest = u / a.T;
+        m = int(rest % a.Mgp);
+        rest /= a.Mgp;
+        cv = int(rest % (a.Cgp / 16));
+        g = int(rest / (a.Cgp / 16));
+    }
     const unsigned flip = a.w_u8 ? 0x80u : 0u;
     u32x4 o = {0u, 0u, 0u, 0u};
 #pragma unroll
     for (int k = 0; k < 16; ++k) {
         const int c = cv * 16 + k;
-        const unsigned e = (c < a.Cg && m < a.Mg) ? (unsigned(w[((size_t(g) * a.Cg + c) * a.Mg + m) * a.T + t]) ^ flip) : 0u;
-        o[k >> 2] |= e << (8 * (k & 3));
+        const bool ok = c < a.Cg && m < a.Mg;  // unconditional load, masked afterwards
+        const unsigned raw = w[ok ? ((size_t(g) * a.Cg + c) * a.Mg + m) * a.T + t : 0];
+        o[k >> 2] |= (ok ? (raw ^ flip) : 0u) << (8 * (k & 3));
     }
     *reinterpret_cast<u32x4 *>(wp + ((size_t(g) * a.T + t) * a.Mgp + m) * a.Cgp + cv * 16) = o;
 }
