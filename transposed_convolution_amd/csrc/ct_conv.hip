@@ -389,8 +389,12 @@ __global__ __launch_bounds__(256) void s2d_kernel(const T *__restrict__ x, T *__
     T *const dst = xs + size_t(u / g8) * inner;
     // every load is issued unconditionally from a valid address and masked afterwards, so
     // the eight loads are in flight together (loads under bounds branches were waited for
-    // one at a time)
+    // one at a time).  An empty input (padding alone can still give a phase copy) has no
+    // valid address: then nothing is loaded and the copy is zeros.
     T vals[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) vals[e] = T(0);
+    if (in_pix > 0)
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
         const int k = min(e0 + e, inner - 1);  // j2 (channels-first) or cp (channels-last)
