@@ -34,9 +34,9 @@
  * keeps no pointer after a call returns.  The float16 implicit-GEMM path re-lays W out
  * into scratch memory: a caller workspace (convtranspose_nd_with_kernel), or else
  * stream-ordered scratch taken and released on the call's stream.  Such scratch comes
- * from the device's default memory pool, whose release threshold the first such call
- * on a device raises (freed scratch stays in the pool for later calls; this applies to
- * every user of that pool in the process).
+ * from a memory pool the library creates for each device on first use and keeps until
+ * the process ends (freed scratch stays in that pool for later calls; the device's
+ * default pool is not touched).
  *
  * Thread safety: every call is re-entrant; the error text is per host thread.
  */
@@ -138,7 +138,8 @@ ct_status convtranspose_useful_macs(int nsp, const int64_t *x_shape, const int64
  * and y is untouched.  Work is asynchronous: the call returns once the kernels are
  * enqueued.  An empty y (some dimension 0) returns CT_OK with no launch.  When the
  * dispatcher picks the float16 implicit-GEMM path, scratch for the re-laid-out weights
- * is taken with hipMallocAsync and released with hipFreeAsync on `stream`.
+ * is taken from the library's pool (hipMallocFromPoolAsync) and released with
+ * hipFreeAsync on `stream`.
  */
 ct_status convtranspose_nd(ct_dtype dtype, int nsp, int channels_last, const void *x,
                            const int64_t *x_shape, const void *w, const int64_t *w_shape,
@@ -157,8 +158,9 @@ ct_status convtranspose_nd(ct_dtype dtype, int nsp, int channels_last, const voi
  *                   the float16 implicit-GEMM path's re-laid-out weights (the float32
  *                   path needs none); it must not be in use
  *                   by other work until this call's kernels have finished on `stream`.
- *                   NULL: the library takes stream-ordered scratch itself
- *                   (hipMallocAsync / hipFreeAsync on `stream`), as convtranspose_nd does.
+ *                   NULL: the library takes stream-ordered scratch itself from its
+ *                   own pool (hipMallocFromPoolAsync / hipFreeAsync on `stream`), as
+ *                   convtranspose_nd does.
  *                   Too small a workspace is CT_EINVAL.
  */
 ct_status convtranspose_nd_with_kernel(ct_kernel kernel, ct_dtype dtype, int nsp, int channels_last,
@@ -264,9 +266,10 @@ ct_status convolution_output_shape(int nsp, const int64_t *x_shape, const int64_
  *           input phases as channels: tap k = s*k' + rho reads phase rho of the padded
  *           input, xs_rho[j] = X[s*j + rho - b], at j = o + k', a stride-1 correlation
  *           over C * prod(s) channels with ceil(K / s) taps.
- * The MFMA path takes stream-ordered scratch (hipMallocAsync / hipFreeAsync on `stream`)
- * for the re-laid-out weights and, for strided calls, the input's phase copy.  Validation happens before anything is enqueued; errors
- * leave y untouched and are reported by convtranspose_last_error().
+ * The MFMA path takes stream-ordered scratch from the library's pool
+ * (hipMallocFromPoolAsync / hipFreeAsync on `stream`) for the re-laid-out weights and, for
+ * strided calls, the input's phase copy.  Validation happens before anything is
+ * enqueued; errors leave y untouched and are reported by convtranspose_last_error().
  */
 ct_status convolution_nd(ct_kernel kernel, ct_dtype dtype, int nsp, int channels_last, const void *x,
                          const int64_t *x_shape, const void *w, const int64_t *w_shape,
@@ -309,8 +312,8 @@ ct_status convolution_nd(ct_kernel kernel, ct_dtype dtype, int nsp, int channels
  *                   and finite, y_zero_point inside y_type's range
  *   attributes and stream   as convtranspose_nd
  * Validation happens before anything is enqueued; errors leave y untouched.  The caller
- * owns every buffer; the MFMA path takes stream-ordered scratch (hipMallocAsync /
- * hipFreeAsync on stream) for the packed weights, their channel sums, the input's channel
+ * owns every buffer; the MFMA path takes stream-ordered scratch from the library's pool
+ * (hipMallocFromPoolAsync / hipFreeAsync on stream) for the packed weights, their channel sums, the input's channel
  * sums and, for channels-first tensors, channels-last copies of x and y.
  */
 ct_status qlinear_convtranspose_nd(ct_kernel kernel, int nsp, int channels_last, const void *x, ct_dtype x_type,

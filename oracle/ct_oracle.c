@@ -638,6 +638,7 @@ int oracle_qconvtranspose(int nsp, const int64_t *x_shape, const int32_t *x, int
     int rc;
     int64_t in_plane, out_plane, taps, t, plane;
     int64_t *tap_coord;
+    int oom = 0;
     rc = or_resolve(nsp, x_shape, w_shape, auto_pad, strides, dilations, pads, output_padding,
                     output_shape, kernel_shape, group, &g, err, errlen);
     if (rc != OR_OK)
@@ -669,8 +670,12 @@ int oracle_qconvtranspose(int nsp, const int64_t *x_shape, const int32_t *x, int
         float mult = or_requant_mult(x_scale, w_scale[q], y_scale);
         int64_t p, cc, ii, kk;
         int a;
-        if (!acc)
-            continue; /* reported below: y keeps the caller's contents */
+        if (!acc) {
+            /* reported after the loop as an error (no plane of y can be trusted then) */
+#pragma omp atomic write
+            oom = 1;
+            continue;
+        }
         for (p = 0; p < out_plane; p++)
             acc[p] = bias ? bias[m] : 0;
         for (cc = 0; cc < g.Cg; cc++) {
@@ -706,6 +711,8 @@ int oracle_qconvtranspose(int nsp, const int64_t *x_shape, const int32_t *x, int
         free(acc);
     }
     free(tap_coord);
+    if (oom)
+        return or_fail(err, errlen, "out of host memory");
     return OR_OK;
 }
 

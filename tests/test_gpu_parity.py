@@ -3,8 +3,9 @@
 Tolerances: |y - ref| <= tol * (1 + |ref|) elementwise with tol = 1e-5 for float32 and
 2e-3 for float16 inputs (float32 accumulation).  Small-integer-valued inputs must give
 exactly the oracle's value rounded once to the element type.  Full-size benchmark
-shapes are checked on seeded sampled outputs (plus every corner); reduced shapes with
-the same attributes, ragged sizes and several tiles are checked on every output."""
+shapes are checked on every output in the dispatcher's own launch configuration (the
+family it must pick is asserted too); reduced shapes with the same attributes, ragged
+sizes and several tiles are checked on every output."""
 import contextlib
 import zlib
 
@@ -84,7 +85,21 @@ def forced_tile(T, tile):
 # benchmark configurations
 # --------------------------------------------------------------------------------------
 WHOLE = [W.C1, W.C2, W.C3]
-SAMPLED = [W.C4, W.C4_NHWC, W.C5_S1, W.C5_S1_P1, W.C5_S2]
+FULL = [W.C4, W.C4_NHWC, W.C5_S1, W.C5_S1_P1, W.C5_S2]
+# the family the dispatcher must pick for each configuration (a silent fall-back to the
+# gather kernel would still be correct, so parity alone would not notice it)
+EXPECTED_FAMILY = {W.C1.name: "direct", W.C2.name: "igemm", W.C3.name: "grouped", W.C4.name: "igemm",
+                   W.C4_NHWC.name: "igemm", W.C5_S1.name: "igemm", W.C5_S1_P1.name: "igemm", W.C5_S2.name: "igemm"}
+
+
+def _auto_family(T, wl, x, w, b):
+    dev = torch.device("cuda:0")
+    tx = torch.from_numpy(np.ascontiguousarray(x)).to(dev)
+    if wl.channels_last:
+        tx = T.to_channels_last(tx)
+    tw = torch.from_numpy(np.ascontiguousarray(w)).to(dev)
+    tb = None if b is None else torch.from_numpy(b).to(dev)
+    return T.convtranspose_select_kernel(tx, tw, tb, channels_last=wl.channels_last, **wl.attrs)
 
 
 @pytest.mark.parametrize("integer", [False, True], ids=["float", "int"])
@@ -93,6 +108,8 @@ SAMPLED = [W.C4, W.C4_NHWC, W.C5_S1, W.C5_S1_P1, W.C5_S2]
 def test_config_whole_output(T, wl, kernel, integer):
     _log(f"[case] whole {wl.name} kernel={kernel} integer={integer}")
     x, w, b = W.make_inputs(wl, integer=integer)
+    if kernel == "auto":
+        assert _auto_family(T, wl, x, w, b) == EXPECTED_FAMILY[wl.name]
     got = gpu_run(T, x, w, b, wl.attrs, wl.channels_last, kernel)
     if got is None:
         pytest.skip(f"{kernel} does not serve {wl.name}")
@@ -101,16 +118,17 @@ def test_config_whole_output(T, wl, kernel, integer):
 
 
 @pytest.mark.parametrize("integer", [False, True], ids=["float", "int"])
-@pytest.mark.parametrize("wl", SAMPLED, ids=lambda w: w.name)
-def test_config_sampled_outputs(T, wl, integer):
-    """Full benchmark size in the dispatcher's own launch configuration."""
-    _log(f"[case] sampled {wl.name} integer={integer}")
+@pytest.mark.parametrize("wl", FULL, ids=lambda w: w.name)
+def test_config_full_size_whole_output(T, wl, integer):
+    """Full benchmark size, in the dispatcher's own launch configuration (the one the
+    benchmark times), compared on every output element with the oracle."""
+    _log(f"[case] full size {wl.name} integer={integer}")
     x, w, b = W.make_inputs(wl, integer=integer)
+    assert _auto_family(T, wl, x, w, b) == EXPECTED_FAMILY[wl.name]
     got = gpu_run(T, x, w, b, wl.attrs, wl.channels_last, "auto")
-    pts = W.make_points(got.shape, 3000, seed=wl.seed + 7)
-    ref = O.convtranspose_at(x, w, b, pts, **wl.attrs)
-    check(got[tuple(pts.T)], ref, wl.dtype, integer, wl.name)
     assert np.all(np.isfinite(got))
+    ref = O.convtranspose(x, w, b, **wl.attrs)
+    check(got, ref, wl.dtype, integer, wl.name)
 
 
 def reduced(wl, x_shape, w_shape, **kw):
@@ -255,6 +273,10 @@ EDGE = [
     ("zero_output_width", (1, 4, 5, 1), (4, 4, 3, 2), dict(pads=[0, 0, 1, 1]), True),
     ("no_input_channels", (2, 0, 4, 4), (0, 3, 3, 3), dict(strides=[2, 2]), True),
     ("empty_spatial_input", (1, 3, 0, 4), (3, 2, 4, 3), dict(strides=[2, 1]), True),
+    # empty inputs with C/group >= 16: routed to the gather kernel, never to the MFMA kernels
+    ("empty_spatial_wide", (1, 16, 4, 0), (16, 16, 4, 4), dict(strides=[2, 2]), True),
+    ("empty_spatial_wide_3d", (1, 16, 3, 0, 4), (16, 16, 3, 3, 3), dict(strides=[2, 2, 2]), True),
+    ("empty_spatial_wide_grouped", (1, 64, 0, 3), (64, 32, 3, 3), dict(strides=[2, 2], group=2), False),
     ("kernel_smaller_than_stride", (1, 8, 5, 6), (8, 8, 2, 1), dict(strides=[3, 2]), True),
     ("large_pads_crop", (1, 8, 9, 9), (8, 8, 5, 5), dict(strides=[2, 2], pads=[4, 3, 2, 5]), True),
     ("same_upper_negative", (1, 4, 6, 5), (4, 4, 1, 1), dict(strides=[2, 3], auto_pad="SAME_UPPER"), True),

@@ -217,9 +217,54 @@ def test_dispatcher_choices(T):
 
     assert pick(W.C1, dtype=0) == "direct"
     assert pick(W.C2, dtype=0) == "igemm"     # float32 implicit GEMM on MFMA
-    assert pick(W.C3) in ("grouped", "direct")
-    assert pick(W.C4) in ("igemm", "direct")
-    assert pick(W.C4, cl=1) in ("igemm", "direct")
+    assert pick(W.C3) == "grouped"            # the depthwise specialisation of the grouped family
+    assert pick(W.C4) == "igemm"
+    assert pick(W.C4_NHWC, cl=1) == "igemm"
+    for wl in (W.C5_S1, W.C5_S1_P1, W.C5_S2):
+        assert pick(wl) == "igemm", wl.name
+
+
+def _select(T, dtype, xs, ws, cl=0, **attrs):
+    lib = T.load_library()
+    at = T._attr_args(len(xs) - 2, **attrs)
+    k = lib.convtranspose_select_kernel(dtype, len(xs) - 2, cl, ctypes.c_void_p(256), T._i64(xs),
+                                        ctypes.c_void_p(256), T._i64(ws), ctypes.c_void_p(256),
+                                        ctypes.c_void_p(256), *at)
+    return T.convtranspose_kernel_name(k)
+
+
+@pytest.mark.parametrize("dtype", [0, 1], ids=["f32", "f16"])
+@pytest.mark.parametrize("cl", [0, 1], ids=["nc", "cl"])
+@pytest.mark.parametrize("case", [
+    ((1, 16, 4, 0), (16, 16, 4, 4), dict(strides=[2, 2])),
+    ((1, 16, 0, 8), (16, 16, 4, 4), dict(strides=[2, 2], pads=[0, 1, 0, 1])),
+    ((2, 32, 0), (32, 16, 3), dict(strides=[2])),
+    ((1, 16, 3, 0, 4), (16, 16, 3, 3, 3), dict(strides=[2, 2, 2])),
+    ((1, 64, 0, 3), (64, 32, 3, 3), dict(strides=[2, 2], group=2)),
+], ids=["2d_last_axis", "2d_first_axis", "1d", "3d", "grouped_2d"])
+def test_empty_input_never_reaches_mfma(T, case, cl, dtype):
+    """An input with a spatial size of 0 but a non-empty output (bias alone) with C/group
+    >= 16 must not be routed to the MFMA kernels, whose operand loads read through x's
+    base pointer (README Files: the empty-input case has a route of its own)."""
+    xs, ws, attrs = case
+    ys, _ = T.convtranspose_output_shape(xs, ws, **attrs)
+    assert int(np.prod(ys)) > 0
+    assert _select(T, dtype, xs, ws, cl, **attrs) == "direct"
+
+
+@pytest.mark.parametrize("dtype", [0, 1], ids=["f32", "f16"])
+@pytest.mark.parametrize("cl", [0, 1], ids=["nc", "cl"])
+def test_empty_input_forward_convolution_not_mfma(T, cl, dtype):
+    """The stride-1 forward convolution with an empty spatial input and padding (a bias-only
+    output) is refused by the MFMA path before any launch (CT_EUNSUPPORTED when forced)."""
+    lib = T.load_library()
+    vp = ctypes.c_void_p
+    xs, ws, attrs = (1, 16, 0, 6), (32, 16, 3, 3), dict(pads=[2, 1, 2, 1])
+    ys = T.convolution_output_shape(xs, ws, **attrs)[0]
+    assert int(np.prod(ys)) > 0
+    st = lib.convolution_nd(3, dtype, 2, cl, vp(256), T._i64(xs), vp(512), T._i64(ws), None, vp(1024),
+                            T._i64(ys), *T._conv_attr_args(2, **attrs), None)
+    assert st == 3, T.convtranspose_last_error()
 
 
 def test_igemm_tile_control(T):
@@ -296,3 +341,4 @@ def test_random_cases_resolve_identically(T):
         x, w, b, attrs = pins.random_case(rng, auto=(t % 3 == 0))
         assert T.convtranspose_output_shape(x.shape, w.shape, **attrs) == \
             tuple(tuple(v) for v in O.output_shape(x.shape, w.shape, **attrs))
+

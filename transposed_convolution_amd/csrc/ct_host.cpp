@@ -11,6 +11,7 @@
 #include <cstring>
 #include <atomic>
 #include <cmath>
+#include <mutex>
 #include <string>
 
 #include "ct_internal.hpp"
@@ -163,18 +164,39 @@ bool axis_phase(const Geom &g, int a, int r, AxisPhase *ph)
 
 hipError_t scratch_malloc(void **p, size_t bytes, hipStream_t st)
 {
-    static std::atomic<bool> pool_set[64];
+    // One memory pool per device, owned by the library and created on first use; freed
+    // scratch stays in it (release threshold: never trim) so repeated calls reuse it
+    // without mapping memory again.  The device's default pool is left as it is.
+    static std::mutex mu;
+    static hipMemPool_t pools[64] = {};
     int dev = 0;
     hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess) return e;
-    if (dev >= 0 && dev < 64 && !pool_set[dev].exchange(true)) {
-        hipMemPool_t pool;
-        if (hipDeviceGetDefaultMemPool(&pool, dev) == hipSuccess) {
+    if (dev < 0 || dev >= 64) return hipMallocAsync(p, bytes, st);
+    hipMemPool_t pool = nullptr;
+    {
+        std::lock_guard<std::mutex> lock(mu);
+        if (!pools[dev]) {
+            hipMemPoolProps props;
+            std::memset(&props, 0, sizeof(props));
+            props.allocType = hipMemAllocationTypePinned;
+            props.handleTypes = hipMemHandleTypeNone;
+            props.location.type = hipMemLocationTypeDevice;
+            props.location.id = dev;
+            hipMemPool_t created = nullptr;
+            e = hipMemPoolCreate(&created, &props);
+            if (e != hipSuccess) return e;
             uint64_t keep = UINT64_MAX;
-            (void)hipMemPoolSetAttribute(pool, hipMemPoolAttrReleaseThreshold, &keep);
+            e = hipMemPoolSetAttribute(created, hipMemPoolAttrReleaseThreshold, &keep);
+            if (e != hipSuccess) {
+                (void)hipMemPoolDestroy(created);
+                return e;
+            }
+            pools[dev] = created;
         }
+        pool = pools[dev];
     }
-    return hipMallocAsync(p, bytes, st);
+    return hipMallocFromPoolAsync(p, bytes, pool, st);
 }
 
 ProfileEvents &profile_events()

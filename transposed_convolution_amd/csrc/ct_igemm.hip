@@ -1363,6 +1363,13 @@ bool launch_config_q8(const Config &c, const Plan &pl, const void *x, const void
 
 bool igemm_supports(const Geom &g, ct_dtype dt, bool cl, const void *x, std::string *why)
 {
+    // An empty input (a spatial size of 0: the outputs are bias alone) never reaches the
+    // MFMA kernels: their halo and operand loads read through x's base pointer, which an
+    // empty tensor need not give a valid address for.
+    if (g.x_elems() <= 0) {
+        *why = "empty input";
+        return false;
+    }
     if (dt == CT_FLOAT32) return igemm32_supports(g, cl, why);
     if (dt != CT_FLOAT16) {
         *why = "float16 and float32 only";

@@ -60,9 +60,10 @@ struct AxisPhase {
 // Fills phase r of axis a; returns false when the phase has more than kMaxPhaseTaps taps.
 bool axis_phase(const Geom &g, int a, int r, AxisPhase *ph);
 
-// Stream-ordered scratch (hipMallocAsync on st).  The first call on a device raises the
-// release threshold of the device's default memory pool, so freed scratch stays in the
-// pool for the next call instead of being unmapped and mapped again.
+// Stream-ordered scratch (hipMallocFromPoolAsync on st) from a memory pool the library
+// creates per device on first use and keeps to the end of the process; its release
+// threshold keeps freed scratch in the pool for the next call instead of unmapping and
+// mapping it again.  Release with hipFreeAsync on the same stream.
 hipError_t scratch_malloc(void **p, size_t bytes, hipStream_t st);
 
 // The per-thread error text convtranspose_last_error() returns.
@@ -182,7 +183,7 @@ bool igemm32_supports(const Geom &g, bool cl, std::string *why);
 ct_status launch_igemm32(const Geom &g, bool cl, const void *x, const void *w, const void *bias, void *y,
                          const Act &act, hipStream_t st, std::string *err);
 // workspace: caller scratch of ws_bytes (>= igemm_workspace_bytes), or NULL to take
-// stream-ordered scratch with hipMallocAsync / hipFreeAsync on st.  w_conv (float16
+// stream-ordered scratch from the library pool (scratch_malloc / hipFreeAsync on st).  w_conv (float16
 // only): w is a forward convolution's weight (M, C/group, k) and g the stride-1
 // transposed convolution that equals that convolution; it is read with reversed taps.
 ct_status launch_igemm(const Geom &g, ct_dtype dt, bool cl, const void *x, const void *w,
