@@ -193,6 +193,32 @@ ct_status convtranspose_nd_fused(ct_kernel kernel, ct_dtype dtype, int nsp, int 
                                  void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * For callers that cannot allocate device memory (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc): convtranspose_nd_with_kernel with the
+ * workspace taken from a fixed 16 MiB array in device memory that the library holds on
+ * each device it runs on until the process ends.  The call itself allocates nothing (no
+ * hipMalloc, hipFree or pool allocation).  Arguments, layout, ownership and errors are
+ * those of convtranspose_nd_with_kernel without the workspace pair.
+ *   A call whose workspace (convtranspose_workspace_size) exceeds
+ *   convtranspose_noalloc_max_workspace() bytes fails with CT_EINVAL before anything is
+ *   enqueued; so do invalid arguments, as for convtranspose_nd_with_kernel.  CT_EDEVICE if
+ *   the array's device address cannot be obtained on the current device.
+ * Every call on a device shares that device's array and leaves its contents behind (the
+ * weight re-layout rewrites every byte a call reads, so nothing is carried over): calls
+ * whose work overlaps on one device -- on different streams, or from different host
+ * threads without ordering -- race on it.  Order them on one stream.
+ */
+ct_status convtranspose_nd_noalloc(ct_kernel kernel, ct_dtype dtype, int nsp, int channels_last, const void *x,
+                                   const int64_t *x_shape, const void *w, const int64_t *w_shape, const void *bias,
+                                   void *y, const int64_t *y_shape, ct_auto_pad auto_pad, const int64_t *strides,
+                                   const int64_t *dilations, const int64_t *pads, const int64_t *output_padding,
+                                   const int64_t *output_shape, const int64_t *kernel_shape, int64_t group,
+                                   void *stream);
+
+/* Bytes of the fixed workspace convtranspose_nd_noalloc serves (16 MiB).  Host only. */
+size_t convtranspose_noalloc_max_workspace(void);
+
+/*
  * Workspace bytes convtranspose_nd_with_kernel needs for these arguments and kernel
  * choice (0 when the chosen family needs none).  x is inspected for alignment only and
  * may be NULL (then assumed 256-byte aligned).  Host only.  Returns CT_OK or the status

@@ -342,3 +342,19 @@ def test_random_cases_resolve_identically(T):
         assert T.convtranspose_output_shape(x.shape, w.shape, **attrs) == \
             tuple(tuple(v) for v in O.output_shape(x.shape, w.shape, **attrs))
 
+
+def test_noalloc_rejects_oversized_workspace(T):
+    """The allocation-free entry point refuses, before touching any device, a call whose
+    workspace exceeds its fixed array (and names the limit)."""
+    lib = T.load_library()
+    assert lib.convtranspose_noalloc_max_workspace() == 16 << 20
+    xs, ws, attrs = (1, 1024, 4, 4), (1024, 1024, 4, 4), dict(strides=[2, 2])
+    ys, _ = T.convtranspose_output_shape(xs, ws, **attrs)
+    at = T._attr_args(2, **attrs)
+    P = ctypes.c_void_p(256)
+    st = lib.convtranspose_nd_noalloc(0, 1, 2, 0, P, T._i64(xs), P, T._i64(ws), None, P, T._i64(ys), *at, None)
+    assert st == 1 and "16777216" in T.convtranspose_last_error()
+    # invalid arguments: the status the call itself gives, nothing launched
+    st = lib.convtranspose_nd_noalloc(0, 1, 2, 0, P, T._i64(xs), P, T._i64((1000, 1024, 4, 4)), None, P,
+                                      T._i64(ys), *at, None)
+    assert st == 1

@@ -70,6 +70,10 @@ def load_library():
     lib.convtranspose_nd_with_kernel.argtypes = [ctypes.c_int] + call + [vp, ctypes.c_size_t, vp]
     lib.convtranspose_nd_fused.argtypes = [ctypes.c_int] + call + [ctypes.c_int, ctypes.c_float, ctypes.c_float,
                                                                    vp, ctypes.c_size_t, vp]
+    lib.convtranspose_nd_noalloc.argtypes = [ctypes.c_int] + call + [vp]
+    lib.convtranspose_nd_noalloc.restype = ctypes.c_int
+    lib.convtranspose_noalloc_max_workspace.argtypes = []
+    lib.convtranspose_noalloc_max_workspace.restype = ctypes.c_size_t
     lib.convtranspose_workspace_size.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, vp,
                                                  i64p, i64p] + attrs + [ctypes.POINTER(ctypes.c_size_t)]
     lib.convtranspose_select_kernel.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, vp, i64p,
@@ -339,6 +343,38 @@ def convtranspose_nd(x: torch.Tensor, w: torch.Tensor, bias: Optional[torch.Tens
                              kernel_shape=kernel_shape, group=group, channels_last=channels_last,
                              out=out, kernel=kernel, stream=stream, activation=activation,
                              act_params=act_params)()
+
+
+def convtranspose_nd_noalloc(x: torch.Tensor, w: torch.Tensor, bias: Optional[torch.Tensor] = None, *,
+                             out: torch.Tensor, auto_pad: str = "NOTSET", strides=None, dilations=None, pads=None,
+                             output_padding=None, output_shape=None, kernel_shape=None, group: int = 1,
+                             channels_last: bool = False, kernel: str = "auto",
+                             stream: Optional[torch.cuda.Stream] = None) -> torch.Tensor:
+    """The C entry point ``convtranspose_nd_noalloc``: Y = ConvTranspose(X, W, bias) into the
+    caller's ``out`` with the library's fixed device workspace, so nothing is allocated
+    (neither here nor in the library).  Arguments as for ``convtranspose_nd``; ``out`` is
+    required.  Calls on one device share the workspace: order them on one stream."""
+    lib = load_library()
+    if x.dtype not in _DTYPES:
+        raise ConvTransposeError(3, f"dtype {x.dtype} is not served (float32, float16)")
+    if kernel not in KERNELS:
+        raise ConvTransposeError(1, f"unknown kernel {kernel!r}")
+    dev = x.device
+    for name, t in (("x", x), ("w", w), ("out", out)) + ((("bias", bias),) if bias is not None else ()):
+        _check_tensor(name, t, dev, x.dtype)
+    if not _dense(x, channels_last) or not _dense(out, channels_last) or not w.is_contiguous():
+        raise ConvTransposeError(1, "x, out and w must be dense in the requested layout")
+    attrs = dict(auto_pad=auto_pad, strides=strides, dilations=dilations, pads=pads,
+                 output_padding=output_padding, output_shape=output_shape,
+                 kernel_shape=kernel_shape, group=group)
+    nsp, xp, xs, wp, ws, bp, yp, at = _call_args(x, w, bias, out, attrs)
+    st_ = stream if stream is not None else torch.cuda.current_stream(dev)
+    with torch.cuda.device(dev):
+        st = lib.convtranspose_nd_noalloc(KERNELS[kernel], _DTYPES[x.dtype], nsp, int(channels_last), xp, xs, wp, ws,
+                                          bp, yp, _i64(tuple(out.shape)), *at, ctypes.c_void_p(st_.cuda_stream))
+    if st:
+        _raise(st)
+    return out
 
 
 IGEMM_TILES = ("256x256", "128x256", "64x512", "64x256", "64x128")
