@@ -42,8 +42,10 @@ def load(path: Optional[str] = None):
     global _lib
     if path is None and _lib is not None:
         return _lib
-    p = path or _LIB
-    if path is None and (not os.path.exists(p) or os.path.getmtime(p) < os.path.getmtime(_SRC)):
+    # CT_ORACLE_LIB: another build of ct_oracle.c (e.g. with sanitizers) as the default
+    env = os.environ.get("CT_ORACLE_LIB") if path is None else None
+    p = path or env or _LIB
+    if path is None and not env and (not os.path.exists(p) or os.path.getmtime(p) < os.path.getmtime(_SRC)):
         build()
     lib = ctypes.CDLL(p)
     i64p = ctypes.POINTER(ctypes.c_int64)

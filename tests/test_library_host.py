@@ -358,3 +358,29 @@ def test_noalloc_rejects_oversized_workspace(T):
     st = lib.convtranspose_nd_noalloc(0, 1, 2, 0, P, T._i64(xs), P, T._i64((1000, 1024, 4, 4)), None, P,
                                       T._i64(ys), *at, None)
     assert st == 1
+
+
+def test_out_of_range_enum_arguments_are_refused(T):
+    """Enum arguments arrive from C as any int: values outside each enum are refused with
+    a status (unknown element type: CT_EUNSUPPORTED; other enums: CT_EINVAL) before
+    anything else happens (nothing launched)."""
+    lib = T.load_library()
+    P = ctypes.c_void_p(256)
+    xs, ws, ys = (1, 4, 5, 5), (4, 2, 3, 3), (1, 2, 11, 11)
+
+    def nd(kernel=0, dtype=1, auto_pad=0, act=0):
+        at = list(T._attr_args(2, strides=[2, 2]))
+        at[0] = auto_pad
+        return lib.convtranspose_nd_fused(kernel, dtype, 2, 0, P, T._i64(xs), P, T._i64(ws), None, P, T._i64(ys),
+                                          *at, act, 0.0, 0.0, None, 0, None)
+
+    for kw, want in ((dict(kernel=9), 1), (dict(kernel=-3), 1), (dict(dtype=-1), 3), (dict(dtype=77), 3),
+                     (dict(auto_pad=99), 1), (dict(auto_pad=-2), 1), (dict(act=8), 1), (dict(act=-1), 1)):
+        assert nd(**kw) == want, kw
+        assert T.convtranspose_last_error()
+    at = list(T._attr_args(2, strides=[2, 2]))
+    at[0] = 42
+    out = (ctypes.c_int64 * 4)()
+    assert lib.convtranspose_output_shape(2, T._i64(xs), T._i64(ws), *at, out, None) == 1
+    assert lib.convtranspose_select_kernel(5, 2, 0, P, T._i64(xs), P, T._i64(ws), None, P,
+                                           *T._attr_args(2, strides=[2, 2])) == -1

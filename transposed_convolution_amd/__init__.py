@@ -28,7 +28,9 @@ __all__ = [
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-_LIB_PATH = os.path.join(_HERE, "libconvtranspose.so")
+# CT_LIBRARY_PATH selects another build of the same library (e.g. one with host-side
+# sanitizers); it must exist like the default one -- there is no fallback.
+_LIB_PATH = os.environ.get("CT_LIBRARY_PATH") or os.path.join(_HERE, "libconvtranspose.so")
 AUTO_PAD = {"NOTSET": 0, "SAME_UPPER": 1, "SAME_LOWER": 2, "VALID": 3}
 KERNELS = {"auto": 0, "direct": 1, "grouped": 2, "igemm": 3, "none": 4}
 # output activation fused into the kernels' output stage (ct_activation), with the number

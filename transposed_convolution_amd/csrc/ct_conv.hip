@@ -582,6 +582,13 @@ ct_status convolution_output_shape(int nsp, const int64_t *x_shape, const int64_
                             const int64_t *kernel_shape, int64_t group, int64_t *y_shape_out, int64_t *pads_out)
 {
     ct::set_last_error(std::string());
+    {
+        ct::EnumArgs ea;
+        ea.auto_pad = ct::enum_int(auto_pad);
+        std::string ee;
+        const ct_status es = ct::check_enum_args(ea, &ee);
+        if (es != CT_OK) return ct::conv_fail(es, ee);
+    }
     if (!y_shape_out) return ct::conv_fail(CT_EINVAL, "y_shape_out is NULL");
     ct::CGeom g;
     std::string err;
@@ -609,6 +616,15 @@ ct_status convolution_nd(ct_kernel kernel, ct_dtype dtype, int nsp, int channels
                          void *stream)
 {
     ct::set_last_error(std::string());
+    {
+        ct::EnumArgs ea;
+        ea.kernel = ct::enum_int(kernel);
+        ea.dtype = ct::enum_int(dtype);
+        ea.auto_pad = ct::enum_int(auto_pad);
+        std::string ee;
+        const ct_status es = ct::check_enum_args(ea, &ee);
+        if (es != CT_OK) return ct::conv_fail(es, ee);
+    }
     if (dtype != CT_FLOAT32 && dtype != CT_FLOAT16)
         return ct::conv_fail(CT_EUNSUPPORTED, "dtype must be CT_FLOAT32 or CT_FLOAT16");
     if (channels_last != 0 && channels_last != 1) return ct::conv_fail(CT_EINVAL, "channels_last must be 0 or 1");

@@ -315,6 +315,13 @@ ct_status convtranspose_output_shape(int nsp, const int64_t *x_shape, const int6
                                      int64_t *y_shape_out, int64_t *pads_out)
 {
     t_error.clear();
+    {
+        ct::EnumArgs ea;
+        ea.auto_pad = ct::enum_int(auto_pad);
+        std::string ee;
+        const ct_status es = ct::check_enum_args(ea, &ee);
+        if (es != CT_OK) return fail(es, ee);
+    }
     if (!y_shape_out) return fail(CT_EINVAL, "y_shape_out is NULL");
     ct::Geom g;
     std::string err;
@@ -342,6 +349,13 @@ ct_status convtranspose_useful_macs(int nsp, const int64_t *x_shape, const int64
                                     const int64_t *kernel_shape, int64_t group, double *macs_out)
 {
     t_error.clear();
+    {
+        ct::EnumArgs ea;
+        ea.auto_pad = ct::enum_int(auto_pad);
+        std::string ee;
+        const ct_status es = ct::check_enum_args(ea, &ee);
+        if (es != CT_OK) return fail(es, ee);
+    }
     if (!macs_out) return fail(CT_EINVAL, "macs_out is NULL");
     ct::Geom g;
     std::string err;
@@ -362,6 +376,14 @@ int convtranspose_select_kernel(ct_dtype dtype, int nsp, int channels_last, cons
                                 int64_t group)
 {
     t_error.clear();
+    {
+        ct::EnumArgs ea;
+        ea.dtype = ct::enum_int(dtype);
+        ea.auto_pad = ct::enum_int(auto_pad);
+        std::string ee;
+        const ct_status es = ct::check_enum_args(ea, &ee);
+        if (es != CT_OK) return (fail(es, ee), -1);
+    }
     ct::Geom g;
     ct_kernel k = CT_KERNEL_AUTO;
     const ct::Attrs at = make_attrs(auto_pad, strides, dilations, pads, output_padding,
@@ -380,6 +402,15 @@ ct_status convtranspose_workspace_size(ct_kernel kernel, ct_dtype dtype, int nsp
                                        const int64_t *kernel_shape, int64_t group, size_t *bytes_out)
 {
     t_error.clear();
+    {
+        ct::EnumArgs ea;
+        ea.kernel = ct::enum_int(kernel);
+        ea.dtype = ct::enum_int(dtype);
+        ea.auto_pad = ct::enum_int(auto_pad);
+        std::string ee;
+        const ct_status es = ct::check_enum_args(ea, &ee);
+        if (es != CT_OK) return fail(es, ee);
+    }
     if (!bytes_out) return fail(CT_EINVAL, "bytes_out is NULL");
     ct::Geom g;
     ct_kernel k = CT_KERNEL_AUTO;
@@ -405,6 +436,16 @@ ct_status convtranspose_nd_fused(ct_kernel kernel, ct_dtype dtype, int nsp, int 
                                  void *workspace, size_t workspace_bytes, void *stream)
 {
     t_error.clear();
+    {
+        ct::EnumArgs ea;
+        ea.kernel = ct::enum_int(kernel);
+        ea.dtype = ct::enum_int(dtype);
+        ea.auto_pad = ct::enum_int(auto_pad);
+        ea.activation = ct::enum_int(activation);
+        std::string ee;
+        const ct_status es = ct::check_enum_args(ea, &ee);
+        if (es != CT_OK) return fail(es, ee);
+    }
     ct::Act act;
     act.kind = int(activation);
     act.p0 = act_p0;
@@ -455,6 +496,16 @@ ct_status convtranspose_nd_with_kernel(ct_kernel kernel, ct_dtype dtype, int nsp
                                        int64_t group, void *workspace, size_t workspace_bytes,
                                        void *stream)
 {
+    t_error.clear();
+    {
+        ct::EnumArgs ea;
+        ea.kernel = ct::enum_int(kernel);
+        ea.dtype = ct::enum_int(dtype);
+        ea.auto_pad = ct::enum_int(auto_pad);
+        std::string ee;
+        const ct_status es = ct::check_enum_args(ea, &ee);
+        if (es != CT_OK) return fail(es, ee);
+    }
     return convtranspose_nd_fused(kernel, dtype, nsp, channels_last, x, x_shape, w, w_shape, bias, y,
                                   y_shape, auto_pad, strides, dilations, pads, output_padding,
                                   output_shape, kernel_shape, group, CT_ACT_IDENTITY, 0.0f, 0.0f,
@@ -469,6 +520,15 @@ ct_status convtranspose_nd(ct_dtype dtype, int nsp, int channels_last, const voi
                            const int64_t *output_shape, const int64_t *kernel_shape,
                            int64_t group, void *stream)
 {
+    t_error.clear();
+    {
+        ct::EnumArgs ea;
+        ea.dtype = ct::enum_int(dtype);
+        ea.auto_pad = ct::enum_int(auto_pad);
+        std::string ee;
+        const ct_status es = ct::check_enum_args(ea, &ee);
+        if (es != CT_OK) return fail(es, ee);
+    }
     return convtranspose_nd_with_kernel(CT_KERNEL_AUTO, dtype, nsp, channels_last, x, x_shape, w,
                                         w_shape, bias, y, y_shape, auto_pad, strides, dilations,
                                         pads, output_padding, output_shape, kernel_shape, group,

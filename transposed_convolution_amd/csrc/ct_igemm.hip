@@ -68,15 +68,17 @@ struct IgArgs {
     int L[3], O[3], s[3], K[3];
     int nchunk, mtiles;
     int nphase, interleave, nblocks;
+    // Every table holds 32-bit words: the kernel reads them with scalar loads (sub-dword
+    // fields would be read by vector loads, each waited for in turn at the kernel's start).
     int ph_start[kMaxPh + 1];
-    unsigned char ph_r[kMaxPh][3];
+    int ph_r[kMaxPh];  // residues of a phase: r0 | r1 << 8 | r2 << 16
     // Taps of residue r on axis a form an arithmetic progression:
     //   k = tk0[a][r] + u * kstep[a],  beta = tb0[a][r] - u * bstep[a],  u in [0, ntap[a][r])
     // with kstep = s / gcd(s, d) and bstep = d / gcd(s, d).
-    signed char ntap[3][kMaxRes];
-    short tk0[3][kMaxRes];
-    short tb0[3][kMaxRes];
-    short kstep[3], bstep[3];
+    int ntap[3][kMaxRes];
+    int tk0[3][kMaxRes];
+    int tb0[3][kMaxRes];
+    int kstep[3], bstep[3];
     Act act;  // output activation
     // quantized instances only (QLinear scheme; see the kernel's Q8 comments)
     struct Quant {
@@ -131,7 +133,13 @@ struct IgCfg {
     static constexpr int KSUB = CC / 16;      // MFMA k-steps per step
     static constexpr int WVEC = BM * CHUNKS / kThreads;
     static constexpr int LDS = lds_budget(OCC);
-    static constexpr int HALO_BYTES = LDS - 2 * BM * ROW - kSinkBytes - tail_bytes(Q8);
+    // DIRECT (one wave row, float16): every wave reads the weights of its MFMAs straight
+    // into registers from the fragment-major packing, so LDS holds no weight tiles but two
+    // halo buffers (the next group's halo is stored while the current one is read).
+    static constexpr bool DIRECT = WAVES_M == 1 && !Q8;
+    static constexpr int HALO_BYTES = DIRECT ? ((LDS - kSinkBytes - tail_bytes(Q8)) / 2) / 16 * 16
+                                             : LDS - 2 * BM * ROW - kSinkBytes - tail_bytes(Q8);
+    static constexpr int HALO_BUFS = DIRECT ? 2 : 1;
     static_assert(BM * CHUNKS % kThreads == 0, "weight tile must split evenly");
     static_assert(HALO_BYTES > 0, "LDS budget");
 };
@@ -170,9 +178,10 @@ __global__ __launch_bounds__(kThreads, OCC) void igemm_kernel(const _Float16 *x,
     // halo stores that have no destination (keeps those stores branch-free).  After the
     // main loop the whole array holds the output tile.
     __shared__ __attribute__((aligned(16))) unsigned char lds[Cfg::LDS];
+    constexpr bool DIRECT = Cfg::DIRECT;
     auto lds_w = [&](int buf) -> unsigned char * { return lds + buf * (BM * ROW); };
-    unsigned char *const lds_h = lds + 2 * BM * ROW;
-    unsigned char *const lds_sink = lds_h + Cfg::HALO_BYTES;
+    unsigned char *const lds_h = DIRECT ? lds : lds + 2 * BM * ROW;  // DIRECT: halo buffer 0
+    unsigned char *const lds_sink = lds_h + Cfg::HALO_BUFS * Cfg::HALO_BYTES;
     float *const sbias = reinterpret_cast<float *>(lds_sink + kSinkBytes);  // kept to the end
     int *const sq_comp = reinterpret_cast<int *>(lds_sink + kSinkBytes);      // Q8: the same region
     float *const sq_mult = reinterpret_cast<float *>(sq_comp + 256);
@@ -199,7 +208,7 @@ __global__ __launch_bounds__(kThreads, OCC) void igemm_kernel(const _Float16 *x,
         while (v >= p.ph_start[ph + 1]) ++ph;
         local = v - p.ph_start[ph];
     }
-    const int r0 = p.ph_r[ph][0], r1 = p.ph_r[ph][1], r2 = p.ph_r[ph][2];  // PAIR: r2 = 0
+    const int r0 = p.ph_r[ph] & 0xff, r1 = (p.ph_r[ph] >> 8) & 0xff, r2 = p.ph_r[ph] >> 16;  // PAIR: r2 = 0
     const int k00 = p.tk0[0][r0], k01 = p.tk0[1][r1], k02 = p.tk0[2][r2];
     const int ks0 = p.kstep[0], ks1 = p.kstep[1], ks2 = p.kstep[2];
     const int b00 = p.tb0[0][r0], bs0 = p.bstep[0], bs1 = p.bstep[1], bs2 = p.bstep[2];
@@ -417,7 +426,7 @@ __global__ __launch_bounds__(kThreads, OCC) void igemm_kernel(const _Float16 *x,
     auto load_halo = [&](int chunk, int t0, u32x4 *reg) -> unsigned {
         return load_halo_part(std::integral_constant<int, 0>{}, std::integral_constant<int, HREG>{}, chunk, t0, reg);
     };
-    auto store_halo = [&](const u32x4 *reg, unsigned valid, int chunk) {
+    auto store_halo_to = [&](unsigned char *const lds_h, const u32x4 *reg, unsigned valid, int chunk) {
         const u32x4 zero = {0u, 0u, 0u, 0u};
         unsigned char *const sink = lds_sink + lane * 16;
         if (CL) {
@@ -467,6 +476,7 @@ __global__ __launch_bounds__(kThreads, OCC) void igemm_kernel(const _Float16 *x,
             }
         }
     };
+    auto store_halo = [&](const u32x4 *reg, unsigned valid, int chunk) { store_halo_to(lds_h, reg, valid, chunk); };
 
     // The bias of the block's channels, staged once (read in the epilogue; the first
     // barrier below, or the epilogue's own, makes it visible).  Q8: per channel the
@@ -505,24 +515,118 @@ __global__ __launch_bounds__(kThreads, OCC) void igemm_kernel(const _Float16 *x,
             nz |= wz != 0;
         }
         need_sx = __syncthreads_or(nz);
-    } else {
-        for (int mm = tid; mm < BMM; mm += kThreads) {
-            const int m = mt * BMM + mm;
-            sbias[mm] = (bias && m < p.Mg) ? float(bias[g * p.Mg + m]) : 0.0f;
-        }
     }
+    // float16: the block's bias (one channel per thread) is loaded here and staged in LDS
+    // after the main loop, so the first operand loads do not wait for it
+    static_assert(BMM <= kThreads, "one bias value per thread");
+    // (an unconditional load from a valid address -- x when there is no bias -- so no
+    // branch makes the compiler convert, and so wait for, the value here)
+    const bool bias_ok = !Q8 && bias && tid < BMM && mt * BMM + tid < p.Mg;
+    const _Float16 bias_h =
+        bias_ok ? bias[g * p.Mg + mt * BMM + tid] : *reinterpret_cast<const _Float16 *>(bias ? bias : x);
 
     // ---------------- main loop ----------------
-    if (nsteps > 0) {
+    if constexpr (DIRECT) {
+        if (nsteps > 0) {
+            // Weights straight from the fragment-major packing into MFMA operand registers:
+            // fragment (32 channels of m, 16 input channels) of (g, tap) is 64 lanes x 16
+            // bytes, contiguous, in lane order.  A ring of RING steps of fragments is kept in
+            // flight, so a fragment is loaded RING - 1 steps before its MFMAs.  No barrier
+            // between the steps of a group: the waves meet once per group, when the next
+            // group's halo (loaded into registers at the group's first step) has been stored
+            // into the other halo buffer.
+            constexpr int RING = (WM * KSUB >= 8) ? 2 : 3;
+            const int KB = p.Cgp / 16, MB = p.Mgp / 32;
+            const f16x8 *const wf = reinterpret_cast<const f16x8 *>(wp);
+            auto load_a = [&](const StepIdx &q, f16x8 (&dst)[WM][KSUB]) {
+                const int tflat = ((k00 + q.t0 * ks0) * p.K[1] + (k01 + q.t1 * ks1)) * p.K[2] + (k02 + q.t2 * ks2);
+                const f16x8 *src =
+                    wf + (((size_t(g) * p.T + tflat) * MB + size_t(mt) * (BM / 32)) * KB + size_t(q.chunk) * KSUB) * 64 +
+                    lane;
+#pragma unroll
+                for (int i = 0; i < WM; ++i)
+#pragma unroll
+                    for (int h = 0; h < KSUB; ++h) dst[i][h] = src[(size_t(i) * KB + h) * 64];
+            };
+            auto mma_direct = [&](const StepIdx &c, const unsigned char *hbuf, const f16x8 (&a)[WM][KSUB]) {
+                const int toff = ((nt1 - 1 - c.t1) * bs1 * tl.HC + (nt2 - 1 - c.t2) * bs2) * ROW;
+                const unsigned char *hb = hbuf + toff;
+                f16x8 b[2][WN];
+#pragma unroll
+                for (int j = 0; j < WN; ++j) b[0][j] = *reinterpret_cast<const f16x8 *>(hb + hoff[j]);
+#pragma unroll
+                for (int h = 0; h < KSUB; ++h) {
+                    const int cb = h & 1, nb = cb ^ 1;
+                    if (h + 1 < KSUB) {
+#pragma unroll
+                        for (int j = 0; j < WN; ++j)
+                            b[nb][j] = *reinterpret_cast<const f16x8 *>(hb + hoff[j] + (h + 1) * 32);
+                    }
+#pragma unroll
+                    for (int i = 0; i < WM; ++i)
+#pragma unroll
+                        for (int j = 0; j < WN; ++j)
+                            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[i][h], b[cb][j], acc[i][j], 0, 0, 0);
+                }
+            };
+            u32x4 hreg[HREG];
+            f16x8 ring[RING][WM][KSUB];
+            StepIdx cur = {0, t0_first, 0, 0};
+            StepIdx pf = cur;  // the next step whose fragments are loaded
+#pragma unroll
+            for (int d = 0; d < RING; ++d) {  // issued first: the halo's wait then covers them
+                load_a(d < nsteps ? pf : cur, ring[d]);  // past the end: a valid, unused tile
+                advance(pf);
+            }
+            {
+                const unsigned v0 = load_halo(0, t0_first, hreg);
+                store_halo_to(lds_h, hreg, v0, 0);
+            }
+            __syncthreads();
+            unsigned hvalid = 0;
+            int hchunk = 0, gi = 0;
+            for (int s0 = 0; s0 < nsteps; s0 += RING) {
+#pragma unroll
+                for (int u = 0; u < RING; ++u) {
+                    const int s = s0 + u;
+                    if (s < nsteps) {
+                        const bool group_first = cur.t1 == 0 && cur.t2 == 0;
+                        const bool group_last = cur.t1 == nt1 - 1 && cur.t2 == nt2 - 1;
+                        if (group_first) {  // the next group's halo comes in during this group
+                            StepIdx ng = cur;
+                            ng.t1 = nt1 - 1;
+                            ng.t2 = nt2 - 1;
+                            advance(ng);
+                            if (ng.chunk < p.nchunk) {
+                                hvalid = load_halo(ng.chunk, ng.t0, hreg);
+                                hchunk = ng.chunk;
+                            }
+                        }
+                        mma_direct(cur, lds_h + (gi & 1) * Cfg::HALO_BYTES, ring[u]);
+                        load_a(s + RING < nsteps ? pf : cur, ring[u]);  // refill: RING steps ahead
+                        advance(pf);
+                        if (group_last) {
+                            if (s + 1 < nsteps) store_halo_to(lds_h + ((gi + 1) & 1) * Cfg::HALO_BYTES, hreg, hvalid, hchunk);
+                            __syncthreads();
+                            ++gi;
+                        }
+                        advance(cur);
+                    }
+                }
+            }
+        }
+    } else if (nsteps > 0) {
         u32x4 wreg[WVEC];
         u32x4 hreg[HREG];
         StepIdx cur = {0, t0_first, 0, 0};
+        // the first weight tile and the first halo are in flight together (the weights,
+        // issued first, are stored as soon as they arrive)
+        load_w(cur, wreg);
         {
             const unsigned v0 = load_halo(0, t0_first, hreg);
+            store_w(0, wreg);
             store_halo(hreg, v0, 0);
         }
-        load_w(cur, wreg);
-        store_w(0, wreg);
         __syncthreads();
         // MFMAs of one step: weight tile from buffer buf, the halo window of the step's taps.
         // pre_w() issues the next weight tile's global loads, pre_h() a part of the next
@@ -671,6 +775,8 @@ __global__ __launch_bounds__(kThreads, OCC) void igemm_kernel(const _Float16 *x,
         }
     }
 
+    if constexpr (!Q8)
+        if (tid < BMM) sbias[tid] = bias_ok ? float(bias_h) : 0.0f;  // made visible by the output stage's barrier
     // The output stage, instantiated once per activation kind (one uniform switch picks
     // the instance), so no value pays for a dispatch.
     auto output_stage = [&](auto fin) {
@@ -682,7 +788,7 @@ __global__ __launch_bounds__(kThreads, OCC) void igemm_kernel(const _Float16 *x,
         // Accumulator element r of tile (i, j) belongs to channel i*32 + (r/4)*8 + (lane/32)*4
         // + r%4 of the wave's rows; the bias is added in float32 before the one rounding.
         typedef float f32x4 __attribute__((ext_vector_type(4)));
-        if (nsteps == 0) __syncthreads();  // no main-loop barrier made the staged bias visible
+        if constexpr (CL && WAVES_M != 2) __syncthreads();  // the staged bias is visible
         const int mwave = PAIR ? 0 : wm * WM * 32;  // first channel of the wave inside the tile
         auto bias_of = [&](int i, int rg, float *bv) {
             const f32x4 b4 = *reinterpret_cast<const f32x4 *>(&sbias[mwave + i * 32 + rg * 8 + (lane >> 5) * 4]);
@@ -758,7 +864,10 @@ __global__ __launch_bounds__(kThreads, OCC) void igemm_kernel(const _Float16 *x,
         constexpr bool PACKED = WAVES_M == 2;
         constexpr int CP = BMM + 4, TP = BN + 8;
         static_assert(CP % 8 == 4, "pitch: an odd number of 8-byte words");
-        static_assert((PACKED ? (PAIR ? 2 : 1) * BN * CP : BMM * TP) * 2 <= Cfg::LDS - kBiasBytes,
+        // the staged bias starts after the operand buffers and the sink
+        constexpr int kBiasOffset =
+            (DIRECT ? 0 : 2 * BM * ROW) + Cfg::HALO_BUFS * Cfg::HALO_BYTES + kSinkBytes;
+        static_assert((PACKED ? (PAIR ? 2 : 1) * BN * CP : BMM * TP) * 2 <= kBiasOffset,
                       "output tile must fit in LDS below the bias");
         __syncthreads();  // every wave is done reading the operand buffers
         _Float16 *const stile = reinterpret_cast<_Float16 *>(lds);
@@ -983,8 +1092,12 @@ __global__ __launch_bounds__(kThreads, OCC) void igemm_kernel(const _Float16 *x,
 // 8 strided reads of W are coalesced across the wave.  conv: W is a forward
 // convolution's weight (M, C/group, k) whose stride-1 adjoint this call computes, read
 // with its taps reversed: Wp[g][t][m][c] = Wconv[g*Mg + m][c][T-1-t].
+// frag: the fragment-major packing read by the one-wave-row instances, in which the MFMA
+// operand fragment (32 rows m, 16 channels c) of (g, t) is 64 lanes x 8 values in lane
+// order (lane = 32 * ((c % 16) / 8) + m % 32):
+//   Wf[g][t][m / 32][c / 16][lane][c % 8]
 struct PackArgs {
-    int G, Cg, Mg, Cgp, Mgp, T, conv;
+    int G, Cg, Mg, Cgp, Mgp, T, conv, frag;
     long long total;  // G * (Cgp/8) * Mgp * T
 };
 
@@ -1022,7 +1135,9 @@ __global__ __launch_bounds__(256) void pack_w_kernel(const _Float16 *__restrict_
         const _Float16 e = w[ok ? src : 0];
         v[k] = ok ? __builtin_bit_cast(unsigned short, e) : (unsigned short)0;
     }
-    _Float16 *dst = wp + ((size_t(g) * a.T + t) * a.Mgp + m) * a.Cgp + cv * 8;
+    const size_t gt = size_t(g) * a.T + t;
+    _Float16 *dst = a.frag ? wp + (((gt * (a.Mgp / 32) + m / 32) * (a.Cgp / 16) + cv / 2) * 64 + (cv & 1) * 32 + m % 32) * 8
+                           : wp + (gt * a.Mgp + m) * a.Cgp + cv * 8;
     u32x4 o;
 #pragma unroll
     for (int k = 0; k < 4; ++k) o[k] = unsigned(v[2 * k]) | (unsigned(v[2 * k + 1]) << 16);
@@ -1124,7 +1239,12 @@ struct Config {
     int bn() const { return (4 / waves_m) * wn * 32; }
     int row() const { return cc * 2 + 16; }
     int chunks() const { return cc / 8; }
-    int halo_bytes(bool q8 = false) const { return lds_budget(occ) - 2 * bm() * row() - kSinkBytes - tail_bytes(q8); }
+    bool direct(bool q8) const { return waves_m == 1 && !q8; }
+    int halo_bytes(bool q8 = false) const
+    {
+        return direct(q8) ? ((lds_budget(occ) - kSinkBytes - tail_bytes(q8)) / 2) / 16 * 16
+                          : lds_budget(occ) - 2 * bm() * row() - kSinkBytes - tail_bytes(q8);
+    }
     bool operator==(const Config &o) const
     {
         return waves_m == o.waves_m && wm == o.wm && wn == o.wn && cc == o.cc && nch_items == o.nch_items &&
@@ -1170,15 +1290,15 @@ bool make_plan_cfg(const Geom &g, bool cl, const Config &cfg, Plan *pl, std::str
         a.s[t] = int(g.s[t]);
         a.K[t] = int(g.K[t]);
         const int64_t gsd = std::__gcd(g.s[t], g.d[t]);
-        a.kstep[t] = short(g.s[t] / gsd);
-        a.bstep[t] = short(g.d[t] / gsd);
+        a.kstep[t] = int(g.s[t] / gsd);
+        a.bstep[t] = int(g.d[t] / gsd);
         if (g.K[t] > 32767 || g.d[t] / gsd > 32767) return no("kernel or dilation too large");
         for (int r = 0; r < g.s[t]; ++r) {
             AxisPhase ph;
             if (!axis_phase(g, t, r, &ph) || ph.ntaps > kMaxTap) return no("more than 8 taps per phase");
-            a.ntap[t][r] = (signed char)ph.ntaps;
-            a.tk0[t][r] = short(ph.ntaps ? ph.k[0] : 0);
-            a.tb0[t][r] = short(ph.ntaps ? ph.beta[0] : 0);
+            a.ntap[t][r] = ph.ntaps;
+            a.tk0[t][r] = ph.ntaps ? ph.k[0] : 0;
+            a.tb0[t][r] = ph.ntaps ? ph.beta[0] : 0;
             for (int k = 0; k < ph.ntaps; ++k)  // the progression the kernel walks
                 if (ph.k[k] != ph.k[0] + k * a.kstep[t] || ph.beta[k] != ph.beta[0] - k * a.bstep[t])
                     return no("internal: taps are not an arithmetic progression");
@@ -1253,9 +1373,7 @@ bool make_plan_cfg(const Geom &g, bool cl, const Config &cfg, Plan *pl, std::str
     bool uniform = true;
     for (int i = 0; i < nph; ++i) {
         a.ph_start[i] = int(total);
-        a.ph_r[i][0] = (unsigned char)list[i].r[0];
-        a.ph_r[i][1] = (unsigned char)list[i].r[1];
-        a.ph_r[i][2] = (unsigned char)list[i].r[2];
+        a.ph_r[i] = list[i].r[0] | (list[i].r[1] << 8) | (list[i].r[2] << 16);
         total += list[i].blocks;
         uniform = uniform && list[i].blocks == list[0].blocks && list[i].taps == list[0].taps;
     }
@@ -1440,6 +1558,7 @@ ct_status launch_igemm(const Geom &g, ct_dtype dt, bool cl, const void *x, const
     pa.Mgp = pl.a.Mgp;
     pa.T = pl.a.T;
     pa.conv = w_conv ? 1 : 0;
+    pa.frag = pl.cfg.direct(false) ? 1 : 0;
     pa.total = (long long)pa.G * (pa.Cgp / 8) * pa.Mgp * pa.T;
     const _Float16 *wt = static_cast<const _Float16 *>(w);
     _Float16 *wpk = static_cast<_Float16 *>(wsp);

@@ -5,6 +5,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
+#include <cstring>
 #include <string>
 
 #include "convtranspose.h"
@@ -68,6 +69,44 @@ hipError_t scratch_malloc(void **p, size_t bytes, hipStream_t st);
 
 // The per-thread error text convtranspose_last_error() returns.
 void set_last_error(const std::string &msg);
+
+// Enum arguments come from C callers as plain ints and may hold any value, while C++ code
+// may assume that an enum object holds one of its type's values.  Entry points therefore
+// read each enum argument's int value without loading it as the enum (enum_int) and
+// refuse values outside the enum (check_enum_args) before using the argument.
+template <class E>
+inline int enum_int(const E &v)
+{
+    static_assert(sizeof(E) == sizeof(int), "the C enums of the ABI are int-sized");
+    int r;
+    std::memcpy(&r, &v, sizeof r);
+    return r;
+}
+struct EnumArgs {
+    int kernel = CT_KERNEL_AUTO, dtype = CT_FLOAT32, auto_pad = CT_NOTSET, activation = CT_ACT_IDENTITY;
+};
+// CT_OK, or CT_EUNSUPPORTED for an unknown element type and CT_EINVAL for another
+// unknown enum value (message in *err).
+inline ct_status check_enum_args(const EnumArgs &e, std::string *err)
+{
+    if (e.dtype < CT_FLOAT32 || e.dtype > CT_UINT8) {
+        *err = "unknown element type";
+        return CT_EUNSUPPORTED;
+    }
+    if (e.auto_pad < CT_NOTSET || e.auto_pad > CT_VALID) {
+        *err = "auto_pad must be NOTSET, SAME_UPPER, SAME_LOWER or VALID";
+        return CT_EINVAL;
+    }
+    if (e.kernel < CT_KERNEL_AUTO || e.kernel > CT_KERNEL_NONE) {
+        *err = "unknown kernel family";
+        return CT_EINVAL;
+    }
+    if (e.activation < CT_ACT_IDENTITY || e.activation > CT_ACT_CLIP) {
+        *err = "unknown activation";
+        return CT_EINVAL;
+    }
+    return CT_OK;
+}
 
 // Events the caller asked to have recorded around the dominant kernel of each call on
 // this host thread (both null: none).

@@ -67,6 +67,19 @@ ct_status convtranspose_nd_noalloc(ct_kernel kernel, ct_dtype dtype, int nsp, in
                                    const int64_t *output_shape, const int64_t *kernel_shape, int64_t group,
                                    void *stream)
 {
+    ct::set_last_error(std::string());
+    {
+        ct::EnumArgs ea;
+        ea.kernel = ct::enum_int(kernel);
+        ea.dtype = ct::enum_int(dtype);
+        ea.auto_pad = ct::enum_int(auto_pad);
+        std::string ee;
+        const ct_status es = ct::check_enum_args(ea, &ee);
+        if (es != CT_OK) {
+            ct::set_last_error(ee);
+            return es;
+        }
+    }
     // host-side sizing first: invalid arguments and too large a workspace fail here,
     // before any device is touched
     size_t need = 0;

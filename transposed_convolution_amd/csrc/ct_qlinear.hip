@@ -160,6 +160,15 @@ ct_status qlinear_convtranspose_nd(ct_kernel kernel, int nsp, int channels_last,
 {
     using namespace ct;
     set_last_error(std::string());
+    for (const int t : {enum_int(x_type), enum_int(w_type), enum_int(y_type)}) {
+        EnumArgs ea;
+        ea.kernel = enum_int(kernel);
+        ea.dtype = t;
+        ea.auto_pad = enum_int(auto_pad);
+        std::string ee;
+        const ct_status es = check_enum_args(ea, &ee);
+        if (es != CT_OK) return q_fail(es, ee);
+    }
     if (!is_q8(x_type) || !is_q8(w_type) || !is_q8(y_type))
         return q_fail(CT_EUNSUPPORTED, "x, w and y types must be CT_UINT8 or CT_INT8");
     if (kernel != CT_KERNEL_AUTO && kernel != CT_KERNEL_DIRECT && kernel != CT_KERNEL_IGEMM)
