@@ -357,12 +357,15 @@ ct_status qlinear_convtranspose_nd(ct_kernel kernel, int nsp, int channels_last,
  * restores the automatic choice, the default: the largest tile that pads the output
  * channels little and still gives every compute unit a block.  tile = 0..4 forces one
  * block shape (output channels x output pixels): 0 = 256 x 256, 1 = 128 x 256,
- * 2 = 64 x 512, 3 = 64 x 256, 4 = 64 x 128 (the last two run two blocks per compute unit).
+ * 2 = 64 x 512, 3 = 64 x 256, 4 = 64 x 128 (the last two run two blocks per compute unit);
+ * tile = 5 forces the all-phase kernel (64 output channels x every residue class of a
+ * 4 x 32 box of the phase grid; strided calls with at least 4 residue classes and C/group
+ * a multiple of 32), which the automatic choice takes for such calls when M/group <= 64.
  * A forced tile that cannot serve a call (its input halo does not fit) makes an
  * implicit-GEMM call fail with CT_EUNSUPPORTED and CT_KERNEL_AUTO choose another kernel
  * family.  The setting is process-wide and is read when a call is made; changing it
  * while another host thread makes calls gives that thread either setting.
- * Returns CT_OK, or CT_EINVAL for a tile outside -1..4.
+ * Returns CT_OK, or CT_EINVAL for a tile outside -1..5.
  */
 ct_status convtranspose_set_igemm_tile(int tile);
 

@@ -435,6 +435,38 @@ def test_forced_tiles(T, tile, cl, integer):
     assert ran >= len(TILE_CASES) - 2, f"tile {tile} served only {ran} of {len(TILE_CASES)} shapes"
 
 
+ALLPHASE = [
+    # (x_shape, w_shape, attrs): strided calls with >= 4 residue classes and C/group a
+    # multiple of 32, on the all-phase kernel (every class of a box in one workgroup)
+    ((1, 32, 5, 8, 16), (32, 24, 3, 3, 3), dict(strides=[2, 2, 2], pads=[1] * 6, output_padding=[1, 1, 1])),
+    ((2, 64, 4, 9, 8), (64, 64, 3, 3, 3), dict(strides=[2, 2, 2], pads=[1] * 6)),
+    ((1, 32, 7, 40), (32, 48, 4, 4), dict(strides=[2, 2], pads=[1, 1, 1, 1])),
+    ((1, 32, 5, 16), (32, 16, 3, 3), dict(strides=[2, 2], pads=[1, 0, 0, 1])),
+    ((1, 64, 3, 6, 8), (64, 16, 3, 3, 3), dict(strides=[2, 2, 2], pads=[1] * 6, group=2)),
+    ((1, 32, 4, 6, 8), (32, 80, 2, 2, 2), dict(strides=[2, 2, 2])),
+    ((1, 32, 6, 8), (32, 40, 3, 3), dict(strides=[2, 2], dilations=[2, 2], pads=[1, 1, 1, 1])),
+    ((2, 32, 3, 24), (32, 8, 5, 3), dict(strides=[2, 2], pads=[2, 1, 2, 1], output_padding=[1, 1])),
+]
+
+
+@pytest.mark.parametrize("integer", [False, True], ids=["float", "int"])
+@pytest.mark.parametrize("cl", [False, True], ids=["nc", "cl"])
+@pytest.mark.parametrize("case", ALLPHASE, ids=lambda c: f"{c[0]}_{c[1]}")
+def test_allphase_kernel(T, case, cl, integer):
+    """The all-phase MFMA kernel (forced) on whole outputs; bit-exact on integer inputs."""
+    xs, ws, attrs = case
+    _log(f"[case] allphase cl={cl} x{xs} w{ws} {attrs} integer={integer}")
+    rng = np.random.default_rng(zlib.crc32(repr(case).encode()) + integer)
+    gen = (lambda sz: rng.integers(-2, 3, size=sz)) if integer else (lambda sz: rng.normal(size=sz))
+    x = gen(xs).astype(np.float16)
+    w = (gen(ws) * (1 if integer else 0.1)).astype(np.float16)
+    b = gen(ws[1] * attrs.get("group", 1)).astype(np.float16)
+    with forced_tile(T, "allphase"):
+        got = gpu_run(T, x, w, b, attrs, cl, "igemm")
+    assert got is not None, "the all-phase kernel must serve this shape"
+    check(got, O.convtranspose(x, w, b, **attrs), "f16", integer, f"allphase x{xs} w{ws} {attrs}")
+
+
 SINGLE_TAP = [
     # (x_shape, w_shape, attrs): M/group > 64 and at most one tap per axis in every phase
     # (kernels no longer than the stride, 1x1): the implicit-GEMM kernel's instance that

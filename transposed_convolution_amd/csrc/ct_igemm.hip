@@ -1392,7 +1392,8 @@ bool make_plan_cfg(const Geom &g, bool cl, const Config &cfg, Plan *pl, std::str
 // compute units x blocks per unit) a block; if none does, the least-padded tile with the
 // most blocks.
 constexpr int kNumConfigs = int(sizeof(kConfigs) / sizeof(kConfigs[0]));
-std::atomic<int> g_forced_tile{-1};  // index into kConfigs, or -1: automatic
+constexpr int kMpTile = kNumConfigs;  // the forced-tile index of the all-phase kernel
+std::atomic<int> g_forced_tile{-1};  // index into kConfigs, kMpTile, or -1: automatic
 
 // tiles with quantized (int8) instances
 bool has_q8(const Config &c) { return c == kWide || c == kHalf || c == kSmall; }
@@ -1400,6 +1401,10 @@ bool has_q8(const Config &c) { return c == kWide || c == kHalf || c == kSmall; }
 bool make_plan(const Geom &g, bool cl, Plan *pl, std::string *why, bool q8 = false)
 {
     const int forced = g_forced_tile.load(std::memory_order_relaxed);
+    if (forced == kMpTile) {
+        *why = "the all-phase kernel is forced";
+        return false;
+    }
     if (forced >= 0) {
         if (q8 && !has_q8(kConfigs[forced])) {
             *why = "the forced tile has no int8 instance";
@@ -1505,9 +1510,28 @@ bool igemm_supports(const Geom &g, ct_dtype dt, bool cl, const void *x, std::str
         *why = "x must be 16-byte aligned";
         return false;
     }
+    const int forced = g_forced_tile.load(std::memory_order_relaxed);
+    if (forced == kMpTile) return mphase_supports(g, cl, why);
     Plan pl;
-    return make_plan(g, cl, &pl, why);
+    if (make_plan(g, cl, &pl, why)) return true;
+    std::string mp_why;
+    return forced < 0 && mphase_supports(g, cl, &mp_why);
 }
+
+namespace {
+// The all-phase kernel serves strided calls with few output channels per group, where
+// the per-class kernel's blocks are short and every class re-reads the same input.
+bool use_mphase(const Geom &g, bool cl)
+{
+    const int forced = g_forced_tile.load(std::memory_order_relaxed);
+    std::string why;
+    if (forced == kMpTile) return true;
+    if (forced >= 0) return false;
+    Plan pl;
+    const bool classic = make_plan(g, cl, &pl, &why);
+    return mphase_supports(g, cl, &why) && (!classic || g.Mg <= 64);
+}
+}  // namespace
 
 size_t igemm_workspace_bytes(const Geom &g, ct_dtype dt)
 {
@@ -1520,10 +1544,11 @@ size_t igemm_workspace_bytes(const Geom &g, ct_dtype dt)
     for (const Config &c : kConfigs)
         for (const bool cl : {false, true})
             if (make_plan_cfg(g, cl, c, &pl, &why)) bytes = std::max(bytes, pl.ws_bytes);
+    for (const bool cl : {false, true}) bytes = std::max(bytes, mphase_workspace_bytes(g, cl));
     return bytes;
 }
 
-int igemm_tile_count() { return kNumConfigs; }
+int igemm_tile_count() { return kNumConfigs + 1; }
 
 void igemm_force_tile(int tile) { g_forced_tile.store(tile, std::memory_order_relaxed); }
 
@@ -1534,6 +1559,35 @@ ct_status launch_igemm(const Geom &g, ct_dtype dt, bool cl, const void *x, const
                        bool w_conv)
 {
     if (dt == CT_FLOAT32) return launch_igemm32(g, cl, x, w, bias, y, act, st, err);
+    if (use_mphase(g, cl)) {
+        const size_t need = mphase_workspace_bytes(g, cl);
+        if (need == 0) {
+            std::string why;
+            mphase_supports(g, cl, &why);
+            *err = why;
+            return CT_EUNSUPPORTED;
+        }
+        void *wsp = workspace;
+        if (!wsp) {
+            hipError_t e = scratch_malloc(&wsp, need, st);
+            if (e != hipSuccess) {
+                *err = std::string("workspace allocation failed: ") + hipGetErrorString(e);
+                return CT_EDEVICE;
+            }
+        } else if (ws_bytes < need) {
+            *err = "workspace is smaller than convtranspose_workspace_size() reports";
+            return CT_EINVAL;
+        }
+        ct_status s = launch_mphase(g, cl, x, w, bias, y, act, wsp, need, st, err, w_conv);
+        if (!workspace) {
+            const hipError_t f = hipFreeAsync(wsp, st);
+            if (s == CT_OK && f != hipSuccess) {
+                *err = std::string("scratch release failed: ") + hipGetErrorString(f);
+                s = CT_EDEVICE;
+            }
+        }
+        return s;
+    }
     Plan pl;
     if (!make_plan(g, cl, &pl, err)) return CT_EUNSUPPORTED;
     pl.a.act = act;
@@ -1582,6 +1636,30 @@ ct_status launch_igemm(const Geom &g, ct_dtype dt, bool cl, const void *x, const
     }
     if (e != hipSuccess) {
         *err = std::string("implicit-GEMM launch failed: ") + hipGetErrorString(e);
+        return CT_EDEVICE;
+    }
+    return CT_OK;
+}
+
+ct_status launch_pack_w_frag(const Geom &g, const void *w, void *wp, int Cgp, int Mgp, bool w_conv, hipStream_t st,
+                             std::string *err)
+{
+    PackArgs pa;
+    pa.G = int(g.G);
+    pa.Cg = int(g.Cg);
+    pa.Mg = int(g.Mg);
+    pa.Cgp = Cgp;
+    pa.Mgp = Mgp;
+    pa.T = int(g.taps());
+    pa.conv = w_conv ? 1 : 0;
+    pa.frag = 1;
+    pa.total = (long long)pa.G * (pa.Cgp / 8) * pa.Mgp * pa.T;
+    if (pa.total > 0)
+        hipLaunchKernelGGL(pack_w_kernel, dim3(unsigned((pa.total + 255) / 256)), dim3(256), 0, st,
+                           static_cast<const _Float16 *>(w), static_cast<_Float16 *>(wp), pa);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) {
+        *err = std::string("weight re-layout launch failed: ") + hipGetErrorString(e);
         return CT_EDEVICE;
     }
     return CT_OK;

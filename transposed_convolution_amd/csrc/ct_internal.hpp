@@ -221,6 +221,17 @@ int igemm_forced_tile();
 bool igemm32_supports(const Geom &g, bool cl, std::string *why);
 ct_status launch_igemm32(const Geom &g, bool cl, const void *x, const void *w, const void *bias, void *y,
                          const Act &act, hipStream_t st, std::string *err);
+// The all-phase kernel (ct_mphase.hip): strided calls with at least 4 residue classes,
+// C/group a multiple of 32; preferred when M/group <= 64.  Its packed weights are the
+// fragment-major packing of 64-channel tiles.
+bool mphase_supports(const Geom &g, bool cl, std::string *why);
+size_t mphase_workspace_bytes(const Geom &g, bool cl);
+ct_status launch_mphase(const Geom &g, bool cl, const void *x, const void *w, const void *bias, void *y,
+                        const Act &act, void *wsp, size_t ws_bytes, hipStream_t st, std::string *err, bool w_conv);
+// W (or a forward convolution's W, taps reversed) into the fragment-major packing with
+// Cgp input and Mgp output channels per group (zero padded).
+ct_status launch_pack_w_frag(const Geom &g, const void *w, void *wp, int Cgp, int Mgp, bool w_conv, hipStream_t st,
+                             std::string *err);
 // workspace: caller scratch of ws_bytes (>= igemm_workspace_bytes), or NULL to take
 // stream-ordered scratch from the library pool (scratch_malloc / hipFreeAsync on st).  w_conv (float16
 // only): w is a forward convolution's weight (M, C/group, k) and g the stride-1
