@@ -39,7 +39,7 @@ sys.path.insert(0, ROOT)
 METRIC = "ConvTranspose TFLOP/s (2*useful MACs) and % of MFMA/HBM roofline on 1 MI355X"
 PEAK_TFLOPS = {"f16": 2500.0, "f32": 157.3}   # dense MFMA peaks of MI355X
 PEAK_HBM_GBS = 8000.0
-KERNEL_SOURCES = {"igemm": ["ct_igemm.hip"], "grouped": ["ct_grouped.hip", "ct_depthwise.hip"],
+KERNEL_SOURCES = {"igemm": ["ct_igemm.hip", "ct_mphase.hip"], "grouped": ["ct_grouped.hip", "ct_depthwise.hip", "ct_dwcl.hip"],
                   "direct": ["ct_direct.hip"]}
 COPY_BYTES = 256 << 20  # calibration copy: 256 MiB read + 256 MiB written
 CALIBRATE_COPY = [False]  # --calibrate-copy: one plain copy before the timed steps
@@ -51,7 +51,7 @@ def log(*a):
 
 def workloads():
     import workloads as W
-    return {"c1": W.C1, "c2": W.C2, "c3": W.C3, "c4": W.C4, "c4_nhwc": W.C4_NHWC,
+    return {"c1": W.C1, "c2": W.C2, "c3": W.C3, "c3_nhwc": W.C3_NHWC, "c4": W.C4, "c4_nhwc": W.C4_NHWC,
             "c5_s1": W.C5_S1, "c5_s1_p1": W.C5_S1_P1, "c5_s2": W.C5_S2,
             "f2_k2s2": W.F2_K2S2, "f2_1x1": W.F2_1X1,
             # the forward convolution with the same W (the adjoint) of a configuration
@@ -409,7 +409,7 @@ def main():
 
 
 # Configurations timed after the headline one in the default run.
-EXTRA_CONFIGS = ("c4_nhwc", "c3", "c5_s1", "c5_s1_p1", "c5_s2")
+EXTRA_CONFIGS = ("c4_nhwc", "c3", "c3_nhwc", "c5_s1", "c5_s1_p1", "c5_s2")
 
 
 def time_workload(key, steps, warmup, rotate_arg):

@@ -84,11 +84,12 @@ def forced_tile(T, tile):
 # --------------------------------------------------------------------------------------
 # benchmark configurations
 # --------------------------------------------------------------------------------------
-WHOLE = [W.C1, W.C2, W.C3]
+WHOLE = [W.C1, W.C2, W.C3, W.C3_NHWC]
 FULL = [W.C4, W.C4_NHWC, W.C5_S1, W.C5_S1_P1, W.C5_S2]
 # the family the dispatcher must pick for each configuration (a silent fall-back to the
 # gather kernel would still be correct, so parity alone would not notice it)
-EXPECTED_FAMILY = {W.C1.name: "direct", W.C2.name: "igemm", W.C3.name: "grouped", W.C4.name: "igemm",
+EXPECTED_FAMILY = {W.C1.name: "direct", W.C2.name: "igemm", W.C3.name: "grouped", W.C3_NHWC.name: "grouped",
+                   W.C4.name: "igemm",
                    W.C4_NHWC.name: "igemm", W.C5_S1.name: "igemm", W.C5_S1_P1.name: "igemm", W.C5_S2.name: "igemm"}
 
 
@@ -355,6 +356,49 @@ def test_depthwise_shapes(T, case, integer):
         check(got, ref, "f16", integer, f"depthwise {kernel} x{xs} {attrs}")
     got = gpu_run(T, x, w, None, attrs, False, "grouped")
     check(got, ref_nb, "f16", integer, f"depthwise no-bias x{xs} {attrs}")
+
+
+DEPTHWISE_CL = [
+    # (x_shape, kernel shape, attrs): channels-last depthwise (group == C), float16, C a
+    # multiple of 8: the channels-last bandwidth kernel (ragged tiles, octet tiles of 32,
+    # residue classes with fewer taps, rank 1)
+    ((2, 64, 9, 13), (4, 4), dict(strides=[2, 2], pads=[1, 1, 1, 1])),
+    ((1, 32, 7, 10), (3, 3), dict(strides=[2, 2], pads=[1, 1, 1, 1], output_padding=[1, 1])),
+    ((2, 16, 5, 6), (3, 3), dict(pads=[1, 1, 1, 1])),
+    ((1, 264, 6, 9), (4, 4), dict(strides=[2, 2], pads=[1, 1, 1, 1])),
+    ((1, 40, 5, 7), (2, 2), dict(strides=[2, 2])),
+    ((1, 8, 6, 5), (2, 2), dict(pads=[0, 1, 1, 0])),
+    ((2, 24, 17), (4,), dict(strides=[2], pads=[1, 1])),
+    ((1, 16, 9), (3,), dict(strides=[2], pads=[1, 0], output_padding=[1])),
+    ((1, 8, 11), (3,), dict(pads=[1, 1])),
+    ((1, 16, 4, 8), (4, 4), dict(strides=[2, 2], auto_pad="SAME_LOWER")),
+]
+
+
+@pytest.mark.parametrize("integer", [False, True], ids=["float", "int"])
+@pytest.mark.parametrize("case", DEPTHWISE_CL, ids=lambda c: f"{c[0]}_k{c[1]}_{sorted(c[2].items())}")
+def test_depthwise_channels_last(T, case, integer):
+    """Channels-last depthwise calls on the grouped family's channels-last kernel (the
+    dispatcher must pick it) against the oracle on whole outputs, with and without bias."""
+    xs, ks, attrs = case
+    C = xs[1]
+    attrs = dict(attrs, group=C)
+    _log(f"[case] depthwise channels-last x{xs} k{ks} {attrs} integer={integer}")
+    rng = np.random.default_rng(zlib.crc32(repr(case).encode()) + integer)
+    gen = (lambda sz: rng.integers(-2, 3, size=sz)) if integer else (lambda sz: rng.normal(size=sz))
+    x = gen(xs).astype(np.float16)
+    w = (gen((C, 1) + tuple(ks)) * (1 if integer else 0.3)).astype(np.float16)
+    b = gen(C).astype(np.float16)
+    dev = torch.device("cuda:0")
+    tx = T.to_channels_last(torch.from_numpy(x).to(dev))
+    assert T.convtranspose_select_kernel(tx, torch.from_numpy(w).to(dev), torch.from_numpy(b).to(dev),
+                                         channels_last=True, **attrs) == "grouped"
+    ref = O.convtranspose(x, w, b, **attrs)
+    for kernel in ("grouped", "auto"):
+        got = gpu_run(T, x, w, b, attrs, True, kernel)
+        check(got, ref, "f16", integer, f"depthwise channels-last {kernel} x{xs} {attrs}")
+    got = gpu_run(T, x, w, None, attrs, True, "grouped")
+    check(got, O.convtranspose(x, w, None, **attrs), "f16", integer, f"depthwise channels-last no-bias x{xs}")
 
 
 PAIRS = [

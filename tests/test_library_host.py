@@ -218,6 +218,7 @@ def test_dispatcher_choices(T):
     assert pick(W.C1, dtype=0) == "direct"
     assert pick(W.C2, dtype=0) == "igemm"     # float32 implicit GEMM on MFMA
     assert pick(W.C3) == "grouped"            # the depthwise specialisation of the grouped family
+    assert pick(W.C3_NHWC, cl=1) == "grouped"  # its channels-last kernel
     assert pick(W.C4) == "igemm"
     assert pick(W.C4_NHWC, cl=1) == "igemm"
     for wl in (W.C5_S1, W.C5_S1_P1, W.C5_S2):

@@ -239,6 +239,7 @@ bool make_gplan(const Geom &g, size_t esz, GPlan *pl, std::string *why)
 
 bool grouped_supports(const Geom &g, ct_dtype dt, bool cl, const void *x)
 {
+    if (g.G >= 2 && dwcl_supports(g, dt, cl, x)) return true;
     if (cl || g.G < 2 || g.Cg > 8 || g.Mg > 8 || g.L[1] * g.L[2] == 0) return false;
     if (depthwise_supports(g, dt, cl, x)) return true;
     GPlan pl;
@@ -254,6 +255,7 @@ ct_status launch_grouped(const Geom &g, ct_dtype dt, bool cl, const void *x, con
         return CT_EUNSUPPORTED;
     }
     if (depthwise_supports(g, dt, cl, x)) return launch_depthwise(g, dt, cl, x, w, bias, y, act, st, err);
+    if (dwcl_supports(g, dt, cl, x)) return launch_dwcl(g, x, w, bias, y, act, st, err);
     GPlan pl;
     if (!make_gplan(g, dt == CT_FLOAT16 ? 2 : 4, &pl, err)) return CT_EUNSUPPORTED;
     pl.a.act = act;

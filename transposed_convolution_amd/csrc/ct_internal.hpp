@@ -210,6 +210,11 @@ ct_status launch_depthwise(const Geom &g, ct_dtype dt, bool cl, const void *x, c
                            const void *bias, void *y, const Act &act, hipStream_t st, std::string *err);
 ct_status launch_grouped(const Geom &g, ct_dtype dt, bool cl, const void *x, const void *w,
                          const void *bias, void *y, const Act &act, hipStream_t st, std::string *err);
+// Channels-last depthwise specialisation inside the grouped family (float16, one channel
+// in and out per group, C a multiple of 8, spatial rank 1 or 2, strides up to 2).
+bool dwcl_supports(const Geom &g, ct_dtype dt, bool cl, const void *x);
+ct_status launch_dwcl(const Geom &g, const void *x, const void *w, const void *bias, void *y, const Act &act,
+                      hipStream_t st, std::string *err);
 bool igemm_supports(const Geom &g, ct_dtype dt, bool cl, const void *x, std::string *why);
 size_t igemm_workspace_bytes(const Geom &g, ct_dtype dt);
 // Tile configurations of the float16 implicit-GEMM kernel: how many there are, and a

@@ -116,6 +116,7 @@ C4 = Workload(
     "c4_2d_f16_decoder_s2", "f16", (8, 512, 64, 64), (512, 256, 4, 4), True,
     dict(strides=[2, 2], pads=[1, 1, 1, 1], group=1),
     ("N", 0.0, 1.0), ("N", 0.0, 1.0 / math.sqrt(512 * 16)), ("N", 0.0, 1.0), seed=4)
+C3_NHWC = C3.with_(name="c3_2d_f16_depthwise_s2_nhwc", channels_last=True)
 C4_NHWC = C4.with_(name="c4_2d_f16_decoder_s2_nhwc", channels_last=True)
 C5_S1 = Workload(
     "c5_3d_f16_s1", "f16", (2, 128, 16, 32, 32), (128, 64, 3, 3, 3), True,
@@ -127,7 +128,7 @@ C5_S2 = C5_S1.with_(
     name="c5_3d_f16_s2_op1",
     attrs=dict(strides=[2, 2, 2], pads=[1] * 6, output_padding=[1, 1, 1], group=1), note="")
 
-CONFIGS = {w.name: w for w in (C1, C2, C3, C4, C4_NHWC, C5_S1, C5_S1_P1, C5_S2)}
+CONFIGS = {w.name: w for w in (C1, C2, C3, C3_NHWC, C4, C4_NHWC, C5_S1, C5_S1_P1, C5_S2)}
 
 # Extra shapes (not benchmark configurations): the decoder tensors of C4 with kernels no
 # longer than the stride, where every output receives at most one tap per axis.
