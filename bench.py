@@ -43,6 +43,7 @@ KERNEL_SOURCES = {"igemm": ["ct_igemm.hip", "ct_mphase.hip"], "grouped": ["ct_gr
                   "direct": ["ct_direct.hip"]}
 COPY_BYTES = 256 << 20  # calibration copy: 256 MiB read + 256 MiB written
 CALIBRATE_COPY = [False]  # --calibrate-copy: one plain copy before the timed steps
+FORCE = ["auto", None]     # --kernel, --igemm-tile
 
 
 def log(*a):
@@ -353,6 +354,9 @@ def main():
     ap.add_argument("--no-extras", action="store_true",
                     help="time only --workload (the default c4 run also times C4 channels-last, C3 and C5)")
     ap.add_argument("--cpu-images", type=int, default=0, help="images in the oracle sample (0: all)")
+    ap.add_argument("--family", default="auto", choices=["auto", "direct", "grouped", "igemm"],
+                    help="kernel family to force (default: the dispatcher's choice)")
+    ap.add_argument("--igemm-tile", default=None, help="force one block shape of the float16 MFMA family")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run one plain device copy of 256 MiB (counter calibration)")
     ap.add_argument("--pmc-summary", default="", help="rocprofv3 output dir to summarise (no GPU use)")
@@ -379,6 +383,9 @@ def main():
     if args.workload.startswith("f4_int8"):
         return bench_quant(args)
     CALIBRATE_COPY[0] = args.calibrate_copy
+    FORCE[0], FORCE[1] = args.family, args.igemm_tile
+    if args.igemm_tile:
+        T.set_igemm_tile(args.igemm_tile)
     head = time_workload(args.workload, args.steps, args.warmup, args.rotate)
     wl = head.pop("_wl")
     inputs = head.pop("_inputs")
@@ -386,6 +393,8 @@ def main():
     if args.workload == "c4" and not args.no_extras:
         # the other benchmark configurations, each timed the same way in its own
         # dispatcher-chosen launch configuration (C3 with rotated buffer sets)
+        FORCE[0], FORCE[1] = "auto", None
+        T.set_igemm_tile(None)
         for key in EXTRA_CONFIGS:
             r = time_workload(key, args.steps, args.warmup, 0)
             r.pop("_wl")
@@ -438,13 +447,14 @@ def time_workload(key, steps, warmup, rotate_arg):
     tx = to_dev(x)
     tw = torch.from_numpy(w).to(dev)
     tb = None if b is None else torch.from_numpy(b).to(dev)
-    kernel = T.convtranspose_select_kernel(tx, tw, tb, channels_last=wl.channels_last, **wl.attrs)
+    kernel = T.convtranspose_select_kernel(tx, tw, tb, channels_last=wl.channels_last, **wl.attrs) \
+        if FORCE[0] == "auto" else FORCE[0]
     bound = "mfma" if kernel == "igemm" else "hbm"
     rotate = rotate_arg or (1 if bound == "mfma" else 4)
     plans = []
     for r in range(rotate):
         xr = tx if r == 0 else tx.clone()
-        plans.append(T.ConvTransposePlan(xr, tw, tb, channels_last=wl.channels_last, **wl.attrs))
+        plans.append(T.ConvTransposePlan(xr, tw, tb, channels_last=wl.channels_last, kernel=FORCE[0], **wl.attrs))
     log(f"workload {wl.name}: x{wl.x_shape} w{wl.w_shape} -> y{yshape}, kernel {kernel}, "
         f"{macs / 1e9:.2f} GMAC, {rotate} buffer set(s)")
 
@@ -510,7 +520,8 @@ def time_workload(key, steps, warmup, rotate_arg):
         "config": {"workload": f"{wl.name}: X{list(wl.x_shape)} W{list(wl.w_shape)} "
                                f"{'bias ' if wl.has_bias else ''}{wl.attrs} -> Y{list(yshape)} "
                                f"{'channels-last' if wl.channels_last else 'NCHW'}",
-                   "kernel": kernel, "useful_macs": macs, "accumulate": "f32", "buffer_sets": rotate,
+                   "kernel": kernel, "igemm_tile": FORCE[1], "useful_macs": macs, "accumulate": "f32",
+                   "buffer_sets": rotate,
                    "parity_max_rel_err": err},
         "roofline": {"bound": bound, "achieved": round(achieved, 2), "peak": peak, "unit": unit,
                      "frac": round(achieved / peak, 4), "traffic": traffic,

@@ -26,6 +26,7 @@ namespace {
 
 constexpr int kThreads32 = 256;
 constexpr int kBM = 64, kBN = 64, kKC = 16;  // tile: channels x pixels x depth per step
+constexpr int kRPT = kKC / 4;                 // depth rows gathered per thread and step
 constexpr int kMaxRes32 = 16, kMaxTap32 = 16, kMaxPh32 = 64;
 
 typedef float f32x16 __attribute__((ext_vector_type(16)));
@@ -74,7 +75,7 @@ __global__ __launch_bounds__(kThreads32) void igemm32_kernel(const float *__rest
     const int depth = p.Cg * T;
     const int Ktot = p.K[0] * p.K[1] * p.K[2];
 
-    // ---- this thread's gather slots: one channel (A) and one pixel (B), 4 depth rows ----
+    // ---- this thread's gather slots: one channel (A) and one pixel (B), kRPT depth rows ----
     const int col = tid % 64, row0 = tid / 64;  // depth rows row0 + 4 i
     const int m_a = mt * kBM + col;              // output channel inside the group
     int jn, jj[3];
@@ -92,38 +93,49 @@ __global__ __launch_bounds__(kThreads32) void igemm32_kernel(const float *__rest
     }
     const size_t in_pix = size_t(p.L[0]) * p.L[1] * p.L[2];
 
-    float areg[4], breg[4];
+    float areg[kRPT], breg[kRPT];
+    // Every load is issued unconditionally from a valid address (element 0 when the slot
+    // is padding or outside the input; the kernel never runs on an empty input or empty
+    // weights) and masked afterwards: loads under a branch are waited for one at a time.
     auto gather = [&](int step) {
+        float av[kRPT], bv[kRPT];
+        bool aok[kRPT], bok[kRPT];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
+        for (int i = 0; i < kRPT; ++i) {
             const int d = step * kKC + row0 + 4 * i;
-            float av = 0.0f, bv = 0.0f;
-            if (d < depth) {
-                const int c = d / T;
-                int t = d - c * T;
-                const int t2 = t % nt[2];
-                t /= nt[2];
-                const int t1 = t % nt[1];
-                const int t0 = t / nt[1];
-                const int k0 = p.tk0[0][r[0]] + t0 * p.kstep[0], k1 = p.tk0[1][r[1]] + t1 * p.kstep[1],
-                          k2 = p.tk0[2][r[2]] + t2 * p.kstep[2];
-                const int gc = g * p.Cg + c;
-                if (m_a < p.Mg) av = w[(size_t(gc) * p.Mg + m_a) * Ktot + (k0 * p.K[1] + k1) * p.K[2] + k2];
-                const int i0 = jj[0] + p.tb0[0][r[0]] - t0 * p.bstep[0];
-                const int i1 = jj[1] + p.tb0[1][r[1]] - t1 * p.bstep[1];
-                const int i2 = jj[2] + p.tb0[2][r[2]] - t2 * p.bstep[2];
-                if (q_ok && i0 >= 0 && i0 < p.L[0] && i1 >= 0 && i1 < p.L[1] && i2 >= 0 && i2 < p.L[2]) {
-                    const size_t pix = (size_t(i0) * p.L[1] + i1) * p.L[2] + i2;
-                    bv = p.cl ? x[(size_t(jn) * in_pix + pix) * p.C + gc] : x[(size_t(jn) * p.C + gc) * in_pix + pix];
-                }
-            }
-            areg[i] = av;
-            breg[i] = bv;
+            const bool din = d < depth;
+            const int dd = din ? d : 0;
+            const int c = dd / T;
+            int t = dd - c * T;
+            const int t2 = t % nt[2];
+            t /= nt[2];
+            const int t1 = t % nt[1];
+            const int t0 = t / nt[1];
+            const int k0 = p.tk0[0][r[0]] + t0 * p.kstep[0], k1 = p.tk0[1][r[1]] + t1 * p.kstep[1],
+                      k2 = p.tk0[2][r[2]] + t2 * p.kstep[2];
+            const int gc = g * p.Cg + c;
+            aok[i] = din && m_a < p.Mg;
+            const size_t aoff = aok[i] ? (size_t(gc) * p.Mg + m_a) * Ktot + (k0 * p.K[1] + k1) * p.K[2] + k2 : 0;
+            av[i] = w[aoff];
+            const int i0 = jj[0] + p.tb0[0][r[0]] - t0 * p.bstep[0];
+            const int i1 = jj[1] + p.tb0[1][r[1]] - t1 * p.bstep[1];
+            const int i2 = jj[2] + p.tb0[2][r[2]] - t2 * p.bstep[2];
+            bok[i] = din && q_ok && i0 >= 0 && i0 < p.L[0] && i1 >= 0 && i1 < p.L[1] && i2 >= 0 && i2 < p.L[2];
+            const size_t pix = bok[i] ? (size_t(i0) * p.L[1] + i1) * p.L[2] + i2 : 0;
+            const size_t boff = !bok[i] ? 0
+                                : p.cl ? (size_t(jn) * in_pix + pix) * p.C + gc
+                                       : (size_t(jn) * p.C + gc) * in_pix + pix;
+            bv[i] = x[boff];
+        }
+#pragma unroll
+        for (int i = 0; i < kRPT; ++i) {
+            areg[i] = aok[i] ? av[i] : 0.0f;
+            breg[i] = bok[i] ? bv[i] : 0.0f;
         }
     };
     auto stage = [&](int buf) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
+        for (int i = 0; i < kRPT; ++i) {
             As[buf][row0 + 4 * i][col] = areg[i];
             Bs[buf][row0 + 4 * i][col] = breg[i];
         }
@@ -255,6 +267,11 @@ bool make_plan32(const Geom &g, bool cl, I32Args *a, int *blocks, std::string *w
 
 bool igemm32_supports(const Geom &g, bool cl, std::string *why)
 {
+    // the gathers load element 0 of x and w for masked slots: both must be non-empty
+    if (g.x_elems() <= 0 || g.w_elems() <= 0) {
+        *why = "empty input or weights";
+        return false;
+    }
     I32Args a;
     int blocks = 0;
     return make_plan32(g, cl, &a, &blocks, why);
