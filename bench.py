@@ -39,7 +39,7 @@ sys.path.insert(0, ROOT)
 METRIC = "ConvTranspose TFLOP/s (2*useful MACs) and % of MFMA/HBM roofline on 1 MI355X"
 PEAK_TFLOPS = {"f16": 2500.0, "f32": 157.3}   # dense MFMA peaks of MI355X
 PEAK_HBM_GBS = 8000.0
-KERNEL_SOURCES = {"igemm": ["ct_igemm.hip", "ct_mphase.hip"], "grouped": ["ct_grouped.hip", "ct_depthwise.hip", "ct_dwcl.hip"],
+KERNEL_SOURCES = {"igemm": ["ct_igemm.hip", "ct_mphase.hip", "ct_tapsplit.hip"], "grouped": ["ct_grouped.hip", "ct_depthwise.hip", "ct_dwcl.hip"],
                   "direct": ["ct_direct.hip"]}
 COPY_BYTES = 256 << 20  # calibration copy: 256 MiB read + 256 MiB written
 CALIBRATE_COPY = [False]  # --calibrate-copy: one plain copy before the timed steps

@@ -360,12 +360,15 @@ ct_status qlinear_convtranspose_nd(ct_kernel kernel, int nsp, int channels_last,
  * 2 = 64 x 512, 3 = 64 x 256, 4 = 64 x 128 (the last two run two blocks per compute unit);
  * tile = 5 forces the all-phase kernel (64 output channels x every residue class of a
  * 4 x 32 box of the phase grid; strided calls with at least 4 residue classes and C/group
- * a multiple of 32), which the automatic choice takes for such calls when M/group <= 64.
- * A forced tile that cannot serve a call (its input halo does not fit) makes an
+ * a multiple of 32), which the automatic choice takes for such calls when M/group <= 64;
+ * tile = 6 forces the tap-split kernel (64 output channels x 64 consecutive output
+ * positions, the taps split over the block's waves; stride 1 on every axis, C/group a
+ * multiple of 32, at most 32 taps), which the automatic choice takes for 3-D stride-1
+ * calls when M/group <= 64.  A forced tile that cannot serve a call (its input halo does not fit) makes an
  * implicit-GEMM call fail with CT_EUNSUPPORTED and CT_KERNEL_AUTO choose another kernel
  * family.  The setting is process-wide and is read when a call is made; changing it
  * while another host thread makes calls gives that thread either setting.
- * Returns CT_OK, or CT_EINVAL for a tile outside -1..5.
+ * Returns CT_OK, or CT_EINVAL for a tile outside -1..6.
  */
 ct_status convtranspose_set_igemm_tile(int tile);
 

@@ -511,6 +511,38 @@ def test_allphase_kernel(T, case, cl, integer):
     check(got, O.convtranspose(x, w, b, **attrs), "f16", integer, f"allphase x{xs} w{ws} {attrs}")
 
 
+TAPSPLIT = [
+    # (x_shape, w_shape, attrs): stride 1, C/group a multiple of 32, on the tap-split kernel
+    # (64 consecutive output positions x 64 channels per workgroup, taps split over waves)
+    ((1, 32, 3, 6, 16), (32, 24, 3, 3, 3), dict()),                                   # rows of 18 flattened
+    ((2, 64, 4, 5, 8), (64, 64, 3, 3, 3), dict(pads=[1] * 6)),
+    ((1, 32, 2, 3, 72), (32, 40, 2, 3, 3), dict(dilations=[1, 2, 1], pads=[0, 1, 1, 0, 0, 2])),  # runs in a row
+    ((1, 64, 5, 16), (64, 96, 3, 3), dict(pads=[1, 1, 1, 1])),                        # two channel tiles
+    ((1, 64, 3, 4, 8), (64, 16, 3, 3, 3), dict(group=2)),
+    ((2, 32, 40), (32, 32, 5), dict(dilations=[3], pads=[2, 1])),
+    ((1, 32, 2, 2, 8), (32, 16, 1, 1, 1), dict()),                                   # one tap: idle waves
+    ((1, 128, 3, 6, 32), (128, 64, 3, 3, 3), dict()),                                # C5's channels and rows
+]
+
+
+@pytest.mark.parametrize("integer", [False, True], ids=["float", "int"])
+@pytest.mark.parametrize("cl", [False, True], ids=["nc", "cl"])
+@pytest.mark.parametrize("case", TAPSPLIT, ids=lambda c: f"{c[0]}_{c[1]}")
+def test_tapsplit_kernel(T, case, cl, integer):
+    """The tap-split MFMA kernel (forced) on whole outputs; bit-exact on integer inputs."""
+    xs, ws, attrs = case
+    _log(f"[case] tapsplit cl={cl} x{xs} w{ws} {attrs} integer={integer}")
+    rng = np.random.default_rng(zlib.crc32(repr(case).encode()) + integer + 11)
+    gen = (lambda sz: rng.integers(-2, 3, size=sz)) if integer else (lambda sz: rng.normal(size=sz))
+    x = gen(xs).astype(np.float16)
+    w = (gen(ws) * (1 if integer else 0.1)).astype(np.float16)
+    b = gen(ws[1] * attrs.get("group", 1)).astype(np.float16)
+    with forced_tile(T, "tapsplit"):
+        got = gpu_run(T, x, w, b, attrs, cl, "igemm")
+    assert got is not None, "the tap-split kernel must serve this shape"
+    check(got, O.convtranspose(x, w, b, **attrs), "f16", integer, f"tapsplit x{xs} w{ws} {attrs}")
+
+
 SINGLE_TAP = [
     # (x_shape, w_shape, attrs): M/group > 64 and at most one tap per axis in every phase
     # (kernels no longer than the stride, 1x1): the implicit-GEMM kernel's instance that

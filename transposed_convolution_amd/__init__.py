@@ -379,7 +379,7 @@ def convtranspose_nd_noalloc(x: torch.Tensor, w: torch.Tensor, bias: Optional[to
     return out
 
 
-IGEMM_TILES = ("256x256", "128x256", "64x512", "64x256", "64x128", "allphase")
+IGEMM_TILES = ("256x256", "128x256", "64x512", "64x256", "64x128", "allphase", "tapsplit")
 
 
 def set_igemm_tile(tile: Optional[str]) -> None:

@@ -96,12 +96,6 @@ struct IgArgs {
 
 __device__ __forceinline__ int floor_div8(int v) { return v >= 0 ? v / 8 : -((-v + 7) / 8); }
 
-// Block b goes to XCD b % 8; give each XCD a contiguous range of work indices.
-__device__ __forceinline__ int xcd_remap(int b, int nb)
-{
-    const int q = nb >> 3, rem = nb & 7, x = b & 7, k = b >> 3;
-    return (x < rem ? x * (q + 1) : rem * (q + 1) + (x - rem) * q) + k;
-}
 
 // Tile geometry of the phase pixels (j1, j2) a block covers.
 struct Tile {
@@ -1392,8 +1386,9 @@ bool make_plan_cfg(const Geom &g, bool cl, const Config &cfg, Plan *pl, std::str
 // compute units x blocks per unit) a block; if none does, the least-padded tile with the
 // most blocks.
 constexpr int kNumConfigs = int(sizeof(kConfigs) / sizeof(kConfigs[0]));
-constexpr int kMpTile = kNumConfigs;  // the forced-tile index of the all-phase kernel
-std::atomic<int> g_forced_tile{-1};  // index into kConfigs, kMpTile, or -1: automatic
+constexpr int kMpTile = kNumConfigs;      // the forced-tile index of the all-phase kernel
+constexpr int kTsTile = kNumConfigs + 1;  // the forced-tile index of the tap-split kernel
+std::atomic<int> g_forced_tile{-1};  // index into kConfigs, kMpTile, kTsTile, or -1: automatic
 
 // tiles with quantized (int8) instances
 bool has_q8(const Config &c) { return c == kWide || c == kHalf || c == kSmall; }
@@ -1401,8 +1396,8 @@ bool has_q8(const Config &c) { return c == kWide || c == kHalf || c == kSmall; }
 bool make_plan(const Geom &g, bool cl, Plan *pl, std::string *why, bool q8 = false)
 {
     const int forced = g_forced_tile.load(std::memory_order_relaxed);
-    if (forced == kMpTile) {
-        *why = "the all-phase kernel is forced";
+    if (forced == kMpTile || forced == kTsTile) {
+        *why = forced == kMpTile ? "the all-phase kernel is forced" : "the tap-split kernel is forced";
         return false;
     }
     if (forced >= 0) {
@@ -1512,10 +1507,11 @@ bool igemm_supports(const Geom &g, ct_dtype dt, bool cl, const void *x, std::str
     }
     const int forced = g_forced_tile.load(std::memory_order_relaxed);
     if (forced == kMpTile) return mphase_supports(g, cl, why);
+    if (forced == kTsTile) return tapsplit_supports(g, cl, why);
     Plan pl;
     if (make_plan(g, cl, &pl, why)) return true;
-    std::string mp_why;
-    return forced < 0 && mphase_supports(g, cl, &mp_why);
+    std::string alt_why;
+    return forced < 0 && (mphase_supports(g, cl, &alt_why) || tapsplit_supports(g, cl, &alt_why));
 }
 
 namespace {
@@ -1531,6 +1527,19 @@ bool use_mphase(const Geom &g, bool cl)
     const bool classic = make_plan(g, cl, &pl, &why);
     return mphase_supports(g, cl, &why) && (!classic || g.Mg <= 64);
 }
+// The tap-split kernel serves stride-1 3-D calls with few output channels per group, where
+// the phase kernel's blocks repeat every weight load in each wave and reload the input
+// halo for every tap group.
+bool use_tapsplit(const Geom &g, bool cl)
+{
+    const int forced = g_forced_tile.load(std::memory_order_relaxed);
+    std::string why;
+    if (forced == kTsTile) return true;
+    if (forced >= 0) return false;
+    if (!tapsplit_supports(g, cl, &why)) return false;
+    Plan pl;
+    return !make_plan(g, cl, &pl, &why) || (g.nsp == 3 && g.Mg <= 64);
+}
 }  // namespace
 
 size_t igemm_workspace_bytes(const Geom &g, ct_dtype dt)
@@ -1544,11 +1553,12 @@ size_t igemm_workspace_bytes(const Geom &g, ct_dtype dt)
     for (const Config &c : kConfigs)
         for (const bool cl : {false, true})
             if (make_plan_cfg(g, cl, c, &pl, &why)) bytes = std::max(bytes, pl.ws_bytes);
-    for (const bool cl : {false, true}) bytes = std::max(bytes, mphase_workspace_bytes(g, cl));
+    for (const bool cl : {false, true})
+        bytes = std::max({bytes, mphase_workspace_bytes(g, cl), tapsplit_workspace_bytes(g, cl)});
     return bytes;
 }
 
-int igemm_tile_count() { return kNumConfigs + 1; }
+int igemm_tile_count() { return kNumConfigs + 2; }
 
 void igemm_force_tile(int tile) { g_forced_tile.store(tile, std::memory_order_relaxed); }
 
@@ -1559,11 +1569,15 @@ ct_status launch_igemm(const Geom &g, ct_dtype dt, bool cl, const void *x, const
                        bool w_conv)
 {
     if (dt == CT_FLOAT32) return launch_igemm32(g, cl, x, w, bias, y, act, st, err);
-    if (use_mphase(g, cl)) {
-        const size_t need = mphase_workspace_bytes(g, cl);
+    const bool mp = use_mphase(g, cl);
+    if (mp || use_tapsplit(g, cl)) {
+        const size_t need = mp ? mphase_workspace_bytes(g, cl) : tapsplit_workspace_bytes(g, cl);
         if (need == 0) {
             std::string why;
-            mphase_supports(g, cl, &why);
+            if (mp)
+                mphase_supports(g, cl, &why);
+            else
+                tapsplit_supports(g, cl, &why);
             *err = why;
             return CT_EUNSUPPORTED;
         }
@@ -1578,7 +1592,8 @@ ct_status launch_igemm(const Geom &g, ct_dtype dt, bool cl, const void *x, const
             *err = "workspace is smaller than convtranspose_workspace_size() reports";
             return CT_EINVAL;
         }
-        ct_status s = launch_mphase(g, cl, x, w, bias, y, act, wsp, need, st, err, w_conv);
+        ct_status s = mp ? launch_mphase(g, cl, x, w, bias, y, act, wsp, need, st, err, w_conv)
+                         : launch_tapsplit(g, cl, x, w, bias, y, act, wsp, need, st, err, w_conv);
         if (!workspace) {
             const hipError_t f = hipFreeAsync(wsp, st);
             if (s == CT_OK && f != hipSuccess) {

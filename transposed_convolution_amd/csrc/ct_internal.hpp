@@ -17,6 +17,27 @@ namespace ct {
 // exactly one tap and one output position and changes nothing else.
 constexpr int kAxes = 3;
 
+// Workgroup b of a launch goes to XCD b % 8 (8 XCDs, each with its own L2); xcd_remap
+// gives the workgroups of each XCD a contiguous range of the nb work indices, so the
+// data neighbouring work items share stays in one L2.
+__device__ __forceinline__ int xcd_remap(int b, int nb)
+{
+    const int q = nb >> 3, rem = nb & 7, x = b & 7, k = b >> 3;
+    return (x < rem ? x * (q + 1) : rem * (q + 1) + (x - rem) * q) + k;
+}
+
+// Division of a non-negative int u by a wave-uniform divisor d >= 1 with one
+// multiply-high instead of the GPU's long integer-division sequence: with
+// m = ceil(2^32 / d), (u * m) >> 32 = floor(u / d) exactly while u * d < 2^32 (the
+// rounding error of m adds less than 1/d to u / d).  Callers keep u * d below 2^32.
+struct UDiv {
+    unsigned m;
+    int d;
+    __device__ __forceinline__ explicit UDiv(int dv) : m(dv > 1 ? unsigned(0xffffffffu / unsigned(dv)) + 1u : 0u), d(dv) {}
+    __device__ __forceinline__ int div(int u) const { return d > 1 ? int(__umulhi(unsigned(u), m)) : u; }
+    __device__ __forceinline__ int mod(int u) const { return u - div(u) * d; }
+};
+
 // Resolved problem geometry (ONNX attribute table applied; README "Attributes").
 struct Geom {
     int nsp = 0;                                  // rank as given (1..3)
@@ -233,6 +254,13 @@ bool mphase_supports(const Geom &g, bool cl, std::string *why);
 size_t mphase_workspace_bytes(const Geom &g, bool cl);
 ct_status launch_mphase(const Geom &g, bool cl, const void *x, const void *w, const void *bias, void *y,
                         const Act &act, void *wsp, size_t ws_bytes, hipStream_t st, std::string *err, bool w_conv);
+// The tap-split kernel (ct_tapsplit.hip): stride 1 on every axis, C/group a multiple of
+// 32, at most 32 taps, the input window of a 64-position box in LDS; preferred for 3-D
+// calls with M/group <= 64.  Its packed weights are the fragment-major packing.
+bool tapsplit_supports(const Geom &g, bool cl, std::string *why);
+size_t tapsplit_workspace_bytes(const Geom &g, bool cl);
+ct_status launch_tapsplit(const Geom &g, bool cl, const void *x, const void *w, const void *bias, void *y,
+                          const Act &act, void *wsp, size_t ws_bytes, hipStream_t st, std::string *err, bool w_conv);
 // W (or a forward convolution's W, taps reversed) into the fragment-major packing with
 // Cgp input and Mgp output channels per group (zero padded).
 ct_status launch_pack_w_frag(const Geom &g, const void *w, void *wp, int Cgp, int Mgp, bool w_conv, hipStream_t st,

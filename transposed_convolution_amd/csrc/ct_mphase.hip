@@ -107,14 +107,16 @@ __global__ __launch_bounds__(kThreads, 1) void mphase_kernel(const _Float16 *x, 
             // 16-byte vectors of 8 channels, channels innermost in both places
             const int cv = p.Cg / 8;
             const int items = pos * cv;
+            const UDiv dcv(cv), dhc(p.HC), dhr(p.HR);  // item -> (position, octet) -> (plane, row, column)
             const _Float16 *xg = x + size_t(g) * p.Cg;
             for (int base = 0; base < items; base += kThreads * kHaloVec) {
                 u32x4 v[kHaloVec];
 #pragma unroll
                 for (int k = 0; k < kHaloVec; ++k) {
                     const int u = base + tid + k * kThreads;
-                    const int q = u / cv, c8 = u - q * cv;
-                    const int hc = q % p.HC, hr = (q / p.HC) % p.HR, hp = q / (p.HC * p.HR);
+                    const int q = dcv.div(u), c8 = u - q * cv;
+                    const int qr = dhc.div(q), hc = q - qr * p.HC;
+                    const int hp = dhr.div(qr), hr = qr - hp * p.HR;
                     const int i0 = i0o + hp, i1 = i1o + hr, i2 = i2o + hc;
                     const bool ok = u < items && i0 >= 0 && i0 < L0 && i1 >= 0 && i1 < L1 && i2 >= 0 && i2 < L2;
                     const size_t off = ok ? (((size_t(n) * L0 + i0) * L1 + i1) * L2 + i2) * p.C + c8 * 8 : 0;
@@ -125,7 +127,7 @@ __global__ __launch_bounds__(kThreads, 1) void mphase_kernel(const _Float16 *x, 
                 for (int k = 0; k < kHaloVec; ++k) {
                     const int u = base + tid + k * kThreads;
                     if (u < items) {
-                        const int q = u / cv, c8 = u - q * cv;
+                        const int q = dcv.div(u), c8 = u - q * cv;
                         *reinterpret_cast<u32x4 *>(lds + q * p.pitch + c8 * 16) = v[k];
                     }
                 }
@@ -139,6 +141,15 @@ __global__ __launch_bounds__(kThreads, 1) void mphase_kernel(const _Float16 *x, 
             const int nvc = floor_div8(i2o + p.HC + 7) - va;
             const int oct = p.Cg / 8;
             const int items = p.HP * p.HR * nvc * oct;
+            const UDiv dnv(nvc), dhr(p.HR), dhp(p.HP);  // item -> (vector, row, plane, octet)
+            auto split = [&](int u, int &vc, int &hr, int &hp, int &o8) {
+                const int t1 = dnv.div(u);
+                vc = u - t1 * nvc;
+                const int t2 = dhr.div(t1);
+                hr = t1 - t2 * p.HR;
+                o8 = dhp.div(t2);
+                hp = t2 - o8 * p.HP;
+            };
             const size_t plane_in = size_t(L0) * L1 * L2;
             const _Float16 *xg = x + (size_t(n) * p.C + size_t(g) * p.Cg) * plane_in;
             constexpr int IT = kHaloVec / 8;
@@ -148,8 +159,8 @@ __global__ __launch_bounds__(kThreads, 1) void mphase_kernel(const _Float16 *x, 
 #pragma unroll
                 for (int it = 0; it < IT; ++it) {
                     const int u = base + tid + it * kThreads;
-                    const int vc = u % nvc, hr = (u / nvc) % p.HR, hp = (u / (nvc * p.HR)) % p.HP;
-                    const int o8 = u / (nvc * p.HR * p.HP);
+                    int vc, hr, hp, o8;
+                    split(u, vc, hr, hp, o8);
                     const int i0 = i0o + hp, i1 = i1o + hr, i2 = (va + vc) * 8;
                     const bool ok = u < items && i0 >= 0 && i0 < L0 && i1 >= 0 && i1 < L1 && i2 >= 0 && i2 < L2;
                     const _Float16 *src = ok ? xg + size_t(o8 * 8) * plane_in + (size_t(i0) * L1 + i1) * L2 + i2 : x;
@@ -162,8 +173,8 @@ __global__ __launch_bounds__(kThreads, 1) void mphase_kernel(const _Float16 *x, 
                 for (int it = 0; it < IT; ++it) {
                     const int u = base + tid + it * kThreads;
                     if (u >= items) continue;
-                    const int vc = u % nvc, hr = (u / nvc) % p.HR, hp = (u / (nvc * p.HR)) % p.HP;
-                    const int o8 = u / (nvc * p.HR * p.HP);
+                    int vc, hr, hp, o8;
+                    split(u, vc, hr, hp, o8);
 #pragma unroll
                     for (int pp = 0; pp < 8; ++pp) {
                         const int hc = (va + vc) * 8 + pp - i2o;
