@@ -44,12 +44,18 @@ struct I32Args {
     Act act;  // output activation
 };
 
+// ALL = 0: depth streamed through two LDS buffers, one step ahead.  ALL > 0 (calls whose
+// depth is at most ALL steps, e.g. 64 channels x 2 taps): every step's operands are
+// gathered at once, staged once and reduced without further barriers, so the block waits
+// for one round of loads instead of one per step.
+template <int ALL>
 __global__ __launch_bounds__(kThreads32) void igemm32_kernel(const float *__restrict__ x, const float *__restrict__ w,
                                                              const float *__restrict__ bias, float *__restrict__ y,
                                                              I32Args p)
 {
-    __shared__ float As[2][kKC][kBM + 4];  // [depth][channel]
-    __shared__ float Bs[2][kKC][kBN + 4];  // [depth][pixel]
+    constexpr int NBUF = ALL > 0 ? ALL : 2;
+    __shared__ float As[NBUF][kKC][kBM + 4];  // [depth][channel]
+    __shared__ float Bs[NBUF][kKC][kBN + 4];  // [depth][pixel]
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wm = wave & 1, wn = wave >> 1;
@@ -72,7 +78,10 @@ __global__ __launch_bounds__(kThreads32) void igemm32_kernel(const float *__rest
     local /= ptiles;
     const int mt = local % p.mtiles;
     const int g = local / p.mtiles;
-    const int depth = p.Cg * T;
+    // depth order: tap-major, d = t * Cgp + c with Cgp = C/group rounded up to 16, so the
+    // 16 depth rows of a step share one tap (wave-uniform) and hold consecutive channels
+    const int Cgp = (p.Cg + kKC - 1) / kKC * kKC;
+    const int depth = Cgp * T;
     const int Ktot = p.K[0] * p.K[1] * p.K[2];
 
     // ---- this thread's gather slots: one channel (A) and one pixel (B), kRPT depth rows ----
@@ -92,40 +101,44 @@ __global__ __launch_bounds__(kThreads32) void igemm32_kernel(const float *__rest
         jn = q / J[0];
     }
     const size_t in_pix = size_t(p.L[0]) * p.L[1] * p.L[2];
-
-    float areg[kRPT], breg[kRPT];
+    const bool m_ok = m_a < p.Mg;
+    // element (channel c, tap) of this thread's operands: A at w + a_base + c * MgK + tap
+    // offset, B at x + b_base + c * cstride + pixel offset of the tap
+    const size_t MgK = size_t(p.Mg) * Ktot;
+    const size_t a_base = size_t(g) * p.Cg * MgK + size_t(m_ok ? m_a : 0) * Ktot;
+    const size_t cstride = p.cl ? 1 : in_pix;
+    const size_t b_base = p.cl ? size_t(jn) * in_pix * p.C + size_t(g) * p.Cg : (size_t(jn) * p.C + size_t(g) * p.Cg) * in_pix;
     // Every load is issued unconditionally from a valid address (element 0 when the slot
     // is padding or outside the input; the kernel never runs on an empty input or empty
     // weights) and masked afterwards: loads under a branch are waited for one at a time.
-    auto gather = [&](int step) {
+    auto gather = [&](int step, float (&areg)[kRPT], float (&breg)[kRPT]) {
+        // the step's tap (uniform) and this thread's input pixel for it
+        const int t = (step * kKC) / Cgp, cb = step * kKC - t * Cgp;
+        const int t2 = t % nt[2], tq = t / nt[2];
+        const int t1 = tq % nt[1], t0 = tq / nt[1];
+        const int k0 = p.tk0[0][r[0]] + t0 * p.kstep[0], k1 = p.tk0[1][r[1]] + t1 * p.kstep[1],
+                  k2 = p.tk0[2][r[2]] + t2 * p.kstep[2];
+        const int tapoff = (k0 * p.K[1] + k1) * p.K[2] + k2;
+        const int i0 = jj[0] + p.tb0[0][r[0]] - t0 * p.bstep[0];
+        const int i1 = jj[1] + p.tb0[1][r[1]] - t1 * p.bstep[1];
+        const int i2 = jj[2] + p.tb0[2][r[2]] - t2 * p.bstep[2];
+        const bool pin = q_ok && i0 >= 0 && i0 < p.L[0] && i1 >= 0 && i1 < p.L[1] && i2 >= 0 && i2 < p.L[2];
+        const size_t pix = pin ? (size_t(i0) * p.L[1] + i1) * p.L[2] + i2 : 0;
+        const size_t pixoff = p.cl ? pix * p.C : pix;
         float av[kRPT], bv[kRPT];
         bool aok[kRPT], bok[kRPT];
+        // running offsets of channel cb + row0 + 4 i (one add per element)
+        size_t ao = a_base + size_t(cb + row0) * MgK + tapoff;
+        size_t bo = b_base + size_t(cb + row0) * cstride + pixoff;
 #pragma unroll
         for (int i = 0; i < kRPT; ++i) {
-            const int d = step * kKC + row0 + 4 * i;
-            const bool din = d < depth;
-            const int dd = din ? d : 0;
-            const int c = dd / T;
-            int t = dd - c * T;
-            const int t2 = t % nt[2];
-            t /= nt[2];
-            const int t1 = t % nt[1];
-            const int t0 = t / nt[1];
-            const int k0 = p.tk0[0][r[0]] + t0 * p.kstep[0], k1 = p.tk0[1][r[1]] + t1 * p.kstep[1],
-                      k2 = p.tk0[2][r[2]] + t2 * p.kstep[2];
-            const int gc = g * p.Cg + c;
-            aok[i] = din && m_a < p.Mg;
-            const size_t aoff = aok[i] ? (size_t(gc) * p.Mg + m_a) * Ktot + (k0 * p.K[1] + k1) * p.K[2] + k2 : 0;
-            av[i] = w[aoff];
-            const int i0 = jj[0] + p.tb0[0][r[0]] - t0 * p.bstep[0];
-            const int i1 = jj[1] + p.tb0[1][r[1]] - t1 * p.bstep[1];
-            const int i2 = jj[2] + p.tb0[2][r[2]] - t2 * p.bstep[2];
-            bok[i] = din && q_ok && i0 >= 0 && i0 < p.L[0] && i1 >= 0 && i1 < p.L[1] && i2 >= 0 && i2 < p.L[2];
-            const size_t pix = bok[i] ? (size_t(i0) * p.L[1] + i1) * p.L[2] + i2 : 0;
-            const size_t boff = !bok[i] ? 0
-                                : p.cl ? (size_t(jn) * in_pix + pix) * p.C + gc
-                                       : (size_t(jn) * p.C + gc) * in_pix + pix;
-            bv[i] = x[boff];
+            const bool cok = cb + row0 + 4 * i < p.Cg;
+            aok[i] = cok && m_ok;
+            av[i] = w[aok[i] ? ao : 0];
+            bok[i] = cok && pin;
+            bv[i] = x[bok[i] ? bo : 0];
+            ao += 4 * MgK;
+            bo += 4 * cstride;
         }
 #pragma unroll
         for (int i = 0; i < kRPT; ++i) {
@@ -133,11 +146,19 @@ __global__ __launch_bounds__(kThreads32) void igemm32_kernel(const float *__rest
             breg[i] = bok[i] ? bv[i] : 0.0f;
         }
     };
-    auto stage = [&](int buf) {
+    auto stage = [&](int buf, const float (&areg)[kRPT], const float (&breg)[kRPT]) {
 #pragma unroll
         for (int i = 0; i < kRPT; ++i) {
             As[buf][row0 + 4 * i][col] = areg[i];
             Bs[buf][row0 + 4 * i][col] = breg[i];
+        }
+    };
+    auto mma_step = [&](int buf, f32x16 &acc) {
+#pragma unroll
+        for (int k = 0; k < kKC; k += 2) {
+            const float a = As[buf][k + (lane >> 5)][wm * 32 + (lane & 31)];
+            const float b = Bs[buf][k + (lane >> 5)][wn * 32 + (lane & 31)];
+            acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, acc, 0, 0, 0);
         }
     };
 
@@ -145,20 +166,28 @@ __global__ __launch_bounds__(kThreads32) void igemm32_kernel(const float *__rest
 #pragma unroll
     for (int e = 0; e < 16; ++e) acc[e] = 0.0f;
     const int nsteps = (depth + kKC - 1) / kKC;
-    if (nsteps > 0) {
-        gather(0);
-        stage(0);
+    if constexpr (ALL > 0) {
+        float ar[ALL][kRPT], br[ALL][kRPT];
+#pragma unroll
+        for (int st = 0; st < ALL; ++st)
+            if (st < nsteps) gather(st, ar[st], br[st]);
+#pragma unroll
+        for (int st = 0; st < ALL; ++st)
+            if (st < nsteps) stage(st, ar[st], br[st]);
+        __syncthreads();
+#pragma unroll
+        for (int st = 0; st < ALL; ++st)
+            if (st < nsteps) mma_step(st, acc);
+    } else if (nsteps > 0) {
+        float areg[kRPT], breg[kRPT];
+        gather(0, areg, breg);
+        stage(0, areg, breg);
         __syncthreads();
         for (int st = 0; st < nsteps; ++st) {
             const int buf = st & 1;
-            if (st + 1 < nsteps) gather(st + 1);  // next step's operands, in flight under the MFMAs
-#pragma unroll
-            for (int k = 0; k < kKC; k += 2) {
-                const float a = As[buf][k + (lane >> 5)][wm * 32 + (lane & 31)];
-                const float b = Bs[buf][k + (lane >> 5)][wn * 32 + (lane & 31)];
-                acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, acc, 0, 0, 0);
-            }
-            if (st + 1 < nsteps) stage(buf ^ 1);
+            if (st + 1 < nsteps) gather(st + 1, areg, breg);  // next step's operands, in flight under the MFMAs
+            mma_step(buf, acc);
+            if (st + 1 < nsteps) stage(buf ^ 1, areg, breg);
             __syncthreads();
         }
     }
@@ -228,6 +257,11 @@ bool make_plan32(const Geom &g, bool cl, I32Args *a, int *blocks, std::string *w
         *why = "kernel too large";
         return false;
     }
+    // depth (C/group rounded up to 16, times the phase's taps) in an int
+    if ((g.Cg + kKC) * g.taps() > INT32_MAX) {
+        *why = "C/group x taps too large";
+        return false;
+    }
     a->mtiles = int((g.Mg + kBM - 1) / kBM);
     int64_t total = 0;
     int nph = 0;
@@ -285,10 +319,21 @@ ct_status launch_igemm32(const Geom &g, bool cl, const void *x, const void *w, c
     if (!make_plan32(g, cl, &a, &blocks, err)) return CT_EUNSUPPORTED;
     a.act = act;
     mark_before(st);
-    if (blocks > 0)
-        hipLaunchKernelGGL(igemm32_kernel, dim3(unsigned(blocks)), dim3(kThreads32), 0, st,
-                           static_cast<const float *>(x), static_cast<const float *>(w),
-                           static_cast<const float *>(bias), static_cast<float *>(y), a);
+    // deepest phase: C/group (rounded up to 16) x its taps; at most 8 steps -> the one-round instance
+    int64_t max_depth = 0;
+    for (int ph = 0; ph < a.nphase; ++ph)
+        max_depth = std::max<int64_t>(max_depth, int64_t((a.Cg + kKC - 1) / kKC * kKC) * a.ntap[0][a.ph_r[ph][0]] *
+                                                     a.ntap[1][a.ph_r[ph][1]] * a.ntap[2][a.ph_r[ph][2]]);
+    const auto *xf = static_cast<const float *>(x);
+    const auto *wf = static_cast<const float *>(w);
+    const auto *bf = static_cast<const float *>(bias);
+    auto *yf = static_cast<float *>(y);
+    if (blocks > 0) {
+        if (max_depth <= 8 * kKC)
+            hipLaunchKernelGGL(igemm32_kernel<8>, dim3(unsigned(blocks)), dim3(kThreads32), 0, st, xf, wf, bf, yf, a);
+        else
+            hipLaunchKernelGGL(igemm32_kernel<0>, dim3(unsigned(blocks)), dim3(kThreads32), 0, st, xf, wf, bf, yf, a);
+    }
     mark_after(st);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) {
