@@ -355,6 +355,8 @@ __global__ __launch_bounds__(kThreads, OCC) void igemm_kernel(const _Float16 *x,
     const int va = floor_div8(i2o);
     const int nvc = floor_div8(i2o + tl.HC + 7) - va;
     const int halo_items = CL ? tl.HR * tl.HC * CHUNKS : tl.HR * nvc * CHUNKS;
+    // halo item -> (row, column or vector) by multiply-high (items * divisor < 2^32)
+    const UDiv dhalo(CL ? tl.HC : nvc);
     // load_halo_part<KB, KE>: loads KB..KE-1 of the HREG halo loads (all of them for
     // <0, HREG>) and returns their validity bits (NHWC: bit per load; NC..: bit per item).
     auto load_halo_part = [&](auto kb, auto ke, int chunk, int t0, u32x4 *reg) -> unsigned {
@@ -368,7 +370,7 @@ __global__ __launch_bounds__(kThreads, OCC) void igemm_kernel(const _Float16 *x,
             for (int k = KB; k < KE; ++k) {
                 const int u = tid + k * kThreads;
                 const int pix = u / CHUNKS, ch = u % CHUNKS;
-                const int hr = pix / tl.HC, hc = pix - hr * tl.HC;
+                const int hr = dhalo.div(pix), hc = pix - hr * tl.HC;
                 const int i1 = i1o + hr, i2 = i2o + hc;
                 const bool inside = u < halo_items && i1 >= 0 && i1 < L1 && i2 >= 0 && i2 < L2;
                 const bool ok = inside && cbase + ch * CH16 < p.Cg;
@@ -387,7 +389,7 @@ __global__ __launch_bounds__(kThreads, OCC) void igemm_kernel(const _Float16 *x,
                 const int u = tid + it * kThreads;
                 const int oct = u % CHUNKS;
                 const int rv = u / CHUNKS;
-                const int hr = rv / nvc, vc = rv - hr * nvc;
+                const int hr = dhalo.div(rv), vc = rv - hr * nvc;
                 const int i1 = i1o + hr;
                 const int i2 = (va + vc) * 8;
                 const bool ok = u < halo_items && i1 >= 0 && i1 < L1 && i2 >= 0 && i2 < L2 && cbase + oct * 8 < p.Cg;
@@ -450,7 +452,7 @@ __global__ __launch_bounds__(kThreads, OCC) void igemm_kernel(const _Float16 *x,
                 const bool here = u < halo_items;
                 const int oct = u % CHUNKS;
                 const int rv = u / CHUNKS;
-                const int hr = rv / nvc, vc = rv - hr * nvc;
+                const int hr = dhalo.div(rv), vc = rv - hr * nvc;
                 const u32x4 *in = reg + it * 8;
                 // transpose 8 channels x 8 columns -> 8 columns x 8 channels
 #pragma unroll
