@@ -690,12 +690,12 @@ __global__ __launch_bounds__(kThreads, OCC) void igemm_kernel(const _Float16 *x,
             }
         };
 
-        if (!CL && nt1 * nt2 == 4) {
+        if (!Q8 && nt1 * nt2 == 4) {
             // Four taps per (chunk, axis-0 tap) group: one group per iteration, unrolled.
             // Each step loads the next step's weight tile and then a fixed quarter of the
             // next group's halo, all unconditionally, so every wait for a weight tile
-            // leaves the halo quarter issued after it in flight.  (Channels-first only:
-            // the channels-last kernel runs out of registers with this loop.)
+            // leaves the halo quarter issued after it in flight.  (Float16 only: the int8
+            // instances keep the one-group-at-a-time halo.)
             const int ngroups = nsteps / 4;
             StepIdx grp = cur;
             for (int gi = 0; gi < ngroups; ++gi) {
