@@ -91,9 +91,10 @@ __global__ __launch_bounds__(kThreads) void dwcl_kernel(const _Float16 *__restri
     {
         const u32x4 zero = {0u, 0u, 0u, 0u};
         const int items = p.HR * p.HC * co;
+        const UDiv dco(co), dhc(p.HC), dkk(KK);  // index splits by multiply-high
         for (int u = tid; u < items; u += kThreads) {
-            const int oc = u % co, q = u / co;
-            const int hc = q % p.HC, hr = q / p.HC;
+            const int q = dco.div(u), oc = u - q * co;
+            const int hr = dhc.div(q), hc = q - hr * p.HC;
             const int i1 = i1o + hr, i2 = i2o + hc;
             const bool ok = i1 >= 0 && i1 < p.L1 && i2 >= 0 && i2 < p.L2 && c_lo + oc * 8 < p.C;
             const size_t off = ok ? ((size_t(n) * p.L1 + i1) * p.L2 + i2) * p.C + c_lo + oc * 8 : 0;
@@ -102,7 +103,7 @@ __global__ __launch_bounds__(kThreads) void dwcl_kernel(const _Float16 *__restri
         }
         const int wn = co * 8 * KK;
         for (int u = tid; u < wn; u += kThreads) {
-            const int c = u / KK, t = u - c * KK;
+            const int c = dkk.div(u), t = u - c * KK;
             const bool ok = c_lo + c < p.C;
             const _Float16 v = w[ok ? size_t(c_lo + c) * KK + t : 0];
             sw[t * (co * 8) + c] = ok ? v : _Float16(0.0f);
