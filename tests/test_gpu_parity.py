@@ -358,6 +358,41 @@ def test_depthwise_shapes(T, case, integer):
     check(got, ref_nb, "f16", integer, f"depthwise no-bias x{xs} {attrs}")
 
 
+GROUPED_3D = [
+    # (x_shape, w_shape, attrs): rank-3 grouped and depthwise calls (C/group, M/group <= 8),
+    # channels-first, on the grouped bandwidth kernel: strides, dilations, pads, output
+    # padding, residue classes without taps, several row bands per plane
+    ((2, 4, 5, 6, 7), (4, 1, 3, 3, 3), dict(strides=[2, 2, 2], pads=[1] * 6, group=4)),
+    ((1, 6, 4, 9, 11), (6, 2, 2, 4, 3), dict(strides=[1, 2, 2], pads=[0, 1, 1, 1, 0, 1], group=3)),
+    ((1, 8, 3, 5, 5), (8, 3, 3, 2, 2), dict(strides=[3, 1, 2], dilations=[2, 1, 1], group=2, output_padding=[1, 0, 1])),
+    ((2, 3, 6, 4, 8), (3, 1, 4, 3, 3), dict(strides=[2, 1, 1], pads=[1, 1, 1, 2, 1, 1], group=3)),
+    ((1, 16, 4, 40, 36), (16, 1, 3, 3, 3), dict(strides=[2, 2, 2], pads=[1] * 6, output_padding=[1, 1, 1], group=16)),
+    ((1, 4, 2, 3, 4), (4, 2, 1, 1, 1), dict(strides=[4, 2, 3], group=2)),
+]
+
+
+@pytest.mark.parametrize("dtype", ["f16", "f32"])
+@pytest.mark.parametrize("integer", [False, True], ids=["float", "int"])
+@pytest.mark.parametrize("case", GROUPED_3D, ids=lambda c: f"{c[0]}_{c[1]}")
+def test_grouped_rank3(T, case, integer, dtype):
+    """Rank-3 grouped calls on the grouped family (the dispatcher must pick it) against
+    the oracle on whole outputs; bit-exact on integer inputs."""
+    xs, ws, attrs = case
+    _log(f"[case] grouped rank 3 x{xs} w{ws} {attrs} integer={integer} {dtype}")
+    rng = np.random.default_rng(zlib.crc32(repr(case).encode()) + integer + (dtype == "f32") * 2)
+    gen = (lambda sz: rng.integers(-2, 3, size=sz)) if integer else (lambda sz: rng.normal(size=sz))
+    x = gen(xs).astype(NPT[dtype])
+    w = (gen(ws) * (1 if integer else 0.3)).astype(NPT[dtype])
+    b = gen(ws[1] * attrs["group"]).astype(NPT[dtype])
+    dev = torch.device("cuda:0")
+    assert T.convtranspose_select_kernel(torch.from_numpy(x).to(dev), torch.from_numpy(w).to(dev),
+                                         torch.from_numpy(b).to(dev), **attrs) == "grouped"
+    ref = O.convtranspose(x, w, b, **attrs)
+    for kernel in ("grouped", "auto"):
+        got = gpu_run(T, x, w, b, attrs, False, kernel)
+        check(got, ref, dtype, integer, f"grouped rank 3 {kernel} x{xs} w{ws} {attrs}")
+
+
 DEPTHWISE_CL = [
     # (x_shape, kernel shape, attrs): channels-last depthwise (group == C), float16, C a
     # multiple of 8: the channels-last bandwidth kernel (ragged tiles, octet tiles of 32,
