@@ -43,6 +43,7 @@ struct DwArgs {
     int lo1, lo2;  // smallest input offset beta over all phases, per axis
     int span1;     // staged rows beyond the band's input rows: hi1 - lo1 + 1
     int stage_elems;    // halves per stage buffer (multiple of 8)
+    int sh;             // column shift of the staged rows (0..3): window reads start 8-byte aligned
     int a0_1[kDwMaxS];  // per row residue: its window's row offset from lo1
     Act act;            // output activation
 };
@@ -65,9 +66,11 @@ __global__ __launch_bounds__(kDwThreads) void depthwise_kernel(const _Float16 *_
     typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
     typedef _Float16 h2 __attribute__((ext_vector_type(2)));
     typedef float f2 __attribute__((ext_vector_type(2)));
-    // Stage: kDwGuard zero elements, then nrows rows of R elements each: input columns
-    // [0, L2) followed by zeros up to R.  Reads left of a row land in the previous row's
-    // zeros (or the leading guard), reads right of it in its own.
+    // Stage: kDwGuard + sh zero elements, then nrows rows of R elements each: input
+    // columns [0, L2) followed by zeros up to R.  Reads left of a row land in the previous
+    // row's zeros (or the leading guard), reads right of it in its own.  The shift sh
+    // makes kDwGuard + sh + lo2 a multiple of 4, so with S <= 2 every window read starts
+    // on an 8-byte boundary (LDS reads that are not naturally aligned stall).
     extern __shared__ __attribute__((aligned(16))) unsigned char dw_lds[];
     _Float16 *const sx = reinterpret_cast<_Float16 *>(dw_lds);
     __shared__ _Float16 seff[NE];
@@ -159,12 +162,29 @@ __global__ __launch_bounds__(kDwThreads) void depthwise_kernel(const _Float16 *_
                 int r = k / cpl;
                 r = r < cur.vr0 ? r : r + cur.nvr;
                 reinterpret_cast<u32x4 *>(sx + kDwGuard + r * R)[k % cpl] = u32x4{0u, 0u, 0u, 0u};
+                // the shifted row's last sh elements spill into the next chunk
+                if (p.sh > 0 && k % cpl == cpl - 1)
+                    reinterpret_cast<u32x4 *>(sx + kDwGuard + r * R)[cpl] = u32x4{0u, 0u, 0u, 0u};
             }
         }
 #pragma unroll
         for (int q = 0; q < NQ; ++q)
-            if ((vok >> q) & 1u)
-                *reinterpret_cast<u32x4 *>(sx + kDwGuard + (cur.vr0 + chr[q]) * R + chc[q]) = v[q];
+            if ((vok >> q) & 1u) {
+                _Float16 *dst = sx + kDwGuard + p.sh + (cur.vr0 + chr[q]) * R + chc[q];
+                const u32x4 vq = v[q];
+                if (p.sh == 0) {  // 16-byte aligned
+                    *reinterpret_cast<u32x4 *>(dst) = vq;
+                } else if (p.sh == 2) {  // 4-byte aligned
+#pragma unroll
+                    for (int k = 0; k < 4; ++k) reinterpret_cast<unsigned *>(dst)[k] = vq[k];
+                } else {  // 2-byte aligned: a half, three aligned pairs, a half
+                    *reinterpret_cast<unsigned short *>(dst) = (unsigned short)(vq[0] & 0xffffu);
+#pragma unroll
+                    for (int k = 0; k < 3; ++k)
+                        reinterpret_cast<unsigned *>(dst + 1)[k] = (vq[k] >> 16) | (vq[k + 1] << 16);
+                    *reinterpret_cast<unsigned short *>(dst + 7) = (unsigned short)(vq[3] >> 16);
+                }
+            }
         if (threadIdx.x < NE) seff[threadIdx.x] = eidx >= 0 ? ew : _Float16(0.0f);
         const float bv = bias ? float(braw) : 0.0f;
         __syncthreads();
@@ -194,17 +214,35 @@ __global__ __launch_bounds__(kDwThreads) void depthwise_kernel(const _Float16 *_
         _Float16 *const yplane = y + size_t(cur.c) * p.O1 * p.O2;
         for (int seg = seg0, jr = jr0; jr < jrows;) {
             const int j1 = cur.j1lo + jr;
-            const _Float16 *row0 = sx + kDwGuard + jr * R + (seg * JC + p.lo2);
+            const _Float16 *row0 = sx + kDwGuard + p.sh + jr * R + (seg * JC + p.lo2);
 #pragma unroll
             for (int rh = 0; rh < S; ++rh) {
                 const int oh = S * j1 + rh;
                 // this row phase's T1 input rows, XW columns from the segment's start
                 const _Float16 *win = row0 + p.a0_1[rh] * R;
                 _Float16 xs[T1][XW];
+                if constexpr (S <= 2) {
+                    // 8-byte aligned: whole 4-element pieces
+                    typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+                    constexpr int NV = (XW + 3) / 4;
 #pragma unroll
-                for (int a = 0; a < T1; ++a)
+                    for (int a = 0; a < T1; ++a) {
+                        const u32x2 *wv = reinterpret_cast<const u32x2 *>(win + a * R);
 #pragma unroll
-                    for (int q = 0; q < XW; ++q) xs[a][q] = win[a * R + q];
+                        for (int v = 0; v < NV; ++v) {
+                            const u32x2 pv = wv[v];
+#pragma unroll
+                            for (int e = 0; e < 4; ++e)
+                                if (4 * v + e < XW)
+                                    xs[a][4 * v + e] = __builtin_bit_cast(_Float16, (unsigned short)((pv[e >> 1] >> (16 * (e & 1))) & 0xffffu));
+                        }
+                    }
+                } else {
+#pragma unroll
+                    for (int a = 0; a < T1; ++a)
+#pragma unroll
+                        for (int q = 0; q < XW; ++q) xs[a][q] = win[a * R + q];
+                }
                 float out[OC];
 #pragma unroll
                 for (int rwp = 0; rwp < S; ++rwp) {
@@ -339,10 +377,15 @@ bool make_dwplan(const Geom &g, ct_dtype dt, bool cl, const void *x, DwPlan *pl)
     if (g.L[2] % 8 != 0 || reinterpret_cast<uintptr_t>(x) % 16 != 0 || -a.lo2 > kDwGuard) return false;
     // row stride: the zeros after a row cover reads left of the next row (lo2) and reads
     // right of this one (last segment, widest phase window)
-    a.row_w = (std::max<int>(int(g.L[2]) - a.lo2, segs * JC + hi2) + 7) / 8 * 8;
+    // shift of the staged rows: kDwGuard + sh + lo2 a multiple of 4 (S <= 2; S = 4 reads
+    // 2-element runs and keeps sh = 0)
+    a.sh = S <= 2 ? ((-(kDwGuard + a.lo2)) % 4 + 4) % 4 : 0;
+    // the shifted row (and its zeroing, one chunk longer) stays inside the row stride
+    a.row_w = (std::max<int>({int(g.L[2]) - a.lo2, segs * JC + hi2, a.sh > 0 ? int(g.L[2]) + 8 : 0}) + 7) / 8 * 8;
     const int64_t cpl = g.L[2] / 8;
     auto rows_for = [&](int b) { return (b + S - 1) / S - 1 + a.span1; };
-    auto bytes_for = [&](int b) { return (int64_t(kDwGuard) + int64_t(rows_for(b)) * a.row_w) * 2; };
+    // + 8: the last row shifted by sh, and the 4-element window reads past a row's end
+    auto bytes_for = [&](int b) { return (int64_t(kDwGuard) + int64_t(rows_for(b)) * a.row_w + 8) * 2; };
     auto fits = [&](int b) { return bytes_for(b) <= kDwStageBytes && rows_for(b) * cpl <= kDwMaxChunks * kDwThreads; };
     // band of output rows (a multiple of S) whose staged rows fit
     int band = int((g.O[1] + S - 1) / S) * S;
