@@ -31,12 +31,22 @@ constexpr int kMaxRes32 = 16, kMaxTap32 = 16, kMaxPh32 = 64;
 
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
+// the word padding slots of a gather read (outside the input, channels past C/group,
+// output channels past M/group); a global-memory variable like x and w, so the selected
+// pointer keeps the global address space (a constant-space one would turn the gathers
+// into flat loads, which the compiler waits for one at a time).  Never written.
+__device__ float kZero32 = 0.0f;
+
 struct I32Args {
     int N, C, M, G, Cg, Mg, cl;
     int L[3], O[3], s[3], K[3];
     int mtiles, nphase;
     int ph_start[kMaxPh32 + 1];
     unsigned char ph_r[kMaxPh32][3];
+    // per phase and axis: tap count, first tap and its input offset (the residue tables
+    // below looked up once on the host), so the kernel reads them in one round
+    signed char ph_nt[kMaxPh32][3];
+    short ph_tk[kMaxPh32][3], ph_tb[kMaxPh32][3];
     // taps of residue r on axis a: k = tk0 + u * kstep, input offset beta = tb0 - u * bstep
     signed char ntap[3][kMaxRes32];
     short tk0[3][kMaxRes32], tb0[3][kMaxRes32];
@@ -48,7 +58,9 @@ struct I32Args {
 // depth is at most ALL steps, e.g. 64 channels x 2 taps): every step's operands are
 // gathered at once, staged once and reduced without further barriers, so the block waits
 // for one round of loads instead of one per step.
-template <int ALL>
+// OFF: the element-offset type, 32-bit when X and W hold fewer than 2^30 elements (one
+// 32-bit add per element and loads addressed from a scalar base), else 64-bit.
+template <int ALL, typename OFF>
 __global__ __launch_bounds__(kThreads32) void igemm32_kernel(const float *__restrict__ x, const float *__restrict__ w,
                                                              const float *__restrict__ bias, float *__restrict__ y,
                                                              I32Args p)
@@ -62,14 +74,17 @@ __global__ __launch_bounds__(kThreads32) void igemm32_kernel(const float *__rest
 
     // ---- work item: phase, pixel tile, channel tile, group ----
     const int v = blockIdx.x;
-    int ph = 0;
-    while (v >= p.ph_start[ph + 1]) ++ph;
+    // the phase: lane i compares the block against boundary i (one vector read of the
+    // boundaries, no chain of dependent argument reads), the ballot counts the passed ones
+    static_assert(kMaxPh32 <= 64, "one boundary per lane");
+    const bool passed = lane >= 1 && lane < p.nphase && v >= p.ph_start[lane];
+    const int ph = __builtin_amdgcn_readfirstlane(__builtin_popcountll(__ballot(passed)));
     int local = v - p.ph_start[ph];
     int r[3], J[3], nt[3];
     for (int a = 0; a < 3; ++a) {
         r[a] = p.ph_r[ph][a];
         J[a] = (p.O[a] - r[a] + p.s[a] - 1) / p.s[a];
-        nt[a] = p.ntap[a][r[a]];
+        nt[a] = p.ph_nt[ph][a];
     }
     const int T = nt[0] * nt[1] * nt[2];
     const int P = p.N * J[0] * J[1] * J[2];
@@ -100,50 +115,50 @@ __global__ __launch_bounds__(kThreads32) void igemm32_kernel(const float *__rest
         jj[0] = q % J[0];
         jn = q / J[0];
     }
-    const size_t in_pix = size_t(p.L[0]) * p.L[1] * p.L[2];
+    const OFF in_pix = OFF(p.L[0]) * p.L[1] * p.L[2];
     const bool m_ok = m_a < p.Mg;
     // element (channel c, tap) of this thread's operands: A at w + a_base + c * MgK + tap
     // offset, B at x + b_base + c * cstride + pixel offset of the tap
-    const size_t MgK = size_t(p.Mg) * Ktot;
-    const size_t a_base = size_t(g) * p.Cg * MgK + size_t(m_ok ? m_a : 0) * Ktot;
-    const size_t cstride = p.cl ? 1 : in_pix;
-    const size_t b_base = p.cl ? size_t(jn) * in_pix * p.C + size_t(g) * p.Cg : (size_t(jn) * p.C + size_t(g) * p.Cg) * in_pix;
-    // Every load is issued unconditionally from a valid address (element 0 when the slot
-    // is padding or outside the input; the kernel never runs on an empty input or empty
-    // weights) and masked afterwards: loads under a branch are waited for one at a time.
+    const OFF MgK = OFF(p.Mg) * Ktot;
+    const OFF a_base = OFF(g) * p.Cg * MgK + OFF(m_ok ? m_a : 0) * Ktot;
+    const OFF cstride = p.cl ? 1 : in_pix;
+    const OFF b_base = p.cl ? OFF(jn) * in_pix * p.C + OFF(g) * p.Cg : (OFF(jn) * p.C + OFF(g) * p.Cg) * in_pix;
+    // Every load is issued unconditionally from a valid address: loads under a branch
+    // are waited for one at a time.
+    // the phase's tap progressions, read from the arguments once
+    int tk[3], tb[3], ks[3], bs[3];
+#pragma unroll
+    for (int a = 0; a < 3; ++a) {
+        tk[a] = p.ph_tk[ph][a];
+        tb[a] = jj[a] + p.ph_tb[ph][a];
+        ks[a] = p.kstep[a];
+        bs[a] = p.bstep[a];
+    }
     auto gather = [&](int step, float (&areg)[kRPT], float (&breg)[kRPT]) {
         // the step's tap (uniform) and this thread's input pixel for it
         const int t = (step * kKC) / Cgp, cb = step * kKC - t * Cgp;
         const int t2 = t % nt[2], tq = t / nt[2];
         const int t1 = tq % nt[1], t0 = tq / nt[1];
-        const int k0 = p.tk0[0][r[0]] + t0 * p.kstep[0], k1 = p.tk0[1][r[1]] + t1 * p.kstep[1],
-                  k2 = p.tk0[2][r[2]] + t2 * p.kstep[2];
+        const int k0 = tk[0] + t0 * ks[0], k1 = tk[1] + t1 * ks[1], k2 = tk[2] + t2 * ks[2];
         const int tapoff = (k0 * p.K[1] + k1) * p.K[2] + k2;
-        const int i0 = jj[0] + p.tb0[0][r[0]] - t0 * p.bstep[0];
-        const int i1 = jj[1] + p.tb0[1][r[1]] - t1 * p.bstep[1];
-        const int i2 = jj[2] + p.tb0[2][r[2]] - t2 * p.bstep[2];
+        const int i0 = tb[0] - t0 * bs[0];
+        const int i1 = tb[1] - t1 * bs[1];
+        const int i2 = tb[2] - t2 * bs[2];
         const bool pin = q_ok && i0 >= 0 && i0 < p.L[0] && i1 >= 0 && i1 < p.L[1] && i2 >= 0 && i2 < p.L[2];
-        const size_t pix = pin ? (size_t(i0) * p.L[1] + i1) * p.L[2] + i2 : 0;
-        const size_t pixoff = p.cl ? pix * p.C : pix;
-        float av[kRPT], bv[kRPT];
-        bool aok[kRPT], bok[kRPT];
-        // running offsets of channel cb + row0 + 4 i (one add per element)
-        size_t ao = a_base + size_t(cb + row0) * MgK + tapoff;
-        size_t bo = b_base + size_t(cb + row0) * cstride + pixoff;
+        const OFF pix = pin ? (OFF(i0) * p.L[1] + i1) * p.L[2] + i2 : 0;
+        const OFF pixoff = p.cl ? pix * p.C : pix;
+        // running offsets of channel cb + row0 + 4 i (one add per element); a padding slot
+        // reads the zero word instead, so no select waits for the loaded value and every
+        // load of the step (of all steps, in the one-round instance) stays in flight
+        OFF ao = a_base + OFF(cb + row0) * MgK + tapoff;
+        OFF bo = b_base + OFF(cb + row0) * cstride + pixoff;
 #pragma unroll
         for (int i = 0; i < kRPT; ++i) {
             const bool cok = cb + row0 + 4 * i < p.Cg;
-            aok[i] = cok && m_ok;
-            av[i] = w[aok[i] ? ao : 0];
-            bok[i] = cok && pin;
-            bv[i] = x[bok[i] ? bo : 0];
+            areg[i] = *((cok && m_ok) ? w + ao : &kZero32);
+            breg[i] = *((cok && pin) ? x + bo : &kZero32);
             ao += 4 * MgK;
             bo += 4 * cstride;
-        }
-#pragma unroll
-        for (int i = 0; i < kRPT; ++i) {
-            areg[i] = aok[i] ? av[i] : 0.0f;
-            breg[i] = bok[i] ? bv[i] : 0.0f;
         }
     };
     auto stage = [&](int buf, const float (&areg)[kRPT], const float (&breg)[kRPT]) {
@@ -284,6 +299,12 @@ bool make_plan32(const Geom &g, bool cl, I32Args *a, int *blocks, std::string *w
                 a->ph_r[nph][0] = (unsigned char)r0;
                 a->ph_r[nph][1] = (unsigned char)r1;
                 a->ph_r[nph][2] = (unsigned char)r2;
+                const int rr[3] = {r0, r1, r2};
+                for (int ax = 0; ax < 3; ++ax) {
+                    a->ph_nt[nph][ax] = a->ntap[ax][rr[ax]];
+                    a->ph_tk[nph][ax] = a->tk0[ax][rr[ax]];
+                    a->ph_tb[nph][ax] = a->tb0[ax][rr[ax]];
+                }
                 total += (P + kBN - 1) / kBN * a->mtiles * g.G;
                 ++nph;
             }
@@ -324,15 +345,22 @@ ct_status launch_igemm32(const Geom &g, bool cl, const void *x, const void *w, c
     for (int ph = 0; ph < a.nphase; ++ph)
         max_depth = std::max<int64_t>(max_depth, int64_t((a.Cg + kKC - 1) / kKC * kKC) * a.ntap[0][a.ph_r[ph][0]] *
                                                      a.ntap[1][a.ph_r[ph][1]] * a.ntap[2][a.ph_r[ph][2]]);
+    // 32-bit element offsets when every offset stays below 2^30 elements
+    const bool off32 = g.x_elems() < (int64_t(1) << 30) && g.w_elems() < (int64_t(1) << 30);
     const auto *xf = static_cast<const float *>(x);
     const auto *wf = static_cast<const float *>(w);
     const auto *bf = static_cast<const float *>(bias);
     auto *yf = static_cast<float *>(y);
     if (blocks > 0) {
-        if (max_depth <= 8 * kKC)
-            hipLaunchKernelGGL(igemm32_kernel<8>, dim3(unsigned(blocks)), dim3(kThreads32), 0, st, xf, wf, bf, yf, a);
+        const dim3 grid = dim3(unsigned(blocks)), block = dim3(kThreads32);
+        if (max_depth <= 8 * kKC && off32)
+            hipLaunchKernelGGL((igemm32_kernel<8, unsigned>), grid, block, 0, st, xf, wf, bf, yf, a);
+        else if (max_depth <= 8 * kKC)
+            hipLaunchKernelGGL((igemm32_kernel<8, size_t>), grid, block, 0, st, xf, wf, bf, yf, a);
+        else if (off32)
+            hipLaunchKernelGGL((igemm32_kernel<0, unsigned>), grid, block, 0, st, xf, wf, bf, yf, a);
         else
-            hipLaunchKernelGGL(igemm32_kernel<0>, dim3(unsigned(blocks)), dim3(kThreads32), 0, st, xf, wf, bf, yf, a);
+            hipLaunchKernelGGL((igemm32_kernel<0, size_t>), grid, block, 0, st, xf, wf, bf, yf, a);
     }
     mark_after(st);
     const hipError_t e = hipGetLastError();
