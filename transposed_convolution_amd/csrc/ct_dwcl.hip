@@ -49,6 +49,8 @@ __device__ __forceinline__ float fma_mix_hi(float acc, unsigned x, unsigned w)
 }
 constexpr int kMaxOct = 8;         // channel octets per tile (64 channels: more, lighter blocks)
 constexpr int kMaxS = 2, kMaxT = 4;
+constexpr int kWinBatch = 6;      // window loads per thread in flight together
+constexpr int kWBatch = 4;        // weight loads per thread in flight together
 
 struct DwClArgs {
     int N, C, L1, L2, O1, O2, K1, K2;
@@ -92,21 +94,50 @@ __global__ __launch_bounds__(kThreads) void dwcl_kernel(const _Float16 *__restri
         const u32x4 zero = {0u, 0u, 0u, 0u};
         const int items = p.HR * p.HC * co;
         const UDiv dco(co), dhc(p.HC), dkk(KK);  // index splits by multiply-high
-        for (int u = tid; u < items; u += kThreads) {
-            const int q = dco.div(u), oc = u - q * co;
-            const int hr = dhc.div(q), hc = q - hr * p.HC;
-            const int i1 = i1o + hr, i2 = i2o + hc;
-            const bool ok = i1 >= 0 && i1 < p.L1 && i2 >= 0 && i2 < p.L2 && c_lo + oc * 8 < p.C;
-            const size_t off = ok ? ((size_t(n) * p.L1 + i1) * p.L2 + i2) * p.C + c_lo + oc * 8 : 0;
-            const u32x4 v = *reinterpret_cast<const u32x4 *>(x + off);  // x[0] when masked
-            *reinterpret_cast<u32x4 *>(sx + q * rowb + oc * 16) = ok ? v : zero;
+        // rounds of kWinBatch loads per thread, all in flight before any is written
+        for (int base = 0; base < items; base += kThreads * kWinBatch) {
+            u32x4 v[kWinBatch];
+            unsigned okm = 0;
+#pragma unroll
+            for (int k = 0; k < kWinBatch; ++k) {
+                const int u = base + tid + k * kThreads;
+                const int q = dco.div(u), oc = u - q * co;
+                const int hr = dhc.div(q), hc = q - hr * p.HC;
+                const int i1 = i1o + hr, i2 = i2o + hc;
+                const bool ok = u < items && i1 >= 0 && i1 < p.L1 && i2 >= 0 && i2 < p.L2 && c_lo + oc * 8 < p.C;
+                const size_t off = ok ? ((size_t(n) * p.L1 + i1) * p.L2 + i2) * p.C + c_lo + oc * 8 : 0;
+                v[k] = *reinterpret_cast<const u32x4 *>(x + off);  // x[0] when masked
+                okm |= unsigned(ok) << k;
+            }
+#pragma unroll
+            for (int k = 0; k < kWinBatch; ++k) {
+                const int u = base + tid + k * kThreads;
+                if (u < items) {
+                    const int q = dco.div(u), oc = u - q * co;
+                    *reinterpret_cast<u32x4 *>(sx + q * rowb + oc * 16) = ((okm >> k) & 1u) ? v[k] : zero;
+                }
+            }
         }
         const int wn = co * 8 * KK;
-        for (int u = tid; u < wn; u += kThreads) {
-            const int c = dkk.div(u), t = u - c * KK;
-            const bool ok = c_lo + c < p.C;
-            const _Float16 v = w[ok ? size_t(c_lo + c) * KK + t : 0];
-            sw[t * (co * 8) + c] = ok ? v : _Float16(0.0f);
+        for (int base = 0; base < wn; base += kThreads * kWBatch) {
+            _Float16 v[kWBatch];
+            unsigned okm = 0;
+#pragma unroll
+            for (int k = 0; k < kWBatch; ++k) {
+                const int u = base + tid + k * kThreads;
+                const int c = dkk.div(u), t = u - c * KK;
+                const bool ok = u < wn && c_lo + c < p.C;
+                v[k] = w[ok ? size_t(c_lo + c) * KK + t : 0];
+                okm |= unsigned(ok) << k;
+            }
+#pragma unroll
+            for (int k = 0; k < kWBatch; ++k) {
+                const int u = base + tid + k * kThreads;
+                if (u < wn) {
+                    const int c = dkk.div(u), t = u - c * KK;
+                    sw[t * (co * 8) + c] = ((okm >> k) & 1u) ? v[k] : _Float16(0.0f);
+                }
+            }
         }
     }
     __syncthreads();
