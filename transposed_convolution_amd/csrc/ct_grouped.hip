@@ -31,6 +31,7 @@ constexpr int kGMaxRes = 16;      // largest stride per axis
 constexpr int kGMaxTaps = 16;     // largest kernel size per axis
 constexpr int kGLdsBytes = 48 * 1024;
 constexpr int kGThreads = 256;
+constexpr int kGBatch = 8;        // staged elements per thread in flight together
 
 struct GArgs {
     int N, C, M, G, Cg, Mg;
@@ -92,17 +93,37 @@ __global__ __launch_bounds__(kGThreads) void grouped_kernel(const T *__restrict_
     for (int u = threadIdx.x; u < p.Cg * p.Mg * ntaps; u += kGThreads)
         sw[u] = float(w[size_t(g) * p.Cg * p.Mg * ntaps + u]);
     const int per_slot = nrows * rw;
-    for (int u = threadIdx.x; u < nt0 * p.Cg * per_slot; u += kGThreads) {
-        const int sl = u / per_slot;  // slot = u0 * Cg + c
-        const int rem = u - sl * per_slot;
-        const int u0 = sl / p.Cg, c = sl - u0 * p.Cg;
-        const int r = rem / rw, col = rem - r * rw;
-        const int i2 = col - p.pad2;
-        const int i0 = j0 + be0 - u0 * p.bs0;
-        T v = T(0.0f);
-        if (i2 >= 0 && i2 < p.L2 && i0 >= 0 && i0 < p.L0)
-            v = x[(size_t(n) * p.C + size_t(g) * p.Cg + c) * vol + size_t(i0) * plane + size_t(ilo + r) * p.L2 + i2];
-        sx[sl * per_ch + r * rw + col] = v;
+    // rounds of kGBatch elements per thread: unconditional loads (element 0 of x when the
+    // slot is padding), all in flight before any is written
+    const int nstage = nt0 * p.Cg * per_slot;
+    const UDiv dslot(per_slot), dcg(p.Cg), drw(rw);  // index splits by multiply-high
+    const T *const xg = x + (size_t(n) * p.C + size_t(g) * p.Cg) * vol;
+    for (int base = 0; base < nstage; base += kGThreads * kGBatch) {
+        T v[kGBatch];
+        unsigned okm = 0;
+#pragma unroll
+        for (int k = 0; k < kGBatch; ++k) {
+            const int u = base + threadIdx.x + k * kGThreads;
+            const int sl = dslot.div(u);  // slot = u0 * Cg + c
+            const int rem = u - sl * per_slot;
+            const int u0 = dcg.div(sl), c = sl - u0 * p.Cg;
+            const int r = drw.div(rem), col = rem - r * rw;
+            const int i2 = col - p.pad2;
+            const int i0 = j0 + be0 - u0 * p.bs0;
+            const bool ok = u < nstage && i2 >= 0 && i2 < p.L2 && i0 >= 0 && i0 < p.L0;
+            v[k] = *(ok ? xg + (size_t(c) * vol + size_t(i0) * plane + size_t(ilo + r) * p.L2 + i2) : x);
+            okm |= unsigned(ok) << k;
+        }
+#pragma unroll
+        for (int k = 0; k < kGBatch; ++k) {
+            const int u = base + threadIdx.x + k * kGThreads;
+            if (u < nstage) {
+                const int sl = dslot.div(u);
+                const int rem = u - sl * per_slot;
+                const int r = drw.div(rem), col = rem - r * rw;
+                sx[sl * per_ch + r * rw + col] = ((okm >> k) & 1u) ? v[k] : T(0.0f);
+            }
+        }
     }
     __syncthreads();
 
