@@ -146,6 +146,17 @@ __global__ __launch_bounds__(kGThreads) void grouped_kernel(const T *__restrict_
         const int nt1 = p.nt_1[r1];
         const int k01 = p.k0_1[r1];
         const int be1 = p.be_1[r1];
+        // per output column: its residue's tap count, first input column and first tap
+        // (looked up once per item, outside the channel and tap loops)
+        int nt2e[8], i2e[8], k2e[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const int ow = ow0 + e;
+            const int r2 = ow % p.s2;
+            nt2e[e] = p.nt_2[r2];
+            i2e[e] = ow / p.s2 + p.be_2[r2];
+            k2e[e] = p.k0_2[r2];
+        }
         for (int c = 0; c < p.Cg; ++c)
         for (int u0 = 0; u0 < nt0; ++u0) {
             const T *xc = sx + (u0 * p.Cg + c) * per_ch;
@@ -157,16 +168,9 @@ __global__ __launch_bounds__(kGThreads) void grouped_kernel(const T *__restrict_
                 const float *wr = wc + (k01 + u1 * p.ks1) * p.K2;
 #pragma unroll
                 for (int e = 0; e < 8; ++e) {
-                    const int ow = ow0 + e;
-                    const int r2 = ow % p.s2;
-                    const int j2 = ow / p.s2;
-                    const int nt2 = p.nt_2[r2];
-                    const int k02 = p.k0_2[r2];
-                    const int be2 = p.be_2[r2];
-                    for (int u2 = 0; u2 < nt2; ++u2) {
+                    for (int u2 = 0; u2 < nt2e[e]; ++u2) {
                         // columns out of [0, L2) read the staged zero padding
-                        const int i2 = j2 + be2 - u2 * p.bs2;
-                        acc[e] += float(xr[i2]) * wr[k02 + u2 * p.ks2];
+                        acc[e] += float(xr[i2e[e] - u2 * p.bs2]) * wr[k2e[e] + u2 * p.ks2];
                     }
                 }
             }

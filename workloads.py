@@ -137,7 +137,11 @@ F2_K2S2 = C4.with_(name="f2_2d_f16_k2_s2", w_shape=(512, 256, 2, 2),
                    w_dist=("N", 0.0, 1.0 / math.sqrt(512 * 4)), seed=6)
 F2_1X1 = C4.with_(name="f2_2d_f16_1x1", w_shape=(512, 256, 1, 1), attrs=dict(strides=[1, 1], group=1),
                   w_dist=("N", 0.0, 1.0 / math.sqrt(512)), seed=7)
-EXTRAS = {w.name: w for w in (F2_K2S2, F2_1X1)}
+# A 3-D depthwise call on C5's input tensors (the grouped family's rank-3 path).
+G3_DW = C5_S2.with_(name="g3_3d_f16_depthwise_s2", w_shape=(128, 1, 3, 3, 3), has_bias=False,
+                    attrs=dict(strides=[2, 2, 2], pads=[1] * 6, output_padding=[1, 1, 1], group=128),
+                    w_dist=("N", 0.0, 0.25), seed=8)
+EXTRAS = {w.name: w for w in (F2_K2S2, F2_1X1, G3_DW)}
 
 
 # --------------------------------------------------------------------------------------
