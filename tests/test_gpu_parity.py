@@ -331,6 +331,9 @@ DEPTHWISE = [
     ((2, 2, 12, 13), 5, dict(pads=[2, 2, 2, 2])),
     ((1, 2, 5, 24), 4, dict(strides=[4, 4], pads=[0, 1, 3, 0])),
     ((1, 3, 20, 24), 4, dict(strides=[2, 2], pads=[3, 0, 0, 3], output_padding=[1, 1])),
+    # stride 1 with rows of whole 8-column pieces (the streaming-store path)
+    ((1, 3, 10, 16), 3, dict(pads=[1, 1, 1, 1])),
+    ((2, 2, 6, 24), 5, dict(pads=[2, 2, 2, 2])),
 ]
 
 

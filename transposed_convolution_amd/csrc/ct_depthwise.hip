@@ -12,17 +12,19 @@
 //
 // Work unit = (plane n*C + channel, band of output rows).  A block stages the band's input
 // rows in LDS (zero columns on both sides, so no column tests remain), then each thread
-// makes S output rows x 8 output columns: for each output row phase it reads T1 input
-// rows at that phase's row offset, and each column phase applies its T1 x T2 sub-kernel
-// (held in registers) at its own column offset within that window.  Blocks are persistent
-// and issue the global loads of their next unit before computing the current one.
-// Products of float16 values are exact in float32; pairs of column taps are summed by a
-// packed float16 dot product with float32 accumulation.  Each result is rounded once to
-// float16 and a row of 8 is written as one 16-byte store.
+// makes 8 columns of one output row at a time: it reads T1 input rows at the row phase's
+// offset, and each column phase applies its T1 x T2 sub-kernel (held in registers) at its
+// own column offset within that window.  Blocks are persistent and issue the global loads
+// of their next unit before computing the current one.  Products of float16 values are
+// exact in float32; pairs of column taps are summed by a packed float16 dot product with
+// float32 accumulation.  Each result is rounded once to float16 and a row of 8 is written
+// as one 16-byte store; consecutive threads write consecutive pieces of Y, so with rows
+// of whole pieces the stores are streaming stores of whole lines.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
 #include <cstring>
+#include <type_traits>
 
 #include "ct_internal.hpp"
 
@@ -101,8 +103,13 @@ __global__ __launch_bounds__(kDwThreads) void depthwise_kernel(const _Float16 *_
         chr[q] = k / cpl;
         chc[q] = (k - chr[q] * cpl) * 8;
     }
-    const int seg0 = threadIdx.x % segs, jr0 = threadIdx.x / segs;
-    const int dseg = kDwThreads % segs, djr = kDwThreads / segs;
+    // item (output row of the band, segment of 8 columns), segments fastest: the lanes of
+    // a wave cover consecutive stretches of Y
+    const int seg0 = threadIdx.x % segs, or0 = threadIdx.x / segs;
+    const int dseg = kDwThreads % segs, dor = kDwThreads / segs;
+    // whole rows of 16-byte pieces: consecutive items are consecutive in Y, so a wave's
+    // stores cover whole lines and go out as streaming stores (Y is read by no block)
+    const bool stream = p.O2 % OC == 0 && reinterpret_cast<uintptr_t>(y) % 16 == 0;
 
     struct Unit {
         int c, ch, oh0, oh1, j1lo, j1hi, ilo, vr0, nvr;
@@ -210,83 +217,130 @@ __global__ __launch_bounds__(kDwThreads) void depthwise_kernel(const _Float16 *_
         if (tn < p.units) issue(nxt);
 
         // ---- compute and store the current unit ----
-        const int jrows = cur.j1hi - cur.j1lo + 1;
+        // Each item is one output row oh = S * j1 + rh: its row phase rh selects the
+        // window's row offset and the sub-kernels (selects over the S phases in registers)
+        const int orows = cur.oh1 - cur.oh0;  // oh0 is a multiple of S: oh0 = S * j1lo
         _Float16 *const yplane = y + size_t(cur.c) * p.O1 * p.O2;
-        for (int seg = seg0, jr = jr0; jr < jrows;) {
-            const int j1 = cur.j1lo + jr;
-            const _Float16 *row0 = sx + kDwGuard + p.sh + jr * R + (seg * JC + p.lo2);
+        int a0r[S];
 #pragma unroll
-            for (int rh = 0; rh < S; ++rh) {
-                const int oh = S * j1 + rh;
-                // this row phase's T1 input rows, XW columns from the segment's start
-                const _Float16 *win = row0 + p.a0_1[rh] * R;
-                _Float16 xs[T1][XW];
-                if constexpr (S <= 2) {
-                    // 8-byte aligned: whole 4-element pieces
-                    typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
-                    constexpr int NV = (XW + 3) / 4;
+        for (int r = 0; r < S; ++r) a0r[r] = p.a0_1[r] * R;
+        // two copies of the item loop, with and without streaming stores: a store under a
+        // run-time choice would be merged with the plain one and lose its cache hint
+        auto items = [&](auto streaming) __attribute__((always_inline)) {
+        for (int seg = seg0, orr = or0; orr < orows;) {
+            const int jr = orr / S, rh = orr - jr * S;
+            // value of row phase rh among S candidates of 32 bits, by byte permutes on its
+            // bits: a select would be folded into an indexed load from a private array
+            const unsigned sel1 = (rh & 1) ? 0x03020100u : 0x07060504u;  // perm(a, b, .) = b : a
+            const unsigned sel2 = (rh & 2) ? 0x03020100u : 0x07060504u;
+            auto pick = [&](const auto (&c)[S]) __attribute__((always_inline)) {
+                using T = typename std::remove_cv<typename std::remove_reference<decltype(c[0])>::type>::type;
+                static_assert(sizeof(T) == 4, "32-bit candidates");
+                auto u = [](T v) { return __builtin_bit_cast(unsigned, v); };
+                if constexpr (S == 1) {
+                    return c[0];
+                } else if constexpr (S == 2) {
+                    return __builtin_bit_cast(T, __builtin_amdgcn_perm(u(c[0]), u(c[1]), sel1));
+                } else {
+                    static_assert(S == 4, "strides 1, 2 and 4");
+                    const unsigned lo = __builtin_amdgcn_perm(u(c[0]), u(c[1]), sel1);
+                    const unsigned hi = __builtin_amdgcn_perm(u(c[2]), u(c[3]), sel1);
+                    return __builtin_bit_cast(T, __builtin_amdgcn_perm(lo, hi, sel2));
+                }
+            };
+            const int a0 = pick(a0r);
+            // this row phase's T1 input rows, XW columns from the segment's start
+            const _Float16 *win = sx + kDwGuard + p.sh + jr * R + a0 + (seg * JC + p.lo2);
+            h2 ws[S][T1][NP > 0 ? NP : 1];
+            float wts[S][T1];
+#pragma unroll
+            for (int rwp = 0; rwp < S; ++rwp)
+#pragma unroll
+                for (int a = 0; a < T1; ++a) {
+#pragma unroll
+                    for (int m = 0; m < NP; ++m) {
+                        h2 c[S];
+#pragma unroll
+                        for (int r = 0; r < S; ++r) c[r] = wp[r][rwp][a][m];
+                        ws[rwp][a][m] = pick(c);
+                    }
+                    float c[S];
+#pragma unroll
+                    for (int r = 0; r < S; ++r) c[r] = wt[r][rwp][a];
+                    wts[rwp][a] = pick(c);
+                }
+            _Float16 xs[T1][XW];
+            if constexpr (S <= 2) {
+                // 8-byte aligned: whole 4-element pieces
+                typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+                constexpr int NV = (XW + 3) / 4;
+#pragma unroll
+                for (int a = 0; a < T1; ++a) {
+                    const u32x2 *wv = reinterpret_cast<const u32x2 *>(win + a * R);
+#pragma unroll
+                    for (int v = 0; v < NV; ++v) {
+                        const u32x2 pv = wv[v];
+#pragma unroll
+                        for (int e = 0; e < 4; ++e)
+                            if (4 * v + e < XW)
+                                xs[a][4 * v + e] = __builtin_bit_cast(_Float16, (unsigned short)((pv[e >> 1] >> (16 * (e & 1))) & 0xffffu));
+                    }
+                }
+            } else {
+#pragma unroll
+                for (int a = 0; a < T1; ++a)
+#pragma unroll
+                    for (int q = 0; q < XW; ++q) xs[a][q] = win[a * R + q];
+            }
+            float out[OC];
+#pragma unroll
+            for (int rwp = 0; rwp < S; ++rwp) {
+                const int o2 = (OFF2 >> rwp) & 1;
+#pragma unroll
+                for (int je = 0; je < JC; ++je) {
+                    float acc = bv;
 #pragma unroll
                     for (int a = 0; a < T1; ++a) {
-                        const u32x2 *wv = reinterpret_cast<const u32x2 *>(win + a * R);
 #pragma unroll
-                        for (int v = 0; v < NV; ++v) {
-                            const u32x2 pv = wv[v];
-#pragma unroll
-                            for (int e = 0; e < 4; ++e)
-                                if (4 * v + e < XW)
-                                    xs[a][4 * v + e] = __builtin_bit_cast(_Float16, (unsigned short)((pv[e >> 1] >> (16 * (e & 1))) & 0xffffu));
-                        }
+                        for (int m = 0; m < NP; ++m)
+                            acc = __builtin_amdgcn_fdot2(h2{xs[a][je + o2 + 2 * m], xs[a][je + o2 + 2 * m + 1]},
+                                                         ws[rwp][a][m], acc, false);
+                        if (T2 & 1) acc += float(xs[a][je + o2 + T2 - 1]) * wts[rwp][a];
                     }
-                } else {
-#pragma unroll
-                    for (int a = 0; a < T1; ++a)
-#pragma unroll
-                        for (int q = 0; q < XW; ++q) xs[a][q] = win[a * R + q];
+                    out[je * S + rwp] = acc;
                 }
-                float out[OC];
+            }
+            if (!p.act.identity()) {
 #pragma unroll
-                for (int rwp = 0; rwp < S; ++rwp) {
-                    const int o2 = (OFF2 >> rwp) & 1;
+                for (int e = 0; e < OC; ++e) out[e] = p.act(out[e]);
+            }
+            _Float16 *yr = yplane + size_t(cur.oh0 + orr) * p.O2 + seg * OC;
+            if (seg * OC + OC <= p.O2 && (reinterpret_cast<uintptr_t>(yr) % 16 == 0)) {
+                u32x4 o;
 #pragma unroll
-                    for (int je = 0; je < JC; ++je) {
-                        float acc = bv;
+                for (int k = 0; k < 4; ++k)
+                    o[k] = __builtin_bit_cast(unsigned, __builtin_convertvector(f2{out[2 * k], out[2 * k + 1]}, h2));
+                if constexpr (decltype(streaming)::value)
+                    __builtin_nontemporal_store(o, reinterpret_cast<u32x4 *>(yr));
+                else
+                    *reinterpret_cast<u32x4 *>(yr) = o;
+            } else {
 #pragma unroll
-                        for (int a = 0; a < T1; ++a) {
-#pragma unroll
-                            for (int m = 0; m < NP; ++m)
-                                acc = __builtin_amdgcn_fdot2(h2{xs[a][je + o2 + 2 * m], xs[a][je + o2 + 2 * m + 1]},
-                                                             wp[rh][rwp][a][m], acc, false);
-                            if (T2 & 1) acc += float(xs[a][je + o2 + T2 - 1]) * wt[rh][rwp][a];
-                        }
-                        out[je * S + rwp] = acc;
-                    }
-                }
-                if (!p.act.identity()) {
-#pragma unroll
-                    for (int e = 0; e < OC; ++e) out[e] = p.act(out[e]);
-                }
-                if (oh < cur.oh1) {
-                    _Float16 *yr = yplane + size_t(oh) * p.O2 + seg * OC;
-                    if (seg * OC + OC <= p.O2 && (reinterpret_cast<uintptr_t>(yr) % 16 == 0)) {
-                        u32x4 o;
-#pragma unroll
-                        for (int k = 0; k < 4; ++k)
-                            o[k] = __builtin_bit_cast(unsigned, __builtin_convertvector(f2{out[2 * k], out[2 * k + 1]}, h2));
-                        *reinterpret_cast<u32x4 *>(yr) = o;
-                    } else {
-#pragma unroll
-                        for (int e = 0; e < OC; ++e)
-                            if (seg * OC + e < p.O2) yr[e] = _Float16(out[e]);
-                    }
-                }
+                for (int e = 0; e < OC; ++e)
+                    if (seg * OC + e < p.O2) yr[e] = _Float16(out[e]);
             }
             seg += dseg;
-            jr += djr;
+            orr += dor;
             if (seg >= segs) {
                 seg -= segs;
-                ++jr;
+                ++orr;
             }
         }
+        };
+        if (stream)
+            items(std::true_type{});
+        else
+            items(std::false_type{});
         __syncthreads();  // the stage and seff are rewritten next
         if (tn >= p.units) break;
         t = tn;

@@ -22,6 +22,7 @@
 
 #include <algorithm>
 #include <cstring>
+#include <type_traits>
 
 #include "ct_internal.hpp"
 
@@ -166,8 +167,12 @@ __global__ __launch_bounds__(kThreads) void dwcl_kernel(const _Float16 *__restri
         for (int k = 0; k < 8; ++k) bv[k] = (bias && c + k < p.C) ? float(bias[c + k]) : 0.0f;
     }
     const bool vec = c_lo + oc * 8 + 8 <= p.C && reinterpret_cast<uintptr_t>(y) % 16 == 0;
+    const bool full_lines = co % 8 == 0 && p.C % 64 == 0 && reinterpret_cast<uintptr_t>(y) % 128 == 0;
 
-    auto body = [&](auto fin) {
+    // streaming stores when adjacent lanes cover whole 128-byte lines of Y (the tile's
+    // channel run of a pixel); two copies of the loop, since a store under a run-time
+    // choice would be merged with the plain one and lose its cache hint
+    auto body = [&](auto fin, auto streaming) {
         for (int pos = slot; pos < kTJ1 * kTJ2; pos += nslots) {
             const int pj1 = pos / kTJ2, pj2 = pos - pj1 * kTJ2;
             const int j1 = j1lo + pj1, j2 = j2lo + pj2;
@@ -198,14 +203,22 @@ __global__ __launch_bounds__(kThreads) void dwcl_kernel(const _Float16 *__restri
                         f16x8 o;
 #pragma unroll
                         for (int k = 0; k < 8; ++k) o[k] = _Float16(fin(acc[k]));
-                        *reinterpret_cast<f16x8 *>(dst) = o;
+                        // Y is written once and read by no block; partial lines go through
+                        // the cache, which merges them
+                        if constexpr (decltype(streaming)::value)
+                            __builtin_nontemporal_store(o, reinterpret_cast<f16x8 *>(dst));
+                        else
+                            *reinterpret_cast<f16x8 *>(dst) = o;
                     } else {
                         for (int k = 0; k < 8 && c_lo + oc * 8 + k < p.C; ++k) dst[k] = _Float16(fin(acc[k]));
                     }
                 }
         }
     };
-    with_activation(p.act, body);
+    if (full_lines)
+        with_activation(p.act, [&](auto fin) { body(fin, std::true_type{}); });
+    else
+        with_activation(p.act, [&](auto fin) { body(fin, std::false_type{}); });
 }
 
 struct DwClPlan {
