@@ -85,12 +85,13 @@ def forced_tile(T, tile):
 # benchmark configurations
 # --------------------------------------------------------------------------------------
 WHOLE = [W.C1, W.C2, W.C3, W.C3_NHWC]
-FULL = [W.C4, W.C4_NHWC, W.C5_S1, W.C5_S1_P1, W.C5_S2]
+FULL = [W.C4, W.C4_NHWC, W.C5_S1, W.C5_S1_P1, W.C5_S2, W.G3_DW]
 # the family the dispatcher must pick for each configuration (a silent fall-back to the
 # gather kernel would still be correct, so parity alone would not notice it)
 EXPECTED_FAMILY = {W.C1.name: "direct", W.C2.name: "igemm", W.C3.name: "grouped", W.C3_NHWC.name: "grouped",
                    W.C4.name: "igemm",
-                   W.C4_NHWC.name: "igemm", W.C5_S1.name: "igemm", W.C5_S1_P1.name: "igemm", W.C5_S2.name: "igemm"}
+                   W.C4_NHWC.name: "igemm", W.C5_S1.name: "igemm", W.C5_S1_P1.name: "igemm", W.C5_S2.name: "igemm",
+                   W.G3_DW.name: "grouped"}
 
 
 def _auto_family(T, wl, x, w, b):
@@ -371,6 +372,16 @@ GROUPED_3D = [
     ((2, 3, 6, 4, 8), (3, 1, 4, 3, 3), dict(strides=[2, 1, 1], pads=[1, 1, 1, 2, 1, 1], group=3)),
     ((1, 16, 4, 40, 36), (16, 1, 3, 3, 3), dict(strides=[2, 2, 2], pads=[1] * 6, output_padding=[1, 1, 1], group=16)),
     ((1, 4, 2, 3, 4), (4, 2, 1, 1, 1), dict(strides=[4, 2, 3], group=2)),
+    # depthwise with rows of a multiple of 8 inputs: the depthwise kernel's planes of
+    # first-axis taps (1, 2 or 3 per output plane, planes outside the input, dilation and
+    # stride 3 on the first axis, row bands)
+    ((2, 8, 5, 12, 16), (8, 1, 3, 3, 3), dict(strides=[2, 2, 2], pads=[1] * 6, output_padding=[1, 1, 1], group=8)),
+    ((1, 4, 6, 9, 24), (4, 1, 4, 4, 4), dict(strides=[2, 2, 2], pads=[1] * 6, group=4)),
+    ((1, 3, 4, 7, 16), (3, 1, 3, 3, 3), dict(pads=[1] * 6, group=3)),
+    ((1, 2, 3, 5, 8), (2, 1, 2, 2, 2), dict(strides=[2, 2, 2], group=2)),
+    ((1, 4, 5, 6, 16), (4, 1, 3, 3, 3), dict(strides=[2, 2, 2], dilations=[2, 1, 1], pads=[2, 1, 1, 0, 1, 1], group=4)),
+    ((1, 2, 3, 4, 8), (2, 1, 3, 2, 2), dict(strides=[3, 2, 2], pads=[2, 0, 0, 3, 0, 0], group=2)),
+    ((1, 6, 3, 70, 32), (6, 1, 3, 4, 4), dict(strides=[2, 2, 2], pads=[1] * 6, group=6)),
 ]
 
 

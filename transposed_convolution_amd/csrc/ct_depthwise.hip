@@ -36,6 +36,7 @@ constexpr int kDwMaxS = 4;                                 // largest stride ser
 constexpr int kDwMaxChunks = 8;                              // 16-byte input chunks per thread per unit
 constexpr int kDwStageBytes = kDwMaxChunks * kDwThreads * 16;  // staged band (float16), upper bound
 constexpr int kDwGuard = 8;                                    // zero elements ahead of staged row 0
+constexpr int kDwMaxS0 = 4;                                    // largest stride on the first axis (rank 3)
 
 struct DwArgs {
     int C, L1, L2, O1, O2, K1, K2, b1, b2, d1, d2;
@@ -47,10 +48,19 @@ struct DwArgs {
     int stage_elems;    // halves per stage buffer (multiple of 8)
     int sh;             // column shift of the staged rows (0..3): window reads start 8-byte aligned
     int a0_1[kDwMaxS];  // per row residue: its window's row offset from lo1
-    Act act;            // output activation
+    // first axis (rank 3; a single plane otherwise): output plane o0 = s0 * j0 + r0 reads
+    // input planes i0 = j0 + be00(r0) - u * bs0 with kernel index k00(r0) + u * ks0 for
+    // u < nt0(r0); the per-residue values are 16-bit fields r0 of these words (a table
+    // indexed at run time would be read from memory inside the unit loop)
+    int L0, O0, K0, s0, ks0, bs0;
+    unsigned long long nt0w, k00w, be00w;
+    int slot_elems;  // halves per staged plane (the planes are staged one after another)
+    Act act;         // output activation
 };
 
-template <int S, int T1, int T2, int OFF2, int NQ>
+// T0: staged input planes per unit (rank 3: the most first-axis taps of an output plane);
+// 0 for ranks 1 and 2, whose units read one plane and skip the first-axis bookkeeping.
+template <int S, int T1, int T2, int OFF2, int NQ, int T0>
 __global__ __launch_bounds__(kDwThreads) void depthwise_kernel(const _Float16 *__restrict__ x,
                                                                const _Float16 *__restrict__ w,
                                                                const _Float16 *__restrict__ bias,
@@ -59,6 +69,7 @@ __global__ __launch_bounds__(kDwThreads) void depthwise_kernel(const _Float16 *_
     constexpr int OC = 8;               // output columns per thread
     constexpr int JC = OC / S;          // input-grid columns they span
     constexpr int NE = S * S * T1 * T2;  // sub-kernel entries over all phases
+    constexpr int NT0 = T0 > 0 ? T0 : 1;  // staged planes
     // column offset of residue r's window (0 or 1), fixed at compile time so every
     // register index below is a constant; row offsets are LDS addresses and stay runtime
     constexpr int MAXO2 = (OFF2 != 0) ? 1 : 0;
@@ -75,7 +86,7 @@ __global__ __launch_bounds__(kDwThreads) void depthwise_kernel(const _Float16 *_
     // on an 8-byte boundary (LDS reads that are not naturally aligned stall).
     extern __shared__ __attribute__((aligned(16))) unsigned char dw_lds[];
     _Float16 *const sx = reinterpret_cast<_Float16 *>(dw_lds);
-    __shared__ _Float16 seff[NE];
+    __shared__ _Float16 seff[NT0 * NE];  // sub-kernels of the unit's first-axis taps
 
     const int R = p.row_w, cpl = p.L2 / 8;
     const int segs = (p.O2 + OC - 1) / OC;
@@ -94,15 +105,6 @@ __global__ __launch_bounds__(kDwThreads) void depthwise_kernel(const _Float16 *_
             t2 / p.d2 < p.K2)
             eidx = (t1 / p.d1) * p.K2 + t2 / p.d2;
     }
-    // chunk q of this thread is the k-th 16-byte piece of the band's valid input rows:
-    // row k / cpl of them, column 8 * (k % cpl)
-    int chr[NQ], chc[NQ];
-#pragma unroll
-    for (int q = 0; q < NQ; ++q) {
-        const int k = threadIdx.x + q * kDwThreads;
-        chr[q] = k / cpl;
-        chc[q] = (k - chr[q] * cpl) * 8;
-    }
     // item (output row of the band, segment of 8 columns), segments fastest: the lanes of
     // a wave cover consecutive stretches of Y
     const int seg0 = threadIdx.x % segs, or0 = threadIdx.x / segs;
@@ -112,13 +114,33 @@ __global__ __launch_bounds__(kDwThreads) void depthwise_kernel(const _Float16 *_
     const bool stream = p.O2 % OC == 0 && reinterpret_cast<uintptr_t>(y) % 16 == 0;
 
     struct Unit {
-        int c, ch, oh0, oh1, j1lo, j1hi, ilo, vr0, nvr;
+        int c, pc, ch, oh0, oh1, j1lo, j1hi, ilo, vr0, nvr;
+        int k0, i0, live;  // first-axis tap 0's kernel index and input plane; bit u: tap u reads a plane
     };
     auto unit_of = [&](int t) {
         Unit u;
         const int band = t % p.nbands;
-        u.c = t / p.nbands;
-        u.ch = u.c % p.C;
+        u.c = t / p.nbands;  // output plane (image, channel, o0)
+        if constexpr (T0 == 0) {
+            u.pc = u.c;
+            u.k0 = u.i0 = 0;
+            u.live = 1;
+        } else {
+            u.pc = u.c / p.O0;  // image and channel
+            const int o0 = u.c - u.pc * p.O0;
+            const int j0 = o0 / p.s0, r0 = o0 - j0 * p.s0;
+            auto field = [&](unsigned long long wd) { return int(short((wd >> (16 * r0)) & 0xffffu)); };
+            u.k0 = field(p.k00w);
+            u.i0 = j0 + field(p.be00w);
+            const int nt0 = field(p.nt0w);
+            u.live = 0;
+#pragma unroll
+            for (int v = 0; v < T0; ++v) {
+                const int i0 = u.i0 - v * p.bs0;
+                if (v < nt0 && i0 >= 0 && i0 < p.L0) u.live |= 1 << v;
+            }
+        }
+        u.ch = u.pc % p.C;
         u.oh0 = band * p.band;
         u.oh1 = min(u.oh0 + p.band, p.O1);
         u.j1lo = u.oh0 / S;
@@ -133,22 +155,54 @@ __global__ __launch_bounds__(kDwThreads) void depthwise_kernel(const _Float16 *_
     // Operands of one unit, loaded ahead.  Loads are unconditional from clamped addresses;
     // the validity mask is applied when the chunk is staged, so nothing waits for the
     // data before then.
+    // Chunk k of a unit is the (k % nch)-th 16-byte piece of the valid rows of staged plane
+    // k / nch (nch pieces per plane); dsto[q] is where chunk q of the thread goes in LDS.
     u32x4 v[NQ];
-    unsigned vok = 0;
-    _Float16 ew, braw;
+    int dsto[NQ];     // rank 3
+    unsigned vok = 0;  // one plane: bit q, chunk q holds input
+    // one plane: chunk k = threadIdx.x + q * kDwThreads is the k-th 16-byte piece of the
+    // band's valid input rows, row chr[q] of them at column chc[q], whatever the unit
+    int chr[NQ], chc[NQ];
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) {
+        const int k = threadIdx.x + q * kDwThreads;
+        chr[q] = k / cpl;
+        chc[q] = (k - chr[q] * cpl) * 8;
+    }
+    _Float16 ew[NT0], braw;
     auto issue = [&](const Unit &u) {
-        const _Float16 *xp = x + size_t(u.c) * plane_in;
-        const _Float16 *xb = xp + (u.ilo + u.vr0) * p.L2;  // first valid row: contiguous from here
-        ew = w[size_t(u.ch) * p.K1 * p.K2 + max(eidx, 0)];
-        braw = *(bias ? bias + u.ch : xp);  // used only with a bias
+        const _Float16 *xp = x + size_t(u.pc) * p.L0 * plane_in;  // the image and channel
         const int nch = u.nvr * cpl;
-        vok = 0;
+        if constexpr (T0 == 0) {
+            const _Float16 *xb = xp + (u.ilo + u.vr0) * p.L2;  // first valid row: contiguous from here
+            ew[0] = w[size_t(u.ch) * p.K1 * p.K2 + max(eidx, 0)];
+            braw = *(bias ? bias + u.ch : xp);  // used only with a bias
+            vok = 0;
+#pragma unroll
+            for (int q = 0; q < NQ; ++q) {
+                const int k = threadIdx.x + q * kDwThreads;
+                const bool ok = k < nch;
+                v[q] = *reinterpret_cast<const u32x4 *>(ok ? xb + 8 * k : xp);
+                vok |= unsigned(ok) << q;
+            }
+            return;
+        }
+        const size_t plane_w = size_t(p.K1) * p.K2;
+#pragma unroll
+        for (int v0 = 0; v0 < NT0; ++v0)
+            ew[v0] = w[(size_t(u.ch) * p.K0 + (((u.live >> v0) & 1) ? u.k0 + v0 * p.ks0 : 0)) * plane_w + max(eidx, 0)];
+        braw = *(bias ? bias + u.ch : xp);  // used only with a bias
+        const UDiv dn(nch > 0 ? nch : 1), dc(cpl);
 #pragma unroll
         for (int q = 0; q < NQ; ++q) {
             const int k = threadIdx.x + q * kDwThreads;
-            const bool ok = k < nch;
-            v[q] = *reinterpret_cast<const u32x4 *>(ok ? xb + 8 * k : xp);
-            vok |= unsigned(ok) << q;
+            const int sl = dn.div(k), kk = k - sl * nch;
+            const bool ok = nch > 0 && sl < NT0 && ((u.live >> sl) & 1);
+            const int r = dc.div(kk), c8 = (kk - r * cpl) * 8;
+            // rows ilo + vr0 + r of input plane i0 - sl * bs0, contiguous from the first valid row
+            const _Float16 *src = xp + (size_t(u.i0 - sl * p.bs0) * plane_in + size_t(u.ilo + u.vr0 + r) * p.L2 + c8);
+            v[q] = *reinterpret_cast<const u32x4 *>(ok ? src : xp);
+            dsto[q] = ok ? sl * p.slot_elems + kDwGuard + p.sh + (u.vr0 + r) * R + c8 : -1;
         }
     };
 
@@ -163,21 +217,27 @@ __global__ __launch_bounds__(kDwThreads) void depthwise_kernel(const _Float16 *_
     for (;;) {
         // ---- stage the current unit ----
         // staged rows without input (above row 0 or below row L1-1): zeros
+        // (in every plane that is read; planes of no tap are neither staged nor read)
         {
             const int nz = (p.nrows - cur.nvr) * cpl;
-            for (int k = threadIdx.x; k < nz; k += kDwThreads) {
-                int r = k / cpl;
-                r = r < cur.vr0 ? r : r + cur.nvr;
-                reinterpret_cast<u32x4 *>(sx + kDwGuard + r * R)[k % cpl] = u32x4{0u, 0u, 0u, 0u};
-                // the shifted row's last sh elements spill into the next chunk
-                if (p.sh > 0 && k % cpl == cpl - 1)
-                    reinterpret_cast<u32x4 *>(sx + kDwGuard + r * R)[cpl] = u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+            for (int v0 = 0; v0 < NT0; ++v0) {
+                if (T0 > 0 && !((cur.live >> v0) & 1)) continue;
+                _Float16 *const sp = sx + v0 * p.slot_elems + kDwGuard;
+                for (int k = threadIdx.x; k < nz; k += kDwThreads) {
+                    int r = k / cpl;
+                    r = r < cur.vr0 ? r : r + cur.nvr;
+                    reinterpret_cast<u32x4 *>(sp + r * R)[k % cpl] = u32x4{0u, 0u, 0u, 0u};
+                    // the shifted row's last sh elements spill into the next chunk
+                    if (p.sh > 0 && k % cpl == cpl - 1)
+                        reinterpret_cast<u32x4 *>(sp + r * R)[cpl] = u32x4{0u, 0u, 0u, 0u};
+                }
             }
         }
 #pragma unroll
         for (int q = 0; q < NQ; ++q)
-            if ((vok >> q) & 1u) {
-                _Float16 *dst = sx + kDwGuard + p.sh + (cur.vr0 + chr[q]) * R + chc[q];
+            if (T0 == 0 ? ((vok >> q) & 1u) != 0 : dsto[q] >= 0) {
+                _Float16 *dst = T0 == 0 ? sx + kDwGuard + p.sh + (cur.vr0 + chr[q]) * R + chc[q] : sx + dsto[q];
                 const u32x4 vq = v[q];
                 if (p.sh == 0) {  // 16-byte aligned
                     *reinterpret_cast<u32x4 *>(dst) = vq;
@@ -192,24 +252,30 @@ __global__ __launch_bounds__(kDwThreads) void depthwise_kernel(const _Float16 *_
                     *reinterpret_cast<unsigned short *>(dst + 7) = (unsigned short)(vq[3] >> 16);
                 }
             }
-        if (threadIdx.x < NE) seff[threadIdx.x] = eidx >= 0 ? ew : _Float16(0.0f);
+        if (threadIdx.x < NE) {
+#pragma unroll
+            for (int v0 = 0; v0 < NT0; ++v0) seff[v0 * NE + threadIdx.x] = eidx >= 0 ? ew[v0] : _Float16(0.0f);
+        }
         const float bv = bias ? float(braw) : 0.0f;
         __syncthreads();
         // sub-kernels in registers: column-tap pairs for the packed dot products, and
         // the odd last column tap (T2 odd) as float
-        h2 wp[S][S][T1][NP > 0 ? NP : 1];
-        float wt[S][S][T1];
+        // (one set per first-axis tap)
+        h2 wp[NT0][S][S][T1][NP > 0 ? NP : 1];
+        float wt[NT0][S][S][T1];
 #pragma unroll
-        for (int rh = 0; rh < S; ++rh)
+        for (int v0 = 0; v0 < NT0; ++v0)
 #pragma unroll
-            for (int rwp = 0; rwp < S; ++rwp)
+            for (int rh = 0; rh < S; ++rh)
 #pragma unroll
-                for (int a = 0; a < T1; ++a) {
-                    const _Float16 *e = seff + ((rh * S + rwp) * T1 + a) * T2;
+                for (int rwp = 0; rwp < S; ++rwp)
 #pragma unroll
-                    for (int m = 0; m < NP; ++m) wp[rh][rwp][a][m] = h2{e[2 * m], e[2 * m + 1]};
-                    wt[rh][rwp][a] = (T2 & 1) ? float(e[T2 - 1]) : 0.0f;
-                }
+                    for (int a = 0; a < T1; ++a) {
+                        const _Float16 *e = seff + v0 * NE + ((rh * S + rwp) * T1 + a) * T2;
+#pragma unroll
+                        for (int m = 0; m < NP; ++m) wp[v0][rh][rwp][a][m] = h2{e[2 * m], e[2 * m + 1]};
+                        wt[v0][rh][rwp][a] = (T2 & 1) ? float(e[T2 - 1]) : 0.0f;
+                    }
 
         // ---- load the next unit ahead, if there is one ----
         const int tn = t + int(gridDim.x);
@@ -251,63 +317,70 @@ __global__ __launch_bounds__(kDwThreads) void depthwise_kernel(const _Float16 *_
             const int a0 = pick(a0r);
             // this row phase's T1 input rows, XW columns from the segment's start
             const _Float16 *win = sx + kDwGuard + p.sh + jr * R + a0 + (seg * JC + p.lo2);
-            h2 ws[S][T1][NP > 0 ? NP : 1];
-            float wts[S][T1];
-#pragma unroll
-            for (int rwp = 0; rwp < S; ++rwp)
-#pragma unroll
-                for (int a = 0; a < T1; ++a) {
-#pragma unroll
-                    for (int m = 0; m < NP; ++m) {
-                        h2 c[S];
-#pragma unroll
-                        for (int r = 0; r < S; ++r) c[r] = wp[r][rwp][a][m];
-                        ws[rwp][a][m] = pick(c);
-                    }
-                    float c[S];
-#pragma unroll
-                    for (int r = 0; r < S; ++r) c[r] = wt[r][rwp][a];
-                    wts[rwp][a] = pick(c);
-                }
-            _Float16 xs[T1][XW];
-            if constexpr (S <= 2) {
-                // 8-byte aligned: whole 4-element pieces
-                typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
-                constexpr int NV = (XW + 3) / 4;
-#pragma unroll
-                for (int a = 0; a < T1; ++a) {
-                    const u32x2 *wv = reinterpret_cast<const u32x2 *>(win + a * R);
-#pragma unroll
-                    for (int v = 0; v < NV; ++v) {
-                        const u32x2 pv = wv[v];
-#pragma unroll
-                        for (int e = 0; e < 4; ++e)
-                            if (4 * v + e < XW)
-                                xs[a][4 * v + e] = __builtin_bit_cast(_Float16, (unsigned short)((pv[e >> 1] >> (16 * (e & 1))) & 0xffffu));
-                    }
-                }
-            } else {
-#pragma unroll
-                for (int a = 0; a < T1; ++a)
-#pragma unroll
-                    for (int q = 0; q < XW; ++q) xs[a][q] = win[a * R + q];
-            }
             float out[OC];
 #pragma unroll
-            for (int rwp = 0; rwp < S; ++rwp) {
-                const int o2 = (OFF2 >> rwp) & 1;
+            for (int e = 0; e < OC; ++e) out[e] = bv;
 #pragma unroll
-                for (int je = 0; je < JC; ++je) {
-                    float acc = bv;
+            for (int v0 = 0; v0 < NT0; ++v0) {
+                if (T0 > 0 && !((cur.live >> v0) & 1)) continue;  // uniform over the block
+                h2 ws[S][T1][NP > 0 ? NP : 1];
+                float wts[S][T1];
+#pragma unroll
+                for (int rwp = 0; rwp < S; ++rwp)
 #pragma unroll
                     for (int a = 0; a < T1; ++a) {
 #pragma unroll
-                        for (int m = 0; m < NP; ++m)
-                            acc = __builtin_amdgcn_fdot2(h2{xs[a][je + o2 + 2 * m], xs[a][je + o2 + 2 * m + 1]},
-                                                         ws[rwp][a][m], acc, false);
-                        if (T2 & 1) acc += float(xs[a][je + o2 + T2 - 1]) * wts[rwp][a];
+                        for (int m = 0; m < NP; ++m) {
+                            h2 c[S];
+#pragma unroll
+                            for (int r = 0; r < S; ++r) c[r] = wp[v0][r][rwp][a][m];
+                            ws[rwp][a][m] = pick(c);
+                        }
+                        float c[S];
+#pragma unroll
+                        for (int r = 0; r < S; ++r) c[r] = wt[v0][r][rwp][a];
+                        wts[rwp][a] = pick(c);
                     }
-                    out[je * S + rwp] = acc;
+                const _Float16 *const wn = win + v0 * p.slot_elems;
+                _Float16 xs[T1][XW];
+                if constexpr (S <= 2) {
+                    // 8-byte aligned: whole 4-element pieces
+                    typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+                    constexpr int NV = (XW + 3) / 4;
+#pragma unroll
+                    for (int a = 0; a < T1; ++a) {
+                        const u32x2 *wv = reinterpret_cast<const u32x2 *>(wn + a * R);
+#pragma unroll
+                        for (int v = 0; v < NV; ++v) {
+                            const u32x2 pv = wv[v];
+#pragma unroll
+                            for (int e = 0; e < 4; ++e)
+                                if (4 * v + e < XW)
+                                    xs[a][4 * v + e] = __builtin_bit_cast(_Float16, (unsigned short)((pv[e >> 1] >> (16 * (e & 1))) & 0xffffu));
+                        }
+                    }
+                } else {
+#pragma unroll
+                    for (int a = 0; a < T1; ++a)
+#pragma unroll
+                        for (int q = 0; q < XW; ++q) xs[a][q] = wn[a * R + q];
+                }
+#pragma unroll
+                for (int rwp = 0; rwp < S; ++rwp) {
+                    const int o2 = (OFF2 >> rwp) & 1;
+#pragma unroll
+                    for (int je = 0; je < JC; ++je) {
+                        float acc = out[je * S + rwp];
+#pragma unroll
+                        for (int a = 0; a < T1; ++a) {
+#pragma unroll
+                            for (int m = 0; m < NP; ++m)
+                                acc = __builtin_amdgcn_fdot2(h2{xs[a][je + o2 + 2 * m], xs[a][je + o2 + 2 * m + 1]},
+                                                             ws[rwp][a][m], acc, false);
+                            if (T2 & 1) acc += float(xs[a][je + o2 + T2 - 1]) * wts[rwp][a];
+                        }
+                        out[je * S + rwp] = acc;
+                    }
                 }
             }
             if (!p.act.identity()) {
@@ -351,6 +424,7 @@ __global__ __launch_bounds__(kDwThreads) void depthwise_kernel(const _Float16 *_
 struct DwPlan {
     DwArgs a;
     int S, T1, T2, off2;  // off2: bit r = column window offset of residue r
+    int T0;               // kernel's T0: most first-axis taps of a residue (rank 3), else 0
     int nq;               // 16-byte input chunks per thread that stage one band
     size_t lds_bytes;     // staged band
 };
@@ -385,9 +459,13 @@ bool axis_windows(const Geom &g, int ax, int S, int *T, int *lo, int *hi, int *a
 }
 
 // Compiled (S, T, column offset pattern) combinations.
-bool dw_compiled(int S, int T1, int T2, int off2)
+bool dw_compiled(int S, int T1, int T2, int off2, int T0)
 {
     if (T1 != T2) return false;
+    // rank 3 (1 to 3 first-axis taps per output plane): stride 2 with up to 3 taps per
+    // row and column phase, stride 1 with 3 taps
+    if (T0 >= 1 && T0 <= 3) return (S == 2 && T1 >= 1 && T1 <= 3) || (S == 1 && T1 == 3 && off2 == 0);
+    if (T0 != 0) return false;
     if (S == 1) return off2 == 0 && (T1 == 3 || T1 == 5);
     if (S == 2) return T1 >= 1 && T1 <= 3;  // every off2 in [0, 4)
     if (S == 4) return T1 == 2 && (off2 == 0 || off2 == 12);
@@ -396,8 +474,8 @@ bool dw_compiled(int S, int T1, int T2, int off2)
 
 bool make_dwplan(const Geom &g, ct_dtype dt, bool cl, const void *x, DwPlan *pl)
 {
-    if (dt != CT_FLOAT16 || cl || g.Cg != 1 || g.Mg != 1 || g.G < 2 || g.nsp > 2 || g.L[0] != 1 ||
-        g.O[0] != 1 || g.L[1] * g.L[2] == 0 || g.L[1] * g.L[2] >= (1ll << 31))
+    if (dt != CT_FLOAT16 || cl || g.Cg != 1 || g.Mg != 1 || g.G < 2 || g.L[0] * g.L[1] * g.L[2] == 0 ||
+        g.O[0] == 0 || g.L[0] * g.L[1] * g.L[2] >= (1ll << 31) || g.O[0] >= (1ll << 31))
         return false;
     const int S = int(g.s[2]);
     if (g.s[1] != S || (S != 1 && S != 2 && S != 4)) return false;
@@ -411,7 +489,32 @@ bool make_dwplan(const Geom &g, ct_dtype dt, bool cl, const void *x, DwPlan *pl)
         if (a0_2[r] > 1) return false;
         off2 |= a0_2[r] << r;
     }
-    if (!dw_compiled(S, T1, T2, off2)) return false;
+    // first axis (a single plane below rank 3): per residue its taps as a progression
+    if (g.s[0] > kDwMaxS0) return false;
+    const int64_t gs0 = std::__gcd(g.s[0], g.d[0]);
+    a.ks0 = int(g.s[0] / gs0);
+    a.bs0 = int(g.d[0] / gs0);
+    int T0 = 0;
+    for (int r = 0; r < g.s[0]; ++r) {
+        AxisPhase ph;
+        if (!axis_phase(g, 0, r, &ph)) return false;
+        for (int u = 1; u < ph.ntaps; ++u)
+            if (ph.k[u] - ph.k[u - 1] != a.ks0 || ph.beta[u - 1] - ph.beta[u] != a.bs0) return false;
+        const int k0 = ph.ntaps ? ph.k[0] : 0, be0 = ph.ntaps ? ph.beta[0] : 0;
+        if (k0 > 32767 || be0 < -32768 || be0 > 32767) return false;
+        a.nt0w |= (unsigned long long)(ph.ntaps & 0xffff) << (16 * r);
+        a.k00w |= (unsigned long long)(k0 & 0xffff) << (16 * r);
+        a.be00w |= (unsigned long long)(unsigned(be0) & 0xffffu) << (16 * r);
+        T0 = std::max(T0, ph.ntaps);
+    }
+    if (T0 == 0) return false;  // no tap reaches any output plane: the generic kernel handles it
+    a.L0 = int(g.L[0]);
+    a.O0 = int(g.O[0]);
+    a.K0 = int(g.K[0]);
+    a.s0 = int(g.s[0]);
+    pl->T0 = g.nsp == 3 ? T0 : 0;
+    if (!dw_compiled(S, T1, T2, off2, pl->T0)) return false;
+    T0 = std::max(pl->T0, 1);  // staged planes
     a.C = int(g.C);
     a.L1 = int(g.L[1]);
     a.L2 = int(g.L[2]);
@@ -440,22 +543,27 @@ bool make_dwplan(const Geom &g, ct_dtype dt, bool cl, const void *x, DwPlan *pl)
     auto rows_for = [&](int b) { return (b + S - 1) / S - 1 + a.span1; };
     // + 8: the last row shifted by sh, and the 4-element window reads past a row's end
     auto bytes_for = [&](int b) { return (int64_t(kDwGuard) + int64_t(rows_for(b)) * a.row_w + 8) * 2; };
-    auto fits = [&](int b) { return bytes_for(b) <= kDwStageBytes && rows_for(b) * cpl <= kDwMaxChunks * kDwThreads; };
+    // (T0 planes of them)
+    auto fits = [&](int b) {
+        return T0 * bytes_for(b) <= kDwStageBytes && T0 * rows_for(b) * cpl <= kDwMaxChunks * kDwThreads;
+    };
     // band of output rows (a multiple of S) whose staged rows fit
     int band = int((g.O[1] + S - 1) / S) * S;
     while (band > S && !fits(band)) band = (band / 2 + S - 1) / S * S;
     if (!fits(band)) return false;
     // few planes: more bands so the grid still fills the chip
-    while (band >= 8 * S && g.N * g.C * ((g.O[1] + band - 1) / band) < 2048) band = (band / 2 + S - 1) / S * S;
+    const int64_t planes = g.N * g.C * g.O[0];  // output planes
+    while (band >= 8 * S && planes * ((g.O[1] + band - 1) / band) < 2048) band = (band / 2 + S - 1) / S * S;
     a.band = band;
     a.nbands = int((g.O[1] + band - 1) / band);
     a.nrows = rows_for(band);
-    const int64_t units = g.N * g.C * a.nbands;
+    const int64_t units = planes * a.nbands;
     if (units <= 0 || units > (1ll << 31) - 1) return false;
     a.units = int(units);
-    a.stage_elems = int(bytes_for(band) / 2);
-    pl->lds_bytes = size_t(bytes_for(band));
-    pl->nq = int((a.nrows * cpl + kDwThreads - 1) / kDwThreads);
+    a.slot_elems = int(bytes_for(band) / 2);
+    a.stage_elems = T0 * a.slot_elems;
+    pl->lds_bytes = size_t(T0) * size_t(bytes_for(band));
+    pl->nq = int((T0 * a.nrows * cpl + kDwThreads - 1) / kDwThreads);
     pl->S = S;
     pl->T1 = T1;
     pl->T2 = T2;
@@ -488,10 +596,10 @@ int resident_blocks(const void *fn, size_t lds)
     return blocks;
 }
 
-template <int S, int T1, int T2, int OFF2, int NQ>
+template <int S, int T1, int T2, int OFF2, int NQ, int T0>
 void launch_t(const DwPlan &pl, const void *x, const void *w, const void *bias, void *y, hipStream_t st)
 {
-    auto fn = depthwise_kernel<S, T1, T2, OFF2, NQ>;
+    auto fn = depthwise_kernel<S, T1, T2, OFF2, NQ, T0>;
     const int res = resident_blocks(reinterpret_cast<const void *>(fn), pl.lds_bytes);
     const int grid = std::min(pl.a.units, res > 0 ? res : pl.a.units);
     hipLaunchKernelGGL(fn, dim3(unsigned(grid)), dim3(kDwThreads), pl.lds_bytes, st,
@@ -499,21 +607,36 @@ void launch_t(const DwPlan &pl, const void *x, const void *w, const void *bias, 
                        static_cast<const _Float16 *>(bias), static_cast<_Float16 *>(y), pl.a);
 }
 
-template <int S, int T1, int T2, int OFF2>
+template <int S, int T1, int T2, int OFF2, int T0>
 void launch_o(const DwPlan &pl, const void *x, const void *w, const void *bias, void *y, hipStream_t st)
 {
-    if (pl.nq <= 2) launch_t<S, T1, T2, OFF2, 2>(pl, x, w, bias, y, st);
-    else launch_t<S, T1, T2, OFF2, kDwMaxChunks>(pl, x, w, bias, y, st);
+    if (pl.nq <= 2) launch_t<S, T1, T2, OFF2, 2, T0>(pl, x, w, bias, y, st);
+    else launch_t<S, T1, T2, OFF2, kDwMaxChunks, T0>(pl, x, w, bias, y, st);
 }
 
-template <int S, int T>
+template <int S, int T, int T0>
 void launch_s2(const DwPlan &pl, const void *x, const void *w, const void *bias, void *y, hipStream_t st)
 {
     switch (pl.off2) {
-    case 0: launch_o<S, T, T, 0>(pl, x, w, bias, y, st); break;
-    case 1: launch_o<S, T, T, 1>(pl, x, w, bias, y, st); break;
-    case 2: launch_o<S, T, T, 2>(pl, x, w, bias, y, st); break;
-    default: launch_o<S, T, T, 3>(pl, x, w, bias, y, st); break;
+    case 0: launch_o<S, T, T, 0, T0>(pl, x, w, bias, y, st); break;
+    case 1: launch_o<S, T, T, 1, T0>(pl, x, w, bias, y, st); break;
+    case 2: launch_o<S, T, T, 2, T0>(pl, x, w, bias, y, st); break;
+    default: launch_o<S, T, T, 3, T0>(pl, x, w, bias, y, st); break;
+    }
+}
+
+// the compiled instances for T0 first-axis taps (dw_compiled lists them)
+template <int T0>
+void launch_all(const DwPlan &pl, const void *x, const void *w, const void *bias, void *y, hipStream_t st)
+{
+    if (pl.S == 1 && pl.T1 == 3) launch_o<1, 3, 3, 0, T0>(pl, x, w, bias, y, st);
+    else if (pl.S == 2 && pl.T1 == 1) launch_s2<2, 1, T0>(pl, x, w, bias, y, st);
+    else if (pl.S == 2 && pl.T1 == 2) launch_s2<2, 2, T0>(pl, x, w, bias, y, st);
+    else if (pl.S == 2) launch_s2<2, 3, T0>(pl, x, w, bias, y, st);
+    else if constexpr (T0 == 0) {
+        if (pl.S == 1) launch_o<1, 5, 5, 0, 0>(pl, x, w, bias, y, st);
+        else if (pl.off2 == 0) launch_o<4, 2, 2, 0, 0>(pl, x, w, bias, y, st);
+        else launch_o<4, 2, 2, 12, 0>(pl, x, w, bias, y, st);
     }
 }
 
@@ -535,13 +658,10 @@ ct_status launch_depthwise(const Geom &g, ct_dtype dt, bool cl, const void *x, c
     }
     pl.a.act = act;
     mark_before(st);
-    if (pl.S == 1 && pl.T1 == 3) launch_o<1, 3, 3, 0>(pl, x, w, bias, y, st);
-    else if (pl.S == 1) launch_o<1, 5, 5, 0>(pl, x, w, bias, y, st);
-    else if (pl.S == 2 && pl.T1 == 1) launch_s2<2, 1>(pl, x, w, bias, y, st);
-    else if (pl.S == 2 && pl.T1 == 2) launch_s2<2, 2>(pl, x, w, bias, y, st);
-    else if (pl.S == 2) launch_s2<2, 3>(pl, x, w, bias, y, st);
-    else if (pl.off2 == 0) launch_o<4, 2, 2, 0>(pl, x, w, bias, y, st);
-    else launch_o<4, 2, 2, 12>(pl, x, w, bias, y, st);
+    if (pl.T0 == 0) launch_all<0>(pl, x, w, bias, y, st);
+    else if (pl.T0 == 1) launch_all<1>(pl, x, w, bias, y, st);
+    else if (pl.T0 == 2) launch_all<2>(pl, x, w, bias, y, st);
+    else launch_all<3>(pl, x, w, bias, y, st);
     mark_after(st);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) {
