@@ -896,7 +896,8 @@ __global__ __launch_bounds__(kThreads, OCC) void igemm_kernel(const _Float16 *x,
         __syncthreads();
         if constexpr (CL) {
             // 8 channels of one pixel per lane and store; a pixel's channels of the tile are
-            // contiguous in Y
+            // contiguous in Y.  The 16-byte output stores of the epilogue are streaming
+            // stores: Y is written once and read by no block.
             const bool vec = (p.M % 8 == 0) && ((g * p.Mg + mt * BM) % 8 == 0) && (mvalid % 8 == 0) &&
                              (reinterpret_cast<uintptr_t>(y) % 16 == 0);
             _Float16 *const yt = y + size_t(n) * opix * p.M + g * p.Mg + mt * BM;
@@ -906,7 +907,8 @@ __global__ __launch_bounds__(kThreads, OCC) void igemm_kernel(const _Float16 *x,
                     const int pl = u / nc8, c8 = u - pl * nc8;
                     const u32x2 lo = *reinterpret_cast<const u32x2 *>(&stile[pl * CP + c8 * 8]);
                     const u32x2 hi = *reinterpret_cast<const u32x2 *>(&stile[pl * CP + c8 * 8 + 4]);
-                    *reinterpret_cast<u32x4 *>(yt + pixel_offset(pl) * p.M + c8 * 8) = u32x4{lo.x, lo.y, hi.x, hi.y};
+                    __builtin_nontemporal_store(u32x4{lo.x, lo.y, hi.x, hi.y},
+                                                reinterpret_cast<u32x4 *>(yt + pixel_offset(pl) * p.M + c8 * 8));
                 }
             } else {
                 for (int u = tid; u < npix * mvalid; u += kThreads) {
@@ -950,7 +952,7 @@ __global__ __launch_bounds__(kThreads, OCC) void igemm_kernel(const _Float16 *x,
     #pragma unroll
                         for (int k = 0; k < 4; ++k)
                             o[k] = lo_hi(c < 2 ? d0[k].x : d0[k].y, c < 2 ? d1[k].x : d1[k].y, c);
-                        *reinterpret_cast<u32x4 *>(yq + size_t(c) * opix) = o;
+                        __builtin_nontemporal_store(o, reinterpret_cast<u32x4 *>(yq + size_t(c) * opix));
                     }
                 }
             } else {
@@ -969,7 +971,8 @@ __global__ __launch_bounds__(kThreads, OCC) void igemm_kernel(const _Float16 *x,
                 for (int u = tid; u < mvalid * per; u += kThreads) {
                     const int ml = u / per, p8 = u - ml * per;
                     const size_t off = (size_t(n) * p.M + g * p.Mg + mt * BM + ml) * opix + pixel_offset(p8 * 8);
-                    *reinterpret_cast<u32x4 *>(y + off) = *reinterpret_cast<const u32x4 *>(&stile[ml * TP + p8 * 8]);
+                    __builtin_nontemporal_store(*reinterpret_cast<const u32x4 *>(&stile[ml * TP + p8 * 8]),
+                                                reinterpret_cast<u32x4 *>(y + off));
                 }
             } else if (vec) {
                 // A lane takes 4 channels x 8 pixels (four 16-byte stores); a wave covers 8
@@ -992,7 +995,7 @@ __global__ __launch_bounds__(kThreads, OCC) void igemm_kernel(const _Float16 *x,
     #pragma unroll
                         for (int k = 0; k < 4; ++k)
                             o[k] = lo_hi(c < 2 ? d[2 * k].x : d[2 * k].y, c < 2 ? d[2 * k + 1].x : d[2 * k + 1].y, c);
-                        *reinterpret_cast<u32x4 *>(yq + size_t(c) * opix) = o;
+                        __builtin_nontemporal_store(o, reinterpret_cast<u32x4 *>(yq + size_t(c) * opix));
                     }
                 }
             } else {

@@ -355,6 +355,7 @@ __global__ __launch_bounds__(kThreads, 1) void mphase_kernel(const _Float16 *x, 
     const int mvalid = min(64, p.Mg - mt * 64);
     const int o0b = p.s[0] * j0, o1b = p.s[1] * row_lo, o2b = p.s[2] * col_lo;
     const int O0 = p.O[0], O1 = p.O[1], O2 = p.O[2];
+    // (the 16-byte output stores are streaming stores: Y is written once and read by no block)
     if constexpr (CL) {
         // one 16-byte vector of 8 channels per (position, channel octet), octet fastest
         const bool vec = (p.M % 8 == 0) && ((g * p.Mg + mt * 64) % 8 == 0) && (reinterpret_cast<uintptr_t>(y) % 16 == 0);
@@ -368,7 +369,7 @@ __global__ __launch_bounds__(kThreads, 1) void mphase_kernel(const _Float16 *x, 
             _Float16 *dst = yb + ((size_t(o0) * O1 + o1) * O2 + o2) * p.M + c8 * 8;
             const _Float16 *src = &stile[e * 72 + c8 * 8];
             if (vec && c8 * 8 + 8 <= mvalid) {
-                *reinterpret_cast<u32x4 *>(dst) = *reinterpret_cast<const u32x4 *>(src);
+                __builtin_nontemporal_store(*reinterpret_cast<const u32x4 *>(src), reinterpret_cast<u32x4 *>(dst));
             } else {
                 for (int k = 0; k < 8 && c8 * 8 + k < mvalid; ++k) dst[k] = src[k];
             }
@@ -399,9 +400,9 @@ __global__ __launch_bounds__(kThreads, 1) void mphase_kernel(const _Float16 *x, 
                 o[1] = (c0.x >> 16) | (c1.x & 0xffff0000u);
                 o[2] = (c0.y & 0xffffu) | (c1.y << 16);
                 o[3] = (c0.y >> 16) | (c1.y & 0xffff0000u);
-                *reinterpret_cast<u32x4 *>(dst) = o;
+                __builtin_nontemporal_store(o, reinterpret_cast<u32x4 *>(dst));
             } else if (vec) {  // s2 = 1: the row is stored as it is
-                *reinterpret_cast<u32x4 *>(dst) = *reinterpret_cast<const u32x4 *>(row + 8 * c);
+                __builtin_nontemporal_store(*reinterpret_cast<const u32x4 *>(row + 8 * c), reinterpret_cast<u32x4 *>(dst));
             } else {
                 for (int k = 0; k < 8 && o2b + c * 8 + k < O2; ++k) {
                     const int e2 = c * 8 + k;
