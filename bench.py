@@ -418,7 +418,7 @@ def main():
 
 
 # Configurations timed after the headline one in the default run.
-EXTRA_CONFIGS = ("c4_nhwc", "c3", "c3_nhwc", "c5_s1", "c5_s1_p1", "c5_s2")
+EXTRA_CONFIGS = ("c4_nhwc", "c3", "c3_nhwc", "c5_s1", "c5_s1_p1", "c5_s2", "g3_dw")
 
 
 def time_workload(key, steps, warmup, rotate_arg):
