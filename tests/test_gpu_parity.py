@@ -421,6 +421,14 @@ DEPTHWISE_CL = [
     ((1, 16, 9), (3,), dict(strides=[2], pads=[1, 0], output_padding=[1])),
     ((1, 8, 11), (3,), dict(pads=[1, 1])),
     ((1, 16, 4, 8), (4, 4), dict(strides=[2, 2], auto_pad="SAME_LOWER")),
+    # rank 3: the planes of each output plane's first-axis taps (1, 2 or 3), planes
+    # outside the input, dilation and stride 3 on the first axis, 64-channel tiles
+    ((2, 16, 5, 6, 7), (3, 3, 3), dict(strides=[2, 2, 2], pads=[1] * 6, output_padding=[1, 1, 1])),
+    ((1, 8, 4, 5, 6), (3, 3, 3), dict(pads=[1] * 6)),
+    ((1, 24, 3, 4, 5), (2, 2, 2), dict(strides=[2, 2, 2])),
+    ((1, 64, 4, 9, 13), (4, 4, 4), dict(strides=[2, 2, 2], pads=[1] * 6)),
+    ((1, 16, 5, 4, 4), (3, 1, 1), dict(strides=[2, 1, 1], dilations=[2, 1, 1], pads=[2, 0, 0, 0, 0, 0])),
+    ((1, 8, 3, 4, 5), (3, 2, 2), dict(strides=[3, 2, 2], pads=[2, 0, 0, 3, 0, 0])),
 ]
 
 

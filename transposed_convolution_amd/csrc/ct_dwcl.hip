@@ -1,5 +1,5 @@
 // ct_dwcl.hip -- depthwise transposed convolution (one input and one output channel per
-// group, group == C) for channels-last float16 tensors, spatial rank 1 or 2.
+// group, group == C) for channels-last float16 tensors, spatial rank 1 to 3.
 //
 // The grouped form of the operator (webgpu-kernels "ai.onnx.ConvTranspose" README,
 // Attributes: group) with C/group == M/group == 1, on the channels-last layout of the
@@ -18,6 +18,9 @@
 //     sums the class's taps (float16 products, float32 accumulation), adds the bias and
 //     writes the 8 channels of the output with one 16-byte store.  Consecutive threads
 //     hold consecutive octets, so a wave writes whole 128-byte runs of channels.
+//   * Rank 3: a workgroup also owns one output plane o0 = s0*j0 + r0; it stages the tile's
+//     window of every input plane j0 + beta that residue r0's first-axis taps read, one
+//     after another, with the taps' weights, and sums over them too.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -50,6 +53,7 @@ __device__ __forceinline__ float fma_mix_hi(float acc, unsigned x, unsigned w)
 }
 constexpr int kMaxOct = 8;         // channel octets per tile (64 channels: more, lighter blocks)
 constexpr int kMaxS = 2, kMaxT = 4;
+constexpr int kMaxS0 = 4;         // largest stride on the first axis (rank 3)
 constexpr int kWinBatch = 6;      // window loads per thread in flight together
 constexpr int kWBatch = 4;        // weight loads per thread in flight together
 
@@ -62,15 +66,22 @@ struct DwClArgs {
     // (-1: no tap, weight 0)
     int off1[kMaxS][kMaxT], off2[kMaxS][kMaxT];
     int k1[kMaxS][kMaxT], k2[kMaxS][kMaxT];
+    // first axis (rank 3; one plane otherwise): output plane o0 = s0 * j0 + r0 reads input
+    // planes j0 + be00(r0) - u * bs0 with kernel index k00(r0) + u * ks0, u < nt0(r0); the
+    // per-residue values are 16-bit fields r0 of these words
+    int L0, O0, K0, s0, ks0, bs0;
+    unsigned long long nt0w, k00w, be00w;
     Act act;
 };
 
-template <int S1, int S2, int T1, int T2>
+// T0: the most first-axis taps of an output plane (rank 3), 0 for ranks 1 and 2
+template <int S1, int S2, int T1, int T2, int T0>
 __global__ __launch_bounds__(kThreads) void dwcl_kernel(const _Float16 *__restrict__ x, const _Float16 *__restrict__ w,
                                                         const _Float16 *__restrict__ bias, _Float16 *__restrict__ y,
                                                         DwClArgs p)
 {
-    constexpr int NE = S1 * S2 * T1 * T2;  // weight entries per channel held by a thread
+    constexpr int NE = S1 * S2 * T1 * T2;  // weight entries per channel and plane held by a thread
+    constexpr int NT0 = T0 > 0 ? T0 : 1;   // staged input planes
     extern __shared__ __attribute__((aligned(16))) unsigned char dwcl_lds[];
     const int tid = threadIdx.x;
 
@@ -80,21 +91,39 @@ __global__ __launch_bounds__(kThreads) void dwcl_kernel(const _Float16 *__restri
     const int t2 = rest % p.tiles2;
     rest /= p.tiles2;
     const int t1 = rest % p.tiles1;
-    const int n = rest / p.tiles1;
+    rest /= p.tiles1;
+    // the output plane and the input planes of its first-axis taps (bit u of live: tap u
+    // reads a plane inside the input)
+    int n = rest, o0 = 0, k0 = 0, i0 = 0, live = 1;
+    if constexpr (T0 > 0) {
+        o0 = rest % p.O0;
+        n = rest / p.O0;
+        const int j0 = o0 / p.s0, r0 = o0 - j0 * p.s0;
+        auto field = [&](unsigned long long wd) { return int(short((wd >> (16 * r0)) & 0xffffu)); };
+        k0 = field(p.k00w);
+        i0 = j0 + field(p.be00w);
+        const int nt0 = field(p.nt0w);
+        live = 0;
+#pragma unroll
+        for (int v = 0; v < T0; ++v)
+            if (v < nt0 && i0 - v * p.bs0 >= 0 && i0 - v * p.bs0 < p.L0) live |= 1 << v;
+    }
     const int co = p.co;                        // octets of this tile
     const int c_lo = ot * co * 8;               // first channel of the tile
     const int j1lo = t1 * kTJ1, j2lo = t2 * kTJ2;
     const int i1o = j1lo + p.bmin1, i2o = j2lo + p.bmin2;
     const int KK = p.K1 * p.K2;
     const int rowb = co * 16;                   // LDS bytes per window position
-    unsigned char *const sx = dwcl_lds;         // [HR][HC][co octets]
-    _Float16 *const sw = reinterpret_cast<_Float16 *>(dwcl_lds + p.HR * p.HC * rowb);  // [tap][co * 8]
+    const int wsz = p.HR * p.HC * rowb;         // LDS bytes per staged plane
+    unsigned char *const sx = dwcl_lds;         // [plane][HR][HC][co octets]
+    _Float16 *const sw = reinterpret_cast<_Float16 *>(dwcl_lds + NT0 * wsz);  // [plane][tap][co * 8]
 
     // ---- the tile's input window and weights into LDS ----
     {
         const u32x4 zero = {0u, 0u, 0u, 0u};
-        const int items = p.HR * p.HC * co;
-        const UDiv dco(co), dhc(p.HC), dkk(KK);  // index splits by multiply-high
+        const int per = p.HR * p.HC * co;  // items per plane
+        const int items = NT0 * per;
+        const UDiv dco(co), dhc(p.HC), dkk(KK), dper(per), dwp(co * 8 * KK);  // index splits by multiply-high
         // rounds of kWinBatch loads per thread, all in flight before any is written
         for (int base = 0; base < items; base += kThreads * kWinBatch) {
             u32x4 v[kWinBatch];
@@ -102,11 +131,13 @@ __global__ __launch_bounds__(kThreads) void dwcl_kernel(const _Float16 *__restri
 #pragma unroll
             for (int k = 0; k < kWinBatch; ++k) {
                 const int u = base + tid + k * kThreads;
-                const int q = dco.div(u), oc = u - q * co;
+                const int sl = T0 > 0 ? dper.div(u) : 0, uu = u - sl * per;
+                const int q = dco.div(uu), oc = uu - q * co;
                 const int hr = dhc.div(q), hc = q - hr * p.HC;
-                const int i1 = i1o + hr, i2 = i2o + hc;
-                const bool ok = u < items && i1 >= 0 && i1 < p.L1 && i2 >= 0 && i2 < p.L2 && c_lo + oc * 8 < p.C;
-                const size_t off = ok ? ((size_t(n) * p.L1 + i1) * p.L2 + i2) * p.C + c_lo + oc * 8 : 0;
+                const int i1 = i1o + hr, i2 = i2o + hc, ip = i0 - sl * p.bs0;
+                const bool ok = u < items && ((live >> sl) & 1) && i1 >= 0 && i1 < p.L1 && i2 >= 0 && i2 < p.L2 &&
+                                c_lo + oc * 8 < p.C;
+                const size_t off = ok ? (((size_t(n) * p.L0 + ip) * p.L1 + i1) * p.L2 + i2) * p.C + c_lo + oc * 8 : 0;
                 v[k] = *reinterpret_cast<const u32x4 *>(x + off);  // x[0] when masked
                 okm |= unsigned(ok) << k;
             }
@@ -114,29 +145,34 @@ __global__ __launch_bounds__(kThreads) void dwcl_kernel(const _Float16 *__restri
             for (int k = 0; k < kWinBatch; ++k) {
                 const int u = base + tid + k * kThreads;
                 if (u < items) {
-                    const int q = dco.div(u), oc = u - q * co;
-                    *reinterpret_cast<u32x4 *>(sx + q * rowb + oc * 16) = ((okm >> k) & 1u) ? v[k] : zero;
+                    const int sl = T0 > 0 ? dper.div(u) : 0, uu = u - sl * per;
+                    const int q = dco.div(uu), oc = uu - q * co;
+                    *reinterpret_cast<u32x4 *>(sx + sl * wsz + q * rowb + oc * 16) = ((okm >> k) & 1u) ? v[k] : zero;
                 }
             }
         }
-        const int wn = co * 8 * KK;
+        // weights of each staged plane's tap: w[c][k0 + u * ks0][t]
+        const int wpl = co * 8 * KK;  // per plane
+        const int wn = NT0 * wpl;
         for (int base = 0; base < wn; base += kThreads * kWBatch) {
             _Float16 v[kWBatch];
             unsigned okm = 0;
 #pragma unroll
             for (int k = 0; k < kWBatch; ++k) {
                 const int u = base + tid + k * kThreads;
-                const int c = dkk.div(u), t = u - c * KK;
-                const bool ok = u < wn && c_lo + c < p.C;
-                v[k] = w[ok ? size_t(c_lo + c) * KK + t : 0];
+                const int sl = T0 > 0 ? dwp.div(u) : 0, uu = u - sl * wpl;
+                const int c = dkk.div(uu), t = uu - c * KK;
+                const bool ok = u < wn && ((live >> sl) & 1) && c_lo + c < p.C;
+                v[k] = w[ok ? (size_t(c_lo + c) * p.K0 + k0 + sl * p.ks0) * KK + t : 0];
                 okm |= unsigned(ok) << k;
             }
 #pragma unroll
             for (int k = 0; k < kWBatch; ++k) {
                 const int u = base + tid + k * kThreads;
                 if (u < wn) {
-                    const int c = dkk.div(u), t = u - c * KK;
-                    sw[t * (co * 8) + c] = ((okm >> k) & 1u) ? v[k] : _Float16(0.0f);
+                    const int sl = T0 > 0 ? dwp.div(u) : 0, uu = u - sl * wpl;
+                    const int c = dkk.div(uu), t = uu - c * KK;
+                    sw[sl * wpl + t * (co * 8) + c] = ((okm >> k) & 1u) ? v[k] : _Float16(0.0f);
                 }
             }
         }
@@ -145,21 +181,24 @@ __global__ __launch_bounds__(kThreads) void dwcl_kernel(const _Float16 *__restri
 
     const int oc = tid % co, slot = tid / co, nslots = kThreads / co;
     if (slot >= nslots) return;  // threads past the last whole slot (co does not divide 256)
-    // the thread's weights: entry e = ((r1 * S2 + r2) * T1 + a) * T2 + cc
-    u32x4 wv[NE];
+    // the thread's weights: entry e = ((r1 * S2 + r2) * T1 + a) * T2 + cc of each plane
+    u32x4 wv[NT0][NE];
 #pragma unroll
-    for (int r1 = 0; r1 < S1; ++r1)
+    for (int v0 = 0; v0 < NT0; ++v0)
 #pragma unroll
-        for (int r2 = 0; r2 < S2; ++r2)
+        for (int r1 = 0; r1 < S1; ++r1)
 #pragma unroll
-            for (int a = 0; a < T1; ++a)
+            for (int r2 = 0; r2 < S2; ++r2)
 #pragma unroll
-                for (int cc = 0; cc < T2; ++cc) {
-                    const int e = ((r1 * S2 + r2) * T1 + a) * T2 + cc;
-                    const int k1 = p.k1[r1][a], k2 = p.k2[r2][cc];
-                    const u32x4 v = *reinterpret_cast<const u32x4 *>(&sw[(k1 >= 0 && k2 >= 0 ? k1 * p.K2 + k2 : 0) * (co * 8) + oc * 8]);
-                    wv[e] = (k1 >= 0 && k2 >= 0) ? v : u32x4{0u, 0u, 0u, 0u};
-                }
+                for (int a = 0; a < T1; ++a)
+#pragma unroll
+                    for (int cc = 0; cc < T2; ++cc) {
+                        const int e = ((r1 * S2 + r2) * T1 + a) * T2 + cc;
+                        const int k1 = p.k1[r1][a], k2 = p.k2[r2][cc];
+                        const u32x4 v = *reinterpret_cast<const u32x4 *>(
+                            &sw[v0 * co * 8 * KK + (k1 >= 0 && k2 >= 0 ? k1 * p.K2 + k2 : 0) * (co * 8) + oc * 8]);
+                        wv[v0][e] = (k1 >= 0 && k2 >= 0) ? v : u32x4{0u, 0u, 0u, 0u};
+                    }
     float bv[8];
     {
         const int c = c_lo + oc * 8;
@@ -186,19 +225,24 @@ __global__ __launch_bounds__(kThreads) void dwcl_kernel(const _Float16 *__restri
 #pragma unroll
                     for (int k = 0; k < 8; ++k) acc[k] = bv[k];
 #pragma unroll
-                    for (int a = 0; a < T1; ++a)
+                    for (int v0 = 0; v0 < NT0; ++v0) {
+                        if (T0 > 0 && !((live >> v0) & 1)) continue;  // uniform over the block
 #pragma unroll
-                        for (int cc = 0; cc < T2; ++cc) {
-                            const int e = ((r1 * S2 + r2) * T1 + a) * T2 + cc;
-                            const int wr = pj1 + p.off1[r1][a], wc = pj2 + p.off2[r2][cc];
-                            const u32x4 xv = *reinterpret_cast<const u32x4 *>(sx + (wr * p.HC + wc) * rowb + oc * 16);
+                        for (int a = 0; a < T1; ++a)
 #pragma unroll
-                            for (int k = 0; k < 4; ++k) {  // channels 2k (low halves), 2k + 1 (high)
-                                acc[2 * k] = fma_mix_lo(acc[2 * k], xv[k], wv[e][k]);
-                                acc[2 * k + 1] = fma_mix_hi(acc[2 * k + 1], xv[k], wv[e][k]);
+                            for (int cc = 0; cc < T2; ++cc) {
+                                const int e = ((r1 * S2 + r2) * T1 + a) * T2 + cc;
+                                const int wr = pj1 + p.off1[r1][a], wc = pj2 + p.off2[r2][cc];
+                                const u32x4 xv =
+                                    *reinterpret_cast<const u32x4 *>(sx + v0 * wsz + (wr * p.HC + wc) * rowb + oc * 16);
+#pragma unroll
+                                for (int k = 0; k < 4; ++k) {  // channels 2k (low halves), 2k + 1 (high)
+                                    acc[2 * k] = fma_mix_lo(acc[2 * k], xv[k], wv[v0][e][k]);
+                                    acc[2 * k + 1] = fma_mix_hi(acc[2 * k + 1], xv[k], wv[v0][e][k]);
+                                }
                             }
-                        }
-                    _Float16 *dst = y + ((size_t(n) * p.O1 + o1) * p.O2 + o2) * p.C + c_lo + oc * 8;
+                    }
+                    _Float16 *dst = y + (((size_t(n) * p.O0 + o0) * p.O1 + o1) * p.O2 + o2) * p.C + c_lo + oc * 8;
                     if (vec) {
                         f16x8 o;
 #pragma unroll
@@ -224,14 +268,38 @@ __global__ __launch_bounds__(kThreads) void dwcl_kernel(const _Float16 *__restri
 struct DwClPlan {
     DwClArgs a;
     int S1, S2, T1, T2;
+    int T0;  // kernel's T0: the most first-axis taps of a residue (rank 3), else 0
     size_t lds;
 };
 
 bool make_dwcl_plan(const Geom &g, DwClPlan *pl)
 {
-    if (g.nsp > 2 || g.L[0] != 1 || g.K[0] != 1 || g.O[0] != 1) return false;
     DwClArgs &a = pl->a;
     std::memset(&a, 0, sizeof(a));
+    // first axis (one plane below rank 3): per residue its taps as a progression
+    if (g.s[0] > kMaxS0) return false;
+    const int64_t gs0 = std::__gcd(g.s[0], g.d[0]);
+    a.ks0 = int(g.s[0] / gs0);
+    a.bs0 = int(g.d[0] / gs0);
+    int T0 = 0;
+    for (int r = 0; r < g.s[0]; ++r) {
+        AxisPhase ph;
+        if (!axis_phase(g, 0, r, &ph)) return false;
+        for (int u = 1; u < ph.ntaps; ++u)
+            if (ph.k[u] - ph.k[u - 1] != a.ks0 || ph.beta[u - 1] - ph.beta[u] != a.bs0) return false;
+        const int k0 = ph.ntaps ? ph.k[0] : 0, be0 = ph.ntaps ? ph.beta[0] : 0;
+        if (k0 > 32767 || be0 < -32768 || be0 > 32767) return false;
+        a.nt0w |= (unsigned long long)(ph.ntaps & 0xffff) << (16 * r);
+        a.k00w |= (unsigned long long)(k0 & 0xffff) << (16 * r);
+        a.be00w |= (unsigned long long)(unsigned(be0) & 0xffffu) << (16 * r);
+        T0 = std::max(T0, ph.ntaps);
+    }
+    if (T0 == 0 || T0 > 3) return false;  // no tap reaches an output plane, or too many planes
+    pl->T0 = g.nsp == 3 ? T0 : 0;
+    a.L0 = int(g.L[0]);
+    a.O0 = int(g.O[0]);
+    a.K0 = int(g.K[0]);
+    a.s0 = int(g.s[0]);
     a.N = int(g.N);
     a.C = int(g.C);
     a.L1 = int(g.L[1]);
@@ -302,29 +370,43 @@ bool make_dwcl_plan(const Geom &g, DwClPlan *pl)
     const int oct = int((g.C + 7) / 8);
     a.co = std::min(oct, kMaxOct);
     a.otiles = (oct + a.co - 1) / a.co;
-    const long long blocks = (long long)g.N * a.tiles1 * a.tiles2 * a.otiles;
+    const long long blocks = (long long)g.N * g.O[0] * a.tiles1 * a.tiles2 * a.otiles;
     if (blocks < 1 || blocks > INT32_MAX) return false;
     a.nblocks = int(blocks);
-    pl->lds = size_t(a.HR) * a.HC * a.co * 16 + size_t(a.co) * 8 * a.K1 * a.K2 * 2;
+    const int nt0 = std::max(pl->T0, 1);  // staged planes
+    pl->lds = nt0 * (size_t(a.HR) * a.HC * a.co * 16 + size_t(a.co) * 8 * a.K1 * a.K2 * 2);
     if (pl->lds > 64 * 1024) return false;
     return true;
 }
 
-template <int S1, int S2, int T1, int T2>
+template <int S1, int S2, int T1, int T2, int T0>
 bool launch_if(const DwClPlan &pl, const void *x, const void *w, const void *b, void *y, hipStream_t st)
 {
-    if (pl.S1 != S1 || pl.S2 != S2 || pl.T1 != T1 || pl.T2 != T2) return false;
-    hipLaunchKernelGGL((dwcl_kernel<S1, S2, T1, T2>), dim3(unsigned(pl.a.nblocks)), dim3(kThreads), pl.lds, st,
+    if (pl.S1 != S1 || pl.S2 != S2 || pl.T1 != T1 || pl.T2 != T2 || pl.T0 != T0) return false;
+    hipLaunchKernelGGL((dwcl_kernel<S1, S2, T1, T2, T0>), dim3(unsigned(pl.a.nblocks)), dim3(kThreads), pl.lds, st,
                        static_cast<const _Float16 *>(x), static_cast<const _Float16 *>(w),
                        static_cast<const _Float16 *>(b), static_cast<_Float16 *>(y), pl.a);
     return true;
 }
 
+// equal strides on the last two axes: ranks 2 and 3
+template <int T0>
+bool launch_square(const DwClPlan &pl, const void *x, const void *w, const void *b, void *y, hipStream_t st)
+{
+    return launch_if<2, 2, 1, 1, T0>(pl, x, w, b, y, st) || launch_if<2, 2, 2, 2, T0>(pl, x, w, b, y, st) ||
+           launch_if<1, 1, 1, 1, T0>(pl, x, w, b, y, st) || launch_if<1, 1, 2, 2, T0>(pl, x, w, b, y, st) ||
+           launch_if<1, 1, 3, 3, T0>(pl, x, w, b, y, st);
+}
+
 bool has_instance(const DwClPlan &pl)
 {
-    static const int inst[][4] = {{2, 2, 1, 1}, {2, 2, 2, 2}, {1, 1, 1, 1}, {1, 1, 2, 2}, {1, 1, 3, 3},
-                                  {1, 2, 1, 1}, {1, 2, 1, 2}, {1, 2, 1, 4}, {1, 1, 1, 2}, {1, 1, 1, 3}, {1, 1, 1, 4}};
-    for (const auto &i : inst)
+    // (S1, S2, T1, T2): ranks 2 and 3, then rank 1 (T0 = 0 only)
+    static const int square[][4] = {{2, 2, 1, 1}, {2, 2, 2, 2}, {1, 1, 1, 1}, {1, 1, 2, 2}, {1, 1, 3, 3}};
+    static const int rank1[][4] = {{1, 2, 1, 1}, {1, 2, 1, 2}, {1, 2, 1, 4}, {1, 1, 1, 2}, {1, 1, 1, 3}, {1, 1, 1, 4}};
+    for (const auto &i : square)
+        if (pl.S1 == i[0] && pl.S2 == i[1] && pl.T1 == i[2] && pl.T2 == i[3]) return pl.T0 >= 0 && pl.T0 <= 3;
+    if (pl.T0 != 0) return false;
+    for (const auto &i : rank1)
         if (pl.S1 == i[0] && pl.S2 == i[1] && pl.T1 == i[2] && pl.T2 == i[3]) return true;
     return false;
 }
@@ -350,12 +432,11 @@ ct_status launch_dwcl(const Geom &g, const void *x, const void *w, const void *b
     pl.a.act = act;
     mark_before(st);
     const bool launched =
-        launch_if<2, 2, 1, 1>(pl, x, w, bias, y, st) || launch_if<2, 2, 2, 2>(pl, x, w, bias, y, st) ||
-        launch_if<1, 1, 1, 1>(pl, x, w, bias, y, st) || launch_if<1, 1, 2, 2>(pl, x, w, bias, y, st) ||
-        launch_if<1, 1, 3, 3>(pl, x, w, bias, y, st) || launch_if<1, 2, 1, 1>(pl, x, w, bias, y, st) ||
-        launch_if<1, 2, 1, 2>(pl, x, w, bias, y, st) || launch_if<1, 2, 1, 4>(pl, x, w, bias, y, st) ||
-        launch_if<1, 1, 1, 2>(pl, x, w, bias, y, st) || launch_if<1, 1, 1, 3>(pl, x, w, bias, y, st) ||
-        launch_if<1, 1, 1, 4>(pl, x, w, bias, y, st);
+        launch_square<0>(pl, x, w, bias, y, st) || launch_if<1, 2, 1, 1, 0>(pl, x, w, bias, y, st) ||
+        launch_if<1, 2, 1, 2, 0>(pl, x, w, bias, y, st) || launch_if<1, 2, 1, 4, 0>(pl, x, w, bias, y, st) ||
+        launch_if<1, 1, 1, 2, 0>(pl, x, w, bias, y, st) || launch_if<1, 1, 1, 3, 0>(pl, x, w, bias, y, st) ||
+        launch_if<1, 1, 1, 4, 0>(pl, x, w, bias, y, st) || launch_square<1>(pl, x, w, bias, y, st) ||
+        launch_square<2>(pl, x, w, bias, y, st) || launch_square<3>(pl, x, w, bias, y, st);
     mark_after(st);
     const hipError_t e = launched ? hipGetLastError() : hipErrorInvalidConfiguration;
     if (e != hipSuccess) {
