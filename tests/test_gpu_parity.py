@@ -547,6 +547,8 @@ ALLPHASE = [
     ((1, 32, 4, 6, 8), (32, 80, 2, 2, 2), dict(strides=[2, 2, 2])),
     ((1, 32, 6, 8), (32, 40, 3, 3), dict(strides=[2, 2], dilations=[2, 2], pads=[1, 1, 1, 1])),
     ((2, 32, 3, 24), (32, 8, 5, 3), dict(strides=[2, 2], pads=[2, 1, 2, 1], output_padding=[1, 1])),
+    # a window too wide for the two-row box (192 channels): the four-row box
+    ((1, 192, 3, 5, 8), (192, 16, 3, 3, 3), dict(strides=[2, 2, 2], pads=[1] * 6)),
 ]
 
 

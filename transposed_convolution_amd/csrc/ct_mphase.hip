@@ -6,7 +6,7 @@
 // The outputs split by residue r modulo the stride on every axis; residue class r of
 // outputs o = r + s*j receives the taps k with (r + b - k*d) divisible by s, from the
 // inputs i = j + beta_k.  Here one workgroup computes, for a box of phase-grid positions
-// j (one plane, 4 rows, 32 columns) and 64 output channels, EVERY residue class at once:
+// j (one plane, 2 or 4 rows, 32 columns) and 64 output channels, EVERY residue class at once:
 // its outputs are the whole box o in [s*j_lo, s*(j_lo + extent)) of Y, and every class
 // reads the same input window, so the window is loaded once for all classes.
 //
@@ -14,8 +14,8 @@
 //     loaded once into LDS ([plane][row][column][channel], a 16-byte pad per position),
 //     then each wave runs without barriers.
 //   * Each of the 4 waves owns up to two residue classes (the host pairs heavy and light
-//     classes so the waves' tap counts are close) over the box's 128 positions and 64
-//     output channels: 2 x 2 x 4 MFMA 32x32 tiles, float32 accumulators.
+//     classes so the waves' tap counts are close) over the box's 64 or 128 positions and
+//     64 output channels: 2 x 2 x (2 or 4) MFMA 32x32 tiles, float32 accumulators.
 //   * A step is one tap x 32 input channels: the wave reads its weight fragments straight
 //     from the fragment-major packing into registers (a ring of RING steps in flight)
 //     and the input fragments of the tap's shifted window from LDS:
@@ -40,14 +40,16 @@ typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kThreads = 256;
-constexpr int kTR = 4;              // phase-grid rows per box (one 32-position tile per row)
 constexpr int kTC = 32;             // phase-grid columns per box
 constexpr int kSlots = 2;           // residue classes per wave
 constexpr int kMaxClass = 8;        // 4 waves x 2 slots
 constexpr int kRing = 4;            // steps of weight fragments in flight per wave
-constexpr int kLds = 160 * 1024 - 2048;
 constexpr int kBiasBytes = 64 * 4;  // the block's 64 bias values (float32) at the end of LDS
-constexpr int kStage = kLds - kBiasBytes;
+// Boxes of TR phase-grid rows (one 32-position tile per row): 2 rows in 78 KB of LDS, two
+// blocks per CU, so one block's window loads and stores overlap the other's MFMAs; or 4
+// rows in 158 KB, one block per CU, for windows that need the room.
+constexpr int lds_bytes(int tr) { return tr == 2 ? 80 * 1024 - 2048 : 160 * 1024 - 2048; }
+constexpr int stage_bytes(int tr) { return lds_bytes(tr) - kBiasBytes; }
 constexpr int kHaloVec = 32;        // 16-byte halo loads per thread and round
 
 struct MpArgs {
@@ -61,18 +63,19 @@ struct MpArgs {
     int kstep[3], bstep[3];
     int ntap[3][8], tk0[3][8], tb0[3][8];
     int wave_cls[4][kSlots];         // residue class r0 | r1 << 8 | r2 << 16, or -1
+    int tr;                          // phase-grid rows per box (2 or 4)
     Act act;
 };
 
 __device__ __forceinline__ int floor_div8(int v) { return v >= 0 ? v / 8 : -((-v + 7) / 8); }
 
-template <bool CL>
-__global__ __launch_bounds__(kThreads, 1) void mphase_kernel(const _Float16 *x, const _Float16 *__restrict__ wf,
-                                                             const _Float16 *__restrict__ bias,
-                                                             _Float16 *__restrict__ y, MpArgs p)
+template <bool CL, int TR>
+__global__ __launch_bounds__(kThreads, TR == 2 ? 2 : 1) void mphase_kernel(const _Float16 *x, const _Float16 *__restrict__ wf,
+                                                                           const _Float16 *__restrict__ bias,
+                                                                           _Float16 *__restrict__ y, MpArgs p)
 {
-    __shared__ __attribute__((aligned(16))) unsigned char lds[kLds];
-    float *const sbias = reinterpret_cast<float *>(lds + kStage);
+    __shared__ __attribute__((aligned(16))) unsigned char lds[lds_bytes(TR)];
+    float *const sbias = reinterpret_cast<float *>(lds + stage_bytes(TR));
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -89,7 +92,7 @@ __global__ __launch_bounds__(kThreads, 1) void mphase_kernel(const _Float16 *x, 
     rest /= p.mtiles;
     const int g = rest % p.G;
     const int n = rest / p.G;
-    const int row_lo = rt * kTR, col_lo = ct * kTC;
+    const int row_lo = rt * TR, col_lo = ct * kTC;
     const int i0o = j0 + p.bmin[0], i1o = row_lo + p.bmin[1], i2o = col_lo + p.bmin[2];
     const int L0 = p.L[0], L1 = p.L[1], L2 = p.L[2];
 
@@ -195,20 +198,20 @@ __global__ __launch_bounds__(kThreads, 1) void mphase_kernel(const _Float16 *x, 
     __syncthreads();
 
     // ---------------- the wave's residue classes ----------------
-    f32x16 acc[kSlots][2][kTR];
+    f32x16 acc[kSlots][2][TR];
 #pragma unroll
     for (int sl = 0; sl < kSlots; ++sl)
 #pragma unroll
         for (int i = 0; i < 2; ++i)
 #pragma unroll
-            for (int jt = 0; jt < kTR; ++jt)
+            for (int jt = 0; jt < TR; ++jt)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) acc[sl][i][jt][r] = 0.0f;
 
     // lane's position in the window for tile jt (row jt) before the tap shift
-    int hoff[kTR];
+    int hoff[TR];
 #pragma unroll
-    for (int jt = 0; jt < kTR; ++jt) hoff[jt] = (jt * p.HC + (lane & 31)) * p.pitch + (lane >> 5) * 16;
+    for (int jt = 0; jt < TR; ++jt) hoff[jt] = (jt * p.HC + (lane & 31)) * p.pitch + (lane >> 5) * 16;
     const int KB = p.Cgp / 16, MB = p.Mgp / 32, CB = p.Cg / 32;
     const f16x8 *const wfrag = reinterpret_cast<const f16x8 *>(wf);
 
@@ -248,11 +251,11 @@ __global__ __launch_bounds__(kThreads, 1) void mphase_kernel(const _Float16 *x, 
                 for (int h = 0; h < 2; ++h) dst[i][h] = src[(size_t(i) * KB + h) * 64];
         };
         // the step's input fragments: tile jt's 32 positions, shifted by the step's tap
-        auto load_b = [&](const Step &q, f16x8 (&b)[kTR][2]) {
+        auto load_b = [&](const Step &q, f16x8 (&b)[TR][2]) {
             const int sh = ((b00 - q.t0 * p.bstep[0]) * p.HR + (b01 - q.t1 * p.bstep[1])) * p.HC + (b02 - q.t2 * p.bstep[2]);
             const unsigned char *hb = lds + sh * p.pitch + q.cb * 64;
 #pragma unroll
-            for (int jt = 0; jt < kTR; ++jt)
+            for (int jt = 0; jt < TR; ++jt)
 #pragma unroll
                 for (int h = 0; h < 2; ++h) b[jt][h] = *reinterpret_cast<const f16x8 *>(hb + hoff[jt] + h * 32);
         };
@@ -260,18 +263,18 @@ __global__ __launch_bounds__(kThreads, 1) void mphase_kernel(const _Float16 *x, 
         // channels of one position; channels-first: the transposed tile (positions x
         // channels), so a lane holds 4 consecutive positions of one channel (the operand
         // fragments have the same register layout in either role)
-        auto mma = [&](const f16x8 (&a)[2][2], const f16x8 (&b)[kTR][2]) {
+        auto mma = [&](const f16x8 (&a)[2][2], const f16x8 (&b)[TR][2]) {
 #pragma unroll
             for (int h = 0; h < 2; ++h)
 #pragma unroll
                 for (int i = 0; i < 2; ++i)
 #pragma unroll
-                    for (int jt = 0; jt < kTR; ++jt)
+                    for (int jt = 0; jt < TR; ++jt)
                         acc[sl][i][jt] = CL ? __builtin_amdgcn_mfma_f32_32x32x16_f16(a[i][h], b[jt][h], acc[sl][i][jt], 0, 0, 0)
                                             : __builtin_amdgcn_mfma_f32_32x32x16_f16(b[jt][h], a[i][h], acc[sl][i][jt], 0, 0, 0);
         };
         f16x8 ring[kRing][2][2];
-        f16x8 bf[2][kTR][2];  // input fragments of the step (two buffers alternating)
+        f16x8 bf[2][TR][2];  // input fragments of the step (two buffers alternating)
         Step cur = {0, 0, 0, 0};
         Step pf = cur;
 #pragma unroll
@@ -321,7 +324,7 @@ __global__ __launch_bounds__(kThreads, 1) void mphase_kernel(const _Float16 *x, 
 #pragma unroll
             for (int i = 0; i < 2; ++i)
 #pragma unroll
-                for (int jt = 0; jt < kTR; ++jt) {
+                for (int jt = 0; jt < TR; ++jt) {
                     const int e1 = p.s[1] * jt + r1;
                     if constexpr (CL) {
                         // [position][channel], pitch 72: lane = position, 4 channels per write
@@ -424,7 +427,7 @@ bool make_mp_plan(const Geom &g, bool cl, MpArgs *a, std::string *why)
     if (g.Cg % 32 != 0) return no("all-phase kernel: C/group must be a multiple of 32");
     if (!cl && g.L[2] % 8 != 0) return no("all-phase kernel: innermost input size must be a multiple of 8");
     if (cl && g.C % 8 != 0) return no("all-phase kernel: C must be a multiple of 8");
-    int nclass = 0;
+    int nclass = 0, span1 = 0;
     int cls_r[kMaxClass][3], cls_taps[kMaxClass];
     for (int t = 0; t < kAxes; ++t) {
         if (g.s[t] > 8) return no("all-phase kernel: stride above 8");
@@ -454,7 +457,7 @@ bool make_mp_plan(const Geom &g, bool cl, MpArgs *a, std::string *why)
         a->bmin[t] = bmin;
         const int span = bmax - bmin;
         if (t == 0) a->HP = 1 + span;
-        if (t == 1) a->HR = kTR + span;
+        if (t == 1) span1 = span;
         if (t == 2) a->HC = kTC + span;
     }
     // residue classes that have outputs
@@ -496,22 +499,29 @@ bool make_mp_plan(const Geom &g, bool cl, MpArgs *a, std::string *why)
     a->mtiles = int((g.Mg + 63) / 64);
     a->Mgp = a->mtiles * 64;
     a->pitch = a->Cg * 2 + 16;
-    a->rtiles = (a->J[1] + kTR - 1) / kTR;
     a->ctiles = (a->J[2] + kTC - 1) / kTC;
     for (int t = 0; t < kAxes; ++t)
         if (g.s[t] & (g.s[t] - 1)) return no("all-phase kernel: strides must be powers of two");
     a->E[0] = a->s[0];
-    a->E[1] = a->s[1] * kTR;
     a->E[2] = a->s[2] * kTC;
-    for (int t = 0; t < kAxes; ++t) a->lgE[t] = __builtin_ctz(unsigned(a->E[t]));
-    a->cpitch = a->E[0] * a->E[1] * a->E[2] + 8;
-    if ((long long)a->HP * a->HR * a->HC * a->pitch > kStage) return no("all-phase kernel: input window exceeds LDS");
-    const long long box = (long long)a->E[0] * a->E[1] * a->E[2];
-    if ((cl ? box * 72 : (long long)a->cpitch * 64) * 2 > kStage) return no("all-phase kernel: output box exceeds LDS");
-    const long long blocks = (long long)g.N * g.G * a->mtiles * a->J[0] * a->rtiles * a->ctiles;
-    if (blocks > INT32_MAX || blocks < 1) return no("all-phase kernel: too many blocks");
-    a->nblocks = int(blocks);
-    return true;
+    // the smaller box when its window and output box fit, else the larger one
+    for (const int tr : {2, 4}) {
+        a->tr = tr;
+        a->HR = tr + span1;
+        a->rtiles = (a->J[1] + tr - 1) / tr;
+        a->E[1] = a->s[1] * tr;
+        for (int t = 0; t < kAxes; ++t) a->lgE[t] = __builtin_ctz(unsigned(a->E[t]));
+        a->cpitch = a->E[0] * a->E[1] * a->E[2] + 8;
+        const long long box = (long long)a->E[0] * a->E[1] * a->E[2];
+        if ((long long)a->HP * a->HR * a->HC * a->pitch > stage_bytes(tr) ||
+            (cl ? box * 72 : (long long)a->cpitch * 64) * 2 > stage_bytes(tr))
+            continue;
+        const long long blocks = (long long)g.N * g.G * a->mtiles * a->J[0] * a->rtiles * a->ctiles;
+        if (blocks > INT32_MAX || blocks < 1) return no("all-phase kernel: too many blocks");
+        a->nblocks = int(blocks);
+        return true;
+    }
+    return no("all-phase kernel: input window or output box exceeds LDS");
 }
 
 }  // namespace
@@ -548,14 +558,18 @@ ct_status launch_mphase(const Geom &g, bool cl, const void *x, const void *w, co
     ct_status s = launch_pack_w_frag(g, w, wsp, a.Cgp, a.Mgp, w_conv, st, err);
     if (s != CT_OK) return s;
     mark_before(st);
-    if (cl)
-        hipLaunchKernelGGL(mphase_kernel<true>, dim3(unsigned(a.nblocks)), dim3(kThreads), 0, st,
-                           static_cast<const _Float16 *>(x), static_cast<const _Float16 *>(wsp),
-                           static_cast<const _Float16 *>(bias), static_cast<_Float16 *>(y), a);
-    else
-        hipLaunchKernelGGL(mphase_kernel<false>, dim3(unsigned(a.nblocks)), dim3(kThreads), 0, st,
-                           static_cast<const _Float16 *>(x), static_cast<const _Float16 *>(wsp),
-                           static_cast<const _Float16 *>(bias), static_cast<_Float16 *>(y), a);
+    auto run = [&](auto kernel) {
+        hipLaunchKernelGGL(kernel, dim3(unsigned(a.nblocks)), dim3(kThreads), 0, st, static_cast<const _Float16 *>(x),
+                           static_cast<const _Float16 *>(wsp), static_cast<const _Float16 *>(bias),
+                           static_cast<_Float16 *>(y), a);
+    };
+    if (cl) {
+        if (a.tr == 2) run(mphase_kernel<true, 2>);
+        else run(mphase_kernel<true, 4>);
+    } else {
+        if (a.tr == 2) run(mphase_kernel<false, 2>);
+        else run(mphase_kernel<false, 4>);
+    }
     mark_after(st);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) {
