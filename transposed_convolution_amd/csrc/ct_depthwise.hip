@@ -37,6 +37,7 @@ constexpr int kDwMaxChunks = 8;                              // 16-byte input ch
 constexpr int kDwStageBytes = kDwMaxChunks * kDwThreads * 16;  // staged band (float16), upper bound
 constexpr int kDwGuard = 8;                                    // zero elements ahead of staged row 0
 constexpr int kDwMaxS0 = 4;                                    // largest stride on the first axis (rank 3)
+constexpr int kDwMaxPlanes = 3;                                // staged input planes per unit (rank 3)
 
 struct DwArgs {
     int C, L1, L2, O1, O2, K1, K2, b1, b2, d1, d2;
@@ -51,15 +52,18 @@ struct DwArgs {
     // first axis (rank 3; a single plane otherwise): output plane o0 = s0 * j0 + r0 reads
     // input planes i0 = j0 + be00(r0) - u * bs0 with kernel index k00(r0) + u * ks0 for
     // u < nt0(r0); the per-residue values are 16-bit fields r0 of these words (a table
-    // indexed at run time would be read from memory inside the unit loop)
+    // indexed at run time would be read from memory inside the unit loop).  A unit takes
+    // every residue of one j0: it stages the npl input planes j0 + bmin0 ... (the union
+    // of its residues' taps) and writes the s0 output planes s0 * j0 + r0.
     int L0, O0, K0, s0, ks0, bs0;
     unsigned long long nt0w, k00w, be00w;
+    int J0, bmin0, npl;
     int slot_elems;  // halves per staged plane (the planes are staged one after another)
     Act act;         // output activation
 };
 
-// T0: staged input planes per unit (rank 3: the most first-axis taps of an output plane);
-// 0 for ranks 1 and 2, whose units read one plane and skip the first-axis bookkeeping.
+// T0: the most first-axis taps of an output plane (rank 3); 0 for ranks 1 and 2, whose
+// units read one plane and skip the first-axis bookkeeping.
 template <int S, int T1, int T2, int OFF2, int NQ, int T0>
 __global__ __launch_bounds__(kDwThreads) void depthwise_kernel(const _Float16 *__restrict__ x,
                                                                const _Float16 *__restrict__ w,
@@ -69,7 +73,9 @@ __global__ __launch_bounds__(kDwThreads) void depthwise_kernel(const _Float16 *_
     constexpr int OC = 8;               // output columns per thread
     constexpr int JC = OC / S;          // input-grid columns they span
     constexpr int NE = S * S * T1 * T2;  // sub-kernel entries over all phases
-    constexpr int NT0 = T0 > 0 ? T0 : 1;  // staged planes
+    constexpr int NT0 = T0 > 0 ? T0 : 1;            // first-axis taps of a residue
+    constexpr int NPL = T0 > 0 ? kDwMaxPlanes : 1;  // staged planes (at most)
+    constexpr int NRS = T0 > 0 ? kDwMaxS0 : 1;      // first-axis residues (at most)
     // column offset of residue r's window (0 or 1), fixed at compile time so every
     // register index below is a constant; row offsets are LDS addresses and stay runtime
     constexpr int MAXO2 = (OFF2 != 0) ? 1 : 0;
@@ -86,7 +92,7 @@ __global__ __launch_bounds__(kDwThreads) void depthwise_kernel(const _Float16 *_
     // on an 8-byte boundary (LDS reads that are not naturally aligned stall).
     extern __shared__ __attribute__((aligned(16))) unsigned char dw_lds[];
     _Float16 *const sx = reinterpret_cast<_Float16 *>(dw_lds);
-    __shared__ _Float16 seff[NT0 * NE];  // sub-kernels of the unit's first-axis taps
+    __shared__ _Float16 seff[NRS * NT0 * NE];  // sub-kernels of the unit's first-axis residues and taps
 
     const int R = p.row_w, cpl = p.L2 / 8;
     const int segs = (p.O2 + OC - 1) / OC;
@@ -113,32 +119,28 @@ __global__ __launch_bounds__(kDwThreads) void depthwise_kernel(const _Float16 *_
     // stores cover whole lines and go out as streaming stores (Y is read by no block)
     const bool stream = p.O2 % OC == 0 && reinterpret_cast<uintptr_t>(y) % 16 == 0;
 
+    // 16-bit field r of a per-residue word
+    auto field = [](unsigned long long wd, int r) { return int(short((wd >> (16 * r)) & 0xffffu)); };
     struct Unit {
         int c, pc, ch, oh0, oh1, j1lo, j1hi, ilo, vr0, nvr;
-        int k0, i0, live;  // first-axis tap 0's kernel index and input plane; bit u: tap u reads a plane
+        int j0, i0, live;  // rank 3: phase-grid plane, input plane of slot 0; bit v: slot v is inside X
     };
     auto unit_of = [&](int t) {
         Unit u;
         const int band = t % p.nbands;
-        u.c = t / p.nbands;  // output plane (image, channel, o0)
+        u.c = t / p.nbands;  // ranks 1-2: the plane; rank 3: (image, channel, j0)
         if constexpr (T0 == 0) {
             u.pc = u.c;
-            u.k0 = u.i0 = 0;
+            u.j0 = u.i0 = 0;
             u.live = 1;
         } else {
-            u.pc = u.c / p.O0;  // image and channel
-            const int o0 = u.c - u.pc * p.O0;
-            const int j0 = o0 / p.s0, r0 = o0 - j0 * p.s0;
-            auto field = [&](unsigned long long wd) { return int(short((wd >> (16 * r0)) & 0xffffu)); };
-            u.k0 = field(p.k00w);
-            u.i0 = j0 + field(p.be00w);
-            const int nt0 = field(p.nt0w);
+            u.pc = u.c / p.J0;  // image and channel
+            u.j0 = u.c - u.pc * p.J0;
+            u.i0 = u.j0 + p.bmin0;
             u.live = 0;
 #pragma unroll
-            for (int v = 0; v < T0; ++v) {
-                const int i0 = u.i0 - v * p.bs0;
-                if (v < nt0 && i0 >= 0 && i0 < p.L0) u.live |= 1 << v;
-            }
+            for (int v = 0; v < NPL; ++v)
+                if (v < p.npl && u.i0 + v >= 0 && u.i0 + v < p.L0) u.live |= 1 << v;
         }
         u.ch = u.pc % p.C;
         u.oh0 = band * p.band;
@@ -169,13 +171,13 @@ __global__ __launch_bounds__(kDwThreads) void depthwise_kernel(const _Float16 *_
         chr[q] = k / cpl;
         chc[q] = (k - chr[q] * cpl) * 8;
     }
-    _Float16 ew[NT0], braw;
+    _Float16 ew[NRS][NT0], braw;
     auto issue = [&](const Unit &u) {
         const _Float16 *xp = x + size_t(u.pc) * p.L0 * plane_in;  // the image and channel
         const int nch = u.nvr * cpl;
         if constexpr (T0 == 0) {
             const _Float16 *xb = xp + (u.ilo + u.vr0) * p.L2;  // first valid row: contiguous from here
-            ew[0] = w[size_t(u.ch) * p.K1 * p.K2 + max(eidx, 0)];
+            ew[0][0] = w[size_t(u.ch) * p.K1 * p.K2 + max(eidx, 0)];
             braw = *(bias ? bias + u.ch : xp);  // used only with a bias
             vok = 0;
 #pragma unroll
@@ -187,20 +189,27 @@ __global__ __launch_bounds__(kDwThreads) void depthwise_kernel(const _Float16 *_
             }
             return;
         }
+        // the sub-kernel entries of every residue's taps (threads below NE)
         const size_t plane_w = size_t(p.K1) * p.K2;
+        if (threadIdx.x < NE) {
 #pragma unroll
-        for (int v0 = 0; v0 < NT0; ++v0)
-            ew[v0] = w[(size_t(u.ch) * p.K0 + (((u.live >> v0) & 1) ? u.k0 + v0 * p.ks0 : 0)) * plane_w + max(eidx, 0)];
+            for (int r = 0; r < NRS; ++r)
+#pragma unroll
+                for (int v0 = 0; v0 < NT0; ++v0) {
+                    const bool okw = r < p.s0 && v0 < field(p.nt0w, r);
+                    ew[r][v0] = w[(size_t(u.ch) * p.K0 + (okw ? field(p.k00w, r) + v0 * p.ks0 : 0)) * plane_w + max(eidx, 0)];
+                }
+        }
         braw = *(bias ? bias + u.ch : xp);  // used only with a bias
         const UDiv dn(nch > 0 ? nch : 1), dc(cpl);
 #pragma unroll
         for (int q = 0; q < NQ; ++q) {
             const int k = threadIdx.x + q * kDwThreads;
             const int sl = dn.div(k), kk = k - sl * nch;
-            const bool ok = nch > 0 && sl < NT0 && ((u.live >> sl) & 1);
+            const bool ok = nch > 0 && sl < p.npl && ((u.live >> sl) & 1);
             const int r = dc.div(kk), c8 = (kk - r * cpl) * 8;
-            // rows ilo + vr0 + r of input plane i0 - sl * bs0, contiguous from the first valid row
-            const _Float16 *src = xp + (size_t(u.i0 - sl * p.bs0) * plane_in + size_t(u.ilo + u.vr0 + r) * p.L2 + c8);
+            // rows ilo + vr0 + r of input plane i0 + sl, contiguous from the first valid row
+            const _Float16 *src = xp + (size_t(u.i0 + sl) * plane_in + size_t(u.ilo + u.vr0 + r) * p.L2 + c8);
             v[q] = *reinterpret_cast<const u32x4 *>(ok ? src : xp);
             dsto[q] = ok ? sl * p.slot_elems + kDwGuard + p.sh + (u.vr0 + r) * R + c8 : -1;
         }
@@ -221,7 +230,7 @@ __global__ __launch_bounds__(kDwThreads) void depthwise_kernel(const _Float16 *_
         {
             const int nz = (p.nrows - cur.nvr) * cpl;
 #pragma unroll
-            for (int v0 = 0; v0 < NT0; ++v0) {
+            for (int v0 = 0; v0 < NPL; ++v0) {
                 if (T0 > 0 && !((cur.live >> v0) & 1)) continue;
                 _Float16 *const sp = sx + v0 * p.slot_elems + kDwGuard;
                 for (int k = threadIdx.x; k < nz; k += kDwThreads) {
@@ -254,13 +263,42 @@ __global__ __launch_bounds__(kDwThreads) void depthwise_kernel(const _Float16 *_
             }
         if (threadIdx.x < NE) {
 #pragma unroll
-            for (int v0 = 0; v0 < NT0; ++v0) seff[v0 * NE + threadIdx.x] = eidx >= 0 ? ew[v0] : _Float16(0.0f);
+            for (int r = 0; r < NRS; ++r)
+#pragma unroll
+                for (int v0 = 0; v0 < NT0; ++v0)
+                    if (T0 == 0 || r < p.s0)
+                        seff[(r * NT0 + v0) * NE + threadIdx.x] =
+                            eidx >= 0 && (T0 == 0 || v0 < field(p.nt0w, r)) ? ew[r][v0] : _Float16(0.0f);
         }
         const float bv = bias ? float(braw) : 0.0f;
         __syncthreads();
+        // ---- load the next unit ahead, if there is one ----
+        const int tn = t + int(gridDim.x);
+        const Unit nxt = unit_of(min(tn, p.units - 1));
+        if (tn < p.units) issue(nxt);
+
+        // ---- compute and store the current unit ----
+        // Each item is one output row oh = S * j1 + rh: its row phase rh selects the
+        // window's row offset and the sub-kernels (selects over the S phases in registers)
+        const int orows = cur.oh1 - cur.oh0;  // oh0 is a multiple of S: oh0 = S * j1lo
+        int a0r[S];
+#pragma unroll
+        for (int r = 0; r < S; ++r) a0r[r] = p.a0_1[r] * R;
+        // rank 3: output plane s0 * j0 + r0 of each first-axis residue r0 in turn; its taps
+        // v0 < ntr read staged plane sbase - v0 * bs0
+        const int nres = T0 > 0 ? p.s0 : 1;
+        for (int r0 = 0; r0 < nres; ++r0) {
+        _Float16 *yplane = y + size_t(cur.c) * p.O1 * p.O2;
+        int ntr = 1, sbase = 0;
+        if constexpr (T0 > 0) {
+            const int o0 = p.s0 * cur.j0 + r0;
+            if (o0 >= p.O0) break;
+            ntr = field(p.nt0w, r0);
+            sbase = field(p.be00w, r0) - p.bmin0;
+            yplane = y + (size_t(cur.pc) * p.O0 + o0) * p.O1 * p.O2;
+        }
         // sub-kernels in registers: column-tap pairs for the packed dot products, and
-        // the odd last column tap (T2 odd) as float
-        // (one set per first-axis tap)
+        // the odd last column tap (T2 odd) as float (one set per first-axis tap)
         h2 wp[NT0][S][S][T1][NP > 0 ? NP : 1];
         float wt[NT0][S][S][T1];
 #pragma unroll
@@ -271,25 +309,11 @@ __global__ __launch_bounds__(kDwThreads) void depthwise_kernel(const _Float16 *_
                 for (int rwp = 0; rwp < S; ++rwp)
 #pragma unroll
                     for (int a = 0; a < T1; ++a) {
-                        const _Float16 *e = seff + v0 * NE + ((rh * S + rwp) * T1 + a) * T2;
+                        const _Float16 *e = seff + (r0 * NT0 + v0) * NE + ((rh * S + rwp) * T1 + a) * T2;
 #pragma unroll
                         for (int m = 0; m < NP; ++m) wp[v0][rh][rwp][a][m] = h2{e[2 * m], e[2 * m + 1]};
                         wt[v0][rh][rwp][a] = (T2 & 1) ? float(e[T2 - 1]) : 0.0f;
                     }
-
-        // ---- load the next unit ahead, if there is one ----
-        const int tn = t + int(gridDim.x);
-        const Unit nxt = unit_of(min(tn, p.units - 1));
-        if (tn < p.units) issue(nxt);
-
-        // ---- compute and store the current unit ----
-        // Each item is one output row oh = S * j1 + rh: its row phase rh selects the
-        // window's row offset and the sub-kernels (selects over the S phases in registers)
-        const int orows = cur.oh1 - cur.oh0;  // oh0 is a multiple of S: oh0 = S * j1lo
-        _Float16 *const yplane = y + size_t(cur.c) * p.O1 * p.O2;
-        int a0r[S];
-#pragma unroll
-        for (int r = 0; r < S; ++r) a0r[r] = p.a0_1[r] * R;
         // two copies of the item loop, with and without streaming stores: a store under a
         // run-time choice would be merged with the plain one and lose its cache hint
         auto items = [&](auto streaming) __attribute__((always_inline)) {
@@ -322,7 +346,8 @@ __global__ __launch_bounds__(kDwThreads) void depthwise_kernel(const _Float16 *_
             for (int e = 0; e < OC; ++e) out[e] = bv;
 #pragma unroll
             for (int v0 = 0; v0 < NT0; ++v0) {
-                if (T0 > 0 && !((cur.live >> v0) & 1)) continue;  // uniform over the block
+                const int slot = sbase - v0 * p.bs0;
+                if (T0 > 0 && !(v0 < ntr && ((cur.live >> slot) & 1))) continue;  // uniform over the block
                 h2 ws[S][T1][NP > 0 ? NP : 1];
                 float wts[S][T1];
 #pragma unroll
@@ -341,7 +366,7 @@ __global__ __launch_bounds__(kDwThreads) void depthwise_kernel(const _Float16 *_
                         for (int r = 0; r < S; ++r) c[r] = wt[v0][r][rwp][a];
                         wts[rwp][a] = pick(c);
                     }
-                const _Float16 *const wn = win + v0 * p.slot_elems;
+                const _Float16 *const wn = win + slot * p.slot_elems;
                 _Float16 xs[T1][XW];
                 if constexpr (S <= 2) {
                     // 8-byte aligned: whole 4-element pieces
@@ -414,6 +439,7 @@ __global__ __launch_bounds__(kDwThreads) void depthwise_kernel(const _Float16 *_
             items(std::true_type{});
         else
             items(std::false_type{});
+        }
         __syncthreads();  // the stage and seff are rewritten next
         if (tn >= p.units) break;
         t = tn;
@@ -494,7 +520,8 @@ bool make_dwplan(const Geom &g, ct_dtype dt, bool cl, const void *x, DwPlan *pl)
     const int64_t gs0 = std::__gcd(g.s[0], g.d[0]);
     a.ks0 = int(g.s[0] / gs0);
     a.bs0 = int(g.d[0] / gs0);
-    int T0 = 0;
+    int T0 = 0, bmin0 = 0, bmax0 = 0;
+    bool any0 = false;
     for (int r = 0; r < g.s[0]; ++r) {
         AxisPhase ph;
         if (!axis_phase(g, 0, r, &ph)) return false;
@@ -506,15 +533,24 @@ bool make_dwplan(const Geom &g, ct_dtype dt, bool cl, const void *x, DwPlan *pl)
         a.k00w |= (unsigned long long)(k0 & 0xffff) << (16 * r);
         a.be00w |= (unsigned long long)(unsigned(be0) & 0xffffu) << (16 * r);
         T0 = std::max(T0, ph.ntaps);
+        if (ph.ntaps) {  // input planes j0 + beta of this residue: beta in [beta[last], beta[0]]
+            bmin0 = any0 ? std::min(bmin0, ph.beta[ph.ntaps - 1]) : ph.beta[ph.ntaps - 1];
+            bmax0 = any0 ? std::max(bmax0, ph.beta[0]) : ph.beta[0];
+            any0 = true;
+        }
     }
     if (T0 == 0) return false;  // no tap reaches any output plane: the generic kernel handles it
     a.L0 = int(g.L[0]);
     a.O0 = int(g.O[0]);
     a.K0 = int(g.K[0]);
     a.s0 = int(g.s[0]);
+    a.J0 = int((g.O[0] + g.s[0] - 1) / g.s[0]);
+    a.bmin0 = bmin0;
+    a.npl = bmax0 - bmin0 + 1;  // staged planes per unit: the union of the residues' taps
     pl->T0 = g.nsp == 3 ? T0 : 0;
     if (!dw_compiled(S, T1, T2, off2, pl->T0)) return false;
-    T0 = std::max(pl->T0, 1);  // staged planes
+    if (pl->T0 > 0 && a.npl > kDwMaxPlanes) return false;
+    const int npl = pl->T0 > 0 ? a.npl : 1;  // staged planes
     a.C = int(g.C);
     a.L1 = int(g.L[1]);
     a.L2 = int(g.L[2]);
@@ -543,16 +579,16 @@ bool make_dwplan(const Geom &g, ct_dtype dt, bool cl, const void *x, DwPlan *pl)
     auto rows_for = [&](int b) { return (b + S - 1) / S - 1 + a.span1; };
     // + 8: the last row shifted by sh, and the 4-element window reads past a row's end
     auto bytes_for = [&](int b) { return (int64_t(kDwGuard) + int64_t(rows_for(b)) * a.row_w + 8) * 2; };
-    // (T0 planes of them)
+    // (npl planes of them)
     auto fits = [&](int b) {
-        return T0 * bytes_for(b) <= kDwStageBytes && T0 * rows_for(b) * cpl <= kDwMaxChunks * kDwThreads;
+        return npl * bytes_for(b) <= kDwStageBytes && npl * rows_for(b) * cpl <= kDwMaxChunks * kDwThreads;
     };
     // band of output rows (a multiple of S) whose staged rows fit
     int band = int((g.O[1] + S - 1) / S) * S;
     while (band > S && !fits(band)) band = (band / 2 + S - 1) / S * S;
     if (!fits(band)) return false;
     // few planes: more bands so the grid still fills the chip
-    const int64_t planes = g.N * g.C * g.O[0];  // output planes
+    const int64_t planes = g.N * g.C * (pl->T0 > 0 ? a.J0 : 1);  // units per band
     while (band >= 8 * S && planes * ((g.O[1] + band - 1) / band) < 2048) band = (band / 2 + S - 1) / S * S;
     a.band = band;
     a.nbands = int((g.O[1] + band - 1) / band);
@@ -561,9 +597,9 @@ bool make_dwplan(const Geom &g, ct_dtype dt, bool cl, const void *x, DwPlan *pl)
     if (units <= 0 || units > (1ll << 31) - 1) return false;
     a.units = int(units);
     a.slot_elems = int(bytes_for(band) / 2);
-    a.stage_elems = T0 * a.slot_elems;
-    pl->lds_bytes = size_t(T0) * size_t(bytes_for(band));
-    pl->nq = int((T0 * a.nrows * cpl + kDwThreads - 1) / kDwThreads);
+    a.stage_elems = npl * a.slot_elems;
+    pl->lds_bytes = size_t(npl) * size_t(bytes_for(band));
+    pl->nq = int((npl * a.nrows * cpl + kDwThreads - 1) / kDwThreads);
     pl->S = S;
     pl->T1 = T1;
     pl->T2 = T2;
