@@ -458,6 +458,46 @@ def test_depthwise_channels_last(T, case, integer):
     check(got, O.convtranspose(x, w, None, **attrs), "f16", integer, f"depthwise channels-last no-bias x{xs}")
 
 
+GROUPED_CL = [
+    # (x_shape, C/group, kernel shape, attrs): channels-last grouped calls with
+    # C/group = M/group in {2, 4, 8} on the channels-last bandwidth kernel (every output
+    # channel of an octet sums its group's inputs; ragged tiles, tap-less residues)
+    ((2, 16, 9, 13), 2, (4, 4), dict(strides=[2, 2], pads=[1, 1, 1, 1])),
+    ((1, 32, 7, 10), 4, (3, 3), dict(strides=[2, 2], pads=[1, 1, 1, 1], output_padding=[1, 1])),
+    ((2, 64, 5, 6), 8, (3, 3), dict(pads=[1, 1, 1, 1])),
+    ((1, 72, 6, 9), 2, (2, 2), dict(strides=[2, 2])),
+    ((1, 128, 5, 7), 8, (4, 4), dict(strides=[2, 2], pads=[1, 1, 1, 1])),
+    ((1, 24, 6, 5), 4, (1, 1), dict()),
+]
+
+
+@pytest.mark.parametrize("integer", [False, True], ids=["float", "int"])
+@pytest.mark.parametrize("case", GROUPED_CL, ids=lambda c: f"{c[0]}_g{c[1]}_k{c[2]}")
+def test_grouped_channels_last(T, case, integer):
+    """Channels-last grouped calls (C/group = M/group in {2, 4, 8}) on the grouped family's
+    channels-last kernel (the dispatcher must pick it) against the oracle on whole
+    outputs, with and without bias; bit-exact on integer inputs."""
+    xs, cg, ks, attrs = case
+    C = xs[1]
+    attrs = dict(attrs, group=C // cg)
+    _log(f"[case] grouped channels-last x{xs} cg{cg} k{ks} {attrs} integer={integer}")
+    rng = np.random.default_rng(zlib.crc32(repr(case).encode()) + integer)
+    gen = (lambda sz: rng.integers(-2, 3, size=sz)) if integer else (lambda sz: rng.normal(size=sz))
+    x = gen(xs).astype(np.float16)
+    w = (gen((C, cg) + tuple(ks)) * (1 if integer else 0.3)).astype(np.float16)
+    b = gen(C).astype(np.float16)
+    dev = torch.device("cuda:0")
+    tx = T.to_channels_last(torch.from_numpy(x).to(dev))
+    assert T.convtranspose_select_kernel(tx, torch.from_numpy(w).to(dev), torch.from_numpy(b).to(dev),
+                                         channels_last=True, **attrs) == "grouped"
+    ref = O.convtranspose(x, w, b, **attrs)
+    for kernel in ("grouped", "auto"):
+        got = gpu_run(T, x, w, b, attrs, True, kernel)
+        check(got, ref, "f16", integer, f"grouped channels-last {kernel} x{xs} cg{cg} {attrs}")
+    got = gpu_run(T, x, w, None, attrs, True, "grouped")
+    check(got, O.convtranspose(x, w, None, **attrs), "f16", integer, f"grouped channels-last no-bias x{xs}")
+
+
 PAIRS = [
     # (x_shape, w_shape, attrs): M/group > 64 and stride 2 on the innermost axis, the
     # channels-first shapes whose two column phases one block computes together when the

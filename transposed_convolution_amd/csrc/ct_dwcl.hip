@@ -21,6 +21,10 @@
 //   * Rank 3: a workgroup also owns one output plane o0 = s0*j0 + r0; it stages the tile's
 //     window of every input plane j0 + beta that residue r0's first-axis taps read, one
 //     after another, with the taps' weights, and sums over them too.
+//   * Groups of CG = C/group = M/group channels, CG in {2, 4, 8} (ranks 1 and 2): an
+//     octet of output channels holds whole groups, whose input channels are the same
+//     octet of X, so the window is staged as for CG = 1; output channel k of the octet
+//     sums input channels (k / CG) * CG + j, j < CG, with weights read from LDS per tap.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -51,6 +55,18 @@ __device__ __forceinline__ float fma_mix_hi(float acc, unsigned x, unsigned w)
     asm("v_fma_mix_f32 %0, %1, %2, %0 op_sel:[1,1,0] op_sel_hi:[1,1,0]" : "+v"(acc) : "v"(x), "v"(w));
     return acc;
 }
+// the same with the half of x and of w chosen separately (xh, wh: high halves; constants
+// after unrolling, so one instruction remains)
+__device__ __forceinline__ float fma_mix_sel(float acc, unsigned x, bool xh, unsigned w, bool wh)
+{
+    if (xh && wh) return fma_mix_hi(acc, x, w);
+    if (!xh && !wh) return fma_mix_lo(acc, x, w);
+    if (xh)
+        asm("v_fma_mix_f32 %0, %1, %2, %0 op_sel:[1,0,0] op_sel_hi:[1,1,0]" : "+v"(acc) : "v"(x), "v"(w));
+    else
+        asm("v_fma_mix_f32 %0, %1, %2, %0 op_sel:[0,1,0] op_sel_hi:[1,1,0]" : "+v"(acc) : "v"(x), "v"(w));
+    return acc;
+}
 constexpr int kMaxOct = 8;         // channel octets per tile (64 channels: more, lighter blocks)
 constexpr int kMaxS = 2, kMaxT = 4;
 constexpr int kMaxS0 = 4;         // largest stride on the first axis (rank 3)
@@ -75,7 +91,8 @@ struct DwClArgs {
 };
 
 // T0: the most first-axis taps of an output plane (rank 3), 0 for ranks 1 and 2
-template <int S1, int S2, int T1, int T2, int T0>
+// CG: channels per group (1: depthwise)
+template <int S1, int S2, int T1, int T2, int T0, int CG>
 __global__ __launch_bounds__(kThreads) void dwcl_kernel(const _Float16 *__restrict__ x, const _Float16 *__restrict__ w,
                                                         const _Float16 *__restrict__ bias, _Float16 *__restrict__ y,
                                                         DwClArgs p)
@@ -151,9 +168,12 @@ __global__ __launch_bounds__(kThreads) void dwcl_kernel(const _Float16 *__restri
                 }
             }
         }
-        // weights of each staged plane's tap: w[c][k0 + u * ks0][t]
-        const int wpl = co * 8 * KK;  // per plane
+        // weights of each staged plane's tap: w[c][k0 + u * ks0][t] into [plane][tap][channel]
+        // (CG = 1), or w[c_in][m % CG][k0 + u * ks0][t] into [plane][tap][j][m] for output
+        // channel m of the tile and input j of its group (CG > 1)
+        const int wpl = co * 8 * KK * CG;  // per plane
         const int wn = NT0 * wpl;
+        const UDiv dgk(CG * KK);
         for (int base = 0; base < wn; base += kThreads * kWBatch) {
             _Float16 v[kWBatch];
             unsigned okm = 0;
@@ -161,18 +181,33 @@ __global__ __launch_bounds__(kThreads) void dwcl_kernel(const _Float16 *__restri
             for (int k = 0; k < kWBatch; ++k) {
                 const int u = base + tid + k * kThreads;
                 const int sl = T0 > 0 ? dwp.div(u) : 0, uu = u - sl * wpl;
-                const int c = dkk.div(uu), t = uu - c * KK;
-                const bool ok = u < wn && ((live >> sl) & 1) && c_lo + c < p.C;
-                v[k] = w[ok ? (size_t(c_lo + c) * p.K0 + k0 + sl * p.ks0) * KK + t : 0];
-                okm |= unsigned(ok) << k;
+                if constexpr (CG == 1) {
+                    const int c = dkk.div(uu), t = uu - c * KK;
+                    const bool ok = u < wn && ((live >> sl) & 1) && c_lo + c < p.C;
+                    v[k] = w[ok ? (size_t(c_lo + c) * p.K0 + k0 + sl * p.ks0) * KK + t : 0];
+                    okm |= unsigned(ok) << k;
+                } else {
+                    const int m = dgk.div(uu), rem = uu - m * (CG * KK);
+                    const int j = dkk.div(rem), t = rem - j * KK;
+                    const int cin = c_lo + (m / CG) * CG + j;
+                    const bool ok = u < wn && ((live >> sl) & 1) && c_lo + m < p.C;
+                    v[k] = w[ok ? ((size_t(cin) * CG + m % CG) * p.K0 + k0 + sl * p.ks0) * KK + t : 0];
+                    okm |= unsigned(ok) << k;
+                }
             }
 #pragma unroll
             for (int k = 0; k < kWBatch; ++k) {
                 const int u = base + tid + k * kThreads;
                 if (u < wn) {
                     const int sl = T0 > 0 ? dwp.div(u) : 0, uu = u - sl * wpl;
-                    const int c = dkk.div(uu), t = uu - c * KK;
-                    sw[sl * wpl + t * (co * 8) + c] = ((okm >> k) & 1u) ? v[k] : _Float16(0.0f);
+                    if constexpr (CG == 1) {
+                        const int c = dkk.div(uu), t = uu - c * KK;
+                        sw[sl * wpl + t * (co * 8) + c] = ((okm >> k) & 1u) ? v[k] : _Float16(0.0f);
+                    } else {
+                        const int m = dgk.div(uu), rem = uu - m * (CG * KK);
+                        const int j = dkk.div(rem), t = rem - j * KK;
+                        sw[sl * wpl + (t * CG + j) * (co * 8) + m] = ((okm >> k) & 1u) ? v[k] : _Float16(0.0f);
+                    }
                 }
             }
         }
@@ -182,9 +217,10 @@ __global__ __launch_bounds__(kThreads) void dwcl_kernel(const _Float16 *__restri
     const int oc = tid % co, slot = tid / co, nslots = kThreads / co;
     if (slot >= nslots) return;  // threads past the last whole slot (co does not divide 256)
     // the thread's weights: entry e = ((r1 * S2 + r2) * T1 + a) * T2 + cc of each plane
-    u32x4 wv[NT0][NE];
+    // (CG = 1; groups read theirs from LDS per tap)
+    u32x4 wv[CG == 1 ? NT0 : 1][CG == 1 ? NE : 1];
 #pragma unroll
-    for (int v0 = 0; v0 < NT0; ++v0)
+    for (int v0 = 0; v0 < (CG == 1 ? NT0 : 0); ++v0)
 #pragma unroll
         for (int r1 = 0; r1 < S1; ++r1)
 #pragma unroll
@@ -233,12 +269,30 @@ __global__ __launch_bounds__(kThreads) void dwcl_kernel(const _Float16 *__restri
                             for (int cc = 0; cc < T2; ++cc) {
                                 const int e = ((r1 * S2 + r2) * T1 + a) * T2 + cc;
                                 const int wr = pj1 + p.off1[r1][a], wc = pj2 + p.off2[r2][cc];
-                                const u32x4 xv =
-                                    *reinterpret_cast<const u32x4 *>(sx + v0 * wsz + (wr * p.HC + wc) * rowb + oc * 16);
+                                if constexpr (CG == 1) {
+                                    const u32x4 xv =
+                                        *reinterpret_cast<const u32x4 *>(sx + v0 * wsz + (wr * p.HC + wc) * rowb + oc * 16);
 #pragma unroll
-                                for (int k = 0; k < 4; ++k) {  // channels 2k (low halves), 2k + 1 (high)
-                                    acc[2 * k] = fma_mix_lo(acc[2 * k], xv[k], wv[v0][e][k]);
-                                    acc[2 * k + 1] = fma_mix_hi(acc[2 * k + 1], xv[k], wv[v0][e][k]);
+                                    for (int k = 0; k < 4; ++k) {  // channels 2k (low halves), 2k + 1 (high)
+                                        acc[2 * k] = fma_mix_lo(acc[2 * k], xv[k], wv[v0][e][k]);
+                                        acc[2 * k + 1] = fma_mix_hi(acc[2 * k + 1], xv[k], wv[v0][e][k]);
+                                    }
+                                } else {
+                                    const int k1 = p.k1[r1][a], k2 = p.k2[r2][cc];
+                                    if (k1 < 0 || k2 < 0) continue;  // no tap (uniform)
+                                    const u32x4 xv =
+                                        *reinterpret_cast<const u32x4 *>(sx + v0 * wsz + (wr * p.HC + wc) * rowb + oc * 16);
+                                    const _Float16 *const wt = sw + (size_t(v0) * KK + k1 * p.K2 + k2) * CG * (co * 8) + oc * 8;
+#pragma unroll
+                                    for (int j = 0; j < CG; ++j) {
+                                        // output k of the octet takes input (k / CG) * CG + j
+                                        const u32x4 wj = *reinterpret_cast<const u32x4 *>(wt + j * (co * 8));
+#pragma unroll
+                                        for (int k = 0; k < 8; ++k) {
+                                            const int xi = (k / CG) * CG + j;
+                                            acc[k] = fma_mix_sel(acc[k], xv[xi >> 1], xi & 1, wj[k >> 1], k & 1);
+                                        }
+                                    }
                                 }
                             }
                     }
@@ -269,6 +323,7 @@ struct DwClPlan {
     DwClArgs a;
     int S1, S2, T1, T2;
     int T0;  // kernel's T0: the most first-axis taps of a residue (rank 3), else 0
+    int CG;  // channels per group (C/group = M/group)
     size_t lds;
 };
 
@@ -374,28 +429,29 @@ bool make_dwcl_plan(const Geom &g, DwClPlan *pl)
     if (blocks < 1 || blocks > INT32_MAX) return false;
     a.nblocks = int(blocks);
     const int nt0 = std::max(pl->T0, 1);  // staged planes
-    pl->lds = nt0 * (size_t(a.HR) * a.HC * a.co * 16 + size_t(a.co) * 8 * a.K1 * a.K2 * 2);
+    pl->CG = int(g.Cg);
+    pl->lds = nt0 * (size_t(a.HR) * a.HC * a.co * 16 + size_t(a.co) * 8 * a.K1 * a.K2 * 2 * pl->CG);
     if (pl->lds > 64 * 1024) return false;
     return true;
 }
 
-template <int S1, int S2, int T1, int T2, int T0>
+template <int S1, int S2, int T1, int T2, int T0, int CG = 1>
 bool launch_if(const DwClPlan &pl, const void *x, const void *w, const void *b, void *y, hipStream_t st)
 {
-    if (pl.S1 != S1 || pl.S2 != S2 || pl.T1 != T1 || pl.T2 != T2 || pl.T0 != T0) return false;
-    hipLaunchKernelGGL((dwcl_kernel<S1, S2, T1, T2, T0>), dim3(unsigned(pl.a.nblocks)), dim3(kThreads), pl.lds, st,
+    if (pl.S1 != S1 || pl.S2 != S2 || pl.T1 != T1 || pl.T2 != T2 || pl.T0 != T0 || pl.CG != CG) return false;
+    hipLaunchKernelGGL((dwcl_kernel<S1, S2, T1, T2, T0, CG>), dim3(unsigned(pl.a.nblocks)), dim3(kThreads), pl.lds, st,
                        static_cast<const _Float16 *>(x), static_cast<const _Float16 *>(w),
                        static_cast<const _Float16 *>(b), static_cast<_Float16 *>(y), pl.a);
     return true;
 }
 
 // equal strides on the last two axes: ranks 2 and 3
-template <int T0>
+template <int T0, int CG = 1>
 bool launch_square(const DwClPlan &pl, const void *x, const void *w, const void *b, void *y, hipStream_t st)
 {
-    return launch_if<2, 2, 1, 1, T0>(pl, x, w, b, y, st) || launch_if<2, 2, 2, 2, T0>(pl, x, w, b, y, st) ||
-           launch_if<1, 1, 1, 1, T0>(pl, x, w, b, y, st) || launch_if<1, 1, 2, 2, T0>(pl, x, w, b, y, st) ||
-           launch_if<1, 1, 3, 3, T0>(pl, x, w, b, y, st);
+    return launch_if<2, 2, 1, 1, T0, CG>(pl, x, w, b, y, st) || launch_if<2, 2, 2, 2, T0, CG>(pl, x, w, b, y, st) ||
+           launch_if<1, 1, 1, 1, T0, CG>(pl, x, w, b, y, st) || launch_if<1, 1, 2, 2, T0, CG>(pl, x, w, b, y, st) ||
+           launch_if<1, 1, 3, 3, T0, CG>(pl, x, w, b, y, st);
 }
 
 bool has_instance(const DwClPlan &pl)
@@ -403,6 +459,12 @@ bool has_instance(const DwClPlan &pl)
     // (S1, S2, T1, T2): ranks 2 and 3, then rank 1 (T0 = 0 only)
     static const int square[][4] = {{2, 2, 1, 1}, {2, 2, 2, 2}, {1, 1, 1, 1}, {1, 1, 2, 2}, {1, 1, 3, 3}};
     static const int rank1[][4] = {{1, 2, 1, 1}, {1, 2, 1, 2}, {1, 2, 1, 4}, {1, 1, 1, 2}, {1, 1, 1, 3}, {1, 1, 1, 4}};
+    if (pl.CG != 1) {  // groups: the rank-2 instances
+        if (pl.CG != 2 && pl.CG != 4 && pl.CG != 8) return false;
+        for (const auto &i : square)
+            if (pl.S1 == i[0] && pl.S2 == i[1] && pl.T1 == i[2] && pl.T2 == i[3]) return pl.T0 == 0;
+        return false;
+    }
     for (const auto &i : square)
         if (pl.S1 == i[0] && pl.S2 == i[1] && pl.T1 == i[2] && pl.T2 == i[3]) return pl.T0 >= 0 && pl.T0 <= 3;
     if (pl.T0 != 0) return false;
@@ -415,7 +477,8 @@ bool has_instance(const DwClPlan &pl)
 
 bool dwcl_supports(const Geom &g, ct_dtype dt, bool cl, const void *x)
 {
-    if (!cl || dt != CT_FLOAT16 || g.Cg != 1 || g.Mg != 1 || g.C % 8 != 0 || g.x_elems() <= 0) return false;
+    if (!cl || dt != CT_FLOAT16 || g.Cg != g.Mg || g.Cg > 8 || 8 % g.Cg != 0 || g.C % 8 != 0 || g.x_elems() <= 0)
+        return false;
     if (reinterpret_cast<uintptr_t>(x) % 16 != 0) return false;
     DwClPlan pl;
     return make_dwcl_plan(g, &pl) && has_instance(pl);
@@ -436,7 +499,9 @@ ct_status launch_dwcl(const Geom &g, const void *x, const void *w, const void *b
         launch_if<1, 2, 1, 2, 0>(pl, x, w, bias, y, st) || launch_if<1, 2, 1, 4, 0>(pl, x, w, bias, y, st) ||
         launch_if<1, 1, 1, 2, 0>(pl, x, w, bias, y, st) || launch_if<1, 1, 1, 3, 0>(pl, x, w, bias, y, st) ||
         launch_if<1, 1, 1, 4, 0>(pl, x, w, bias, y, st) || launch_square<1>(pl, x, w, bias, y, st) ||
-        launch_square<2>(pl, x, w, bias, y, st) || launch_square<3>(pl, x, w, bias, y, st);
+        launch_square<2>(pl, x, w, bias, y, st) || launch_square<3>(pl, x, w, bias, y, st) ||
+        launch_square<0, 2>(pl, x, w, bias, y, st) || launch_square<0, 4>(pl, x, w, bias, y, st) ||
+        launch_square<0, 8>(pl, x, w, bias, y, st);
     mark_after(st);
     const hipError_t e = launched ? hipGetLastError() : hipErrorInvalidConfiguration;
     if (e != hipSuccess) {
