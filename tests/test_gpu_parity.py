@@ -458,6 +458,49 @@ def test_depthwise_channels_last(T, case, integer):
     check(got, O.convtranspose(x, w, None, **attrs), "f16", integer, f"depthwise channels-last no-bias x{xs}")
 
 
+GROUPED_NC = [
+    # (x_shape, C/group, kernel size, attrs): channels-first grouped calls with
+    # C/group = M/group in {2, 4, 8}: rows of a multiple of 8 inputs take the depthwise
+    # kernel's group mode (a unit stages the group's input planes and writes its output
+    # planes), the others and the uncompiled combinations the generic grouped kernel
+    ((2, 16, 9, 16), 2, 4, dict(strides=[2, 2], pads=[1, 1, 1, 1])),
+    ((1, 32, 7, 24), 4, 3, dict(strides=[2, 2], pads=[1, 1, 1, 1], output_padding=[1, 1])),
+    ((2, 64, 5, 8), 8, 4, dict(strides=[2, 2], pads=[1, 1, 1, 1])),
+    ((1, 24, 6, 16), 4, 3, dict(pads=[1, 1, 1, 1])),
+    ((1, 16, 5, 16), 2, 6, dict(strides=[2, 2], pads=[2, 2, 2, 2])),
+    ((1, 64, 6, 8), 8, 3, dict(pads=[1, 1, 1, 1])),
+    ((1, 48, 10, 40), 2, 2, dict(strides=[2, 2])),
+    ((1, 16, 150, 64), 2, 4, dict(strides=[2, 2], pads=[1, 1, 1, 1])),
+    ((2, 8, 7, 13), 2, 4, dict(strides=[2, 2], pads=[1, 1, 1, 1])),
+]
+
+
+@pytest.mark.parametrize("integer", [False, True], ids=["float", "int"])
+@pytest.mark.parametrize("case", GROUPED_NC, ids=lambda c: f"{c[0]}_g{c[1]}_k{c[2]}")
+def test_grouped_channels_first(T, case, integer):
+    """Channels-first grouped calls with small groups on the grouped family (the
+    dispatcher must pick it) against the oracle on whole outputs, with and without bias;
+    bit-exact on integer inputs."""
+    xs, cg, k, attrs = case
+    C = xs[1]
+    attrs = dict(attrs, group=C // cg)
+    _log(f"[case] grouped channels-first x{xs} cg{cg} k{k} {attrs} integer={integer}")
+    rng = np.random.default_rng(zlib.crc32(repr(case).encode()) + integer)
+    gen = (lambda sz: rng.integers(-2, 3, size=sz)) if integer else (lambda sz: rng.normal(size=sz))
+    x = gen(xs).astype(np.float16)
+    w = (gen((C, cg, k, k)) * (1 if integer else 0.3)).astype(np.float16)
+    b = gen(C).astype(np.float16)
+    dev = torch.device("cuda:0")
+    assert T.convtranspose_select_kernel(torch.from_numpy(x).to(dev), torch.from_numpy(w).to(dev),
+                                         torch.from_numpy(b).to(dev), **attrs) == "grouped"
+    ref = O.convtranspose(x, w, b, **attrs)
+    for kernel in ("grouped", "auto"):
+        got = gpu_run(T, x, w, b, attrs, False, kernel)
+        check(got, ref, "f16", integer, f"grouped channels-first {kernel} x{xs} cg{cg} {attrs}")
+    got = gpu_run(T, x, w, None, attrs, False, "grouped")
+    check(got, O.convtranspose(x, w, None, **attrs), "f16", integer, f"grouped channels-first no-bias x{xs}")
+
+
 GROUPED_CL = [
     # (x_shape, C/group, kernel shape, attrs): channels-last grouped calls with
     # C/group = M/group in {2, 4, 8} on the channels-last bandwidth kernel (every output

@@ -63,8 +63,11 @@ struct DwArgs {
 };
 
 // T0: the most first-axis taps of an output plane (rank 3); 0 for ranks 1 and 2, whose
-// units read one plane and skip the first-axis bookkeeping.
-template <int S, int T1, int T2, int OFF2, int NQ, int T0>
+// units read one plane and skip the first-axis bookkeeping.  CG: channels per group
+// (C/group = M/group; ranks 1 and 2): a unit stages the CG input planes of one group and
+// writes its CG output planes, each the sum over the group's input channels (CG = 1:
+// depthwise).
+template <int S, int T1, int T2, int OFF2, int NQ, int T0, int CG = 1>
 __global__ __launch_bounds__(kDwThreads) void depthwise_kernel(const _Float16 *__restrict__ x,
                                                                const _Float16 *__restrict__ w,
                                                                const _Float16 *__restrict__ bias,
@@ -73,9 +76,13 @@ __global__ __launch_bounds__(kDwThreads) void depthwise_kernel(const _Float16 *_
     constexpr int OC = 8;               // output columns per thread
     constexpr int JC = OC / S;          // input-grid columns they span
     constexpr int NE = S * S * T1 * T2;  // sub-kernel entries over all phases
-    constexpr int NT0 = T0 > 0 ? T0 : 1;            // first-axis taps of a residue
-    constexpr int NPL = T0 > 0 ? kDwMaxPlanes : 1;  // staged planes (at most)
-    constexpr int NRS = T0 > 0 ? kDwMaxS0 : 1;      // first-axis residues (at most)
+    static_assert(T0 == 0 || CG == 1, "groups of channels for ranks 1 and 2 only");
+    constexpr bool GRP = CG > 1;
+    constexpr bool MULTI = T0 > 0 || GRP;  // several staged planes and output planes per unit
+    // per unit: input planes read per output plane, staged planes, output planes (at most)
+    constexpr int NT0 = T0 > 0 ? T0 : CG;
+    constexpr int NPL = T0 > 0 ? kDwMaxPlanes : CG;
+    constexpr int NRS = T0 > 0 ? kDwMaxS0 : CG;
     // column offset of residue r's window (0 or 1), fixed at compile time so every
     // register index below is a constant; row offsets are LDS addresses and stay runtime
     constexpr int MAXO2 = (OFF2 != 0) ? 1 : 0;
@@ -93,6 +100,7 @@ __global__ __launch_bounds__(kDwThreads) void depthwise_kernel(const _Float16 *_
     extern __shared__ __attribute__((aligned(16))) unsigned char dw_lds[];
     _Float16 *const sx = reinterpret_cast<_Float16 *>(dw_lds);
     __shared__ _Float16 seff[NRS * NT0 * NE];  // sub-kernels of the unit's first-axis residues and taps
+    __shared__ float sbias[NRS];                // several output planes: their bias
 
     const int R = p.row_w, cpl = p.L2 / 8;
     const int segs = (p.O2 + OC - 1) / OC;
@@ -129,10 +137,14 @@ __global__ __launch_bounds__(kDwThreads) void depthwise_kernel(const _Float16 *_
         Unit u;
         const int band = t % p.nbands;
         u.c = t / p.nbands;  // ranks 1-2: the plane; rank 3: (image, channel, j0)
-        if constexpr (T0 == 0) {
+        if constexpr (!MULTI) {
             u.pc = u.c;
             u.j0 = u.i0 = 0;
             u.live = 1;
+        } else if constexpr (GRP) {  // u.c: (image, group); its planes are u.c * CG + j
+            u.pc = u.c;
+            u.j0 = u.i0 = 0;
+            u.live = (1 << CG) - 1;
         } else {
             u.pc = u.c / p.J0;  // image and channel
             u.j0 = u.c - u.pc * p.J0;
@@ -142,7 +154,7 @@ __global__ __launch_bounds__(kDwThreads) void depthwise_kernel(const _Float16 *_
             for (int v = 0; v < NPL; ++v)
                 if (v < p.npl && u.i0 + v >= 0 && u.i0 + v < p.L0) u.live |= 1 << v;
         }
-        u.ch = u.pc % p.C;
+        u.ch = GRP ? u.pc % (p.C / CG) : u.pc % p.C;  // grouped: the group
         u.oh0 = band * p.band;
         u.oh1 = min(u.oh0 + p.band, p.O1);
         u.j1lo = u.oh0 / S;
@@ -171,11 +183,11 @@ __global__ __launch_bounds__(kDwThreads) void depthwise_kernel(const _Float16 *_
         chr[q] = k / cpl;
         chc[q] = (k - chr[q] * cpl) * 8;
     }
-    _Float16 ew[NRS][NT0], braw;
+    _Float16 ew[NRS][NT0], braw;  // several output planes: thread r < NRS loads plane r's bias
     auto issue = [&](const Unit &u) {
         const _Float16 *xp = x + size_t(u.pc) * p.L0 * plane_in;  // the image and channel
         const int nch = u.nvr * cpl;
-        if constexpr (T0 == 0) {
+        if constexpr (!MULTI) {
             const _Float16 *xb = xp + (u.ilo + u.vr0) * p.L2;  // first valid row: contiguous from here
             ew[0][0] = w[size_t(u.ch) * p.K1 * p.K2 + max(eidx, 0)];
             braw = *(bias ? bias + u.ch : xp);  // used only with a bias
@@ -189,18 +201,23 @@ __global__ __launch_bounds__(kDwThreads) void depthwise_kernel(const _Float16 *_
             }
             return;
         }
-        // the sub-kernel entries of every residue's taps (threads below NE)
+        // the sub-kernel entries of every residue's taps (threads below NE); grouped: of
+        // output channel r of the group and its input channel v0, w[g CG + v0][r]
         const size_t plane_w = size_t(p.K1) * p.K2;
         if (threadIdx.x < NE) {
 #pragma unroll
             for (int r = 0; r < NRS; ++r)
 #pragma unroll
                 for (int v0 = 0; v0 < NT0; ++v0) {
-                    const bool okw = r < p.s0 && v0 < field(p.nt0w, r);
-                    ew[r][v0] = w[(size_t(u.ch) * p.K0 + (okw ? field(p.k00w, r) + v0 * p.ks0 : 0)) * plane_w + max(eidx, 0)];
+                    if constexpr (GRP) {
+                        ew[r][v0] = w[(size_t(u.ch * CG + v0) * CG + r) * plane_w + max(eidx, 0)];
+                    } else {
+                        const bool okw = r < p.s0 && v0 < field(p.nt0w, r);
+                        ew[r][v0] = w[(size_t(u.ch) * p.K0 + (okw ? field(p.k00w, r) + v0 * p.ks0 : 0)) * plane_w + max(eidx, 0)];
+                    }
                 }
         }
-        braw = *(bias ? bias + u.ch : xp);  // used only with a bias
+        braw = *(bias ? bias + (GRP ? u.ch * CG + min(int(threadIdx.x), NRS - 1) : u.ch) : xp);  // only with a bias
         const UDiv dn(nch > 0 ? nch : 1), dc(cpl);
 #pragma unroll
         for (int q = 0; q < NQ; ++q) {
@@ -231,7 +248,7 @@ __global__ __launch_bounds__(kDwThreads) void depthwise_kernel(const _Float16 *_
             const int nz = (p.nrows - cur.nvr) * cpl;
 #pragma unroll
             for (int v0 = 0; v0 < NPL; ++v0) {
-                if (T0 > 0 && !((cur.live >> v0) & 1)) continue;
+                if (MULTI && !((cur.live >> v0) & 1)) continue;
                 _Float16 *const sp = sx + v0 * p.slot_elems + kDwGuard;
                 for (int k = threadIdx.x; k < nz; k += kDwThreads) {
                     int r = k / cpl;
@@ -245,8 +262,8 @@ __global__ __launch_bounds__(kDwThreads) void depthwise_kernel(const _Float16 *_
         }
 #pragma unroll
         for (int q = 0; q < NQ; ++q)
-            if (T0 == 0 ? ((vok >> q) & 1u) != 0 : dsto[q] >= 0) {
-                _Float16 *dst = T0 == 0 ? sx + kDwGuard + p.sh + (cur.vr0 + chr[q]) * R + chc[q] : sx + dsto[q];
+            if (!MULTI ? ((vok >> q) & 1u) != 0 : dsto[q] >= 0) {
+                _Float16 *dst = !MULTI ? sx + kDwGuard + p.sh + (cur.vr0 + chr[q]) * R + chc[q] : sx + dsto[q];
                 const u32x4 vq = v[q];
                 if (p.sh == 0) {  // 16-byte aligned
                     *reinterpret_cast<u32x4 *>(dst) = vq;
@@ -261,6 +278,7 @@ __global__ __launch_bounds__(kDwThreads) void depthwise_kernel(const _Float16 *_
                     *reinterpret_cast<unsigned short *>(dst + 7) = (unsigned short)(vq[3] >> 16);
                 }
             }
+        if (MULTI && threadIdx.x < NRS) sbias[threadIdx.x] = bias ? float(braw) : 0.0f;
         if (threadIdx.x < NE) {
 #pragma unroll
             for (int r = 0; r < NRS; ++r)
@@ -270,7 +288,6 @@ __global__ __launch_bounds__(kDwThreads) void depthwise_kernel(const _Float16 *_
                         seff[(r * NT0 + v0) * NE + threadIdx.x] =
                             eidx >= 0 && (T0 == 0 || v0 < field(p.nt0w, r)) ? ew[r][v0] : _Float16(0.0f);
         }
-        const float bv = bias ? float(braw) : 0.0f;
         __syncthreads();
         // ---- load the next unit ahead, if there is one ----
         const int tn = t + int(gridDim.x);
@@ -286,10 +303,12 @@ __global__ __launch_bounds__(kDwThreads) void depthwise_kernel(const _Float16 *_
         for (int r = 0; r < S; ++r) a0r[r] = p.a0_1[r] * R;
         // rank 3: output plane s0 * j0 + r0 of each first-axis residue r0 in turn; its taps
         // v0 < ntr read staged plane sbase - v0 * bs0
-        const int nres = T0 > 0 ? p.s0 : 1;
+        // grouped: output channel r0 of the group, its taps v0 < CG the group's input planes
+        const int nres = T0 > 0 ? p.s0 : CG;
         for (int r0 = 0; r0 < nres; ++r0) {
-        _Float16 *yplane = y + size_t(cur.c) * p.O1 * p.O2;
-        int ntr = 1, sbase = 0;
+        const float bv = !MULTI ? (bias ? float(braw) : 0.0f) : sbias[GRP ? r0 : 0];
+        _Float16 *yplane = y + (size_t(cur.c) * CG + (GRP ? r0 : 0)) * p.O1 * p.O2;
+        int ntr = NT0, sbase = 0;
         if constexpr (T0 > 0) {
             const int o0 = p.s0 * cur.j0 + r0;
             if (o0 >= p.O0) break;
@@ -346,7 +365,7 @@ __global__ __launch_bounds__(kDwThreads) void depthwise_kernel(const _Float16 *_
             for (int e = 0; e < OC; ++e) out[e] = bv;
 #pragma unroll
             for (int v0 = 0; v0 < NT0; ++v0) {
-                const int slot = sbase - v0 * p.bs0;
+                const int slot = GRP ? v0 : sbase - v0 * p.bs0;
                 if (T0 > 0 && !(v0 < ntr && ((cur.live >> slot) & 1))) continue;  // uniform over the block
                 h2 ws[S][T1][NP > 0 ? NP : 1];
                 float wts[S][T1];
@@ -451,6 +470,7 @@ struct DwPlan {
     DwArgs a;
     int S, T1, T2, off2;  // off2: bit r = column window offset of residue r
     int T0;               // kernel's T0: most first-axis taps of a residue (rank 3), else 0
+    int CG;               // channels per group (1: depthwise)
     int nq;               // 16-byte input chunks per thread that stage one band
     size_t lds_bytes;     // staged band
 };
@@ -485,9 +505,14 @@ bool axis_windows(const Geom &g, int ax, int S, int *T, int *lo, int *hi, int *a
 }
 
 // Compiled (S, T, column offset pattern) combinations.
-bool dw_compiled(int S, int T1, int T2, int off2, int T0)
+bool dw_compiled(int S, int T1, int T2, int off2, int T0, int CG)
 {
     if (T1 != T2) return false;
+    // groups of 2, 4 or 8 channels (ranks 1 and 2): stride 2 with up to 2 taps per phase
+    // and row, and with 3 or stride 1 with 3 for groups up to 4 (registers)
+    if (CG > 1)
+        return T0 == 0 && (CG == 2 || CG == 4 || CG == 8) &&
+               ((S == 2 && T1 <= 2) || (CG <= 4 && ((S == 2 && T1 == 3) || (S == 1 && T1 == 3 && off2 == 0))));
     // rank 3 (1 to 3 first-axis taps per output plane): stride 2 with up to 3 taps per
     // row and column phase, stride 1 with 3 taps
     if (T0 >= 1 && T0 <= 3) return (S == 2 && T1 >= 1 && T1 <= 3) || (S == 1 && T1 == 3 && off2 == 0);
@@ -500,7 +525,8 @@ bool dw_compiled(int S, int T1, int T2, int off2, int T0)
 
 bool make_dwplan(const Geom &g, ct_dtype dt, bool cl, const void *x, DwPlan *pl)
 {
-    if (dt != CT_FLOAT16 || cl || g.Cg != 1 || g.Mg != 1 || g.G < 2 || g.L[0] * g.L[1] * g.L[2] == 0 ||
+    if (dt != CT_FLOAT16 || cl || g.Cg != g.Mg || g.Cg > 8 || (g.Cg > 1 && g.nsp == 3) || g.G < 2 ||
+        g.L[0] * g.L[1] * g.L[2] == 0 ||
         g.O[0] == 0 || g.L[0] * g.L[1] * g.L[2] >= (1ll << 31) || g.O[0] >= (1ll << 31))
         return false;
     const int S = int(g.s[2]);
@@ -548,9 +574,14 @@ bool make_dwplan(const Geom &g, ct_dtype dt, bool cl, const void *x, DwPlan *pl)
     a.bmin0 = bmin0;
     a.npl = bmax0 - bmin0 + 1;  // staged planes per unit: the union of the residues' taps
     pl->T0 = g.nsp == 3 ? T0 : 0;
-    if (!dw_compiled(S, T1, T2, off2, pl->T0)) return false;
+    pl->CG = int(g.Cg);
+    if (!dw_compiled(S, T1, T2, off2, pl->T0, pl->CG)) return false;
     if (pl->T0 > 0 && a.npl > kDwMaxPlanes) return false;
-    const int npl = pl->T0 > 0 ? a.npl : 1;  // staged planes
+    if (pl->CG > 1) {  // a group's CG input planes, image by image: plane (n G + g) CG + j
+        a.L0 = pl->CG;
+        a.npl = pl->CG;
+    }
+    const int npl = pl->T0 > 0 || pl->CG > 1 ? a.npl : 1;  // staged planes
     a.C = int(g.C);
     a.L1 = int(g.L[1]);
     a.L2 = int(g.L[2]);
@@ -588,7 +619,7 @@ bool make_dwplan(const Geom &g, ct_dtype dt, bool cl, const void *x, DwPlan *pl)
     while (band > S && !fits(band)) band = (band / 2 + S - 1) / S * S;
     if (!fits(band)) return false;
     // few planes: more bands so the grid still fills the chip
-    const int64_t planes = g.N * g.C * (pl->T0 > 0 ? a.J0 : 1);  // units per band
+    const int64_t planes = g.N * (g.C / pl->CG) * (pl->T0 > 0 ? a.J0 : 1);  // units per band
     while (band >= 8 * S && planes * ((g.O[1] + band - 1) / band) < 2048) band = (band / 2 + S - 1) / S * S;
     a.band = band;
     a.nbands = int((g.O[1] + band - 1) / band);
@@ -632,10 +663,10 @@ int resident_blocks(const void *fn, size_t lds)
     return blocks;
 }
 
-template <int S, int T1, int T2, int OFF2, int NQ, int T0>
+template <int S, int T1, int T2, int OFF2, int NQ, int T0, int CG>
 void launch_t(const DwPlan &pl, const void *x, const void *w, const void *bias, void *y, hipStream_t st)
 {
-    auto fn = depthwise_kernel<S, T1, T2, OFF2, NQ, T0>;
+    auto fn = depthwise_kernel<S, T1, T2, OFF2, NQ, T0, CG>;
     const int res = resident_blocks(reinterpret_cast<const void *>(fn), pl.lds_bytes);
     const int grid = std::min(pl.a.units, res > 0 ? res : pl.a.units);
     hipLaunchKernelGGL(fn, dim3(unsigned(grid)), dim3(kDwThreads), pl.lds_bytes, st,
@@ -643,36 +674,44 @@ void launch_t(const DwPlan &pl, const void *x, const void *w, const void *bias, 
                        static_cast<const _Float16 *>(bias), static_cast<_Float16 *>(y), pl.a);
 }
 
-template <int S, int T1, int T2, int OFF2, int T0>
+template <int S, int T1, int T2, int OFF2, int T0, int CG>
 void launch_o(const DwPlan &pl, const void *x, const void *w, const void *bias, void *y, hipStream_t st)
 {
-    if (pl.nq <= 2) launch_t<S, T1, T2, OFF2, 2, T0>(pl, x, w, bias, y, st);
-    else launch_t<S, T1, T2, OFF2, kDwMaxChunks, T0>(pl, x, w, bias, y, st);
+    if constexpr (CG == 1) {  // groups: the large-chunk instance only
+        if (pl.nq <= 2) {
+            launch_t<S, T1, T2, OFF2, 2, T0, 1>(pl, x, w, bias, y, st);
+            return;
+        }
+    }
+    launch_t<S, T1, T2, OFF2, kDwMaxChunks, T0, CG>(pl, x, w, bias, y, st);
 }
 
-template <int S, int T, int T0>
+template <int S, int T, int T0, int CG>
 void launch_s2(const DwPlan &pl, const void *x, const void *w, const void *bias, void *y, hipStream_t st)
 {
     switch (pl.off2) {
-    case 0: launch_o<S, T, T, 0, T0>(pl, x, w, bias, y, st); break;
-    case 1: launch_o<S, T, T, 1, T0>(pl, x, w, bias, y, st); break;
-    case 2: launch_o<S, T, T, 2, T0>(pl, x, w, bias, y, st); break;
-    default: launch_o<S, T, T, 3, T0>(pl, x, w, bias, y, st); break;
+    case 0: launch_o<S, T, T, 0, T0, CG>(pl, x, w, bias, y, st); break;
+    case 1: launch_o<S, T, T, 1, T0, CG>(pl, x, w, bias, y, st); break;
+    case 2: launch_o<S, T, T, 2, T0, CG>(pl, x, w, bias, y, st); break;
+    default: launch_o<S, T, T, 3, T0, CG>(pl, x, w, bias, y, st); break;
     }
 }
 
-// the compiled instances for T0 first-axis taps (dw_compiled lists them)
-template <int T0>
+// the compiled instances for T0 first-axis taps and CG channels per group (dw_compiled
+// lists them)
+template <int T0, int CG = 1>
 void launch_all(const DwPlan &pl, const void *x, const void *w, const void *bias, void *y, hipStream_t st)
 {
-    if (pl.S == 1 && pl.T1 == 3) launch_o<1, 3, 3, 0, T0>(pl, x, w, bias, y, st);
-    else if (pl.S == 2 && pl.T1 == 1) launch_s2<2, 1, T0>(pl, x, w, bias, y, st);
-    else if (pl.S == 2 && pl.T1 == 2) launch_s2<2, 2, T0>(pl, x, w, bias, y, st);
-    else if (pl.S == 2) launch_s2<2, 3, T0>(pl, x, w, bias, y, st);
-    else if constexpr (T0 == 0) {
-        if (pl.S == 1) launch_o<1, 5, 5, 0, 0>(pl, x, w, bias, y, st);
-        else if (pl.off2 == 0) launch_o<4, 2, 2, 0, 0>(pl, x, w, bias, y, st);
-        else launch_o<4, 2, 2, 12, 0>(pl, x, w, bias, y, st);
+    if (pl.S == 2 && pl.T1 == 1) launch_s2<2, 1, T0, CG>(pl, x, w, bias, y, st);
+    else if (pl.S == 2 && pl.T1 == 2) launch_s2<2, 2, T0, CG>(pl, x, w, bias, y, st);
+    else if constexpr (CG <= 4) {
+        if (pl.S == 1 && pl.T1 == 3) launch_o<1, 3, 3, 0, T0, CG>(pl, x, w, bias, y, st);
+        else if (pl.S == 2) launch_s2<2, 3, T0, CG>(pl, x, w, bias, y, st);
+        else if constexpr (T0 == 0 && CG == 1) {
+            if (pl.S == 1) launch_o<1, 5, 5, 0, 0, 1>(pl, x, w, bias, y, st);
+            else if (pl.off2 == 0) launch_o<4, 2, 2, 0, 0, 1>(pl, x, w, bias, y, st);
+            else launch_o<4, 2, 2, 12, 0, 1>(pl, x, w, bias, y, st);
+        }
     }
 }
 
@@ -694,7 +733,10 @@ ct_status launch_depthwise(const Geom &g, ct_dtype dt, bool cl, const void *x, c
     }
     pl.a.act = act;
     mark_before(st);
-    if (pl.T0 == 0) launch_all<0>(pl, x, w, bias, y, st);
+    if (pl.CG == 2) launch_all<0, 2>(pl, x, w, bias, y, st);
+    else if (pl.CG == 4) launch_all<0, 4>(pl, x, w, bias, y, st);
+    else if (pl.CG == 8) launch_all<0, 8>(pl, x, w, bias, y, st);
+    else if (pl.T0 == 0) launch_all<0>(pl, x, w, bias, y, st);
     else if (pl.T0 == 1) launch_all<1>(pl, x, w, bias, y, st);
     else if (pl.T0 == 2) launch_all<2>(pl, x, w, bias, y, st);
     else launch_all<3>(pl, x, w, bias, y, st);
