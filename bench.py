@@ -54,7 +54,7 @@ def workloads():
     import workloads as W
     return {"c1": W.C1, "c2": W.C2, "c3": W.C3, "c3_nhwc": W.C3_NHWC, "c4": W.C4, "c4_nhwc": W.C4_NHWC,
             "c5_s1": W.C5_S1, "c5_s1_p1": W.C5_S1_P1, "c5_s2": W.C5_S2,
-            "f2_k2s2": W.F2_K2S2, "f2_1x1": W.F2_1X1, "g3_dw": W.G3_DW, "g2_nhwc": W.G2_NHWC,
+            "f2_k2s2": W.F2_K2S2, "f2_1x1": W.F2_1X1, "g3_dw": W.G3_DW, "g2_nchw": W.G2_NCHW, "g2_nhwc": W.G2_NHWC,
             # the forward convolution with the same W (the adjoint) of a configuration
             "adj_c5_s1": W.C5_S1, "adj_c4": W.C4,
             # the quantized (QLinear scheme) decoder shapes
@@ -418,7 +418,7 @@ def main():
 
 
 # Configurations timed after the headline one in the default run.
-EXTRA_CONFIGS = ("c4_nhwc", "c3", "c3_nhwc", "c5_s1", "c5_s1_p1", "c5_s2", "g3_dw")
+EXTRA_CONFIGS = ("c4_nhwc", "c3", "c3_nhwc", "c5_s1", "c5_s1_p1", "c5_s2", "g3_dw", "g2_nchw", "g2_nhwc")
 
 
 def time_workload(key, steps, warmup, rotate_arg):

@@ -84,14 +84,14 @@ def forced_tile(T, tile):
 # --------------------------------------------------------------------------------------
 # benchmark configurations
 # --------------------------------------------------------------------------------------
-WHOLE = [W.C1, W.C2, W.C3, W.C3_NHWC]
+WHOLE = [W.C1, W.C2, W.C3, W.C3_NHWC, W.G2_NCHW, W.G2_NHWC]
 FULL = [W.C4, W.C4_NHWC, W.C5_S1, W.C5_S1_P1, W.C5_S2, W.G3_DW]
 # the family the dispatcher must pick for each configuration (a silent fall-back to the
 # gather kernel would still be correct, so parity alone would not notice it)
 EXPECTED_FAMILY = {W.C1.name: "direct", W.C2.name: "igemm", W.C3.name: "grouped", W.C3_NHWC.name: "grouped",
                    W.C4.name: "igemm",
                    W.C4_NHWC.name: "igemm", W.C5_S1.name: "igemm", W.C5_S1_P1.name: "igemm", W.C5_S2.name: "igemm",
-                   W.G3_DW.name: "grouped"}
+                   W.G3_DW.name: "grouped", W.G2_NCHW.name: "grouped", W.G2_NHWC.name: "grouped"}
 
 
 def _auto_family(T, wl, x, w, b):

@@ -141,10 +141,10 @@ F2_1X1 = C4.with_(name="f2_2d_f16_1x1", w_shape=(512, 256, 1, 1), attrs=dict(str
 G3_DW = C5_S2.with_(name="g3_3d_f16_depthwise_s2", w_shape=(128, 1, 3, 3, 3), has_bias=False,
                     attrs=dict(strides=[2, 2, 2], pads=[1] * 6, output_padding=[1, 1, 1], group=128),
                     w_dist=("N", 0.0, 0.25), seed=8)
-# C3's shapes as a grouped call with 2 channels per group, channels-last
-G2_NHWC = C3.with_(name="g2_2d_f16_grouped2_s2_nhwc", w_shape=(256, 2, 4, 4), channels_last=True,
-                   attrs=dict(C3.attrs, group=128), seed=9)
-EXTRAS = {w.name: w for w in (F2_K2S2, F2_1X1, G3_DW, G2_NHWC)}
+# C3's shapes as a grouped call with 2 channels per group, channels-first and channels-last
+G2_NCHW = C3.with_(name="g2_2d_f16_grouped2_s2", w_shape=(256, 2, 4, 4), attrs=dict(C3.attrs, group=128), seed=9)
+G2_NHWC = G2_NCHW.with_(name="g2_2d_f16_grouped2_s2_nhwc", channels_last=True)
+EXTRAS = {w.name: w for w in (F2_K2S2, F2_1X1, G3_DW, G2_NCHW, G2_NHWC)}
 
 
 # --------------------------------------------------------------------------------------
