@@ -655,7 +655,7 @@ def test_allphase_kernel(T, case, cl, integer):
 
 TAPSPLIT = [
     # (x_shape, w_shape, attrs): stride 1, C/group a multiple of 32, on the tap-split kernel
-    # (64 consecutive output positions x 64 channels per workgroup, taps split over waves)
+    # (64 or 96 consecutive output positions x 64 channels per workgroup, taps split over waves)
     ((1, 32, 3, 6, 16), (32, 24, 3, 3, 3), dict()),                                   # rows of 18 flattened
     ((2, 64, 4, 5, 8), (64, 64, 3, 3, 3), dict(pads=[1] * 6)),
     ((1, 32, 2, 3, 72), (32, 40, 2, 3, 3), dict(dilations=[1, 2, 1], pads=[0, 1, 1, 0, 0, 2])),  # runs in a row
@@ -664,6 +664,9 @@ TAPSPLIT = [
     ((2, 32, 40), (32, 32, 5), dict(dilations=[3], pads=[2, 1])),
     ((1, 32, 2, 2, 8), (32, 16, 1, 1, 1), dict()),                                   # one tap: idle waves
     ((1, 128, 3, 6, 32), (128, 64, 3, 3, 3), dict()),                                # C5's channels and rows
+    # 1800 boxes of 64 positions or 1200 of 96 (planes of 192 outputs): the planner takes
+    # the 96-position boxes, which need fewer rounds of block slots
+    ((1, 32, 600, 12, 16), (32, 64, 1, 3, 3), dict(pads=[0, 1, 1, 0, 1, 1])),
 ]
 
 

@@ -5,9 +5,10 @@
 // implicit-gather GEMM that reduces over input channels x taps and stores outputs
 // directly).  With stride 1 on every axis every output o receives every tap k, from the
 // input i = o + b - k*d, so an output box of consecutive positions reads one input
-// window: the box grown by (K-1)*d on each axis.  One workgroup computes a box of 64
+// window: the box grown by (K-1)*d on each axis.  One workgroup computes a box of 64 or 96
 // consecutive output positions of one output plane (flattened over rows when a row is
-// shorter than the box, else a run inside one row) x 64 output channels:
+// shorter than the box, else a run inside one row) x 64 output channels; 96 when that
+// puts the call's blocks in fewer rounds of the chip's block slots:
 //
 //   * Two workgroups share a compute unit (78 KB of LDS each), so one's window loads
 //     overlap the other's MFMAs.  The input window ([plane][row][column][channel], a
@@ -15,17 +16,17 @@
 //     64): the channels go through it in passes, each loaded by the whole block between
 //     two barriers.
 //   * Each of the 4 waves takes every fourth tap and computes the WHOLE box over its taps
-//     (2 x 2 MFMA 32x32 tiles, float32 accumulators), so the waves read disjoint weights
+//     (2 x 2 or 2 x 3 MFMA 32x32 tiles, float32 accumulators), so the waves read disjoint weights
 //     and need no barrier in the main loop; a lane's input fragment address is its own
 //     position's window offset plus the tap's shift, so rows of any width pack the box.
 //   * A step is one tap x 32 input channels: weight fragments straight from the
 //     fragment-major packing into registers (a ring of kRing steps in flight), input
-//     fragments from LDS, v_mfma_f32_32x32x16_f16, 8 per step.
+//     fragments from LDS, v_mfma_f32_32x32x16_f16, 8 or 12 per step.
 //   * Epilogue: the four waves' partial sums meet in LDS (float32, one tile row at a
 //     time), a wave adds up one tile, adds the bias, rounds once and stages it in the
 //     output box in LDS; the box then goes out as
-//     contiguous runs (channels-first: 64 positions of a channel; channels-last: 64
-//     channels of a position).
+//     contiguous runs (channels-first: the box's positions of a channel; channels-last:
+//     64 channels of a position).
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -42,16 +43,16 @@ typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kThreads = 256;
-constexpr int kNT = 2;               // 32-position MFMA tiles per box
-constexpr int kBox = kNT * 32;       // output positions per box
-constexpr int kRing = 6;             // steps of weight fragments in flight per wave
+// A box holds NT 32-position MFMA tiles (NT = 2 or 3, chosen per call: 3 when it lets the
+// blocks of the call fit fewer rounds of the chip's two-per-CU slots)
+constexpr int box_of(int nt) { return nt * 32; }                 // output positions per box
+constexpr int part_bytes(int nt) { return 4 * nt * 16 * 64 * 4; }  // one tile row of the waves' partial sums
+constexpr int kRing = 4;             // steps of weight fragments in flight per wave
 constexpr int kMaxTaps = 32;
 constexpr int kLds = 78 * 1024;      // two workgroups per compute unit
 constexpr int kBiasBytes = 64 * 4;   // the block's 64 bias values (float32) at the end of LDS
 constexpr int kStage = kLds - kBiasBytes;
 constexpr int kHaloVec = 8;          // 16-byte window loads per thread and round
-constexpr int kPartBytes = 4 * kNT * 16 * 64 * 4;  // one tile row of the waves' partial sums (float32)
-constexpr int kSPitch = kBox + 8;    // staging pitch (halves) of the output box
 
 struct TsArgs {
     int N, C, M, Cg, Mg, G, T, Mgp, Cgp;
@@ -62,17 +63,22 @@ struct TsArgs {
     int seg;                    // 1: a box is a run inside one output row; 0: flattened rows
     int tpr, ptiles, mtiles, nblocks;
     int ntap_w[4];              // taps of each wave (taps w, w + 4, ...)
+    int nt;                     // 32-position tiles per box (the kernel's NT)
     int toff[kMaxTaps];         // window shift of tap t in positions
     Act act;
 };
 
 __device__ __forceinline__ int floor_div8(int v) { return v >= 0 ? v / 8 : -((-v + 7) / 8); }
 
-template <bool CL>
+template <bool CL, int NT>
 __global__ __launch_bounds__(kThreads, 2) void tapsplit_kernel(const _Float16 *x, const _Float16 *__restrict__ wf,
                                                                const _Float16 *__restrict__ bias,
                                                                _Float16 *__restrict__ y, TsArgs p)
 {
+    constexpr int kNT = NT;                         // 32-position MFMA tiles per box
+    constexpr int kBox = box_of(NT);                // output positions per box
+    constexpr int kPartBytes = part_bytes(NT);      // float32 partial sums of one tile row
+    constexpr int kSPitch = kBox + 8;               // staging pitch (halves) of the output box
     __shared__ __attribute__((aligned(16))) unsigned char lds[kLds];
     float *const sbias = reinterpret_cast<float *>(lds + kStage);
     const int tid = threadIdx.x;
@@ -304,9 +310,9 @@ __global__ __launch_bounds__(kThreads, 2) void tapsplit_kernel(const _Float16 *x
     }
 
     // ---------------- epilogue: partial sums meet in LDS, the box goes out ----------------
-    // Two rounds (tile row i = 0, 1): every wave writes its two tiles of row i, then
-    // waves 2i and 2i + 1 add up tile (i, 0) and (i, 1) of all four waves, add the bias,
-    // round once and stage them in the output box.
+    // Two rounds (tile row i = 0, 1): every wave writes its NT tiles of row i, then NT
+    // waves (2i and 2i + 1 for NT = 2, else 0 .. NT - 1) add up tile (i, j) of all four
+    // waves, add the bias, round once and stage them in the output box.
     __syncthreads();  // every wave is done with the input window
     if (tid < 64) sbias[tid] = bias_ok ? float(bias_h) : 0.0f;
     float *const part = reinterpret_cast<float *>(lds);  // [wave][jt][r][lane]
@@ -327,7 +333,7 @@ __global__ __launch_bounds__(kThreads, 2) void tapsplit_kernel(const _Float16 *x
 #pragma unroll
             for (int r = 0; r < 16; ++r) part[((wave * kNT + jt) * 16 + r) * 64 + lane] = acc[fi][jt][r];
         __syncthreads();
-        if (wave / kNT == fi) {  // wave-uniform
+        if (kNT == 2 ? wave / kNT == fi : wave < kNT) {  // wave-uniform
             const int fj = wave % kNT;
             f32x16 sum;
 #pragma unroll
@@ -404,6 +410,19 @@ __global__ __launch_bounds__(kThreads, 2) void tapsplit_kernel(const _Float16 *x
 }
 
 // ---------------- host-side planning ----------------
+// compute units of the current device (256 when there is none to ask)
+int device_cus()
+{
+    static thread_local int dev_cached = -1, cus_cached = 0;
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return 256;
+    if (dev == dev_cached) return cus_cached;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) return 256;
+    dev_cached = dev;
+    cus_cached = cus;
+    return cus;
+}
+
 bool make_ts_plan(const Geom &g, bool cl, TsArgs *a, std::string *why)
 {
     auto no = [&](const char *m) {
@@ -426,13 +445,7 @@ bool make_ts_plan(const Geom &g, bool cl, TsArgs *a, std::string *why)
         a->org[t] = int(g.b[t]) - span[t];
     }
     const int O2 = a->O[2];
-    a->seg = O2 >= kBox ? 1 : 0;
-    a->tpr = a->seg ? (O2 + kBox - 1) / kBox : 1;
-    a->ptiles = a->seg ? a->O[1] * a->tpr : int((int64_t(a->O[1]) * O2 + kBox - 1) / kBox);
     a->HP = 1 + span[0];
-    // rows a flattened box can touch: a run of kBox positions starting anywhere in a row
-    a->HR = (a->seg ? 1 : (O2 - 1 + kBox - 1) / O2 + 1) + span[1];
-    a->HC = (a->seg ? kBox : O2) + span[2];
     a->N = int(g.N);
     a->C = int(g.C);
     a->M = int(g.M);
@@ -443,21 +456,44 @@ bool make_ts_plan(const Geom &g, bool cl, TsArgs *a, std::string *why)
     a->Cgp = a->Cg;
     a->mtiles = int((g.Mg + 63) / 64);
     a->Mgp = a->mtiles * 64;
-    a->cw = a->Cg % 64 == 0 ? 64 : 32;
-    a->passes = a->Cg / a->cw;
-    a->pitch = a->cw * 2 + 16;
-    if ((long long)a->HP * a->HR * a->HC * a->pitch > kStage) return no("tap-split kernel: input window exceeds LDS");
-    static_assert(kPartBytes + 64 * kSPitch * 2 <= kStage && kBox * 72 * 2 <= kStage - kPartBytes, "epilogue LDS");
     for (int w = 0; w < 4; ++w) a->ntap_w[w] = (a->T - w + 3) / 4;
-    int t = 0;
-    for (int k0 = 0; k0 < g.K[0]; ++k0)
-        for (int k1 = 0; k1 < g.K[1]; ++k1)
-            for (int k2 = 0; k2 < g.K[2]; ++k2, ++t)
-                a->toff[t] = int(((g.K[0] - 1 - k0) * g.d[0] * a->HR + (g.K[1] - 1 - k1) * g.d[1]) * a->HC +
-                                 (g.K[2] - 1 - k2) * g.d[2]);
-    const long long blocks = (long long)g.N * g.G * a->mtiles * a->O[0] * a->ptiles;
-    if (blocks > INT32_MAX || blocks < 1) return no("tap-split kernel: too many blocks");
-    a->nblocks = int(blocks);
+    static_assert(part_bytes(3) + 64 * (box_of(3) + 8) * 2 <= kStage && box_of(3) * 72 * 2 <= kStage - part_bytes(3),
+                  "epilogue LDS");
+    // the box-dependent part for NT tiles per box; false when the window does not fit
+    auto fit = [&](TsArgs &b, int nt) {
+        const int box = box_of(nt);
+        b.nt = nt;
+        b.seg = O2 >= box ? 1 : 0;
+        b.tpr = b.seg ? (O2 + box - 1) / box : 1;
+        b.ptiles = b.seg ? b.O[1] * b.tpr : int((int64_t(b.O[1]) * O2 + box - 1) / box);
+        // rows a flattened box can touch: a run of box positions starting anywhere in a row
+        b.HR = (b.seg ? 1 : (O2 - 1 + box - 1) / O2 + 1) + span[1];
+        b.HC = (b.seg ? box : O2) + span[2];
+        // 64 channels per window pass when they fit, else 32
+        const long long positions = (long long)b.HP * b.HR * b.HC;
+        b.cw = b.Cg % 64 == 0 && positions * (64 * 2 + 16) <= kStage ? 64 : 32;
+        b.passes = b.Cg / b.cw;
+        b.pitch = b.cw * 2 + 16;
+        if (positions * b.pitch > kStage) return false;
+        int t = 0;
+        for (int k0 = 0; k0 < g.K[0]; ++k0)
+            for (int k1 = 0; k1 < g.K[1]; ++k1)
+                for (int k2 = 0; k2 < g.K[2]; ++k2, ++t)
+                    b.toff[t] = int(((g.K[0] - 1 - k0) * g.d[0] * b.HR + (g.K[1] - 1 - k1) * g.d[1]) * b.HC +
+                                    (g.K[2] - 1 - k2) * g.d[2]);
+        const long long blocks = (long long)g.N * g.G * b.mtiles * b.O[0] * b.ptiles;
+        if (blocks > INT32_MAX || blocks < 1) return false;
+        b.nblocks = int(blocks);
+        return true;
+    };
+    TsArgs a2 = *a, a3 = *a;
+    const bool ok2 = fit(a2, 2), ok3 = fit(a3, 3);
+    // rounds of the chip's two-per-CU block slots
+    const long long slots = 2LL * device_cus();
+    auto rounds = [&](const TsArgs &b) { return (b.nblocks + slots - 1) / slots; };
+    if (ok3 && (!ok2 || rounds(a3) < rounds(a2))) *a = a3;
+    else if (ok2) *a = a2;
+    else return no("tap-split kernel: input window exceeds LDS");
     return true;
 }
 
@@ -495,14 +531,18 @@ ct_status launch_tapsplit(const Geom &g, bool cl, const void *x, const void *w, 
     ct_status s = launch_pack_w_frag(g, w, wsp, a.Cgp, a.Mgp, w_conv, st, err);
     if (s != CT_OK) return s;
     mark_before(st);
-    if (cl)
-        hipLaunchKernelGGL(tapsplit_kernel<true>, dim3(unsigned(a.nblocks)), dim3(kThreads), 0, st,
-                           static_cast<const _Float16 *>(x), static_cast<const _Float16 *>(wsp),
-                           static_cast<const _Float16 *>(bias), static_cast<_Float16 *>(y), a);
-    else
-        hipLaunchKernelGGL(tapsplit_kernel<false>, dim3(unsigned(a.nblocks)), dim3(kThreads), 0, st,
-                           static_cast<const _Float16 *>(x), static_cast<const _Float16 *>(wsp),
-                           static_cast<const _Float16 *>(bias), static_cast<_Float16 *>(y), a);
+    auto run = [&](auto kernel) {
+        hipLaunchKernelGGL(kernel, dim3(unsigned(a.nblocks)), dim3(kThreads), 0, st, static_cast<const _Float16 *>(x),
+                           static_cast<const _Float16 *>(wsp), static_cast<const _Float16 *>(bias),
+                           static_cast<_Float16 *>(y), a);
+    };
+    if (cl) {
+        if (a.nt == 3) run(tapsplit_kernel<true, 3>);
+        else run(tapsplit_kernel<true, 2>);
+    } else {
+        if (a.nt == 3) run(tapsplit_kernel<false, 3>);
+        else run(tapsplit_kernel<false, 2>);
+    }
     mark_after(st);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) {
