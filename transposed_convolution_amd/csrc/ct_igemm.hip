@@ -308,15 +308,21 @@ __global__ __launch_bounds__(kThreads, OCC) void igemm_kernel(const _Float16 *x,
 
     // ---------------- weight tile: BM rows x CC channels of Wp ----------------
     const size_t wrow0 = size_t(g) * p.T;
+    // The packed weights' padded sizes as opaque scalars: the compiler then keeps them
+    // (spilling to vector lanes if it must) instead of re-reading them from the kernel
+    // arguments inside the loop, where that scalar load's wait also waits for the LDS
+    // reads in flight.
+    int wCgp = p.Cgp, wMgp = p.Mgp;
+    asm volatile("" : "+s"(wCgp), "+s"(wMgp));
     // PAIR: rows [0, BMM) hold column phase 0's tap, rows [BMM, BM) phase 1's tap; the
     // loads k < WVEC/2 of every thread cover exactly the first half.
     static_assert(!PAIR || (WVEC % 2 == 0 && (WVEC / 2) * kThreads == BMM * CHUNKS), "phase halves");
     auto load_w = [&](const StepIdx &q, u32x4 *reg) {
-        const int stride_vec = p.Cgp / CH16;  // 16-byte vectors per Wp row
+        const int stride_vec = wCgp / CH16;  // 16-byte vectors per Wp row
         if constexpr (!PAIR) {
             const int tflat = ((k00 + q.t0 * ks0) * p.K[1] + (k01 + q.t1 * ks1)) * p.K[2] + (k02 + q.t2 * ks2);
-            const size_t row0 = (wrow0 + tflat) * p.Mgp + size_t(mt) * BM;
-            const u32x4 *src = reinterpret_cast<const u32x4 *>(we + row0 * p.Cgp + size_t(q.chunk) * CCH);
+            const size_t row0 = (wrow0 + tflat) * wMgp + size_t(mt) * BM;
+            const u32x4 *src = reinterpret_cast<const u32x4 *>(we + row0 * wCgp + size_t(q.chunk) * CCH);
 #pragma unroll
             for (int k = 0; k < WVEC; ++k) {
                 const int u = tid + k * kThreads;
@@ -326,8 +332,8 @@ __global__ __launch_bounds__(kThreads, OCC) void igemm_kernel(const _Float16 *x,
             const int tb = ((k00 + q.t0 * ks0) * p.K[1] + (k01 + q.t1 * ks1)) * p.K[2] + q.t2 * ks2;
 #pragma unroll
             for (int h = 0; h < 2; ++h) {  // column phase h: WVEC / 2 loads
-                const size_t row0 = (wrow0 + tb + p.tk0[2][h]) * p.Mgp + size_t(mt) * BMM;
-                const u32x4 *src = reinterpret_cast<const u32x4 *>(we + row0 * p.Cgp + size_t(q.chunk) * CCH);
+                const size_t row0 = (wrow0 + tb + p.tk0[2][h]) * wMgp + size_t(mt) * BMM;
+                const u32x4 *src = reinterpret_cast<const u32x4 *>(we + row0 * wCgp + size_t(q.chunk) * CCH);
 #pragma unroll
                 for (int k = 0; k < WVEC / 2; ++k) {
                     const int u = tid + k * kThreads;
@@ -357,6 +363,12 @@ __global__ __launch_bounds__(kThreads, OCC) void igemm_kernel(const _Float16 *x,
     const int halo_items = CL ? tl.HR * tl.HC * CHUNKS : tl.HR * nvc * CHUNKS;
     // halo item -> (row, column or vector) by multiply-high (items * divisor < 2^32)
     const UDiv dhalo(CL ? tl.HC : nvc);
+    // Every halo item of a lane has the same 16-byte channel chunk (CHUNKS divides the
+    // block size), so "chunk lies inside C/group" is cbase < ch_lim with a per-lane limit
+    // held in a vector register: the loop never re-reads C/group from the kernel arguments
+    // (a scalar load there is waited for together with the LDS reads in flight).
+    static_assert(kThreads % CHUNKS == 0, "one channel chunk per lane");
+    const int ch_lim = p.Cg - (tid % CHUNKS) * CH16;
     // load_halo_part<KB, KE>: loads KB..KE-1 of the HREG halo loads (all of them for
     // <0, HREG>) and returns their validity bits (NHWC: bit per load; NC..: bit per item).
     auto load_halo_part = [&](auto kb, auto ke, int chunk, int t0, u32x4 *reg) -> unsigned {
@@ -372,8 +384,8 @@ __global__ __launch_bounds__(kThreads, OCC) void igemm_kernel(const _Float16 *x,
                 const int pix = u / CHUNKS, ch = u % CHUNKS;
                 const int hr = dhalo.div(pix), hc = pix - hr * tl.HC;
                 const int i1 = i1o + hr, i2 = i2o + hc;
-                const bool inside = u < halo_items && i1 >= 0 && i1 < L1 && i2 >= 0 && i2 < L2;
-                const bool ok = inside && cbase + ch * CH16 < p.Cg;
+                const bool inside = (u < halo_items) & (i1 >= 0) & (i1 < L1) & (i2 >= 0) & (i2 < L2);
+                const bool ok = inside & (cbase < ch_lim);
                 const size_t off = ok ? (size_t(i1) * L2 + i2) * p.C + ch * CH16 : 0;
                 reg[k] = *reinterpret_cast<const u32x4 *>((ok ? xb : xe) + off);
                 // Q8: the bit records the position only (channel padding is zeroed on store)
@@ -392,7 +404,7 @@ __global__ __launch_bounds__(kThreads, OCC) void igemm_kernel(const _Float16 *x,
                 const int hr = dhalo.div(rv), vc = rv - hr * nvc;
                 const int i1 = i1o + hr;
                 const int i2 = (va + vc) * 8;
-                const bool ok = u < halo_items && i1 >= 0 && i1 < L1 && i2 >= 0 && i2 < L2 && cbase + oct * 8 < p.Cg;
+                const bool ok = (u < halo_items) & (i1 >= 0) & (i1 < L1) & (i2 >= 0) & (i2 < L2) & (cbase < ch_lim);
                 const XE *src = ok ? xb + size_t(oct * 8) * plane_in + size_t(i1) * L2 + i2 : xe;
                 const size_t step = ok ? plane_in : 0;
                 if constexpr (ROWS8) {
