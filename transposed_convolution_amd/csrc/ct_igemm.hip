@@ -148,7 +148,7 @@ struct IgCfg {
 // channel) and T the iterated tap count.  A step is CC * 2 int8 channels (the same
 // 16-byte chunks and LDS rows as the float16 instances).
 template <bool CL, int WAVES_M, int WM, int WN, int CC, int NCH_ITEMS, int NHWC_VECS, int OCC, bool PAIR, bool ROWS8,
-          bool Q8 = false>
+          bool Q8 = false, bool WDMA = false>
 __global__ __launch_bounds__(kThreads, OCC) void igemm_kernel(const _Float16 *x, const _Float16 *__restrict__ wp,
                                                             const _Float16 *__restrict__ bias,
                                                             _Float16 *__restrict__ y, IgArgs p)
@@ -173,9 +173,19 @@ __global__ __launch_bounds__(kThreads, OCC) void igemm_kernel(const _Float16 *x,
     // main loop the whole array holds the output tile.
     __shared__ __attribute__((aligned(16))) unsigned char lds[Cfg::LDS];
     constexpr bool DIRECT = Cfg::DIRECT;
-    auto lds_w = [&](int buf) -> unsigned char * { return lds + buf * (BM * ROW); };
-    unsigned char *const lds_h = DIRECT ? lds : lds + 2 * BM * ROW;  // DIRECT: halo buffer 0
-    unsigned char *const lds_sink = lds_h + Cfg::HALO_BUFS * Cfg::HALO_BYTES;
+    // WDMA (the 256 x 256 float16 block with four taps per group): the weight tiles are
+    // copied from global memory straight into LDS (no registers), two steps ahead, into a
+    // ring of three buffers of unpadded 128-byte rows whose 16-byte chunks are permuted
+    // per row (see wdma_issue), so fragment reads stay free of bank conflicts.
+    static_assert(!WDMA || (!Q8 && !DIRECT && BM == 256 && CC == 64 && WAVES_M == 2), "WDMA: the 256 x 256 float16 block");
+    constexpr int WROW = WDMA ? CC * 2 : ROW;  // LDS bytes per weight row
+    constexpr int NWBUF = WDMA ? 3 : 2;
+    constexpr int HALO_B =
+        WDMA ? Cfg::LDS - NWBUF * BM * WROW - kSinkBytes - tail_bytes(Q8) : Cfg::HALO_BYTES;
+    static_assert(HALO_B > 0, "LDS budget");
+    auto lds_w = [&](int buf) -> unsigned char * { return lds + buf * (BM * WROW); };
+    unsigned char *const lds_h = DIRECT ? lds : lds + NWBUF * BM * WROW;  // DIRECT: halo buffer 0
+    unsigned char *const lds_sink = lds_h + Cfg::HALO_BUFS * HALO_B;
     float *const sbias = reinterpret_cast<float *>(lds_sink + kSinkBytes);  // kept to the end
     int *const sq_comp = reinterpret_cast<int *>(lds_sink + kSinkBytes);      // Q8: the same region
     float *const sq_mult = reinterpret_cast<float *>(sq_comp + 256);
@@ -623,6 +633,150 @@ __global__ __launch_bounds__(kThreads, OCC) void igemm_kernel(const _Float16 *x,
                 }
             }
         }
+    } else if constexpr (WDMA) {
+        if (nsteps > 0) {
+            // Step s reads weight buffer s % 3; during step s the tile of step s + 2 is copied
+            // into buffer (s + 2) % 3, which step s - 1 read last (done: every wave passed the
+            // barrier that ended step s - 1).  The barrier that ends step s first waits until
+            // this wave's copy of step s + 1's tile has landed: it was issued in step s - 1,
+            // so only the copies and halo loads issued in step s may still be in flight
+            // (vector memory operations complete in issue order).
+            //
+            // LDS layout of a tile: row R (output channel of the block) holds 8 chunks of 16
+            // bytes (8 input channels each); chunk c is stored at position c ^ f(R) with
+            // f(R) = (R & 7) ^ ((R >> 3) & 1), which gives the 16 lanes of one LDS cycle (16
+            // consecutive rows, one chunk) 16 distinct bank groups, and 8 consecutive rows 8.
+            // One copy instruction of a wave fills 64 consecutive 16-byte slots = 8 rows.
+            const int dr = lane >> 3, dp = lane & 7;
+            const int dc0 = dp ^ dr, dc1 = dc0 ^ 1;  // source chunk for even / odd instructions
+            const int half = PAIR ? (wave >> 1) : 0;  // PAIR: waves 0-1 phase 0 rows, 2-3 phase 1
+            const int drow = (PAIR ? (wave & 1) : wave) * 64 + dr;  // Wp row (within the tile) of k = 0
+            // byte offsets inside the packed weights (the host plans WDMA for packed weights
+            // under 2^31 bytes only)
+            const int doff0 = (drow * wCgp + dc0 * 8) * 2, doff1 = (drow * wCgp + dc1 * 8) * 2;
+            int tk_half = PAIR ? int(p.tk0[2][half]) : 0;
+            asm volatile("" : "+s"(tk_half));
+            // Buffer-resource copies (not global-address ones): the compiler counts a
+            // global-address copy into LDS as a pending LDS access of unknown order and then
+            // waits for every LDS read in flight; these it counts as vector memory only.
+            const __amdgpu_buffer_rsrc_t wrs = __builtin_amdgcn_make_buffer_rsrc(
+                const_cast<XE *>(we), short(0), p.G * p.T * wMgp * wCgp * 2, 0x00020000);
+            auto wdma_issue = [&](const StepIdx &q, int buf) {
+                const int tflat = ((k00 + q.t0 * ks0) * p.K[1] + (k01 + q.t1 * ks1)) * p.K[2] +
+                                  (PAIR ? q.t2 * ks2 + tk_half : k02 + q.t2 * ks2);
+                const int src = (((int(wrow0) + tflat) * wMgp + mt * BMM) * wCgp + q.chunk * CCH) * 2;
+                unsigned char *dst = lds_w(buf) + wave * 8 * 1024;
+#pragma unroll
+                for (int k = 0; k < 8; ++k)
+                    __builtin_amdgcn_raw_ptr_buffer_load_lds(wrs, (__attribute__((address_space(3))) void *)(dst + k * 1024),
+                                                             16, (k & 1) ? doff1 : doff0, src + k * 16 * wCgp, 0, 0);
+            };
+            // fragment (rows i*32 + l of the wave, chunk 2h + (lane >> 5)) of a tile
+            const int fl = lane & 31, ff = (fl & 7) ^ ((fl >> 3) & 1);
+            const int abase = (wm * WM * 32 + fl) * WROW + (((lane >> 5) ^ (ff & 1)) << 4);
+            const int asw = (ff & 6) << 4;
+            u32x4 hreg[HREG];
+            StepIdx cur = {0, t0_first, 0, 0};
+            {
+                StepIdx nx = cur;
+                advance(nx);
+                wdma_issue(cur, 0);
+                wdma_issue(nsteps > 1 ? nx : cur, 1);  // one step only: a harmless copy
+                const unsigned v0 = load_halo(0, t0_first, hreg);
+                store_halo(hreg, v0, 0);
+            }
+            asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+            auto mma_step_d = [&](const StepIdx &c, int buf, auto pre0, auto pre1) {
+                const int toff = ((nt1 - 1 - c.t1) * bs1 * tl.HC + (nt2 - 1 - c.t2) * bs2 + cshift) * ROW;
+                const unsigned char *hb = lds_h + toff;
+                const unsigned char *wb = lds_w(buf) + abase;
+                f16x8 a[2][WM], b[2][WN];
+#pragma unroll
+                for (int i = 0; i < WM; ++i) a[0][i] = *reinterpret_cast<const f16x8 *>(wb + i * 32 * WROW + asw);
+#pragma unroll
+                for (int j = 0; j < WN; ++j) b[0][j] = *reinterpret_cast<const f16x8 *>(hb + hoff[j]);
+#pragma unroll
+                for (int h = 0; h < KSUB; ++h) {
+                    const int cb = h & 1, nb = cb ^ 1;
+                    if (h + 1 < KSUB) {
+                        const int ah = ((h + 1) << 5) ^ asw;
+#pragma unroll
+                        for (int i = 0; i < WM; ++i) a[nb][i] = *reinterpret_cast<const f16x8 *>(wb + i * 32 * WROW + ah);
+#pragma unroll
+                        for (int j = 0; j < WN; ++j)
+                            b[nb][j] = *reinterpret_cast<const f16x8 *>(hb + hoff[j] + (h + 1) * 32);
+                    }
+                    if (h == 0 || h == 1) {
+                        if (h == 0) pre0();
+                        else pre1();
+                        __builtin_amdgcn_sched_group_barrier(0x100, 2 * (WM + WN), 0);
+#pragma unroll
+                        for (int k = 0; k < WM * WN; ++k) {
+                            __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+                            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                        }
+                    } else {
+                        __builtin_amdgcn_sched_barrier(0);
+                    }
+#pragma unroll
+                    for (int i = 0; i < WM; ++i)
+#pragma unroll
+                        for (int j = 0; j < WN; ++j)
+                            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[cb][i], b[cb][j], acc[i][j], 0, 0, 0);
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+            };
+            // Four taps per (chunk, axis-0 tap) group (the host plans this kernel only then):
+            // each step copies the tile of two steps ahead and loads a fixed quarter of the
+            // next group's halo (the last step loads its quarter first, so the halo store
+            // after it need not wait for that step's copies).
+            const int ngroups = nsteps / 4;
+            StepIdx grp = cur;
+            int wb0 = 0;  // buffer of the group's first step: (4 * gi) % 3
+            for (int gi = 0; gi < ngroups; ++gi) {
+                StepIdx ng = grp;
+                ng.t1 = nt1 - 1;
+                ng.t2 = nt2 - 1;
+                advance(ng);
+                const bool has_ng = gi + 1 < ngroups;
+                const int hch = has_ng ? ng.chunk : grp.chunk, ht0 = has_ng ? ng.t0 : grp.t0;  // last: a harmless reload
+                unsigned hv = 0;
+                auto g4_step = [&](auto U) {
+                    constexpr int u = decltype(U)::value;
+                    constexpr int PB = HREG * u / 4, PE = HREG * (u + 1) / 4;
+                    const int s = gi * 4 + u;
+                    StepIdx c = grp;
+                    c.t1 = u / nt2;
+                    c.t2 = u - c.t1 * nt2;
+                    StepIdx n2 = c;  // the step two ahead (within this group or the next)
+                    advance(n2);
+                    advance(n2);
+                    const StepIdx wtile = s + 2 < nsteps ? n2 : c;  // past the end: a harmless copy
+                    const int bcur = (wb0 + u) % 3, bnext2 = (wb0 + u + 2) % 3;
+                    auto dma = [&] { wdma_issue(wtile, bnext2); };
+                    auto halo = [&] {
+                        hv |= load_halo_part(std::integral_constant<int, PB>{}, std::integral_constant<int, PE>{},
+                                             hch, ht0, hreg);
+                    };
+                    if constexpr (u == 3) mma_step_d(c, bcur, halo, dma);
+                    else mma_step_d(c, bcur, dma, halo);
+                    // 8 copies and PE - PB halo loads were issued in this step
+                    asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(8 + PE - PB) : "memory");
+                };
+                g4_step(std::integral_constant<int, 0>{});
+                g4_step(std::integral_constant<int, 1>{});
+                g4_step(std::integral_constant<int, 2>{});
+                g4_step(std::integral_constant<int, 3>{});
+                if (has_ng) {  // the next group's halo, between two barriers
+                    store_halo(hreg, hv, hch);
+                    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+                }
+                grp = ng;
+                wb0 = (wb0 + 1) % 3;
+            }
+            // the copies past the last step land before the output stage reuses the LDS
+            asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+        }
     } else if (nsteps > 0) {
         u32x4 wreg[WVEC];
         u32x4 hreg[HREG];
@@ -874,7 +1028,7 @@ __global__ __launch_bounds__(kThreads, OCC) void igemm_kernel(const _Float16 *x,
         static_assert(CP % 8 == 4, "pitch: an odd number of 8-byte words");
         // the staged bias starts after the operand buffers and the sink
         constexpr int kBiasOffset =
-            (DIRECT ? 0 : 2 * BM * ROW) + Cfg::HALO_BUFS * Cfg::HALO_BYTES + kSinkBytes;
+            (DIRECT ? 0 : NWBUF * BM * WROW) + Cfg::HALO_BUFS * HALO_B + kSinkBytes;
         static_assert((PACKED ? (PAIR ? 2 : 1) * BN * CP : BMM * TP) * 2 <= kBiasOffset,
                       "output tile must fit in LDS below the bias");
         __syncthreads();  // every wave is done reading the operand buffers
@@ -1251,6 +1405,8 @@ struct Config {
     int row() const { return cc * 2 + 16; }
     int chunks() const { return cc / 8; }
     bool direct(bool q8) const { return waves_m == 1 && !q8; }
+    // the halo budget of the WDMA instance (three unpadded weight buffers)
+    int halo_bytes_wdma() const { return lds_budget(occ) - 3 * bm() * cc * 2 - kSinkBytes - tail_bytes(false); }
     int halo_bytes(bool q8 = false) const
     {
         return direct(q8) ? ((lds_budget(occ) - kSinkBytes - tail_bytes(q8)) / 2) / 16 * 16
@@ -1280,6 +1436,7 @@ constexpr Config kConfigs[] = {kWide, kHalf, kNarrow, kMid, kSmall};
 struct Plan {
     Config cfg;
     bool pair;  // column-phase pairs (see IgCfg)
+    bool wdma;  // the 256 x 256 block with weight tiles copied straight into LDS (see WDMA)
     IgArgs a;
     size_t ws_bytes;
 };
@@ -1341,6 +1498,10 @@ bool make_plan_cfg(const Geom &g, bool cl, const Config &cfg, Plan *pl, std::str
     };
     PhaseInfo list[kMaxPh];
     int nph = 0;
+    // WDMA: the 256 x 256 float16 block, rows of whole 16-byte vectors (or channels-last),
+    // every phase with taps having four taps per (chunk, axis-0 tap) group, and the halo
+    // within the smaller budget
+    bool wdma = !q8 && cfg == kWide && (cl || g.L[2] % 8 == 0);
     for (int r0 = 0; r0 < g.s[0]; ++r0)
         for (int r1 = 0; r1 < g.s[1]; ++r1)
             for (int r2 = 0; r2 < (pair ? 1 : g.s[2]); ++r2) {  // a pair is listed as r2 = 0
@@ -1372,6 +1533,8 @@ bool make_plan_cfg(const Geom &g, bool cl, const Config &cfg, Plan *pl, std::str
                 const int HR = seg ? 1 + e1 : std::min<int>(J1, (rmax + BN + J2 - 1) / J2) + e1;
                 const int HC = seg ? BN + e2 : J2 + e2;
                 if ((long long)HR * HC * cfg.row() > cfg.halo_bytes(q8)) return no("input halo exceeds LDS");
+                if (pi.taps > 0 && (n1 * n2 != 4 || (long long)HR * HC * cfg.row() > cfg.halo_bytes_wdma()))
+                    wdma = false;
                 if (cl && (long long)HR * HC * cfg.chunks() > (long long)cfg.nhwc_vecs * kThreads)
                     return no("input halo exceeds the loads of one block");
                 const int nvc = (HC + 7) / 8 + 1;
@@ -1394,7 +1557,9 @@ bool make_plan_cfg(const Geom &g, bool cl, const Config &cfg, Plan *pl, std::str
     a.interleave = uniform ? 1 : 0;
     pl->cfg = cfg;
     pl->pair = pair;
+    pl->wdma = wdma;
     pl->ws_bytes = size_t(a.G) * a.T * a.Mgp * a.Cgp * (q8 ? 1 : sizeof(_Float16));
+    if (pl->ws_bytes >= (size_t(1) << 31)) pl->wdma = false;  // its copies use 32-bit byte offsets
     return true;
 }
 
@@ -1455,12 +1620,12 @@ bool make_plan(const Geom &g, bool cl, Plan *pl, std::string *why, bool q8 = fal
 }
 
 template <bool CL, int WAVES_M, int WM, int WN, int CC, int NCH_ITEMS, int NHWC_VECS, int OCC, bool PAIR = false,
-          bool ROWS8 = true, bool Q8 = false>
+          bool ROWS8 = true, bool Q8 = false, bool WDMA = false>
 void launch_cfg(const IgArgs &a, const _Float16 *x, const _Float16 *wp, const _Float16 *b, _Float16 *y,
                 hipStream_t st)
 {
-    hipLaunchKernelGGL((igemm_kernel<CL, WAVES_M, WM, WN, CC, NCH_ITEMS, NHWC_VECS, OCC, PAIR, ROWS8, Q8>), dim3(unsigned(a.nblocks)),
-                       dim3(kThreads), 0, st, x, wp, b, y, a);
+    hipLaunchKernelGGL((igemm_kernel<CL, WAVES_M, WM, WN, CC, NCH_ITEMS, NHWC_VECS, OCC, PAIR, ROWS8, Q8, WDMA>),
+                       dim3(unsigned(a.nblocks)), dim3(kThreads), 0, st, x, wp, b, y, a);
 }
 
 // Launches the instance of one configuration for the plan's layout (and column-phase
@@ -1470,6 +1635,17 @@ bool launch_config(const Config &c, const Plan &pl, bool cl, const _Float16 *x, 
                    const _Float16 *b, _Float16 *y, hipStream_t st)
 {
     if (!(c == Config{WAVES_M, WM, WN, CC, NCH_ITEMS, NHWC_VECS, OCC})) return false;
+    if constexpr (WAVES_M == 2 && WM == 4 && WN == 4 && CC == 64) {
+        if (pl.wdma) {
+            if (cl)
+                launch_cfg<true, 2, 4, 4, 64, NCH_ITEMS, NHWC_VECS, OCC, false, true, false, true>(pl.a, x, wp, b, y, st);
+            else if (pl.pair)
+                launch_cfg<false, 2, 4, 4, 64, NCH_ITEMS, NHWC_VECS, OCC, true, true, false, true>(pl.a, x, wp, b, y, st);
+            else
+                launch_cfg<false, 2, 4, 4, 64, NCH_ITEMS, NHWC_VECS, OCC, false, true, false, true>(pl.a, x, wp, b, y, st);
+            return true;
+        }
+    }
     if (cl)
         launch_cfg<true, WAVES_M, WM, WN, CC, NCH_ITEMS, NHWC_VECS, OCC>(pl.a, x, wp, b, y, st);
     else if (pl.a.L[2] % 8 != 0)
