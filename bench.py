@@ -44,6 +44,7 @@ KERNEL_SOURCES = {"igemm": ["ct_igemm.hip", "ct_mphase.hip", "ct_tapsplit.hip"],
 COPY_BYTES = 256 << 20  # calibration copy: 256 MiB read + 256 MiB written
 CALIBRATE_COPY = [False]  # --calibrate-copy: one plain copy before the timed steps
 FORCE = ["auto", None]     # --kernel, --igemm-tile
+OPERANDS = ["random"]      # --operands
 
 
 def log(*a):
@@ -357,6 +358,9 @@ def main():
     ap.add_argument("--family", default="auto", choices=["auto", "direct", "grouped", "igemm"],
                     help="kernel family to force (default: the dispatcher's choice)")
     ap.add_argument("--igemm-tile", default=None, help="force one block shape of the float16 MFMA family")
+    ap.add_argument("--operands", default="random", choices=["random", "zero-x"],
+                    help="zero-x: X all zeros, the same work on operands with no bit activity (separates the "
+                         "kernel's own limits from the clock the chip sustains under random operands)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run one plain device copy of 256 MiB (counter calibration)")
     ap.add_argument("--pmc-summary", default="", help="rocprofv3 output dir to summarise (no GPU use)")
@@ -383,6 +387,7 @@ def main():
     if args.workload.startswith("f4_int8"):
         return bench_quant(args)
     CALIBRATE_COPY[0] = args.calibrate_copy
+    OPERANDS[0] = args.operands
     FORCE[0], FORCE[1] = args.family, args.igemm_tile
     if args.igemm_tile:
         T.set_igemm_tile(args.igemm_tile)
@@ -436,6 +441,8 @@ def time_workload(key, steps, warmup, rotate_arg):
     wl = workloads()[key]
     dev = torch.device("cuda:0")
     x, w, b = W.make_inputs(wl)
+    if OPERANDS[0] == "zero-x":  # the same work on an input with no bit activity
+        x = np.zeros_like(x)
     yshape, _ = T.convtranspose_output_shape(wl.x_shape, wl.w_shape, **wl.attrs)
     macs = T.convtranspose_useful_macs(wl.x_shape, wl.w_shape, **wl.attrs)
     flops = 2.0 * macs
@@ -521,7 +528,7 @@ def time_workload(key, steps, warmup, rotate_arg):
                                f"{'bias ' if wl.has_bias else ''}{wl.attrs} -> Y{list(yshape)} "
                                f"{'channels-last' if wl.channels_last else 'NCHW'}",
                    "kernel": kernel, "igemm_tile": FORCE[1], "useful_macs": macs, "accumulate": "f32",
-                   "buffer_sets": rotate,
+                   "buffer_sets": rotate, "operands": OPERANDS[0],
                    "parity_max_rel_err": err},
         "roofline": {"bound": bound, "achieved": round(achieved, 2), "peak": peak, "unit": unit,
                      "frac": round(achieved / peak, 4), "traffic": traffic,
