@@ -619,6 +619,42 @@ def test_forced_tiles(T, tile, cl, integer):
     assert ran >= len(TILE_CASES) - 2, f"tile {tile} served only {ran} of {len(TILE_CASES)} shapes"
 
 
+WDMA_CASES = [
+    # (x_shape, w_shape, attrs): shapes on which the 256 x 256 block takes its weight tiles
+    # through the three-buffer LDS copy ring (four taps per (channel chunk, axis-0 tap)
+    # group in every phase with taps; channels-first rows of whole 16-byte vectors)
+    ((2, 64, 9, 16), (64, 40, 4, 2), dict(strides=[2, 1], pads=[1, 0, 1, 1])),        # channels-first, unpaired
+    ((1, 64, 4, 6, 16), (64, 48, 3, 4, 4), dict(strides=[1, 2, 2], pads=[1] * 6)),    # 3-D: axis-0 taps cropped
+    ((1, 200, 6, 8), (200, 72, 4, 4), dict(strides=[2, 2], pads=[1] * 4)),            # partial chunk, padded rows
+    ((2, 256, 5, 8), (256, 32, 4, 4), dict(strides=[2, 2], pads=[1] * 4)),            # 16 steps round the ring
+    ((1, 16, 3, 8), (16, 16, 4, 4), dict(strides=[2, 2], pads=[1] * 4)),              # one group of four steps
+    ((3, 40, 11, 24), (40, 300, 4, 4), dict(strides=[2, 2], pads=[1, 1, 1, 1])),      # several channel tiles
+]
+
+
+@pytest.mark.parametrize("integer", [False, True], ids=["float", "int"])
+@pytest.mark.parametrize("cl", [False, True], ids=["nc", "cl"])
+@pytest.mark.parametrize("case", WDMA_CASES, ids=lambda c: f"{c[0]}_{c[1]}")
+def test_weight_copy_ring(T, case, cl, integer):
+    """The 256 x 256 float16 block with weight tiles copied into a ring of three LDS
+    buffers two steps ahead, on whole outputs: unpaired and paired channels-first rows,
+    channels-last, 3-D with axis-0 taps outside the input, a partial channel chunk,
+    padded output-channel rows, several laps of the ring and a single group."""
+    xs, ws, attrs = case
+    _log(f"[case] weight ring cl={cl} x{xs} w{ws} {attrs} integer={integer}")
+    rng = np.random.default_rng(zlib.crc32(repr(case).encode()) + 2 * integer + cl)
+    gen = (lambda sz: rng.integers(-2, 3, size=sz)) if integer else (lambda sz: rng.normal(size=sz))
+    x = gen(xs).astype(np.float16)
+    w = (gen(ws) * (1 if integer else 0.1)).astype(np.float16)
+    b = gen(ws[1] * attrs.get("group", 1)).astype(np.float16)
+    ref = O.convtranspose(x, w, b, **attrs)
+    for _ in range(2):  # a second call finds the ring's buffers holding the first call's tiles
+        with forced_tile(T, "256x256"):
+            got = gpu_run(T, x, w, b, attrs, cl, "igemm")
+        assert got is not None, "the 256 x 256 block serves these shapes"
+        check(got, ref, "f16", integer, f"weight ring cl={cl} x{xs} w{ws} {attrs}")
+
+
 ALLPHASE = [
     # (x_shape, w_shape, attrs): strided calls with >= 4 residue classes and C/group a
     # multiple of 32, on the all-phase kernel (every class of a box in one workgroup)
