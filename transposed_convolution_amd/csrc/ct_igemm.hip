@@ -415,8 +415,13 @@ __global__ __launch_bounds__(kThreads, OCC) void igemm_kernel(const _Float16 *x,
                 const int i1 = i1o + hr;
                 const int i2 = (va + vc) * 8;
                 const bool ok = (u < halo_items) & (i1 >= 0) & (i1 < L1) & (i2 >= 0) & (i2 < L2) & (cbase < ch_lim);
-                const XE *src = ok ? xb + size_t(oct * 8) * plane_in + size_t(i1) * L2 + i2 : xe;
-                const size_t step = ok ? plane_in : 0;
+                // branch-free: the offset is computed for every item and masked (a select
+                // of the whole address becomes a branch around its arithmetic, which splits
+                // the step's schedule and keeps these instructions out of the MFMA stream)
+                const size_t mask = size_t(0) - size_t(ok);
+                const size_t off = (size_t(oct * 8) * plane_in + size_t(i1) * L2 + size_t(i2)) & mask;
+                const XE *src = (ok ? xb : xe) + off;
+                const size_t step = plane_in & mask;
                 if constexpr (ROWS8) {
 #pragma unroll
                     for (int k = 0; k < 8; ++k)
