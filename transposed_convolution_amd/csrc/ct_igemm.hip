@@ -173,11 +173,11 @@ __global__ __launch_bounds__(kThreads, OCC) void igemm_kernel(const _Float16 *x,
     // main loop the whole array holds the output tile.
     __shared__ __attribute__((aligned(16))) unsigned char lds[Cfg::LDS];
     constexpr bool DIRECT = Cfg::DIRECT;
-    // WDMA (the 256 x 256 float16 block with four taps per group): the weight tiles are
+    // WDMA (the 256 x 256 block, float16 or int8, with four taps per group): the weight tiles are
     // copied from global memory straight into LDS (no registers), two steps ahead, into a
     // ring of three buffers of unpadded 128-byte rows whose 16-byte chunks are permuted
     // per row (see wdma_issue), so fragment reads stay free of bank conflicts.
-    static_assert(!WDMA || (!Q8 && !DIRECT && BM == 256 && CC == 64 && WAVES_M == 2), "WDMA: the 256 x 256 float16 block");
+    static_assert(!WDMA || (!DIRECT && BM == 256 && CC == 64 && WAVES_M == 2), "WDMA: the 256 x 256 block");
     constexpr int WROW = WDMA ? CC * 2 : ROW;  // LDS bytes per weight row
     constexpr int NWBUF = WDMA ? 3 : 2;
     constexpr int HALO_B =
@@ -658,23 +658,24 @@ __global__ __launch_bounds__(kThreads, OCC) void igemm_kernel(const _Float16 *x,
             const int drow = (PAIR ? (wave & 1) : wave) * 64 + dr;  // Wp row (within the tile) of k = 0
             // byte offsets inside the packed weights (the host plans WDMA for packed weights
             // under 2^31 bytes only)
-            const int doff0 = (drow * wCgp + dc0 * 8) * 2, doff1 = (drow * wCgp + dc1 * 8) * 2;
+            constexpr int ES = int(sizeof(XE));  // bytes per element (a 16-byte chunk holds CH16)
+            const int doff0 = (drow * wCgp + dc0 * CH16) * ES, doff1 = (drow * wCgp + dc1 * CH16) * ES;
             int tk_half = PAIR ? int(p.tk0[2][half]) : 0;
             asm volatile("" : "+s"(tk_half));
             // Buffer-resource copies (not global-address ones): the compiler counts a
             // global-address copy into LDS as a pending LDS access of unknown order and then
             // waits for every LDS read in flight; these it counts as vector memory only.
             const __amdgpu_buffer_rsrc_t wrs = __builtin_amdgcn_make_buffer_rsrc(
-                const_cast<XE *>(we), short(0), p.G * p.T * wMgp * wCgp * 2, 0x00020000);
+                const_cast<XE *>(we), short(0), p.G * p.T * wMgp * wCgp * ES, 0x00020000);
             auto wdma_issue = [&](const StepIdx &q, int buf) {
                 const int tflat = ((k00 + q.t0 * ks0) * p.K[1] + (k01 + q.t1 * ks1)) * p.K[2] +
                                   (PAIR ? q.t2 * ks2 + tk_half : k02 + q.t2 * ks2);
-                const int src = (((int(wrow0) + tflat) * wMgp + mt * BMM) * wCgp + q.chunk * CCH) * 2;
+                const int src = (((int(wrow0) + tflat) * wMgp + mt * BMM) * wCgp + q.chunk * CCH) * ES;
                 unsigned char *dst = lds_w(buf) + wave * 8 * 1024;
 #pragma unroll
                 for (int k = 0; k < 8; ++k)
                     __builtin_amdgcn_raw_ptr_buffer_load_lds(wrs, (__attribute__((address_space(3))) void *)(dst + k * 1024),
-                                                             16, (k & 1) ? doff1 : doff0, src + k * 16 * wCgp, 0, 0);
+                                                             16, (k & 1) ? doff1 : doff0, src + k * 8 * wCgp * ES, 0, 0);
             };
             // fragment (rows i*32 + l of the wave, chunk 2h + (lane >> 5)) of a tile
             const int fl = lane & 31, ff = (fl & 7) ^ ((fl >> 3) & 1);
@@ -727,7 +728,12 @@ __global__ __launch_bounds__(kThreads, OCC) void igemm_kernel(const _Float16 *x,
                     for (int i = 0; i < WM; ++i)
 #pragma unroll
                         for (int j = 0; j < WN; ++j)
-                            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[cb][i], b[cb][j], acc[i][j], 0, 0, 0);
+                            if constexpr (Q8)
+                                acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(__builtin_bit_cast(i32x4, a[cb][i]),
+                                                                                 __builtin_bit_cast(i32x4, b[cb][j]),
+                                                                                 acc[i][j], 0, 0, 0);
+                            else
+                                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[cb][i], b[cb][j], acc[i][j], 0, 0, 0);
                     __builtin_amdgcn_sched_barrier(0);
                 }
             };
@@ -1411,7 +1417,7 @@ struct Config {
     int chunks() const { return cc / 8; }
     bool direct(bool q8) const { return waves_m == 1 && !q8; }
     // the halo budget of the WDMA instance (three unpadded weight buffers)
-    int halo_bytes_wdma() const { return lds_budget(occ) - 3 * bm() * cc * 2 - kSinkBytes - tail_bytes(false); }
+    int halo_bytes_wdma(bool q8 = false) const { return lds_budget(occ) - 3 * bm() * cc * 2 - kSinkBytes - tail_bytes(q8); }
     int halo_bytes(bool q8 = false) const
     {
         return direct(q8) ? ((lds_budget(occ) - kSinkBytes - tail_bytes(q8)) / 2) / 16 * 16
@@ -1506,7 +1512,7 @@ bool make_plan_cfg(const Geom &g, bool cl, const Config &cfg, Plan *pl, std::str
     // WDMA: the 256 x 256 float16 block, rows of whole 16-byte vectors (or channels-last),
     // every phase with taps having four taps per (chunk, axis-0 tap) group, and the halo
     // within the smaller budget
-    bool wdma = !q8 && cfg == kWide && (cl || g.L[2] % 8 == 0);
+    bool wdma = cfg == kWide && (cl || g.L[2] % 8 == 0);
     for (int r0 = 0; r0 < g.s[0]; ++r0)
         for (int r1 = 0; r1 < g.s[1]; ++r1)
             for (int r2 = 0; r2 < (pair ? 1 : g.s[2]); ++r2) {  // a pair is listed as r2 = 0
@@ -1538,7 +1544,7 @@ bool make_plan_cfg(const Geom &g, bool cl, const Config &cfg, Plan *pl, std::str
                 const int HR = seg ? 1 + e1 : std::min<int>(J1, (rmax + BN + J2 - 1) / J2) + e1;
                 const int HC = seg ? BN + e2 : J2 + e2;
                 if ((long long)HR * HC * cfg.row() > cfg.halo_bytes(q8)) return no("input halo exceeds LDS");
-                if (pi.taps > 0 && (n1 * n2 != 4 || (long long)HR * HC * cfg.row() > cfg.halo_bytes_wdma()))
+                if (pi.taps > 0 && (n1 * n2 != 4 || (long long)HR * HC * cfg.row() > cfg.halo_bytes_wdma(q8)))
                     wdma = false;
                 if (cl && (long long)HR * HC * cfg.chunks() > (long long)cfg.nhwc_vecs * kThreads)
                     return no("input halo exceeds the loads of one block");
@@ -1669,6 +1675,14 @@ template <int WAVES_M, int WM, int WN, int CC, int NCH_ITEMS, int NHWC_VECS, int
 bool launch_config_q8(const Config &c, const Plan &pl, const void *x, const void *wp, void *y, hipStream_t st)
 {
     if (!(c == Config{WAVES_M, WM, WN, CC, NCH_ITEMS, NHWC_VECS, OCC})) return false;
+    if constexpr (WAVES_M == 2 && WM == 4 && WN == 4 && CC == 64) {
+        if (pl.wdma) {
+            launch_cfg<true, 2, 4, 4, 64, NCH_ITEMS, NHWC_VECS, OCC, false, true, true, true>(
+                pl.a, static_cast<const _Float16 *>(x), static_cast<const _Float16 *>(wp), nullptr,
+                static_cast<_Float16 *>(y), st);
+            return true;
+        }
+    }
     launch_cfg<true, WAVES_M, WM, WN, CC, NCH_ITEMS, NHWC_VECS, OCC, false, true, true>(
         pl.a, static_cast<const _Float16 *>(x), static_cast<const _Float16 *>(wp), nullptr, static_cast<_Float16 *>(y),
         st);
