@@ -648,7 +648,7 @@ __global__ __launch_bounds__(kThreads, OCC) void igemm_kernel(const _Float16 *x,
             // (vector memory operations complete in issue order).
             //
             // LDS layout of a tile: row R (output channel of the block) holds 8 chunks of 16
-            // bytes (8 input channels each); chunk c is stored at position c ^ f(R) with
+            // bytes (8 float16 or 16 int8 input channels); chunk c is stored at position c ^ f(R) with
             // f(R) = (R & 7) ^ ((R >> 3) & 1), which gives the 16 lanes of one LDS cycle (16
             // consecutive rows, one chunk) 16 distinct bank groups, and 8 consecutive rows 8.
             // One copy instruction of a wave fills 64 consecutive 16-byte slots = 8 rows.
