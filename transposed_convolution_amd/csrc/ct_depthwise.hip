@@ -333,9 +333,11 @@ __global__ __launch_bounds__(kDwThreads) void depthwise_kernel(const _Float16 *_
                         for (int m = 0; m < NP; ++m) wp[v0][rh][rwp][a][m] = h2{e[2 * m], e[2 * m + 1]};
                         wt[v0][rh][rwp][a] = (T2 & 1) ? float(e[T2 - 1]) : 0.0f;
                     }
-        // two copies of the item loop, with and without streaming stores: a store under a
-        // run-time choice would be merged with the plain one and lose its cache hint
-        auto items = [&](auto streaming) __attribute__((always_inline)) {
+        // copies of the item loop, with and without streaming stores (a store under a
+        // run-time choice would be merged with the plain one and lose its cache hint) and
+        // with and without an activation (a run-time test in the loop made the compiler
+        // shuffle the eight results between registers on every item)
+        auto items = [&](auto streaming, auto identity) __attribute__((always_inline)) {
         for (int seg = seg0, orr = or0; orr < orows;) {
             const int jr = orr / S, rh = orr - jr * S;
             // value of row phase rh among S candidates of 32 bits, by byte permutes on its
@@ -427,7 +429,7 @@ __global__ __launch_bounds__(kDwThreads) void depthwise_kernel(const _Float16 *_
                     }
                 }
             }
-            if (!p.act.identity()) {
+            if constexpr (!decltype(identity)::value) {
 #pragma unroll
                 for (int e = 0; e < OC; ++e) out[e] = p.act(out[e]);
             }
@@ -454,10 +456,15 @@ __global__ __launch_bounds__(kDwThreads) void depthwise_kernel(const _Float16 *_
             }
         }
         };
-        if (stream)
-            items(std::true_type{});
+        const bool idn = p.act.identity();
+        if (stream && idn)
+            items(std::true_type{}, std::true_type{});
+        else if (stream)
+            items(std::true_type{}, std::false_type{});
+        else if (idn)
+            items(std::false_type{}, std::true_type{});
         else
-            items(std::false_type{});
+            items(std::false_type{}, std::false_type{});
         }
         __syncthreads();  // the stage and seff are rewritten next
         if (tn >= p.units) break;
