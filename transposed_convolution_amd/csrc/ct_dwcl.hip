@@ -40,7 +40,10 @@ typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kThreads = 256;
-constexpr int kTJ1 = 8, kTJ2 = 16;  // phase-grid positions per tile
+// phase-grid positions per tile: 14 x 8 divides a 56 x 56 phase grid exactly and gives
+// each of the 32 position slots 3-4 positions; 8 x 16 left a quarter of the tiles an
+// eighth empty, 8 x 8 gave too little work per thread, 28 x 8 too few blocks
+constexpr int kTJ1 = 14, kTJ2 = 8;
 
 // acc + x * w for the low (high) float16 halves of x and w, in float32 with one rounding
 // (v_fma_mix_f32: the float16 operands are widened exactly), so weights stay packed
